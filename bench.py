@@ -1,0 +1,203 @@
+"""Throughput benchmark of the chunked-state forward (the hot path), one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_context_131k]
+
+A step is one kata_fwd_chunked call (chunk-state build, prefix scan over chunk states,
+intra-chunk tiles + inter-chunk readout + output gate) over the whole workload, with q, k, v
+already resident in HBM and the output and workspace preallocated.  W untimed steps, then K
+steps timed with HIP events on the stream the kernels are launched on; the library's own
+per-kernel events give the dominant kernel's average duration for the roofline figure.
+
+Printed: one JSON line.  value = head-tokens (B*H*T) per second.  roofline: algorithmic bytes
+of the dominant kernel per launch / its average duration, against MI355X's 8 TB/s HBM peak.
+cpu_baseline: the fp64 CPU oracle (brute-force closed form) timed on a bounded uniform sample
+of the same workload's query rows, scaled to head-tokens/s.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd tokens/sec (B·H·T/s) at p=16,d_v=64 vs T; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+KERNEL_SOURCES = {  # files whose content defines each kernel's code
+    "chunk_output": ["kernelized_psd_feature_amd/csrc/fast.hip",
+                     "kernelized_psd_feature_amd/csrc/generic.hip"],
+    "quadratic": ["kernelized_psd_feature_amd/csrc/fast.hip",
+                  "kernelized_psd_feature_amd/csrc/generic.hip"],
+}
+
+
+def algorithmic_bytes_per_token(p, dv, in_bytes=2, out_bytes=4):
+    # read q, k (p each) and v (dv) once, write o (dv) once
+    return in_bytes * (2 * p + dv) + out_bytes * dv
+
+
+def chunked_flops_per_token(p, dv, C):
+    # state build 2p^2 dv + normalizer 2p^2, readout 2p^2 dv + q^T Z q (2p^2 + 2p),
+    # intra-chunk tile (C+1)/2 causal pairs on average of 2p + 2dv + 2 (score, square, PV,
+    # row sum), epilogue dv
+    return (4 * p * p * dv + 4 * p * p + 2 * p + (C + 1) * (p + dv + 1) + dv)
+
+
+def source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload, sha):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("kernel_source_sha") != sha:
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, target_s=12.0):
+    """Time the oracle's closed form on uniformly sampled query rows of one head of the
+    workload; head-tokens/s of the oracle on the full workload = rows / seconds (a uniform
+    sample has the workload's average cost per row)."""
+    import numpy as np
+    import torch
+
+    import kata_workloads as W
+    import oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    q, k, v = W.make_inputs(w, 0, B=1, H=1)
+    Q, Kk, V = (x[0, :, 0].to(torch.float64).numpy() for x in (q, k, v))
+    rng = np.random.default_rng(0)
+    n, done, spent = 32, 0, 0.0
+    while spent < target_s:
+        rows = rng.integers(0, w.T, size=n)
+        t0 = time.perf_counter()
+        O.closed_form_rows(Q, Kk, V, rows, block=16)
+        spent += time.perf_counter() - t0
+        done += n
+        n = min(4 * n, 4096)
+    return {
+        "value": done / spent, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+        "sample": f"{done} query rows drawn uniformly from head 0 (T={w.T}) of the {w.name} "
+                  f"workload, fp64 brute-force closed form, {spent:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_context_131k")
+    ap.add_argument("--form", choices=["chunked", "quadratic"], default="chunked")
+    ap.add_argument("--seg", type=int, default=0, help="chunks per segment (0 = library default)")
+    ap.add_argument("--layout", choices=["bthd", "bhtd"], default="bthd")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="run only a device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(every (batch, head) is independent; see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kata_workloads as W
+    import kernelized_psd_feature_amd as K
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n}), flush=True)
+        return
+
+    w = next(x for x in W.WORKLOADS.values() if x.name == args.workload)
+    q, k, v = W.make_inputs(w, 0)
+    if args.layout == "bhtd":
+        q, k, v = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
+    q, k, v = (x.to(dev) for x in (q, k, v))
+    o = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    ws = None
+    if args.form == "chunked":
+        need = K.chunked_workspace_size(q, k, v, chunk=w.chunk, seg_chunks=args.seg)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
+    def step():
+        if args.form == "chunked":
+            K.fwd_chunked(q, k, v, chunk=w.chunk, seg_chunks=args.seg, out=o, workspace=ws)
+        else:
+            K.fwd_quadratic(q, k, v, out=o)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    K.timing_begin()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    per_kernel = K.timing_end()
+    ms = start.elapsed_time(stop) / args.steps
+    tokens = w.B * w.H * w.T
+    value = tokens / (ms / 1e3)
+
+    dom = "chunk_output" if args.form == "chunked" else "quadratic"
+    launches, total_ms = per_kernel[dom]
+    avg_ms = total_ms / max(launches, 1)
+    bpt = algorithmic_bytes_per_token(w.p, w.dv)
+    bytes_launch = bpt * tokens
+    achieved = bytes_launch / (avg_ms / 1e3) / 1e9
+    sha = source_sha(KERNEL_SOURCES[dom])
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": load_traffic(dom, w.name, sha),
+    }
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "p": w.p, "dv": w.dv,
+                   "chunk": w.chunk, "form": args.form, "seg_chunks": args.seg,
+                   "layout": args.layout.upper(), "out_dtype": "fp32", "eps": 1e-6},
+        "roofline": roofline,
+        "kernels_ms": {n: round(t / max(c, 1), 5) for n, (c, t) in per_kernel.items() if c},
+        "step_roofline_frac": round(bpt * tokens / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "dominant_kernel_source_sha": sha,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

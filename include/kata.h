@@ -1,0 +1,178 @@
+/*
+ * kata.h -- C ABI of the MI355X (gfx950) library for causal, normalized linear attention
+ * with the rank-one PSD feature map psi(u) = u u^T ("KATA").
+ *
+ * What every forward call computes, per batch b and head h, for t = 0 .. T-1:
+ *
+ *     o_t = sum_{s<=t} (q_t . k_s)^2 v_s  /  (eps + sum_{s<=t} (q_t . k_s)^2)
+ *
+ * Sources: gist.science "Technische Samenvatting", section 2.2 (psi(u) = u u^T squares the raw
+ * inner product) and section 2.1 (the normalizing denominator is a convex output gate);
+ * ai.info "AI summary", Main Findings, the bullet on the free readout gate.  eps is added once,
+ * outside the sum; the diagonal s = t is included; q and k are used as given (no scaling).
+ *
+ * Conventions shared by every call
+ *   - All data pointers are DEVICE pointers on the current HIP device, owned by the caller.
+ *     The library never allocates, frees or retains them; scratch memory comes only from the
+ *     caller's workspace, whose size is queried first.  Inputs are read-only.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every call only
+ *     enqueues work on that stream and returns without synchronizing.  A kernel fault shows
+ *     up at the caller's next synchronization, not in the return code.
+ *   - Tensor layout: q, k are [B][T][H][p], v and o are [B][T][H][d_v] (the layout of the
+ *     pages' kernel call, KATA README), addressed through ELEMENT strides for the (b, t, h)
+ *     axes; the last axis is contiguous.  Head-major [B][H][T][D] is the same call with other
+ *     strides.  Every row (the base pointer and each stride times the element size) must be
+ *     16-byte aligned.
+ *   - Validation happens on the host, before anything is enqueued: a call that returns an
+ *     error has launched nothing.  No call aborts or throws across the ABI.
+ *   - Thread safety: calls may come from several host threads; the only global state is a
+ *     lazily filled per-device property cache and the optional timing recorder (one per
+ *     host thread).
+ */
+#ifndef KATA_H
+#define KATA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KATA_OK = 0,
+  KATA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, stride, alignment or eps       */
+  KATA_ERR_UNSUPPORTED = 2,      /* a valid problem this build has no kernel for          */
+  KATA_ERR_WORKSPACE = 3,        /* workspace pointer null or smaller than required       */
+  KATA_ERR_DEVICE = 4            /* no usable gfx950 device, or a launch error            */
+} kata_status;
+
+typedef enum { KATA_F32 = 0, KATA_BF16 = 1 } kata_dtype;
+
+/* One attention problem.  Sizes:
+ *   B, H, T >= 1;  p in {8, 16, 32} (q/k width);  dv in {16, 64} (value width);
+ *   chunk: C for the chunked form, one of {16, 32, 64}, T % C == 0 (ignored by the quadratic
+ *          form); chunk c covers tokens [cC, (c+1)C).
+ *   seg_chunks: chunked form only: chunks per segment L (0 = library default).  The chunked
+ *          form keeps the running state on chip for L consecutive chunks and combines the
+ *          per-segment states with the prefix scan; L = 1 scans every chunk state.
+ *   eps: finite, >= 0 (1e-6 in every workload).
+ *   in_dtype: dtype of q, k, v (and dO); out_dtype: dtype of o.  Allowed pairs:
+ *          (BF16 -> F32), (BF16 -> BF16), (F32 -> F32).  Gradients are always F32.
+ *   sq, sk, sv, so, sdo: element strides of the (b, t, h) axes of q, k, v, o and dO.
+ *          Gradient outputs dq, dk, dv use the strides of q, k, v respectively. */
+typedef struct {
+  int32_t B, H, T, p, dv;
+  int32_t chunk;
+  int32_t seg_chunks;
+  float eps;
+  int32_t in_dtype;
+  int32_t out_dtype;
+  int64_t sq[3], sk[3], sv[3], so[3], sdo[3];
+} kata_problem;
+
+/* Flash-style O(T^2) forward: tiles of Q K^T, squared and causally masked, then P V and a
+ * row sum for the denominator; the feature state is never formed.
+ * Source: gist.science section 2.3 (quadratic operating point, FlashAttention-style kernel
+ * that does not materialize the state); KATA README (direct kernel call on (B,T,H,D)).
+ *   q, k, v: inputs as above.  o: output [B][T][H][dv] of out_dtype.
+ *   den: optional (NULL allowed) fp32 [B][T][H], contiguous, receives D_t = eps + sum_s a.
+ * Errors: INVALID_ARGUMENT / UNSUPPORTED / DEVICE as described above. */
+kata_status kata_fwd_quadratic(const kata_problem* pr, const void* q, const void* k,
+                               const void* v, void* o, float* den, void* stream);
+
+/* Bytes of device workspace kata_fwd_chunked needs for this problem (0 for an invalid one). */
+size_t kata_fwd_chunked_workspace_size(const kata_problem* pr);
+
+/* Exact O(T) chunked-state forward.  For each chunk c the state is
+ *     dS_c = sum_{s in c} vec(k_s k_s^T) v_s^T  (p^2 x dv),   dZ_c = sum_{s in c} k_s k_s^T,
+ * an exclusive prefix scan gives S_{<c}, Z_{<c}, and for t in chunk c
+ *     o_t = (vec(q_t q_t^T)^T S_{<c} + sum_{s in c, s<=t} a_ts v_s)
+ *           / (eps + q_t^T Z_{<c} q_t + sum_{s in c, s<=t} a_ts).
+ * Source: gist.science section 2.3 (chunked parallelism: intra-chunk attention on matrix
+ * units, inter-chunk state propagation by an associative scan, depth O(log N_C)); ai.info
+ * Main Findings (chunk recurrence without a triangular solve; state size); the paper review's
+ * Validation paragraph (the chunked-state form is exact).
+ * Arguments as kata_fwd_quadratic, plus a device workspace of at least
+ * kata_fwd_chunked_workspace_size(pr) bytes, 256-byte aligned; its contents on entry are
+ * ignored and on exit undefined.  Errors: as above, plus WORKSPACE. */
+kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* k,
+                             const void* v, void* o, float* den, void* workspace,
+                             size_t ws_bytes, void* stream);
+
+/* Bytes of workspace kata_chunk_state_scan needs (0 when n_chunks fits one tree). */
+size_t kata_chunk_state_scan_workspace_size(int64_t n_seq, int64_t n_chunks,
+                                            int64_t state_elems);
+
+/* Associative prefix scan over chunk states, in place, fp32:
+ *     states[s][c][e]  <-  sum_{i<c} states[s][i][e]    (exclusive != 0)
+ *     states[s][c][e]  <-  sum_{i<=c} states[s][i][e]   (exclusive == 0)
+ * for every sequence s < n_seq and element e < state_elems, each element independently.
+ * The operator is plain addition because the state update is additive and commutative
+ * (ai.info Main Findings, readout-gate bullet); it is evaluated as a Kogge-Stone tree of depth
+ * ceil(log2 n_chunks) (gist.science section 2.3: depth O(N_C) -> O(log N_C); the paper
+ * review's Results paragraph: O(log(T/C))).
+ *   states: device fp32 [n_seq][n_chunks][state_elems], contiguous, 16-byte aligned,
+ *           state_elems % 4 == 0.
+ *   totals: optional device fp32 [n_seq][state_elems]: receives the inclusive total (the
+ *           state after the last chunk).
+ *   workspace/ws_bytes: at least kata_chunk_state_scan_workspace_size(...) bytes (NULL/0 when
+ *           that is 0).
+ *   levels: optional host int32 out: the depth of the combining tree that was run.
+ * Errors: INVALID_ARGUMENT, WORKSPACE, DEVICE. */
+kata_status kata_chunk_state_scan(float* states, int64_t n_seq, int64_t n_chunks,
+                                  int64_t state_elems, int32_t exclusive, float* totals,
+                                  void* workspace, size_t ws_bytes, int32_t* levels,
+                                  void* stream);
+
+/* Bytes of workspace kata_bwd needs. */
+size_t kata_bwd_workspace_size(const kata_problem* pr);
+
+/* Gradients of L = sum_t <dO_t, o_t> with respect to q, k, v, all arithmetic in fp32:
+ *     delta_t = dO_t . o_t,   G_ts = (dO_t . v_s - delta_t) / D_t   (s <= t)
+ *     dq_t = sum_s 2 (q_t.k_s) G_ts k_s,  dk_s = sum_t 2 (q_t.k_s) G_ts q_t,
+ *     dv_s = sum_{t>=s} (q_t.k_s)^2 dO_t / D_t.
+ * Source: the KATA README names a flash forward/backward; the formulas are the derivative
+ * of the closed form above (the pages print none).
+ *   dO: [B][T][H][dv] of in_dtype (strides sdo).  dq, dk, dv: fp32 outputs with the strides
+ *   of q, k, v.  The workspace holds D_t and delta_t (fp32 [B][T][H] each).
+ * Errors: as kata_fwd_chunked. */
+kata_status kata_bwd(const kata_problem* pr, const void* q, const void* k, const void* v,
+                     const void* dO, void* dq, void* dk, void* dv, void* workspace,
+                     size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* kata_status_string(kata_status s);
+
+/* Text describing the last error returned on this host thread ("" if none). */
+const char* kata_last_error(void);
+
+/* ---- Per-kernel timing (measurement support; off by default) --------------------------
+ * kata_timing_begin(): on this host thread, from now on every kernel the library enqueues is
+ * bracketed by a pair of HIP events on the stream it is launched on.
+ * kata_timing_end(): synchronizes those events and returns, per kernel kind, the number of
+ * launches and the summed elapsed milliseconds; recording stops.  Kinds are indexed by
+ * kata_kernel_kind.  Returns INVALID_ARGUMENT if begin was not called, DEVICE on an event
+ * error. */
+typedef enum {
+  KATA_K_QUADRATIC = 0,
+  KATA_K_CHUNK_STATE = 1,
+  KATA_K_SCAN = 2,
+  KATA_K_CHUNK_OUTPUT = 3,
+  KATA_K_BWD = 4,
+  KATA_K_COUNT = 5
+} kata_kernel_kind;
+
+typedef struct {
+  int64_t launches[KATA_K_COUNT];
+  double total_ms[KATA_K_COUNT];
+} kata_kernel_times;
+
+kata_status kata_timing_begin(void);
+kata_status kata_timing_end(kata_kernel_times* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KATA_H */

@@ -1,0 +1,68 @@
+// Device-side helpers shared by the gfx950 kernels, and the launcher declarations the host
+// API calls.  Nothing here is part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace kata {
+
+// Problem description passed to kernels by value.
+struct DevProblem {
+  int B, H, T, p, dv, C;
+  float eps;
+  long long sq[3], sk[3], sv[3], so[3], sdo[3];   // element strides of (b, t, h)
+};
+
+__device__ __forceinline__ long long row_off(const long long* s, int b, int t, int h) {
+  return (long long)b * s[0] + (long long)t * s[1] + (long long)h * s[2];
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }   // RNE
+
+// ---- launchers (defined in the .hip files) --------------------------------------------
+// in_bf16 / out_bf16 select the element types; every launcher returns hipGetLastError().
+
+hipError_t launch_quadratic_generic(const DevProblem& pr, bool in_bf16, bool out_bf16,
+                                    const void* q, const void* k, const void* v, void* o,
+                                    float* den, hipStream_t st);
+
+hipError_t launch_chunk_state_generic(const DevProblem& pr, bool in_bf16, const void* k,
+                                      const void* v, float* states, int n_chunks,
+                                      hipStream_t st);
+
+hipError_t launch_chunk_output_generic(const DevProblem& pr, bool in_bf16, bool out_bf16,
+                                       const void* q, const void* k, const void* v, void* o,
+                                       float* den, const float* states, int n_chunks,
+                                       hipStream_t st);
+
+// Prefix scan of one tile-level: rows [tile*tile_rows, ...) of every sequence, `strip`
+// coordinates per workgroup.  tile_offsets (nullable) holds the exclusive offset of each
+// tile, [n_seq][n_tiles][elems].
+hipError_t launch_scan_tiles(float* x, long long n_seq, long long n, long long elems,
+                             int strip, int tile_rows, int n_tiles, int exclusive,
+                             float* totals, const float* tile_offsets, hipStream_t st);
+
+hipError_t launch_tile_sums(const float* x, long long n_seq, long long n, long long elems,
+                            int tile_rows, int n_tiles, float* sums, hipStream_t st);
+
+hipError_t launch_bwd_prep(const DevProblem& pr, bool in_bf16, const void* q, const void* k,
+                           const void* v, const void* dO, float* D, float* delta,
+                           hipStream_t st);
+hipError_t launch_bwd_dq(const DevProblem& pr, bool in_bf16, const void* q, const void* k,
+                         const void* v, const void* dO, const float* D, const float* delta,
+                         float* dq, hipStream_t st);
+hipError_t launch_bwd_dkdv(const DevProblem& pr, bool in_bf16, const void* q, const void* k,
+                           const void* v, const void* dO, const float* D, const float* delta,
+                           float* dk, float* dv, hipStream_t st);
+
+}  // namespace kata

@@ -1,0 +1,251 @@
+// fp32-arithmetic VALU kernels for gfx950: the quadratic forward, the chunk-state build and
+// chunk readout of the chunked forward (one segment per chunk), for every supported
+// (p, dv, dtype).  They are the exact-arithmetic path (fp32 throughout, no bf16 rounding of
+// intermediates) used for fp32 inputs and for shapes without an MFMA kernel.
+//
+// Math: a_ts = (q_t . k_s)^2 for s <= t (gist.science section 2.2: psi(u) = u u^T squares the
+// inner product), o_t = sum a_ts v_s / (eps + sum a_ts) (section 2.1; ai.info Main Findings,
+// readout-gate bullet).  Chunked form: gist.science section 2.3.
+#include "device.h"
+
+namespace kata {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = 64;   // queries (or chunk tokens) per workgroup; 4 threads per row
+
+// ------------------------------------------------------------------------------------
+// Quadratic forward.  Grid (ceil(T/64), H, B); thread (row = tid % 64, part = tid / 64)
+// owns dv/4 output columns of one query.  Keys are staged 64 at a time in LDS.
+// ------------------------------------------------------------------------------------
+template <typename Tin, typename Tout, int P, int DV>
+__global__ __launch_bounds__(kThreads) void quadratic_generic_kernel(
+    DevProblem pr, const Tin* __restrict__ q, const Tin* __restrict__ k,
+    const Tin* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den) {
+  constexpr int DP = DV / 4;
+  __shared__ float ks[kRows][P];
+  __shared__ float vs[kRows][DV];
+  const int b = blockIdx.z, h = blockIdx.y, t0 = blockIdx.x * kRows;
+  const int row = threadIdx.x % kRows, part = threadIdx.x / kRows;
+  const int t = t0 + row;
+
+  float qr[P];
+  if (t < pr.T) {
+    const Tin* qp = q + row_off(pr.sq, b, t, h);
+#pragma unroll
+    for (int i = 0; i < P; ++i) qr[i] = to_f32(qp[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < P; ++i) qr[i] = 0.f;
+  }
+  float acc[DP];
+#pragma unroll
+  for (int j = 0; j < DP; ++j) acc[j] = 0.f;
+  float l = 0.f;
+
+  const int kend = min(pr.T, t0 + kRows);
+  for (int s0 = 0; s0 < kend; s0 += kRows) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kRows * P; e += kThreads) {
+      int s = e / P, i = e % P, ss = s0 + s;
+      ks[s][i] = ss < pr.T ? to_f32(k[row_off(pr.sk, b, ss, h) + i]) : 0.f;
+    }
+    for (int e = threadIdx.x; e < kRows * DV; e += kThreads) {
+      int s = e / DV, d = e % DV, ss = s0 + s;
+      vs[s][d] = ss < pr.T ? to_f32(v[row_off(pr.sv, b, ss, h) + d]) : 0.f;
+    }
+    __syncthreads();
+    const int smax = min(kRows, kend - s0);
+    for (int s = 0; s < smax; ++s) {
+      if (s0 + s <= t) {                       // causal mask by selection
+        float dot = 0.f;
+#pragma unroll
+        for (int i = 0; i < P; ++i) dot = fmaf(qr[i], ks[s][i], dot);
+        const float a = dot * dot;
+        l += a;
+#pragma unroll
+        for (int j = 0; j < DP; ++j) acc[j] = fmaf(a, vs[s][part * DP + j], acc[j]);
+      }
+    }
+  }
+  if (t < pr.T) {
+    const float D = pr.eps + l;
+    Tout* op = o + row_off(pr.so, b, t, h) + part * DP;
+#pragma unroll
+    for (int j = 0; j < DP; ++j) op[j] = from_f32<Tout>(acc[j] / D);
+    if (den && part == 0) den[((long long)b * pr.T + t) * pr.H + h] = D;
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Chunk states, one chunk per workgroup.  Grid (n_chunks, H, B).  State layout (floats):
+// e = d * p^2 + (i * p + j) for d < dv  ->  dS[i*p+j][d] = sum_s k_i k_j v_d
+//     d = dv                            ->  dZ[i][j]     = sum_s k_i k_j
+// ------------------------------------------------------------------------------------
+template <typename Tin, int P, int DV>
+__global__ __launch_bounds__(kThreads) void chunk_state_generic_kernel(
+    DevProblem pr, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    float* __restrict__ states, int n_chunks) {
+  constexpr int PP = P * P;
+  constexpr int E = PP * (DV + 1);
+  __shared__ float ks[kRows][P];
+  __shared__ float vs[kRows][DV + 1];
+  const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
+  const int C = pr.C, tb = c * C;
+  for (int e = threadIdx.x; e < C * P; e += kThreads) {
+    int s = e / P, i = e % P;
+    ks[s][i] = to_f32(k[row_off(pr.sk, b, tb + s, h) + i]);
+  }
+  for (int e = threadIdx.x; e < C * (DV + 1); e += kThreads) {
+    int s = e / (DV + 1), d = e % (DV + 1);
+    vs[s][d] = d < DV ? to_f32(v[row_off(pr.sv, b, tb + s, h) + d]) : 1.f;
+  }
+  __syncthreads();
+  float* out = states + ((long long)(b * pr.H + h) * n_chunks + c) * E;
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    const int d = e / PP, f = e % PP, i = f / P, j = f % P;
+    float acc = 0.f;
+    for (int s = 0; s < C; ++s) acc = fmaf(ks[s][i] * ks[s][j], vs[s][d], acc);
+    out[e] = acc;
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Chunk readout, one chunk per workgroup, from the exclusive prefix state S_{<c}, Z_{<c}.
+// Grid (n_chunks, H, B); thread (row = token in chunk, part = dv/4 columns).
+// ------------------------------------------------------------------------------------
+template <typename Tin, typename Tout, int P, int DV>
+__global__ __launch_bounds__(kThreads) void chunk_output_generic_kernel(
+    DevProblem pr, const Tin* __restrict__ q, const Tin* __restrict__ k,
+    const Tin* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den,
+    const float* __restrict__ states, int n_chunks) {
+  constexpr int PP = P * P;
+  constexpr int E = PP * (DV + 1);
+  constexpr int DP = DV / 4;
+  __shared__ float ks[kRows][P];
+  __shared__ float vs[kRows][DV];
+  const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
+  const int C = pr.C, tb = c * C;
+  const int row = threadIdx.x % kRows, part = threadIdx.x / kRows;
+  for (int e = threadIdx.x; e < C * P; e += kThreads) {
+    int s = e / P, i = e % P;
+    ks[s][i] = to_f32(k[row_off(pr.sk, b, tb + s, h) + i]);
+  }
+  for (int e = threadIdx.x; e < C * DV; e += kThreads) {
+    int s = e / DV, d = e % DV;
+    vs[s][d] = to_f32(v[row_off(pr.sv, b, tb + s, h) + d]);
+  }
+  __syncthreads();
+  if (row >= C) return;
+  const int t = tb + row;
+  float qr[P];
+  const Tin* qp = q + row_off(pr.sq, b, t, h);
+#pragma unroll
+  for (int i = 0; i < P; ++i) qr[i] = to_f32(qp[i]);
+
+  // inter-chunk: phi(q)^T S_{<c} and q^T Z_{<c} q, phi_f = q_i q_j
+  const float* S = states + ((long long)(b * pr.H + h) * n_chunks + c) * E;
+  float acc[DP];
+#pragma unroll
+  for (int j = 0; j < DP; ++j) acc[j] = 0.f;
+  float zq = 0.f;
+  for (int i = 0; i < P; ++i) {
+    for (int jj = 0; jj < P; ++jj) {
+      const float phi = qr[i] * qr[jj];
+      const int f = i * P + jj;
+#pragma unroll
+      for (int j = 0; j < DP; ++j) acc[j] = fmaf(phi, S[(part * DP + j) * PP + f], acc[j]);
+      zq = fmaf(phi, S[DV * PP + f], zq);
+    }
+  }
+  // intra-chunk: causal tile, diagonal included
+  float l = 0.f;
+  for (int s = 0; s <= row; ++s) {
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) dot = fmaf(qr[i], ks[s][i], dot);
+    const float a = dot * dot;
+    l += a;
+#pragma unroll
+    for (int j = 0; j < DP; ++j) acc[j] = fmaf(a, vs[s][part * DP + j], acc[j]);
+  }
+  const float D = pr.eps + (zq + l);
+  Tout* op = o + row_off(pr.so, b, t, h) + part * DP;
+#pragma unroll
+  for (int j = 0; j < DP; ++j) op[j] = from_f32<Tout>(acc[j] / D);
+  if (den && part == 0) den[((long long)b * pr.T + t) * pr.H + h] = D;
+}
+
+// ---- dispatch over (P, DV, dtypes) ----------------------------------------------------
+template <template <typename, typename, int, int> class Launch, typename... Args>
+hipError_t dispatch_io(int p, int dv, bool in_bf16, bool out_bf16, Args&&... args) {
+#define KATA_CASE(P_, DV_)                                                                   \
+  if (p == P_ && dv == DV_) {                                                                \
+    if (in_bf16 && out_bf16) return Launch<__bf16, __bf16, P_, DV_>::run(args...);           \
+    if (in_bf16) return Launch<__bf16, float, P_, DV_>::run(args...);                        \
+    return Launch<float, float, P_, DV_>::run(args...);                                      \
+  }
+  KATA_CASE(8, 16) KATA_CASE(8, 64) KATA_CASE(16, 16) KATA_CASE(16, 64) KATA_CASE(32, 16)
+  KATA_CASE(32, 64)
+#undef KATA_CASE
+  return hipErrorInvalidValue;
+}
+
+template <typename Tin, typename Tout, int P, int DV>
+struct QuadLaunch {
+  static hipError_t run(const DevProblem& pr, const void* q, const void* k, const void* v,
+                        void* o, float* den, hipStream_t st) {
+    dim3 grid((pr.T + kRows - 1) / kRows, pr.H, pr.B);
+    quadratic_generic_kernel<Tin, Tout, P, DV><<<grid, kThreads, 0, st>>>(
+        pr, (const Tin*)q, (const Tin*)k, (const Tin*)v, (Tout*)o, den);
+    return hipGetLastError();
+  }
+};
+
+template <typename Tin, typename Tout, int P, int DV>
+struct StateLaunch {
+  static hipError_t run(const DevProblem& pr, const void* k, const void* v, float* states,
+                        int n_chunks, hipStream_t st) {
+    dim3 grid(n_chunks, pr.H, pr.B);
+    chunk_state_generic_kernel<Tin, P, DV><<<grid, kThreads, 0, st>>>(
+        pr, (const Tin*)k, (const Tin*)v, states, n_chunks);
+    return hipGetLastError();
+  }
+};
+
+template <typename Tin, typename Tout, int P, int DV>
+struct OutputLaunch {
+  static hipError_t run(const DevProblem& pr, const void* q, const void* k, const void* v,
+                        void* o, float* den, const float* states, int n_chunks,
+                        hipStream_t st) {
+    dim3 grid(n_chunks, pr.H, pr.B);
+    chunk_output_generic_kernel<Tin, Tout, P, DV><<<grid, kThreads, 0, st>>>(
+        pr, (const Tin*)q, (const Tin*)k, (const Tin*)v, (Tout*)o, den, states, n_chunks);
+    return hipGetLastError();
+  }
+};
+
+}  // namespace
+
+hipError_t launch_quadratic_generic(const DevProblem& pr, bool in_bf16, bool out_bf16,
+                                    const void* q, const void* k, const void* v, void* o,
+                                    float* den, hipStream_t st) {
+  return dispatch_io<QuadLaunch>(pr.p, pr.dv, in_bf16, out_bf16, pr, q, k, v, o, den, st);
+}
+
+hipError_t launch_chunk_state_generic(const DevProblem& pr, bool in_bf16, const void* k,
+                                      const void* v, float* states, int n_chunks,
+                                      hipStream_t st) {
+  // the state kernel has no output tensor; pass out_bf16 = false
+  return dispatch_io<StateLaunch>(pr.p, pr.dv, in_bf16, false, pr, k, v, states, n_chunks, st);
+}
+
+hipError_t launch_chunk_output_generic(const DevProblem& pr, bool in_bf16, bool out_bf16,
+                                       const void* q, const void* k, const void* v, void* o,
+                                       float* den, const float* states, int n_chunks,
+                                       hipStream_t st) {
+  return dispatch_io<OutputLaunch>(pr.p, pr.dv, in_bf16, out_bf16, pr, q, k, v, o, den,
+                                   states, n_chunks, st);
+}
+
+}  // namespace kata

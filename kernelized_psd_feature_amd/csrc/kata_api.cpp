@@ -1,0 +1,366 @@
+// Host implementation of the C ABI declared in include/kata.h.
+//
+// Every entry point validates its arguments on the host (plan.cpp), checks that the current
+// device is a gfx950, then enqueues its kernels on the caller's stream and returns without
+// synchronizing.  Scratch memory comes only from the caller's workspace.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "device.h"
+#include "kata.h"
+#include "plan.h"
+
+namespace kata {
+hipError_t launch_quadratic_fast(const DevProblem& pr, bool out_bf16, const void* q,
+                                 const void* k, const void* v, void* o, float* den,
+                                 hipStream_t st);
+bool quadratic_fast_supported(const kata_problem* pr);
+bool chunk_fast_available();
+hipError_t launch_chunk_state_fast(const DevProblem& pr, int L, int n_seg, const void* k,
+                                   const void* v, float* states, hipStream_t st);
+hipError_t launch_chunk_output_fast(const DevProblem& pr, bool out_bf16, int L, int n_seg,
+                                    const void* q, const void* k, const void* v, void* o,
+                                    float* den, const float* states, hipStream_t st);
+}  // namespace kata
+
+namespace {
+
+using kata::Form;
+
+thread_local std::string g_last_error;
+
+kata_status set_error(kata_status s, const std::string& why) {
+  g_last_error = why;
+  return s;
+}
+
+// ---- device check: the code objects in this library are built for gfx950 only ----------
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mutex;
+int g_dev_state[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
+
+kata_status check_device(void) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_error(KATA_ERR_DEVICE, std::string("no usable HIP device: ") +
+                                          hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_dev_mutex);
+  if (g_dev_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return set_error(KATA_ERR_DEVICE, std::string("hipGetDeviceProperties failed: ") +
+                                            hipGetErrorString(e));
+    g_dev_state[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    if (g_dev_state[dev] < 0) g_last_error = std::string("device is ") + prop.gcnArchName;
+  }
+  if (g_dev_state[dev] < 0) return set_error(KATA_ERR_DEVICE, "device is not a gfx950");
+  return KATA_OK;
+}
+
+// ---- optional per-kernel timing ----------------------------------------------------
+struct TimingRec {
+  int kind;
+  hipEvent_t a, b;
+};
+struct TimingState {
+  bool on = false;
+  std::vector<TimingRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+thread_local TimingState g_timing;
+
+// Brackets one launch with events when timing is on.
+struct Timed {
+  int kind;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  Timed(int kind_, hipStream_t st_) : kind(kind_), st(st_) {
+    if (g_timing.on) {
+      a = g_timing.get();
+      if (a && hipEventRecord(a, st) != hipSuccess) {
+        g_timing.pool.push_back(a);
+        a = nullptr;
+      }
+    }
+  }
+  ~Timed() {
+    if (a) {
+      hipEvent_t b = g_timing.get();
+      if (b && hipEventRecord(b, st) == hipSuccess) {
+        g_timing.recs.push_back({kind, a, b});
+      } else {
+        g_timing.pool.push_back(a);
+        if (b) g_timing.pool.push_back(b);
+      }
+    }
+  }
+};
+
+kata::DevProblem to_dev(const kata_problem* pr) {
+  kata::DevProblem d;
+  d.B = pr->B;
+  d.H = pr->H;
+  d.T = pr->T;
+  d.p = pr->p;
+  d.dv = pr->dv;
+  d.C = pr->chunk;
+  d.eps = pr->eps;
+  for (int i = 0; i < 3; ++i) {
+    d.sq[i] = pr->sq[i];
+    d.sk[i] = pr->sk[i];
+    d.sv[i] = pr->sv[i];
+    d.so[i] = pr->so[i];
+    d.sdo[i] = pr->sdo[i];
+  }
+  return d;
+}
+
+kata_status launch_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return KATA_OK;
+  return set_error(KATA_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+kata_status check_forward_args(const kata_problem* pr, Form f, const void* q, const void* k,
+                               const void* v, const void* o, const float* den) {
+  std::string why;
+  kata_status s = kata::validate_problem(pr, f, &why);
+  if (s != KATA_OK) return set_error(s, why);
+  const size_t ei = kata::elem_size(pr->in_dtype), eo = kata::elem_size(pr->out_dtype);
+  if ((s = kata::validate_tensor(q, pr->sq, ei, "q", &why)) != KATA_OK) return set_error(s, why);
+  if ((s = kata::validate_tensor(k, pr->sk, ei, "k", &why)) != KATA_OK) return set_error(s, why);
+  if ((s = kata::validate_tensor(v, pr->sv, ei, "v", &why)) != KATA_OK) return set_error(s, why);
+  if ((s = kata::validate_tensor(o, pr->so, eo, "o", &why)) != KATA_OK) return set_error(s, why);
+  if (den && reinterpret_cast<uintptr_t>(den) % 4)
+    return set_error(KATA_ERR_INVALID_ARGUMENT, "den is not 4-byte aligned");
+  return KATA_OK;
+}
+
+// Recursive prefix scan driver (see plan_scan).
+hipError_t run_scan(float* x, int64_t n_seq, int64_t n, int64_t elems, int exclusive,
+                    float* totals, char* ws, hipStream_t st) {
+  kata::ScanPlan sp = kata::plan_scan(n_seq, n, elems);
+  if (sp.n_tiles == 1)
+    return kata::launch_scan_tiles(x, n_seq, n, elems, (int)sp.strip, (int)n, 1, exclusive,
+                                   totals, nullptr, st);
+  float* sums = reinterpret_cast<float*>(ws);
+  char* sub = ws + ((size_t(n_seq) * sp.n_tiles * elems * 4 + 255) & ~size_t(255));
+  hipError_t e = kata::launch_tile_sums(x, n_seq, n, elems, (int)sp.tile_rows,
+                                        (int)sp.n_tiles, sums, st);
+  if (e != hipSuccess) return e;
+  e = run_scan(sums, n_seq, sp.n_tiles, elems, 1, nullptr, sub, st);
+  if (e != hipSuccess) return e;
+  return kata::launch_scan_tiles(x, n_seq, n, elems, (int)sp.strip, (int)sp.tile_rows,
+                                 (int)sp.n_tiles, exclusive, totals, sums, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kata_status_string(kata_status s) {
+  switch (s) {
+    case KATA_OK: return "ok";
+    case KATA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case KATA_ERR_UNSUPPORTED: return "unsupported problem";
+    case KATA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KATA_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* kata_last_error(void) { return g_last_error.c_str(); }
+
+kata_status kata_fwd_quadratic(const kata_problem* pr, const void* q, const void* k,
+                               const void* v, void* o, float* den, void* stream) {
+  g_last_error.clear();
+  kata_status s = check_forward_args(pr, Form::Quadratic, q, k, v, o, den);
+  if (s != KATA_OK) return s;
+  if ((s = check_device()) != KATA_OK) return s;
+  const kata::DevProblem dp = to_dev(pr);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool in_bf16 = pr->in_dtype == KATA_BF16, out_bf16 = pr->out_dtype == KATA_BF16;
+  Timed t(KATA_K_QUADRATIC, st);
+  if (kata::quadratic_fast_supported(pr))
+    return launch_status(kata::launch_quadratic_fast(dp, out_bf16, q, k, v, o, den, st),
+                         "quadratic forward");
+  return launch_status(kata::launch_quadratic_generic(dp, in_bf16, out_bf16, q, k, v, o, den, st),
+                       "quadratic forward");
+}
+
+size_t kata_fwd_chunked_workspace_size(const kata_problem* pr) {
+  if (kata::validate_problem(pr, Form::Chunked, nullptr) != KATA_OK) return 0;
+  return kata::plan_chunked(pr, kata::chunk_fast_available()).ws_bytes;
+}
+
+kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* k,
+                             const void* v, void* o, float* den, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  kata_status s = check_forward_args(pr, Form::Chunked, q, k, v, o, den);
+  if (s != KATA_OK) return s;
+  const kata::ChunkPlan cp = kata::plan_chunked(pr, kata::chunk_fast_available());
+  if (!workspace || ws_bytes < cp.ws_bytes)
+    return set_error(KATA_ERR_WORKSPACE, "workspace needs " + std::to_string(cp.ws_bytes) +
+                                             " bytes, got " + std::to_string(ws_bytes));
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return set_error(KATA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  if ((s = check_device()) != KATA_OK) return s;
+  const kata::DevProblem dp = to_dev(pr);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool in_bf16 = pr->in_dtype == KATA_BF16, out_bf16 = pr->out_dtype == KATA_BF16;
+  float* states = reinterpret_cast<float*>(workspace);
+  char* scan_ws = reinterpret_cast<char*>(workspace) + cp.states_bytes;
+  hipError_t e;
+  {
+    Timed t(KATA_K_CHUNK_STATE, st);
+    e = cp.fast ? kata::launch_chunk_state_fast(dp, cp.L, cp.n_seg, k, v, states, st)
+                : kata::launch_chunk_state_generic(dp, in_bf16, k, v, states, cp.n_chunks, st);
+  }
+  if (e != hipSuccess) return launch_status(e, "chunk-state kernel");
+  {
+    // exclusive prefix over segments (one segment: the prefix is zero)
+    Timed t(KATA_K_SCAN, st);
+    e = run_scan(states, cp.n_seq, cp.n_seg, cp.state_elems, 1, nullptr, scan_ws, st);
+  }
+  if (e != hipSuccess) return launch_status(e, "chunk-state scan");
+  {
+    Timed t(KATA_K_CHUNK_OUTPUT, st);
+    e = cp.fast ? kata::launch_chunk_output_fast(dp, out_bf16, cp.L, cp.n_seg, q, k, v, o,
+                                                 den, states, st)
+                : kata::launch_chunk_output_generic(dp, in_bf16, out_bf16, q, k, v, o, den,
+                                                    states, cp.n_chunks, st);
+  }
+  return launch_status(e, "chunk-output kernel");
+}
+
+size_t kata_chunk_state_scan_workspace_size(int64_t n_seq, int64_t n_chunks,
+                                            int64_t state_elems) {
+  if (n_seq < 1 || n_chunks < 1 || state_elems < 4) return 0;
+  return kata::plan_scan(n_seq, n_chunks, state_elems).ws_bytes;
+}
+
+kata_status kata_chunk_state_scan(float* states, int64_t n_seq, int64_t n_chunks,
+                                  int64_t state_elems, int32_t exclusive, float* totals,
+                                  void* workspace, size_t ws_bytes, int32_t* levels,
+                                  void* stream) {
+  g_last_error.clear();
+  if (!states) return set_error(KATA_ERR_INVALID_ARGUMENT, "states is null");
+  if (n_seq < 1 || n_chunks < 1 || state_elems < 4 || state_elems % 4)
+    return set_error(KATA_ERR_INVALID_ARGUMENT,
+                     "need n_seq >= 1, n_chunks >= 1, state_elems >= 4 and a multiple of 4");
+  if (n_seq > 65535 || n_chunks > (int64_t(1) << 26) || state_elems > (int64_t(1) << 30))
+    return set_error(KATA_ERR_INVALID_ARGUMENT, "scan sizes out of range");
+  if (reinterpret_cast<uintptr_t>(states) % 16 || (totals && reinterpret_cast<uintptr_t>(totals) % 16))
+    return set_error(KATA_ERR_INVALID_ARGUMENT, "states/totals must be 16-byte aligned");
+  const kata::ScanPlan sp = kata::plan_scan(n_seq, n_chunks, state_elems);
+  if (sp.ws_bytes && (!workspace || ws_bytes < sp.ws_bytes))
+    return set_error(KATA_ERR_WORKSPACE, "workspace needs " + std::to_string(sp.ws_bytes) +
+                                             " bytes, got " + std::to_string(ws_bytes));
+  if (workspace && reinterpret_cast<uintptr_t>(workspace) % 256)
+    return set_error(KATA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  if (levels) *levels = sp.levels;
+  kata_status s = check_device();
+  if (s != KATA_OK) return s;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Timed t(KATA_K_SCAN, st);
+  return launch_status(run_scan(states, n_seq, n_chunks, state_elems, exclusive ? 1 : 0,
+                                totals, reinterpret_cast<char*>(workspace), st),
+                       "chunk-state scan");
+}
+
+size_t kata_bwd_workspace_size(const kata_problem* pr) {
+  if (kata::validate_problem(pr, Form::Backward, nullptr) != KATA_OK) return 0;
+  return kata::bwd_workspace_bytes(pr);
+}
+
+kata_status kata_bwd(const kata_problem* pr, const void* q, const void* k, const void* v,
+                     const void* dO, void* dq, void* dk, void* dv, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  std::string why;
+  kata_status s = kata::validate_problem(pr, Form::Backward, &why);
+  if (s != KATA_OK) return set_error(s, why);
+  const size_t ei = kata::elem_size(pr->in_dtype);
+  struct {
+    const void* p;
+    const int64_t* st;
+    size_t es;
+    const char* name;
+  } ts[] = {{q, pr->sq, ei, "q"},  {k, pr->sk, ei, "k"},  {v, pr->sv, ei, "v"},
+            {dO, pr->sdo, ei, "dO"}, {dq, pr->sq, 4, "dq"}, {dk, pr->sk, 4, "dk"},
+            {dv, pr->sv, 4, "dv"}};
+  for (auto& x : ts)
+    if ((s = kata::validate_tensor(x.p, x.st, x.es, x.name, &why)) != KATA_OK)
+      return set_error(s, why);
+  const size_t need = kata::bwd_workspace_bytes(pr);
+  if (!workspace || ws_bytes < need)
+    return set_error(KATA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) +
+                                             " bytes, got " + std::to_string(ws_bytes));
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return set_error(KATA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  if ((s = check_device()) != KATA_OK) return s;
+  const kata::DevProblem dp = to_dev(pr);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool in_bf16 = pr->in_dtype == KATA_BF16;
+  float* D = reinterpret_cast<float*>(workspace);
+  float* delta = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + need / 2);
+  Timed t(KATA_K_BWD, st);
+  hipError_t e = kata::launch_bwd_prep(dp, in_bf16, q, k, v, dO, D, delta, st);
+  if (e == hipSuccess)
+    e = kata::launch_bwd_dq(dp, in_bf16, q, k, v, dO, D, delta, static_cast<float*>(dq), st);
+  if (e == hipSuccess)
+    e = kata::launch_bwd_dkdv(dp, in_bf16, q, k, v, dO, D, delta, static_cast<float*>(dk),
+                              static_cast<float*>(dv), st);
+  return launch_status(e, "backward");
+}
+
+kata_status kata_timing_begin(void) {
+  g_last_error.clear();
+  for (auto& r : g_timing.recs) {
+    g_timing.pool.push_back(r.a);
+    g_timing.pool.push_back(r.b);
+  }
+  g_timing.recs.clear();
+  g_timing.on = true;
+  return KATA_OK;
+}
+
+kata_status kata_timing_end(kata_kernel_times* out) {
+  g_last_error.clear();
+  if (!out) return set_error(KATA_ERR_INVALID_ARGUMENT, "out is null");
+  if (!g_timing.on) return set_error(KATA_ERR_INVALID_ARGUMENT, "timing was not begun");
+  g_timing.on = false;
+  std::memset(out, 0, sizeof(*out));
+  kata_status s = KATA_OK;
+  for (auto& r : g_timing.recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      s = set_error(KATA_ERR_DEVICE, "event timing failed");
+    if (r.kind >= 0 && r.kind < KATA_K_COUNT) {
+      out->launches[r.kind] += 1;
+      out->total_ms[r.kind] += ms;
+    }
+    g_timing.pool.push_back(r.a);
+    g_timing.pool.push_back(r.b);
+  }
+  g_timing.recs.clear();
+  return s;
+}
+
+}  // extern "C"

@@ -1,0 +1,166 @@
+// Host-side argument validation and launch planning (pure C++, no HIP).
+#include "plan.h"
+
+#include <cmath>
+
+namespace kata {
+
+namespace {
+
+kata_status fail(std::string* why, kata_status s, const std::string& msg) {
+  if (why) *why = msg;
+  return s;
+}
+
+bool in_set(int32_t x, std::initializer_list<int32_t> s) {
+  for (int32_t y : s)
+    if (x == y) return true;
+  return false;
+}
+
+int64_t next_pow2(int64_t x) {
+  int64_t p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+int ceil_log2(int64_t x) {
+  int l = 0;
+  while ((int64_t(1) << l) < x) ++l;
+  return l;
+}
+
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+}  // namespace
+
+size_t elem_size(int32_t dtype) {
+  return dtype == KATA_F32 ? 4 : dtype == KATA_BF16 ? 2 : 0;
+}
+
+bool dtype_pair_ok(int32_t in, int32_t out, Form f) {
+  if (in != KATA_F32 && in != KATA_BF16) return false;
+  if (f == Form::Backward) return true;                 // gradients are always fp32
+  if (in == KATA_F32) return out == KATA_F32;
+  return out == KATA_F32 || out == KATA_BF16;
+}
+
+kata_status validate_problem(const kata_problem* pr, Form f, std::string* why) {
+  if (!pr) return fail(why, KATA_ERR_INVALID_ARGUMENT, "problem pointer is null");
+  if (pr->B < 1 || pr->H < 1 || pr->T < 1)
+    return fail(why, KATA_ERR_INVALID_ARGUMENT, "B, H and T must be >= 1");
+  if (pr->T > kMaxT) return fail(why, KATA_ERR_UNSUPPORTED, "T exceeds 2^26");
+  if (int64_t(pr->B) * pr->H > 65535)
+    return fail(why, KATA_ERR_UNSUPPORTED, "B*H exceeds 65535");
+  if (pr->p < 1 || pr->dv < 1)
+    return fail(why, KATA_ERR_INVALID_ARGUMENT, "p and dv must be >= 1");
+  if (!in_set(pr->p, {8, 16, 32}))
+    return fail(why, KATA_ERR_UNSUPPORTED, "p must be 8, 16 or 32");
+  if (!in_set(pr->dv, {16, 64}))
+    return fail(why, KATA_ERR_UNSUPPORTED, "dv must be 16 or 64");
+  if (!std::isfinite(pr->eps) || pr->eps < 0.0f)
+    return fail(why, KATA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (!dtype_pair_ok(pr->in_dtype, pr->out_dtype, f))
+    return fail(why, KATA_ERR_INVALID_ARGUMENT,
+                "dtype pair must be bf16->fp32, bf16->bf16 or fp32->fp32");
+  if (f == Form::Chunked) {
+    if (pr->chunk < 1) return fail(why, KATA_ERR_INVALID_ARGUMENT, "chunk must be >= 1");
+    if (!in_set(pr->chunk, {16, 32, 64}))
+      return fail(why, KATA_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64");
+    if (pr->T % pr->chunk)
+      return fail(why, KATA_ERR_UNSUPPORTED, "T must be a multiple of chunk");
+    if (pr->seg_chunks < 0)
+      return fail(why, KATA_ERR_INVALID_ARGUMENT, "seg_chunks must be >= 0");
+  }
+  const int64_t* strides[5] = {pr->sq, pr->sk, pr->sv, pr->so, pr->sdo};
+  const char* names[5] = {"q", "k", "v", "o", "dO"};
+  const int64_t last[5] = {pr->p, pr->p, pr->dv, pr->dv, pr->dv};
+  const int64_t sizes[3] = {pr->B, pr->T, pr->H};
+  for (int i = 0; i < 5; ++i) {
+    if (i == 4 && f != Form::Backward) continue;
+    // every (b, t, h) row must start past the previous row's last element along some order;
+    // the minimal check that catches swapped or zero strides: each stride of an axis with
+    // more than one entry is >= the row length.
+    for (int a = 0; a < 3; ++a) {
+      int64_t s = strides[i][a];
+      if (s < 0) return fail(why, KATA_ERR_INVALID_ARGUMENT, std::string(names[i]) + ": negative stride");
+      if (sizes[a] > 1 && s < last[i])
+        return fail(why, KATA_ERR_INVALID_ARGUMENT,
+                    std::string(names[i]) + ": stride smaller than the row length");
+    }
+  }
+  return KATA_OK;
+}
+
+kata_status validate_tensor(const void* ptr, const int64_t st[3], size_t esize,
+                            const char* name, std::string* why) {
+  if (!ptr) return fail(why, KATA_ERR_INVALID_ARGUMENT, std::string(name) + " is null");
+  if (reinterpret_cast<uintptr_t>(ptr) % 16)
+    return fail(why, KATA_ERR_INVALID_ARGUMENT, std::string(name) + " is not 16-byte aligned");
+  for (int a = 0; a < 3; ++a)
+    if ((uint64_t(st[a]) * esize) % 16)
+      return fail(why, KATA_ERR_INVALID_ARGUMENT,
+                  std::string(name) + ": stride is not a multiple of 16 bytes");
+  return KATA_OK;
+}
+
+ScanPlan plan_scan(int64_t n_seq, int64_t n, int64_t elems) {
+  ScanPlan sp;
+  sp.n_seq = n_seq;
+  sp.n = n;
+  sp.elems = elems;
+  if (n <= 0 || n_seq <= 0 || elems <= 0) return sp;
+  int64_t np2 = next_pow2(n);
+  if (np2 * 4 <= kScanLdsFloats) {
+    // one tree over all n rows; strip of coordinates as wide as the LDS tile allows
+    int64_t strip = kScanLdsFloats / np2;
+    if (strip > 64) strip = 64;
+    sp.strip = strip;
+    sp.tile_rows = n;
+    sp.n_tiles = 1;
+    sp.ws_bytes = 0;
+    sp.levels = ceil_log2(n);
+    return sp;
+  }
+  // tiles of 256 rows; their totals are scanned by a recursive plan
+  sp.tile_rows = 256;
+  sp.strip = 64;
+  sp.n_tiles = (n + sp.tile_rows - 1) / sp.tile_rows;
+  ScanPlan sub = plan_scan(n_seq, sp.n_tiles, elems);
+  sp.ws_bytes = round256(size_t(n_seq) * size_t(sp.n_tiles) * size_t(elems) * 4) + sub.ws_bytes;
+  // tile sums (tree, log2 tile) -> scan of the totals -> tile tree + offset add
+  sp.levels = 2 * ceil_log2(sp.tile_rows) + sub.levels + 1;
+  return sp;
+}
+
+ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
+  ChunkPlan cp;
+  cp.n_chunks = pr->T / pr->chunk;
+  cp.n_seq = int64_t(pr->B) * pr->H;
+  cp.state_elems = int64_t(pr->p) * pr->p * (pr->dv + 1);
+  cp.fast = (fast_available && pr->in_dtype == KATA_BF16 && pr->p == 16 && pr->dv == 64 && pr->chunk == 64) ? 1 : 0;
+  if (cp.fast) {
+    int L = pr->seg_chunks;
+    if (L == 0) {
+      // enough workgroups to fill 256 CUs about four deep, segments no longer than 32 chunks
+      L = 32;
+      while (L > 1 && cp.n_seq * ((cp.n_chunks + L - 1) / L) < 1024) L >>= 1;
+    }
+    if (L > cp.n_chunks) L = cp.n_chunks;
+    cp.L = L;
+  } else {
+    cp.L = 1;   // the VALU path scans every chunk state
+  }
+  cp.n_seg = (cp.n_chunks + cp.L - 1) / cp.L;
+  cp.states_bytes = round256(size_t(cp.n_seq) * size_t(cp.n_seg) * size_t(cp.state_elems) * 4);
+  cp.scan_ws_bytes = plan_scan(cp.n_seq, cp.n_seg, cp.state_elems).ws_bytes;
+  cp.ws_bytes = cp.states_bytes + cp.scan_ws_bytes;
+  return cp;
+}
+
+size_t bwd_workspace_bytes(const kata_problem* pr) {
+  // D_t and delta_t, fp32 [B][H][T] each
+  return 2 * round256(size_t(pr->B) * pr->H * pr->T * 4);
+}
+
+}  // namespace kata

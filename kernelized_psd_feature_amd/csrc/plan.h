@@ -1,0 +1,58 @@
+// Host-side argument validation and launch planning.  Pure C++ (no HIP): it is compiled into
+// libkata.so and, on its own, into a CPU test driver built with sanitizers.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "kata.h"
+
+namespace kata {
+
+enum class Form { Quadratic, Chunked, Backward };
+
+// Which kernels run a chunked forward, and the workspace they need.
+struct ChunkPlan {
+  int fast = 0;               // 1: bf16 MFMA kernels; 0: fp32-arithmetic VALU kernels
+  int L = 1;                  // chunks per segment
+  int n_chunks = 0;           // N_c = T / C per (b, h)
+  int n_seg = 0;              // ceil(N_c / L)
+  int dv_split = 1;           // workgroups sharing one segment, each owning dv / dv_split columns
+  int64_t n_seq = 0;          // B * H
+  int64_t state_elems = 0;    // floats in one segment state: p^2 (dv + 1)
+  size_t states_bytes = 0;    // n_seq * n_seg * state_elems * 4, rounded up to 256
+  size_t scan_ws_bytes = 0;   // extra workspace of the prefix scan over n_seg segments
+  size_t ws_bytes = 0;        // total
+};
+
+// Prefix-scan tiling: a single Kogge-Stone tree when the chunk count fits one LDS tile, else
+// tiles of `tile_rows` rows whose totals are scanned recursively.
+struct ScanPlan {
+  int64_t n_seq = 0, n = 0, elems = 0;
+  int64_t tile_rows = 0;      // rows one workgroup scans in LDS
+  int64_t strip = 0;          // coordinates per workgroup
+  int64_t n_tiles = 0;        // ceil(n / tile_rows)
+  size_t ws_bytes = 0;        // tile totals (recursive), 0 for a single tile
+  int levels = 0;             // depth of the combining tree
+};
+
+constexpr int64_t kMaxT = int64_t(1) << 26;
+constexpr int64_t kScanLdsFloats = 16384;   // per buffer; two buffers = 128 KiB of LDS
+
+size_t elem_size(int32_t dtype);
+bool dtype_pair_ok(int32_t in, int32_t out, Form f);
+
+// Checks sizes, dtypes, eps and strides.  Returns KATA_OK or an error with `why` filled in.
+kata_status validate_problem(const kata_problem* pr, Form f, std::string* why);
+
+// Checks that a tensor's base pointer and strides keep every row 16-byte aligned.
+kata_status validate_tensor(const void* ptr, const int64_t st[3], size_t esize,
+                            const char* name, std::string* why);
+
+ScanPlan plan_scan(int64_t n_seq, int64_t n, int64_t elems);
+// pr must have passed validate_problem; fast_available: the MFMA chunked kernels are built.
+ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available);
+size_t bwd_workspace_bytes(const kata_problem* pr);
+
+}  // namespace kata

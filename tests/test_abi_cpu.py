@@ -1,0 +1,209 @@
+"""C-ABI checks that need no GPU: libkata.so loads, exports every function include/kata.h
+declares, and rejects bad arguments with the documented status codes before touching a
+device.  Fake (never dereferenced) device pointers are used: validation runs first."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import kernelized_psd_feature_amd as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kata.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, DEVICE = 0, 1, 2, 3, 4
+FAKE = 0x7F0000000000          # 256-byte aligned, never dereferenced
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    names = set(re.findall(r"\b(kata_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
+
+
+def _lib():
+    if not os.path.exists(K.library_path()):
+        pytest.fail("libkata.so is not built (run python -m kernelized_psd_feature_amd.build)")
+    return K._lib()
+
+
+def _problem(B=1, H=2, T=128, p=16, dv=64, chunk=64, eps=1e-6, in_dt=1, out_dt=0, seg=0):
+    pr = K._Problem()
+    pr.B, pr.H, pr.T, pr.p, pr.dv, pr.chunk, pr.seg_chunks, pr.eps = B, H, T, p, dv, chunk, seg, eps
+    pr.in_dtype, pr.out_dtype = in_dt, out_dt
+    pr.sq[:] = (T * H * p, H * p, p)
+    pr.sk[:] = (T * H * p, H * p, p)
+    pr.sv[:] = (T * H * dv, H * dv, dv)
+    pr.so[:] = (T * H * dv, H * dv, dv)
+    pr.sdo[:] = (T * H * dv, H * dv, dv)
+    return pr
+
+
+def _fake(n=1):
+    return [ctypes.c_void_p(FAKE + i * (1 << 30)) for i in range(n)]
+
+
+def _quad(pr, ptrs=None, den=None):
+    q, k, v, o = ptrs or _fake(4)
+    return _lib().kata_fwd_quadratic(ctypes.byref(pr) if pr is not None else None, q, k, v, o,
+                                     den, None)
+
+
+def _chunked(pr, ws_bytes=None, ws=True):
+    lib = _lib()
+    q, k, v, o, w = _fake(5)
+    need = lib.kata_fwd_chunked_workspace_size(ctypes.byref(pr))
+    return lib.kata_fwd_chunked(ctypes.byref(pr), q, k, v, o, None, w if ws else None,
+                                need if ws_bytes is None else ws_bytes, None)
+
+
+def test_header_declares_the_four_operations():
+    names = _declared_functions()
+    for f in ("kata_fwd_quadratic", "kata_fwd_chunked", "kata_chunk_state_scan", "kata_bwd"):
+        assert f in names
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib()
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"declared but not exported: {missing}"
+
+
+def test_status_strings():
+    lib = _lib()
+    for s in range(5):
+        assert lib.kata_status_string(s)
+    assert lib.kata_status_string(99) == b"unknown status"
+
+
+def test_null_problem_is_invalid():
+    assert _quad(None) == INVALID
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("B", 0, INVALID), ("H", 0, INVALID), ("T", 0, INVALID), ("p", 0, INVALID),
+    ("p", 12, UNSUPPORTED), ("p", 64, UNSUPPORTED), ("dv", 32, UNSUPPORTED),
+    ("eps", -1.0, INVALID), ("eps", float("nan"), INVALID), ("eps", float("inf"), INVALID),
+    ("in_dtype", 7, INVALID), ("out_dtype", 7, INVALID),
+])
+def test_bad_problem_fields(field, value, code):
+    pr = _problem()
+    setattr(pr, field, value)
+    assert _quad(pr) == code
+    assert _lib().kata_last_error()
+
+
+def test_fp32_in_bf16_out_is_rejected():
+    assert _quad(_problem(in_dt=0, out_dt=1)) == INVALID
+
+
+def test_null_and_misaligned_pointers():
+    pr = _problem()
+    q, k, v, o = _fake(4)
+    assert _quad(pr, [None, k, v, o]) == INVALID
+    assert _quad(pr, [q, k, v, None]) == INVALID
+    assert _quad(pr, [ctypes.c_void_p(FAKE + 2), k, v, o]) == INVALID
+    assert _quad(pr, [q, k, v, o], den=ctypes.c_void_p(FAKE + 2)) == INVALID
+
+
+def test_bad_strides():
+    pr = _problem()
+    pr.sq[2] = 3                                     # rows overlap
+    assert _quad(pr) == INVALID
+    pr = _problem()
+    pr.sv[1] = pr.sv[1] + 1                          # breaks 16-byte row alignment
+    assert _quad(pr) == INVALID
+    pr = _problem()
+    pr.sk[0] = -1
+    assert _quad(pr) == INVALID
+
+
+def test_chunked_rejects_ragged_T_and_bad_chunk():
+    assert _chunked(_problem(T=100)) == UNSUPPORTED
+    assert _chunked(_problem(chunk=48)) == UNSUPPORTED
+    assert _chunked(_problem(chunk=0)) == INVALID
+    assert _chunked(_problem(seg=-1)) == INVALID
+
+
+def test_chunked_workspace_checks():
+    pr = _problem()
+    need = _lib().kata_fwd_chunked_workspace_size(ctypes.byref(pr))
+    assert need > 0
+    assert _chunked(pr, ws=False) == WORKSPACE
+    assert _chunked(pr, ws_bytes=need - 1) == WORKSPACE
+
+
+def test_workspace_size_of_invalid_problem_is_zero():
+    assert _lib().kata_fwd_chunked_workspace_size(ctypes.byref(_problem(T=100))) == 0
+    assert _lib().kata_bwd_workspace_size(ctypes.byref(_problem(p=5))) == 0
+
+
+@pytest.mark.parametrize("p,dv", [(8, 16), (16, 64), (32, 64)])
+def test_chunked_workspace_holds_the_segment_states(p, dv):
+    # one fp32 state of p^2 (dv + 1) entries per segment; at least one segment per (b, h)
+    pr = _problem(B=2, H=3, T=256, p=p, dv=dv, chunk=32, in_dt=0)
+    need = _lib().kata_fwd_chunked_workspace_size(ctypes.byref(pr))
+    assert need >= 2 * 3 * p * p * (dv + 1) * 4
+
+
+def test_scan_argument_checks():
+    lib = _lib()
+    (s,) = _fake(1)
+    lv = ctypes.c_int32(-1)
+    assert lib.kata_chunk_state_scan(None, 1, 4, 16, 1, None, None, 0, None, None) == INVALID
+    assert lib.kata_chunk_state_scan(s, 0, 4, 16, 1, None, None, 0, None, None) == INVALID
+    assert lib.kata_chunk_state_scan(s, 1, 4, 18, 1, None, None, 0, None, None) == INVALID
+    assert lib.kata_chunk_state_scan(ctypes.c_void_p(FAKE + 4), 1, 4, 16, 1, None, None, 0,
+                                     None, None) == INVALID
+    # hierarchical sizes need a workspace
+    need = lib.kata_chunk_state_scan_workspace_size(2, 10000, 64)
+    assert need > 0
+    assert lib.kata_chunk_state_scan(s, 2, 10000, 64, 1, None, None, 0, ctypes.byref(lv),
+                                     None) == WORKSPACE
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 8, 64, 100, 2048, 4096])
+def test_scan_reports_log_depth(n):
+    # a single Kogge-Stone tree: ceil(log2 n) levels (2048 chunk states -> 11)
+    lib = _lib()
+    assert lib.kata_chunk_state_scan_workspace_size(4, n, 16640) == 0
+    lv = ctypes.c_int32(-1)
+    st = lib.kata_chunk_state_scan(_fake(1)[0], 4, n, 16640, 1, None, None, 0,
+                                   ctypes.byref(lv), None)
+    assert lv.value == math.ceil(math.log2(n)) if n > 1 else lv.value == 0
+    assert st in (OK, DEVICE)
+
+
+def test_backward_argument_checks():
+    lib = _lib()
+    pr = _problem()
+    ptrs = _fake(8)
+    need = lib.kata_bwd_workspace_size(ctypes.byref(pr))
+    assert need >= 2 * 2 * 128 * 4
+    args = [ctypes.byref(pr)] + ptrs[:7] + [ptrs[7], need, None]
+    bad = list(args)
+    bad[4] = None                                     # dO
+    assert lib.kata_bwd(*bad) == INVALID
+    bad = list(args)
+    bad[9] = need - 1
+    assert lib.kata_bwd(*bad) == WORKSPACE
+
+
+def test_valid_call_without_a_gpu_reports_device_error():
+    # This container has no GPU: a fully valid call gets past validation and fails cleanly
+    # at the device check instead of crashing.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _quad(_problem()) == DEVICE
+    assert _lib().kata_last_error()
+
+
+def test_timing_end_without_begin_is_invalid():
+    t = K._Times()
+    assert _lib().kata_timing_end(ctypes.byref(t)) == INVALID

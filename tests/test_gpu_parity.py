@@ -1,0 +1,376 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 CPU oracle on the same
+seeded inputs.  Tolerances: max-abs 1e-2 for bf16 inputs, 1e-4 for fp32 inputs (outputs in
+fp32).  Small sizes are compared element by element; full workload sizes on sampled rows
+(every row of the first and last chunk of sampled heads plus random rows)."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kata_workloads as W
+import kernelized_psd_feature_amd as K
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+
+
+def _np(x):
+    return x.to(torch.float64).cpu().numpy()
+
+
+def _to_gpu(*xs):
+    return [x.to(DEV) for x in xs]
+
+
+def _run(form, q, k, v, chunk=64, **kw):
+    if form == "quadratic":
+        return K.fwd_quadratic(q, k, v, **kw)
+    return K.fwd_chunked(q, k, v, chunk=chunk, **kw)
+
+
+def _check_rows(qc, kc, vc, o_gpu, heads, rows_fn, tol, eps=1e-6, tag=""):
+    """Compare o_gpu (CPU float tensor, (B,T,H,dv)) with the oracle on rows_fn(T) rows of
+    each sampled (b, h)."""
+    worst = 0.0
+    for b, h in heads:
+        Q, Kk, V = _np(qc[b, :, h]), _np(kc[b, :, h]), _np(vc[b, :, h])
+        rows = rows_fn(Q.shape[0])
+        ref, _ = O.closed_form_rows(Q, Kk, V, rows, eps)
+        got = o_gpu[b, rows, h].double().numpy()
+        err = float(np.abs(got - ref).max())
+        worst = max(worst, err)
+    say(f"{tag}: max-abs {worst:.3e} (tol {tol})")
+    assert worst <= tol
+
+
+def _rows_sampler(rng, n_random, C=64):
+    def f(T):
+        edge = np.concatenate([np.arange(min(C, T)), np.arange(max(0, T - C), T)])
+        rnd = rng.choice(T, size=min(n_random, T), replace=False)
+        return np.unique(np.concatenate([edge, rnd]))
+    return f
+
+
+# ------------------------------------------------------------ workload 1: tiny fp32 ----
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("form", ["quadratic", "chunked"])
+def test_tiny_fp32_against_oracle(seed, form):
+    w = W.WORKLOADS[1]
+    q, k, v = W.make_inputs(w, seed)
+    ref, dref = O.closed_form(_np(q), _np(k), _np(v))
+    o, d = _run(form, *_to_gpu(q, k, v), chunk=w.chunk, return_den=True)
+    err = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
+    say(f"tiny fp32 {form} seed {seed}: max-abs {err:.3e}")
+    assert err <= TOL[torch.float32]
+    np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=2e-5)
+
+
+# ------------------------------------------------------------ workload 2: 340M layer ---
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("form", ["quadratic", "chunked"])
+def test_layer340m_full_size(seed, form):
+    w = W.WORKLOADS[2]
+    q, k, v = W.make_inputs(w, seed)
+    o = _run(form, *_to_gpu(q, k, v), chunk=w.chunk).cpu()
+    rng = np.random.default_rng(100 + seed)
+    heads = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(3)]
+    # three whole heads, element by element
+    _check_rows(q, k, v, o, heads, lambda T: np.arange(T), TOL[w.dtype],
+                tag=f"layer340m {form} seed {seed} whole heads")
+    # sampled rows of every head
+    all_heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    _check_rows(q, k, v, o, all_heads, _rows_sampler(rng, 8), TOL[w.dtype],
+                tag=f"layer340m {form} seed {seed} all heads")
+
+
+@pytest.mark.parametrize("T", [64, 300, 448])
+def test_layer340m_recipe_small_T_every_element(T):
+    # ragged tail for the quadratic form (T = 300), one chunk (T = 64), several segments
+    w = W.WORKLOADS[2]
+    q, k, v = W.make_inputs(w, 7, T=T, B=2, H=3)
+    ref, dref = O.closed_form(_np(q), _np(k), _np(v))
+    qg, kg, vg = _to_gpu(q, k, v)
+    forms = ["quadratic"] + (["chunked"] if T % 64 == 0 else [])
+    for form in forms:
+        o, d = _run(form, qg, kg, vg, return_den=True)
+        err = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
+        say(f"T={T} {form}: max-abs {err:.3e}")
+        assert err <= TOL[w.dtype]
+        np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=1e-2)
+
+
+# ------------------------------------------------------------ workload 3: p = 32 -------
+
+@pytest.mark.parametrize("T", [1024, 4096, 8192, 16384])
+@pytest.mark.parametrize("form", ["quadratic", "chunked"])
+def test_crossover_p32_sampled(T, form):
+    w = W.WORKLOADS[3]
+    q, k, v = W.make_inputs(w, 0, T=T)
+    o = _run(form, *_to_gpu(q, k, v), chunk=w.chunk).cpu()
+    rng = np.random.default_rng(T)
+    heads = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(3)]
+    _check_rows(q, k, v, o, heads, _rows_sampler(rng, 128), TOL[w.dtype],
+                tag=f"p32 T={T} {form}")
+
+
+# ------------------------------------------------------------ workload 4: 131k tokens --
+
+@pytest.mark.parametrize("form", ["chunked", "quadratic"])
+def test_long_context_sampled(form):
+    w = W.WORKLOADS[4]
+    q, k, v = W.make_inputs(w, 0)
+    qg, kg, vg = _to_gpu(q, k, v)
+    o = _run(form, qg, kg, vg, chunk=w.chunk)
+    torch.cuda.synchronize()
+    o = o.cpu()
+    assert torch.isfinite(o).all()
+    rng = np.random.default_rng(4)
+    heads = [(0, 0), (0, int(rng.integers(1, w.H)))]
+    _check_rows(q, k, v, o, heads, _rows_sampler(rng, 192), TOL[w.dtype],
+                tag=f"long context {form}")
+
+
+# ------------------------------------------------------------ workload 5: backward -----
+
+def test_training_slice_forward_and_backward():
+    # a fresh forward + backward on the first 256 tokens of the workload's tensors
+    w = W.WORKLOADS[5]
+    q, k, v, dO = W.make_inputs(w, 0, T=256, with_dO=True)
+    qn, kn, vn, gn = _np(q), _np(k), _np(v), _np(dO)
+    ref, _ = O.closed_form(qn, kn, vn)
+    dq_r, dk_r, dv_r = O.backward(qn, kn, vn, gn)
+    qg, kg, vg, gg = _to_gpu(q, k, v, dO)
+    o = K.fwd_chunked(qg, kg, vg, chunk=64)
+    dq, dk, dv = K.bwd(qg, kg, vg, gg)
+    err_o = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
+    errs = [float((g.cpu().double() - torch.from_numpy(r)).abs().max())
+            for g, r in ((dq, dq_r), (dk, dk_r), (dv, dv_r))]
+    scale = [float(np.abs(r).max()) for r in (dq_r, dk_r, dv_r)]
+    say(f"training slice: o {err_o:.3e}; dq/dk/dv max-abs {errs}, ref max |g| {scale}")
+    assert err_o <= TOL[w.dtype]
+    assert max(errs) <= 1e-2
+
+
+def test_training_full_T_backward_sampled_heads():
+    w = W.WORKLOADS[5]
+    q, k, v, dO = W.make_inputs(w, 1, with_dO=True)
+    qg, kg, vg, gg = _to_gpu(q, k, v, dO)
+    dq, dk, dv = K.bwd(qg, kg, vg, gg)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for b, h in [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(2)]:
+        sl = lambda x: _np(x[b:b + 1, :, h:h + 1])
+        refs = O.backward(sl(q), sl(k), sl(v), sl(dO))
+        for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+            err = float(np.abs(g[b:b + 1, :, h:h + 1].cpu().double().numpy() - r).max())
+            say(f"full-T backward head ({b},{h}) {name}: max-abs {err:.3e} (ref max {np.abs(r).max():.3e})")
+            assert err <= 1e-2
+
+
+def test_backward_matches_finite_differences_tiny_fp32():
+    rng = np.random.default_rng(21)
+    B, T, H, p, dv = 1, 16, 2, 8, 16
+    q = rng.standard_normal((B, T, H, p))
+    k = rng.standard_normal((B, T, H, p))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, dv))
+    dO = rng.standard_normal((B, T, H, dv))
+    eps = 1e-2
+    tq, tk, tv, tg = (torch.tensor(x, dtype=torch.float32) for x in (q, k, v, dO))
+    # the oracle sees the fp32-rounded inputs
+    q, k, v, dO = (x.double().numpy() for x in (tq, tk, tv, tg))
+    dq, dk, dv_ = K.bwd(*_to_gpu(tq, tk, tv, tg), eps=eps)
+
+    def loss(qq, kk, vv):
+        o, _ = O.closed_form(qq, kk, vv, eps)
+        return float((o * dO).sum())
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv_)):
+        g = g.cpu().double().numpy()
+        num = np.empty_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (loss(args_p["q"], args_p["k"], args_p["v"])
+                        - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+        scale = max(1.0, float(np.abs(num).max()))
+        err = float(np.abs(g - num).max())
+        say(f"finite differences d{name}: max-abs {err:.3e} (scale {scale:.2f})")
+        assert err <= 1e-4 * scale
+
+
+# ------------------------------------------------------------ prefix scan --------------
+
+@pytest.mark.parametrize("n", [1, 2, 7, 64, 2048, 5000])
+@pytest.mark.parametrize("exclusive", [True, False])
+def test_scan_matches_oracle(n, exclusive):
+    E = 16640 if n <= 64 else 1024
+    g = torch.Generator().manual_seed(n)
+    x = torch.randn((3, n, E), generator=g, dtype=torch.float32)
+    ref_ex, ref_tot = O.exclusive_scan(x.double().numpy(), axis=1)
+    ref = ref_ex if exclusive else ref_ex + x.double().numpy()
+    xg = x.to(DEV)
+    levels, tot = K.chunk_state_scan(xg, exclusive=exclusive, want_totals=True)
+    err = float(np.abs(xg.cpu().double().numpy() - ref).max())
+    err_t = float(np.abs(tot.cpu().double().numpy() - ref_tot).max())
+    bound = 1e-5 * max(1.0, math.sqrt(n)) * 8
+    say(f"scan n={n} exclusive={exclusive}: levels {levels}, max-abs {err:.2e}, totals {err_t:.2e}")
+    assert err <= bound and err_t <= bound
+    if n <= 4096:
+        assert levels == (math.ceil(math.log2(n)) if n > 1 else 0)
+
+
+# ------------------------------------------------------------ special cases ------------
+
+@pytest.mark.parametrize("form", ["quadratic", "chunked"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_special_cases(form, dtype):
+    T, p, dv = 128, 16, 64
+    g = torch.Generator().manual_seed(3)
+    v = torch.randn((1, T, 1, dv), generator=g).to(dtype)
+    e1 = torch.zeros((1, T, 1, p), dtype=dtype)
+    e1[..., 0] = 1
+    # identical unit keys: causal running mean
+    o = _run(form, *_to_gpu(e1, e1, v)).cpu().double()
+    want = torch.cumsum(v.double(), dim=1) / (torch.arange(T, dtype=torch.float64) + 1 + 1e-6)[None, :, None, None]
+    assert float((o - want).abs().max()) <= TOL[dtype]
+    # q = 0: o = 0 exactly
+    o = _run(form, *_to_gpu(torch.zeros_like(e1), e1, v)).cpu()
+    assert torch.all(o == 0)
+    # orthonormal keys, each query equal to an earlier key: exact retrieval v_j / (1 + eps)
+    Tn = 16
+    basis = torch.eye(p, dtype=dtype)[torch.randperm(p, generator=g)]
+    kk = basis[:Tn][None, :, None, :].contiguous()
+    j = torch.tensor([int(torch.randint(0, t + 1, (1,), generator=g)) for t in range(Tn)])
+    qq = kk[:, j].contiguous()
+    vv = v[:, :Tn].contiguous()
+    o = _run(form, *_to_gpu(qq, kk, vv), chunk=16).cpu().double()
+    want = vv[:, j].double() / (1 + 1e-6)
+    assert float((o - want).abs().max()) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("form", ["quadratic", "chunked"])
+def test_future_tokens_do_not_change_earlier_outputs_bitwise(form):
+    w = W.WORKLOADS[2]
+    q, k, v = _to_gpu(*W.make_inputs(w, 2, T=1024, B=1, H=4))
+    o1 = _run(form, q, k, v)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, 517:] = torch.randn_like(k2[:, 517:].float()).to(k2.dtype)
+    v2[:, 517:] = 7.0
+    o2 = _run(form, q, k2, v2)
+    assert torch.equal(o1[:, :517], o2[:, :517])
+    assert not torch.equal(o1[:, 517:], o2[:, 517:])
+
+
+@pytest.mark.parametrize("form", ["quadratic", "chunked"])
+def test_non_finite_future_chunks_do_not_leak(form):
+    # a non-finite value in a later 64-token chunk never reaches earlier chunks' outputs
+    w = W.WORKLOADS[2]
+    q, k, v = _to_gpu(*W.make_inputs(w, 3, T=512, B=1, H=2))
+    o1 = _run(form, q, k, v)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, 320:] = float("nan")
+    v2[:, 320:] = float("inf")
+    o2 = _run(form, q, k2, v2)
+    assert torch.equal(o1[:, :320], o2[:, :320])
+
+
+def test_non_finite_future_tokens_do_not_leak_fp32_path():
+    # the fp32 path masks every (t, s > t) pair by selection, token by token
+    w = W.WORKLOADS[1]
+    q, k, v = _to_gpu(*W.make_inputs(w, 4))
+    for form in ("quadratic", "chunked"):
+        o1 = _run(form, q, k, v, chunk=32)
+        k2, v2 = k.clone(), v.clone()
+        k2[:, 77:] = float("nan")
+        v2[:, 77:] = float("inf")
+        o2 = _run(form, q, k2, v2, chunk=32)
+        assert torch.equal(o1[:, :77], o2[:, :77]), form
+
+
+@pytest.mark.parametrize("form", ["quadratic", "chunked"])
+def test_deterministic_and_layout_independent(form):
+    w = W.WORKLOADS[2]
+    q, k, v = _to_gpu(*W.make_inputs(w, 5, T=1024, B=2, H=4))
+    o1 = _run(form, q, k, v)
+    o2 = _run(form, q, k, v)
+    assert torch.equal(o1, o2)
+    # head-major storage, passed as a (B, T, H, D) view
+    qh, kh, vh = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
+    o3 = _run(form, qh, kh, vh)
+    assert torch.equal(o1, o3)
+
+
+@pytest.mark.parametrize("form", ["quadratic", "chunked"])
+def test_bf16_output_is_the_rounded_fp32_output(form):
+    w = W.WORKLOADS[2]
+    q, k, v = _to_gpu(*W.make_inputs(w, 6, T=512, B=1, H=4))
+    o32 = _run(form, q, k, v)
+    o16 = _run(form, q, k, v, out_dtype=torch.bfloat16)
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
+def test_chunked_and_quadratic_agree_on_gpu():
+    w = W.WORKLOADS[2]
+    q, k, v = _to_gpu(*W.make_inputs(w, 8, T=2048, B=2, H=4))
+    a = _run("quadratic", q, k, v)
+    b = _run("chunked", q, k, v)
+    assert float((a - b).abs().max()) <= 2e-2
+
+
+@pytest.mark.parametrize("seg", [1, 2, 3, 32])
+def test_segment_length_does_not_change_the_result(seg):
+    w = W.WORKLOADS[2]
+    q, k, v = W.make_inputs(w, 9, T=2048, B=1, H=2)
+    ref, _ = O.closed_form(_np(q), _np(k), _np(v))
+    o = K.fwd_chunked(*_to_gpu(q, k, v), chunk=64, seg_chunks=seg).cpu().double()
+    err = float((o - torch.from_numpy(ref)).abs().max())
+    say(f"seg_chunks={seg}: max-abs {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
+def test_timing_records_every_kernel():
+    w = W.WORKLOADS[2]
+    q, k, v = _to_gpu(*W.make_inputs(w, 0, T=1024, B=1, H=4))
+    K.timing_begin()
+    K.fwd_chunked(q, k, v)
+    K.fwd_quadratic(q, k, v)
+    t = K.timing_end()
+    assert t["chunk_state"][0] == 1 and t["scan"][0] == 1 and t["chunk_output"][0] == 1
+    assert t["quadratic"][0] == 1
+    assert all(ms > 0 for n, ms in t.values() if n)
+
+
+def test_single_runtime_is_loaded():
+    # the library must resolve the HIP runtime torch already loaded, not a second copy
+    K._lib()
+    maps = open("/proc/self/maps").read()
+    paths = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    say(f"libamdhip64 mapped from: {sorted(paths)}")
+    assert len({p for p in paths}) == 1
