@@ -235,7 +235,6 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_fast_kernel(
 // ==========================================================================================
 struct __align__(16) WalkLds {
   Tiles tl;
-  float Zs[2][P][P];             // Z_{<c} in fp32, double-buffered across chunks
   f32x4 red[4][3][4][64];        // readout shares for other waves' tokens
   float den[C];
 };
@@ -260,12 +259,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
       S[mt][nt] = *reinterpret_cast<const f32x4*>(pre + ((w * 16 + mt * 4 + nt) * 64 + lane) * 4);
-  f32x4 Z = zero4();
-  if (w == 0) {
-    Z = *reinterpret_cast<const f32x4*>(pre + F * DV + lane * 4);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sm.Zs[0][4 * g + r][l16] = Z[r];
-  }
+  // every wave keeps its own copy of Z_{<c} (4 registers); lane holds Z[4g + r][lane % 16]
+  f32x4 Z = *reinterpret_cast<const f32x4*>(pre + F * DV + lane * 4);
 
   Stage st;
   stage_load(st, pr, q, k, v, b, h, c0 * C, true, tid);
@@ -274,51 +269,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
 
   for (int c = 0; c < nc; ++c) {
     const int tok0 = (c0 + c) * C;
-    const int zb = c & 1;
     if (c + 1 < nc) stage_load(st, pr, q, k, v, b, h, tok0 + C, true, tid);
-
-    // ---- readout of the prefix: shares of rows [64w, 64w+64) for all four token tiles ----
-    f32x4 O[4][4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) O[tt][nt] = zero4();
-    {
-      bf16x8 sb[2][4];   // S as B operand: K step m' covers state tiles 2m', 2m'+1
-#pragma unroll
-      for (int mp = 0; mp < 2; ++mp)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            sb[mp][nt][r] = (__bf16)S[2 * mp][nt][r];
-            sb[mp][nt][4 + r] = (__bf16)S[2 * mp + 1][nt][r];
-          }
-        }
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int t = 16 * tt + l16;
-        const uint2 qi = *reinterpret_cast<const uint2*>(&tl.Qs[t][4 * w]);   // q_t[4w..4w+3]
-        const uint2 qj = *reinterpret_cast<const uint2*>(&tl.Qs[t][4 * g]);   // q_t[4g..4g+3]
-        const float qiv[4] = {bf_lo(qi.x), bf_hi(qi.x), bf_lo(qi.y), bf_hi(qi.y)};
-        const float qjv[4] = {bf_lo(qj.x), bf_hi(qj.x), bf_lo(qj.y), bf_hi(qj.y)};
-#pragma unroll
-        for (int mp = 0; mp < 2; ++mp) {
-          // slot r' -> feature (i, j) = (4w + 2mp + r'/4, 4g + r'%4)
-          bf16x8 a;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            a[r] = (__bf16)(qiv[2 * mp] * qjv[r]);
-            a[4 + r] = (__bf16)(qiv[2 * mp + 1] * qjv[r]);
-          }
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) O[tt][nt] = mfma32(a, sb[mp][nt], O[tt][nt]);
-        }
-      }
-    }
 
     // ---- intra-chunk tile of this wave's tokens t in [16w, 16w+16) ----
     float lsum = 0.f;
+    f32x4 Oown[4] = {zero4(), zero4(), zero4(), zero4()};
     {
       const s16x4 qf = row4_frag(tl.Qs, 16 * w, lane);
       const int t = 16 * w + l16;
@@ -341,38 +296,85 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
 #pragma unroll
         for (int r = 0; r < 8; ++r) a[r] = pa[r];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) O[w][nt] = mfma32(a, v_frag(tl, m, nt, lane), O[w][nt]);
+        for (int nt = 0; nt < 4; ++nt) Oown[nt] = mfma32(a, v_frag(tl, m, nt, lane), Oown[nt]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- inter-chunk denominator q^T Z_{<c} q (fp32) for this wave's tokens ----
+    // ---- inter-chunk denominator q^T Z_{<c} q for this wave's tokens ----
+    // Y = Z q_t on MFMA with Z split into bf16 hi + lo (fp32-accurate; q is exact in bf16):
+    // Z's accumulator layout (lane: column lane%16, rows 4g + r) is, Z being symmetric, the
+    // A layout of a 16 x 16 x 16 product; q_t[4g..4g+3] is the same B operand as the scores.
     float zq = 0.f;
     {
-      const int t = 16 * w + l16;
-      const uint4 q0 = *reinterpret_cast<const uint4*>(&tl.Qs[t][0]);
-      const uint4 q1 = *reinterpret_cast<const uint4*>(&tl.Qs[t][8]);
-      const float qf[16] = {bf_lo(q0.x), bf_hi(q0.x), bf_lo(q0.y), bf_hi(q0.y),
-                            bf_lo(q0.z), bf_hi(q0.z), bf_lo(q0.w), bf_hi(q0.w),
-                            bf_lo(q1.x), bf_hi(q1.x), bf_lo(q1.y), bf_hi(q1.y),
-                            bf_lo(q1.z), bf_hi(q1.z), bf_lo(q1.w), bf_hi(q1.w)};
+      const s16x4 qf = row4_frag(tl.Qs, 16 * w, lane);
+      s16x4 zhi, zlo;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 4 * g + r;
-        float y = 0.f;
+        const __bf16 hi = (__bf16)Z[r];
+        zhi[r] = __builtin_bit_cast(short, hi);
+        zlo[r] = __builtin_bit_cast(short, (__bf16)(Z[r] - (float)hi));
+      }
+      f32x4 y = mfma16(zhi, qf, zero4());
+      y = mfma16(zlo, qf, y);                   // y[r] = (Z q_t)[4g + r], t = 16w + lane%16
+      const uint2 qq = __builtin_bit_cast(uint2, qf);
+      zq = fmaf(bf_lo(qq.x), y[0], zq);
+      zq = fmaf(bf_hi(qq.x), y[1], zq);
+      zq = fmaf(bf_lo(qq.y), y[2], zq);
+      zq = fmaf(bf_hi(qq.y), y[3], zq);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- readout of the prefix with rows [64w, 64w+64) of the state, one token tile at a
+    // time; shares of other waves' tokens go to LDS, this wave's own share is kept.
+    // (tt is a compile-time index after unrolling and w is uniform per wave, so no register
+    // array is ever indexed at run time.)
+    {
+      bf16x8 sb[2][4];   // S as B operand: K step m' covers state tiles 2m', 2m'+1
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          const float4 z = *reinterpret_cast<const float4*>(&sm.Zs[zb][i][4 * j4]);
-          y = fmaf(z.x, qf[4 * j4], y);
-          y = fmaf(z.y, qf[4 * j4 + 1], y);
-          y = fmaf(z.z, qf[4 * j4 + 2], y);
-          y = fmaf(z.w, qf[4 * j4 + 3], y);
+      for (int mp = 0; mp < 2; ++mp)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sb[mp][nt][r] = (__bf16)S[2 * mp][nt][r];
+            sb[mp][nt][4 + r] = (__bf16)S[2 * mp + 1][nt][r];
+          }
         }
-        zq = fmaf(qf[i], y, zq);
+#pragma unroll 1
+      for (int tt = 0; tt < 4; ++tt) {
+        const int t = 16 * tt + l16;
+        const uint2 qi = *reinterpret_cast<const uint2*>(&tl.Qs[t][4 * w]);   // q_t[4w..4w+3]
+        const uint2 qj = *reinterpret_cast<const uint2*>(&tl.Qs[t][4 * g]);   // q_t[4g..4g+3]
+        const float qiv[4] = {bf_lo(qi.x), bf_hi(qi.x), bf_lo(qi.y), bf_hi(qi.y)};
+        const float qjv[4] = {bf_lo(qj.x), bf_hi(qj.x), bf_lo(qj.y), bf_hi(qj.y)};
+        f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+        for (int mp = 0; mp < 2; ++mp) {
+          // slot r' -> feature (i, j) = (4w + 2mp + r'/4, 4g + r'%4)
+          bf16x8 a;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            a[r] = (__bf16)(qiv[2 * mp] * qjv[r]);
+            a[4 + r] = (__bf16)(qiv[2 * mp + 1] * qjv[r]);
+          }
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) O[nt] = mfma32(a, sb[mp][nt], O[nt]);
+        }
+        if (tt == w) {
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) Oown[nt] += O[nt];
+        } else {
+          const int slot = w < tt ? w : w - 1;
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) sm.red[tt][slot][nt][lane] = O[nt];
+        }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- state update with this chunk: S += Phi(K)^T V, Z += K^T K ----
-#pragma unroll
+#pragma unroll 1
     for (int m = 0; m < 2; ++m) {
       bf16x8 vb[4];
 #pragma unroll
@@ -383,24 +385,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) S[mt][nt] = mfma32(a, vb[nt], S[mt][nt]);
       }
-      if (w == 0) {
-        const bf16x8 kf = kcol_frag(tl, m, lane);
-        Z = mfma32(kf, kf, Z);
-      }
+      const bf16x8 kf = kcol_frag(tl, m, lane);
+      Z = mfma32(kf, kf, Z);
     }
-    if (w == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.Zs[zb ^ 1][4 * g + r][l16] = Z[r];
-    }
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- hand the other waves their readout shares; finish the denominators ----
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      if (tt == w) continue;
-      const int slot = w < tt ? w : w - 1;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) sm.red[tt][slot][nt][lane] = O[tt][nt];
-    }
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
     zq += __shfl_xor(zq, 16);
@@ -411,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
     f32x4 acc[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      acc[nt] = O[w][nt];
+      acc[nt] = Oown[nt];
 #pragma unroll
       for (int s2 = 0; s2 < 3; ++s2) acc[nt] += sm.red[w][s2][nt][lane];
     }
