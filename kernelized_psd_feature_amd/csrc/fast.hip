@@ -34,13 +34,16 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int P = 16, DV = 64, C = 64, F = P * P;
 constexpr int kThreads = 256;
 constexpr int kStateFloats = F * (DV + 1);     // 16640: S (4 waves x 16 tiles x 256) + Z (256)
-constexpr int QROW = 24;                       // bf16 per row of the Q / K tiles (16 + pad)
-constexpr int KTROW = 68;                      // fp32 per row of the K^T tile (64 + pad)
-constexpr int VTROW = 72;                      // bf16 per row of the V^T tile (64 + pad)
+// LDS row strides, chosen so that every access pattern below is free of bank conflicts
+// (32 banks of 4 bytes; 4-, 8- and 16-byte accesses served 32, 16 and 8 lanes at a time):
+constexpr int QROW = 20;                       // bf16 per q / k row: 40 B, 8-byte aligned
+constexpr int KTROW = 68;                      // fp32 per row of the K^T tile
+constexpr int VROW = 80;                       // bf16 per v row: 160 B, 16-byte aligned
 
 __device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -58,12 +61,12 @@ struct __align__(16) Tiles {
   __bf16 Qs[C][QROW];     // q rows (bf16), row-major
   __bf16 Ks[C][QROW];     // k rows (bf16), row-major
   float KT[P][KTROW];     // k transposed, fp32 (exact copies of the bf16 inputs)
-  __bf16 VT[DV][VTROW];   // v transposed, bf16
+  __bf16 V[C][VROW];      // v rows (bf16), row-major
 };
 
 // One thread's share of a chunk's global loads, held in registers while the previous chunk
-// is computed.  Threads 0..127 carry half a q row, 128..255 half a k row; every thread
-// carries 16 bytes of two consecutive v rows.
+// is computed.  Waves 0-1 carry half a q row each (token = lane, half = wave), waves 2-3 half
+// a k row; every thread carries 16 bytes of two consecutive v rows.
 struct Stage {
   uint4 qk;
   uint4 v0, v1;
@@ -71,52 +74,74 @@ struct Stage {
 
 __device__ __forceinline__ uint4 ld16(const __bf16* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__device__ __forceinline__ void stage_load(Stage& st, const DevProblem& pr, const __bf16* q,
-                                           const __bf16* k, const __bf16* v, int b, int h,
-                                           int tok0, bool with_q, int tid) {
-  const int half = tid & 1;
-  if (tid < 128) {
-    if (with_q) st.qk = ld16(q + row_off(pr.sq, b, tok0 + (tid >> 1), h) + 8 * half);
-  } else {
-    st.qk = ld16(k + row_off(pr.sk, b, tok0 + ((tid - 128) >> 1), h) + 8 * half);
+// Per-thread global addresses of the staged pieces; advanced by one chunk with `next`.
+struct StagePtrs {
+  const __bf16* qk;     // q (waves 0-1) or k (waves 2-3) piece, or nullptr
+  const __bf16* v0;     // v row 2a, 16 bytes at column 8 c8
+  long long qk_step, v_step;
+  __device__ __forceinline__ void next() {
+    if (qk) qk += qk_step;
+    v0 += v_step;
   }
+};
+
+__device__ __forceinline__ StagePtrs stage_ptrs(const DevProblem& pr, const __bf16* q,
+                                                const __bf16* k, const __bf16* v, int b, int h,
+                                                int tok0, bool with_q, int tid) {
+  StagePtrs sp;
+  const int w = tid >> 6, lane = tid & 63;
+  if (w < 2)
+    sp.qk = with_q ? q + row_off(pr.sq, b, tok0 + lane, h) + 8 * w : nullptr;
+  else
+    sp.qk = k + row_off(pr.sk, b, tok0 + lane, h) + 8 * (w - 2);
+  sp.qk_step = (long long)C * (w < 2 ? pr.sq[1] : pr.sk[1]);
   const int a = tid >> 3, c8 = tid & 7;
-  st.v0 = ld16(v + row_off(pr.sv, b, tok0 + 2 * a, h) + 8 * c8);
-  st.v1 = ld16(v + row_off(pr.sv, b, tok0 + 2 * a + 1, h) + 8 * c8);
+  sp.v0 = v + row_off(pr.sv, b, tok0 + 2 * a, h) + 8 * c8;
+  sp.v_step = (long long)C * pr.sv[1];
+  return sp;
+}
+
+__device__ __forceinline__ void stage_load(Stage& st, const StagePtrs& sp, long long sv_t) {
+  if (sp.qk) st.qk = ld16(sp.qk);
+  st.v0 = ld16(sp.v0);
+  st.v1 = ld16(sp.v0 + sv_t);
 }
 
 __device__ __forceinline__ void stage_store(const Stage& st, Tiles& tl, bool with_q, int tid) {
-  const int half = tid & 1;
-  if (tid < 128) {
-    if (with_q) *reinterpret_cast<uint4*>(&tl.Qs[tid >> 1][8 * half]) = st.qk;
+  const int w = tid >> 6, lane = tid & 63;
+  if (w < 2) {
+    if (with_q) {
+      *reinterpret_cast<uint2*>(&tl.Qs[lane][8 * w]) = uint2{st.qk.x, st.qk.y};
+      *reinterpret_cast<uint2*>(&tl.Qs[lane][8 * w + 4]) = uint2{st.qk.z, st.qk.w};
+    }
   } else {
-    const int s = (tid - 128) >> 1;
-    *reinterpret_cast<uint4*>(&tl.Ks[s][8 * half]) = st.qk;
-    const uint32_t w[4] = {st.qk.x, st.qk.y, st.qk.z, st.qk.w};
+    const int half = w - 2;
+    *reinterpret_cast<uint2*>(&tl.Ks[lane][8 * half]) = uint2{st.qk.x, st.qk.y};
+    *reinterpret_cast<uint2*>(&tl.Ks[lane][8 * half + 4]) = uint2{st.qk.z, st.qk.w};
+    const uint32_t wd[4] = {st.qk.x, st.qk.y, st.qk.z, st.qk.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      tl.KT[8 * half + 2 * e][s] = bf_lo(w[e]);
-      tl.KT[8 * half + 2 * e + 1][s] = bf_hi(w[e]);
+      tl.KT[8 * half + 2 * e][lane] = bf_lo(wd[e]);
+      tl.KT[8 * half + 2 * e + 1][lane] = bf_hi(wd[e]);
     }
   }
   const int a = tid >> 3, c8 = tid & 7;
-  const uint32_t w0[4] = {st.v0.x, st.v0.y, st.v0.z, st.v0.w};
-  const uint32_t w1[4] = {st.v1.x, st.v1.y, st.v1.z, st.v1.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    // column d = 8*c8 + 2e (low halves) and d + 1 (high halves); rows 2a, 2a+1 as one dword
-    *reinterpret_cast<uint32_t*>(&tl.VT[8 * c8 + 2 * e][2 * a]) = (w0[e] & 0xffffu) | (w1[e] << 16);
-    *reinterpret_cast<uint32_t*>(&tl.VT[8 * c8 + 2 * e + 1][2 * a]) = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
-  }
+  *reinterpret_cast<uint4*>(&tl.V[2 * a][8 * c8]) = st.v0;
+  *reinterpret_cast<uint4*>(&tl.V[2 * a + 1][8 * c8]) = st.v1;
 }
 
-// B operand of a 32-key step m for value columns [16 nt, 16 nt + 16), slot order kappa.
-__device__ __forceinline__ bf16x8 v_frag(const Tiles& tl, int m, int nt, int lane) {
-  const int d = 16 * nt + (lane & 15), g = lane >> 4;
-  const uint2 lo = *reinterpret_cast<const uint2*>(&tl.VT[d][32 * m + 4 * g]);
-  const uint2 hi = *reinterpret_cast<const uint2*>(&tl.VT[d][32 * m + 16 + 4 * g]);
-  uint4 u = {lo.x, lo.y, hi.x, hi.y};
-  return __builtin_bit_cast(bf16x8, u);
+// B operand of a 32-key step m for value columns [16 nt, 16 nt + 16), slot order kappa, read
+// from the row-major V tile with two LDS transpose loads.  Within a 16-lane block, lane i's
+// slot r of ds_read_b64_tr_b16 is element (i % 4) of the 8 bytes addressed by block lane
+// 4r + i/4; block lane j therefore points at V[key(g, j/4)][16 nt + 4 (j % 4)], which hands
+// lane i the value V[key(g, r)][16 nt + i].
+__device__ __forceinline__ bf16x8 v_frag(const __bf16 (*V)[VROW], int m, int nt, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int row = 32 * m + 4 * g + (j >> 2), col = 16 * nt + 4 * (j & 3);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&V[row][col]));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&V[row + 16][col]));
+  const uint2 ul = __builtin_bit_cast(uint2, lo), uh = __builtin_bit_cast(uint2, hi);
+  return __builtin_bit_cast(bf16x8, uint4{ul.x, ul.y, uh.x, uh.y});
 }
 
 // A operand of the state update for feature rows f = 16 i + (lane%16), i fixed, 32-key step
@@ -154,14 +179,15 @@ __device__ __forceinline__ s16x4 row4_frag(const __bf16 (*X)[QROW], int row0, in
 
 // Squared, causally masked score tile -> bf16 P slots and their fp32 row-sum share.
 // sc holds S^T[s][t] for keys s = s0 + 4g + r and query t = t0 + lane%16.
+template <bool kMask>
 __device__ __forceinline__ void square_mask(const f32x4& sc, int s0, int t, int lane,
                                             __bf16 out[4], float& lsum) {
   const int g = lane >> 4;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int s = s0 + 4 * g + r;
     const float x = sc[r];
-    const __bf16 pb = (s <= t) ? (__bf16)(x * x) : (__bf16)0.f;   // select, never multiply
+    __bf16 pb = (__bf16)(x * x);
+    if (kMask) pb = (s0 + 4 * g + r <= t) ? pb : (__bf16)0.f;   // select, never multiply
     out[r] = pb;
     lsum += (float)pb;
   }
@@ -182,6 +208,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_fast_kernel(
   const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n_chunks = pr.T / C;
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
+  const long long sv_t = pr.sv[1];
 
   f32x4 S[4][4];
 #pragma unroll
@@ -190,17 +217,21 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_fast_kernel(
     for (int nt = 0; nt < 4; ++nt) S[mt][nt] = zero4();
   f32x4 Z = zero4();
 
+  StagePtrs sp = stage_ptrs(pr, nullptr, k, v, b, h, c0 * C, false, tid);
   Stage st;
-  stage_load(st, pr, nullptr, k, v, b, h, c0 * C, false, tid);
+  stage_load(st, sp, sv_t);
   stage_store(st, tl, false, tid);
   __syncthreads();
   for (int c = 0; c < nc; ++c) {
-    if (c + 1 < nc) stage_load(st, pr, nullptr, k, v, b, h, (c0 + c + 1) * C, false, tid);
+    if (c + 1 < nc) {
+      sp.next();
+      stage_load(st, sp, sv_t);
+    }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       bf16x8 vb[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(tl, m, nt, lane);
+      for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(tl.V, m, nt, lane);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const bf16x8 a = phik_frag(tl, 4 * w + mt, m, lane);
@@ -235,8 +266,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_fast_kernel(
 // ==========================================================================================
 struct __align__(16) WalkLds {
   Tiles tl;
-  f32x4 red[4][3][4][64];        // readout shares for other waves' tokens
-  float den[C];
+  f32x4 red[4][3][4][64];        // inbox of wave tt: readout shares from the other waves
+  float den[C];                  // D_t of the chunk's tokens
+  float inv[C];                  // 1 / D_t
 };
 
 template <typename Tout>
@@ -250,6 +282,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
   const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n_chunks = pr.T / C;
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
+  const long long sv_t = pr.sv[1];
 
   // prefix state of this segment
   const float* pre = states + ((long long)(b * pr.H + h) * n_seg + seg) * kStateFloats;
@@ -262,20 +295,28 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
   // every wave keeps its own copy of Z_{<c} (4 registers); lane holds Z[4g + r][lane % 16]
   f32x4 Z = *reinterpret_cast<const f32x4*>(pre + F * DV + lane * 4);
 
+  StagePtrs sp = stage_ptrs(pr, q, k, v, b, h, c0 * C, true, tid);
   Stage st;
-  stage_load(st, pr, q, k, v, b, h, c0 * C, true, tid);
+  stage_load(st, sp, sv_t);
   stage_store(st, tl, true, tid);
   __syncthreads();
 
+  // output row pointer of this lane's first token (16w + 4g) in the first chunk
+  Tout* orow = o + row_off(pr.so, b, c0 * C + 16 * w + 4 * g, h) + l16;
+  const long long so_t = pr.so[1];
+
   for (int c = 0; c < nc; ++c) {
     const int tok0 = (c0 + c) * C;
-    if (c + 1 < nc) stage_load(st, pr, q, k, v, b, h, tok0 + C, true, tid);
+    if (c + 1 < nc) {
+      sp.next();
+      stage_load(st, sp, sv_t);
+    }
 
     // ---- intra-chunk tile of this wave's tokens t in [16w, 16w+16) ----
     float lsum = 0.f;
     f32x4 Oown[4] = {zero4(), zero4(), zero4(), zero4()};
+    const s16x4 qf = row4_frag(tl.Qs, 16 * w, lane);
     {
-      const s16x4 qf = row4_frag(tl.Qs, 16 * w, lane);
       const int t = 16 * w + l16;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -284,9 +325,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int ms = 2 * m + half;
-          if (ms <= w) {
+          if (ms < w) {
             const f32x4 sc = mfma16(row4_frag(tl.Ks, 16 * ms, lane), qf, zero4());
-            square_mask(sc, 16 * ms, t, lane, &pa[4 * half], lsum);
+            square_mask<false>(sc, 16 * ms, t, lane, &pa[4 * half], lsum);
+          } else if (ms == w) {
+            const f32x4 sc = mfma16(row4_frag(tl.Ks, 16 * ms, lane), qf, zero4());
+            square_mask<true>(sc, 16 * ms, t, lane, &pa[4 * half], lsum);
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) pa[4 * half + r] = (__bf16)0.f;
@@ -296,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
 #pragma unroll
         for (int r = 0; r < 8; ++r) a[r] = pa[r];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) Oown[nt] = mfma32(a, v_frag(tl, m, nt, lane), Oown[nt]);
+        for (int nt = 0; nt < 4; ++nt) Oown[nt] = mfma32(a, v_frag(tl.V, m, nt, lane), Oown[nt]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -307,7 +351,6 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
     // A layout of a 16 x 16 x 16 product; q_t[4g..4g+3] is the same B operand as the scores.
     float zq = 0.f;
     {
-      const s16x4 qf = row4_frag(tl.Qs, 16 * w, lane);
       s16x4 zhi, zlo;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -323,12 +366,19 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
       zq = fmaf(bf_lo(qq.y), y[2], zq);
       zq = fmaf(bf_hi(qq.y), y[3], zq);
     }
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    zq += __shfl_xor(zq, 16);
+    zq += __shfl_xor(zq, 32);
+    if (g == 0) {
+      const float D = pr.eps + (zq + lsum);
+      sm.den[16 * w + l16] = D;
+      sm.inv[16 * w + l16] = 1.f / D;
+    }
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- readout of the prefix with rows [64w, 64w+64) of the state, one token tile at a
-    // time; shares of other waves' tokens go to LDS, this wave's own share is kept.
-    // (tt is a compile-time index after unrolling and w is uniform per wave, so no register
-    // array is ever indexed at run time.)
+    // ---- readout of the prefix with rows [64w, 64w+64) of the state: this wave's own token
+    // tile accumulates in place, the other three tiles' shares go to their owners' inboxes ----
     {
       bf16x8 sb[2][4];   // S as B operand: K step m' covers state tiles 2m', 2m'+1
 #pragma unroll
@@ -341,34 +391,40 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
             sb[mp][nt][4 + r] = (__bf16)S[2 * mp + 1][nt][r];
           }
         }
-#pragma unroll 1
-      for (int tt = 0; tt < 4; ++tt) {
+      // slot r' of the A operand -> feature (i, j) = (4w + 2mp + r'/4, 4g + r'%4)
+      auto phiq = [&](int tt, int mp, bf16x8& a) {
         const int t = 16 * tt + l16;
-        const uint2 qi = *reinterpret_cast<const uint2*>(&tl.Qs[t][4 * w]);   // q_t[4w..4w+3]
-        const uint2 qj = *reinterpret_cast<const uint2*>(&tl.Qs[t][4 * g]);   // q_t[4g..4g+3]
-        const float qiv[4] = {bf_lo(qi.x), bf_hi(qi.x), bf_lo(qi.y), bf_hi(qi.y)};
-        const float qjv[4] = {bf_lo(qj.x), bf_hi(qj.x), bf_lo(qj.y), bf_hi(qj.y)};
+        const uint2 qi = *reinterpret_cast<const uint2*>(&tl.Qs[t][4 * w + 2 * mp]);
+        const uint2 qj = *reinterpret_cast<const uint2*>(&tl.Qs[t][4 * g]);
+        const float i0 = bf_lo(qi.x), i1 = bf_hi(qi.x);
+        const float jv[4] = {bf_lo(qj.x), bf_hi(qj.x), bf_lo(qj.y), bf_hi(qj.y)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          a[r] = (__bf16)(i0 * jv[r]);
+          a[4 + r] = (__bf16)(i1 * jv[r]);
+        }
+      };
+#pragma unroll
+      for (int mp = 0; mp < 2; ++mp) {
+        bf16x8 a;
+        phiq(w, mp, a);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) Oown[nt] = mfma32(a, sb[mp][nt], Oown[nt]);
+      }
+#pragma unroll 1
+      for (int i = 1; i < 4; ++i) {
+        const int tt = (w + i) & 3;
         f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
         for (int mp = 0; mp < 2; ++mp) {
-          // slot r' -> feature (i, j) = (4w + 2mp + r'/4, 4g + r'%4)
           bf16x8 a;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            a[r] = (__bf16)(qiv[2 * mp] * qjv[r]);
-            a[4 + r] = (__bf16)(qiv[2 * mp + 1] * qjv[r]);
-          }
+          phiq(tt, mp, a);
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) O[nt] = mfma32(a, sb[mp][nt], O[nt]);
         }
-        if (tt == w) {
+        const int slot = w < tt ? w : w - 1;
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) Oown[nt] += O[nt];
-        } else {
-          const int slot = w < tt ? w : w - 1;
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) sm.red[tt][slot][nt][lane] = O[nt];
-        }
+        for (int nt = 0; nt < 4; ++nt) sm.red[tt][slot][nt][lane] = O[nt];
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -378,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
     for (int m = 0; m < 2; ++m) {
       bf16x8 vb[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(tl, m, nt, lane);
+      for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(tl.V, m, nt, lane);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const bf16x8 a = phik_frag(tl, 4 * w + mt, m, lane);
@@ -389,34 +445,25 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
       Z = mfma32(kf, kf, Z);
     }
     __builtin_amdgcn_sched_barrier(0);
-
-    // ---- hand the other waves their readout shares; finish the denominators ----
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    zq += __shfl_xor(zq, 16);
-    zq += __shfl_xor(zq, 32);
-    if (g == 0) sm.den[16 * w + l16] = pr.eps + (zq + lsum);
     __syncthreads();
 
-    f32x4 acc[4];
+    // ---- finish this wave's tokens: own share + three inbox shares, gate, store ----
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      acc[nt] = Oown[nt];
 #pragma unroll
-      for (int s2 = 0; s2 < 3; ++s2) acc[nt] += sm.red[w][s2][nt][lane];
+      for (int s2 = 0; s2 < 3; ++s2) Oown[nt] += sm.red[w][s2][nt][lane];
     }
     // lane holds tokens 16w + 4g + r, value column 16 nt + l16
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int tl_ = 16 * w + 4 * g + r;
-      const float D = sm.den[tl_];
-      const float inv = 1.f / D;
-      Tout* op = o + row_off(pr.so, b, tok0 + tl_, h);
+      const float inv = sm.inv[16 * w + 4 * g + r];
+      Tout* op = orow + r * so_t;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) op[16 * nt + l16] = cvt_out<Tout>(acc[nt][r] * inv);
+      for (int nt = 0; nt < 4; ++nt) op[16 * nt] = cvt_out<Tout>(Oown[nt][r] * inv);
     }
     if (den_out && lane < 16)
       den_out[((long long)b * pr.T + tok0 + 16 * w + lane) * pr.H + h] = sm.den[16 * w + lane];
+    orow += C * so_t;
 
     if (c + 1 < nc) stage_store(st, tl, true, tid);
     __syncthreads();
@@ -430,36 +477,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
 // ==========================================================================================
 struct __align__(16) QuadLds {
   __bf16 Ks[C][QROW];
-  __bf16 VT[DV][VTROW];
+  __bf16 V[C][VROW];
+  float inv[C];
   float den[C];
 };
-
-__device__ __forceinline__ void quad_stage_load(uint4& kq, uint4& v0, uint4& v1,
-                                                const DevProblem& pr, const __bf16* k,
-                                                const __bf16* v, int b, int h, int s0, int tid) {
-  const uint4 z = {0u, 0u, 0u, 0u};
-  if (tid < 128) {
-    const int s = s0 + (tid >> 1);
-    kq = s < pr.T ? ld16(k + row_off(pr.sk, b, s, h) + 8 * (tid & 1)) : z;
-  }
-  const int a = tid >> 3, c8 = tid & 7;
-  const int s = s0 + 2 * a;
-  v0 = s < pr.T ? ld16(v + row_off(pr.sv, b, s, h) + 8 * c8) : z;
-  v1 = s + 1 < pr.T ? ld16(v + row_off(pr.sv, b, s + 1, h) + 8 * c8) : z;
-}
-
-__device__ __forceinline__ void quad_stage_store(const uint4& kq, const uint4& v0,
-                                                 const uint4& v1, QuadLds& sm, int tid) {
-  if (tid < 128) *reinterpret_cast<uint4*>(&sm.Ks[tid >> 1][8 * (tid & 1)]) = kq;
-  const int a = tid >> 3, c8 = tid & 7;
-  const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w};
-  const uint32_t w1[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    *reinterpret_cast<uint32_t*>(&sm.VT[8 * c8 + 2 * e][2 * a]) = (w0[e] & 0xffffu) | (w1[e] << 16);
-    *reinterpret_cast<uint32_t*>(&sm.VT[8 * c8 + 2 * e + 1][2 * a]) = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
-  }
-}
 
 template <typename Tout>
 __global__ __launch_bounds__(kThreads, 2) void quadratic_fast_kernel(
@@ -470,20 +491,43 @@ __global__ __launch_bounds__(kThreads, 2) void quadratic_fast_kernel(
   const int qb = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int t0 = qb * C;
   const int t = t0 + 16 * w + l16;             // this lane's query (fragment column)
+  const uint4 z4 = {0u, 0u, 0u, 0u};
 
   // query operand of the score tile: q_t[4g..4g+3]
   s16x4 qf = {0, 0, 0, 0};
   if (t < pr.T)
     qf = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2*>(q + row_off(pr.sq, b, t, h) + 4 * g));
 
+  // staging: waves 0-1 half a k row each (key = lane), every thread 16 B of two v rows
+  const int a = tid >> 3, c8 = tid & 7;
+  auto load = [&](int s0) {
+    Stage x;
+    x.qk = z4;
+    if (w < 2) {
+      const int s = s0 + lane;
+      x.qk = s < pr.T ? ld16(k + row_off(pr.sk, b, s, h) + 8 * w) : z4;
+    }
+    const int s = s0 + 2 * a;
+    x.v0 = s < pr.T ? ld16(v + row_off(pr.sv, b, s, h) + 8 * c8) : z4;
+    x.v1 = s + 1 < pr.T ? ld16(v + row_off(pr.sv, b, s + 1, h) + 8 * c8) : z4;
+    return x;
+  };
+  auto store = [&](const Stage& x) {
+    if (w < 2) {
+      *reinterpret_cast<uint2*>(&sm.Ks[lane][8 * w]) = uint2{x.qk.x, x.qk.y};
+      *reinterpret_cast<uint2*>(&sm.Ks[lane][8 * w + 4]) = uint2{x.qk.z, x.qk.w};
+    }
+    *reinterpret_cast<uint4*>(&sm.V[2 * a][8 * c8]) = x.v0;
+    *reinterpret_cast<uint4*>(&sm.V[2 * a + 1][8 * c8]) = x.v1;
+  };
+
   f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
   float lsum = 0.f;
-  uint4 kq = {0u, 0u, 0u, 0u}, v0, v1;
-  quad_stage_load(kq, v0, v1, pr, k, v, b, h, 0, tid);
-  quad_stage_store(kq, v0, v1, sm, tid);
+  Stage x = load(0);
+  store(x);
   __syncthreads();
   for (int kb = 0; kb <= qb; ++kb) {
-    if (kb < qb) quad_stage_load(kq, v0, v1, pr, k, v, b, h, (kb + 1) * C, tid);
+    if (kb < qb) x = load((kb + 1) * C);
     const int s_base = kb * C;
     const bool diag = (kb == qb);
 #pragma unroll
@@ -493,39 +537,40 @@ __global__ __launch_bounds__(kThreads, 2) void quadratic_fast_kernel(
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int ms = 2 * m + half;
-        if (!diag || ms <= w) {
+        if (!diag || ms < w) {
           const f32x4 sc = mfma16(row4_frag(sm.Ks, 16 * ms, lane), qf, zero4());
-          square_mask(sc, s_base + 16 * ms, t, lane, &pa[4 * half], lsum);
+          square_mask<false>(sc, s_base + 16 * ms, t, lane, &pa[4 * half], lsum);
+        } else if (ms == w) {
+          const f32x4 sc = mfma16(row4_frag(sm.Ks, 16 * ms, lane), qf, zero4());
+          square_mask<true>(sc, s_base + 16 * ms, t, lane, &pa[4 * half], lsum);
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) pa[4 * half + r] = (__bf16)0.f;
         }
       }
-      bf16x8 a;
+      bf16x8 af;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) a[r] = pa[r];
+      for (int r = 0; r < 8; ++r) af[r] = pa[r];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int d = 16 * nt + l16;
-        const uint2 lo = *reinterpret_cast<const uint2*>(&sm.VT[d][32 * m + 4 * g]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&sm.VT[d][32 * m + 16 + 4 * g]);
-        const uint4 u = {lo.x, lo.y, hi.x, hi.y};
-        O[nt] = mfma32(a, __builtin_bit_cast(bf16x8, u), O[nt]);
-      }
+      for (int nt = 0; nt < 4; ++nt) O[nt] = mfma32(af, v_frag(sm.V, m, nt, lane), O[nt]);
     }
     __syncthreads();
-    if (kb < qb) quad_stage_store(kq, v0, v1, sm, tid);
+    if (kb < qb) store(x);
     __syncthreads();
   }
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
-  if (g == 0) sm.den[16 * w + l16] = pr.eps + lsum;
+  if (g == 0) {
+    const float D = pr.eps + lsum;
+    sm.den[16 * w + l16] = D;
+    sm.inv[16 * w + l16] = 1.f / D;
+  }
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int tr = 16 * w + 4 * g + r;
     if (t0 + tr >= pr.T) continue;
-    const float inv = 1.f / sm.den[tr];
+    const float inv = sm.inv[tr];
     Tout* op = o + row_off(pr.so, b, t0 + tr, h);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) op[16 * nt + l16] = cvt_out<Tout>(O[nt][r] * inv);
