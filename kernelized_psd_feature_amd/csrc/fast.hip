@@ -87,17 +87,17 @@ struct StagePtrs {
 
 __device__ __forceinline__ StagePtrs stage_ptrs(const DevProblem& pr, const __bf16* q,
                                                 const __bf16* k, const __bf16* v, int b, int h,
-                                                int tok0, bool with_q, int tid) {
+                                                int tok0, bool with_q, int tid, int dir = 1) {
   StagePtrs sp;
   const int w = tid >> 6, lane = tid & 63;
   if (w < 2)
     sp.qk = with_q ? q + row_off(pr.sq, b, tok0 + lane, h) + 8 * w : nullptr;
   else
     sp.qk = k + row_off(pr.sk, b, tok0 + lane, h) + 8 * (w - 2);
-  sp.qk_step = (long long)C * (w < 2 ? pr.sq[1] : pr.sk[1]);
+  sp.qk_step = (long long)dir * C * (w < 2 ? pr.sq[1] : pr.sk[1]);
   const int a = tid >> 3, c8 = tid & 7;
   sp.v0 = v + row_off(pr.sv, b, tok0 + 2 * a, h) + 8 * c8;
-  sp.v_step = (long long)C * pr.sv[1];
+  sp.v_step = (long long)dir * C * pr.sv[1];
   return sp;
 }
 
@@ -200,10 +200,10 @@ __device__ __forceinline__ Tout cvt_out(float x) { return from_f32<Tout>(x); }
 // Segment state: S_seg = sum over the segment's chunks of Phi(K_c)^T V_c and Z_seg = sum K^T K.
 // Grid (n_seg, H, B).  Wave w owns feature rows [64 w, 64 w + 64) x all 64 value columns.
 // ==========================================================================================
-__global__ __launch_bounds__(kThreads, 2) void chunk_state_fast_kernel(
+__global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
     DevProblem pr, int L, int n_seg, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, float* __restrict__ states) {
-  __shared__ Tiles tl;
+  __shared__ Tiles tl[2];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n_chunks = pr.T / C;
@@ -217,12 +217,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_fast_kernel(
     for (int nt = 0; nt < 4; ++nt) S[mt][nt] = zero4();
   f32x4 Z = zero4();
 
-  StagePtrs sp = stage_ptrs(pr, nullptr, k, v, b, h, c0 * C, false, tid);
+  // The sum is order-free, so the segment is read last chunk first: the walk that follows
+  // starts at the segment's first chunks, which are then the most recently read.
+  StagePtrs sp = stage_ptrs(pr, nullptr, k, v, b, h, (c0 + nc - 1) * C, false, tid, -1);
   Stage st;
   stage_load(st, sp, sv_t);
-  stage_store(st, tl, false, tid);
+  stage_store(st, tl[0], false, tid);
   __syncthreads();
   for (int c = 0; c < nc; ++c) {
+    const Tiles& cur = tl[c & 1];
     if (c + 1 < nc) {
       sp.next();
       stage_load(st, sp, sv_t);
@@ -231,20 +234,20 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_fast_kernel(
     for (int m = 0; m < 2; ++m) {
       bf16x8 vb[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(tl.V, m, nt, lane);
+      for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(cur.V, m, nt, lane);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 a = phik_frag(tl, 4 * w + mt, m, lane);
+        const bf16x8 a = phik_frag(cur, 4 * w + mt, m, lane);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) S[mt][nt] = mfma32(a, vb[nt], S[mt][nt]);
       }
       if (w == 0) {
-        const bf16x8 kf = kcol_frag(tl, m, lane);
+        const bf16x8 kf = kcol_frag(cur, m, lane);
         Z = mfma32(kf, kf, Z);
       }
     }
-    __syncthreads();
-    if (c + 1 < nc) stage_store(st, tl, false, tid);
+    // the other buffer was last read in the previous iteration, before its barrier
+    if (c + 1 < nc) stage_store(st, tl[(c + 1) & 1], false, tid);
     __syncthreads();
   }
   float* out = states + ((long long)(b * pr.H + h) * n_seg + seg) * kStateFloats;
@@ -260,19 +263,20 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_fast_kernel(
 // Segment walk: start from the segment's exclusive prefix (S_{<c}, Z_{<c}); for every chunk,
 // outputs = (readout of the prefix + causal intra-chunk tile) / (eps + denominators), then
 // the chunk's own state is added.  Grid (n_seg, H, B).
-//   Wave w: owns state rows [64 w, 64 w + 64) (as in the state kernel), computes the readout
-//   share of those rows for all 64 tokens, and finishes tokens [16 w, 16 w + 16): their intra
-//   tile, the other waves' readout shares (through LDS), the denominator and the store.
+//   Wave w owns state rows [64 w, 64 w + 64) (fp32, in registers, as in the state kernel) and
+//   the chunk's tokens [16 w, 16 w + 16).  Once per chunk every wave publishes its state rows
+//   in LDS as bf16 B operands; each wave then reads out its own tokens over all 256 rows, so
+//   no partial outputs cross waves.
 // ==========================================================================================
 struct __align__(16) WalkLds {
   Tiles tl;
-  f32x4 red[4][3][4][64];        // inbox of wave tt: readout shares from the other waves
+  uint4 Sb[8][4][64];            // S_{<c} as B operands: [32-row K step][value tile][lane]
   float den[C];                  // D_t of the chunk's tokens
   float inv[C];                  // 1 / D_t
 };
 
 template <typename Tout>
-__global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
+__global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     DevProblem pr, int L, int n_seg, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den_out,
     const float* __restrict__ states) {
@@ -295,10 +299,28 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
   // every wave keeps its own copy of Z_{<c} (4 registers); lane holds Z[4g + r][lane % 16]
   f32x4 Z = *reinterpret_cast<const f32x4*>(pre + F * DV + lane * 4);
 
+  // publish this wave's state rows as bf16 B operands: K step 2w + mp covers state tiles
+  // 2mp, 2mp+1 of this wave (slot r' -> row 16 (4w + 2mp + r'/4) + 4g + r'%4)
+  auto publish = [&]() {
+#pragma unroll
+    for (int mp = 0; mp < 2; ++mp)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        bf16x8 x;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[r] = (__bf16)S[2 * mp][nt][r];
+          x[4 + r] = (__bf16)S[2 * mp + 1][nt][r];
+        }
+        sm.Sb[2 * w + mp][nt][lane] = __builtin_bit_cast(uint4, x);
+      }
+  };
+
   StagePtrs sp = stage_ptrs(pr, q, k, v, b, h, c0 * C, true, tid);
   Stage st;
   stage_load(st, sp, sv_t);
   stage_store(st, tl, true, tid);
+  publish();
   __syncthreads();
 
   // output row pointer of this lane's first token (16w + 4g) in the first chunk
@@ -311,41 +333,38 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
       sp.next();
       stage_load(st, sp, sv_t);
     }
+    const int t = 16 * w + l16;                  // this lane's token (fragment column / row)
 
-    // ---- intra-chunk tile of this wave's tokens t in [16w, 16w+16) ----
+    // ---- intra-chunk tile of this wave's tokens ----
     float lsum = 0.f;
-    f32x4 Oown[4] = {zero4(), zero4(), zero4(), zero4()};
+    f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
     const s16x4 qf = row4_frag(tl.Qs, 16 * w, lane);
-    {
-      const int t = 16 * w + l16;
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        if (2 * m > w) break;                        // key tiles entirely in the future
-        __bf16 pa[8];
+    for (int m = 0; m < 2; ++m) {
+      if (2 * m > w) break;                        // key tiles entirely in the future
+      __bf16 pa[8];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int ms = 2 * m + half;
-          if (ms < w) {
-            const f32x4 sc = mfma16(row4_frag(tl.Ks, 16 * ms, lane), qf, zero4());
-            square_mask<false>(sc, 16 * ms, t, lane, &pa[4 * half], lsum);
-          } else if (ms == w) {
-            const f32x4 sc = mfma16(row4_frag(tl.Ks, 16 * ms, lane), qf, zero4());
-            square_mask<true>(sc, 16 * ms, t, lane, &pa[4 * half], lsum);
-          } else {
+      for (int half = 0; half < 2; ++half) {
+        const int ms = 2 * m + half;
+        if (ms < w) {
+          const f32x4 sc = mfma16(row4_frag(tl.Ks, 16 * ms, lane), qf, zero4());
+          square_mask<false>(sc, 16 * ms, t, lane, &pa[4 * half], lsum);
+        } else if (ms == w) {
+          const f32x4 sc = mfma16(row4_frag(tl.Ks, 16 * ms, lane), qf, zero4());
+          square_mask<true>(sc, 16 * ms, t, lane, &pa[4 * half], lsum);
+        } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pa[4 * half + r] = (__bf16)0.f;
-          }
+          for (int r = 0; r < 4; ++r) pa[4 * half + r] = (__bf16)0.f;
         }
-        bf16x8 a;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) a[r] = pa[r];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) Oown[nt] = mfma32(a, v_frag(tl.V, m, nt, lane), Oown[nt]);
       }
+      bf16x8 a;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) a[r] = pa[r];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) O[nt] = mfma32(a, v_frag(tl.V, m, nt, lane), O[nt]);
     }
-    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- inter-chunk denominator q^T Z_{<c} q for this wave's tokens ----
+    // ---- inter-chunk denominator q^T Z_{<c} q ----
     // Y = Z q_t on MFMA with Z split into bf16 hi + lo (fp32-accurate; q is exact in bf16):
     // Z's accumulator layout (lane: column lane%16, rows 4g + r) is, Z being symmetric, the
     // A layout of a 16 x 16 x 16 product; q_t[4g..4g+3] is the same B operand as the scores.
@@ -359,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
         zlo[r] = __builtin_bit_cast(short, (__bf16)(Z[r] - (float)hi));
       }
       f32x4 y = mfma16(zhi, qf, zero4());
-      y = mfma16(zlo, qf, y);                   // y[r] = (Z q_t)[4g + r], t = 16w + lane%16
+      y = mfma16(zlo, qf, y);                   // y[r] = (Z q_t)[4g + r]
       const uint2 qq = __builtin_bit_cast(uint2, qf);
       zq = fmaf(bf_lo(qq.x), y[0], zq);
       zq = fmaf(bf_hi(qq.x), y[1], zq);
@@ -372,62 +391,47 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
     zq += __shfl_xor(zq, 32);
     if (g == 0) {
       const float D = pr.eps + (zq + lsum);
-      sm.den[16 * w + l16] = D;
-      sm.inv[16 * w + l16] = 1.f / D;
+      sm.den[t] = D;
+      sm.inv[t] = 1.f / D;
     }
-    __builtin_amdgcn_sched_barrier(0);
 
-    // ---- readout of the prefix with rows [64w, 64w+64) of the state: this wave's own token
-    // tile accumulates in place, the other three tiles' shares go to their owners' inboxes ----
+    // ---- readout phi(q_t)^T S_{<c} over all 256 state rows (8 K steps of 32) ----
     {
-      bf16x8 sb[2][4];   // S as B operand: K step m' covers state tiles 2m', 2m'+1
+      const uint4 q0 = *reinterpret_cast<const uint4*>(&tl.Qs[t][0]);
+      const uint4 q1 = *reinterpret_cast<const uint4*>(&tl.Qs[t][8]);
+      const float qv[16] = {bf_lo(q0.x), bf_hi(q0.x), bf_lo(q0.y), bf_hi(q0.y),
+                            bf_lo(q0.z), bf_hi(q0.z), bf_lo(q0.w), bf_hi(q0.w),
+                            bf_lo(q1.x), bf_hi(q1.x), bf_lo(q1.y), bf_hi(q1.y),
+                            bf_lo(q1.z), bf_hi(q1.z), bf_lo(q1.w), bf_hi(q1.w)};
+      const uint2 q4 = *reinterpret_cast<const uint2*>(&tl.Qs[t][4 * g]);
+      const float qj[4] = {bf_lo(q4.x), bf_hi(q4.x), bf_lo(q4.y), bf_hi(q4.y)};
 #pragma unroll
-      for (int mp = 0; mp < 2; ++mp)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            sb[mp][nt][r] = (__bf16)S[2 * mp][nt][r];
-            sb[mp][nt][4 + r] = (__bf16)S[2 * mp + 1][nt][r];
-          }
-        }
-      // slot r' of the A operand -> feature (i, j) = (4w + 2mp + r'/4, 4g + r'%4)
-      auto phiq = [&](int tt, int mp, bf16x8& a) {
-        const int t = 16 * tt + l16;
-        const uint2 qi = *reinterpret_cast<const uint2*>(&tl.Qs[t][4 * w + 2 * mp]);
-        const uint2 qj = *reinterpret_cast<const uint2*>(&tl.Qs[t][4 * g]);
-        const float i0 = bf_lo(qi.x), i1 = bf_hi(qi.x);
-        const float jv[4] = {bf_lo(qj.x), bf_hi(qj.x), bf_lo(qj.y), bf_hi(qj.y)};
+      for (int kk = 0; kk < 8; ++kk) {
+        // slot r' -> feature (i, j) = (2kk + r'/4, 4g + r'%4)
+        bf16x8 a;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          a[r] = (__bf16)(i0 * jv[r]);
-          a[4 + r] = (__bf16)(i1 * jv[r]);
+          a[r] = (__bf16)(qv[2 * kk] * qj[r]);
+          a[4 + r] = (__bf16)(qv[2 * kk + 1] * qj[r]);
         }
-      };
 #pragma unroll
-      for (int mp = 0; mp < 2; ++mp) {
-        bf16x8 a;
-        phiq(w, mp, a);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) Oown[nt] = mfma32(a, sb[mp][nt], Oown[nt]);
-      }
-#pragma unroll 1
-      for (int i = 1; i < 4; ++i) {
-        const int tt = (w + i) & 3;
-        f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
-#pragma unroll
-        for (int mp = 0; mp < 2; ++mp) {
-          bf16x8 a;
-          phiq(tt, mp, a);
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) O[nt] = mfma32(a, sb[mp][nt], O[nt]);
-        }
-        const int slot = w < tt ? w : w - 1;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) sm.red[tt][slot][nt][lane] = O[nt];
+        for (int nt = 0; nt < 4; ++nt)
+          O[nt] = mfma32(a, __builtin_bit_cast(bf16x8, sm.Sb[kk][nt][lane]), O[nt]);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- gate and store this wave's tokens: lane holds tokens 16w + 4g + r, column 16nt + l16
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float inv = sm.inv[16 * w + 4 * g + r];
+      Tout* op = orow + r * so_t;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)   // streamed out: never re-read by this kernel
+        __builtin_nontemporal_store(cvt_out<Tout>(O[nt][r] * inv), op + 16 * nt);
+    }
+    if (den_out && lane < 16)
+      den_out[((long long)b * pr.T + tok0 + 16 * w + lane) * pr.H + h] = sm.den[16 * w + lane];
+    orow += C * so_t;
 
     // ---- state update with this chunk: S += Phi(K)^T V, Z += K^T K ----
 #pragma unroll 1
@@ -444,28 +448,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_output_fast_kernel(
       const bf16x8 kf = kcol_frag(tl, m, lane);
       Z = mfma32(kf, kf, Z);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-
-    // ---- finish this wave's tokens: own share + three inbox shares, gate, store ----
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-      for (int s2 = 0; s2 < 3; ++s2) Oown[nt] += sm.red[w][s2][nt][lane];
+    __syncthreads();                               // all reads of this chunk's tiles and Sb done
+    if (c + 1 < nc) {
+      stage_store(st, tl, true, tid);
+      publish();
     }
-    // lane holds tokens 16w + 4g + r, value column 16 nt + l16
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float inv = sm.inv[16 * w + 4 * g + r];
-      Tout* op = orow + r * so_t;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) op[16 * nt] = cvt_out<Tout>(Oown[nt][r] * inv);
-    }
-    if (den_out && lane < 16)
-      den_out[((long long)b * pr.T + tok0 + 16 * w + lane) * pr.H + h] = sm.den[16 * w + lane];
-    orow += C * so_t;
-
-    if (c + 1 < nc) stage_store(st, tl, true, tid);
     __syncthreads();
   }
 }

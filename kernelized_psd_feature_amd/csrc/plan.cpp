@@ -142,9 +142,19 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
   if (cp.fast) {
     int L = pr->seg_chunks;
     if (L == 0) {
-      // enough workgroups to fill 256 CUs about four deep, segments no longer than 32 chunks
-      L = 32;
-      while (L > 1 && cp.n_seq * ((cp.n_chunks + L - 1) / L) < 1024) L >>= 1;
+      // Fill the workgroup slots of the GPU (256 CUs x 3 resident workgroups) in as few whole
+      // rounds as possible, with segments of at most 64 chunks: fewer, longer segments mean
+      // less prefix-scan traffic, whole rounds avoid an idle tail.
+      const int64_t slots = 768;
+      L = 1;
+      if (cp.n_seq * cp.n_chunks > slots) {
+        for (int64_t rounds = 1;; ++rounds) {
+          const int64_t seg_target = (rounds * slots) / cp.n_seq;
+          if (seg_target < 1) continue;
+          L = int((cp.n_chunks + seg_target - 1) / seg_target);
+          if (L <= 64) break;
+        }
+      }
     }
     if (L > cp.n_chunks) L = cp.n_chunks;
     cp.L = L;
