@@ -29,9 +29,9 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 KERNEL_SOURCES = {  # files whose content defines each kernel's code
     "chunk_output": ["kernelized_psd_feature_amd/csrc/fast.hip",
-                     "kernelized_psd_feature_amd/csrc/generic.hip"],
+                     "kernelized_psd_feature_amd/csrc/device.h"],
     "quadratic": ["kernelized_psd_feature_amd/csrc/fast.hip",
-                  "kernelized_psd_feature_amd/csrc/generic.hip"],
+                  "kernelized_psd_feature_amd/csrc/device.h"],
 }
 
 
@@ -56,8 +56,9 @@ def source_sha(files):
 
 
 def load_traffic(kernel, workload, sha):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel source; else None."""
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by the factor a plain device copy of known size
+    gives), if the counters were taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
     if not os.path.exists(path):
         return None
@@ -66,6 +67,26 @@ def load_traffic(kernel, workload, sha):
     if c.get("kernel_source_sha") != sha:
         return None
     return c.get("traffic_bytes_per_launch")
+
+
+def cold_cache_ms(step, n, dev):
+    """Average step time with the 256 MB Infinity Cache and the L2s flushed before every
+    step (a 1 GiB buffer is rewritten outside the timed events)."""
+    import torch
+
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    total = 0.0
+    for _ in range(n):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        total += a.elapsed_time(b)
+    del flush
+    return total / n
 
 
 def cpu_baseline(w, target_s=12.0):
@@ -194,6 +215,7 @@ def main():
         "step_roofline_frac": round(bpt * tokens / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "dominant_kernel_source_sha": sha,
     }
+    line["ms_per_step_cold_cache"] = round(cold_cache_ms(step, max(5, args.steps // 5), dev), 5)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
