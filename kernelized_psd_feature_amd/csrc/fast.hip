@@ -218,18 +218,18 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
   f32x4 Z = zero4();
 
   // The sum is order-free, so the segment is read last chunk first: the walk that follows
-  // starts at the segment's first chunks, which are then the most recently read.
+  // starts at the segment's first chunks, which are then the most recently read.  Two chunks
+  // are in flight in registers (loaded two iterations before they are staged into LDS); the
+  // loop is unrolled by two so the register ring is indexed at compile time only.
   StagePtrs sp = stage_ptrs(pr, nullptr, k, v, b, h, (c0 + nc - 1) * C, false, tid, -1);
-  Stage st;
-  stage_load(st, sp, sv_t);
-  stage_store(st, tl[0], false, tid);
+  Stage sa, sb;
+  stage_load(sa, sp, sv_t);
+  stage_store(sa, tl[0], false, tid);
+  if (nc > 1) { sp.next(); stage_load(sa, sp, sv_t); }
+  if (nc > 2) { sp.next(); stage_load(sb, sp, sv_t); }
   __syncthreads();
-  for (int c = 0; c < nc; ++c) {
+  auto step = [&](int c, Stage& next, Stage& after) {
     const Tiles& cur = tl[c & 1];
-    if (c + 1 < nc) {
-      sp.next();
-      stage_load(st, sp, sv_t);
-    }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       bf16x8 vb[4];
@@ -247,8 +247,14 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
       }
     }
     // the other buffer was last read in the previous iteration, before its barrier
-    if (c + 1 < nc) stage_store(st, tl[(c + 1) & 1], false, tid);
+    if (c + 1 < nc) stage_store(next, tl[(c + 1) & 1], false, tid);
+    if (c + 3 < nc) { sp.next(); stage_load(next, sp, sv_t); }   // chunk c + 3
     __syncthreads();
+    (void)after;
+  };
+  for (int c = 0; c < nc; c += 2) {
+    step(c, sa, sb);                 // chunk c+1 is in sa, chunk c+2 in sb
+    if (c + 1 < nc) step(c + 1, sb, sa);
   }
   float* out = states + ((long long)(b * pr.H + h) * n_seg + seg) * kStateFloats;
 #pragma unroll

@@ -19,6 +19,9 @@ namespace {
 constexpr int kScanThreads = 256;
 constexpr int kMaxSlots = 16;   // float4 slots per thread: 256 threads * 16 * 4 = 16384 floats
 
+// kSlots: float4 slots per thread, a power of two >= ceil(tile_rows * strip / 4 / 256), so the
+// per-thread loops run no more iterations than the tile needs.
+template <int kSlots>
 __global__ __launch_bounds__(kScanThreads) void scan_tile_kernel(
     float* __restrict__ x, long long n, long long elems, int strip, int tile_rows,
     int n_tiles, int exclusive, float* __restrict__ totals,
@@ -35,10 +38,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_tile_kernel(
   float4* buf1 = lds + (long long)tile_rows * sv;
   float* base = x + (seq * n + r0) * elems + col0;
 
-  float4 val[kMaxSlots];
-  int rowv[kMaxSlots];
+  float4 val[kSlots];
+  int rowv[kSlots];
 #pragma unroll
-  for (int m = 0; m < kMaxSlots; ++m) {
+  for (int m = 0; m < kSlots; ++m) {
     const int slot = threadIdx.x + m * kScanThreads;
     const int r = slot / sv, cv = slot % sv;
     rowv[m] = r;
@@ -51,13 +54,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_tile_kernel(
   for (int off = 1; off < nr; off <<= 1, ++lvl) {
     float4* buf = (lvl & 1) ? buf1 : buf0;
 #pragma unroll
-    for (int m = 0; m < kMaxSlots; ++m) {
+    for (int m = 0; m < kSlots; ++m) {
       const int slot = threadIdx.x + m * kScanThreads;
       if (slot < nslots) buf[slot] = val[m];
     }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < kMaxSlots; ++m) {
+    for (int m = 0; m < kSlots; ++m) {
       const int slot = threadIdx.x + m * kScanThreads;
       if (slot < nslots && rowv[m] >= off) {
         const float4 y = buf[slot - off * sv];
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_tile_kernel(
   if (tile_offsets) {
     const float* ob = tile_offsets + (seq * n_tiles + tile) * elems + col0;
 #pragma unroll
-    for (int m = 0; m < kMaxSlots; ++m) {
+    for (int m = 0; m < kSlots; ++m) {
       const int slot = threadIdx.x + m * kScanThreads;
       const int cv = slot % sv;
       if (slot < nslots && col0 + cv * 4 < elems) {
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_tile_kernel(
   const bool last_tile = (tile == n_tiles - 1);
   if (totals && last_tile) {
 #pragma unroll
-    for (int m = 0; m < kMaxSlots; ++m) {
+    for (int m = 0; m < kSlots; ++m) {
       const int slot = threadIdx.x + m * kScanThreads;
       const int cv = slot % sv;
       if (slot < nslots && rowv[m] == nr - 1 && col0 + cv * 4 < elems)
@@ -92,13 +95,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_tile_kernel(
     // exclusive[r] = inclusive[r - 1]; row 0 takes the tile offset (or zero)
     float4* buf = (lvl & 1) ? buf1 : buf0;
 #pragma unroll
-    for (int m = 0; m < kMaxSlots; ++m) {
+    for (int m = 0; m < kSlots; ++m) {
       const int slot = threadIdx.x + m * kScanThreads;
       if (slot < nslots) buf[slot] = val[m];
     }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < kMaxSlots; ++m) {
+    for (int m = 0; m < kSlots; ++m) {
       const int slot = threadIdx.x + m * kScanThreads;
       const int cv = slot % sv;
       if (slot < nslots && col0 + cv * 4 < elems) {
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_tile_kernel(
     }
   }
 #pragma unroll
-  for (int m = 0; m < kMaxSlots; ++m) {
+  for (int m = 0; m < kSlots; ++m) {
     const int slot = threadIdx.x + m * kScanThreads;
     const int cv = slot % sv;
     if (slot < nslots && col0 + cv * 4 < elems)
@@ -153,15 +156,27 @@ hipError_t launch_scan_tiles(float* x, long long n_seq, long long n, long long e
     return hipErrorInvalidValue;
   dim3 grid((unsigned)((elems + strip - 1) / strip), n_tiles, (unsigned)n_seq);
   size_t lds = 2 * (size_t)tile_rows * (strip / 4) * sizeof(float4);
-  static bool lds_attr_set = false;   // up to 128 KiB of the 160 KiB LDS of a gfx950 CU
-  if (!lds_attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)scan_tile_kernel,
+  const long long slots = ((long long)tile_rows * (strip / 4) + kScanThreads - 1) / kScanThreads;
+  int ks = 1;
+  while (ks < slots) ks <<= 1;
+  auto go = [&](auto kern) -> hipError_t {
+    // up to 128 KiB of the 160 KiB LDS of a gfx950 CU
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
     if (e != hipSuccess) return e;
-    lds_attr_set = true;
+    kern<<<grid, kScanThreads, lds, st>>>(x, n, elems, strip, tile_rows, n_tiles, exclusive,
+                                          totals, tile_offsets);
+    return hipSuccess;
+  };
+  hipError_t e;
+  switch (ks) {
+    case 1: e = go(scan_tile_kernel<1>); break;
+    case 2: e = go(scan_tile_kernel<2>); break;
+    case 4: e = go(scan_tile_kernel<4>); break;
+    case 8: e = go(scan_tile_kernel<8>); break;
+    default: e = go(scan_tile_kernel<16>); break;
   }
-  scan_tile_kernel<<<grid, kScanThreads, lds, st>>>(x, n, elems, strip, tile_rows, n_tiles,
-                                                     exclusive, totals, tile_offsets);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 
