@@ -131,6 +131,8 @@ def main():
     ap.add_argument("--form", choices=["chunked", "quadratic"], default="chunked")
     ap.add_argument("--seg", type=int, default=0, help="chunks per segment (0 = library default)")
     ap.add_argument("--layout", choices=["bthd", "bhtd"], default="bthd")
+    ap.add_argument("--state", choices=["direct", "packed"], default="direct",
+                    help="chunk-state storage: all p^2 rows or the p(p+1)/2 unique ones")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="run only a device copy of this many MiB (counter calibration)")
@@ -165,12 +167,14 @@ def main():
     o = torch.empty(v.shape, dtype=torch.float32, device=dev)
     ws = None
     if args.form == "chunked":
-        need = K.chunked_workspace_size(q, k, v, chunk=w.chunk, seg_chunks=args.seg)
+        need = K.chunked_workspace_size(q, k, v, chunk=w.chunk, seg_chunks=args.seg,
+                                        state=args.state)
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
     def step():
         if args.form == "chunked":
-            K.fwd_chunked(q, k, v, chunk=w.chunk, seg_chunks=args.seg, out=o, workspace=ws)
+            K.fwd_chunked(q, k, v, chunk=w.chunk, seg_chunks=args.seg, out=o, workspace=ws,
+                          state=args.state)
         else:
             K.fwd_quadratic(q, k, v, out=o)
 
@@ -209,7 +213,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "p": w.p, "dv": w.dv,
                    "chunk": w.chunk, "form": args.form, "seg_chunks": args.seg,
-                   "layout": args.layout.upper(), "out_dtype": "fp32", "eps": 1e-6},
+                   "state": args.state, "layout": args.layout.upper(), "out_dtype": "fp32", "eps": 1e-6},
         "roofline": roofline,
         "kernels_ms": {n: round(t / max(c, 1), 5) for n, (c, t) in per_kernel.items() if c},
         "step_roofline_frac": round(bpt * tokens / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -49,6 +49,14 @@ typedef enum {
 
 typedef enum { KATA_F32 = 0, KATA_BF16 = 1 } kata_dtype;
 
+/* Storage of the chunk states S = sum vec(k k^T) v^T of the chunked form.  S is symmetric in
+ * its (i, j) feature pair (vec(k k^T) is), so its p(p+1)/2 unique rows determine it exactly
+ * (ai.info AI summary, Main Findings, state-size bullet: d^2 outer-product entries or
+ * d(d+1)/2 unique packed coordinates).  DIRECT keeps all p^2 rows; PACKED keeps the unique
+ * rows with the off-diagonal ones counted twice, so phi(q)^T S is read out over half the rows.
+ * Both give the same outputs up to rounding. */
+typedef enum { KATA_STATE_DIRECT = 0, KATA_STATE_PACKED = 1 } kata_state_layout;
+
 /* One attention problem.  Sizes:
  *   B, H, T >= 1;  p in {8, 16, 32} (q/k width);  dv in {16, 64} (value width);
  *   chunk: C for the chunked form, one of {16, 32, 64}, T % C == 0 (ignored by the quadratic
@@ -56,6 +64,9 @@ typedef enum { KATA_F32 = 0, KATA_BF16 = 1 } kata_dtype;
  *   seg_chunks: chunked form only: chunks per segment L (0 = library default).  The chunked
  *          form keeps the running state on chip for L consecutive chunks and combines the
  *          per-segment states with the prefix scan; L = 1 scans every chunk state.
+ *   state_layout: chunked form only, a kata_state_layout.  PACKED is implemented by the bf16
+ *          p = 16, dv = 64, chunk = 64 kernels; every other problem computes the direct form
+ *          whatever this field says.
  *   eps: finite, >= 0 (1e-6 in every workload).
  *   in_dtype: dtype of q, k, v (and dO); out_dtype: dtype of o.  Allowed pairs:
  *          (BF16 -> F32), (BF16 -> BF16), (F32 -> F32).  Gradients are always F32.
@@ -65,6 +76,7 @@ typedef struct {
   int32_t B, H, T, p, dv;
   int32_t chunk;
   int32_t seg_chunks;
+  int32_t state_layout;
   float eps;
   int32_t in_dtype;
   int32_t out_dtype;

@@ -45,7 +45,8 @@ class _Problem(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
         ("p", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
-        ("seg_chunks", ctypes.c_int32), ("eps", ctypes.c_float),
+        ("seg_chunks", ctypes.c_int32), ("state_layout", ctypes.c_int32),
+        ("eps", ctypes.c_float),
         ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
         ("sq", ctypes.c_int64 * 3), ("sk", ctypes.c_int64 * 3), ("sv", ctypes.c_int64 * 3),
         ("so", ctypes.c_int64 * 3), ("sdo", ctypes.c_int64 * 3),
@@ -121,8 +122,11 @@ def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+STATE_LAYOUTS = {"direct": 0, "packed": 1}
+
+
 def _make_problem(q, k, v, o=None, dO=None, chunk=0, seg_chunks=0, eps=1e-6,
-                  out_dtype=torch.float32):
+                  out_dtype=torch.float32, state="direct"):
     for name, x in (("q", q), ("k", k), ("v", v)):
         if not x.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
@@ -132,6 +136,9 @@ def _make_problem(q, k, v, o=None, dO=None, chunk=0, seg_chunks=0, eps=1e-6,
     pr = _Problem()
     pr.B, pr.H, pr.T, pr.p, pr.dv = B, H, T, p, v.shape[3]
     pr.chunk, pr.seg_chunks, pr.eps = chunk, seg_chunks, eps
+    if state not in STATE_LAYOUTS:
+        raise ValueError(f"state must be one of {sorted(STATE_LAYOUTS)}")
+    pr.state_layout = STATE_LAYOUTS[state]
     pr.in_dtype, pr.out_dtype = _dtype_code(q.dtype), _dtype_code(out_dtype)
     pr.sq[:] = _bth_strides(q, "q")
     pr.sk[:] = _bth_strides(k, "k")
@@ -160,21 +167,24 @@ def fwd_quadratic(q, k, v, eps=1e-6, out_dtype=torch.float32, out=None, return_d
     return (o, den) if return_den else o
 
 
-def chunked_workspace_size(q, k, v, chunk=64, seg_chunks=0, out_dtype=torch.float32):
-    pr = _make_problem(q, k, v, chunk=chunk, seg_chunks=seg_chunks, out_dtype=out_dtype)
+def chunked_workspace_size(q, k, v, chunk=64, seg_chunks=0, out_dtype=torch.float32,
+                           state="direct"):
+    pr = _make_problem(q, k, v, chunk=chunk, seg_chunks=seg_chunks, out_dtype=out_dtype,
+                       state=state)
     return int(_lib().kata_fwd_chunked_workspace_size(ctypes.byref(pr)))
 
 
 def fwd_chunked(q, k, v, chunk=64, eps=1e-6, out_dtype=torch.float32, seg_chunks=0,
-                out=None, workspace=None, return_den=False):
+                out=None, workspace=None, return_den=False, state="direct"):
     """Exact O(T) chunked-state forward (chunk states, prefix scan, readout).
 
+    state: "direct" (all p^2 state rows) or "packed" (the p(p+1)/2 unique rows).
     workspace: optional preallocated uint8 GPU tensor of at least chunked_workspace_size()
     bytes (allocated here otherwise).  Returns o (and D_t if return_den)."""
     o = _out(q, v, out_dtype, out)
     den = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_den else None
     pr = _make_problem(q, k, v, o, chunk=chunk, seg_chunks=seg_chunks, eps=eps,
-                       out_dtype=out_dtype)
+                       out_dtype=out_dtype, state=state)
     lib = _lib()
     need = int(lib.kata_fwd_chunked_workspace_size(ctypes.byref(pr)))
     if workspace is None:

@@ -57,12 +57,16 @@ __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w <<
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // ---- chunk tiles in LDS ------------------------------------------------------------------
-struct __align__(16) Tiles {
-  __bf16 Qs[C][QROW];     // q rows (bf16), row-major
-  __bf16 Ks[C][QROW];     // k rows (bf16), row-major
-  float KT[P][KTROW];     // k transposed, fp32 (exact copies of the bf16 inputs)
-  __bf16 V[C][VROW];      // v rows (bf16), row-major
+// kPacked adds rows to the K^T tile: rows 16..31 hold 2 k (the weight of an off-diagonal
+// packed state row) and row 32 zeros (the padding rows of the packed layout).
+template <bool kPacked>
+struct __align__(16) TilesT {
+  __bf16 Qs[C][QROW];                 // q rows (bf16), row-major
+  __bf16 Ks[C][QROW];                 // k rows (bf16), row-major
+  float KT[kPacked ? 2 * P + 1 : P][KTROW];   // k transposed, fp32 (exact copies)
+  __bf16 V[C][VROW];                  // v rows (bf16), row-major
 };
+using Tiles = TilesT<false>;
 
 // One thread's share of a chunk's global loads, held in registers while the previous chunk
 // is computed.  Waves 0-1 carry half a q row each (token = lane, half = wave), waves 2-3 half
@@ -107,7 +111,9 @@ __device__ __forceinline__ void stage_load(Stage& st, const StagePtrs& sp, long 
   st.v1 = ld16(sp.v0 + sv_t);
 }
 
-__device__ __forceinline__ void stage_store(const Stage& st, Tiles& tl, bool with_q, int tid) {
+template <bool kPacked>
+__device__ __forceinline__ void stage_store(const Stage& st, TilesT<kPacked>& tl, bool with_q,
+                                            int tid) {
   const int w = tid >> 6, lane = tid & 63;
   if (w < 2) {
     if (with_q) {
@@ -121,8 +127,13 @@ __device__ __forceinline__ void stage_store(const Stage& st, Tiles& tl, bool wit
     const uint32_t wd[4] = {st.qk.x, st.qk.y, st.qk.z, st.qk.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      tl.KT[8 * half + 2 * e][lane] = bf_lo(wd[e]);
-      tl.KT[8 * half + 2 * e + 1][lane] = bf_hi(wd[e]);
+      const float lo = bf_lo(wd[e]), hi = bf_hi(wd[e]);
+      tl.KT[8 * half + 2 * e][lane] = lo;
+      tl.KT[8 * half + 2 * e + 1][lane] = hi;
+      if (kPacked) {
+        tl.KT[P + 8 * half + 2 * e][lane] = 2.f * lo;       // exact
+        tl.KT[P + 8 * half + 2 * e + 1][lane] = 2.f * hi;
+      }
     }
   }
   const int a = tid >> 3, c8 = tid & 7;
@@ -146,7 +157,8 @@ __device__ __forceinline__ bf16x8 v_frag(const __bf16 (*V)[VROW], int m, int nt,
 
 // A operand of the state update for feature rows f = 16 i + (lane%16), i fixed, 32-key step
 // m: phi_f(k_s) = k_s[i] k_s[j], slot order kappa.
-__device__ __forceinline__ bf16x8 phik_frag(const Tiles& tl, int i, int m, int lane) {
+template <class TL>
+__device__ __forceinline__ bf16x8 phik_frag(const TL& tl, int i, int m, int lane) {
   const int j = lane & 15, g = lane >> 4;
   const float4 ia = *reinterpret_cast<const float4*>(&tl.KT[i][32 * m + 4 * g]);
   const float4 ib = *reinterpret_cast<const float4*>(&tl.KT[i][32 * m + 16 + 4 * g]);
@@ -160,8 +172,39 @@ __device__ __forceinline__ bf16x8 phik_frag(const Tiles& tl, int i, int m, int l
   return f;
 }
 
+// Packed layout: tile t (0..9) row 4g + r holds the state row of the pair
+// (a + (t & 1), 4J + r), (a, J) the double group 4 (t >> 1) + g.  The 20 double groups list,
+// for J = 0..3, the even a <= 4J + 2: every unique pair i <= j appears exactly once (weight 2
+// off the diagonal, 1 on it) and the 24 pairs i > j are zero rows.
+__device__ __forceinline__ void double_group(int idx, int& a, int& J) {
+  J = idx < 2 ? 0 : idx < 6 ? 1 : idx < 12 ? 2 : 3;
+  const int start = J == 0 ? 0 : J == 1 ? 2 : J == 2 ? 6 : 12;
+  a = 2 * (idx - start);
+}
+// Tiles owned by wave w: slots 0, 1 -> tiles 2w, 2w + 1; slot 2 -> tile 8 + w (waves 0, 1).
+__device__ __forceinline__ int packed_tile(int w, int slot) { return slot < 2 ? 2 * w + slot : 8 + w; }
+
+// A operand of the packed state update: row (lane % 16) of the tile is the pair (i, j);
+// irow selects the K^T row for the i factor (i, 16 + i for the doubled copy, 32 for zeros).
+template <class TL>
+__device__ __forceinline__ bf16x8 phik_packed_frag(const TL& tl, int irow, int jrow, int m,
+                                                   int lane) {
+  const int g = lane >> 4;
+  const float4 ia = *reinterpret_cast<const float4*>(&tl.KT[irow][32 * m + 4 * g]);
+  const float4 ib = *reinterpret_cast<const float4*>(&tl.KT[irow][32 * m + 16 + 4 * g]);
+  const float4 ja = *reinterpret_cast<const float4*>(&tl.KT[jrow][32 * m + 4 * g]);
+  const float4 jb = *reinterpret_cast<const float4*>(&tl.KT[jrow][32 * m + 16 + 4 * g]);
+  bf16x8 f;
+  f[0] = (__bf16)(ia.x * ja.x); f[1] = (__bf16)(ia.y * ja.y);
+  f[2] = (__bf16)(ia.z * ja.z); f[3] = (__bf16)(ia.w * ja.w);
+  f[4] = (__bf16)(ib.x * jb.x); f[5] = (__bf16)(ib.y * jb.y);
+  f[6] = (__bf16)(ib.z * jb.z); f[7] = (__bf16)(ib.w * jb.w);
+  return f;
+}
+
 // k_s[i] for i = lane%16 over the slots of 32-key step m (A and B operand of Z = K^T K).
-__device__ __forceinline__ bf16x8 kcol_frag(const Tiles& tl, int m, int lane) {
+template <class TL>
+__device__ __forceinline__ bf16x8 kcol_frag(const TL& tl, int m, int lane) {
   const int i = lane & 15, g = lane >> 4;
   const float4 a = *reinterpret_cast<const float4*>(&tl.KT[i][32 * m + 4 * g]);
   const float4 c = *reinterpret_cast<const float4*>(&tl.KT[i][32 * m + 16 + 4 * g]);
@@ -197,25 +240,103 @@ template <typename Tout>
 __device__ __forceinline__ Tout cvt_out(float x) { return from_f32<Tout>(x); }
 
 // ==========================================================================================
-// Segment state: S_seg = sum over the segment's chunks of Phi(K_c)^T V_c and Z_seg = sum K^T K.
-// Grid (n_seg, H, B).  Wave w owns feature rows [64 w, 64 w + 64) x all 64 value columns.
+// Per-layout constants shared by the state and walk kernels.
+//   direct: 16 state tiles (tile = i, rows j), wave w owns tiles 4w .. 4w+3, 8 readout K steps.
+//   packed: 10 state tiles (see double_group), waves 0-1 own 3 tiles and waves 2-3 own 2 (the
+//           higher waves have more intra-chunk work), 5 readout K steps.
+// State layout in the workspace (floats): tile t, value tile nt, lane -> ((t*4 + nt)*64 +
+// lane)*4 .. +3 (the accumulator registers as they are), then Z as one 16 x 16 tile.
 // ==========================================================================================
+template <bool kPacked>
+struct Layout {
+  static constexpr int kSlots = kPacked ? 3 : 4;         // state tiles a wave can own
+  static constexpr int kTiles = kPacked ? 10 : 16;
+  static constexpr int kSteps = kTiles / 2;              // readout K steps of 32 rows
+  static constexpr int kZOff = kTiles * 16 * DV;         // offset of Z in a stored state
+  static constexpr int kStateFloats = kZOff + 256;
+  __device__ static bool owns(int w, int slot) { return !kPacked || slot < 2 || w < 2; }
+  __device__ static int tile(int w, int slot) { return kPacked ? packed_tile(w, slot) : 4 * w + slot; }
+};
+static_assert(Layout<false>::kStateFloats == kStateFloats, "direct state size");
+
+// Row sources of the packed update's A operand for this lane's row of each owned tile.
+template <bool kPacked>
+struct UpdateRows {
+  int irow[Layout<kPacked>::kSlots], jrow[Layout<kPacked>::kSlots];
+  __device__ void init(int w, int lane) {
+#pragma unroll
+    for (int sl = 0; sl < Layout<kPacked>::kSlots; ++sl) {
+      if (!kPacked) {
+        irow[sl] = 4 * w + sl;                  // broadcast row i of the tile
+        jrow[sl] = lane & 15;
+      } else {
+        const int t = packed_tile(w, sl), row = lane & 15;
+        int a, J;
+        double_group(4 * (t >> 1) + (row >> 2), a, J);
+        const int i = a + (t & 1), j = 4 * J + (row & 3);
+        irow[sl] = i > j ? 2 * P : (i == j ? i : P + i);
+        jrow[sl] = j;
+      }
+    }
+  }
+};
+
+// S[slot] += Phi(K)^T V over one staged chunk, and Z += K^T K if with_z.
+template <bool kPacked, class TL>
+__device__ __forceinline__ void state_update(const TL& tl, const UpdateRows<kPacked>& ur,
+                                             f32x4 (&S)[Layout<kPacked>::kSlots][4], f32x4& Z,
+                                             int w, int lane, bool with_z) {
+#pragma unroll 1
+  for (int m = 0; m < 2; ++m) {
+    bf16x8 vb[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(tl.V, m, nt, lane);
+#pragma unroll
+    for (int sl = 0; sl < Layout<kPacked>::kSlots; ++sl) {
+      if (!Layout<kPacked>::owns(w, sl)) continue;
+      const bf16x8 a = kPacked ? phik_packed_frag(tl, ur.irow[sl], ur.jrow[sl], m, lane)
+                               : phik_frag(tl, ur.irow[sl], m, lane);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) S[sl][nt] = mfma32(a, vb[nt], S[sl][nt]);
+    }
+    if (with_z) {
+      const bf16x8 kf = kcol_frag(tl, m, lane);
+      Z = mfma32(kf, kf, Z);
+    }
+  }
+}
+
+template <bool kPacked>
+__device__ __forceinline__ void zero_pad_rows(TilesT<kPacked>& tl, int tid) {
+  if (kPacked && tid < KTROW) tl.KT[kPacked ? 2 * P : 0][tid] = 0.f;
+}
+
+// ==========================================================================================
+// Segment state: S_seg = sum over the segment's chunks of Phi(K_c)^T V_c and Z_seg = sum K^T K.
+// Grid (n_seg, H, B).
+// ==========================================================================================
+template <bool kPacked>
 __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
     DevProblem pr, int L, int n_seg, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, float* __restrict__ states) {
-  __shared__ Tiles tl[2];
+  using LY = Layout<kPacked>;
+  __shared__ TilesT<kPacked> tl[2];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n_chunks = pr.T / C;
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
   const long long sv_t = pr.sv[1];
 
-  f32x4 S[4][4];
+  f32x4 S[LY::kSlots][4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int sl = 0; sl < LY::kSlots; ++sl)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) S[mt][nt] = zero4();
+    for (int nt = 0; nt < 4; ++nt) S[sl][nt] = zero4();
   f32x4 Z = zero4();
+  UpdateRows<kPacked> ur;
+  ur.init(w, lane);
+  zero_pad_rows(tl[0], tid);
+  zero_pad_rows(tl[1], tid);
 
   // The sum is order-free, so the segment is read last chunk first: the walk that follows
   // starts at the segment's first chunks, which are then the most recently read.  Two chunks
@@ -228,66 +349,54 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
   if (nc > 1) { sp.next(); stage_load(sa, sp, sv_t); }
   if (nc > 2) { sp.next(); stage_load(sb, sp, sv_t); }
   __syncthreads();
-  auto step = [&](int c, Stage& next, Stage& after) {
-    const Tiles& cur = tl[c & 1];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      bf16x8 vb[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(cur.V, m, nt, lane);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 a = phik_frag(cur, 4 * w + mt, m, lane);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) S[mt][nt] = mfma32(a, vb[nt], S[mt][nt]);
-      }
-      if (w == 0) {
-        const bf16x8 kf = kcol_frag(cur, m, lane);
-        Z = mfma32(kf, kf, Z);
-      }
-    }
+  auto step = [&](int c, Stage& next) {
+    state_update<kPacked>(tl[c & 1], ur, S, Z, w, lane, w == 0);
     // the other buffer was last read in the previous iteration, before its barrier
     if (c + 1 < nc) stage_store(next, tl[(c + 1) & 1], false, tid);
     if (c + 3 < nc) { sp.next(); stage_load(next, sp, sv_t); }   // chunk c + 3
     __syncthreads();
-    (void)after;
   };
   for (int c = 0; c < nc; c += 2) {
-    step(c, sa, sb);                 // chunk c+1 is in sa, chunk c+2 in sb
-    if (c + 1 < nc) step(c + 1, sb, sa);
+    step(c, sa);                     // chunk c+1 is in sa, chunk c+2 in sb
+    if (c + 1 < nc) step(c + 1, sb);
   }
-  float* out = states + ((long long)(b * pr.H + h) * n_seg + seg) * kStateFloats;
+  float* out = states + ((long long)(b * pr.H + h) * n_seg + seg) * LY::kStateFloats;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int sl = 0; sl < LY::kSlots; ++sl) {
+    if (!LY::owns(w, sl)) continue;
+    const int t = LY::tile(w, sl);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
-      *reinterpret_cast<f32x4*>(out + ((w * 16 + mt * 4 + nt) * 64 + lane) * 4) = S[mt][nt];
-  if (w == 0) *reinterpret_cast<f32x4*>(out + F * DV + lane * 4) = Z;
+      *reinterpret_cast<f32x4*>(out + ((t * 4 + nt) * 64 + lane) * 4) = S[sl][nt];
+  }
+  if (w == 0) *reinterpret_cast<f32x4*>(out + LY::kZOff + lane * 4) = Z;
 }
 
 // ==========================================================================================
 // Segment walk: start from the segment's exclusive prefix (S_{<c}, Z_{<c}); for every chunk,
 // outputs = (readout of the prefix + causal intra-chunk tile) / (eps + denominators), then
 // the chunk's own state is added.  Grid (n_seg, H, B).
-//   Wave w owns state rows [64 w, 64 w + 64) (fp32, in registers, as in the state kernel) and
-//   the chunk's tokens [16 w, 16 w + 16).  Once per chunk every wave publishes its state rows
-//   in LDS as bf16 B operands; each wave then reads out its own tokens over all 256 rows, so
-//   no partial outputs cross waves.
+//   Each wave owns some state tiles (fp32, in registers, as in the state kernel) and the
+//   chunk's tokens [16 w, 16 w + 16).  Once per chunk every wave publishes its state tiles in
+//   LDS as bf16 B operands; each wave then reads out its own tokens over all state rows, so no
+//   partial outputs cross waves.
 // ==========================================================================================
+template <bool kPacked>
 struct __align__(16) WalkLds {
-  Tiles tl;
-  uint4 Sb[8][4][64];            // S_{<c} as B operands: [32-row K step][value tile][lane]
-  float den[C];                  // D_t of the chunk's tokens
-  float inv[C];                  // 1 / D_t
+  TilesT<kPacked> tl;
+  uint4 Sb[Layout<kPacked>::kSteps][4][64];   // S_{<c} as B operands: [K step][value tile][lane]
+  float den[C];                               // D_t of the chunk's tokens
+  float inv[C];                               // 1 / D_t
 };
 
-template <typename Tout>
+template <typename Tout, bool kPacked>
 __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     DevProblem pr, int L, int n_seg, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den_out,
     const float* __restrict__ states) {
-  __shared__ WalkLds sm;
-  Tiles& tl = sm.tl;
+  using LY = Layout<kPacked>;
+  __shared__ WalkLds<kPacked> sm;
+  TilesT<kPacked>& tl = sm.tl;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n_chunks = pr.T / C;
@@ -295,31 +404,53 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
   const long long sv_t = pr.sv[1];
 
   // prefix state of this segment
-  const float* pre = states + ((long long)(b * pr.H + h) * n_seg + seg) * kStateFloats;
-  f32x4 S[4][4];
+  const float* pre = states + ((long long)(b * pr.H + h) * n_seg + seg) * LY::kStateFloats;
+  f32x4 S[LY::kSlots][4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int sl = 0; sl < LY::kSlots; ++sl) {
+    const int t = LY::tile(w, sl);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
-      S[mt][nt] = *reinterpret_cast<const f32x4*>(pre + ((w * 16 + mt * 4 + nt) * 64 + lane) * 4);
+      S[sl][nt] = LY::owns(w, sl) ? *reinterpret_cast<const f32x4*>(pre + ((t * 4 + nt) * 64 + lane) * 4)
+                                  : zero4();
+  }
   // every wave keeps its own copy of Z_{<c} (4 registers); lane holds Z[4g + r][lane % 16]
-  f32x4 Z = *reinterpret_cast<const f32x4*>(pre + F * DV + lane * 4);
+  f32x4 Z = *reinterpret_cast<const f32x4*>(pre + LY::kZOff + lane * 4);
+  UpdateRows<kPacked> ur;
+  ur.init(w, lane);
+  zero_pad_rows(tl, tid);
 
-  // publish this wave's state rows as bf16 B operands: K step 2w + mp covers state tiles
-  // 2mp, 2mp+1 of this wave (slot r' -> row 16 (4w + 2mp + r'/4) + 4g + r'%4)
+  // readout rows of this lane group: direct K step kk covers rows (2kk + r'/4, 4g + r'%4);
+  // packed K step m' covers (a + r'/4, 4J + r'%4) with (a, J) the double group 4m' + g
+  int qa_off[LY::kSteps], qj_off[LY::kSteps];
+#pragma unroll
+  for (int kk = 0; kk < LY::kSteps; ++kk) {
+    if (kPacked) {
+      int a, J;
+      double_group(4 * kk + g, a, J);
+      qa_off[kk] = a;
+      qj_off[kk] = 4 * J;
+    } else {
+      qa_off[kk] = 2 * kk;
+      qj_off[kk] = 4 * g;
+    }
+  }
+
+  // publish this wave's state tiles as bf16 B operands: tile t fills slots 4 (t & 1) .. +3
+  // of K step t >> 1 (slot r' of lane group g <-> row 4g + r'%4 of tile 2(t>>1) + r'/4)
   auto publish = [&]() {
 #pragma unroll
-    for (int mp = 0; mp < 2; ++mp)
+    for (int sl = 0; sl < LY::kSlots; ++sl) {
+      if (!LY::owns(w, sl)) continue;
+      const int t = LY::tile(w, sl);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        bf16x8 x;
+        __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 x;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[r] = (__bf16)S[2 * mp][nt][r];
-          x[4 + r] = (__bf16)S[2 * mp + 1][nt][r];
-        }
-        sm.Sb[2 * w + mp][nt][lane] = __builtin_bit_cast(uint4, x);
+        for (int r = 0; r < 4; ++r) x[r] = (__bf16)S[sl][nt][r];
+        reinterpret_cast<uint2*>(&sm.Sb[t >> 1][nt][lane])[t & 1] = __builtin_bit_cast(uint2, x);
       }
+    }
   };
 
   StagePtrs sp = stage_ptrs(pr, q, k, v, b, h, c0 * C, true, tid);
@@ -401,29 +532,22 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
       sm.inv[t] = 1.f / D;
     }
 
-    // ---- readout phi(q_t)^T S_{<c} over all 256 state rows (8 K steps of 32) ----
-    {
-      const uint4 q0 = *reinterpret_cast<const uint4*>(&tl.Qs[t][0]);
-      const uint4 q1 = *reinterpret_cast<const uint4*>(&tl.Qs[t][8]);
-      const float qv[16] = {bf_lo(q0.x), bf_hi(q0.x), bf_lo(q0.y), bf_hi(q0.y),
-                            bf_lo(q0.z), bf_hi(q0.z), bf_lo(q0.w), bf_hi(q0.w),
-                            bf_lo(q1.x), bf_hi(q1.x), bf_lo(q1.y), bf_hi(q1.y),
-                            bf_lo(q1.z), bf_hi(q1.z), bf_lo(q1.w), bf_hi(q1.w)};
-      const uint2 q4 = *reinterpret_cast<const uint2*>(&tl.Qs[t][4 * g]);
-      const float qj[4] = {bf_lo(q4.x), bf_hi(q4.x), bf_lo(q4.y), bf_hi(q4.y)};
+    // ---- readout phi(q_t)^T S_{<c} over all published state rows ----
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        // slot r' -> feature (i, j) = (2kk + r'/4, 4g + r'%4)
-        bf16x8 a;
+    for (int kk = 0; kk < LY::kSteps; ++kk) {
+      const uint32_t qa = *reinterpret_cast<const uint32_t*>(&tl.Qs[t][qa_off[kk]]);
+      const uint2 qj = *reinterpret_cast<const uint2*>(&tl.Qs[t][qj_off[kk]]);
+      const float i0 = bf_lo(qa), i1 = bf_hi(qa);
+      const float jv[4] = {bf_lo(qj.x), bf_hi(qj.x), bf_lo(qj.y), bf_hi(qj.y)};
+      bf16x8 a;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          a[r] = (__bf16)(qv[2 * kk] * qj[r]);
-          a[4 + r] = (__bf16)(qv[2 * kk + 1] * qj[r]);
-        }
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          O[nt] = mfma32(a, __builtin_bit_cast(bf16x8, sm.Sb[kk][nt][lane]), O[nt]);
+      for (int r = 0; r < 4; ++r) {
+        a[r] = (__bf16)(i0 * jv[r]);
+        a[4 + r] = (__bf16)(i1 * jv[r]);
       }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        O[nt] = mfma32(a, __builtin_bit_cast(bf16x8, sm.Sb[kk][nt][lane]), O[nt]);
     }
 
     // ---- gate and store this wave's tokens: lane holds tokens 16w + 4g + r, column 16nt + l16
@@ -440,20 +564,7 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     orow += C * so_t;
 
     // ---- state update with this chunk: S += Phi(K)^T V, Z += K^T K ----
-#pragma unroll 1
-    for (int m = 0; m < 2; ++m) {
-      bf16x8 vb[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(tl.V, m, nt, lane);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 a = phik_frag(tl, 4 * w + mt, m, lane);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) S[mt][nt] = mfma32(a, vb[nt], S[mt][nt]);
-      }
-      const bf16x8 kf = kcol_frag(tl, m, lane);
-      Z = mfma32(kf, kf, Z);
-    }
+    state_update<kPacked>(tl, ur, S, Z, w, lane, true);
     __syncthreads();                               // all reads of this chunk's tiles and Sb done
     if (c + 1 < nc) {
       stage_store(st, tl, true, tid);
@@ -593,28 +704,36 @@ hipError_t launch_quadratic_fast(const DevProblem& pr, bool out_bf16, const void
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_state_fast(const DevProblem& pr, int L, int n_seg, const void* k,
-                                   const void* v, float* states, hipStream_t st) {
+hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int L, int n_seg,
+                                   const void* k, const void* v, float* states, hipStream_t st) {
   if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;
   dim3 grid(n_seg, pr.H, pr.B);
-  chunk_state_fast_kernel<<<grid, kThreads, 0, st>>>(pr, L, n_seg, (const __bf16*)k,
-                                                     (const __bf16*)v, states);
+  if (packed)
+    chunk_state_fast_kernel<true><<<grid, kThreads, 0, st>>>(pr, L, n_seg, (const __bf16*)k,
+                                                             (const __bf16*)v, states);
+  else
+    chunk_state_fast_kernel<false><<<grid, kThreads, 0, st>>>(pr, L, n_seg, (const __bf16*)k,
+                                                              (const __bf16*)v, states);
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_output_fast(const DevProblem& pr, bool out_bf16, int L, int n_seg,
-                                    const void* q, const void* k, const void* v, void* o,
-                                    float* den, const float* states, hipStream_t st) {
+hipError_t launch_chunk_output_fast(const DevProblem& pr, bool packed, bool out_bf16, int L,
+                                    int n_seg, const void* q, const void* k, const void* v,
+                                    void* o, float* den, const float* states, hipStream_t st) {
   if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;
   dim3 grid(n_seg, pr.H, pr.B);
-  if (out_bf16)
-    chunk_output_fast_kernel<__bf16><<<grid, kThreads, 0, st>>>(
-        pr, L, n_seg, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, den,
-        states);
-  else
-    chunk_output_fast_kernel<float><<<grid, kThreads, 0, st>>>(
-        pr, L, n_seg, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (float*)o, den,
-        states);
+  const __bf16 *qq = (const __bf16*)q, *kk = (const __bf16*)k, *vv = (const __bf16*)v;
+  if (out_bf16) {
+    if (packed)
+      chunk_output_fast_kernel<__bf16, true><<<grid, kThreads, 0, st>>>(pr, L, n_seg, qq, kk, vv, (__bf16*)o, den, states);
+    else
+      chunk_output_fast_kernel<__bf16, false><<<grid, kThreads, 0, st>>>(pr, L, n_seg, qq, kk, vv, (__bf16*)o, den, states);
+  } else {
+    if (packed)
+      chunk_output_fast_kernel<float, true><<<grid, kThreads, 0, st>>>(pr, L, n_seg, qq, kk, vv, (float*)o, den, states);
+    else
+      chunk_output_fast_kernel<float, false><<<grid, kThreads, 0, st>>>(pr, L, n_seg, qq, kk, vv, (float*)o, den, states);
+  }
   return hipGetLastError();
 }
 

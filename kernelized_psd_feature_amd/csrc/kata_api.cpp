@@ -20,11 +20,11 @@ hipError_t launch_quadratic_fast(const DevProblem& pr, bool out_bf16, const void
                                  hipStream_t st);
 bool quadratic_fast_supported(const kata_problem* pr);
 bool chunk_fast_available();
-hipError_t launch_chunk_state_fast(const DevProblem& pr, int L, int n_seg, const void* k,
-                                   const void* v, float* states, hipStream_t st);
-hipError_t launch_chunk_output_fast(const DevProblem& pr, bool out_bf16, int L, int n_seg,
-                                    const void* q, const void* k, const void* v, void* o,
-                                    float* den, const float* states, hipStream_t st);
+hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int L, int n_seg,
+                                   const void* k, const void* v, float* states, hipStream_t st);
+hipError_t launch_chunk_output_fast(const DevProblem& pr, bool packed, bool out_bf16, int L,
+                                    int n_seg, const void* q, const void* k, const void* v,
+                                    void* o, float* den, const float* states, hipStream_t st);
 }  // namespace kata
 
 namespace {
@@ -229,7 +229,7 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
   hipError_t e;
   {
     Timed t(KATA_K_CHUNK_STATE, st);
-    e = cp.fast ? kata::launch_chunk_state_fast(dp, cp.L, cp.n_seg, k, v, states, st)
+    e = cp.fast ? kata::launch_chunk_state_fast(dp, cp.packed, cp.L, cp.n_seg, k, v, states, st)
                 : kata::launch_chunk_state_generic(dp, in_bf16, k, v, states, cp.n_chunks, st);
   }
   if (e != hipSuccess) return launch_status(e, "chunk-state kernel");
@@ -241,8 +241,8 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
   if (e != hipSuccess) return launch_status(e, "chunk-state scan");
   {
     Timed t(KATA_K_CHUNK_OUTPUT, st);
-    e = cp.fast ? kata::launch_chunk_output_fast(dp, out_bf16, cp.L, cp.n_seg, q, k, v, o,
-                                                 den, states, st)
+    e = cp.fast ? kata::launch_chunk_output_fast(dp, cp.packed, out_bf16, cp.L, cp.n_seg, q,
+                                                 k, v, o, den, states, st)
                 : kata::launch_chunk_output_generic(dp, in_bf16, out_bf16, q, k, v, o, den,
                                                     states, cp.n_chunks, st);
   }

@@ -71,6 +71,8 @@ kata_status validate_problem(const kata_problem* pr, Form f, std::string* why) {
       return fail(why, KATA_ERR_UNSUPPORTED, "T must be a multiple of chunk");
     if (pr->seg_chunks < 0)
       return fail(why, KATA_ERR_INVALID_ARGUMENT, "seg_chunks must be >= 0");
+    if (pr->state_layout != KATA_STATE_DIRECT && pr->state_layout != KATA_STATE_PACKED)
+      return fail(why, KATA_ERR_INVALID_ARGUMENT, "state_layout must be DIRECT or PACKED");
   }
   const int64_t* strides[5] = {pr->sq, pr->sk, pr->sv, pr->so, pr->sdo};
   const char* names[5] = {"q", "k", "v", "o", "dO"};
@@ -158,6 +160,10 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
     }
     if (L > cp.n_chunks) L = cp.n_chunks;
     cp.L = L;
+    cp.packed = pr->state_layout == KATA_STATE_PACKED ? 1 : 0;
+    // packed: 10 tiles of 16 rows (the 136 unique (i, j) rows and 24 zero rows) x 64 columns,
+    // plus the full 16 x 16 Z
+    if (cp.packed) cp.state_elems = 160 * 64 + 256;
   } else {
     cp.L = 1;   // the VALU path scans every chunk state
   }

@@ -15,6 +15,7 @@ enum class Form { Quadratic, Chunked, Backward };
 // Which kernels run a chunked forward, and the workspace they need.
 struct ChunkPlan {
   int fast = 0;               // 1: bf16 MFMA kernels; 0: fp32-arithmetic VALU kernels
+  int packed = 0;             // 1: the MFMA kernels keep the unique (i <= j) state rows
   int L = 1;                  // chunks per segment
   int n_chunks = 0;           // N_c = T / C per (b, h)
   int n_seg = 0;              // ceil(N_c / L)

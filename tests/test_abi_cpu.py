@@ -128,6 +128,9 @@ def test_chunked_rejects_ragged_T_and_bad_chunk():
     assert _chunked(_problem(chunk=48)) == UNSUPPORTED
     assert _chunked(_problem(chunk=0)) == INVALID
     assert _chunked(_problem(seg=-1)) == INVALID
+    pr = _problem()
+    pr.state_layout = 2
+    assert _chunked(pr) == INVALID
 
 
 def test_chunked_workspace_checks():
@@ -141,6 +144,29 @@ def test_chunked_workspace_checks():
 def test_workspace_size_of_invalid_problem_is_zero():
     assert _lib().kata_fwd_chunked_workspace_size(ctypes.byref(_problem(T=100))) == 0
     assert _lib().kata_bwd_workspace_size(ctypes.byref(_problem(p=5))) == 0
+
+
+def test_packed_state_workspace_holds_the_unique_rows():
+    # packed states: 10 tiles of 16 x 64 (136 unique rows + 24 zero rows) + the 16 x 16 Z,
+    # against 256 x 64 + 256 for the direct layout; same segmentation for both
+    lib = _lib()
+    for T in (1024, 131072):
+        d = _problem(B=1, H=16, T=T)
+        pk = _problem(B=1, H=16, T=T)
+        pk.state_layout = 1
+        nd = lib.kata_fwd_chunked_workspace_size(ctypes.byref(d))
+        npk = lib.kata_fwd_chunked_workspace_size(ctypes.byref(pk))
+        assert 0 < npk < nd
+        n_states = 16 * (T // 64) if T == 1024 else None
+        if n_states:   # one segment per chunk when the chunks do not fill the GPU
+            assert npk >= n_states * (160 * 64 + 256) * 4
+            assert nd >= n_states * 16640 * 4
+    # a packed request on a problem the MFMA kernels do not take sizes as direct
+    f = _problem(B=1, H=2, T=256, p=8, dv=16, chunk=32, in_dt=0)
+    fp = _problem(B=1, H=2, T=256, p=8, dv=16, chunk=32, in_dt=0)
+    fp.state_layout = 1
+    assert lib.kata_fwd_chunked_workspace_size(ctypes.byref(f)) == \
+        lib.kata_fwd_chunked_workspace_size(ctypes.byref(fp))
 
 
 @pytest.mark.parametrize("p,dv", [(8, 16), (16, 64), (32, 64)])

@@ -374,3 +374,82 @@ def test_single_runtime_is_loaded():
     paths = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
     say(f"libamdhip64 mapped from: {sorted(paths)}")
     assert len({p for p in paths}) == 1
+
+
+# ------------------------------------------------------------ packed symmetric state ---
+# The packed layout keeps the 136 unique (i <= j) feature rows of each 256-row state, off-
+# diagonal rows doubled; it must reach the same outputs as the direct layout to tolerance.
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_packed_state_layer340m_full_size(seed):
+    w = W.WORKLOADS[2]
+    q, k, v = W.make_inputs(w, seed)
+    o = K.fwd_chunked(*_to_gpu(q, k, v), chunk=w.chunk, state="packed").cpu()
+    rng = np.random.default_rng(200 + seed)
+    heads = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(3)]
+    _check_rows(q, k, v, o, heads, lambda T: np.arange(T), TOL[w.dtype],
+                tag=f"layer340m packed seed {seed} whole heads")
+    all_heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    _check_rows(q, k, v, o, all_heads, _rows_sampler(rng, 8), TOL[w.dtype],
+                tag=f"layer340m packed seed {seed} all heads")
+
+
+@pytest.mark.parametrize("T", [64, 448])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_packed_state_small_T_every_element(T, out_dtype):
+    w = W.WORKLOADS[2]
+    q, k, v = W.make_inputs(w, 11, T=T, B=2, H=3)
+    ref, dref = O.closed_form(_np(q), _np(k), _np(v))
+    o, d = K.fwd_chunked(*_to_gpu(q, k, v), chunk=64, state="packed", out_dtype=out_dtype,
+                         return_den=True)
+    err = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
+    say(f"packed T={T} out {out_dtype}: max-abs {err:.3e}")
+    assert err <= TOL[w.dtype]
+    np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=1e-2)
+
+
+@pytest.mark.parametrize("seg", [1, 3, 32])
+def test_packed_state_segment_lengths(seg):
+    w = W.WORKLOADS[2]
+    q, k, v = W.make_inputs(w, 9, T=2048, B=1, H=2)
+    ref, _ = O.closed_form(_np(q), _np(k), _np(v))
+    o = K.fwd_chunked(*_to_gpu(q, k, v), chunk=64, seg_chunks=seg, state="packed")
+    err = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
+    say(f"packed seg_chunks={seg}: max-abs {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
+def test_packed_state_long_context_sampled():
+    w = W.WORKLOADS[4]
+    q, k, v = W.make_inputs(w, 0)
+    o = K.fwd_chunked(*_to_gpu(q, k, v), chunk=w.chunk, state="packed")
+    torch.cuda.synchronize()
+    o = o.cpu()
+    assert torch.isfinite(o).all()
+    rng = np.random.default_rng(44)
+    heads = [(0, 0), (0, int(rng.integers(1, w.H)))]
+    _check_rows(q, k, v, o, heads, _rows_sampler(rng, 192), TOL[w.dtype],
+                tag="long context packed")
+
+
+def test_packed_state_agrees_with_direct_and_is_causal():
+    w = W.WORKLOADS[2]
+    q, k, v = _to_gpu(*W.make_inputs(w, 12, T=1024, B=2, H=4))
+    a = K.fwd_chunked(q, k, v, state="direct")
+    b = K.fwd_chunked(q, k, v, state="packed")
+    say(f"packed vs direct: max-abs {float((a - b).abs().max()):.3e}")
+    assert float((a - b).abs().max()) <= 2e-2
+    assert torch.equal(b, K.fwd_chunked(q, k, v, state="packed"))
+    k2, v2 = k.clone(), v.clone()
+    k2[:, 320:] = float("nan")
+    v2[:, 320:] = float("inf")
+    b2 = K.fwd_chunked(q, k2, v2, state="packed")
+    assert torch.equal(b[:, :320], b2[:, :320])
+
+
+def test_packed_state_request_on_the_fp32_path_computes_the_direct_form():
+    w = W.WORKLOADS[1]
+    q, k, v = _to_gpu(*W.make_inputs(w, 0))
+    a = K.fwd_chunked(q, k, v, chunk=w.chunk, state="direct")
+    b = K.fwd_chunked(q, k, v, chunk=w.chunk, state="packed")
+    assert torch.equal(a, b)
