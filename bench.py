@@ -11,7 +11,10 @@ per-kernel events give the dominant kernel's average duration for the roofline f
 Printed: one JSON line.  value = head-tokens (B*H*T) per second.  roofline: algorithmic bytes
 of the dominant kernel per launch / its average duration, against MI355X's 8 TB/s HBM peak.
 cpu_baseline: the fp64 CPU oracle (brute-force closed form) timed on a bounded uniform sample
-of the same workload's query rows, scaled to head-tokens/s.
+of the same workload's query rows, scaled to head-tokens/s.  sweep: tokens/s of the chunked
+form at T = 1k .. 128k with B*T = 131072 (the metric's dependence on T).
+
+    python bench.py --form decode     # one decode step for 512 x 16 heads (recurrent form)
 """
 
 import argparse
@@ -32,6 +35,8 @@ KERNEL_SOURCES = {  # files whose content defines each kernel's code
                      "kernelized_psd_feature_amd/csrc/device.h"],
     "quadratic": ["kernelized_psd_feature_amd/csrc/fast.hip",
                   "kernelized_psd_feature_amd/csrc/device.h"],
+    "decode": ["kernelized_psd_feature_amd/csrc/decode.hip",
+               "kernelized_psd_feature_amd/csrc/device.h"],
 }
 
 
@@ -122,44 +127,60 @@ def cpu_baseline(w, target_s=12.0):
     }
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="long_context_131k")
-    ap.add_argument("--form", choices=["chunked", "quadratic"], default="chunked")
-    ap.add_argument("--seg", type=int, default=0, help="chunks per segment (0 = library default)")
-    ap.add_argument("--layout", choices=["bthd", "bhtd"], default="bthd")
-    ap.add_argument("--state", choices=["direct", "packed"], default="direct",
-                    help="chunk-state storage: all p^2 rows or the p(p+1)/2 unique ones")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", type=int, default=0,
-                    help="run only a device copy of this many MiB (counter calibration)")
-    args = ap.parse_args()
+def timed_steps(step, steps, warmup, dev):
+    """W untimed steps, then K steps between two events on the launch stream; returns the
+    average ms per step and the library's per-kernel event timings of the K steps."""
+    import torch
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(every (batch, head) is independent; see the sharding notes).", file=sys.stderr)
-        sys.exit(2)
+    import kernelized_psd_feature_amd as K
 
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    K.timing_begin()
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    per_kernel = K.timing_end()
+    return start.elapsed_time(stop) / steps, per_kernel
+
+
+def sweep(q, k, v, args, dev):
+    """Forward tokens/s of the chunked form at each T of the metric's sweep, B*T = 131072,
+    16 heads: the 131k workload's tensors viewed as (131072 / T, T, 16, D)."""
     import torch
 
     import kata_workloads as W
     import kernelized_psd_feature_amd as K
 
-    dev = torch.device("cuda:0")
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n}), flush=True)
-        return
+    out = []
+    o = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    for T in W.SWEEP_T:
+        B = q.shape[0] * q.shape[1] // T
+        qs, ks, vs, os_ = (x.reshape(B, T, *x.shape[2:]) for x in (q, k, v, o))
+        ws = torch.empty(max(K.chunked_workspace_size(qs, ks, vs, state=args.state), 256),
+                         dtype=torch.uint8, device=dev)
 
-    w = next(x for x in W.WORKLOADS.values() if x.name == args.workload)
+        def step():
+            K.fwd_chunked(qs, ks, vs, out=os_, workspace=ws, state=args.state)
+
+        ms, _ = timed_steps(step, 20, 5, dev)
+        out.append({"T": T, "B": B, "ms": round(ms, 5),
+                    "tokens_per_s": round(B * 16 * T / (ms / 1e3), 1)})
+        del ws
+    return out
+
+
+def run_chunked(args, dev, w):
+    import torch
+
+    import kata_workloads as W
+    import kernelized_psd_feature_amd as K
+
     q, k, v = W.make_inputs(w, 0)
     if args.layout == "bhtd":
         q, k, v = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
@@ -178,50 +199,148 @@ def main():
         else:
             K.fwd_quadratic(q, k, v, out=o)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    K.timing_begin()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    per_kernel = K.timing_end()
-    ms = start.elapsed_time(stop) / args.steps
+    ms, per_kernel = timed_steps(step, args.steps, args.warmup, dev)
     tokens = w.B * w.H * w.T
-    value = tokens / (ms / 1e3)
-
     dom = "chunk_output" if args.form == "chunked" else "quadratic"
     launches, total_ms = per_kernel[dom]
     avg_ms = total_ms / max(launches, 1)
     bpt = algorithmic_bytes_per_token(w.p, w.dv)
-    bytes_launch = bpt * tokens
-    achieved = bytes_launch / (avg_ms / 1e3) / 1e9
+    achieved = bpt * tokens / (avg_ms / 1e3) / 1e9
     sha = source_sha(KERNEL_SOURCES[dom])
-    roofline = {
-        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": load_traffic(dom, w.name, sha),
-    }
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "metric": METRIC, "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "p": w.p, "dv": w.dv,
                    "chunk": w.chunk, "form": args.form, "seg_chunks": args.seg,
-                   "state": args.state, "layout": args.layout.upper(), "out_dtype": "fp32", "eps": 1e-6},
-        "roofline": roofline,
+                   "state": args.state, "layout": args.layout.upper(), "out_dtype": "fp32",
+                   "eps": 1e-6},
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(dom, w.name, sha),
+        },
         "kernels_ms": {n: round(t / max(c, 1), 5) for n, (c, t) in per_kernel.items() if c},
         "step_roofline_frac": round(bpt * tokens / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "dominant_kernel_source_sha": sha,
     }
     line["ms_per_step_cold_cache"] = round(cold_cache_ms(step, max(5, args.steps // 5), dev), 5)
+    if args.form == "chunked" and w.name == "long_context_131k" and not args.no_sweep \
+            and args.layout == "bthd":
+        del ws
+        line["sweep"] = sweep(q, k, v, args, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
+    return line
+
+
+def decode_bytes_per_token(p, dv, in_bytes=2, out_bytes=4):
+    # the fp32 state of the (b, h), read once and written once, plus q, k, v in and o out
+    return 2 * 4 * p * p * (dv + 1) + algorithmic_bytes_per_token(p, dv, in_bytes, out_bytes)
+
+
+def cpu_baseline_decode(w, target_s=10.0):
+    """Time the oracle's token-by-token recurrence (a decode step per token) on one head of
+    the workload's recipe; head-tokens/s."""
+    import torch
+
+    import kata_workloads as W
+    import oracle as O
+
+    q, k, v = W.make_inputs(w, 0, B=1, H=1, T=64)
+    Q, Kk, V = (x.to(torch.float64).numpy() for x in (q, k, v))
+    done, spent = 0, 0.0
+    while spent < target_s:
+        t0 = time.perf_counter()
+        O.recurrent(Q, Kk, V)
+        spent += time.perf_counter() - t0
+        done += Q.shape[1]
+    return {"value": done / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} decode steps of one head (p={w.p}, d_v={w.dv}) by the fp64 "
+                      f"token-by-token recurrence, {spent:.1f} s"}
+
+
+def run_decode(args, dev):
+    import torch
+
+    import kata_workloads as W
+    import kernelized_psd_feature_amd as K
+
+    w = W.DECODE
+    q, k, v = (x.to(dev) for x in W.make_inputs(w, 0))
+    state = torch.zeros(K.state_shape(k, v), dtype=torch.float32, device=dev)
+    o = torch.empty(v.shape, dtype=torch.float32, device=dev)
+
+    def step():
+        K.decode(q, k, v, state, out=o)
+
+    ms, per_kernel = timed_steps(step, args.steps, args.warmup, dev)
+    tokens = w.B * w.H * w.T
+    launches, total_ms = per_kernel["decode"]
+    avg_ms = total_ms / max(launches, 1)
+    bpt = decode_bytes_per_token(w.p, w.dv)
+    achieved = bpt * tokens / (avg_ms / 1e3) / 1e9
+    line = {
+        "metric": "decode tokens/sec (B·H new tokens per step / s), p=16, d_v=64",
+        "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "tokens_per_step": w.T, "p": w.p,
+                   "dv": w.dv, "form": "decode", "state_bytes": 4 * tokens * w.p ** 2 * (w.dv + 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic("decode", w.name,
+                                             source_sha(KERNEL_SOURCES["decode"]))},
+        "kernels_ms": {n: round(t / max(c, 1), 5) for n, (c, t) in per_kernel.items() if c},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode(w)
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="long_context_131k")
+    ap.add_argument("--form", choices=["chunked", "quadratic", "decode"], default="chunked")
+    ap.add_argument("--seg", type=int, default=0, help="chunks per segment (0 = library default)")
+    ap.add_argument("--layout", choices=["bthd", "bhtd"], default="bthd")
+    ap.add_argument("--state", choices=["direct", "packed"], default="packed",
+                    help="chunk-state storage: all p^2 rows or the p(p+1)/2 unique ones")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the T sweep")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="run only a device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(every (batch, head) is independent; see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kata_workloads as W
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n}), flush=True)
+        return
+    if args.form == "decode":
+        line = run_decode(args, dev)
+    else:
+        w = next(x for x in W.WORKLOADS.values() if x.name == args.workload)
+        line = run_chunked(args, dev, w)
     print(json.dumps(line), flush=True)
 
 

@@ -137,6 +137,35 @@ kata_status kata_chunk_state_scan(float* states, int64_t n_seq, int64_t n_chunks
                                   void* workspace, size_t ws_bytes, int32_t* levels,
                                   void* stream);
 
+/* ---- Recurrent form: prefill and decode ---------------------------------------------
+ * The state of one (b, h) after tokens 0 .. t is
+ *     S_t = sum_{s<=t} vec(k_s k_s^T) v_s^T  (p^2 x dv),   Z_t = sum_{s<=t} k_s k_s^T,
+ * and o_t = vec(q_t q_t^T)^T S_t / (eps + q_t^T Z_t q_t): the same outputs as the forms above,
+ * computed with a constant-size state per token (ai.info AI summary, Main Findings, the bullet
+ * on constant-time recurrent inference; gist.science section 2.2 for vec(u u^T)).
+ * State layout: device fp32 [B][H][dv + 1][p * p], contiguous, 16-byte aligned; row d < dv of
+ * a (b, h) holds S[(i, j)][d] at column i * p + j, row dv holds Z[i][j] at column i * p + j.
+ */
+
+/* Bytes of workspace kata_recurrent_state needs (0 for an invalid problem). */
+size_t kata_recurrent_state_workspace_size(const kata_problem* pr);
+
+/* Prefill: state <- (S, Z) after the problem's T tokens, from k and v (q is not read).  The
+ * problem is checked as for kata_fwd_chunked (T % chunk == 0; state_layout is ignored); the
+ * bf16 p = 16, dv = 64, chunk = 64 problem uses the MFMA state kernel (phi(k) rounded to bf16
+ * before the products with v, fp32 accumulation), every other one fp32 arithmetic.  The state
+ * is overwritten.  Errors: as kata_fwd_chunked. */
+kata_status kata_recurrent_state(const kata_problem* pr, const void* k, const void* v,
+                                 float* state, void* workspace, size_t ws_bytes, void* stream);
+
+/* Decode: advances state over the problem's T tokens one at a time (T = 1 is one decode step)
+ * and writes o_t (and D_t = eps + q_t^T Z_t q_t into den if not NULL) for each, all
+ * arithmetic in fp32.  pr->chunk, seg_chunks and state_layout are ignored.  state is read and
+ * written in place; calls that share a state must be ordered on one stream.
+ * Errors: INVALID_ARGUMENT / UNSUPPORTED / DEVICE as for the forward calls. */
+kata_status kata_decode(const kata_problem* pr, const void* q, const void* k, const void* v,
+                        void* o, float* den, float* state, void* stream);
+
 /* Bytes of workspace kata_bwd needs. */
 size_t kata_bwd_workspace_size(const kata_problem* pr);
 
@@ -172,7 +201,9 @@ typedef enum {
   KATA_K_SCAN = 2,
   KATA_K_CHUNK_OUTPUT = 3,
   KATA_K_BWD = 4,
-  KATA_K_COUNT = 5
+  KATA_K_DECODE = 5,
+  KATA_K_STATE_SUM = 6,
+  KATA_K_COUNT = 7
 } kata_kernel_kind;
 
 typedef struct {

@@ -20,7 +20,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "SWEEP_T", "make_inputs", "sweep_workload"]
+__all__ = ["Workload", "WORKLOADS", "DECODE", "SWEEP_T", "make_inputs", "sweep_workload"]
 
 
 @dataclass(frozen=True)
@@ -54,6 +54,12 @@ WORKLOADS = {
     5: Workload(5, "training_4k", B=8, H=16, T=4096, p=16, dv=64, chunk=64,
                 dtype=torch.bfloat16),
 }
+
+# Decode: one new token for each of 512 sequences of 16 heads, p=16, d_v=64 (a serving batch
+# whose 545 MB of fp32 state exceeds the 256 MB Infinity Cache, so every step streams the
+# state from HBM).
+DECODE = Workload(6, "decode_b512", B=512, H=16, T=1, p=16, dv=64, chunk=64,
+                  dtype=torch.bfloat16)
 
 # Throughput sweep at p=16, d_v=64, 16 heads, with B*T held at 131072 head-positions.
 SWEEP_T = (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072)

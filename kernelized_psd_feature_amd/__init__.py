@@ -10,6 +10,8 @@ path: if libkata.so is missing, or a call fails, an exception is raised.
     o = fwd_quadratic(q, k, v)                  # flash-style O(T^2) form
     dq, dk, dv = bwd(q, k, v, dO)               # fp32 gradients of sum(dO * o)
     levels, totals = chunk_state_scan(states)   # in-place exclusive prefix scan
+    state = recurrent_state(k, v)               # (S, Z) after the given tokens (prefill)
+    o = decode(q, k, v, state)                  # advance the state token by token
 
 q, k: (B, T, H, p); v: (B, T, H, dv) -- the layout of the pages' kernel call -- with the last
 dimension contiguous; any (b, t, h) strides that keep rows 16-byte aligned are accepted
@@ -24,6 +26,7 @@ import torch
 __all__ = [
     "KataError", "fwd_quadratic", "fwd_chunked", "chunked_workspace_size",
     "chunk_state_scan", "scan_workspace_size", "bwd", "bwd_workspace_size",
+    "recurrent_state", "recurrent_state_workspace_size", "decode", "state_shape",
     "timing_begin", "timing_end", "library_path", "KERNEL_KINDS",
 ]
 
@@ -32,7 +35,8 @@ _LIB_PATH = os.path.join(_HERE, "libkata.so")
 _LIB = None
 
 KATA_F32, KATA_BF16 = 0, 1
-KERNEL_KINDS = ("quadratic", "chunk_state", "scan", "chunk_output", "bwd")
+KERNEL_KINDS = ("quadratic", "chunk_state", "scan", "chunk_output", "bwd", "decode",
+                "state_sum")
 
 
 class KataError(RuntimeError):
@@ -54,7 +58,7 @@ class _Problem(ctypes.Structure):
 
 
 class _Times(ctypes.Structure):
-    _fields_ = [("launches", ctypes.c_int64 * 5), ("total_ms", ctypes.c_double * 5)]
+    _fields_ = [("launches", ctypes.c_int64 * 7), ("total_ms", ctypes.c_double * 7)]
 
 
 def library_path():
@@ -77,6 +81,9 @@ def _lib():
             "kata_chunk_state_scan_workspace_size": (SZ, [I64, I64, I64]),
             "kata_chunk_state_scan": (I32, [VP, I64, I64, I64, I32, VP, VP, SZ,
                                             ctypes.POINTER(I32), VP]),
+            "kata_recurrent_state_workspace_size": (SZ, [P]),
+            "kata_recurrent_state": (I32, [P, VP, VP, VP, VP, SZ, VP]),
+            "kata_decode": (I32, [P, VP, VP, VP, VP, VP, VP, VP]),
             "kata_bwd_workspace_size": (SZ, [P]),
             "kata_bwd": (I32, [P, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
             "kata_status_string": (ctypes.c_char_p, [I32]),
@@ -168,17 +175,18 @@ def fwd_quadratic(q, k, v, eps=1e-6, out_dtype=torch.float32, out=None, return_d
 
 
 def chunked_workspace_size(q, k, v, chunk=64, seg_chunks=0, out_dtype=torch.float32,
-                           state="direct"):
+                           state="packed"):
     pr = _make_problem(q, k, v, chunk=chunk, seg_chunks=seg_chunks, out_dtype=out_dtype,
                        state=state)
     return int(_lib().kata_fwd_chunked_workspace_size(ctypes.byref(pr)))
 
 
 def fwd_chunked(q, k, v, chunk=64, eps=1e-6, out_dtype=torch.float32, seg_chunks=0,
-                out=None, workspace=None, return_den=False, state="direct"):
+                out=None, workspace=None, return_den=False, state="packed"):
     """Exact O(T) chunked-state forward (chunk states, prefix scan, readout).
 
-    state: "direct" (all p^2 state rows) or "packed" (the p(p+1)/2 unique rows).
+    state: "packed" (the p(p+1)/2 unique state rows, the faster layout) or "direct" (all p^2
+    rows); both give the same outputs up to rounding.
     workspace: optional preallocated uint8 GPU tensor of at least chunked_workspace_size()
     bytes (allocated here otherwise).  Returns o (and D_t if return_den)."""
     o = _out(q, v, out_dtype, out)
@@ -221,6 +229,52 @@ def chunk_state_scan(states, exclusive=True, want_totals=False, workspace=None):
                                          ctypes.byref(levels), _stream(states.device)),
                "kata_chunk_state_scan")
     return levels.value, totals
+
+
+def state_shape(k, v):
+    """Shape of the recurrent state of (B, T, H, p) keys and (B, T, H, dv) values:
+    (B, H, dv + 1, p * p) fp32; [b, h, d] holds S[(i, j), d] at column i * p + j for d < dv
+    and Z[i, j] for d = dv."""
+    B, _, H, p = k.shape
+    return (B, H, v.shape[-1] + 1, p * p)
+
+
+def recurrent_state_workspace_size(k, v, chunk=64):
+    pr = _make_problem(k, k, v, chunk=chunk)
+    return int(_lib().kata_recurrent_state_workspace_size(ctypes.byref(pr)))
+
+
+def recurrent_state(k, v, chunk=64, out=None, workspace=None):
+    """Prefill: the state (S, Z) after all T tokens of k, v (T % chunk == 0), in the layout
+    of state_shape()."""
+    state = out if out is not None else torch.empty(state_shape(k, v), dtype=torch.float32,
+                                                    device=k.device)
+    if state.shape != state_shape(k, v) or state.dtype != torch.float32 or not state.is_contiguous():
+        raise ValueError("state must be a contiguous fp32 tensor of state_shape(k, v)")
+    pr = _make_problem(k, k, v, chunk=chunk)
+    lib = _lib()
+    need = int(lib.kata_recurrent_state_workspace_size(ctypes.byref(pr)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=k.device)
+    with torch.cuda.device(k.device):
+        _check(lib.kata_recurrent_state(ctypes.byref(pr), _ptr(k), _ptr(v), _ptr(state),
+                                        _ptr(workspace), workspace.numel(), _stream(k.device)),
+               "kata_recurrent_state")
+    return state
+
+
+def decode(q, k, v, state, eps=1e-6, out_dtype=torch.float32, out=None, return_den=False):
+    """Advance `state` (in place) over the T tokens of q, k, v one at a time; returns o (and
+    D_t).  T = 1 is one decode step."""
+    if state.shape != state_shape(k, v) or state.dtype != torch.float32 or not state.is_contiguous():
+        raise ValueError("state must be a contiguous fp32 tensor of state_shape(k, v)")
+    o = _out(q, v, out_dtype, out)
+    den = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_den else None
+    pr = _make_problem(q, k, v, o, eps=eps, out_dtype=out_dtype)
+    with torch.cuda.device(q.device):
+        _check(_lib().kata_decode(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                  _ptr(den), _ptr(state), _stream(q.device)), "kata_decode")
+    return (o, den) if return_den else o
 
 
 def bwd_workspace_size(q, k, v):

@@ -55,6 +55,11 @@ hipError_t launch_scan_tiles(float* x, long long n_seq, long long n, long long e
 hipError_t launch_tile_sums(const float* x, long long n_seq, long long n, long long elems,
                             int tile_rows, int n_tiles, float* sums, hipStream_t st);
 
+hipError_t launch_decode(const DevProblem& pr, bool in_bf16, bool out_bf16, const void* q,
+                         const void* k, const void* v, void* o, float* den, float* state,
+                         hipStream_t st);
+hipError_t launch_state_sum(const float* src, long long n_seq, long long n, long long elems,
+                            bool tiles, float* dst, hipStream_t st);
 hipError_t launch_bwd_prep(const DevProblem& pr, bool in_bf16, const void* q, const void* k,
                            const void* v, const void* dO, float* D, float* delta,
                            hipStream_t st);

@@ -284,6 +284,78 @@ kata_status kata_chunk_state_scan(float* states, int64_t n_seq, int64_t n_chunks
                        "chunk-state scan");
 }
 
+namespace {
+// The recurrent-state build always uses the direct layout: its result is the public
+// [dv + 1][p^2] state, which the sum kernel writes from direct segment states.
+kata::ChunkPlan recurrent_plan(const kata_problem* pr) {
+  kata_problem d = *pr;
+  d.state_layout = KATA_STATE_DIRECT;
+  return kata::plan_chunked(&d, kata::chunk_fast_available());
+}
+
+kata_status check_state(const float* state) {
+  if (!state) return set_error(KATA_ERR_INVALID_ARGUMENT, "state is null");
+  if (reinterpret_cast<uintptr_t>(state) % 16)
+    return set_error(KATA_ERR_INVALID_ARGUMENT, "state is not 16-byte aligned");
+  return KATA_OK;
+}
+}  // namespace
+
+size_t kata_recurrent_state_workspace_size(const kata_problem* pr) {
+  if (kata::validate_problem(pr, Form::Chunked, nullptr) != KATA_OK) return 0;
+  return recurrent_plan(pr).states_bytes;
+}
+
+kata_status kata_recurrent_state(const kata_problem* pr, const void* k, const void* v,
+                                 float* state, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  std::string why;
+  kata_status s = kata::validate_problem(pr, Form::Chunked, &why);
+  if (s != KATA_OK) return set_error(s, why);
+  const size_t ei = kata::elem_size(pr->in_dtype);
+  if ((s = kata::validate_tensor(k, pr->sk, ei, "k", &why)) != KATA_OK) return set_error(s, why);
+  if ((s = kata::validate_tensor(v, pr->sv, ei, "v", &why)) != KATA_OK) return set_error(s, why);
+  if ((s = check_state(state)) != KATA_OK) return s;
+  const kata::ChunkPlan cp = recurrent_plan(pr);
+  if (!workspace || ws_bytes < cp.states_bytes)
+    return set_error(KATA_ERR_WORKSPACE, "workspace needs " + std::to_string(cp.states_bytes) +
+                                             " bytes, got " + std::to_string(ws_bytes));
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return set_error(KATA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  if ((s = check_device()) != KATA_OK) return s;
+  const kata::DevProblem dp = to_dev(pr);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float* states = reinterpret_cast<float*>(workspace);
+  hipError_t e;
+  {
+    Timed t(KATA_K_CHUNK_STATE, st);
+    e = cp.fast ? kata::launch_chunk_state_fast(dp, false, cp.L, cp.n_seg, k, v, states, st)
+                : kata::launch_chunk_state_generic(dp, pr->in_dtype == KATA_BF16, k, v, states,
+                                                   cp.n_chunks, st);
+  }
+  if (e != hipSuccess) return launch_status(e, "chunk-state kernel");
+  Timed t(KATA_K_STATE_SUM, st);
+  return launch_status(kata::launch_state_sum(states, cp.n_seq, cp.n_seg, cp.state_elems,
+                                              cp.fast != 0, state, st),
+                       "state sum");
+}
+
+kata_status kata_decode(const kata_problem* pr, const void* q, const void* k, const void* v,
+                        void* o, float* den, float* state, void* stream) {
+  g_last_error.clear();
+  kata_status s = check_forward_args(pr, Form::Quadratic, q, k, v, o, den);
+  if (s != KATA_OK) return s;
+  if ((s = check_state(state)) != KATA_OK) return s;
+  if ((s = check_device()) != KATA_OK) return s;
+  const kata::DevProblem dp = to_dev(pr);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Timed t(KATA_K_DECODE, st);
+  return launch_status(kata::launch_decode(dp, pr->in_dtype == KATA_BF16,
+                                           pr->out_dtype == KATA_BF16, q, k, v, o, den, state,
+                                           st),
+                       "decode");
+}
+
 size_t kata_bwd_workspace_size(const kata_problem* pr) {
   if (kata::validate_problem(pr, Form::Backward, nullptr) != KATA_OK) return 0;
   return kata::bwd_workspace_bytes(pr);

@@ -228,8 +228,44 @@ def test_valid_call_without_a_gpu_reports_device_error():
         pytest.skip("a GPU is present")
     assert _quad(_problem()) == DEVICE
     assert _lib().kata_last_error()
+    lib = _lib()
+    q, k, v, o = _fake(4)
+    st = ctypes.c_void_p(FAKE + (1 << 24))
+    # decode ignores chunk: T = 1 with chunk = 0 passes validation
+    one = _problem(T=1, chunk=0)
+    assert lib.kata_decode(ctypes.byref(one), q, k, v, o, None, st, None) == DEVICE
+    pr = _problem()
+    need = lib.kata_recurrent_state_workspace_size(ctypes.byref(pr))
+    ws = ctypes.c_void_p(FAKE + (1 << 28))
+    assert lib.kata_recurrent_state(ctypes.byref(pr), k, v, st, ws, need, None) == DEVICE
 
 
 def test_timing_end_without_begin_is_invalid():
     t = K._Times()
     assert _lib().kata_timing_end(ctypes.byref(t)) == INVALID
+
+
+def test_recurrent_entry_points_check_their_arguments():
+    lib = _lib()
+    pr = _problem()
+    q, k, v, o = _fake(4)
+    st = ctypes.c_void_p(FAKE + (1 << 24))
+    # decode: null or misaligned state, bad problem
+    assert lib.kata_decode(ctypes.byref(pr), q, k, v, o, None, None, None) == INVALID
+    assert lib.kata_decode(ctypes.byref(pr), q, k, v, o, None,
+                           ctypes.c_void_p(FAKE + 4), None) == INVALID
+    bad = _problem(p=12)
+    assert lib.kata_decode(ctypes.byref(bad), q, k, v, o, None, st, None) == UNSUPPORTED
+    # prefill: checked like the chunked form, plus the state and the workspace
+    assert lib.kata_recurrent_state_workspace_size(ctypes.byref(_problem(T=100))) == 0
+    need = lib.kata_recurrent_state_workspace_size(ctypes.byref(pr))
+    assert need >= 2 * 16 * 16 * 65 * 4
+    ws = ctypes.c_void_p(FAKE + (1 << 28))
+    assert lib.kata_recurrent_state(ctypes.byref(_problem(T=100)), k, v, st, ws, need, None) == UNSUPPORTED
+    assert lib.kata_recurrent_state(ctypes.byref(pr), k, v, None, ws, need, None) == INVALID
+    assert lib.kata_recurrent_state(ctypes.byref(pr), k, v, st, ws, need - 1, None) == WORKSPACE
+    assert lib.kata_recurrent_state(ctypes.byref(pr), k, v, st, None, need, None) == WORKSPACE
+    # the packed request does not change the prefill's (direct) workspace
+    pk = _problem()
+    pk.state_layout = 1
+    assert lib.kata_recurrent_state_workspace_size(ctypes.byref(pk)) == need

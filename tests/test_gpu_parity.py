@@ -376,60 +376,61 @@ def test_single_runtime_is_loaded():
     assert len({p for p in paths}) == 1
 
 
-# ------------------------------------------------------------ packed symmetric state ---
-# The packed layout keeps the 136 unique (i <= j) feature rows of each 256-row state, off-
-# diagonal rows doubled; it must reach the same outputs as the direct layout to tolerance.
+# ------------------------------------------------------------ state layouts ------------
+# The default (packed) layout keeps the 136 unique (i <= j) feature rows of each 256-row
+# state, off-diagonal rows doubled, and is what the tests above run; the direct layout keeps
+# all 256 rows and must reach the same outputs to tolerance.
 
 @pytest.mark.parametrize("seed", [0, 1])
-def test_packed_state_layer340m_full_size(seed):
+def test_direct_state_layer340m_full_size(seed):
     w = W.WORKLOADS[2]
     q, k, v = W.make_inputs(w, seed)
-    o = K.fwd_chunked(*_to_gpu(q, k, v), chunk=w.chunk, state="packed").cpu()
+    o = K.fwd_chunked(*_to_gpu(q, k, v), chunk=w.chunk, state="direct").cpu()
     rng = np.random.default_rng(200 + seed)
     heads = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(3)]
     _check_rows(q, k, v, o, heads, lambda T: np.arange(T), TOL[w.dtype],
-                tag=f"layer340m packed seed {seed} whole heads")
+                tag=f"layer340m direct seed {seed} whole heads")
     all_heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     _check_rows(q, k, v, o, all_heads, _rows_sampler(rng, 8), TOL[w.dtype],
-                tag=f"layer340m packed seed {seed} all heads")
+                tag=f"layer340m direct seed {seed} all heads")
 
 
 @pytest.mark.parametrize("T", [64, 448])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_packed_state_small_T_every_element(T, out_dtype):
+def test_direct_state_small_T_every_element(T, out_dtype):
     w = W.WORKLOADS[2]
     q, k, v = W.make_inputs(w, 11, T=T, B=2, H=3)
     ref, dref = O.closed_form(_np(q), _np(k), _np(v))
-    o, d = K.fwd_chunked(*_to_gpu(q, k, v), chunk=64, state="packed", out_dtype=out_dtype,
+    o, d = K.fwd_chunked(*_to_gpu(q, k, v), chunk=64, state="direct", out_dtype=out_dtype,
                          return_den=True)
     err = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
-    say(f"packed T={T} out {out_dtype}: max-abs {err:.3e}")
+    say(f"direct T={T} out {out_dtype}: max-abs {err:.3e}")
     assert err <= TOL[w.dtype]
     np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=1e-2)
 
 
 @pytest.mark.parametrize("seg", [1, 3, 32])
-def test_packed_state_segment_lengths(seg):
+def test_direct_state_segment_lengths(seg):
     w = W.WORKLOADS[2]
     q, k, v = W.make_inputs(w, 9, T=2048, B=1, H=2)
     ref, _ = O.closed_form(_np(q), _np(k), _np(v))
-    o = K.fwd_chunked(*_to_gpu(q, k, v), chunk=64, seg_chunks=seg, state="packed")
+    o = K.fwd_chunked(*_to_gpu(q, k, v), chunk=64, seg_chunks=seg, state="direct")
     err = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
-    say(f"packed seg_chunks={seg}: max-abs {err:.3e}")
+    say(f"direct seg_chunks={seg}: max-abs {err:.3e}")
     assert err <= TOL[w.dtype]
 
 
-def test_packed_state_long_context_sampled():
+def test_direct_state_long_context_sampled():
     w = W.WORKLOADS[4]
     q, k, v = W.make_inputs(w, 0)
-    o = K.fwd_chunked(*_to_gpu(q, k, v), chunk=w.chunk, state="packed")
+    o = K.fwd_chunked(*_to_gpu(q, k, v), chunk=w.chunk, state="direct")
     torch.cuda.synchronize()
     o = o.cpu()
     assert torch.isfinite(o).all()
     rng = np.random.default_rng(44)
     heads = [(0, 0), (0, int(rng.integers(1, w.H)))]
     _check_rows(q, k, v, o, heads, _rows_sampler(rng, 192), TOL[w.dtype],
-                tag="long context packed")
+                tag="long context direct")
 
 
 def test_packed_state_agrees_with_direct_and_is_causal():
@@ -453,3 +454,109 @@ def test_packed_state_request_on_the_fp32_path_computes_the_direct_form():
     a = K.fwd_chunked(q, k, v, chunk=w.chunk, state="direct")
     b = K.fwd_chunked(q, k, v, chunk=w.chunk, state="packed")
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------ recurrent form -----------
+# Prefill builds the state (S, Z) after a prefix; decode advances it token by token.  The
+# public state layout is [B][H][dv + 1][p^2]: row d < dv holds S[(i, j), d], row dv holds Z.
+
+def _oracle_state(k, v):
+    """(S, Z) after all tokens, from the oracle's chunk states with one chunk, in the
+    public layout; and the bound sum_s |phi_f(k_s)| |v_s,d| (Z: sum_s |k_i k_j|) that the
+    bf16 rounding of phi(k) on the MFMA path is measured against."""
+    kn, vn = _np(k), _np(v)
+    B, T, H, p = kn.shape
+    dv = vn.shape[-1]
+    dS, dZ = O.chunk_states(kn, vn, T)
+    st = np.empty((B, H, dv + 1, p * p))
+    st[:, :, :dv] = np.swapaxes(dS[:, :, 0], -1, -2)
+    st[:, :, dv] = dZ[:, :, 0].reshape(B, H, p * p)
+    aS, aZ = O.chunk_states(np.abs(kn), np.abs(vn), T)
+    mag = np.empty_like(st)
+    mag[:, :, :dv] = np.swapaxes(aS[:, :, 0], -1, -2)
+    mag[:, :, dv] = aZ[:, :, 0].reshape(B, H, p * p)
+    return st, mag
+
+
+@pytest.mark.parametrize("case", ["tiny_fp32", "layer340m_mfma", "p32_bf16", "p8_dv64_fp32"])
+def test_recurrent_state_matches_oracle(case):
+    if case == "tiny_fp32":
+        w, T, B, H, C, rel = W.WORKLOADS[1], 256, 1, 1, 32, 1e-5
+    elif case == "layer340m_mfma":
+        w, T, B, H, C, rel = W.WORKLOADS[2], 1024, 2, 3, 64, 2.0 ** -8
+    elif case == "p32_bf16":
+        w, T, B, H, C, rel = W.WORKLOADS[3], 256, 1, 2, 64, 1e-5
+    else:
+        w, T, B, H, C, rel = W.WORKLOADS[1], 128, 1, 2, 32, 1e-5
+    q, k, v = W.make_inputs(w, 21, T=T, B=B, H=H)
+    if case == "p8_dv64_fp32":
+        v = torch.randn((B, T, H, 64), generator=torch.Generator().manual_seed(5))
+    want, mag = _oracle_state(k, v)
+    kg, vg = _to_gpu(k, v)
+    got = K.recurrent_state(kg, vg, chunk=C).cpu().double().numpy()
+    # bf16 phi(k) (MFMA path): each product is off by at most 2^-9 of |phi_f(k) v_d|, bound
+    # 2^-8 with the fp32 accumulation; fp32 paths: sums of C chunk terms then of T / C chunk
+    # states in fp32, at most (C + T / C) 2^-24 < 1e-5 of the magnitude sum
+    err = np.abs(got - want)
+    lim = rel * mag + 1e-6
+    say(f"recurrent state {case}: max-abs {err.max():.3e}, max err/bound {(err / lim).max():.3f}")
+    assert np.all(err <= lim)
+
+
+@pytest.mark.parametrize("case", ["tiny_fp32", "p32_bf16", "p8_dv64_fp32"])
+def test_decode_from_zero_state_matches_closed_form(case):
+    if case == "tiny_fp32":
+        w, T, B, H = W.WORKLOADS[1], 256, 1, 1
+    elif case == "p32_bf16":
+        w, T, B, H = W.WORKLOADS[3], 96, 1, 2
+    else:
+        w, T, B, H = W.WORKLOADS[1], 64, 2, 2
+    q, k, v = W.make_inputs(w, 22, T=T, B=B, H=H)
+    if case == "p8_dv64_fp32":
+        v = torch.randn((B, T, H, 64), generator=torch.Generator().manual_seed(6))
+    ref, dref = O.closed_form(_np(q), _np(k), _np(v))
+    qg, kg, vg = _to_gpu(q, k, v)
+    state = torch.zeros(K.state_shape(kg, vg), dtype=torch.float32, device=DEV)
+    o, d = K.decode(qg, kg, vg, state, return_den=True)        # all T tokens in one call
+    err = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
+    say(f"decode {case}: max-abs {err:.3e}")
+    assert err <= TOL[w.dtype]
+    np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=1e-5)
+    want, _ = _oracle_state(k, v)
+    assert float(np.abs(state.cpu().double().numpy() - want).max()) <= 1e-3
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_prefill_then_decode_steps_match_closed_form(out_dtype):
+    # the 340M-layer recipe: prefill 512 tokens (MFMA state kernel), then 8 single-token steps
+    w = W.WORKLOADS[2]
+    T0, n = 512, 8
+    q, k, v = W.make_inputs(w, 23, T=T0 + n, B=2, H=4)
+    qg, kg, vg = _to_gpu(q, k, v)
+    state = K.recurrent_state(kg[:, :T0].contiguous(), vg[:, :T0].contiguous())
+    outs = []
+    for t in range(T0, T0 + n):
+        sl = slice(t, t + 1)
+        outs.append(K.decode(qg[:, sl].contiguous(), kg[:, sl].contiguous(),
+                             vg[:, sl].contiguous(), state, out_dtype=out_dtype))
+    o = torch.cat(outs, dim=1).cpu()
+    rows = np.arange(T0, T0 + n)
+    for b in range(2):
+        for h in range(4):
+            ref, _ = O.closed_form_rows(_np(q[b, :, h]), _np(k[b, :, h]), _np(v[b, :, h]), rows)
+            err = float(np.abs(o[b, :, h].double().numpy() - ref).max())
+            assert err <= TOL[w.dtype], (b, h, err)
+    want, mag = _oracle_state(k, v)
+    err = np.abs(state.cpu().double().numpy() - want)
+    assert np.all(err <= 2.0 ** -8 * mag + 1e-5)
+
+
+def test_decode_bf16_output_is_the_rounded_fp32_output_and_state_is_the_same():
+    w = W.WORKLOADS[2]
+    q, k, v = _to_gpu(*W.make_inputs(w, 24, T=64, B=2, H=4))
+    s1 = torch.zeros(K.state_shape(k, v), dtype=torch.float32, device=DEV)
+    s2 = s1.clone()
+    o32 = K.decode(q, k, v, s1)
+    o16 = K.decode(q, k, v, s2, out_dtype=torch.bfloat16)
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(s1, s2)
