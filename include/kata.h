@@ -182,6 +182,26 @@ kata_status kata_bwd(const kata_problem* pr, const void* q, const void* k, const
                      const void* dO, void* dq, void* dk, void* dv, void* workspace,
                      size_t ws_bytes, void* stream);
 
+/* Bytes of workspace kata_bwd_chunked needs (0 for an invalid problem). */
+size_t kata_bwd_chunked_workspace_size(const kata_problem* pr);
+
+/* The same gradients as kata_bwd in O(T): the chunked forward's exclusive prefix states give
+ * the part of dq from earlier chunks,
+ *     dq_t += 2 [mat(S_{<c} g_t) - e_t Z_{<c}] q_t,   g_t = dO_t / D_t, e_t = delta_t / D_t,
+ * and a suffix scan over chunks of R = sum vec(q q^T) g^T and r = sum e vec(q q^T) (the
+ * prefix scan run over the chunk states stored in reverse order) gives the part of dk and dv
+ * from later chunks,
+ *     dk_s += 2 [mat(R_{>c} v_s) - mat(r_{>c})] k_s,   dv_s += R_{>c}^T vec(k_s k_s^T);
+ * the terms inside a chunk are its causal tile.  Source: derived from the chunked form of
+ * gist.science section 2.3 (states, associative scan) and the closed form above; the pages
+ * print no backward.  All arithmetic is fp32 (the forward pass inside included).
+ * Arguments as kata_bwd; the problem is checked as for kata_fwd_chunked (T % chunk == 0).
+ * The workspace holds one fp32 state of p^2 (dv + 1) floats per chunk and (b, h), the scan's
+ * workspace, and g_t, e_t.  Errors: as kata_bwd. */
+kata_status kata_bwd_chunked(const kata_problem* pr, const void* q, const void* k,
+                             const void* v, const void* dO, void* dq, void* dk, void* dv,
+                             void* workspace, size_t ws_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* kata_status_string(kata_status s);
 

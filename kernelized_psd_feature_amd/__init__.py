@@ -85,6 +85,8 @@ def _lib():
             "kata_recurrent_state": (I32, [P, VP, VP, VP, VP, SZ, VP]),
             "kata_decode": (I32, [P, VP, VP, VP, VP, VP, VP, VP]),
             "kata_bwd_workspace_size": (SZ, [P]),
+            "kata_bwd_chunked_workspace_size": (SZ, [P]),
+            "kata_bwd_chunked": (I32, [P, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
             "kata_bwd": (I32, [P, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]),
             "kata_status_string": (ctypes.c_char_p, [I32]),
             "kata_last_error": (ctypes.c_char_p, []),
@@ -282,8 +284,11 @@ def bwd_workspace_size(q, k, v):
     return int(_lib().kata_bwd_workspace_size(ctypes.byref(pr)))
 
 
-def bwd(q, k, v, dO, eps=1e-6, workspace=None):
-    """fp32 gradients (dq, dk, dv) of sum(dO * o), o the forward output."""
+def bwd(q, k, v, dO, eps=1e-6, workspace=None, chunk=None):
+    """fp32 gradients (dq, dk, dv) of sum(dO * o), o the forward output.
+
+    chunk=None: the flash-style O(T^2) backward; chunk=C: the chunked O(T) backward (forward
+    prefix states for dq, a reverse scan of query states for dk and dv; T % C == 0)."""
     if dO.shape != v.shape or dO.dtype != q.dtype:
         raise ValueError("dO must match v's shape and q's dtype")
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
@@ -292,15 +297,17 @@ def bwd(q, k, v, dO, eps=1e-6, workspace=None):
     # gradient outputs share the strides of their inputs
     qs, ks, vs = (q, k, v) if q.is_contiguous() and k.is_contiguous() and v.is_contiguous() \
         else (q.contiguous(), k.contiguous(), v.contiguous())
-    pr = _make_problem(qs, ks, vs, dO=dO, eps=eps)
+    pr = _make_problem(qs, ks, vs, dO=dO, eps=eps, chunk=chunk or 0)
     lib = _lib()
-    need = int(lib.kata_bwd_workspace_size(ctypes.byref(pr)))
+    size_fn, fn, name = ((lib.kata_bwd_workspace_size, lib.kata_bwd, "kata_bwd") if chunk is None
+                         else (lib.kata_bwd_chunked_workspace_size, lib.kata_bwd_chunked,
+                               "kata_bwd_chunked"))
+    need = int(size_fn(ctypes.byref(pr)))
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     with torch.cuda.device(q.device):
-        _check(lib.kata_bwd(ctypes.byref(pr), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(dO),
-                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
-                            _stream(q.device)), "kata_bwd")
+        _check(fn(ctypes.byref(pr), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(dO), _ptr(dq), _ptr(dk),
+                  _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q.device)), name)
     return dq, dk, dv
 
 

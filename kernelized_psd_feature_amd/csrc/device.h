@@ -60,6 +60,18 @@ hipError_t launch_decode(const DevProblem& pr, bool in_bf16, bool out_bf16, cons
                          hipStream_t st);
 hipError_t launch_state_sum(const float* src, long long n_seq, long long n, long long elems,
                             bool tiles, float* dst, hipStream_t st);
+hipError_t launch_bwd_chunk_prep(const DevProblem& pr, bool in_bf16, const void* dO, float* g,
+                                 float* e, hipStream_t st);
+hipError_t launch_bwd_chunk_dq(const DevProblem& pr, bool in_bf16, const void* q, const void* k,
+                               const void* v, const float* g, const float* e,
+                               const float* states, int n_chunks, float* dq, hipStream_t st);
+hipError_t launch_bwd_rev_state(const DevProblem& pr, bool in_bf16, const void* q,
+                                const float* g, const float* e, float* states, int n_chunks,
+                                hipStream_t st);
+hipError_t launch_bwd_chunk_dkdv(const DevProblem& pr, bool in_bf16, const void* q,
+                                 const void* k, const void* v, const float* g, const float* e,
+                                 const float* states, int n_chunks, float* dk, float* dv,
+                                 hipStream_t st);
 hipError_t launch_bwd_prep(const DevProblem& pr, bool in_bf16, const void* q, const void* k,
                            const void* v, const void* dO, float* D, float* delta,
                            hipStream_t st);

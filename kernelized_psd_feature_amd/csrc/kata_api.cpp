@@ -402,6 +402,93 @@ kata_status kata_bwd(const kata_problem* pr, const void* q, const void* k, const
   return launch_status(e, "backward");
 }
 
+namespace {
+struct BwdChunkedLayout {
+  int64_t n_seq = 0, n_chunks = 0, elems = 0;
+  size_t states = 0, scan = 0, g = 0, e = 0, total = 0;
+};
+
+BwdChunkedLayout bwd_chunked_layout(const kata_problem* pr) {
+  auto r256 = [](size_t b) { return (b + 255) & ~size_t(255); };
+  BwdChunkedLayout L;
+  L.n_seq = int64_t(pr->B) * pr->H;
+  L.n_chunks = pr->T / pr->chunk;
+  L.elems = int64_t(pr->p) * pr->p * (pr->dv + 1);
+  const size_t tokens = size_t(pr->B) * pr->T * pr->H;
+  L.states = r256(size_t(L.n_seq) * L.n_chunks * L.elems * 4);
+  L.scan = r256(kata::plan_scan(L.n_seq, L.n_chunks, L.elems).ws_bytes);
+  L.g = r256(tokens * pr->dv * 4);
+  L.e = r256(tokens * 4);
+  L.total = L.states + L.scan + L.g + L.e;
+  return L;
+}
+}  // namespace
+
+size_t kata_bwd_chunked_workspace_size(const kata_problem* pr) {
+  if (kata::validate_problem(pr, Form::Chunked, nullptr) != KATA_OK) return 0;
+  return bwd_chunked_layout(pr).total;
+}
+
+kata_status kata_bwd_chunked(const kata_problem* pr, const void* q, const void* k,
+                             const void* v, const void* dO, void* dq, void* dk, void* dv,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  std::string why;
+  kata_status s = kata::validate_problem(pr, Form::Chunked, &why);
+  if (s != KATA_OK) return set_error(s, why);
+  const size_t ei = kata::elem_size(pr->in_dtype);
+  struct {
+    const void* p;
+    const int64_t* st;
+    size_t es;
+    const char* name;
+  } ts[] = {{q, pr->sq, ei, "q"},  {k, pr->sk, ei, "k"},  {v, pr->sv, ei, "v"},
+            {dO, pr->sdo, ei, "dO"}, {dq, pr->sq, 4, "dq"}, {dk, pr->sk, 4, "dk"},
+            {dv, pr->sv, 4, "dv"}};
+  for (auto& x : ts)
+    if ((s = kata::validate_tensor(x.p, x.st, x.es, x.name, &why)) != KATA_OK)
+      return set_error(s, why);
+  const BwdChunkedLayout L = bwd_chunked_layout(pr);
+  if (!workspace || ws_bytes < L.total)
+    return set_error(KATA_ERR_WORKSPACE, "workspace needs " + std::to_string(L.total) +
+                                             " bytes, got " + std::to_string(ws_bytes));
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return set_error(KATA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  if ((s = check_device()) != KATA_OK) return s;
+  kata::DevProblem dp = to_dev(pr);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const bool in_bf16 = pr->in_dtype == KATA_BF16;
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* states = reinterpret_cast<float*>(ws);
+  char* scan_ws = ws + L.states;
+  float* g = reinterpret_cast<float*>(ws + L.states + L.scan);
+  float* e = reinterpret_cast<float*>(ws + L.states + L.scan + L.g);
+  const int nc = int(L.n_chunks);
+  // fp32 forward: o (into g) and D_t (into e), leaving the exclusive prefix states
+  kata::DevProblem dpo = dp;
+  dpo.so[0] = int64_t(pr->T) * pr->H * pr->dv;
+  dpo.so[1] = int64_t(pr->H) * pr->dv;
+  dpo.so[2] = pr->dv;
+  Timed t(KATA_K_BWD, st);
+  hipError_t err = kata::launch_chunk_state_generic(dp, in_bf16, k, v, states, nc, st);
+  if (err == hipSuccess)
+    err = run_scan(states, L.n_seq, L.n_chunks, L.elems, 1, nullptr, scan_ws, st);
+  if (err == hipSuccess)
+    err = kata::launch_chunk_output_generic(dpo, in_bf16, false, q, k, v, g, e, states, nc, st);
+  if (err == hipSuccess) err = kata::launch_bwd_chunk_prep(dp, in_bf16, dO, g, e, st);
+  if (err == hipSuccess)
+    err = kata::launch_bwd_chunk_dq(dp, in_bf16, q, k, v, g, e, states, nc,
+                                    static_cast<float*>(dq), st);
+  // reverse chunk states of the queries, suffix sums by the same exclusive scan
+  if (err == hipSuccess) err = kata::launch_bwd_rev_state(dp, in_bf16, q, g, e, states, nc, st);
+  if (err == hipSuccess)
+    err = run_scan(states, L.n_seq, L.n_chunks, L.elems, 1, nullptr, scan_ws, st);
+  if (err == hipSuccess)
+    err = kata::launch_bwd_chunk_dkdv(dp, in_bf16, q, k, v, g, e, states, nc,
+                                      static_cast<float*>(dk), static_cast<float*>(dv), st);
+  return launch_status(err, "chunked backward");
+}
+
 kata_status kata_timing_begin(void) {
   g_last_error.clear();
   for (auto& r : g_timing.recs) {

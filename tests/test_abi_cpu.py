@@ -269,3 +269,20 @@ def test_recurrent_entry_points_check_their_arguments():
     pk = _problem()
     pk.state_layout = 1
     assert lib.kata_recurrent_state_workspace_size(ctypes.byref(pk)) == need
+
+
+def test_chunked_backward_checks_its_arguments():
+    lib = _lib()
+    pr = _problem()
+    t = _fake(7)
+    need = lib.kata_bwd_chunked_workspace_size(ctypes.byref(pr))
+    # one fp32 state per chunk and (b, h), plus g (dv floats) and e per token
+    assert need >= 2 * 2 * 16 * 16 * 65 * 4 + 128 * 2 * 65 * 4
+    assert lib.kata_bwd_chunked_workspace_size(ctypes.byref(_problem(T=100))) == 0
+    ws = ctypes.c_void_p(FAKE + (1 << 33))
+    assert lib.kata_bwd_chunked(ctypes.byref(_problem(T=100)), *t, ws, need, None) == UNSUPPORTED
+    assert lib.kata_bwd_chunked(ctypes.byref(pr), *t, ws, need - 1, None) == WORKSPACE
+    assert lib.kata_bwd_chunked(ctypes.byref(pr), *t, None, need, None) == WORKSPACE
+    t2 = list(t)
+    t2[4] = None                                    # dq missing
+    assert lib.kata_bwd_chunked(ctypes.byref(pr), *t2, ws, need, None) == INVALID

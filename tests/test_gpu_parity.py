@@ -224,6 +224,111 @@ def test_backward_matches_finite_differences_tiny_fp32():
         assert err <= 1e-4 * scale
 
 
+# ------------------------------------------------------------ chunked backward ---------
+# The O(T) backward: forward prefix states for dq, a reverse scan of query states for dk, dv.
+
+def _bwd_errs(got, refs):
+    return [float(np.abs(g.cpu().double().numpy() - r).max()) for g, r in zip(got, refs)]
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_chunked_backward_training_slice(chunk):
+    w = W.WORKLOADS[5]
+    B, H = (8, 16) if chunk == 64 else (2, 4)
+    q, k, v, dO = W.make_inputs(w, 0, T=256, B=B, H=H, with_dO=True)
+    refs = O.backward(_np(q), _np(k), _np(v), _np(dO))
+    got = K.bwd(*_to_gpu(q, k, v, dO), chunk=chunk)
+    errs = _bwd_errs(got, refs)
+    say(f"chunked backward C={chunk} T=256: dq/dk/dv max-abs {errs}, "
+        f"ref max |g| {[float(np.abs(r).max()) for r in refs]}")
+    assert max(errs) <= 1e-2
+
+
+def test_chunked_backward_full_T_sampled_heads():
+    w = W.WORKLOADS[5]
+    q, k, v, dO = W.make_inputs(w, 1, with_dO=True)
+    got = K.bwd(*_to_gpu(q, k, v, dO), chunk=64)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(55)
+    for b, h in [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(2)]:
+        sl = lambda x: _np(x[b:b + 1, :, h:h + 1])
+        refs = O.backward(sl(q), sl(k), sl(v), sl(dO))
+        for name, g, r in zip(("dq", "dk", "dv"), got, refs):
+            err = float(np.abs(g[b:b + 1, :, h:h + 1].cpu().double().numpy() - r).max())
+            say(f"chunked full-T backward head ({b},{h}) {name}: max-abs {err:.3e}")
+            assert err <= 1e-2
+
+
+@pytest.mark.parametrize("case", ["p32_bf16", "p8_dv64_fp32", "tiny_fp32"])
+def test_chunked_backward_other_shapes(case):
+    if case == "p32_bf16":
+        w, T, B, H, C, tol = W.WORKLOADS[3], 256, 1, 2, 64, 1e-2
+    elif case == "p8_dv64_fp32":
+        w, T, B, H, C, tol = W.WORKLOADS[1], 128, 2, 2, 32, 1e-4
+    else:
+        w, T, B, H, C, tol = W.WORKLOADS[1], 256, 1, 1, 32, 1e-4
+    q, k, v, dO = W.make_inputs(w, 3, T=T, B=B, H=H, with_dO=True)
+    if case == "p8_dv64_fp32":
+        gen = torch.Generator().manual_seed(9)
+        v = torch.randn((B, T, H, 64), generator=gen)
+        dO = torch.randn((B, T, H, 64), generator=gen)
+    refs = O.backward(_np(q), _np(k), _np(v), _np(dO))
+    errs = _bwd_errs(K.bwd(*_to_gpu(q, k, v, dO), chunk=C), refs)
+    scale = max(1.0, max(float(np.abs(r).max()) for r in refs))
+    say(f"chunked backward {case}: max-abs {errs} (ref scale {scale:.2f})")
+    assert max(errs) <= tol * (scale if tol < 1e-2 else 1.0)
+
+
+def test_chunked_backward_matches_finite_differences_tiny_fp32():
+    # two chunks of 16, so the inter-chunk (prefix and suffix state) terms are exercised
+    rng = np.random.default_rng(31)
+    B, T, H, p, dv = 1, 32, 2, 8, 16
+    q = rng.standard_normal((B, T, H, p))
+    k = rng.standard_normal((B, T, H, p))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, dv))
+    dO = rng.standard_normal((B, T, H, dv))
+    eps = 1e-2
+    tq, tk, tv, tg = (torch.tensor(x, dtype=torch.float32) for x in (q, k, v, dO))
+    q, k, v, dO = (x.double().numpy() for x in (tq, tk, tv, tg))
+    grads = K.bwd(*_to_gpu(tq, tk, tv, tg), eps=eps, chunk=16)
+
+    def loss(qq, kk, vv):
+        o, _ = O.closed_form(qq, kk, vv, eps)
+        return float((o * dO).sum())
+
+    h = 1e-6
+    for name, x, g in (("q", q, grads[0]), ("k", k, grads[1]), ("v", v, grads[2])):
+        g = g.cpu().double().numpy()
+        num = np.empty_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (loss(args_p["q"], args_p["k"], args_p["v"])
+                        - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+        scale = max(1.0, float(np.abs(num).max()))
+        err = float(np.abs(g - num).max())
+        say(f"chunked backward finite differences d{name}: max-abs {err:.3e} (scale {scale:.2f})")
+        assert err <= 1e-4 * scale
+
+
+def test_chunked_and_flash_backward_agree():
+    w = W.WORKLOADS[2]
+    q, k, v = W.make_inputs(w, 13, T=1024, B=2, H=4)
+    dO = torch.randn(v.shape, generator=torch.Generator().manual_seed(13)).to(v.dtype)
+    qg, kg, vg, gg = _to_gpu(q, k, v, dO)
+    a = K.bwd(qg, kg, vg, gg)
+    b = K.bwd(qg, kg, vg, gg, chunk=64)
+    for name, x, y in zip(("dq", "dk", "dv"), a, b):
+        d = float((x - y).abs().max())
+        say(f"flash vs chunked backward {name}: max-abs {d:.3e} (max |g| {float(x.abs().max()):.2e})")
+        assert d <= 1e-2
+
+
 # ------------------------------------------------------------ prefix scan --------------
 
 @pytest.mark.parametrize("n", [1, 2, 7, 64, 2048, 5000])
