@@ -16,13 +16,21 @@ Sources (page title, then section):
            coordinates, feature-value state n*d_v), the bullet on the chunk recurrence.
   [Review] "Paper Review: Kernelized Linear Attention" on romaanj.github.io, Validation and
            Results paragraphs (exact O(T) chunked-state form; scan depth O(log(T/C))).
-  [README] the KATA GitHub README (ayghri/KATA): the direct kernel call takes (B,T,H,D) tensors.
+  [README] the KATA GitHub README (ayghri/KATA): the direct kernel call takes (B,T,H,D) tensors,
+           and its usage example passes a factor count (num_groups) to the concatenated-PSD
+           ("concat-SPD") kernel.
+  KATA-Mg: [Gist 2.3] the variants bullet (several PSD factors); [AIsum state-size bullet]
+           state d(d/g + 1)/2 * d_v, the full map at g = 1; [Review] Comparison paragraph
+           (two 32-dimensional factors at head dimension 64, 135,168 state entries).
 
 The computation (every array here is float64):
   feature(u)  = vec(u u^T), row-major index i*p + j                       [Gist 2.2]
   a[t,s]      = <feature(q_t), feature(k_s)> = (q_t . k_s)^2,  s <= t      [Gist 2.2; AIsum]
   D_t         = eps + sum_{s<=t} a[t,s]                                    [AIsum gate bullet]
   o_t         = sum_{s<=t} a[t,s] v_s / D_t                                [Gist 2.1; AIsum]
+KATA-Mg (groups = g): the p coordinates form g consecutive groups of p/g; the feature is the
+concatenation over groups of vec(u^(j) u^(j)^T), so a[t,s] = sum_j (q_t^(j) . k_s^(j))^2 with
+one shared denominator.  groups = 1 is the computation above.
 Readings where the pages are silent: eps is added once, outside the sum, eps = 1e-6; the
 diagonal s = t is included (the gate's beta_t weights the current value v_t); no scaling or
 normalization of q, k inside the operation; chunk c covers tokens [cC, (c+1)C) and T % C == 0.
@@ -45,6 +53,11 @@ Pins (each function is checked against something other than itself in tests/test
                     equal to closed_form for every C dividing T; the special cases.
   gate_terms        alpha + beta == 1 and o_t == alpha_t * ohat_{t-1} + beta_t * v_t.
   backward          central finite differences of closed_form (fp64).
+  groups (KATA-Mg)  groups = p reduces to the positive-orthant feature u*u (a closed form of
+                    its own); every grouped output is the sum of per-group ungrouped numerators
+                    over the sum of per-group denominators; integer identity for the grouped
+                    feature; packed widths against the printed state sizes; every form agrees
+                    with the grouped closed form; backward against finite differences.
 """
 
 import numpy as np
@@ -61,6 +74,8 @@ __all__ = [
     "gate_terms",
     "backward",
     "state_elems",
+    "group_mask",
+    "packed_width",
 ]
 
 EPS = 1e-6
@@ -78,15 +93,53 @@ def _heads(x):
             yield b, h, x[b, :, h, :]
 
 
-def feature(u):
+def _group_slices(p, groups):
+    if groups < 1 or p % groups:
+        raise ValueError("groups must divide p")
+    w = p // groups
+    return [slice(j * w, (j + 1) * w) for j in range(groups)]
+
+
+def feature(u, groups=1):
     """Rank-one PSD feature psi(u) = u u^T, flattened row-major: index i*p + j.
 
     [Gist 2.2] psi(u) = u u^T; [AIsum, squaring bullet] its inner product squares the raw
     inner product.  Works on any leading shape: (..., p) -> (..., p*p).
+    groups = g (KATA-Mg [Gist 2.3 variants; README concat-SPD]): the concatenation over the g
+    groups of consecutive coordinates of vec(u^(j) u^(j)^T), width p^2 / g.
     """
     u = _f64(u)
     p = u.shape[-1]
-    return (u[..., :, None] * u[..., None, :]).reshape(*u.shape[:-1], p * p)
+    if groups == 1:
+        return (u[..., :, None] * u[..., None, :]).reshape(*u.shape[:-1], p * p)
+    parts = [(u[..., sl, None] * u[..., None, sl]).reshape(*u.shape[:-1], -1)
+             for sl in _group_slices(p, groups)]
+    return np.concatenate(parts, axis=-1)
+
+
+def group_mask(p, groups=1):
+    """Boolean (p, p): True where coordinates i and j lie in the same group."""
+    g = np.empty(p, dtype=np.int64)
+    for j, sl in enumerate(_group_slices(p, groups)):
+        g[sl] = j
+    return g[:, None] == g[None, :]
+
+
+def packed_width(p, groups=1):
+    """Unique coordinates of the (grouped) feature: the pairs i <= j within one group,
+    counted one by one.  [AIsum state-size bullet: d(d+1)/2 packed coordinates; KATA-Mg
+    state d(d/g + 1)/2 * d_v.]"""
+    m = group_mask(p, groups)
+    return int(sum(1 for i in range(p) for j in range(i, p) if m[i, j]))
+
+
+def _scores(Qb, Kb, groups):
+    """a[t,s] = sum_j (q_t^(j) . k_s^(j))^2 for the rows of Qb against the rows of Kb."""
+    a = 0.0
+    for sl in _group_slices(Qb.shape[-1], groups):
+        sc = Qb[:, sl] @ Kb[:, sl].T                  # q_t . k_s within one group
+        a = a + sc * sc                               # (q_t . k_s)^2  [Gist 2.2]
+    return a
 
 
 def state_elems(p, dv):
@@ -107,21 +160,19 @@ def _masked_sum(a, V, mask):
     return prod.sum(axis=1)
 
 
-def _closed_form_head(Q, K, V, eps, block):
+def _closed_form_head(Q, K, V, eps, block, groups):
     T = Q.shape[0]
     o = np.empty((T, V.shape[1]))
     den = np.empty(T)
     for i0 in range(0, T, block):
         i1 = min(T, i0 + block)
         # keys before the block are in every row's past: plain products
-        sc = Q[i0:i1] @ K[:i0].T                      # q_t . k_s
-        a = sc * sc                                   # (q_t . k_s)^2  [Gist 2.2]
+        a = _scores(Q[i0:i1], K[:i0], groups)
         num = a @ V[:i0]
         asum = a.sum(axis=1)
         # keys inside the block: causal, diagonal included, by selection
         mask = np.arange(i0, i1)[None, :] <= np.arange(i0, i1)[:, None]
-        sd = Q[i0:i1] @ K[i0:i1].T
-        ad = np.where(mask, sd * sd, 0.0)
+        ad = np.where(mask, _scores(Q[i0:i1], K[i0:i1], groups), 0.0)
         num = num + _masked_sum(ad, V[i0:i1], mask)
         d = eps + (asum + ad.sum(axis=1))             # D_t = eps + sum a  [AIsum gate]
         o[i0:i1] = num / d[:, None]                   # o_t = N_t / D_t    [Gist 2.1]
@@ -129,23 +180,25 @@ def _closed_form_head(Q, K, V, eps, block):
     return o, den
 
 
-def closed_form(q, k, v, eps=EPS, block=512):
+def closed_form(q, k, v, eps=EPS, block=512, groups=1):
     """o_t = sum_{s<=t} (q_t.k_s)^2 v_s / (eps + sum_{s<=t} (q_t.k_s)^2), per (b, h).
 
     Inputs (B,T,H,p), (B,T,H,p), (B,T,H,d_v); returns (o (B,T,H,d_v), D (B,T,H)), float64.
     Brute force over query blocks of `block` rows; masked pairs are selected away, never
     multiplied by zero, so a non-finite value in a future token cannot reach o_t.
+    groups = g: the KATA-Mg score sum_j (q_t^(j) . k_s^(j))^2.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, H, _ = q.shape
     o = np.empty((B, T, H, v.shape[-1]))
     den = np.empty((B, T, H))
     for b, h, Q in _heads(q):
-        o[b, :, h], den[b, :, h] = _closed_form_head(Q, k[b, :, h], v[b, :, h], eps, block)
+        o[b, :, h], den[b, :, h] = _closed_form_head(Q, k[b, :, h], v[b, :, h], eps, block,
+                                                     groups)
     return o, den
 
 
-def closed_form_rows(q, k, v, rows, eps=EPS, block=256):
+def closed_form_rows(q, k, v, rows, eps=EPS, block=256, groups=1):
     """The closed form for selected rows of ONE head.
 
     q, k: (T, p); v: (T, d_v); rows: 1-D int array of token indices.  Returns
@@ -161,13 +214,11 @@ def closed_form_rows(q, k, v, rows, eps=EPS, block=256):
         sel = order[j0:j0 + block]
         t = rows[sel]
         s0 = int(t.min())                             # keys < s0 are past for every row
-        sc = Q[t] @ K[:s0].T
-        a = sc * sc
+        a = _scores(Q[t], K[:s0], groups)
         num = a @ V[:s0]
         asum = a.sum(axis=1)
         for r, tr in enumerate(t):                    # the rest: keys s0..t of this row only
-            st = Q[tr] @ K[s0:tr + 1].T
-            at = st * st
+            at = _scores(Q[tr:tr + 1], K[s0:tr + 1], groups)[0]
             num[r] += at @ V[s0:tr + 1]
             asum[r] += at.sum()
         d = eps + asum
@@ -180,27 +231,29 @@ def closed_form_rows(q, k, v, rows, eps=EPS, block=256):
 # Recurrent form: the fixed-size state updated token by token.
 # ----------------------------------------------------------------------------------------
 
-def recurrent(q, k, v, eps=EPS):
+def recurrent(q, k, v, eps=EPS, groups=1):
     """S_t = S_{t-1} + feature(k_t) v_t^T,  Z_t = Z_{t-1} + k_t k_t^T,
     o_t = S_t^T feature(q_t) / (eps + q_t^T Z_t q_t).
 
     [Gist 2.3 / AIsum: linear attention as a recurrence on a fixed-size state; the update is
-    additive and commutative].  Token-by-token Python loop: small inputs only.
+    additive and commutative].  Token-by-token Python loop: small inputs only.  groups = g:
+    the grouped feature, and Z keeps only its within-group entries.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, H, p = q.shape
     dv = v.shape[-1]
+    gm = group_mask(p, groups)
     o = np.empty((B, T, H, dv))
     den = np.empty((B, T, H))
     for b, h, Q in _heads(q):
         K, V = k[b, :, h], v[b, :, h]
-        S = np.zeros((p * p, dv))
+        S = np.zeros((p * p // groups, dv))
         Z = np.zeros((p, p))
         for t in range(T):
-            S += np.outer(feature(K[t]), V[t])
-            Z += np.outer(K[t], K[t])
+            S += np.outer(feature(K[t], groups), V[t])
+            Z += np.where(gm, np.outer(K[t], K[t]), 0.0)
             d = eps + Q[t] @ Z @ Q[t]
-            o[b, t, h] = feature(Q[t]) @ S / d
+            o[b, t, h] = feature(Q[t], groups) @ S / d
             den[b, t, h] = d
     return o, den
 
@@ -209,13 +262,14 @@ def recurrent(q, k, v, eps=EPS):
 # Chunked-state form: per-chunk states, exclusive prefix scan, intra-chunk block.
 # ----------------------------------------------------------------------------------------
 
-def chunk_states(k, v, C):
+def chunk_states(k, v, C, groups=1):
     """Per-chunk states of every head.
 
     dS_c = sum_{s in chunk c} feature(k_s) v_s^T   (p^2 x d_v)
     dZ_c = sum_{s in chunk c} k_s k_s^T            (p x p)
     [Gist 2.3: chunked parallelism; AIsum chunk-recurrence bullet: inter-chunk cost
-    O(C n_psi d_v)].  Returns dS (B,H,Nc,p*p,d_v) and dZ (B,H,Nc,p,p).
+    O(C n_psi d_v)].  Returns dS (B,H,Nc,p*p,d_v) and dZ (B,H,Nc,p,p).  groups = g: the
+    grouped feature (p^2/g rows) and the within-group entries of dZ.
     """
     k, v = _f64(k), _f64(v)
     B, T, H, p = k.shape
@@ -223,14 +277,15 @@ def chunk_states(k, v, C):
     if T % C:
         raise ValueError("T must be a multiple of the chunk size")
     nc = T // C
-    dS = np.empty((B, H, nc, p * p, dv))
+    gm = group_mask(p, groups)
+    dS = np.empty((B, H, nc, p * p // groups, dv))
     dZ = np.empty((B, H, nc, p, p))
     for b, h, K in _heads(k):
         V = v[b, :, h]
         for c in range(nc):
             Kc, Vc = K[c * C:(c + 1) * C], V[c * C:(c + 1) * C]
-            dS[b, h, c] = feature(Kc).T @ Vc
-            dZ[b, h, c] = Kc.T @ Kc
+            dS[b, h, c] = feature(Kc, groups).T @ Vc
+            dZ[b, h, c] = np.where(gm, Kc.T @ Kc, 0.0)
     return dS, dZ
 
 
@@ -251,7 +306,7 @@ def exclusive_scan(x, axis=2):
     return np.moveaxis(out, 0, axis), run
 
 
-def chunked(q, k, v, C, eps=EPS):
+def chunked(q, k, v, C, eps=EPS, groups=1):
     """Exact O(T) chunked-state form.  For t in chunk c:
 
     num_t = feature(q_t)^T S_{<c} + sum_{s in c, s<=t} a[t,s] v_s
@@ -265,7 +320,7 @@ def chunked(q, k, v, C, eps=EPS):
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, H, p = q.shape
     dv = v.shape[-1]
-    dS, dZ = chunk_states(k, v, C)
+    dS, dZ = chunk_states(k, v, C, groups)
     S_prev, _ = exclusive_scan(dS, axis=2)
     Z_prev, _ = exclusive_scan(dZ, axis=2)
     o = np.empty((B, T, H, dv))
@@ -276,10 +331,9 @@ def chunked(q, k, v, C, eps=EPS):
         for c in range(T // C):
             sl = slice(c * C, (c + 1) * C)
             Qc, Kc, Vc = Q[sl], K[sl], V[sl]
-            inter_num = feature(Qc) @ S_prev[b, h, c]
+            inter_num = feature(Qc, groups) @ S_prev[b, h, c]
             inter_den = np.einsum("ti,ij,tj->t", Qc, Z_prev[b, h, c], Qc)
-            sc = Qc @ Kc.T
-            a = np.where(tri, sc * sc, 0.0)
+            a = np.where(tri, _scores(Qc, Kc, groups), 0.0)
             d = eps + inter_den + a.sum(axis=1)
             o[b, sl, h] = (inter_num + _masked_sum(a, Vc, tri)) / d[:, None]
             den[b, sl, h] = d
@@ -321,7 +375,7 @@ def gate_terms(q, k, v, eps=EPS):
 # Backward of the closed form.
 # ----------------------------------------------------------------------------------------
 
-def backward(q, k, v, dO, eps=EPS, block=512):
+def backward(q, k, v, dO, eps=EPS, block=512, groups=1):
     """Gradients of L = sum_t <dO_t, o_t> with o the closed form (derived here; the pages
     name a flash backward [README kernel list] but print no formula).
 
@@ -331,28 +385,31 @@ def backward(q, k, v, dO, eps=EPS, block=512):
       dq_t    = sum_s 2 s_ts G_ts k_s
       dk_s    = sum_t 2 s_ts G_ts q_t
       dv_s    = sum_{t>=s} a_ts dO_t / D_t
-    Tiled over query blocks; returns float64 (dq, dk, dv).
+    Tiled over query blocks; returns float64 (dq, dk, dv).  groups = g: a_ts is the grouped
+    score, and the coordinates of group j take s_ts^(j) = q_t^(j) . k_s^(j) in place of s_ts.
     """
     q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    T = q.shape[1]
+    T, p = q.shape[1], q.shape[3]
+    slices = _group_slices(p, groups)
     for b, h, Q in _heads(q):
         K, V, G_out = k[b, :, h], v[b, :, h], dO[b, :, h]
         for i0 in range(0, T, block):
             i1 = min(T, i0 + block)
             t_idx = np.arange(i0, i1)[:, None]
             mask = np.arange(i1)[None, :] <= t_idx
-            sc = np.where(mask, Q[i0:i1] @ K[:i1].T, 0.0)
-            a = sc * sc
+            scs = [np.where(mask, Q[i0:i1, sl] @ K[:i1, sl].T, 0.0) for sl in slices]
+            a = sum(sc * sc for sc in scs)
             d = eps + a.sum(axis=1)
             o = (a @ V[:i1]) / d[:, None]
             dOb = G_out[i0:i1]
             delta = (dOb * o).sum(axis=1)
             g = np.where(mask, (dOb @ V[:i1].T - delta[:, None]) / d[:, None], 0.0)
-            ds = 2.0 * sc * g
-            dq[b, i0:i1, h] = ds @ K[:i1]
-            dk[b, :i1, h] += ds.T @ Q[i0:i1]
+            for sl, sc in zip(slices, scs):
+                ds = 2.0 * sc * g
+                dq[b, i0:i1, h, sl] = ds @ K[:i1, sl]
+                dk[b, :i1, h, sl] += ds.T @ Q[i0:i1, sl]
             dv[b, :i1, h] += (a / d[:, None]).T @ dOb
     return dq, dk, dv

@@ -384,3 +384,146 @@ def test_backward_causality():
     np.testing.assert_array_equal(dv1[:, 6:], dv2[:, 6:])
     np.testing.assert_array_equal(dk1[:, 6:], dk2[:, 6:])
     np.testing.assert_array_equal(np.delete(dq1, 5, axis=1), np.delete(dq2, 5, axis=1))
+
+
+# ------------------------------------------------------------ KATA-Mg (groups) ----------
+
+def _orthant_closed_form(q, k, v, eps):
+    """groups = p: every group is one coordinate, so a_ts = sum_i q_i^2 k_i^2 -- linear
+    attention with the positive-orthant feature u*u, written out directly."""
+    B, T, H, _ = q.shape
+    o = np.empty((B, T, H, v.shape[-1]))
+    d = np.empty((B, T, H))
+    for b in range(B):
+        for h in range(H):
+            W = np.tril((q[b, :, h] ** 2) @ (k[b, :, h] ** 2).T)
+            d[b, :, h] = eps + W.sum(axis=1)
+            o[b, :, h] = (W @ v[b, :, h]) / d[b, :, h][:, None]
+    return o, d
+
+
+def _all_grouped_forms(q, k, v, eps, g):
+    T = q.shape[1]
+    out = {"closed_form": O.closed_form(q, k, v, eps, block=5, groups=g),
+           "recurrent": O.recurrent(q, k, v, eps, groups=g),
+           "chunked": O.chunked(q, k, v, 4 if T % 4 == 0 else T, eps, groups=g)}
+    B, _, H, _ = q.shape
+    o = np.empty((B, T, H, v.shape[-1]))
+    d = np.empty((B, T, H))
+    rows = np.arange(T)[::-1]
+    for b in range(B):
+        for h in range(H):
+            ob, db = O.closed_form_rows(q[b, :, h], k[b, :, h], v[b, :, h], rows, eps,
+                                        block=3, groups=g)
+            o[b, rows, h], d[b, rows, h] = ob, db
+    out["closed_form_rows"] = (o, d)
+    return out
+
+
+@pytest.mark.parametrize("p", [4, 8])
+def test_groups_equal_p_is_the_positive_orthant_feature(p):
+    rng = np.random.default_rng(40 + p)
+    q, k, v = _rand(rng, 2, 12, 2, p, 3, unit_q=False)
+    want = _orthant_closed_form(q, k, v, 1e-6)
+    for name, (o, d) in _all_grouped_forms(q, k, v, 1e-6, p).items():
+        np.testing.assert_allclose(o, want[0], rtol=1e-11, atol=1e-12, err_msg=name)
+        np.testing.assert_allclose(d, want[1], rtol=1e-11, err_msg=name)
+
+
+@pytest.mark.parametrize("p,g", [(8, 2), (8, 4), (16, 2), (6, 3)])
+def test_grouped_output_is_sum_of_per_group_numerators_over_shared_denominator(p, g):
+    # a_ts = sum_j a_ts^(j), so N_t = sum_j N_t^(j) and D_t - eps = sum_j (D_t^(j) - eps),
+    # each per-group term being the ungrouped closed form on that group's coordinates
+    rng = np.random.default_rng(50 + p + g)
+    q, k, v = _rand(rng, 1, 14, 2, p, 5)
+    eps = 1e-3
+    num = 0.0
+    dsum = 0.0
+    w = p // g
+    for j in range(g):
+        sl = slice(j * w, (j + 1) * w)
+        oj, dj = O.closed_form(q[..., sl], k[..., sl], v, eps)
+        num = num + oj * dj[..., None]
+        dsum = dsum + (dj - eps)
+    want_d = eps + dsum
+    want_o = num / want_d[..., None]
+    for name, (o, d) in _all_grouped_forms(q, k, v, eps, g).items():
+        np.testing.assert_allclose(o, want_o, rtol=1e-10, atol=1e-12, err_msg=name)
+        np.testing.assert_allclose(d, want_d, rtol=1e-12, err_msg=name)
+
+
+def test_grouped_feature_inner_product_is_sum_of_group_squares_exactly():
+    rng = np.random.default_rng(60)
+    for p, g in [(8, 2), (16, 4), (32, 2), (12, 3)]:
+        q = rng.integers(-3, 4, size=(50, p)).astype(np.float64)
+        k = rng.integers(-3, 4, size=(50, p)).astype(np.float64)
+        got = (O.feature(q, g) * O.feature(k, g)).sum(axis=-1)
+        w = p // g
+        want = sum((q[:, j * w:(j + 1) * w] * k[:, j * w:(j + 1) * w]).sum(axis=-1) ** 2
+                   for j in range(g))
+        assert np.array_equal(got, want)
+        assert O.feature(q, g).shape[-1] == p * p // g
+
+
+def test_grouped_packed_widths_match_printed_state_sizes():
+    g = _load("state_sizes.json")
+    assert O.packed_width(64, 1) == g["packed_width_d64"]["value"]
+    assert O.packed_width(64, 2) == g["mg_packed_width_formula"]["value_d64_g2"]
+    # the review's entry counts: twice the packed state, d_v = 64
+    assert 2 * O.packed_width(64, 1) * 64 == g["m1_state_entries_d64_dv64"]["value"]
+    assert 2 * O.packed_width(64, 2) * 64 == g["m2_state_entries_d64_dv64"]["value"]
+    for d in (8, 16, 32, 64):
+        for gg in (1, 2, 4):
+            assert O.packed_width(d, gg) == d * (d // gg + 1) // 2
+
+
+def test_grouped_chunk_states_are_per_group_outer_products():
+    rng = np.random.default_rng(61)
+    p, g, C = 8, 2, 4
+    _, k, v = _rand(rng, 1, 8, 1, p, 3)
+    dS, dZ = O.chunk_states(k, v, C, groups=g)
+    assert dS.shape == (1, 1, 2, p * p // g, 3)
+    for c in range(2):
+        Kc, Vc = k[0, c * C:(c + 1) * C, 0], v[0, c * C:(c + 1) * C, 0]
+        rows = []
+        for j in range(g):
+            blk = Kc[:, j * 4:(j + 1) * 4]
+            rows.append(np.einsum("si,sj,sd->ijd", blk, blk, Vc).reshape(16, 3))
+        np.testing.assert_allclose(dS[0, 0, c], np.concatenate(rows), rtol=1e-13, atol=1e-15)
+        Zfull = Kc.T @ Kc
+        assert np.all(dZ[0, 0, c][:4, 4:] == 0) and np.all(dZ[0, 0, c][4:, :4] == 0)
+        np.testing.assert_allclose(dZ[0, 0, c][:4, :4], Zfull[:4, :4], rtol=1e-14)
+
+
+def test_groups_one_is_the_ungrouped_computation_bitwise():
+    rng = np.random.default_rng(62)
+    q, k, v = _rand(rng, 1, 9, 2, 8, 4)
+    a = O.closed_form(q, k, v)
+    b = O.closed_form(q, k, v, groups=1)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("g", [2, 4])
+def test_grouped_backward_matches_central_finite_differences(g):
+    rng = np.random.default_rng(70 + g)
+    B, T, H, p, dv = 1, 6, 1, 8, 3
+    q, k, v = _rand(rng, B, T, H, p, dv, unit_q=False)
+    dO = rng.standard_normal((B, T, H, dv))
+    eps = 1e-2
+    dq, dk, dv_ = O.backward(q, k, v, dO, eps, block=4, groups=g)
+
+    def loss(q, k, v):
+        return float((O.closed_form(q, k, v, eps, groups=g)[0] * dO).sum())
+
+    h = 1e-6
+    for name, x, gr in (("q", q, dq), ("k", k, dk), ("v", v, dv_)):
+        num = np.empty_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (loss(**args_p) - loss(**args_m)) / (2 * h)
+        np.testing.assert_allclose(gr, num, rtol=1e-6, atol=1e-7, err_msg=name)

@@ -1,7 +1,8 @@
 """Plants plausible mistakes in a scratch copy of the CPU oracle and checks that the oracle's
 pins (tests/test_oracle.py) catch every one: a dropped eps, an excluded diagonal, |q.k|
 instead of (q.k)^2, a state read before its update, an inclusive scan, a wrong sign or a
-perturbed operand in the backward, a shifted feature index, a wrong gate weight.  CPU only."""
+perturbed operand in the backward, a shifted feature index, a wrong gate weight, and KATA-Mg
+grouping mistakes that leave the ungrouped computation unchanged.  CPU only."""
 
 import os
 import shutil
@@ -19,18 +20,34 @@ MUTATIONS = {
         "mask = np.arange(i0, i1)[None, :] <= np.arange(i0, i1)[:, None]",
         "mask = np.arange(i0, i1)[None, :] < np.arange(i0, i1)[:, None]"),
     "abs_instead_of_square": (
-        "a = sc * sc                                   # (q_t . k_s)^2  [Gist 2.2]",
-        "a = np.abs(sc)"),
+        "a = a + sc * sc                               # (q_t . k_s)^2  [Gist 2.2]",
+        "a = a + np.abs(sc)"),
+    # KATA-Mg: each of these is invisible at groups = 1
+    "groups_square_of_sum": (
+        "        a = a + sc * sc                               # (q_t . k_s)^2  [Gist 2.2]\n"
+        "    return a",
+        "        a = a + sc\n    return a * a"),
+    "groups_recurrent_full_Z": ("Z += np.where(gm, np.outer(K[t], K[t]), 0.0)",
+                                "Z += np.outer(K[t], K[t])"),
+    "groups_chunk_full_Z": ("dZ[b, h, c] = np.where(gm, Kc.T @ Kc, 0.0)",
+                            "dZ[b, h, c] = Kc.T @ Kc"),
+    "groups_backward_wrong_slice": ("dq[b, i0:i1, h, sl] = ds @ K[:i1, sl]",
+                                    "dq[b, i0:i1, h, sl] = ds @ K[:i1, slices[0]]"),
     "rows_skip_diagonal": (
-        "st = Q[tr] @ K[s0:tr + 1].T",
-        "st = Q[tr] @ K[s0:tr].T\n            at = st * st\n            num[r] += at @ V[s0:tr]\n"
-        "            asum[r] += at.sum()\n            continue"),
+        "at = _scores(Q[tr:tr + 1], K[s0:tr + 1], groups)[0]\n"
+        "            num[r] += at @ V[s0:tr + 1]",
+        "at = _scores(Q[tr:tr + 1], K[s0:tr], groups)[0]\n"
+        "            num[r] += at @ V[s0:tr]"),
     "recurrent_eps_squared": ("d = eps + Q[t] @ Z @ Q[t]", "d = eps * eps + Q[t] @ Z @ Q[t]"),
     "recurrent_read_before_update": (
-        "            S += np.outer(feature(K[t]), V[t])\n            Z += np.outer(K[t], K[t])\n"
-        "            d = eps + Q[t] @ Z @ Q[t]\n            o[b, t, h] = feature(Q[t]) @ S / d",
-        "            d = eps + Q[t] @ Z @ Q[t]\n            o[b, t, h] = feature(Q[t]) @ S / d\n"
-        "            S += np.outer(feature(K[t]), V[t])\n            Z += np.outer(K[t], K[t])"),
+        "            S += np.outer(feature(K[t], groups), V[t])\n"
+        "            Z += np.where(gm, np.outer(K[t], K[t]), 0.0)\n"
+        "            d = eps + Q[t] @ Z @ Q[t]\n"
+        "            o[b, t, h] = feature(Q[t], groups) @ S / d",
+        "            d = eps + Q[t] @ Z @ Q[t]\n"
+        "            o[b, t, h] = feature(Q[t], groups) @ S / d\n"
+        "            S += np.outer(feature(K[t], groups), V[t])\n"
+        "            Z += np.where(gm, np.outer(K[t], K[t]), 0.0)"),
     "inclusive_scan": ("        out[c] = run\n        run = run + x[c]",
                        "        run = run + x[c]\n        out[c] = run"),
     "chunk_denominator_operand": (
@@ -39,8 +56,8 @@ MUTATIONS = {
     "backward_delta_sign": (
         "g = np.where(mask, (dOb @ V[:i1].T - delta[:, None]) / d[:, None], 0.0)",
         "g = np.where(mask, (dOb @ V[:i1].T + delta[:, None]) / d[:, None], 0.0)"),
-    "backward_dk_scaled": ("dk[b, :i1, h] += ds.T @ Q[i0:i1]",
-                           "dk[b, :i1, h] += 1.0001 * (ds.T @ Q[i0:i1])"),
+    "backward_dk_scaled": ("dk[b, :i1, h, sl] += ds.T @ Q[i0:i1, sl]",
+                           "dk[b, :i1, h, sl] += 1.0001 * (ds.T @ Q[i0:i1, sl])"),
     "feature_shifted_index": (
         "return (u[..., :, None] * u[..., None, :]).reshape(*u.shape[:-1], p * p)",
         "return (u[..., :, None] * np.roll(u, 1, axis=-1)[..., None, :])"
