@@ -77,6 +77,7 @@ typedef struct {
   int32_t chunk;
   int32_t seg_chunks;
   int32_t state_layout;
+  int32_t groups;
   float eps;
   int32_t in_dtype;
   int32_t out_dtype;

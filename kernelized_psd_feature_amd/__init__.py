@@ -50,7 +50,7 @@ class _Problem(ctypes.Structure):
         ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
         ("p", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
         ("seg_chunks", ctypes.c_int32), ("state_layout", ctypes.c_int32),
-        ("eps", ctypes.c_float),
+        ("groups", ctypes.c_int32), ("eps", ctypes.c_float),
         ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
         ("sq", ctypes.c_int64 * 3), ("sk", ctypes.c_int64 * 3), ("sv", ctypes.c_int64 * 3),
         ("so", ctypes.c_int64 * 3), ("sdo", ctypes.c_int64 * 3),
@@ -135,7 +135,7 @@ STATE_LAYOUTS = {"direct": 0, "packed": 1}
 
 
 def _make_problem(q, k, v, o=None, dO=None, chunk=0, seg_chunks=0, eps=1e-6,
-                  out_dtype=torch.float32, state="direct"):
+                  out_dtype=torch.float32, state="direct", groups=1):
     for name, x in (("q", q), ("k", k), ("v", v)):
         if not x.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
@@ -148,6 +148,7 @@ def _make_problem(q, k, v, o=None, dO=None, chunk=0, seg_chunks=0, eps=1e-6,
     if state not in STATE_LAYOUTS:
         raise ValueError(f"state must be one of {sorted(STATE_LAYOUTS)}")
     pr.state_layout = STATE_LAYOUTS[state]
+    pr.groups = groups
     pr.in_dtype, pr.out_dtype = _dtype_code(q.dtype), _dtype_code(out_dtype)
     pr.sq[:] = _bth_strides(q, "q")
     pr.sk[:] = _bth_strides(k, "k")
@@ -165,11 +166,14 @@ def _out(q, v, out_dtype, out):
     return out
 
 
-def fwd_quadratic(q, k, v, eps=1e-6, out_dtype=torch.float32, out=None, return_den=False):
-    """Flash-style O(T^2) forward.  Returns o (and D_t = eps + sum_s a_ts, fp32 (B,T,H))."""
+def fwd_quadratic(q, k, v, eps=1e-6, out_dtype=torch.float32, out=None, return_den=False,
+                  groups=1):
+    """Flash-style O(T^2) forward.  Returns o (and D_t = eps + sum_s a_ts, fp32 (B,T,H)).
+    groups=g: KATA-Mg, a_ts = sum_j (q_t^(j) . k_s^(j))^2 over g consecutive coordinate
+    groups (every public call takes this argument)."""
     o = _out(q, v, out_dtype, out)
     den = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_den else None
-    pr = _make_problem(q, k, v, o, eps=eps, out_dtype=out_dtype)
+    pr = _make_problem(q, k, v, o, eps=eps, out_dtype=out_dtype, groups=groups)
     with torch.cuda.device(q.device):
         _check(_lib().kata_fwd_quadratic(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                          _ptr(den), _stream(q.device)), "kata_fwd_quadratic")
@@ -177,14 +181,14 @@ def fwd_quadratic(q, k, v, eps=1e-6, out_dtype=torch.float32, out=None, return_d
 
 
 def chunked_workspace_size(q, k, v, chunk=64, seg_chunks=0, out_dtype=torch.float32,
-                           state="packed"):
+                           state="packed", groups=1):
     pr = _make_problem(q, k, v, chunk=chunk, seg_chunks=seg_chunks, out_dtype=out_dtype,
-                       state=state)
+                       state=state, groups=groups)
     return int(_lib().kata_fwd_chunked_workspace_size(ctypes.byref(pr)))
 
 
 def fwd_chunked(q, k, v, chunk=64, eps=1e-6, out_dtype=torch.float32, seg_chunks=0,
-                out=None, workspace=None, return_den=False, state="packed"):
+                out=None, workspace=None, return_den=False, state="packed", groups=1):
     """Exact O(T) chunked-state forward (chunk states, prefix scan, readout).
 
     state: "packed" (the p(p+1)/2 unique state rows, the faster layout) or "direct" (all p^2
@@ -194,7 +198,7 @@ def fwd_chunked(q, k, v, chunk=64, eps=1e-6, out_dtype=torch.float32, seg_chunks
     o = _out(q, v, out_dtype, out)
     den = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_den else None
     pr = _make_problem(q, k, v, o, chunk=chunk, seg_chunks=seg_chunks, eps=eps,
-                       out_dtype=out_dtype, state=state)
+                       out_dtype=out_dtype, state=state, groups=groups)
     lib = _lib()
     need = int(lib.kata_fwd_chunked_workspace_size(ctypes.byref(pr)))
     if workspace is None:
@@ -241,19 +245,19 @@ def state_shape(k, v):
     return (B, H, v.shape[-1] + 1, p * p)
 
 
-def recurrent_state_workspace_size(k, v, chunk=64):
-    pr = _make_problem(k, k, v, chunk=chunk)
+def recurrent_state_workspace_size(k, v, chunk=64, groups=1):
+    pr = _make_problem(k, k, v, chunk=chunk, groups=groups)
     return int(_lib().kata_recurrent_state_workspace_size(ctypes.byref(pr)))
 
 
-def recurrent_state(k, v, chunk=64, out=None, workspace=None):
+def recurrent_state(k, v, chunk=64, out=None, workspace=None, groups=1):
     """Prefill: the state (S, Z) after all T tokens of k, v (T % chunk == 0), in the layout
     of state_shape()."""
     state = out if out is not None else torch.empty(state_shape(k, v), dtype=torch.float32,
                                                     device=k.device)
     if state.shape != state_shape(k, v) or state.dtype != torch.float32 or not state.is_contiguous():
         raise ValueError("state must be a contiguous fp32 tensor of state_shape(k, v)")
-    pr = _make_problem(k, k, v, chunk=chunk)
+    pr = _make_problem(k, k, v, chunk=chunk, groups=groups)
     lib = _lib()
     need = int(lib.kata_recurrent_state_workspace_size(ctypes.byref(pr)))
     if workspace is None:
@@ -265,26 +269,27 @@ def recurrent_state(k, v, chunk=64, out=None, workspace=None):
     return state
 
 
-def decode(q, k, v, state, eps=1e-6, out_dtype=torch.float32, out=None, return_den=False):
+def decode(q, k, v, state, eps=1e-6, out_dtype=torch.float32, out=None, return_den=False,
+           groups=1):
     """Advance `state` (in place) over the T tokens of q, k, v one at a time; returns o (and
     D_t).  T = 1 is one decode step."""
     if state.shape != state_shape(k, v) or state.dtype != torch.float32 or not state.is_contiguous():
         raise ValueError("state must be a contiguous fp32 tensor of state_shape(k, v)")
     o = _out(q, v, out_dtype, out)
     den = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_den else None
-    pr = _make_problem(q, k, v, o, eps=eps, out_dtype=out_dtype)
+    pr = _make_problem(q, k, v, o, eps=eps, out_dtype=out_dtype, groups=groups)
     with torch.cuda.device(q.device):
         _check(_lib().kata_decode(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                   _ptr(den), _ptr(state), _stream(q.device)), "kata_decode")
     return (o, den) if return_den else o
 
 
-def bwd_workspace_size(q, k, v):
-    pr = _make_problem(q, k, v)
+def bwd_workspace_size(q, k, v, groups=1):
+    pr = _make_problem(q, k, v, groups=groups)
     return int(_lib().kata_bwd_workspace_size(ctypes.byref(pr)))
 
 
-def bwd(q, k, v, dO, eps=1e-6, workspace=None, chunk=None):
+def bwd(q, k, v, dO, eps=1e-6, workspace=None, chunk=None, groups=1):
     """fp32 gradients (dq, dk, dv) of sum(dO * o), o the forward output.
 
     chunk=None: the flash-style O(T^2) backward; chunk=C: the chunked O(T) backward (forward
@@ -297,7 +302,7 @@ def bwd(q, k, v, dO, eps=1e-6, workspace=None, chunk=None):
     # gradient outputs share the strides of their inputs
     qs, ks, vs = (q, k, v) if q.is_contiguous() and k.is_contiguous() and v.is_contiguous() \
         else (q.contiguous(), k.contiguous(), v.contiguous())
-    pr = _make_problem(qs, ks, vs, dO=dO, eps=eps, chunk=chunk or 0)
+    pr = _make_problem(qs, ks, vs, dO=dO, eps=eps, chunk=chunk or 0, groups=groups)
     lib = _lib()
     size_fn, fn, name = ((lib.kata_bwd_workspace_size, lib.kata_bwd, "kata_bwd") if chunk is None
                          else (lib.kata_bwd_chunked_workspace_size, lib.kata_bwd_chunked,

@@ -43,6 +43,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
 #pragma unroll
   for (int j = 0; j < DP; ++j) acc[j] = 0.f;
   float l = 0.f;
+  const Groups grp = make_groups(P, pr.gs);
   const int kend = min(pr.T, t0 + kRows);
   for (int s0 = 0; s0 < kend; s0 += kRows) {
     __syncthreads();
@@ -58,10 +59,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
     const int smax = min(kRows, kend - s0);
     for (int s = 0; s < smax; ++s) {
       if (s0 + s <= t) {
-        float dot = 0.f;
-#pragma unroll
-        for (int i = 0; i < P; ++i) dot = fmaf(qr[i], ks[s][i], dot);
-        const float a = dot * dot;
+        const float a = grouped_square(qr, ks[s], grp);
         l += a;
 #pragma unroll
         for (int j = 0; j < DP; ++j) acc[j] = fmaf(a, vs[s][part * DP + j], acc[j]);
@@ -104,6 +102,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
   for (int d = 0; d < DV; ++d) g[d] = live ? to_f32(dO[row_off(pr.sdo, b, t, h) + d]) : 0.f;
   const float invD = live ? 1.f / Din[bht(pr, b, h, t)] : 0.f;
   const float dl = live ? delta[bht(pr, b, h, t)] : 0.f;
+  const Groups grp = make_groups(P, pr.gs);
   const int kend = min(pr.T, t0 + kThreads);
   for (int s0 = 0; s0 < kend; s0 += kRows) {
     __syncthreads();
@@ -119,14 +118,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     const int smax = min(kRows, kend - s0);
     for (int s = 0; s < smax; ++s) {
       if (live && s0 + s <= t) {
-        float sc = 0.f, gv = 0.f;
-#pragma unroll
-        for (int i = 0; i < P; ++i) sc = fmaf(qr[i], ks[s][i], sc);
+        float sc[P], gv = 0.f;
+        grouped_dots(qr, ks[s], grp, sc);
 #pragma unroll
         for (int d = 0; d < DV; ++d) gv = fmaf(g[d], vs[s][d], gv);
-        const float ds = 2.f * sc * ((gv - dl) * invD);
+        const float G = (gv - dl) * invD;
 #pragma unroll
-        for (int i = 0; i < P; ++i) acc[i] = fmaf(ds, ks[s][i], acc[i]);
+        for (int i = 0; i < P; ++i) acc[i] = fmaf(2.f * sc[i] * G, ks[s][i], acc[i]);
       }
     }
   }
@@ -161,6 +159,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
     vr[d] = live ? to_f32(v[row_off(pr.sv, b, s, h) + d]) : 0.f;
     av[d] = 0.f;
   }
+  const Groups grp = make_groups(P, pr.gs);
   for (int q0 = s_base; q0 < pr.T; q0 += kRows) {     // queries t >= s_base
     __syncthreads();
     for (int e = threadIdx.x; e < kRows * P; e += kThreads) {
@@ -180,15 +179,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
     const int rmax = min(kRows, pr.T - q0);
     for (int r = 0; r < rmax; ++r) {
       if (live && q0 + r >= s) {
-        float sc = 0.f, gv = 0.f;
-#pragma unroll
-        for (int i = 0; i < P; ++i) sc = fmaf(qs[r][i], kr[i], sc);
+        float sc[P], gv = 0.f;
+        const float a = grouped_dots(kr, qs[r], grp, sc);
 #pragma unroll
         for (int d = 0; d < DV; ++d) gv = fmaf(gs[r][d], vr[d], gv);
-        const float ds = 2.f * sc * ((gv - dls[r]) * invD[r]);
-        const float w = sc * sc * invD[r];
+        const float G = (gv - dls[r]) * invD[r];
+        const float w = a * invD[r];
 #pragma unroll
-        for (int i = 0; i < P; ++i) ak[i] = fmaf(ds, qs[r][i], ak[i]);
+        for (int i = 0; i < P; ++i) ak[i] = fmaf(2.f * sc[i] * G, qs[r][i], ak[i]);
 #pragma unroll
         for (int d = 0; d < DV; ++d) av[d] = fmaf(w, gs[r][d], av[d]);
       }

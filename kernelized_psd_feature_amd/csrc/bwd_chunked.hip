@@ -114,16 +114,15 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_dq_kernel(
       acc[i] = u;
     }
     // this chunk: sum_{s<=t} (q . k_s) G_ts k_s, G_ts split over the parts' value columns
+    const Groups grp = make_groups(P, pr.gs);
     for (int s = 0; s <= row; ++s) {
-      float dot = 0.f;
-#pragma unroll
-      for (int i = 0; i < P; ++i) dot = fmaf(qr[i], ks[s][i], dot);
+      float sc[P];
+      grouped_dots(qr, ks[s], grp, sc);
       float G = part ? 0.f : -et;
 #pragma unroll
       for (int j = 0; j < DP; ++j) G = fmaf(gr[j], vs[s][part * DP + j], G);
-      const float w = dot * G;
 #pragma unroll
-      for (int i = 0; i < P; ++i) acc[i] = fmaf(w, ks[s][i], acc[i]);
+      for (int i = 0; i < P; ++i) acc[i] = fmaf(sc[i] * G, ks[s][i], acc[i]);
     }
   }
   reduce_parts<P>(acc, red, row, part);
@@ -157,7 +156,8 @@ __global__ __launch_bounds__(kThreads) void bwd_rev_state_kernel(
   for (int x = threadIdx.x; x < E; x += kThreads) {
     const int d = x / PP, f = x % PP, i = f / P, jj = f % P;
     float acc = 0.f;
-    for (int s = 0; s < C; ++s) acc = fmaf(qs[s][i] * qs[s][jj], gs[s][d], acc);
+    if (same_group(i, jj, pr.gs))
+      for (int s = 0; s < C; ++s) acc = fmaf(qs[s][i] * qs[s][jj], gs[s][d], acc);
     out[x] = acc;
   }
 }
@@ -222,19 +222,18 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_dkdv_kernel(
       acc[i] = w;
     }
     // this chunk: t >= s
+    const Groups grp = make_groups(P, pr.gs);
     for (int tt = row; tt < C; ++tt) {
-      float dot = 0.f;
-#pragma unroll
-      for (int i = 0; i < P; ++i) dot = fmaf(qs[tt][i], kr[i], dot);
+      float sc[P];
+      const float a = grouped_dots(kr, qs[tt], grp, sc);
       float G = part ? 0.f : -es[tt];
 #pragma unroll
       for (int j = 0; j < DP; ++j) {
         G = fmaf(gs[tt][part * DP + j], vr[j], G);
-        dvacc[j] = fmaf(dot * dot, gs[tt][part * DP + j], dvacc[j]);
+        dvacc[j] = fmaf(a, gs[tt][part * DP + j], dvacc[j]);
       }
-      const float w = dot * G;
 #pragma unroll
-      for (int i = 0; i < P; ++i) acc[i] = fmaf(w, qs[tt][i], acc[i]);
+      for (int i = 0; i < P; ++i) acc[i] = fmaf(sc[i] * G, qs[tt][i], acc[i]);
     }
     float* dvp = dv + row_off(pr.sv, b, s, h) + part * DP;
 #pragma unroll

@@ -77,8 +77,9 @@ __global__ __launch_bounds__(kThreads) void decode_rows_kernel(
     float num = 0.f, zq = 0.f;
 #pragma unroll
     for (int r = 0; r < E; ++r) {
-      const float kk = ki * to_f32(kt[j0 + r]);      // phi_f(k_t)
-      const float qq = qi * to_f32(qt[j0 + r]);      // phi_f(q_t)
+      const bool in = same_group(i, j0 + r, pr.gs);   // KATA-Mg: pairs within one group
+      const float kk = in ? ki * to_f32(kt[j0 + r]) : 0.f;   // phi_f(k_t)
+      const float qq = in ? qi * to_f32(qt[j0 + r]) : 0.f;   // phi_f(q_t)
       s[r] = fmaf(kk, vd, s[r]);
       z[r] += kk;
       num = fmaf(qq, s[r], num);
@@ -109,7 +110,8 @@ __global__ __launch_bounds__(64) void decode_z_kernel(DevProblem pr, const Tin* 
     const Tin* kt = k + row_off(pr.sk, b, t, h);
     const float ki = to_f32(kt[i]);
 #pragma unroll
-    for (int r = 0; r < E; ++r) z[r] += ki * to_f32(kt[j0 + r]);
+    for (int r = 0; r < E; ++r)
+      z[r] += same_group(i, j0 + r, pr.gs) ? ki * to_f32(kt[j0 + r]) : 0.f;
   }
   store_run(zr, z);
 }

@@ -11,9 +11,65 @@ namespace kata {
 // Problem description passed to kernels by value.
 struct DevProblem {
   int B, H, T, p, dv, C;
+  int gs;                                          // KATA-Mg group width (p: one group)
   float eps;
   long long sq[3], sk[3], sv[3], so[3], sdo[3];   // element strides of (b, t, h)
 };
+
+// ---- KATA-Mg scores ------------------------------------------------------------------
+// The p coordinates form groups of gs consecutive entries; the score of a (query, key) pair
+// is the sum over groups of the squared group dot product (a single group: (q . k)^2), and
+// the feature pair (i, j) exists only within a group.  Bit i of `start` / `last` marks the
+// first / last coordinate of a group, so the loops below stay fully unrolled.
+struct Groups {
+  unsigned start, last;
+};
+
+__device__ __forceinline__ Groups make_groups(int p, int gs) {
+  Groups g{0u, 0u};
+  for (int i = 0; i < p; ++i) {
+    if (i % gs == 0) g.start |= 1u << i;
+    if (i % gs == gs - 1) g.last |= 1u << i;
+  }
+  return g;
+}
+
+__device__ __forceinline__ bool same_group(int i, int j, int gs) { return i / gs == j / gs; }
+
+// sum over groups of (x . y restricted to the group)^2
+template <int P, typename Y>
+__device__ __forceinline__ float grouped_square(const float (&x)[P], const Y& y, Groups g) {
+  float a = 0.f, run = 0.f;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    run = fmaf(x[i], y[i], ((g.start >> i) & 1u) ? 0.f : run);
+    if ((g.last >> i) & 1u) a = fmaf(run, run, a);
+  }
+  return a;
+}
+
+// As grouped_square, and sc[i] = the dot product of coordinate i's group.
+template <int P, typename Y>
+__device__ __forceinline__ float grouped_dots(const float (&x)[P], const Y& y, Groups g,
+                                              float (&sc)[P]) {
+  float cum[P];
+  float run = 0.f;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    run = fmaf(x[i], y[i], ((g.start >> i) & 1u) ? 0.f : run);
+    cum[i] = run;
+  }
+  float a = 0.f, cur = 0.f;
+#pragma unroll
+  for (int i = P - 1; i >= 0; --i) {
+    if ((g.last >> i) & 1u) {
+      cur = cum[i];
+      a = fmaf(cur, cur, a);
+    }
+    sc[i] = cur;
+  }
+  return a;
+}
 
 __device__ __forceinline__ long long row_off(const long long* s, int b, int t, int h) {
   return (long long)b * s[0] + (long long)t * s[1] + (long long)h * s[2];

@@ -42,6 +42,7 @@ __global__ __launch_bounds__(kThreads) void quadratic_generic_kernel(
 #pragma unroll
   for (int j = 0; j < DP; ++j) acc[j] = 0.f;
   float l = 0.f;
+  const Groups grp = make_groups(P, pr.gs);
 
   const int kend = min(pr.T, t0 + kRows);
   for (int s0 = 0; s0 < kend; s0 += kRows) {
@@ -58,10 +59,7 @@ __global__ __launch_bounds__(kThreads) void quadratic_generic_kernel(
     const int smax = min(kRows, kend - s0);
     for (int s = 0; s < smax; ++s) {
       if (s0 + s <= t) {                       // causal mask by selection
-        float dot = 0.f;
-#pragma unroll
-        for (int i = 0; i < P; ++i) dot = fmaf(qr[i], ks[s][i], dot);
-        const float a = dot * dot;
+        const float a = grouped_square(qr, ks[s], grp);
         l += a;
 #pragma unroll
         for (int j = 0; j < DP; ++j) acc[j] = fmaf(a, vs[s][part * DP + j], acc[j]);
@@ -105,7 +103,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_generic_kernel(
   for (int e = threadIdx.x; e < E; e += kThreads) {
     const int d = e / PP, f = e % PP, i = f / P, j = f % P;
     float acc = 0.f;
-    for (int s = 0; s < C; ++s) acc = fmaf(ks[s][i] * ks[s][j], vs[s][d], acc);
+    if (same_group(i, j, pr.gs))               // other feature pairs are zero rows
+      for (int s = 0; s < C; ++s) acc = fmaf(ks[s][i] * ks[s][j], vs[s][d], acc);
     out[e] = acc;
   }
 }
@@ -160,11 +159,9 @@ __global__ __launch_bounds__(kThreads) void chunk_output_generic_kernel(
   }
   // intra-chunk: causal tile, diagonal included
   float l = 0.f;
+  const Groups grp = make_groups(P, pr.gs);
   for (int s = 0; s <= row; ++s) {
-    float dot = 0.f;
-#pragma unroll
-    for (int i = 0; i < P; ++i) dot = fmaf(qr[i], ks[s][i], dot);
-    const float a = dot * dot;
+    const float a = grouped_square(qr, ks[s], grp);
     l += a;
 #pragma unroll
     for (int j = 0; j < DP; ++j) acc[j] = fmaf(a, vs[s][part * DP + j], acc[j]);

@@ -120,6 +120,7 @@ kata::DevProblem to_dev(const kata_problem* pr) {
   d.p = pr->p;
   d.dv = pr->dv;
   d.C = pr->chunk;
+  d.gs = pr->groups > 1 ? pr->p / pr->groups : pr->p;
   d.eps = pr->eps;
   for (int i = 0; i < 3; ++i) {
     d.sq[i] = pr->sq[i];
@@ -196,7 +197,7 @@ kata_status kata_fwd_quadratic(const kata_problem* pr, const void* q, const void
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool in_bf16 = pr->in_dtype == KATA_BF16, out_bf16 = pr->out_dtype == KATA_BF16;
   Timed t(KATA_K_QUADRATIC, st);
-  if (kata::quadratic_fast_supported(pr))
+  if (pr->groups <= 1 && kata::quadratic_fast_supported(pr))
     return launch_status(kata::launch_quadratic_fast(dp, out_bf16, q, k, v, o, den, st),
                          "quadratic forward");
   return launch_status(kata::launch_quadratic_generic(dp, in_bf16, out_bf16, q, k, v, o, den, st),

@@ -58,6 +58,8 @@ kata_status validate_problem(const kata_problem* pr, Form f, std::string* why) {
     return fail(why, KATA_ERR_UNSUPPORTED, "p must be 8, 16 or 32");
   if (!in_set(pr->dv, {16, 64}))
     return fail(why, KATA_ERR_UNSUPPORTED, "dv must be 16 or 64");
+  if (pr->groups < 0 || pr->groups > pr->p || (pr->groups > 1 && pr->p % pr->groups))
+    return fail(why, KATA_ERR_INVALID_ARGUMENT, "groups must be 0, 1 or a divisor of p");
   if (!std::isfinite(pr->eps) || pr->eps < 0.0f)
     return fail(why, KATA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
   if (!dtype_pair_ok(pr->in_dtype, pr->out_dtype, f))
@@ -140,7 +142,8 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
   cp.n_chunks = pr->T / pr->chunk;
   cp.n_seq = int64_t(pr->B) * pr->H;
   cp.state_elems = int64_t(pr->p) * pr->p * (pr->dv + 1);
-  cp.fast = (fast_available && pr->in_dtype == KATA_BF16 && pr->p == 16 && pr->dv == 64 && pr->chunk == 64) ? 1 : 0;
+  cp.fast = (fast_available && pr->in_dtype == KATA_BF16 && pr->p == 16 && pr->dv == 64 &&
+             pr->chunk == 64 && pr->groups <= 1) ? 1 : 0;
   if (cp.fast) {
     int L = pr->seg_chunks;
     if (L == 0) {

@@ -90,6 +90,7 @@ def test_null_problem_is_invalid():
     ("p", 12, UNSUPPORTED), ("p", 64, UNSUPPORTED), ("dv", 32, UNSUPPORTED),
     ("eps", -1.0, INVALID), ("eps", float("nan"), INVALID), ("eps", float("inf"), INVALID),
     ("in_dtype", 7, INVALID), ("out_dtype", 7, INVALID),
+    ("groups", -1, INVALID), ("groups", 3, INVALID), ("groups", 17, INVALID),
 ])
 def test_bad_problem_fields(field, value, code):
     pr = _problem()
@@ -286,3 +287,16 @@ def test_chunked_backward_checks_its_arguments():
     t2 = list(t)
     t2[4] = None                                    # dq missing
     assert lib.kata_bwd_chunked(ctypes.byref(pr), *t2, ws, need, None) == INVALID
+
+
+def test_groups_do_not_change_workspace_sizes():
+    # KATA-Mg keeps the p^2-row state layout (pairs across groups are zero rows)
+    lib = _lib()
+    for g in (0, 1, 2, 4, 16):
+        pr = _problem(B=1, H=2, T=256, chunk=32, in_dt=0)
+        pr.groups = g
+        base = _problem(B=1, H=2, T=256, chunk=32, in_dt=0)
+        assert lib.kata_fwd_chunked_workspace_size(ctypes.byref(pr)) == \
+            lib.kata_fwd_chunked_workspace_size(ctypes.byref(base))
+        assert lib.kata_bwd_chunked_workspace_size(ctypes.byref(pr)) == \
+            lib.kata_bwd_chunked_workspace_size(ctypes.byref(base))

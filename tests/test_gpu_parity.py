@@ -665,3 +665,73 @@ def test_decode_bf16_output_is_the_rounded_fp32_output_and_state_is_the_same():
     o16 = K.decode(q, k, v, s2, out_dtype=torch.bfloat16)
     assert torch.equal(o16, o32.to(torch.bfloat16))
     assert torch.equal(s1, s2)
+
+
+# ------------------------------------------------------------ KATA-Mg (groups) ----------
+# g concatenated PSD factors over consecutive coordinate groups; fp32 kernels.
+
+MG_CASES = {   # name: (workload, T, B, H, groups)
+    "layer340m_g2": (2, 448, 2, 3, 2),
+    "layer340m_g4": (2, 256, 1, 2, 4),
+    "tiny_fp32_g2": (1, 256, 1, 1, 2),
+    "tiny_fp32_g8": (1, 256, 1, 1, 8),
+    "p32_g2": (3, 256, 1, 2, 2),
+}
+
+
+@pytest.mark.parametrize("case", sorted(MG_CASES))
+def test_mg_forward_forms_match_oracle(case):
+    wid, T, B, H, g = MG_CASES[case]
+    w = W.WORKLOADS[wid]
+    q, k, v = W.make_inputs(w, 30, T=T, B=B, H=H)
+    ref, dref = O.closed_form(_np(q), _np(k), _np(v), groups=g)
+    qg, kg, vg = _to_gpu(q, k, v)
+    state = torch.zeros(K.state_shape(kg, vg), dtype=torch.float32, device=DEV)
+    outs = {
+        "quadratic": K.fwd_quadratic(qg, kg, vg, groups=g, return_den=True),
+        "chunked": K.fwd_chunked(qg, kg, vg, chunk=w.chunk, groups=g, return_den=True),
+        "decode": K.decode(qg, kg, vg, state, groups=g, return_den=True),
+    }
+    for name, (o, d) in outs.items():
+        err = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
+        say(f"KATA-Mg {case} {name}: max-abs {err:.3e}")
+        assert err <= TOL[w.dtype], name
+        np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=1e-4, err_msg=name)
+
+
+def test_mg_recurrent_state_matches_oracle():
+    w, g, p = W.WORKLOADS[2], 2, 16
+    q, k, v = W.make_inputs(w, 31, T=512, B=1, H=2)
+    got = K.recurrent_state(*_to_gpu(k, v), groups=g).cpu().double().numpy()
+    dS, dZ = O.chunk_states(_np(k), _np(v), 512, groups=g)
+    wd = p // g
+    want = np.zeros_like(got)
+    for j in range(g):                  # group j's (i', j') row -> feature (j wd + i', j wd + j')
+        for a in range(wd):
+            for c in range(wd):
+                f = (j * wd + a) * p + (j * wd + c)
+                want[:, :, :64, f] = dS[:, :, 0, j * wd * wd + a * wd + c, :]
+    want[:, :, 64] = dZ[:, :, 0].reshape(1, 2, p * p)
+    err = float(np.abs(got - want).max())
+    say(f"KATA-Mg recurrent state: max-abs {err:.3e}")
+    assert err <= 1e-4 * max(1.0, float(np.abs(want).max()))
+
+
+@pytest.mark.parametrize("chunk", [None, 32])
+@pytest.mark.parametrize("g", [2, 4])
+def test_mg_backward_matches_oracle(g, chunk):
+    w = W.WORKLOADS[5]
+    q, k, v, dO = W.make_inputs(w, 32, T=256, B=2, H=2, with_dO=True)
+    refs = O.backward(_np(q), _np(k), _np(v), _np(dO), groups=g)
+    got = K.bwd(*_to_gpu(q, k, v, dO), chunk=chunk, groups=g)
+    errs = [float(np.abs(x.cpu().double().numpy() - r).max()) for x, r in zip(got, refs)]
+    say(f"KATA-Mg backward g={g} chunk={chunk}: max-abs {errs}")
+    assert max(errs) <= 1e-2
+
+
+def test_mg_groups_one_is_the_plain_computation_bitwise():
+    w = W.WORKLOADS[1]
+    q, k, v = _to_gpu(*W.make_inputs(w, 33))
+    for f in (lambda **kw: K.fwd_quadratic(q, k, v, **kw),
+              lambda **kw: K.fwd_chunked(q, k, v, chunk=32, **kw)):
+        assert torch.equal(f(), f(groups=1))
