@@ -225,7 +225,9 @@ def run_chunked(args, dev, w):
         "step_roofline_frac": round(bpt * tokens / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "dominant_kernel_source_sha": sha,
     }
-    line["ms_per_step_cold_cache"] = round(cold_cache_ms(step, max(5, args.steps // 5), dev), 5)
+    if not args.no_cold_cache:
+        line["ms_per_step_cold_cache"] = round(cold_cache_ms(step, max(5, args.steps // 5), dev),
+                                               5)
     if args.form == "chunked" and w.name == "long_context_131k" and not args.no_sweep \
             and args.layout == "bthd":
         del ws
@@ -313,6 +315,8 @@ def main():
                     help="chunk-state storage: all p^2 rows or the p(p+1)/2 unique ones")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the T sweep")
+    ap.add_argument("--no-cold-cache", action="store_true",
+                    help="skip the cache-flushed repetition (profiler runs)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="run only a device copy of this many MiB (counter calibration)")
     args = ap.parse_args()

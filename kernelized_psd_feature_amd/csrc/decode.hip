@@ -69,17 +69,26 @@ __global__ __launch_bounds__(kThreads) void decode_rows_kernel(
   float s[E], z[E];
   load_run(s, st + (long long)d * PP + f0);
   load_run(z, st + (long long)DV * PP + f0);
+  unsigned in = 0;                                 // bit r: feature (i, j0 + r) is in a group
+#pragma unroll
+  for (int r = 0; r < E; ++r) in |= same_group(i, j0 + r, pr.gs) ? 1u << r : 0u;
   for (int t = 0; t < pr.T; ++t) {
     const Tin* qt = q + row_off(pr.sq, b, t, h);
     const Tin* kt = k + row_off(pr.sk, b, t, h);
     const float qi = to_f32(qt[i]), ki = to_f32(kt[i]);
     const float vd = to_f32(v[row_off(pr.sv, b, t, h) + d]);
+    float kj[E], qj[E];
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      kj[r] = to_f32(kt[j0 + r]);
+      qj[r] = to_f32(qt[j0 + r]);
+    }
     float num = 0.f, zq = 0.f;
 #pragma unroll
     for (int r = 0; r < E; ++r) {
-      const bool in = same_group(i, j0 + r, pr.gs);   // KATA-Mg: pairs within one group
-      const float kk = in ? ki * to_f32(kt[j0 + r]) : 0.f;   // phi_f(k_t)
-      const float qq = in ? qi * to_f32(qt[j0 + r]) : 0.f;   // phi_f(q_t)
+      const bool on = (in >> r) & 1u;
+      const float kk = on ? ki * kj[r] : 0.f;        // phi_f(k_t)
+      const float qq = on ? qi * qj[r] : 0.f;        // phi_f(q_t)
       s[r] = fmaf(kk, vd, s[r]);
       z[r] += kk;
       num = fmaf(qq, s[r], num);
@@ -106,12 +115,17 @@ __global__ __launch_bounds__(64) void decode_z_kernel(DevProblem pr, const Tin* 
   float* zr = state + ((long long)b * pr.H + h) * (long long)(DV + 1) * PP + (long long)DV * PP + f0;
   float z[E];
   load_run(z, zr);
+  unsigned in = 0;
+#pragma unroll
+  for (int r = 0; r < E; ++r) in |= same_group(i, j0 + r, pr.gs) ? 1u << r : 0u;
   for (int t = 0; t < pr.T; ++t) {
     const Tin* kt = k + row_off(pr.sk, b, t, h);
     const float ki = to_f32(kt[i]);
 #pragma unroll
-    for (int r = 0; r < E; ++r)
-      z[r] += same_group(i, j0 + r, pr.gs) ? ki * to_f32(kt[j0 + r]) : 0.f;
+    for (int r = 0; r < E; ++r) {
+      const float kk = ki * to_f32(kt[j0 + r]);
+      z[r] += ((in >> r) & 1u) ? kk : 0.f;
+    }
   }
   store_run(zr, z);
 }
