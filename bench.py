@@ -12,7 +12,8 @@ Printed: one JSON line.  value = head-tokens (B*H*T) per second.  roofline: algo
 of the dominant kernel per launch / its average duration, against MI355X's 8 TB/s HBM peak.
 cpu_baseline: the fp64 CPU oracle (brute-force closed form) timed on a bounded uniform sample
 of the same workload's query rows, scaled to head-tokens/s.  sweep: tokens/s of the chunked
-form at T = 1k .. 128k with B*T = 131072 (the metric's dependence on T).
+form at T = 1k .. 128k with B*T = 131072 (the metric's dependence on T), each beside the
+sequential inter-chunk form (one segment per sequence, no scan) and the ratio of the two.
 
     python bench.py --form decode     # one decode step for 512 x 16 heads (recurrent form)
 """
@@ -162,16 +163,24 @@ def sweep(q, k, v, args, dev):
     for T in W.SWEEP_T:
         B = q.shape[0] * q.shape[1] // T
         qs, ks, vs, os_ = (x.reshape(B, T, *x.shape[2:]) for x in (q, k, v, o))
-        ws = torch.empty(max(K.chunked_workspace_size(qs, ks, vs, state=args.state), 256),
-                         dtype=torch.uint8, device=dev)
+        point = {"T": T, "B": B}
+        # default segmentation (walks + scan), then the sequential inter-chunk form: one
+        # segment per sequence carries the state through all T / 64 chunks
+        for key, seg in (("", 0), ("sequential_", T // 64)):
+            ws = torch.empty(max(K.chunked_workspace_size(qs, ks, vs, seg_chunks=seg,
+                                                          state=args.state), 256),
+                             dtype=torch.uint8, device=dev)
 
-        def step():
-            K.fwd_chunked(qs, ks, vs, out=os_, workspace=ws, state=args.state)
+            def step():
+                K.fwd_chunked(qs, ks, vs, seg_chunks=seg, out=os_, workspace=ws,
+                              state=args.state)
 
-        ms, _ = timed_steps(step, 20, 5, dev)
-        out.append({"T": T, "B": B, "ms": round(ms, 5),
-                    "tokens_per_s": round(B * 16 * T / (ms / 1e3), 1)})
-        del ws
+            ms, _ = timed_steps(step, 20, 5, dev)
+            point[key + "ms"] = round(ms, 5)
+            point[key + "tokens_per_s"] = round(B * 16 * T / (ms / 1e3), 1)
+            del ws
+        point["scan_speedup"] = round(point["sequential_ms"] / point["ms"], 3)
+        out.append(point)
     return out
 
 
@@ -232,6 +241,8 @@ def run_chunked(args, dev, w):
             and args.layout == "bthd":
         del ws
         line["sweep"] = sweep(q, k, v, args, dev)
+        sp = [x["scan_speedup"] for x in line["sweep"]]
+        line["scan_speedup_mean"] = round(sum(sp) / len(sp), 3)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     return line

@@ -63,7 +63,10 @@ typedef enum { KATA_STATE_DIRECT = 0, KATA_STATE_PACKED = 1 } kata_state_layout;
  *          form); chunk c covers tokens [cC, (c+1)C).
  *   seg_chunks: chunked form only: chunks per segment L (0 = library default).  The chunked
  *          form keeps the running state on chip for L consecutive chunks and combines the
- *          per-segment states with the prefix scan; L = 1 scans every chunk state.
+ *          per-segment states with the prefix scan; L = 1 scans every chunk state, and
+ *          L >= T / chunk is the sequential inter-chunk form (one segment per sequence carries
+ *          the state through every chunk in order; no scan).  The fp32 kernels always scan
+ *          every chunk state.
  *   state_layout: chunked form only, a kata_state_layout.  PACKED is implemented by the bf16
  *          p = 16, dv = 64, chunk = 64 kernels; every other problem computes the direct form
  *          whatever this field says.

@@ -317,7 +317,7 @@ __device__ __forceinline__ void zero_pad_rows(TilesT<kPacked>& tl, int tid) {
 // ==========================================================================================
 template <bool kPacked>
 __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
-    DevProblem pr, int L, int n_seg, const __bf16* __restrict__ k,
+    DevProblem pr, int L, int n_seg, int n_used, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, float* __restrict__ states) {
   using LY = Layout<kPacked>;
   __shared__ TilesT<kPacked> tl[2];
@@ -326,6 +326,14 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
   const int n_chunks = pr.T / C;
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
   const long long sv_t = pr.sv[1];
+  if (seg >= n_used) {
+    // a state no prefix needs (the last segment's, in the forward): zeros for the scan, and
+    // its k, v are not read
+    float4* out = reinterpret_cast<float4*>(
+        states + ((long long)(b * pr.H + h) * n_seg + seg) * LY::kStateFloats);
+    for (int x = tid; x < LY::kStateFloats / 4; x += kThreads) out[x] = float4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
 
   f32x4 S[LY::kSlots][4];
 #pragma unroll
@@ -403,19 +411,21 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
   const long long sv_t = pr.sv[1];
 
-  // prefix state of this segment
-  const float* pre = states + ((long long)(b * pr.H + h) * n_seg + seg) * LY::kStateFloats;
+  // prefix state of this segment (states == nullptr: one segment per sequence, prefix zero)
+  const float* pre =
+      states ? states + ((long long)(b * pr.H + h) * n_seg + seg) * LY::kStateFloats : nullptr;
   f32x4 S[LY::kSlots][4];
 #pragma unroll
   for (int sl = 0; sl < LY::kSlots; ++sl) {
     const int t = LY::tile(w, sl);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
-      S[sl][nt] = LY::owns(w, sl) ? *reinterpret_cast<const f32x4*>(pre + ((t * 4 + nt) * 64 + lane) * 4)
-                                  : zero4();
+      S[sl][nt] = (pre && LY::owns(w, sl))
+                      ? *reinterpret_cast<const f32x4*>(pre + ((t * 4 + nt) * 64 + lane) * 4)
+                      : zero4();
   }
   // every wave keeps its own copy of Z_{<c} (4 registers); lane holds Z[4g + r][lane % 16]
-  f32x4 Z = *reinterpret_cast<const f32x4*>(pre + LY::kZOff + lane * 4);
+  f32x4 Z = pre ? *reinterpret_cast<const f32x4*>(pre + LY::kZOff + lane * 4) : zero4();
   UpdateRows<kPacked> ur;
   ur.init(w, lane);
   zero_pad_rows(tl, tid);
@@ -705,15 +715,18 @@ hipError_t launch_quadratic_fast(const DevProblem& pr, bool out_bf16, const void
 }
 
 hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int L, int n_seg,
-                                   const void* k, const void* v, float* states, hipStream_t st) {
+                                   int n_used, const void* k, const void* v, float* states,
+                                   hipStream_t st) {
   if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;
   dim3 grid(n_seg, pr.H, pr.B);
   if (packed)
-    chunk_state_fast_kernel<true><<<grid, kThreads, 0, st>>>(pr, L, n_seg, (const __bf16*)k,
-                                                             (const __bf16*)v, states);
+    chunk_state_fast_kernel<true><<<grid, kThreads, 0, st>>>(pr, L, n_seg, n_used,
+                                                             (const __bf16*)k, (const __bf16*)v,
+                                                             states);
   else
-    chunk_state_fast_kernel<false><<<grid, kThreads, 0, st>>>(pr, L, n_seg, (const __bf16*)k,
-                                                              (const __bf16*)v, states);
+    chunk_state_fast_kernel<false><<<grid, kThreads, 0, st>>>(pr, L, n_seg, n_used,
+                                                              (const __bf16*)k, (const __bf16*)v,
+                                                              states);
   return hipGetLastError();
 }
 

@@ -20,8 +20,10 @@ hipError_t launch_quadratic_fast(const DevProblem& pr, bool out_bf16, const void
                                  hipStream_t st);
 bool quadratic_fast_supported(const kata_problem* pr);
 bool chunk_fast_available();
+// Segment states; segments seg >= n_used get a zero state without reading their tokens.
 hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int L, int n_seg,
-                                   const void* k, const void* v, float* states, hipStream_t st);
+                                   int n_used, const void* k, const void* v, float* states,
+                                   hipStream_t st);
 hipError_t launch_chunk_output_fast(const DevProblem& pr, bool packed, bool out_bf16, int L,
                                     int n_seg, const void* q, const void* k, const void* v,
                                     void* o, float* den, const float* states, hipStream_t st);
@@ -228,22 +230,29 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
   float* states = reinterpret_cast<float*>(workspace);
   char* scan_ws = reinterpret_cast<char*>(workspace) + cp.states_bytes;
   hipError_t e;
-  {
-    Timed t(KATA_K_CHUNK_STATE, st);
-    e = cp.fast ? kata::launch_chunk_state_fast(dp, cp.packed, cp.L, cp.n_seg, k, v, states, st)
-                : kata::launch_chunk_state_generic(dp, in_bf16, k, v, states, cp.n_chunks, st);
+  // One segment per sequence (the sequential inter-chunk form): every walk starts from a zero
+  // prefix, so no segment state or scan is needed.
+  const bool one_segment = cp.fast && cp.n_seg == 1;
+  if (!one_segment) {
+    {
+      Timed t(KATA_K_CHUNK_STATE, st);
+      // the last segment's state enters no prefix
+      e = cp.fast ? kata::launch_chunk_state_fast(dp, cp.packed, cp.L, cp.n_seg, cp.n_seg - 1, k,
+                                                  v, states, st)
+                  : kata::launch_chunk_state_generic(dp, in_bf16, k, v, states, cp.n_chunks, st);
+    }
+    if (e != hipSuccess) return launch_status(e, "chunk-state kernel");
+    {
+      // exclusive prefix over segments
+      Timed t(KATA_K_SCAN, st);
+      e = run_scan(states, cp.n_seq, cp.n_seg, cp.state_elems, 1, nullptr, scan_ws, st);
+    }
+    if (e != hipSuccess) return launch_status(e, "chunk-state scan");
   }
-  if (e != hipSuccess) return launch_status(e, "chunk-state kernel");
-  {
-    // exclusive prefix over segments (one segment: the prefix is zero)
-    Timed t(KATA_K_SCAN, st);
-    e = run_scan(states, cp.n_seq, cp.n_seg, cp.state_elems, 1, nullptr, scan_ws, st);
-  }
-  if (e != hipSuccess) return launch_status(e, "chunk-state scan");
   {
     Timed t(KATA_K_CHUNK_OUTPUT, st);
     e = cp.fast ? kata::launch_chunk_output_fast(dp, cp.packed, out_bf16, cp.L, cp.n_seg, q,
-                                                 k, v, o, den, states, st)
+                                                 k, v, o, den, one_segment ? nullptr : states, st)
                 : kata::launch_chunk_output_generic(dp, in_bf16, out_bf16, q, k, v, o, den,
                                                     states, cp.n_chunks, st);
   }
@@ -330,7 +339,8 @@ kata_status kata_recurrent_state(const kata_problem* pr, const void* k, const vo
   hipError_t e;
   {
     Timed t(KATA_K_CHUNK_STATE, st);
-    e = cp.fast ? kata::launch_chunk_state_fast(dp, false, cp.L, cp.n_seg, k, v, states, st)
+    e = cp.fast ? kata::launch_chunk_state_fast(dp, false, cp.L, cp.n_seg, cp.n_seg, k, v,
+                                                states, st)
                 : kata::launch_chunk_state_generic(dp, pr->in_dtype == KATA_BF16, k, v, states,
                                                    cp.n_chunks, st);
   }

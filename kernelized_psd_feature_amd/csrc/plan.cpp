@@ -147,12 +147,16 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
   if (cp.fast) {
     int L = pr->seg_chunks;
     if (L == 0) {
-      // Fill the workgroup slots of the GPU (256 CUs x 3 resident workgroups) in as few whole
-      // rounds as possible, with segments of at most 64 chunks: fewer, longer segments mean
-      // less prefix-scan traffic, whole rounds avoid an idle tail.
-      const int64_t slots = 768;
+      // With a walk per sequence on every CU (B*H >= 256), one segment per sequence: no
+      // segment states (which cost a second read of k and v) and no scan.  Otherwise fill the
+      // workgroup slots of the GPU (256 CUs x 3 resident workgroups) in as few whole rounds as
+      // possible, with segments of at most 64 chunks: fewer, longer segments mean less
+      // prefix-scan traffic, whole rounds avoid an idle tail.
+      const int64_t slots = 768, cus = 256;
       L = 1;
-      if (cp.n_seq * cp.n_chunks > slots) {
+      if (cp.n_seq >= cus) {
+        L = cp.n_chunks;
+      } else if (cp.n_seq * cp.n_chunks > slots) {
         for (int64_t rounds = 1;; ++rounds) {
           const int64_t seg_target = (rounds * slots) / cp.n_seq;
           if (seg_target < 1) continue;

@@ -472,6 +472,28 @@ def test_timing_records_every_kernel():
     assert all(ms > 0 for n, ms in t.values() if n)
 
 
+def test_single_segment_plan_launches_only_the_walk():
+    # one segment per sequence (the sequential inter-chunk form): no state pass, no scan
+    w = W.WORKLOADS[2]
+    q, k, v = _to_gpu(*W.make_inputs(w, 0, T=1024, B=1, H=4))
+    K.timing_begin()
+    o = K.fwd_chunked(q, k, v, seg_chunks=16)
+    t = K.timing_end()
+    assert t["chunk_state"][0] == 0 and t["scan"][0] == 0 and t["chunk_output"][0] == 1
+    ref, _ = O.closed_form(*(_np(x.cpu()) for x in (q, k, v)))
+    assert float((o.cpu().double() - torch.from_numpy(ref)).abs().max()) <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("state", ["packed", "direct"])
+def test_sequential_inter_chunk_form_long_context(state):
+    w = W.WORKLOADS[4]
+    q, k, v = W.make_inputs(w, 0, H=2)
+    o = K.fwd_chunked(*_to_gpu(q, k, v), chunk=64, seg_chunks=w.T // 64, state=state).cpu()
+    rng = np.random.default_rng(77)
+    _check_rows(q, k, v, o, [(0, 0), (0, 1)], _rows_sampler(rng, 128), TOL[w.dtype],
+                tag=f"sequential inter-chunk form, 131k tokens, {state}")
+
+
 def test_single_runtime_is_loaded():
     # the library must resolve the HIP runtime torch already loaded, not a second copy
     K._lib()
