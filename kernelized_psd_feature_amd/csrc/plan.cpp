@@ -116,9 +116,13 @@ ScanPlan plan_scan(int64_t n_seq, int64_t n, int64_t elems) {
   if (n <= 0 || n_seq <= 0 || elems <= 0) return sp;
   int64_t np2 = next_pow2(n);
   if (np2 * 4 <= kScanLdsFloats) {
-    // one tree over all n rows; strip of coordinates as wide as the LDS tile allows
-    int64_t strip = kScanLdsFloats / np2;
-    if (strip > 64) strip = 64;
+    // one tree over all n rows; a strip of at least 64 coordinates, widened for short scans
+    // so that a workgroup moves about 2048 floats (few rows would otherwise leave most of
+    // its threads idle; wider strips cost parallelism), and at most what the LDS tile holds
+    const int64_t cap = kScanLdsFloats / np2;
+    int64_t strip = ((2048 / n + 63) / 64) * 64;
+    if (strip < 64) strip = 64;
+    if (strip > cap) strip = cap;
     sp.strip = strip;
     sp.tile_rows = n;
     sp.n_tiles = 1;
