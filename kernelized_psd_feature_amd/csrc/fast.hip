@@ -16,25 +16,12 @@
 // only as a readout operand.  Z = sum k k^T is exact (bf16 x bf16 products in fp32), and the
 // inter-chunk denominator q^T Z q is evaluated in fp32 on the vector ALUs.
 //
-// MFMA fragment conventions (v_mfma_f32_16x16x32_bf16 / _16x16x16bf16_1k, wave64):
-//   A (16 x K): lane l holds row l%16 and K-slots [KPL*(l/16), KPL*(l/16)+KPL)
-//   B (K x 16): lane l holds column l%16 and the same K-slots
-//   D (16 x 16 fp32): lane l holds column l%16, rows 4*(l/16) + r, r = 0..3
-// A contraction only needs A and B to enumerate K in the same order, so the K order below is
-// chosen to match the D layout of the producing product ("slot kappa"): for a 32-wide K step m
-// over keys, slot r' of lane group g is key 32m + 16*(r'/4) + 4g + r'%4.  With that order the
-// squared-score tile (computed transposed, keys as rows) is directly the A operand of P.V, and
-// the fp32 state tiles are directly the B operand of the readout.
 #include "device.h"
 #include "kata.h"
+#include "mfma_util.h"
 
 namespace kata {
 namespace {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int P = 16, DV = 64, C = 64, F = P * P;
 constexpr int kThreads = 256;
@@ -44,17 +31,6 @@ constexpr int kStateFloats = F * (DV + 1);     // 16640: S (4 waves x 16 tiles x
 constexpr int QROW = 20;                       // bf16 per q / k row: 40 B, 8-byte aligned
 constexpr int KTROW = 68;                      // fp32 per row of the K^T tile
 constexpr int VROW = 80;                       // bf16 per v row: 160 B, 16-byte aligned
-
-__device__ __forceinline__ f32x4 mfma32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(const s16x4& a, const s16x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // ---- chunk tiles in LDS ------------------------------------------------------------------
 // kPacked adds rows to the K^T tile: rows 16..31 hold 2 k (the weight of an off-diagonal
@@ -75,8 +51,6 @@ struct Stage {
   uint4 qk;
   uint4 v0, v1;
 };
-
-__device__ __forceinline__ uint4 ld16(const __bf16* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // Per-thread global addresses of the staged pieces; advanced by one chunk with `next`.
 struct StagePtrs {
@@ -141,20 +115,6 @@ __device__ __forceinline__ void stage_store(const Stage& st, TilesT<kPacked>& tl
   *reinterpret_cast<uint4*>(&tl.V[2 * a + 1][8 * c8]) = st.v1;
 }
 
-// B operand of a 32-key step m for value columns [16 nt, 16 nt + 16), slot order kappa, read
-// from the row-major V tile with two LDS transpose loads.  Within a 16-lane block, lane i's
-// slot r of ds_read_b64_tr_b16 is element (i % 4) of the 8 bytes addressed by block lane
-// 4r + i/4; block lane j therefore points at V[key(g, j/4)][16 nt + 4 (j % 4)], which hands
-// lane i the value V[key(g, r)][16 nt + i].
-__device__ __forceinline__ bf16x8 v_frag(const __bf16 (*V)[VROW], int m, int nt, int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const int row = 32 * m + 4 * g + (j >> 2), col = 16 * nt + 4 * (j & 3);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&V[row][col]));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&V[row + 16][col]));
-  const uint2 ul = __builtin_bit_cast(uint2, lo), uh = __builtin_bit_cast(uint2, hi);
-  return __builtin_bit_cast(bf16x8, uint4{ul.x, ul.y, uh.x, uh.y});
-}
-
 // A operand of the state update for feature rows f = 16 i + (lane%16), i fixed, 32-key step
 // m: phi_f(k_s) = k_s[i] k_s[j], slot order kappa.
 template <class TL>
@@ -172,15 +132,8 @@ __device__ __forceinline__ bf16x8 phik_frag(const TL& tl, int i, int m, int lane
   return f;
 }
 
-// Packed layout: tile t (0..9) row 4g + r holds the state row of the pair
-// (a + (t & 1), 4J + r), (a, J) the double group 4 (t >> 1) + g.  The 20 double groups list,
-// for J = 0..3, the even a <= 4J + 2: every unique pair i <= j appears exactly once (weight 2
-// off the diagonal, 1 on it) and the 24 pairs i > j are zero rows.
-__device__ __forceinline__ void double_group(int idx, int& a, int& J) {
-  J = idx < 2 ? 0 : idx < 6 ? 1 : idx < 12 ? 2 : 3;
-  const int start = J == 0 ? 0 : J == 1 ? 2 : J == 2 ? 6 : 12;
-  a = 2 * (idx - start);
-}
+// Packed layout: tile t (0..9) row 4g + r holds the state row of the pair (a + (t & 1), 4J + r),
+// (a, J) = double_group(4 (t >> 1) + g); see double_group for the covering of the pairs.
 // Tiles owned by wave w: slots 0, 1 -> tiles 2w, 2w + 1; slot 2 -> tile 8 + w (waves 0, 1).
 __device__ __forceinline__ int packed_tile(int w, int slot) { return slot < 2 ? 2 * w + slot : 8 + w; }
 
@@ -219,25 +172,6 @@ __device__ __forceinline__ s16x4 row4_frag(const __bf16 (*X)[QROW], int row0, in
   const uint2 u = *reinterpret_cast<const uint2*>(&X[row0 + (lane & 15)][4 * (lane >> 4)]);
   return __builtin_bit_cast(s16x4, u);
 }
-
-// Squared, causally masked score tile -> bf16 P slots and their fp32 row-sum share.
-// sc holds S^T[s][t] for keys s = s0 + 4g + r and query t = t0 + lane%16.
-template <bool kMask>
-__device__ __forceinline__ void square_mask(const f32x4& sc, int s0, int t, int lane,
-                                            __bf16 out[4], float& lsum) {
-  const int g = lane >> 4;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float x = sc[r];
-    __bf16 pb = (__bf16)(x * x);
-    if (kMask) pb = (s0 + 4 * g + r <= t) ? pb : (__bf16)0.f;   // select, never multiply
-    out[r] = pb;
-    lsum += (float)pb;
-  }
-}
-
-template <typename Tout>
-__device__ __forceinline__ Tout cvt_out(float x) { return from_f32<Tout>(x); }
 
 // ==========================================================================================
 // Per-layout constants shared by the state and walk kernels.

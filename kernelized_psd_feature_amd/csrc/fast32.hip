@@ -1,0 +1,625 @@
+// bf16 MFMA kernels for gfx950 at p = 32, d_v = 64, chunk C = 64: the chunk-state build and
+// the segment walk of the chunked forward, and the flash-style quadratic forward.
+//
+// Same method and precision as the p = 16 kernels (gist.science "Technische Samenvatting"
+// sections 2.1-2.3; ai.info AI summary, Main Findings): a_ts = (q_t . k_s)^2, bf16 MFMA
+// products with fp32 accumulation, P rounded to bf16 with the row sum taken from the rounded
+// values, fp32 running state, inter-chunk denominator q^T Z q in fp32 (Z split into bf16 hi +
+// lo on MFMA).
+//
+// The state is always packed (the 528 unique pairs i <= j of the 32 x 32 feature, the ai.info
+// state-size bullet's packed coordinates): 72 double groups = 36 tiles of 16 rows, 18 readout
+// K steps.  That is 147 KB of fp32 per state, too much for four waves' registers, so a
+// workgroup has eight waves (two per SIMD, one workgroup per CU):
+//   state tiles  wave w owns tiles rank(w) + 8 s (5 tiles for ranks 0-3, 4 for ranks 4-7; the
+//                waves with the most intra-chunk work own fewer),
+//   tokens       wave w serves tokens [16 tg, 16 tg + 16) of a chunk, tg = w % 4, and the value
+//                columns [32 ch, 32 ch + 32), ch = w / 4, so no partial outputs cross waves.
+#include "device.h"
+#include "kata.h"
+#include "mfma_util.h"
+
+namespace kata {
+namespace {
+
+constexpr int P = 32, DV = 64, C = 64;
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int kTiles = 36, kSteps = 18, kSlots = 5;
+constexpr int kZOff = kTiles * 16 * DV;              // 36864
+constexpr int kStateFloats = kZOff + 4 * 256;        // + Z as 2 x 2 tiles of 16 x 16
+static_assert(kStateFloats == 36 * 16 * 64 + 4 * 256, "packed p = 32 state size (plan.h)");
+constexpr int QROW = 40;                             // bf16 per q / k row: 80 B
+constexpr int KTROW = 68;                            // fp32 per K^T row
+constexpr int VROW = 80;                             // bf16 per v row: 160 B
+constexpr int KTROWS = 2 * P + 1;                    // k, 2 k, zeros
+
+struct __align__(16) Tiles32 {
+  __bf16 Qs[C][QROW];
+  __bf16 Ks[C][QROW];
+  float KT[KTROWS][KTROW];
+  __bf16 V[C][VROW];
+};
+
+struct __align__(16) StateTiles32 {                  // the state pass needs no q and no k rows
+  float KT[KTROWS][KTROW];
+  __bf16 V[C][VROW];
+};
+
+// waves in the order that receives 5, 5, 5, 5, 4, 4, 4, 4 tiles: token groups 0 and 1 first
+__device__ __forceinline__ int wave_rank(int w) { return (w & 1) | ((w >> 2) << 1) | (((w >> 1) & 1) << 2); }
+__device__ __forceinline__ bool owns(int w, int s) { return wave_rank(w) + 8 * s < kTiles; }
+__device__ __forceinline__ int tile_of(int w, int s) { return wave_rank(w) + 8 * s; }
+
+// One thread's share of a chunk's loads: threads 0-255 a quarter q row, 256-511 a quarter
+// k row (row = (tid & 255) / 4, columns 8 (tid % 4) ..), every thread 16 B of one v row
+// (row tid / 8, columns 8 (tid % 8) ..).
+struct Stage32 {
+  uint4 qk, v;
+};
+
+struct Ptrs32 {
+  const __bf16* qk;
+  const __bf16* v;
+  long long qk_step, v_step;
+  __device__ __forceinline__ void next() {
+    if (qk) qk += qk_step;
+    v += v_step;
+  }
+};
+
+__device__ __forceinline__ Ptrs32 ptrs32(const DevProblem& pr, const __bf16* q, const __bf16* k,
+                                         const __bf16* v, int b, int h, int tok0, bool with_q,
+                                         int tid, int dir) {
+  Ptrs32 p;
+  const int lo = tid & 255, row = lo >> 2, qc = lo & 3;
+  if (tid < 256) {
+    p.qk = with_q ? q + row_off(pr.sq, b, tok0 + row, h) + 8 * qc : nullptr;
+    p.qk_step = (long long)dir * C * pr.sq[1];
+  } else {
+    p.qk = k + row_off(pr.sk, b, tok0 + row, h) + 8 * qc;
+    p.qk_step = (long long)dir * C * pr.sk[1];
+  }
+  p.v = v + row_off(pr.sv, b, tok0 + (tid >> 3), h) + 8 * (tid & 7);
+  p.v_step = (long long)dir * C * pr.sv[1];
+  return p;
+}
+
+__device__ __forceinline__ void load32(Stage32& s, const Ptrs32& p) {
+  if (p.qk) s.qk = ld16(p.qk);
+  s.v = ld16(p.v);
+}
+
+// k piece -> K^T rows (k, 2 k); q / k piece -> row-major rows (when the tile has them)
+template <class TL>
+__device__ __forceinline__ void store_kt(const Stage32& s, TL& tl, int tid) {
+  const int lo = tid & 255, row = lo >> 2, qc = lo & 3;
+  const uint32_t wd[4] = {s.qk.x, s.qk.y, s.qk.z, s.qk.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = bf_lo(wd[e]), c = bf_hi(wd[e]);
+    tl.KT[8 * qc + 2 * e][row] = a;
+    tl.KT[8 * qc + 2 * e + 1][row] = c;
+    tl.KT[P + 8 * qc + 2 * e][row] = 2.f * a;           // exact
+    tl.KT[P + 8 * qc + 2 * e + 1][row] = 2.f * c;
+  }
+}
+
+__device__ __forceinline__ void store32(const Stage32& s, Tiles32& tl, bool with_q, int tid) {
+  const int lo = tid & 255, row = lo >> 2, qc = lo & 3;
+  if (tid < 256) {
+    if (with_q) *reinterpret_cast<uint4*>(&tl.Qs[row][8 * qc]) = s.qk;
+  } else {
+    *reinterpret_cast<uint4*>(&tl.Ks[row][8 * qc]) = s.qk;
+    store_kt(s, tl, tid);
+  }
+  *reinterpret_cast<uint4*>(&tl.V[tid >> 3][8 * (tid & 7)]) = s.v;
+}
+
+__device__ __forceinline__ void store_state32(const Stage32& s, StateTiles32& tl, int tid) {
+  if (tid >= 256) store_kt(s, tl, tid);
+  *reinterpret_cast<uint4*>(&tl.V[tid >> 3][8 * (tid & 7)]) = s.v;
+}
+
+template <class TL>
+__device__ __forceinline__ void zero_row(TL& tl, int tid) {
+  if (tid < KTROW) tl.KT[2 * P][tid] = 0.f;
+}
+
+// A operand of the packed update for this lane's tile row (irow selects k_i, 2 k_i or zeros),
+// 32-key step m in slot order kappa.
+template <class TL>
+__device__ __forceinline__ bf16x8 phik(const TL& tl, int irow, int jrow, int m, int lane) {
+  const int g = lane >> 4;
+  const float4 ia = *reinterpret_cast<const float4*>(&tl.KT[irow][32 * m + 4 * g]);
+  const float4 ib = *reinterpret_cast<const float4*>(&tl.KT[irow][32 * m + 16 + 4 * g]);
+  const float4 ja = *reinterpret_cast<const float4*>(&tl.KT[jrow][32 * m + 4 * g]);
+  const float4 jb = *reinterpret_cast<const float4*>(&tl.KT[jrow][32 * m + 16 + 4 * g]);
+  bf16x8 f;
+  f[0] = (__bf16)(ia.x * ja.x); f[1] = (__bf16)(ia.y * ja.y);
+  f[2] = (__bf16)(ia.z * ja.z); f[3] = (__bf16)(ia.w * ja.w);
+  f[4] = (__bf16)(ib.x * jb.x); f[5] = (__bf16)(ib.y * jb.y);
+  f[6] = (__bf16)(ib.z * jb.z); f[7] = (__bf16)(ib.w * jb.w);
+  return f;
+}
+
+// k_s[16 mi + lane%16] over the slots of 32-key step m (operand of Z = K^T K)
+template <class TL>
+__device__ __forceinline__ bf16x8 kcol(const TL& tl, int mi, int m, int lane) {
+  const int i = 16 * mi + (lane & 15), g = lane >> 4;
+  const float4 a = *reinterpret_cast<const float4*>(&tl.KT[i][32 * m + 4 * g]);
+  const float4 c = *reinterpret_cast<const float4*>(&tl.KT[i][32 * m + 16 + 4 * g]);
+  bf16x8 f;
+  f[0] = (__bf16)a.x; f[1] = (__bf16)a.y; f[2] = (__bf16)a.z; f[3] = (__bf16)a.w;
+  f[4] = (__bf16)c.x; f[5] = (__bf16)c.y; f[6] = (__bf16)c.z; f[7] = (__bf16)c.w;
+  return f;
+}
+
+// Row sources of this lane's row of each owned tile.
+struct Rows32 {
+  int irow[kSlots], jrow[kSlots];
+  __device__ void init(int w, int lane) {
+#pragma unroll
+    for (int sl = 0; sl < kSlots; ++sl) {
+      const int t = owns(w, sl) ? tile_of(w, sl) : 0, row = lane & 15;
+      int a, J;
+      double_group(4 * (t >> 1) + (row >> 2), a, J);
+      const int i = a + (t & 1), j = 4 * J + (row & 3);
+      irow[sl] = i > j ? 2 * P : (i == j ? i : P + i);
+      jrow[sl] = j;
+    }
+  }
+};
+
+// S[slot] += Phi(K)^T V over one staged chunk; Z += K^T K (all four 16 x 16 tiles) if with_z.
+template <class TL>
+__device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, f32x4 (&S)[kSlots][4],
+                                         f32x4 (&Z)[2][2], int w, int lane, bool with_z) {
+#pragma unroll 1
+  for (int m = 0; m < 2; ++m) {
+    bf16x8 vb[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(tl.V, m, nt, lane);
+#pragma unroll
+    for (int sl = 0; sl < kSlots; ++sl) {
+      if (!owns(w, sl)) continue;
+      const bf16x8 a = phik(tl, rw.irow[sl], rw.jrow[sl], m, lane);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) S[sl][nt] = mfma32(a, vb[nt], S[sl][nt]);
+    }
+    if (with_z) {
+      const bf16x8 k0 = kcol(tl, 0, m, lane), k1 = kcol(tl, 1, m, lane);
+      Z[0][0] = mfma32(k0, k0, Z[0][0]);
+      Z[0][1] = mfma32(k0, k1, Z[0][1]);
+      Z[1][0] = mfma32(k1, k0, Z[1][0]);
+      Z[1][1] = mfma32(k1, k1, Z[1][1]);
+    }
+  }
+}
+
+// ==========================================================================================
+// Segment state: S_seg = sum over the segment's chunks of Phi(K_c)^T V_c, Z_seg = sum K^T K.
+// Grid (n_seg, H, B); segments seg >= n_used get a zero state without reading their tokens.
+// State layout (floats): tile t, value tile nt, lane -> ((t * 4 + nt) * 64 + lane) * 4, then
+// Z tile (mi, kj) -> kZOff + ((mi * 2 + kj) * 64 + lane) * 4.
+// ==========================================================================================
+__global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
+    DevProblem pr, int L, int n_seg, int n_used, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, float* __restrict__ states) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  StateTiles32* tl = reinterpret_cast<StateTiles32*>(smem);    // two buffers
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int n_chunks = pr.T / C;
+  const int c0 = seg * L, nc = min(L, n_chunks - c0);
+  float* out = states + ((long long)(b * pr.H + h) * n_seg + seg) * kStateFloats;
+  if (seg >= n_used) {
+    float4* o4 = reinterpret_cast<float4*>(out);
+    for (int x = tid; x < kStateFloats / 4; x += kThreads) o4[x] = float4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  f32x4 S[kSlots][4], Z[2][2];
+#pragma unroll
+  for (int sl = 0; sl < kSlots; ++sl)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) S[sl][nt] = zero4();
+  Z[0][0] = Z[0][1] = Z[1][0] = Z[1][1] = zero4();
+  Rows32 rw;
+  rw.init(w, lane);
+  zero_row(tl[0], tid);
+  zero_row(tl[1], tid);
+
+  // last chunk first (the sum is order-free; the walk then starts on recently read chunks),
+  // one chunk in flight in registers, two LDS buffers, one barrier per chunk
+  Ptrs32 p = ptrs32(pr, nullptr, k, v, b, h, (c0 + nc - 1) * C, false, tid, -1);
+  Stage32 st;
+  load32(st, p);
+  store_state32(st, tl[0], tid);
+  if (nc > 1) {
+    p.next();
+    load32(st, p);
+  }
+  __syncthreads();
+  for (int c = 0; c < nc; ++c) {
+    update32(tl[c & 1], rw, S, Z, w, lane, w == 0);
+    if (c + 1 < nc) store_state32(st, tl[(c + 1) & 1], tid);   // buffer read last iteration
+    if (c + 2 < nc) {
+      p.next();
+      load32(st, p);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int sl = 0; sl < kSlots; ++sl) {
+    if (!owns(w, sl)) continue;
+    const int t = tile_of(w, sl);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      *reinterpret_cast<f32x4*>(out + ((t * 4 + nt) * 64 + lane) * 4) = S[sl][nt];
+  }
+  if (w == 0) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int kj = 0; kj < 2; ++kj)
+        *reinterpret_cast<f32x4*>(out + kZOff + ((mi * 2 + kj) * 64 + lane) * 4) = Z[mi][kj];
+  }
+}
+
+// ==========================================================================================
+// Segment walk (see the file comment for the work split).  Grid (n_seg, H, B).
+// ==========================================================================================
+struct __align__(16) Walk32Lds {
+  Tiles32 tl;
+  uint4 Sb[kSteps][4][64];        // S_{<c} as bf16 B operands: [K step][value tile][lane]
+  unsigned char dg[4 * kSteps][2];   // double group -> (a, J)
+};
+
+template <typename Tout>
+__global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
+    DevProblem pr, int L, int n_seg, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den_out,
+    const float* __restrict__ states) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  Walk32Lds& sm = *reinterpret_cast<Walk32Lds*>(smem);
+  Tiles32& tl = sm.tl;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int tg = w & 3, ch = w >> 2;
+  const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int n_chunks = pr.T / C;
+  const int c0 = seg * L, nc = min(L, n_chunks - c0);
+
+  const float* pre =
+      states ? states + ((long long)(b * pr.H + h) * n_seg + seg) * kStateFloats : nullptr;
+  f32x4 S[kSlots][4], Z[2][2];
+#pragma unroll
+  for (int sl = 0; sl < kSlots; ++sl) {
+    const int t = owns(w, sl) ? tile_of(w, sl) : 0;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      S[sl][nt] = (pre && owns(w, sl))
+                      ? *reinterpret_cast<const f32x4*>(pre + ((t * 4 + nt) * 64 + lane) * 4)
+                      : zero4();
+  }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int kj = 0; kj < 2; ++kj)
+      Z[mi][kj] = pre ? *reinterpret_cast<const f32x4*>(pre + kZOff + ((mi * 2 + kj) * 64 + lane) * 4)
+                      : zero4();
+  Rows32 rw;
+  rw.init(w, lane);
+  zero_row(tl, tid);
+  if (tid < 4 * kSteps) {
+    int a, J;
+    double_group(tid, a, J);
+    sm.dg[tid][0] = (unsigned char)a;
+    sm.dg[tid][1] = (unsigned char)(4 * J);
+  }
+
+  auto publish = [&]() {
+#pragma unroll
+    for (int sl = 0; sl < kSlots; ++sl) {
+      if (!owns(w, sl)) continue;
+      const int t = tile_of(w, sl);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 x;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = (__bf16)S[sl][nt][r];
+        reinterpret_cast<uint2*>(&sm.Sb[t >> 1][nt][lane])[t & 1] = __builtin_bit_cast(uint2, x);
+      }
+    }
+  };
+
+  Ptrs32 p = ptrs32(pr, q, k, v, b, h, c0 * C, true, tid, 1);
+  Stage32 st;
+  load32(st, p);
+  store32(st, tl, true, tid);
+  publish();
+  __syncthreads();
+
+  const int t = 16 * tg + l16;                 // this lane's token (fragment column / row)
+  Tout* orow = o + row_off(pr.so, b, c0 * C + 16 * tg + 4 * g, h) + 32 * ch + l16;
+  const long long so_t = pr.so[1];
+
+  for (int c = 0; c < nc; ++c) {
+    const int tok0 = (c0 + c) * C;
+    if (c + 1 < nc) {
+      p.next();
+      load32(st, p);
+    }
+
+    // ---- intra-chunk tile of this wave's tokens and value columns ----
+    float lsum = 0.f;
+    f32x4 O[2] = {zero4(), zero4()};
+    const bf16x8 qf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&tl.Qs[t][8 * g]));
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      if (2 * m > tg) break;                       // key tiles entirely in the future
+      __bf16 pa[8];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int ms = 2 * m + half;
+        if (ms <= tg) {
+          const bf16x8 kf = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const uint4*>(&tl.Ks[16 * ms + l16][8 * g]));
+          const f32x4 sc = mfma32(kf, qf, zero4());
+          if (ms < tg)
+            square_mask<false>(sc, 16 * ms, t, lane, &pa[4 * half], lsum);
+          else
+            square_mask<true>(sc, 16 * ms, t, lane, &pa[4 * half], lsum);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pa[4 * half + r] = (__bf16)0.f;
+        }
+      }
+      bf16x8 a;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) a[r] = pa[r];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) O[n] = mfma32(a, v_frag(tl.V, m, 2 * ch + n, lane), O[n]);
+    }
+
+    // ---- inter-chunk denominator q^T Z_{<c} q on MFMA (Z = hi + lo in bf16) ----
+    // Z tile (mi, kj)'s accumulator layout is, Z being symmetric, the A operand of output rows
+    // 16 kj.. and K rows 16 mi.. of y = Z q.
+    float zq = 0.f;
+    {
+      s16x4 qb[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+        qb[mi] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2*>(&tl.Qs[t][16 * mi + 4 * g]));
+#pragma unroll
+      for (int kj = 0; kj < 2; ++kj) {
+        f32x4 y = zero4();
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+          s16x4 zhi, zlo;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const __bf16 hi = (__bf16)Z[mi][kj][r];
+            zhi[r] = __builtin_bit_cast(short, hi);
+            zlo[r] = __builtin_bit_cast(short, (__bf16)(Z[mi][kj][r] - (float)hi));
+          }
+          y = mfma16(zhi, qb[mi], y);
+          y = mfma16(zlo, qb[mi], y);
+        }
+        // y[r] = (Z q_t)[16 kj + 4 g + r]
+        const uint2 qq = __builtin_bit_cast(uint2, qb[kj]);
+        zq = fmaf(bf_lo(qq.x), y[0], zq);
+        zq = fmaf(bf_hi(qq.x), y[1], zq);
+        zq = fmaf(bf_lo(qq.y), y[2], zq);
+        zq = fmaf(bf_hi(qq.y), y[3], zq);
+      }
+    }
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    zq += __shfl_xor(zq, 16);
+    zq += __shfl_xor(zq, 32);
+    const float D = pr.eps + (zq + lsum);          // D_t of token t (every lane group)
+    const float inv = 1.f / D;
+
+    // ---- readout phi(q_t)^T S_{<c} over the 18 K steps, this wave's two value tiles ----
+#pragma unroll 2
+    for (int kk = 0; kk < kSteps; ++kk) {
+      const int ga = sm.dg[4 * kk + g][0], gj = sm.dg[4 * kk + g][1];
+      const uint32_t qa = *reinterpret_cast<const uint32_t*>(&tl.Qs[t][ga]);
+      const uint2 qj = *reinterpret_cast<const uint2*>(&tl.Qs[t][gj]);
+      const float i0 = bf_lo(qa), i1 = bf_hi(qa);
+      const float jv[4] = {bf_lo(qj.x), bf_hi(qj.x), bf_lo(qj.y), bf_hi(qj.y)};
+      bf16x8 a;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        a[r] = (__bf16)(i0 * jv[r]);
+        a[4 + r] = (__bf16)(i1 * jv[r]);
+      }
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+        O[n] = mfma32(a, __builtin_bit_cast(bf16x8, sm.Sb[kk][2 * ch + n][lane]), O[n]);
+    }
+
+    // ---- gate and store: lane holds tokens 16 tg + 4 g + r, columns 32 ch + 16 n + l16 ----
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ir = __shfl(inv, 4 * g + r);    // token 4 g + r's 1 / D (lane 4 g + r)
+      Tout* op = orow + r * so_t;
+#pragma unroll
+      for (int n = 0; n < 2; ++n) __builtin_nontemporal_store(cvt_out<Tout>(O[n][r] * ir), op + 16 * n);
+    }
+    if (den_out && ch == 0 && lane < 16)
+      den_out[((long long)b * pr.T + tok0 + t) * pr.H + h] = D;
+    orow += C * so_t;
+
+    // ---- state update with this chunk ----
+    update32(tl, rw, S, Z, w, lane, true);
+    __syncthreads();                               // all reads of this chunk's tiles and Sb
+    if (c + 1 < nc) {
+      store32(st, tl, true, tid);
+      publish();
+    }
+    __syncthreads();
+  }
+}
+
+// ==========================================================================================
+// Flash-style quadratic forward at p = 32: 64 queries per workgroup (16 per wave, 4 waves),
+// key blocks of 64 staged in LDS.  Grid (ceil(T/64), H, B), heaviest blocks first.
+// ==========================================================================================
+constexpr int kQThreads = 256;
+
+struct QStage {
+  uint4 k, v0, v1;
+};
+
+struct __align__(16) Quad32Lds {
+  __bf16 Ks[C][QROW];
+  __bf16 V[C][VROW];
+  float inv[C];
+  float den[C];
+};
+
+template <typename Tout>
+__global__ __launch_bounds__(kQThreads, 2) void quadratic32_kernel(
+    DevProblem pr, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den_out) {
+  __shared__ Quad32Lds sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int qb = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int t0 = qb * C;
+  const int t = t0 + 16 * w + l16;
+  bf16x8 qf = __builtin_bit_cast(bf16x8, uint4{0u, 0u, 0u, 0u});
+  if (t < pr.T) qf = __builtin_bit_cast(bf16x8, ld16(q + row_off(pr.sq, b, t, h) + 8 * g));
+
+  // staging: a quarter k row per thread (row tid / 4), 16 B of two v rows per thread
+  const int kr = tid >> 2, kc = tid & 3, a2 = tid >> 3, c8 = tid & 7;
+  auto load = [&](int s0) {
+    QStage x;
+    x.k = s0 + kr < pr.T ? ld16(k + row_off(pr.sk, b, s0 + kr, h) + 8 * kc) : uint4{0u, 0u, 0u, 0u};
+    const int s = s0 + 2 * a2;
+    x.v0 = s < pr.T ? ld16(v + row_off(pr.sv, b, s, h) + 8 * c8) : uint4{0u, 0u, 0u, 0u};
+    x.v1 = s + 1 < pr.T ? ld16(v + row_off(pr.sv, b, s + 1, h) + 8 * c8) : uint4{0u, 0u, 0u, 0u};
+    return x;
+  };
+  auto store = [&](const QStage& x) {
+    *reinterpret_cast<uint4*>(&sm.Ks[kr][8 * kc]) = x.k;
+    *reinterpret_cast<uint4*>(&sm.V[2 * a2][8 * c8]) = x.v0;
+    *reinterpret_cast<uint4*>(&sm.V[2 * a2 + 1][8 * c8]) = x.v1;
+  };
+  auto key_frag = [&](int ms) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.Ks[16 * ms + l16][8 * g]));
+  };
+
+  f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
+  float lsum = 0.f;
+  QStage x = load(0);
+  store(x);
+  __syncthreads();
+  for (int kb = 0; kb <= qb; ++kb) {
+    if (kb < qb) x = load((kb + 1) * C);
+    const int s_base = kb * C;
+    const bool diag = (kb == qb);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      if (diag && 2 * m > w) break;
+      __bf16 pa[8];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int ms = 2 * m + half;
+        if (!diag || ms < w) {
+          const f32x4 sc = mfma32(key_frag(ms), qf, zero4());
+          square_mask<false>(sc, s_base + 16 * ms, t, lane, &pa[4 * half], lsum);
+        } else if (ms == w) {
+          const f32x4 sc = mfma32(key_frag(ms), qf, zero4());
+          square_mask<true>(sc, s_base + 16 * ms, t, lane, &pa[4 * half], lsum);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pa[4 * half + r] = (__bf16)0.f;
+        }
+      }
+      bf16x8 af;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) af[r] = pa[r];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) O[nt] = mfma32(af, v_frag(sm.V, m, nt, lane), O[nt]);
+    }
+    __syncthreads();
+    if (kb < qb) store(x);
+    __syncthreads();
+  }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (g == 0) {
+    const float D = pr.eps + lsum;
+    sm.den[16 * w + l16] = D;
+    sm.inv[16 * w + l16] = 1.f / D;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tr = 16 * w + 4 * g + r;
+    if (t0 + tr >= pr.T) continue;
+    const float inv = sm.inv[tr];
+    Tout* op = o + row_off(pr.so, b, t0 + tr, h);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) op[16 * nt + l16] = cvt_out<Tout>(O[nt][r] * inv);
+  }
+  if (den_out && lane < 16 && t0 + 16 * w + lane < pr.T)
+    den_out[((long long)b * pr.T + t0 + 16 * w + lane) * pr.H + h] = sm.den[16 * w + lane];
+}
+
+}  // namespace
+
+bool fast32_supported(const kata_problem* pr) {
+  return pr->in_dtype == KATA_BF16 && pr->p == P && pr->dv == DV && pr->groups <= 1;
+}
+
+hipError_t launch_chunk_state32(const DevProblem& pr, int L, int n_seg, int n_used,
+                                const void* k, const void* v, float* states, hipStream_t st) {
+  if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;
+  const size_t lds = 2 * sizeof(StateTiles32);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_state32_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  chunk_state32_kernel<<<dim3(n_seg, pr.H, pr.B), kThreads, lds, st>>>(
+      pr, L, n_seg, n_used, (const __bf16*)k, (const __bf16*)v, states);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int n_seg,
+                                 const void* q, const void* k, const void* v, void* o,
+                                 float* den, const float* states, hipStream_t st) {
+  if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;
+  const size_t lds = sizeof(Walk32Lds);
+  dim3 grid(n_seg, pr.H, pr.B);
+  const __bf16 *qq = (const __bf16*)q, *kk = (const __bf16*)k, *vv = (const __bf16*)v;
+  hipError_t e;
+  if (out_bf16) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_output32_kernel<__bf16>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    chunk_output32_kernel<__bf16><<<grid, kThreads, lds, st>>>(pr, L, n_seg, qq, kk, vv,
+                                                               (__bf16*)o, den, states);
+  } else {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_output32_kernel<float>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    chunk_output32_kernel<float><<<grid, kThreads, lds, st>>>(pr, L, n_seg, qq, kk, vv,
+                                                              (float*)o, den, states);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quadratic32(const DevProblem& pr, bool out_bf16, const void* q, const void* k,
+                              const void* v, void* o, float* den, hipStream_t st) {
+  if (pr.p != P || pr.dv != DV) return hipErrorInvalidValue;
+  dim3 grid((pr.T + C - 1) / C, pr.H, pr.B);
+  if (out_bf16)
+    quadratic32_kernel<__bf16><<<grid, kQThreads, 0, st>>>(
+        pr, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, den);
+  else
+    quadratic32_kernel<float><<<grid, kQThreads, 0, st>>>(
+        pr, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (float*)o, den);
+  return hipGetLastError();
+}
+
+}  // namespace kata

@@ -20,6 +20,14 @@ hipError_t launch_quadratic_fast(const DevProblem& pr, bool out_bf16, const void
                                  hipStream_t st);
 bool quadratic_fast_supported(const kata_problem* pr);
 bool chunk_fast_available();
+bool fast32_supported(const kata_problem* pr);
+hipError_t launch_chunk_state32(const DevProblem& pr, int L, int n_seg, int n_used,
+                                const void* k, const void* v, float* states, hipStream_t st);
+hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int n_seg,
+                                 const void* q, const void* k, const void* v, void* o,
+                                 float* den, const float* states, hipStream_t st);
+hipError_t launch_quadratic32(const DevProblem& pr, bool out_bf16, const void* q, const void* k,
+                              const void* v, void* o, float* den, hipStream_t st);
 // Segment states; segments seg >= n_used get a zero state without reading their tokens.
 hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int L, int n_seg,
                                    int n_used, const void* k, const void* v, float* states,
@@ -202,6 +210,9 @@ kata_status kata_fwd_quadratic(const kata_problem* pr, const void* q, const void
   if (pr->groups <= 1 && kata::quadratic_fast_supported(pr))
     return launch_status(kata::launch_quadratic_fast(dp, out_bf16, q, k, v, o, den, st),
                          "quadratic forward");
+  if (kata::fast32_supported(pr))
+    return launch_status(kata::launch_quadratic32(dp, out_bf16, q, k, v, o, den, st),
+                         "quadratic forward");
   return launch_status(kata::launch_quadratic_generic(dp, in_bf16, out_bf16, q, k, v, o, den, st),
                        "quadratic forward");
 }
@@ -237,9 +248,10 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
     {
       Timed t(KATA_K_CHUNK_STATE, st);
       // the last segment's state enters no prefix
-      e = cp.fast ? kata::launch_chunk_state_fast(dp, cp.packed, cp.L, cp.n_seg, cp.n_seg - 1, k,
-                                                  v, states, st)
-                  : kata::launch_chunk_state_generic(dp, in_bf16, k, v, states, cp.n_chunks, st);
+      e = cp.fast32 ? kata::launch_chunk_state32(dp, cp.L, cp.n_seg, cp.n_seg - 1, k, v, states, st)
+          : cp.fast ? kata::launch_chunk_state_fast(dp, cp.packed, cp.L, cp.n_seg, cp.n_seg - 1,
+                                                    k, v, states, st)
+                    : kata::launch_chunk_state_generic(dp, in_bf16, k, v, states, cp.n_chunks, st);
     }
     if (e != hipSuccess) return launch_status(e, "chunk-state kernel");
     {
@@ -251,8 +263,11 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
   }
   {
     Timed t(KATA_K_CHUNK_OUTPUT, st);
-    e = cp.fast ? kata::launch_chunk_output_fast(dp, cp.packed, out_bf16, cp.L, cp.n_seg, q,
-                                                 k, v, o, den, one_segment ? nullptr : states, st)
+    const float* pre = one_segment ? nullptr : states;
+    e = cp.fast32 ? kata::launch_chunk_output32(dp, out_bf16, cp.L, cp.n_seg, q, k, v, o, den,
+                                                pre, st)
+        : cp.fast ? kata::launch_chunk_output_fast(dp, cp.packed, out_bf16, cp.L, cp.n_seg, q,
+                                                   k, v, o, den, pre, st)
                 : kata::launch_chunk_output_generic(dp, in_bf16, out_bf16, q, k, v, o, den,
                                                     states, cp.n_chunks, st);
   }
@@ -300,7 +315,9 @@ namespace {
 kata::ChunkPlan recurrent_plan(const kata_problem* pr) {
   kata_problem d = *pr;
   d.state_layout = KATA_STATE_DIRECT;
-  return kata::plan_chunked(&d, kata::chunk_fast_available());
+  kata::ChunkPlan cp = kata::plan_chunked(&d, kata::chunk_fast_available());
+  if (cp.fast32) cp = kata::plan_chunked(&d, false);   // p = 32: the fp32 state kernel
+  return cp;
 }
 
 kata_status check_state(const float* state) {

@@ -146,8 +146,10 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
   cp.n_chunks = pr->T / pr->chunk;
   cp.n_seq = int64_t(pr->B) * pr->H;
   cp.state_elems = int64_t(pr->p) * pr->p * (pr->dv + 1);
-  cp.fast = (fast_available && pr->in_dtype == KATA_BF16 && pr->p == 16 && pr->dv == 64 &&
-             pr->chunk == 64 && pr->groups <= 1) ? 1 : 0;
+  const bool mfma_shape = fast_available && pr->in_dtype == KATA_BF16 && pr->dv == 64 &&
+                          pr->chunk == 64 && pr->groups <= 1;
+  cp.fast = (mfma_shape && (pr->p == 16 || pr->p == 32)) ? 1 : 0;
+  cp.fast32 = (cp.fast && pr->p == 32) ? 1 : 0;
   if (cp.fast) {
     int L = pr->seg_chunks;
     if (L == 0) {
@@ -156,7 +158,8 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
       // workgroup slots of the GPU (256 CUs x 3 resident workgroups) in as few whole rounds as
       // possible, with segments of at most 64 chunks: fewer, longer segments mean less
       // prefix-scan traffic, whole rounds avoid an idle tail.
-      const int64_t slots = 768, cus = 256;
+      // (the p = 32 walk is one eight-wave workgroup per CU: 256 slots)
+      const int64_t cus = 256, slots = cp.fast32 ? 256 : 768;
       L = 1;
       if (cp.n_seq >= cus) {
         L = cp.n_chunks;
@@ -171,10 +174,10 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
     }
     if (L > cp.n_chunks) L = cp.n_chunks;
     cp.L = L;
-    cp.packed = pr->state_layout == KATA_STATE_PACKED ? 1 : 0;
+    cp.packed = (pr->state_layout == KATA_STATE_PACKED || cp.fast32) ? 1 : 0;
     // packed: 10 tiles of 16 rows (the 136 unique (i, j) rows and 24 zero rows) x 64 columns,
-    // plus the full 16 x 16 Z
-    if (cp.packed) cp.state_elems = 160 * 64 + 256;
+    // plus the full 16 x 16 Z; p = 32: 36 tiles (528 unique rows and 48 zero rows) and Z
+    if (cp.packed) cp.state_elems = cp.fast32 ? kState32Floats : 160 * 64 + 256;
   } else {
     cp.L = 1;   // the VALU path scans every chunk state
   }

@@ -15,6 +15,7 @@ enum class Form { Quadratic, Chunked, Backward };
 // Which kernels run a chunked forward, and the workspace they need.
 struct ChunkPlan {
   int fast = 0;               // 1: bf16 MFMA kernels; 0: fp32-arithmetic VALU kernels
+  int fast32 = 0;             // 1: the MFMA kernels are the p = 32 ones (always packed)
   int packed = 0;             // 1: the MFMA kernels keep the unique (i <= j) state rows
   int L = 1;                  // chunks per segment
   int n_chunks = 0;           // N_c = T / C per (b, h)
@@ -54,6 +55,9 @@ kata_status validate_tensor(const void* ptr, const int64_t st[3], size_t esize,
 ScanPlan plan_scan(int64_t n_seq, int64_t n, int64_t elems);
 // pr must have passed validate_problem; fast_available: the MFMA chunked kernels are built.
 ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available);
+
+// Floats in one packed p = 32 segment state (36 tiles of 16 x 64 plus Z as four 16 x 16 tiles).
+constexpr int64_t kState32Floats = 36 * 16 * 64 + 4 * 256;
 size_t bwd_workspace_bytes(const kata_problem* pr);
 
 }  // namespace kata

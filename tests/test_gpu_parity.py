@@ -757,3 +757,43 @@ def test_mg_groups_one_is_the_plain_computation_bitwise():
     for f in (lambda **kw: K.fwd_quadratic(q, k, v, **kw),
               lambda **kw: K.fwd_chunked(q, k, v, chunk=32, **kw)):
         assert torch.equal(f(), f(groups=1))
+
+
+# ------------------------------------------------------------ p = 32 MFMA kernels -------
+# The crossover recipe (bf16, p = 32, d_v = 64, C = 64): packed 528-row states, eight-wave walk.
+
+@pytest.mark.parametrize("T", [64, 256, 448])
+@pytest.mark.parametrize("form", ["chunked", "quadratic"])
+def test_p32_every_element(T, form):
+    w = W.WORKLOADS[3]
+    q, k, v = W.make_inputs(w, 40, T=T, B=2, H=3)
+    ref, dref = O.closed_form(_np(q), _np(k), _np(v))
+    o, d = _run(form, *_to_gpu(q, k, v), return_den=True)
+    err = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
+    say(f"p32 {form} T={T}: max-abs {err:.3e}")
+    assert err <= TOL[w.dtype]
+    np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=1e-2)
+
+
+@pytest.mark.parametrize("seg", [1, 3, 7, 64])
+def test_p32_segment_lengths(seg):
+    w = W.WORKLOADS[3]
+    q, k, v = W.make_inputs(w, 41, T=1024, B=1, H=2)
+    ref, _ = O.closed_form(_np(q), _np(k), _np(v))
+    o = K.fwd_chunked(*_to_gpu(q, k, v), seg_chunks=seg)
+    err = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
+    say(f"p32 seg_chunks={seg}: max-abs {err:.3e}")
+    assert err <= TOL[w.dtype]
+
+
+def test_p32_bf16_output_causality_and_determinism():
+    w = W.WORKLOADS[3]
+    q, k, v = _to_gpu(*W.make_inputs(w, 42, T=512, B=1, H=4))
+    for form in ("chunked", "quadratic"):
+        o32 = _run(form, q, k, v)
+        assert torch.equal(o32, _run(form, q, k, v))
+        assert torch.equal(_run(form, q, k, v, out_dtype=torch.bfloat16), o32.to(torch.bfloat16))
+        k2, v2 = k.clone(), v.clone()
+        k2[:, 320:] = float("nan")
+        v2[:, 320:] = float("inf")
+        assert torch.equal(o32[:, :320], _run(form, q, k2, v2)[:, :320]), form
