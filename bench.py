@@ -8,8 +8,9 @@ already resident in HBM and the output and workspace preallocated.  W untimed st
 steps timed with HIP events on the stream the kernels are launched on; the library's own
 per-kernel events give the dominant kernel's average duration for the roofline figure.
 
-Printed: one JSON line.  value = head-tokens (B*H*T) per second.  roofline: algorithmic bytes
-of the dominant kernel per launch / its average duration, against MI355X's 8 TB/s HBM peak.
+Printed: one JSON line.  value = head-tokens (B*H*T) per second.  roofline: the algorithmic
+bytes (bf16 q, k, v in, fp32 o out) or flops of the step, whichever bound is slower at MI355X's
+peaks (8 TB/s HBM, 2.5 PFLOP/s dense bf16 MFMA), over the dominant kernel's average duration.
 cpu_baseline: the fp64 CPU oracle (brute-force closed form) timed on a bounded uniform sample
 of the same workload's query rows, scaled to head-tokens/s.  sweep: tokens/s of the chunked
 form at T = 1k .. 128k with B*T = 131072 (the metric's dependence on T), each beside the
@@ -33,11 +34,19 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 KERNEL_SOURCES = {  # files whose content defines each kernel's code
     "chunk_output": ["kernelized_psd_feature_amd/csrc/fast.hip",
+                     "kernelized_psd_feature_amd/csrc/mfma_util.h",
                      "kernelized_psd_feature_amd/csrc/device.h"],
     "quadratic": ["kernelized_psd_feature_amd/csrc/fast.hip",
+                  "kernelized_psd_feature_amd/csrc/mfma_util.h",
                   "kernelized_psd_feature_amd/csrc/device.h"],
     "decode": ["kernelized_psd_feature_amd/csrc/decode.hip",
                "kernelized_psd_feature_amd/csrc/device.h"],
+    "chunk_output32": ["kernelized_psd_feature_amd/csrc/fast32.hip",
+                       "kernelized_psd_feature_amd/csrc/mfma_util.h",
+                       "kernelized_psd_feature_amd/csrc/device.h"],
+    "quadratic32": ["kernelized_psd_feature_amd/csrc/fast32.hip",
+                    "kernelized_psd_feature_amd/csrc/mfma_util.h",
+                    "kernelized_psd_feature_amd/csrc/device.h"],
 }
 
 
@@ -47,10 +56,30 @@ def algorithmic_bytes_per_token(p, dv, in_bytes=2, out_bytes=4):
 
 
 def chunked_flops_per_token(p, dv, C):
-    # state build 2p^2 dv + normalizer 2p^2, readout 2p^2 dv + q^T Z q (2p^2 + 2p),
-    # intra-chunk tile (C+1)/2 causal pairs on average of 2p + 2dv + 2 (score, square, PV,
-    # row sum), epilogue dv
-    return (4 * p * p * dv + 4 * p * p + 2 * p + (C + 1) * (p + dv + 1) + dv)
+    # state build and readout 2 p^2 (d_v + 1) each, intra-chunk tile (C+1)/2 causal pairs on
+    # average of 2 (p + d_v + 1) (score, PV, row sum), q^T Z q 2 p^2, the scan's
+    # 2 p^2 (d_v + 1) / C, epilogue d_v
+    return (4 * p * p * (dv + 1) + (C + 1) * (p + dv + 1) + 2 * p * p
+            + 2 * p * p * (dv + 1) // C + dv)
+
+
+def quadratic_flops_per_token(p, dv, T):
+    # (T + 1) / 2 causal pairs per query on average, 2 (p + d_v + 1) flops each, epilogue d_v
+    return (T + 1) * (p + dv + 1) + dv
+
+
+def roofline(flops, nbytes, seconds):
+    """The bound is whichever of the MFMA (bf16 dense) and HBM rooflines takes longer for
+    the algorithmic flops and bytes; achieved = that quantity / the measured time."""
+    t_mfma = flops / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    if t_mfma > t_hbm:
+        a = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(a, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(a / BF16_MFMA_PEAK_TFLOPS, 4)}
+    a = nbytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK_GBS, 4)}
 
 
 def source_sha(files):
@@ -214,8 +243,12 @@ def run_chunked(args, dev, w):
     launches, total_ms = per_kernel[dom]
     avg_ms = total_ms / max(launches, 1)
     bpt = algorithmic_bytes_per_token(w.p, w.dv)
-    achieved = bpt * tokens / (avg_ms / 1e3) / 1e9
-    sha = source_sha(KERNEL_SOURCES[dom])
+    fpt = (chunked_flops_per_token(w.p, w.dv, w.chunk) if args.form == "chunked"
+           else quadratic_flops_per_token(w.p, w.dv, w.T))
+    sources = KERNEL_SOURCES[dom if w.p == 16 else dom + "32"]
+    sha = source_sha(sources)
+    roof = roofline(fpt * tokens, bpt * tokens, avg_ms / 1e3)
+    roof["traffic"] = load_traffic(dom, w.name, sha)
     line = {
         "metric": METRIC, "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -225,13 +258,9 @@ def run_chunked(args, dev, w):
                    "chunk": w.chunk, "form": args.form, "seg_chunks": args.seg,
                    "state": args.state, "layout": args.layout.upper(), "out_dtype": "fp32",
                    "eps": 1e-6},
-        "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": load_traffic(dom, w.name, sha),
-        },
+        "roofline": roof,
         "kernels_ms": {n: round(t / max(c, 1), 5) for n, (c, t) in per_kernel.items() if c},
-        "step_roofline_frac": round(bpt * tokens / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_roofline_frac": roofline(fpt * tokens, bpt * tokens, ms / 1e3)["frac"],
         "dominant_kernel_source_sha": sha,
     }
     if not args.no_cold_cache:
