@@ -227,15 +227,15 @@ def run_chunked(args, dev, w):
     ws = None
     if args.form == "chunked":
         need = K.chunked_workspace_size(q, k, v, chunk=w.chunk, seg_chunks=args.seg,
-                                        state=args.state)
+                                        state=args.state, groups=args.groups)
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
     def step():
         if args.form == "chunked":
             K.fwd_chunked(q, k, v, chunk=w.chunk, seg_chunks=args.seg, out=o, workspace=ws,
-                          state=args.state)
+                          state=args.state, groups=args.groups)
         else:
-            K.fwd_quadratic(q, k, v, out=o)
+            K.fwd_quadratic(q, k, v, out=o, groups=args.groups)
 
     ms, per_kernel = timed_steps(step, args.steps, args.warmup, dev)
     tokens = w.B * w.H * w.T
@@ -256,8 +256,8 @@ def run_chunked(args, dev, w):
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "p": w.p, "dv": w.dv,
                    "chunk": w.chunk, "form": args.form, "seg_chunks": args.seg,
-                   "state": args.state, "layout": args.layout.upper(), "out_dtype": "fp32",
-                   "eps": 1e-6},
+                   "state": args.state, "groups": args.groups, "layout": args.layout.upper(),
+                   "out_dtype": "fp32", "eps": 1e-6},
         "roofline": roof,
         "kernels_ms": {n: round(t / max(c, 1), 5) for n, (c, t) in per_kernel.items() if c},
         "step_roofline_frac": roofline(fpt * tokens, bpt * tokens, ms / 1e3)["frac"],
@@ -353,6 +353,8 @@ def main():
     ap.add_argument("--layout", choices=["bthd", "bhtd"], default="bthd")
     ap.add_argument("--state", choices=["direct", "packed"], default="packed",
                     help="chunk-state storage: all p^2 rows or the p(p+1)/2 unique ones")
+    ap.add_argument("--groups", type=int, default=1,
+                    help="KATA-Mg factor count g (1: the single PSD factor)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the T sweep")
     ap.add_argument("--no-cold-cache", action="store_true",

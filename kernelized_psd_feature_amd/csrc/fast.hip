@@ -132,10 +132,8 @@ __device__ __forceinline__ bf16x8 phik_frag(const TL& tl, int i, int m, int lane
   return f;
 }
 
-// Packed layout: tile t (0..9) row 4g + r holds the state row of the pair (a + (t & 1), 4J + r),
-// (a, J) = double_group(4 (t >> 1) + g); see double_group for the covering of the pairs.
-// Tiles owned by wave w: slots 0, 1 -> tiles 2w, 2w + 1; slot 2 -> tile 8 + w (waves 0, 1).
-__device__ __forceinline__ int packed_tile(int w, int slot) { return slot < 2 ? 2 * w + slot : 8 + w; }
+// Packed layout: tile t row 4g + r holds the state row of the pair (a + (t & 1), 4J + r),
+// (a, J) the double group 4 (t >> 1) + g of the layout's list.
 
 // A operand of the packed state update: row (lane % 16) of the tile is the pair (i, j);
 // irow selects the K^T row for the i factor (i, 16 + i for the doubled copy, 32 for zeros).
@@ -173,40 +171,79 @@ __device__ __forceinline__ s16x4 row4_frag(const __bf16 (*X)[QROW], int row0, in
   return __builtin_bit_cast(s16x4, u);
 }
 
+// Squared-score tile of keys [s0, s0 + 16) (rows) against this lane's query t (column), from
+// the A operand kf (k rows) and the B operand qf (q_t[4g .. 4g + 3]), masked and rounded to bf16
+// P.  GW < 16 (KATA-Mg, groups of GW coordinates): one product per group, the query operand cut
+// to the lane groups holding that group's coordinates, and the squared group dots summed.
+template <int GW, bool kMask>
+__device__ __forceinline__ void score_tile(const s16x4& kf, const s16x4& qf, int s0, int t,
+                                           int lane, __bf16 out[4], float& lsum) {
+  if constexpr (GW == P) {
+    square_mask<kMask>(mfma16(kf, qf, zero4()), s0, t, lane, out, lsum);
+  } else {
+    const int grp = (4 * (lane >> 4)) / GW;
+    f32x4 x2 = zero4();
+#pragma unroll
+    for (int j = 0; j < P / GW; ++j) {
+      const s16x4 qj = grp == j ? qf : s16x4{0, 0, 0, 0};
+      const f32x4 sc = mfma16(kf, qj, zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x2[r] = fmaf(sc[r], sc[r], x2[r]);
+    }
+    weight_mask<kMask>(x2, s0, t, lane, out, lsum);
+  }
+}
+
 // ==========================================================================================
 // Per-layout constants shared by the state and walk kernels.
 //   direct: 16 state tiles (tile = i, rows j), wave w owns tiles 4w .. 4w+3, 8 readout K steps.
-//   packed: 10 state tiles (see double_group), waves 0-1 own 3 tiles and waves 2-3 own 2 (the
-//           higher waves have more intra-chunk work), 5 readout K steps.
+//   packed: the double groups of the unique pairs (see mfma_util.h), two per 16-row tile:
+//           10 tiles at GW = 16, 5 readout K steps.  Wave w owns tiles w, w + 4, w + 8, so
+//           waves 0-1 own 3 and waves 2-3 (more intra-chunk work) own 2.
+//   KATA-Mg (packed, groups of GW = 8 or 4 consecutive coordinates): only the double groups
+//           inside one group exist, 6 or 4 tiles.
 // State layout in the workspace (floats): tile t, value tile nt, lane -> ((t*4 + nt)*64 +
 // lane)*4 .. +3 (the accumulator registers as they are), then Z as one 16 x 16 tile.
 // ==========================================================================================
-template <bool kPacked>
+template <bool kPacked, int GW = P>
 struct Layout {
-  static constexpr int kSlots = kPacked ? 3 : 4;         // state tiles a wave can own
-  static constexpr int kTiles = kPacked ? 10 : 16;
+  static_assert(kPacked || GW == P, "the direct layout is ungrouped");
+  static_assert(GW == 16 || GW == 8 || GW == 4, "group width");
+  static constexpr int kGroupDG = (GW / 4) * (GW / 4 + 1);   // double groups in one group
+  static constexpr int kTiles = kPacked ? (P / GW) * kGroupDG / 2 : 16;
+  static constexpr int kSlots = (kTiles + 3) / 4;        // state tiles a wave can own
   static constexpr int kSteps = kTiles / 2;              // readout K steps of 32 rows
   static constexpr int kZOff = kTiles * 16 * DV;         // offset of Z in a stored state
   static constexpr int kStateFloats = kZOff + 256;
-  __device__ static bool owns(int w, int slot) { return !kPacked || slot < 2 || w < 2; }
-  __device__ static int tile(int w, int slot) { return kPacked ? packed_tile(w, slot) : 4 * w + slot; }
+  __device__ static bool owns(int w, int slot) { return !kPacked || w + 4 * slot < kTiles; }
+  __device__ static int tile(int w, int slot) { return kPacked ? w + 4 * slot : 4 * w + slot; }
+  // double group idx of the (grouped) list -> (a, J)
+  __device__ static void dg(int idx, int& a, int& J) {
+    const int grp = idx / kGroupDG;
+    double_group(idx - grp * kGroupDG, a, J);
+    a += grp * GW;
+    J += grp * (GW / 4);
+  }
 };
 static_assert(Layout<false>::kStateFloats == kStateFloats, "direct state size");
+static_assert(Layout<true>::kTiles == 10 && Layout<true, 8>::kTiles == 6 &&
+              Layout<true, 4>::kTiles == 4, "packed tile counts (plan.cpp)");
 
 // Row sources of the packed update's A operand for this lane's row of each owned tile.
-template <bool kPacked>
+template <bool kPacked, int GW>
 struct UpdateRows {
-  int irow[Layout<kPacked>::kSlots], jrow[Layout<kPacked>::kSlots];
+  using LY = Layout<kPacked, GW>;
+  int irow[LY::kSlots], jrow[LY::kSlots];
   __device__ void init(int w, int lane) {
 #pragma unroll
-    for (int sl = 0; sl < Layout<kPacked>::kSlots; ++sl) {
+    for (int sl = 0; sl < LY::kSlots; ++sl) {
       if (!kPacked) {
         irow[sl] = 4 * w + sl;                  // broadcast row i of the tile
         jrow[sl] = lane & 15;
       } else {
-        const int t = packed_tile(w, sl), row = lane & 15;
+        const int t = LY::owns(w, sl) ? LY::tile(w, sl) : 0, row = lane & 15;
         int a, J;
-        double_group(4 * (t >> 1) + (row >> 2), a, J);
+        LY::dg(4 * (t >> 1) + (row >> 2), a, J);
         const int i = a + (t & 1), j = 4 * J + (row & 3);
         irow[sl] = i > j ? 2 * P : (i == j ? i : P + i);
         jrow[sl] = j;
@@ -216,18 +253,19 @@ struct UpdateRows {
 };
 
 // S[slot] += Phi(K)^T V over one staged chunk, and Z += K^T K if with_z.
-template <bool kPacked, class TL>
-__device__ __forceinline__ void state_update(const TL& tl, const UpdateRows<kPacked>& ur,
-                                             f32x4 (&S)[Layout<kPacked>::kSlots][4], f32x4& Z,
-                                             int w, int lane, bool with_z) {
+template <bool kPacked, int GW, class TL>
+__device__ __forceinline__ void state_update(const TL& tl, const UpdateRows<kPacked, GW>& ur,
+                                             f32x4 (&S)[Layout<kPacked, GW>::kSlots][4],
+                                             f32x4& Z, int w, int lane, bool with_z) {
+  using LY = Layout<kPacked, GW>;
 #pragma unroll 1
   for (int m = 0; m < 2; ++m) {
     bf16x8 vb[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(tl.V, m, nt, lane);
 #pragma unroll
-    for (int sl = 0; sl < Layout<kPacked>::kSlots; ++sl) {
-      if (!Layout<kPacked>::owns(w, sl)) continue;
+    for (int sl = 0; sl < LY::kSlots; ++sl) {
+      if (!LY::owns(w, sl)) continue;
       const bf16x8 a = kPacked ? phik_packed_frag(tl, ur.irow[sl], ur.jrow[sl], m, lane)
                                : phik_frag(tl, ur.irow[sl], m, lane);
 #pragma unroll
@@ -249,11 +287,11 @@ __device__ __forceinline__ void zero_pad_rows(TilesT<kPacked>& tl, int tid) {
 // Segment state: S_seg = sum over the segment's chunks of Phi(K_c)^T V_c and Z_seg = sum K^T K.
 // Grid (n_seg, H, B).
 // ==========================================================================================
-template <bool kPacked>
+template <bool kPacked, int GW>
 __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
     DevProblem pr, int L, int n_seg, int n_used, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, float* __restrict__ states) {
-  using LY = Layout<kPacked>;
+  using LY = Layout<kPacked, GW>;
   __shared__ TilesT<kPacked> tl[2];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -275,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) S[sl][nt] = zero4();
   f32x4 Z = zero4();
-  UpdateRows<kPacked> ur;
+  UpdateRows<kPacked, GW> ur;
   ur.init(w, lane);
   zero_pad_rows(tl[0], tid);
   zero_pad_rows(tl[1], tid);
@@ -292,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
   if (nc > 2) { sp.next(); stage_load(sb, sp, sv_t); }
   __syncthreads();
   auto step = [&](int c, Stage& next) {
-    state_update<kPacked>(tl[c & 1], ur, S, Z, w, lane, w == 0);
+    state_update<kPacked, GW>(tl[c & 1], ur, S, Z, w, lane, w == 0);
     // the other buffer was last read in the previous iteration, before its barrier
     if (c + 1 < nc) stage_store(next, tl[(c + 1) & 1], false, tid);
     if (c + 3 < nc) { sp.next(); stage_load(next, sp, sv_t); }   // chunk c + 3
@@ -323,21 +361,21 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
 //   LDS as bf16 B operands; each wave then reads out its own tokens over all state rows, so no
 //   partial outputs cross waves.
 // ==========================================================================================
-template <bool kPacked>
+template <bool kPacked, int GW>
 struct __align__(16) WalkLds {
   TilesT<kPacked> tl;
-  uint4 Sb[Layout<kPacked>::kSteps][4][64];   // S_{<c} as B operands: [K step][value tile][lane]
+  uint4 Sb[Layout<kPacked, GW>::kSteps][4][64];   // S_{<c} as B operands: [K step][value tile][lane]
   float den[C];                               // D_t of the chunk's tokens
   float inv[C];                               // 1 / D_t
 };
 
-template <typename Tout, bool kPacked>
+template <typename Tout, bool kPacked, int GW>
 __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     DevProblem pr, int L, int n_seg, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den_out,
     const float* __restrict__ states) {
-  using LY = Layout<kPacked>;
-  __shared__ WalkLds<kPacked> sm;
+  using LY = Layout<kPacked, GW>;
+  __shared__ WalkLds<kPacked, GW> sm;
   TilesT<kPacked>& tl = sm.tl;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -360,7 +398,7 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
   }
   // every wave keeps its own copy of Z_{<c} (4 registers); lane holds Z[4g + r][lane % 16]
   f32x4 Z = pre ? *reinterpret_cast<const f32x4*>(pre + LY::kZOff + lane * 4) : zero4();
-  UpdateRows<kPacked> ur;
+  UpdateRows<kPacked, GW> ur;
   ur.init(w, lane);
   zero_pad_rows(tl, tid);
 
@@ -371,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
   for (int kk = 0; kk < LY::kSteps; ++kk) {
     if (kPacked) {
       int a, J;
-      double_group(4 * kk + g, a, J);
+      LY::dg(4 * kk + g, a, J);
       qa_off[kk] = a;
       qj_off[kk] = 4 * J;
     } else {
@@ -428,11 +466,11 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
       for (int half = 0; half < 2; ++half) {
         const int ms = 2 * m + half;
         if (ms < w) {
-          const f32x4 sc = mfma16(row4_frag(tl.Ks, 16 * ms, lane), qf, zero4());
-          square_mask<false>(sc, 16 * ms, t, lane, &pa[4 * half], lsum);
+          score_tile<GW, false>(row4_frag(tl.Ks, 16 * ms, lane), qf, 16 * ms, t, lane,
+                                &pa[4 * half], lsum);
         } else if (ms == w) {
-          const f32x4 sc = mfma16(row4_frag(tl.Ks, 16 * ms, lane), qf, zero4());
-          square_mask<true>(sc, 16 * ms, t, lane, &pa[4 * half], lsum);
+          score_tile<GW, true>(row4_frag(tl.Ks, 16 * ms, lane), qf, 16 * ms, t, lane,
+                               &pa[4 * half], lsum);
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) pa[4 * half + r] = (__bf16)0.f;
@@ -454,9 +492,11 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
       s16x4 zhi, zlo;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const __bf16 hi = (__bf16)Z[r];
+        // KATA-Mg: only the within-group blocks of Z enter q^T Z q
+        const float zr = (GW == P || (4 * g + r) / GW == l16 / GW) ? Z[r] : 0.f;
+        const __bf16 hi = (__bf16)zr;
         zhi[r] = __builtin_bit_cast(short, hi);
-        zlo[r] = __builtin_bit_cast(short, (__bf16)(Z[r] - (float)hi));
+        zlo[r] = __builtin_bit_cast(short, (__bf16)(zr - (float)hi));
       }
       f32x4 y = mfma16(zhi, qf, zero4());
       y = mfma16(zlo, qf, y);                   // y[r] = (Z q_t)[4g + r]
@@ -508,7 +548,7 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     orow += C * so_t;
 
     // ---- state update with this chunk: S += Phi(K)^T V, Z += K^T K ----
-    state_update<kPacked>(tl, ur, S, Z, w, lane, true);
+    state_update<kPacked, GW>(tl, ur, S, Z, w, lane, true);
     __syncthreads();                               // all reads of this chunk's tiles and Sb done
     if (c + 1 < nc) {
       stage_store(st, tl, true, tid);
@@ -530,7 +570,7 @@ struct __align__(16) QuadLds {
   float den[C];
 };
 
-template <typename Tout>
+template <typename Tout, int GW>
 __global__ __launch_bounds__(kThreads, 2) void quadratic_fast_kernel(
     DevProblem pr, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den_out) {
@@ -586,11 +626,11 @@ __global__ __launch_bounds__(kThreads, 2) void quadratic_fast_kernel(
       for (int half = 0; half < 2; ++half) {
         const int ms = 2 * m + half;
         if (!diag || ms < w) {
-          const f32x4 sc = mfma16(row4_frag(sm.Ks, 16 * ms, lane), qf, zero4());
-          square_mask<false>(sc, s_base + 16 * ms, t, lane, &pa[4 * half], lsum);
+          score_tile<GW, false>(row4_frag(sm.Ks, 16 * ms, lane), qf, s_base + 16 * ms, t, lane,
+                                &pa[4 * half], lsum);
         } else if (ms == w) {
-          const f32x4 sc = mfma16(row4_frag(sm.Ks, 16 * ms, lane), qf, zero4());
-          square_mask<true>(sc, s_base + 16 * ms, t, lane, &pa[4 * half], lsum);
+          score_tile<GW, true>(row4_frag(sm.Ks, 16 * ms, lane), qf, s_base + 16 * ms, t, lane,
+                               &pa[4 * half], lsum);
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) pa[4 * half + r] = (__bf16)0.f;
@@ -629,58 +669,96 @@ __global__ __launch_bounds__(kThreads, 2) void quadratic_fast_kernel(
 
 }  // namespace
 
+// KATA-Mg group count -> group width of the MFMA kernels (0 when they do not take it)
+int fast_group_width(int groups) {
+  return groups <= 1 ? P : groups == 2 ? 8 : groups == 4 ? 4 : 0;
+}
+
 bool quadratic_fast_supported(const kata_problem* pr) {
-  return pr->in_dtype == KATA_BF16 && pr->p == P && pr->dv == DV;
+  return pr->in_dtype == KATA_BF16 && pr->p == P && pr->dv == DV && fast_group_width(pr->groups);
 }
 
 bool chunk_fast_available() { return true; }
 
-hipError_t launch_quadratic_fast(const DevProblem& pr, bool out_bf16, const void* q,
+namespace {
+template <typename Tout>
+void quadratic_dispatch(const DevProblem& pr, int gw, dim3 grid, hipStream_t st, const __bf16* q,
+                        const __bf16* k, const __bf16* v, Tout* o, float* den) {
+  if (gw == 8)
+    quadratic_fast_kernel<Tout, 8><<<grid, kThreads, 0, st>>>(pr, q, k, v, o, den);
+  else if (gw == 4)
+    quadratic_fast_kernel<Tout, 4><<<grid, kThreads, 0, st>>>(pr, q, k, v, o, den);
+  else
+    quadratic_fast_kernel<Tout, P><<<grid, kThreads, 0, st>>>(pr, q, k, v, o, den);
+}
+
+template <typename Tout, bool kPacked, int GW>
+void walk_launch(const DevProblem& pr, int L, int n_seg, dim3 grid, hipStream_t st,
+                 const __bf16* q, const __bf16* k, const __bf16* v, void* o, float* den,
+                 const float* states) {
+  chunk_output_fast_kernel<Tout, kPacked, GW><<<grid, kThreads, 0, st>>>(
+      pr, L, n_seg, q, k, v, (Tout*)o, den, states);
+}
+
+template <typename Tout>
+void walk_dispatch(const DevProblem& pr, bool packed, int gw, int L, int n_seg, dim3 grid,
+                   hipStream_t st, const __bf16* q, const __bf16* k, const __bf16* v, void* o,
+                   float* den, const float* states) {
+  if (gw == 8)
+    walk_launch<Tout, true, 8>(pr, L, n_seg, grid, st, q, k, v, o, den, states);
+  else if (gw == 4)
+    walk_launch<Tout, true, 4>(pr, L, n_seg, grid, st, q, k, v, o, den, states);
+  else if (packed)
+    walk_launch<Tout, true, P>(pr, L, n_seg, grid, st, q, k, v, o, den, states);
+  else
+    walk_launch<Tout, false, P>(pr, L, n_seg, grid, st, q, k, v, o, den, states);
+}
+}  // namespace
+
+// gw: group width (16, or 8 / 4 for KATA-Mg, which always use the packed layout)
+hipError_t launch_quadratic_fast(const DevProblem& pr, int gw, bool out_bf16, const void* q,
                                  const void* k, const void* v, void* o, float* den,
                                  hipStream_t st) {
+  if (gw != P && gw != 8 && gw != 4) return hipErrorInvalidValue;
   dim3 grid((pr.T + C - 1) / C, pr.H, pr.B);
+  const __bf16 *qq = (const __bf16*)q, *kk = (const __bf16*)k, *vv = (const __bf16*)v;
   if (out_bf16)
-    quadratic_fast_kernel<__bf16><<<grid, kThreads, 0, st>>>(
-        pr, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, den);
+    quadratic_dispatch<__bf16>(pr, gw, grid, st, qq, kk, vv, (__bf16*)o, den);
   else
-    quadratic_fast_kernel<float><<<grid, kThreads, 0, st>>>(
-        pr, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (float*)o, den);
+    quadratic_dispatch<float>(pr, gw, grid, st, qq, kk, vv, (float*)o, den);
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int L, int n_seg,
+hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int gw, int L, int n_seg,
                                    int n_used, const void* k, const void* v, float* states,
                                    hipStream_t st) {
   if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;
+  if (gw != P && gw != 8 && gw != 4) return hipErrorInvalidValue;
   dim3 grid(n_seg, pr.H, pr.B);
-  if (packed)
-    chunk_state_fast_kernel<true><<<grid, kThreads, 0, st>>>(pr, L, n_seg, n_used,
-                                                             (const __bf16*)k, (const __bf16*)v,
-                                                             states);
+  const __bf16 *kk = (const __bf16*)k, *vv = (const __bf16*)v;
+  if (gw == 8)
+    chunk_state_fast_kernel<true, 8><<<grid, kThreads, 0, st>>>(pr, L, n_seg, n_used, kk, vv, states);
+  else if (gw == 4)
+    chunk_state_fast_kernel<true, 4><<<grid, kThreads, 0, st>>>(pr, L, n_seg, n_used, kk, vv, states);
+  else if (packed)
+    chunk_state_fast_kernel<true, P><<<grid, kThreads, 0, st>>>(pr, L, n_seg, n_used, kk, vv, states);
   else
-    chunk_state_fast_kernel<false><<<grid, kThreads, 0, st>>>(pr, L, n_seg, n_used,
-                                                              (const __bf16*)k, (const __bf16*)v,
-                                                              states);
+    chunk_state_fast_kernel<false, P><<<grid, kThreads, 0, st>>>(pr, L, n_seg, n_used, kk, vv, states);
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_output_fast(const DevProblem& pr, bool packed, bool out_bf16, int L,
-                                    int n_seg, const void* q, const void* k, const void* v,
-                                    void* o, float* den, const float* states, hipStream_t st) {
+hipError_t launch_chunk_output_fast(const DevProblem& pr, bool packed, int gw, bool out_bf16,
+                                    int L, int n_seg, const void* q, const void* k,
+                                    const void* v, void* o, float* den, const float* states,
+                                    hipStream_t st) {
   if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;
+  if (gw != P && gw != 8 && gw != 4) return hipErrorInvalidValue;
   dim3 grid(n_seg, pr.H, pr.B);
   const __bf16 *qq = (const __bf16*)q, *kk = (const __bf16*)k, *vv = (const __bf16*)v;
-  if (out_bf16) {
-    if (packed)
-      chunk_output_fast_kernel<__bf16, true><<<grid, kThreads, 0, st>>>(pr, L, n_seg, qq, kk, vv, (__bf16*)o, den, states);
-    else
-      chunk_output_fast_kernel<__bf16, false><<<grid, kThreads, 0, st>>>(pr, L, n_seg, qq, kk, vv, (__bf16*)o, den, states);
-  } else {
-    if (packed)
-      chunk_output_fast_kernel<float, true><<<grid, kThreads, 0, st>>>(pr, L, n_seg, qq, kk, vv, (float*)o, den, states);
-    else
-      chunk_output_fast_kernel<float, false><<<grid, kThreads, 0, st>>>(pr, L, n_seg, qq, kk, vv, (float*)o, den, states);
-  }
+  if (out_bf16)
+    walk_dispatch<__bf16>(pr, packed, gw, L, n_seg, grid, st, qq, kk, vv, o, den, states);
+  else
+    walk_dispatch<float>(pr, packed, gw, L, n_seg, grid, st, qq, kk, vv, o, den, states);
   return hipGetLastError();
 }
 

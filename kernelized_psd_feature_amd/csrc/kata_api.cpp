@@ -15,7 +15,8 @@
 #include "plan.h"
 
 namespace kata {
-hipError_t launch_quadratic_fast(const DevProblem& pr, bool out_bf16, const void* q,
+int fast_group_width(int groups);
+hipError_t launch_quadratic_fast(const DevProblem& pr, int gw, bool out_bf16, const void* q,
                                  const void* k, const void* v, void* o, float* den,
                                  hipStream_t st);
 bool quadratic_fast_supported(const kata_problem* pr);
@@ -29,12 +30,13 @@ hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int
 hipError_t launch_quadratic32(const DevProblem& pr, bool out_bf16, const void* q, const void* k,
                               const void* v, void* o, float* den, hipStream_t st);
 // Segment states; segments seg >= n_used get a zero state without reading their tokens.
-hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int L, int n_seg,
+hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int gw, int L, int n_seg,
                                    int n_used, const void* k, const void* v, float* states,
                                    hipStream_t st);
-hipError_t launch_chunk_output_fast(const DevProblem& pr, bool packed, bool out_bf16, int L,
-                                    int n_seg, const void* q, const void* k, const void* v,
-                                    void* o, float* den, const float* states, hipStream_t st);
+hipError_t launch_chunk_output_fast(const DevProblem& pr, bool packed, int gw, bool out_bf16,
+                                    int L, int n_seg, const void* q, const void* k,
+                                    const void* v, void* o, float* den, const float* states,
+                                    hipStream_t st);
 }  // namespace kata
 
 namespace {
@@ -207,8 +209,9 @@ kata_status kata_fwd_quadratic(const kata_problem* pr, const void* q, const void
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool in_bf16 = pr->in_dtype == KATA_BF16, out_bf16 = pr->out_dtype == KATA_BF16;
   Timed t(KATA_K_QUADRATIC, st);
-  if (pr->groups <= 1 && kata::quadratic_fast_supported(pr))
-    return launch_status(kata::launch_quadratic_fast(dp, out_bf16, q, k, v, o, den, st),
+  if (kata::quadratic_fast_supported(pr))
+    return launch_status(kata::launch_quadratic_fast(dp, kata::fast_group_width(pr->groups),
+                                                     out_bf16, q, k, v, o, den, st),
                          "quadratic forward");
   if (kata::fast32_supported(pr))
     return launch_status(kata::launch_quadratic32(dp, out_bf16, q, k, v, o, den, st),
@@ -249,8 +252,8 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
       Timed t(KATA_K_CHUNK_STATE, st);
       // the last segment's state enters no prefix
       e = cp.fast32 ? kata::launch_chunk_state32(dp, cp.L, cp.n_seg, cp.n_seg - 1, k, v, states, st)
-          : cp.fast ? kata::launch_chunk_state_fast(dp, cp.packed, cp.L, cp.n_seg, cp.n_seg - 1,
-                                                    k, v, states, st)
+          : cp.fast ? kata::launch_chunk_state_fast(dp, cp.packed, cp.gw, cp.L, cp.n_seg,
+                                                    cp.n_seg - 1, k, v, states, st)
                     : kata::launch_chunk_state_generic(dp, in_bf16, k, v, states, cp.n_chunks, st);
     }
     if (e != hipSuccess) return launch_status(e, "chunk-state kernel");
@@ -266,8 +269,8 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
     const float* pre = one_segment ? nullptr : states;
     e = cp.fast32 ? kata::launch_chunk_output32(dp, out_bf16, cp.L, cp.n_seg, q, k, v, o, den,
                                                 pre, st)
-        : cp.fast ? kata::launch_chunk_output_fast(dp, cp.packed, out_bf16, cp.L, cp.n_seg, q,
-                                                   k, v, o, den, pre, st)
+        : cp.fast ? kata::launch_chunk_output_fast(dp, cp.packed, cp.gw, out_bf16, cp.L,
+                                                   cp.n_seg, q, k, v, o, den, pre, st)
                 : kata::launch_chunk_output_generic(dp, in_bf16, out_bf16, q, k, v, o, den,
                                                     states, cp.n_chunks, st);
   }
@@ -316,7 +319,8 @@ kata::ChunkPlan recurrent_plan(const kata_problem* pr) {
   kata_problem d = *pr;
   d.state_layout = KATA_STATE_DIRECT;
   kata::ChunkPlan cp = kata::plan_chunked(&d, kata::chunk_fast_available());
-  if (cp.fast32) cp = kata::plan_chunked(&d, false);   // p = 32: the fp32 state kernel
+  // the public state is the direct one: p = 32 and KATA-Mg prefill on the fp32 state kernel
+  if (cp.fast32 || cp.gw != 16) cp = kata::plan_chunked(&d, false);
   return cp;
 }
 
@@ -356,7 +360,7 @@ kata_status kata_recurrent_state(const kata_problem* pr, const void* k, const vo
   hipError_t e;
   {
     Timed t(KATA_K_CHUNK_STATE, st);
-    e = cp.fast ? kata::launch_chunk_state_fast(dp, false, cp.L, cp.n_seg, cp.n_seg, k, v,
+    e = cp.fast ? kata::launch_chunk_state_fast(dp, false, 16, cp.L, cp.n_seg, cp.n_seg, k, v,
                                                 states, st)
                 : kata::launch_chunk_state_generic(dp, pr->in_dtype == KATA_BF16, k, v, states,
                                                    cp.n_chunks, st);

@@ -55,8 +55,8 @@ __device__ __forceinline__ bf16x8 v_frag(const __bf16 (*V)[ROW], int m, int nt, 
   return __builtin_bit_cast(bf16x8, uint4{ul.x, ul.y, uh.x, uh.y});
 }
 
-// Double group idx -> (a, J): group J starts at index J (J + 1) and holds the J + 1 ... even a
-// values 0, 2, .., 4J + 2 (2J + 2 groups).  p = 16 has 20 groups, p = 32 has 72.
+// Double group idx -> (a, J): the groups of column block J are indices J (J + 1) ..
+// J (J + 1) + 2J + 1, one for each even a = 0, 2, .., 4J + 2.  p = 16 has 20 groups, p = 32 72.
 __device__ __forceinline__ void double_group(int idx, int& a, int& J) {
   J = 0;
   while ((J + 1) * (J + 2) <= idx) ++J;
@@ -74,6 +74,20 @@ __device__ __forceinline__ void square_mask(const f32x4& sc, int s0, int t, int 
     const float x = sc[r];
     __bf16 pb = (__bf16)(x * x);
     if (kMask) pb = (s0 + 4 * g + r <= t) ? pb : (__bf16)0.f;   // select, never multiply
+    out[r] = pb;
+    lsum += (float)pb;
+  }
+}
+
+// As square_mask for a tile of weights that are already sums of squares (KATA-Mg).
+template <bool kMask>
+__device__ __forceinline__ void weight_mask(const f32x4& x2, int s0, int t, int lane,
+                                            __bf16 out[4], float& lsum) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    __bf16 pb = (__bf16)x2[r];
+    if (kMask) pb = (s0 + 4 * g + r <= t) ? pb : (__bf16)0.f;
     out[r] = pb;
     lsum += (float)pb;
   }

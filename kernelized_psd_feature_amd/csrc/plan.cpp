@@ -146,10 +146,15 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
   cp.n_chunks = pr->T / pr->chunk;
   cp.n_seq = int64_t(pr->B) * pr->H;
   cp.state_elems = int64_t(pr->p) * pr->p * (pr->dv + 1);
+  // MFMA kernels: bf16, d_v = 64, C = 64; p = 16 with g in {1, 2, 4} (group widths 16, 8,
+  // 4), or p = 32 with g = 1
   const bool mfma_shape = fast_available && pr->in_dtype == KATA_BF16 && pr->dv == 64 &&
-                          pr->chunk == 64 && pr->groups <= 1;
-  cp.fast = (mfma_shape && (pr->p == 16 || pr->p == 32)) ? 1 : 0;
+                          pr->chunk == 64;
+  const int g = pr->groups <= 1 ? 1 : pr->groups;
+  cp.fast = (mfma_shape && ((pr->p == 16 && (g == 1 || g == 2 || g == 4)) ||
+                            (pr->p == 32 && g == 1))) ? 1 : 0;
   cp.fast32 = (cp.fast && pr->p == 32) ? 1 : 0;
+  cp.gw = pr->p / g;
   if (cp.fast) {
     int L = pr->seg_chunks;
     if (L == 0) {
@@ -174,10 +179,14 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
     }
     if (L > cp.n_chunks) L = cp.n_chunks;
     cp.L = L;
-    cp.packed = (pr->state_layout == KATA_STATE_PACKED || cp.fast32) ? 1 : 0;
+    cp.packed = (pr->state_layout == KATA_STATE_PACKED || cp.fast32 || g > 1) ? 1 : 0;
     // packed: 10 tiles of 16 rows (the 136 unique (i, j) rows and 24 zero rows) x 64 columns,
-    // plus the full 16 x 16 Z; p = 32: 36 tiles (528 unique rows and 48 zero rows) and Z
-    if (cp.packed) cp.state_elems = cp.fast32 ? kState32Floats : 160 * 64 + 256;
+    // plus the full 16 x 16 Z; KATA-Mg at p = 16: 6 tiles (g = 2) or 4 (g = 4), the
+    // within-group pairs only; p = 32: 36 tiles (528 unique rows and 48 zero rows) and Z
+    if (cp.packed) {
+      const int tiles16 = g == 1 ? 10 : g == 2 ? 6 : 4;
+      cp.state_elems = cp.fast32 ? kState32Floats : int64_t(tiles16) * 16 * 64 + 256;
+    }
   } else {
     cp.L = 1;   // the VALU path scans every chunk state
   }

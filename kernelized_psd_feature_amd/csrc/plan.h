@@ -17,6 +17,7 @@ struct ChunkPlan {
   int fast = 0;               // 1: bf16 MFMA kernels; 0: fp32-arithmetic VALU kernels
   int fast32 = 0;             // 1: the MFMA kernels are the p = 32 ones (always packed)
   int packed = 0;             // 1: the MFMA kernels keep the unique (i <= j) state rows
+  int gw = 16;                // p = 16 MFMA kernels: KATA-Mg group width (16 = one group)
   int L = 1;                  // chunks per segment
   int n_chunks = 0;           // N_c = T / C per (b, h)
   int n_seg = 0;              // ceil(N_c / L)
