@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkata.so")
 
 SOURCES = ["kata_api.cpp", "plan.cpp", "generic.hip", "scan.hip", "bwd.hip", "fast.hip", "fast32.hip",
-           "decode.hip", "bwd_chunked.hip"]
+           "quadratic.hip", "decode.hip", "bwd_chunked.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

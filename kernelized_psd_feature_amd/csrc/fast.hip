@@ -1,6 +1,7 @@
-// bf16 MFMA kernels for gfx950 (p = 16, d_v = 64, chunk C = 64): the chunk-state build, the
+// bf16 MFMA kernels for gfx950 (p = 16, d_v = 64, chunk C = 64): the chunk-state build and the
 // segment walk of the chunked forward (intra-chunk tile + inter-chunk readout + output gate +
-// state update), and the flash-style quadratic forward.
+// state update), including KATA-Mg group widths 8 and 4.  (The quadratic form is in
+// quadratic.hip.)
 //
 // Method (gist.science "Technische Samenvatting" sections 2.1-2.3; ai.info AI summary, Main
 // Findings): a_ts = (q_t . k_s)^2 = <vec(q q^T), vec(k k^T)>, o_t = sum_{s<=t} a_ts v_s / D_t,
@@ -558,115 +559,6 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
   }
 }
 
-// ==========================================================================================
-// Flash-style quadratic forward: 64 queries per workgroup (16 per wave), key blocks of 64
-// staged in LDS; scores, square + mask, P.V and the row sum, no running maximum (the scores
-// are squares, so nothing needs rescaling).  Grid (ceil(T/64), H, B), heaviest blocks first.
-// ==========================================================================================
-struct __align__(16) QuadLds {
-  __bf16 Ks[C][QROW];
-  __bf16 V[C][VROW];
-  float inv[C];
-  float den[C];
-};
-
-template <typename Tout, int GW>
-__global__ __launch_bounds__(kThreads, 2) void quadratic_fast_kernel(
-    DevProblem pr, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-    const __bf16* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den_out) {
-  __shared__ QuadLds sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
-  const int qb = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int t0 = qb * C;
-  const int t = t0 + 16 * w + l16;             // this lane's query (fragment column)
-  const uint4 z4 = {0u, 0u, 0u, 0u};
-
-  // query operand of the score tile: q_t[4g..4g+3]
-  s16x4 qf = {0, 0, 0, 0};
-  if (t < pr.T)
-    qf = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2*>(q + row_off(pr.sq, b, t, h) + 4 * g));
-
-  // staging: waves 0-1 half a k row each (key = lane), every thread 16 B of two v rows
-  const int a = tid >> 3, c8 = tid & 7;
-  auto load = [&](int s0) {
-    Stage x;
-    x.qk = z4;
-    if (w < 2) {
-      const int s = s0 + lane;
-      x.qk = s < pr.T ? ld16(k + row_off(pr.sk, b, s, h) + 8 * w) : z4;
-    }
-    const int s = s0 + 2 * a;
-    x.v0 = s < pr.T ? ld16(v + row_off(pr.sv, b, s, h) + 8 * c8) : z4;
-    x.v1 = s + 1 < pr.T ? ld16(v + row_off(pr.sv, b, s + 1, h) + 8 * c8) : z4;
-    return x;
-  };
-  auto store = [&](const Stage& x) {
-    if (w < 2) {
-      *reinterpret_cast<uint2*>(&sm.Ks[lane][8 * w]) = uint2{x.qk.x, x.qk.y};
-      *reinterpret_cast<uint2*>(&sm.Ks[lane][8 * w + 4]) = uint2{x.qk.z, x.qk.w};
-    }
-    *reinterpret_cast<uint4*>(&sm.V[2 * a][8 * c8]) = x.v0;
-    *reinterpret_cast<uint4*>(&sm.V[2 * a + 1][8 * c8]) = x.v1;
-  };
-
-  f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
-  float lsum = 0.f;
-  Stage x = load(0);
-  store(x);
-  __syncthreads();
-  for (int kb = 0; kb <= qb; ++kb) {
-    if (kb < qb) x = load((kb + 1) * C);
-    const int s_base = kb * C;
-    const bool diag = (kb == qb);
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      if (diag && 2 * m > w) break;
-      __bf16 pa[8];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int ms = 2 * m + half;
-        if (!diag || ms < w) {
-          score_tile<GW, false>(row4_frag(sm.Ks, 16 * ms, lane), qf, s_base + 16 * ms, t, lane,
-                                &pa[4 * half], lsum);
-        } else if (ms == w) {
-          score_tile<GW, true>(row4_frag(sm.Ks, 16 * ms, lane), qf, s_base + 16 * ms, t, lane,
-                               &pa[4 * half], lsum);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pa[4 * half + r] = (__bf16)0.f;
-        }
-      }
-      bf16x8 af;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) af[r] = pa[r];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) O[nt] = mfma32(af, v_frag(sm.V, m, nt, lane), O[nt]);
-    }
-    __syncthreads();
-    if (kb < qb) store(x);
-    __syncthreads();
-  }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  if (g == 0) {
-    const float D = pr.eps + lsum;
-    sm.den[16 * w + l16] = D;
-    sm.inv[16 * w + l16] = 1.f / D;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int tr = 16 * w + 4 * g + r;
-    if (t0 + tr >= pr.T) continue;
-    const float inv = sm.inv[tr];
-    Tout* op = o + row_off(pr.so, b, t0 + tr, h);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) op[16 * nt + l16] = cvt_out<Tout>(O[nt][r] * inv);
-  }
-  if (den_out && lane < 16 && t0 + 16 * w + lane < pr.T)
-    den_out[((long long)b * pr.T + t0 + 16 * w + lane) * pr.H + h] = sm.den[16 * w + lane];
-}
-
 }  // namespace
 
 // KATA-Mg group count -> group width of the MFMA kernels (0 when they do not take it)
@@ -681,17 +573,6 @@ bool quadratic_fast_supported(const kata_problem* pr) {
 bool chunk_fast_available() { return true; }
 
 namespace {
-template <typename Tout>
-void quadratic_dispatch(const DevProblem& pr, int gw, dim3 grid, hipStream_t st, const __bf16* q,
-                        const __bf16* k, const __bf16* v, Tout* o, float* den) {
-  if (gw == 8)
-    quadratic_fast_kernel<Tout, 8><<<grid, kThreads, 0, st>>>(pr, q, k, v, o, den);
-  else if (gw == 4)
-    quadratic_fast_kernel<Tout, 4><<<grid, kThreads, 0, st>>>(pr, q, k, v, o, den);
-  else
-    quadratic_fast_kernel<Tout, P><<<grid, kThreads, 0, st>>>(pr, q, k, v, o, den);
-}
-
 template <typename Tout, bool kPacked, int GW>
 void walk_launch(const DevProblem& pr, int L, int n_seg, dim3 grid, hipStream_t st,
                  const __bf16* q, const __bf16* k, const __bf16* v, void* o, float* den,
@@ -716,19 +597,6 @@ void walk_dispatch(const DevProblem& pr, bool packed, int gw, int L, int n_seg, 
 }  // namespace
 
 // gw: group width (16, or 8 / 4 for KATA-Mg, which always use the packed layout)
-hipError_t launch_quadratic_fast(const DevProblem& pr, int gw, bool out_bf16, const void* q,
-                                 const void* k, const void* v, void* o, float* den,
-                                 hipStream_t st) {
-  if (gw != P && gw != 8 && gw != 4) return hipErrorInvalidValue;
-  dim3 grid((pr.T + C - 1) / C, pr.H, pr.B);
-  const __bf16 *qq = (const __bf16*)q, *kk = (const __bf16*)k, *vv = (const __bf16*)v;
-  if (out_bf16)
-    quadratic_dispatch<__bf16>(pr, gw, grid, st, qq, kk, vv, (__bf16*)o, den);
-  else
-    quadratic_dispatch<float>(pr, gw, grid, st, qq, kk, vv, (float*)o, den);
-  return hipGetLastError();
-}
-
 hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int gw, int L, int n_seg,
                                    int n_used, const void* k, const void* v, float* states,
                                    hipStream_t st) {

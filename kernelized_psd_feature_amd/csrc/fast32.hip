@@ -1,5 +1,5 @@
 // bf16 MFMA kernels for gfx950 at p = 32, d_v = 64, chunk C = 64: the chunk-state build and
-// the segment walk of the chunked forward, and the flash-style quadratic forward.
+// the segment walk of the chunked forward.  (The quadratic form is in quadratic.hip.)
 //
 // Same method and precision as the p = 16 kernels (gist.science "Technische Samenvatting"
 // sections 2.1-2.3; ai.info AI summary, Main Findings): a_ts = (q_t . k_s)^2, bf16 MFMA
@@ -461,112 +461,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
   }
 }
 
-// ==========================================================================================
-// Flash-style quadratic forward at p = 32: 64 queries per workgroup (16 per wave, 4 waves),
-// key blocks of 64 staged in LDS.  Grid (ceil(T/64), H, B), heaviest blocks first.
-// ==========================================================================================
-constexpr int kQThreads = 256;
-
-struct QStage {
-  uint4 k, v0, v1;
-};
-
-struct __align__(16) Quad32Lds {
-  __bf16 Ks[C][QROW];
-  __bf16 V[C][VROW];
-  float inv[C];
-  float den[C];
-};
-
-template <typename Tout>
-__global__ __launch_bounds__(kQThreads, 2) void quadratic32_kernel(
-    DevProblem pr, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-    const __bf16* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den_out) {
-  __shared__ Quad32Lds sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
-  const int qb = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int t0 = qb * C;
-  const int t = t0 + 16 * w + l16;
-  bf16x8 qf = __builtin_bit_cast(bf16x8, uint4{0u, 0u, 0u, 0u});
-  if (t < pr.T) qf = __builtin_bit_cast(bf16x8, ld16(q + row_off(pr.sq, b, t, h) + 8 * g));
-
-  // staging: a quarter k row per thread (row tid / 4), 16 B of two v rows per thread
-  const int kr = tid >> 2, kc = tid & 3, a2 = tid >> 3, c8 = tid & 7;
-  auto load = [&](int s0) {
-    QStage x;
-    x.k = s0 + kr < pr.T ? ld16(k + row_off(pr.sk, b, s0 + kr, h) + 8 * kc) : uint4{0u, 0u, 0u, 0u};
-    const int s = s0 + 2 * a2;
-    x.v0 = s < pr.T ? ld16(v + row_off(pr.sv, b, s, h) + 8 * c8) : uint4{0u, 0u, 0u, 0u};
-    x.v1 = s + 1 < pr.T ? ld16(v + row_off(pr.sv, b, s + 1, h) + 8 * c8) : uint4{0u, 0u, 0u, 0u};
-    return x;
-  };
-  auto store = [&](const QStage& x) {
-    *reinterpret_cast<uint4*>(&sm.Ks[kr][8 * kc]) = x.k;
-    *reinterpret_cast<uint4*>(&sm.V[2 * a2][8 * c8]) = x.v0;
-    *reinterpret_cast<uint4*>(&sm.V[2 * a2 + 1][8 * c8]) = x.v1;
-  };
-  auto key_frag = [&](int ms) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&sm.Ks[16 * ms + l16][8 * g]));
-  };
-
-  f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
-  float lsum = 0.f;
-  QStage x = load(0);
-  store(x);
-  __syncthreads();
-  for (int kb = 0; kb <= qb; ++kb) {
-    if (kb < qb) x = load((kb + 1) * C);
-    const int s_base = kb * C;
-    const bool diag = (kb == qb);
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      if (diag && 2 * m > w) break;
-      __bf16 pa[8];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int ms = 2 * m + half;
-        if (!diag || ms < w) {
-          const f32x4 sc = mfma32(key_frag(ms), qf, zero4());
-          square_mask<false>(sc, s_base + 16 * ms, t, lane, &pa[4 * half], lsum);
-        } else if (ms == w) {
-          const f32x4 sc = mfma32(key_frag(ms), qf, zero4());
-          square_mask<true>(sc, s_base + 16 * ms, t, lane, &pa[4 * half], lsum);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pa[4 * half + r] = (__bf16)0.f;
-        }
-      }
-      bf16x8 af;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) af[r] = pa[r];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) O[nt] = mfma32(af, v_frag(sm.V, m, nt, lane), O[nt]);
-    }
-    __syncthreads();
-    if (kb < qb) store(x);
-    __syncthreads();
-  }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  if (g == 0) {
-    const float D = pr.eps + lsum;
-    sm.den[16 * w + l16] = D;
-    sm.inv[16 * w + l16] = 1.f / D;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int tr = 16 * w + 4 * g + r;
-    if (t0 + tr >= pr.T) continue;
-    const float inv = sm.inv[tr];
-    Tout* op = o + row_off(pr.so, b, t0 + tr, h);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) op[16 * nt + l16] = cvt_out<Tout>(O[nt][r] * inv);
-  }
-  if (den_out && lane < 16 && t0 + 16 * w + lane < pr.T)
-    den_out[((long long)b * pr.T + t0 + 16 * w + lane) * pr.H + h] = sm.den[16 * w + lane];
-}
-
 }  // namespace
 
 bool fast32_supported(const kata_problem* pr) {
@@ -606,19 +500,6 @@ hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int
     chunk_output32_kernel<float><<<grid, kThreads, lds, st>>>(pr, L, n_seg, qq, kk, vv,
                                                               (float*)o, den, states);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_quadratic32(const DevProblem& pr, bool out_bf16, const void* q, const void* k,
-                              const void* v, void* o, float* den, hipStream_t st) {
-  if (pr.p != P || pr.dv != DV) return hipErrorInvalidValue;
-  dim3 grid((pr.T + C - 1) / C, pr.H, pr.B);
-  if (out_bf16)
-    quadratic32_kernel<__bf16><<<grid, kQThreads, 0, st>>>(
-        pr, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, den);
-  else
-    quadratic32_kernel<float><<<grid, kQThreads, 0, st>>>(
-        pr, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (float*)o, den);
   return hipGetLastError();
 }
 

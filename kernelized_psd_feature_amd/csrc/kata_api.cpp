@@ -16,7 +16,7 @@
 
 namespace kata {
 int fast_group_width(int groups);
-hipError_t launch_quadratic_fast(const DevProblem& pr, int gw, bool out_bf16, const void* q,
+hipError_t launch_quadratic_mfma(const DevProblem& pr, int gw, bool out_bf16, const void* q,
                                  const void* k, const void* v, void* o, float* den,
                                  hipStream_t st);
 bool quadratic_fast_supported(const kata_problem* pr);
@@ -27,8 +27,7 @@ hipError_t launch_chunk_state32(const DevProblem& pr, int L, int n_seg, int n_us
 hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int n_seg,
                                  const void* q, const void* k, const void* v, void* o,
                                  float* den, const float* states, hipStream_t st);
-hipError_t launch_quadratic32(const DevProblem& pr, bool out_bf16, const void* q, const void* k,
-                              const void* v, void* o, float* den, hipStream_t st);
+
 // Segment states; segments seg >= n_used get a zero state without reading their tokens.
 hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int gw, int L, int n_seg,
                                    int n_used, const void* k, const void* v, float* states,
@@ -210,11 +209,11 @@ kata_status kata_fwd_quadratic(const kata_problem* pr, const void* q, const void
   const bool in_bf16 = pr->in_dtype == KATA_BF16, out_bf16 = pr->out_dtype == KATA_BF16;
   Timed t(KATA_K_QUADRATIC, st);
   if (kata::quadratic_fast_supported(pr))
-    return launch_status(kata::launch_quadratic_fast(dp, kata::fast_group_width(pr->groups),
+    return launch_status(kata::launch_quadratic_mfma(dp, kata::fast_group_width(pr->groups),
                                                      out_bf16, q, k, v, o, den, st),
                          "quadratic forward");
   if (kata::fast32_supported(pr))
-    return launch_status(kata::launch_quadratic32(dp, out_bf16, q, k, v, o, den, st),
+    return launch_status(kata::launch_quadratic_mfma(dp, 32, out_bf16, q, k, v, o, den, st),
                          "quadratic forward");
   return launch_status(kata::launch_quadratic_generic(dp, in_bf16, out_bf16, q, k, v, o, den, st),
                        "quadratic forward");
