@@ -862,3 +862,63 @@ def test_mg_mfma_causality_and_bf16_output():
         k2[:, 320:] = float("nan")
         v2[:, 320:] = float("inf")
         assert torch.equal(o[:, :320], _run(form, q, k2, v2, groups=4)[:, :320]), form
+
+
+# ------------------------------------------------------------ bench shapes ---------------
+
+def test_decode_bench_shape_after_prefill():
+    # the decode benchmark's batch: 512 sequences x 16 heads, one new token after a
+    # 64-token prefill (MFMA state kernel), sampled heads against the closed form
+    w = W.DECODE
+    q, k, v = W.make_inputs(w, 70, T=65)
+    qg, kg, vg = _to_gpu(q, k, v)
+    state = K.recurrent_state(kg[:, :64].contiguous(), vg[:, :64].contiguous())
+    o = K.decode(qg[:, 64:].contiguous(), kg[:, 64:].contiguous(), vg[:, 64:].contiguous(),
+                 state).cpu()
+    rng = np.random.default_rng(71)
+    worst = 0.0
+    for b, h in [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(24)]:
+        ref, _ = O.closed_form_rows(_np(q[b, :, h]), _np(k[b, :, h]), _np(v[b, :, h]), [64])
+        worst = max(worst, float(np.abs(o[b, 0, h].double().numpy() - ref[0]).max()))
+    say(f"decode at 512 x 16 heads after prefill: max-abs {worst:.3e}")
+    assert worst <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("T", [1024, 8192])
+def test_sweep_shapes_sampled(T):
+    # B * T = 131072 with 16 heads: many sequences, one segment per sequence (no state pass)
+    w = W.WORKLOADS[4]
+    q, k, v = W.make_inputs(w, 0)
+    B = 131072 // T
+    q, k, v = (x.reshape(B, T, *x.shape[2:]) for x in (q, k, v))
+    o = K.fwd_chunked(*_to_gpu(q, k, v)).cpu()
+    rng = np.random.default_rng(T)
+    heads = [(int(rng.integers(B)), int(rng.integers(16))) for _ in range(4)]
+    _check_rows(q, k, v, o, heads, _rows_sampler(rng, 64), TOL[w.dtype],
+                tag=f"sweep shape T={T} B={B}")
+
+
+@pytest.mark.parametrize("case", ["p32", "p16_g2"])
+def test_quadratic_ragged_T(case):
+    wid, g = (3, 1) if case == "p32" else (2, 2)
+    w = W.WORKLOADS[wid]
+    q, k, v = W.make_inputs(w, 72, T=300, B=1, H=2)
+    ref, dref = O.closed_form(_np(q), _np(k), _np(v), groups=g)
+    o, d = K.fwd_quadratic(*_to_gpu(q, k, v), groups=g, return_den=True)
+    err = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
+    say(f"quadratic {case} T=300: max-abs {err:.3e}")
+    assert err <= TOL[w.dtype]
+    np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=1e-2)
+
+
+def test_state_pass_skips_only_the_last_segment():
+    # several segments per sequence: every segment but the last feeds a prefix; outputs of
+    # every segment must still be right (the skipped state is the last one's)
+    w = W.WORKLOADS[2]
+    q, k, v = W.make_inputs(w, 73, T=2048, B=8, H=16)
+    o = K.fwd_chunked(*_to_gpu(q, k, v), seg_chunks=5).cpu()
+    rng = np.random.default_rng(74)
+    heads = [(b, h) for b in range(8) for h in range(16)]
+    _check_rows(q, k, v, o, heads, lambda T: np.array([0, 319, 320, 639, 640, 1600, 1919, 1920,
+                                                       2047]), TOL[w.dtype],
+                tag="segment boundaries, all heads")
