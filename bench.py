@@ -5,8 +5,10 @@
 A step is one kata_fwd_chunked call (chunk-state build, prefix scan over chunk states,
 intra-chunk tiles + inter-chunk readout + output gate) over the whole workload, with q, k, v
 already resident in HBM and the output and workspace preallocated.  W untimed steps, then K
-steps timed with HIP events on the stream the kernels are launched on; the library's own
-per-kernel events give the dominant kernel's average duration for the roofline figure.
+steps timed with HIP events on the stream the kernels are launched on (value, ms_per_step),
+then K more steps in which the library's own per-kernel events on the same stream give the
+dominant kernel's average duration for the roofline figure (those events add a few
+microseconds per kernel, so that pass's step time is reported separately).
 
 Printed: one JSON line.  value = head-tokens (B*H*T) per second.  roofline: the algorithmic
 bytes (bf16 q, k, v in, fp32 o out) or flops of the step, whichever bound is slower at MI355X's
@@ -158,8 +160,10 @@ def cpu_baseline(w, target_s=12.0):
 
 
 def timed_steps(step, steps, warmup, dev):
-    """W untimed steps, then K steps between two events on the launch stream; returns the
-    average ms per step and the library's per-kernel event timings of the K steps."""
+    """W untimed steps, then K steps between two events on the launch stream (the step time),
+    then K more steps with the library's per-kernel events on the same stream (the kernel
+    durations; those events cost a few microseconds per kernel, so they stay out of the step
+    time).  Returns (ms per step, {kernel: (launches, total ms)}, instrumented ms per step)."""
     import torch
 
     import kernelized_psd_feature_amd as K
@@ -168,15 +172,22 @@ def timed_steps(step, steps, warmup, dev):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    K.timing_begin()
-    start.record(stream)
-    for _ in range(steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    per_kernel = K.timing_end()
-    return start.elapsed_time(stop) / steps, per_kernel
+
+    def region(instrumented):
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if instrumented:
+            K.timing_begin()
+        start.record(stream)
+        for _ in range(steps):
+            step()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        per_kernel = K.timing_end() if instrumented else None
+        return start.elapsed_time(stop) / steps, per_kernel
+
+    ms, _ = region(False)
+    ms_inst, per_kernel = region(True)
+    return ms, per_kernel, ms_inst
 
 
 def sweep(q, k, v, args, dev):
@@ -204,7 +215,7 @@ def sweep(q, k, v, args, dev):
                 K.fwd_chunked(qs, ks, vs, seg_chunks=seg, out=os_, workspace=ws,
                               state=args.state)
 
-            ms, _ = timed_steps(step, 20, 5, dev)
+            ms, _, _ = timed_steps(step, 20, 5, dev)
             point[key + "ms"] = round(ms, 5)
             point[key + "tokens_per_s"] = round(B * 16 * T / (ms / 1e3), 1)
             del ws
@@ -237,7 +248,7 @@ def run_chunked(args, dev, w):
         else:
             K.fwd_quadratic(q, k, v, out=o, groups=args.groups)
 
-    ms, per_kernel = timed_steps(step, args.steps, args.warmup, dev)
+    ms, per_kernel, ms_inst = timed_steps(step, args.steps, args.warmup, dev)
     tokens = w.B * w.H * w.T
     dom = "chunk_output" if args.form == "chunked" else "quadratic"
     launches, total_ms = per_kernel[dom]
@@ -260,6 +271,7 @@ def run_chunked(args, dev, w):
                    "out_dtype": "fp32", "eps": 1e-6},
         "roofline": roof,
         "kernels_ms": {n: round(t / max(c, 1), 5) for n, (c, t) in per_kernel.items() if c},
+        "ms_per_step_with_kernel_events": round(ms_inst, 5),
         "step_roofline_frac": roofline(fpt * tokens, bpt * tokens, ms / 1e3)["frac"],
         "dominant_kernel_source_sha": sha,
     }
@@ -317,7 +329,7 @@ def run_decode(args, dev):
     def step():
         K.decode(q, k, v, state, out=o)
 
-    ms, per_kernel = timed_steps(step, args.steps, args.warmup, dev)
+    ms, per_kernel, ms_inst = timed_steps(step, args.steps, args.warmup, dev)
     tokens = w.B * w.H * w.T
     launches, total_ms = per_kernel["decode"]
     avg_ms = total_ms / max(launches, 1)
@@ -336,6 +348,7 @@ def run_decode(args, dev):
                      "traffic": load_traffic("decode", w.name,
                                              source_sha(KERNEL_SOURCES["decode"]))},
         "kernels_ms": {n: round(t / max(c, 1), 5) for n, (c, t) in per_kernel.items() if c},
+        "ms_per_step_with_kernel_events": round(ms_inst, 5),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(w)

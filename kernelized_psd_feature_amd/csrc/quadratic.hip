@@ -122,7 +122,11 @@ __global__ __launch_bounds__(kThreads, 2) void quadratic_kernel(
   __shared__ QLds<P> sm;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in a scalar
-  const int qb = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;   // heavy first
+  // Longest query blocks first over all (b, h) (longest-processing-time order), so short
+  // sequences end without a long tail.  Consecutive blocks go to consecutive XCDs; with B*H a
+  // multiple of 8 every block of one (b, h) lands on the same XCD and shares its L2 for K, V.
+  const int nbh = pr.B * pr.H, id = blockIdx.x;
+  const int qb = (gridDim.x / nbh) - 1 - id / nbh, h = (id % nbh) % pr.H, b = (id % nbh) / pr.H;
   const int t0 = qb * QB;
   const int tw = t0 + QW * w;                       // this wave's first query
   int tq[2];                                        // this lane's query in each query tile
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 2) void quadratic_kernel(
 template <typename Tout, int P, int GW>
 void launch_t(const DevProblem& pr, hipStream_t st, const void* q, const void* k,
               const void* v, void* o, float* den) {
-  dim3 grid((pr.T + QB - 1) / QB, pr.H, pr.B);
+  dim3 grid(((pr.T + QB - 1) / QB) * pr.H * pr.B);
   quadratic_kernel<Tout, P, GW><<<grid, kThreads, 0, st>>>(
       pr, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (Tout*)o, den);
 }
@@ -288,11 +292,16 @@ hipError_t launch_dispatch(const DevProblem& pr, int gw, hipStream_t st, const v
 
 }  // namespace
 
+// The grid is one-dimensional: every query block of every (b, h).
+bool quadratic_mfma_grid_fits(const DevProblem& pr) {
+  return int64_t((pr.T + QB - 1) / QB) * pr.B * pr.H <= 0x7fffffffLL;
+}
+
 // gw: KATA-Mg group width (p for a single group)
 hipError_t launch_quadratic_mfma(const DevProblem& pr, int gw, bool out_bf16, const void* q,
                                  const void* k, const void* v, void* o, float* den,
                                  hipStream_t st) {
-  if (pr.dv != DV) return hipErrorInvalidValue;
+  if (pr.dv != DV || !quadratic_mfma_grid_fits(pr)) return hipErrorInvalidValue;
   return out_bf16 ? launch_dispatch<__bf16>(pr, gw, st, q, k, v, o, den)
                   : launch_dispatch<float>(pr, gw, st, q, k, v, o, den);
 }
