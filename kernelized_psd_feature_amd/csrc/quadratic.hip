@@ -4,15 +4,20 @@
 //
 //   o_t = sum_{s<=t} a_ts v_s / (eps + sum_{s<=t} a_ts)
 //
-// A workgroup of four waves takes 128 queries, each wave two 16-query tiles, and walks the
-// key blocks of 64 up to its diagonal.  Per 32-key step a wave forms the squared, masked score
-// tiles of both query tiles (keys as rows, so they are directly the A operands of P.V), then
-// reads each V fragment once from LDS and feeds it to both query tiles: the V reads, the
-// limiting LDS traffic, are spent on twice the MFMA work of one query tile per wave.  Key and
-// value blocks are double-buffered in LDS (one barrier per block); the next block's global
-// loads are in flight while the current one is computed.  No running maximum is kept: the
-// weights are squares, so nothing needs rescaling.  The row sum of the denominator adds the
-// same bf16-rounded weights that enter P.V, and runs on MFMA too (P against a block of ones).
+// A workgroup of four waves takes 4 QW queries; a wave holds NB blocks of 32 queries and walks
+// the key blocks of 64 up to its diagonal, 32 keys per step.  Every product is the full-rate
+// 32x32x16 bf16 MFMA (the 16-deep 16x16 shape runs at half rate on gfx950):
+//   scores  S^T (32 keys x 32 queries) = K_step . Q^T, depth p (one product at p = 16, two at
+//           p = 32; KATA-Mg: one per group with the query operand cut to the group);
+//   P.V     O (32 queries x 64 values) += P (32 x 32 keys) . V_step, four products.
+// The result layout of the score product (lane l: query l % 32, keys 8 (v / 4) + 4 (l / 32) +
+// v % 4 for its 16 registers v) is, after squaring and rounding to bf16, directly the A operand
+// of P.V for two 16-key halves; the V operands are read in that key order with LDS transpose
+// loads, once per step for all NB query blocks of the wave.  The denominator's row sums add the
+// same bf16-rounded weights that enter P.V (dot2 against ones, fp32 accumulate).  No running
+// maximum is kept: the weights are squares, so nothing needs rescaling.  Key and value blocks
+// are double-buffered in LDS (one barrier per block); the next block's global loads are in
+// flight while the current one is computed.
 #include "device.h"
 #include "kata.h"
 #include "mfma_util.h"
@@ -23,23 +28,26 @@ namespace kata {
 namespace {
 
 constexpr int DV = 64, KB = 64;        // value width, keys per block
-constexpr int QW = 32, QB = 128;       // queries per wave, per workgroup
-constexpr int kThreads = 256;
-constexpr int VROW = 80;               // bf16 per v row (160 B)
+constexpr int kThreads = 256;          // four waves
+constexpr int VROW = 80;               // bf16 per v row (160 B: transpose reads conflict-free)
+
+// NB blocks of 32 queries per wave
+template <int NB>
+struct QShape {
+  static constexpr int QW = 32 * NB, QB = 4 * QW;
+};
 
 template <int P>
 struct QTraits;
 template <>
 struct QTraits<16> {
-  static constexpr int KROW = 20;      // bf16 per k row (40 B)
-  using Frag = s16x4;
-  __device__ static f32x4 mma(const Frag& a, const Frag& b) { return mfma16(a, b, zero4()); }
+  static constexpr int KROW = 24;      // bf16 per k row (48 B, 16-byte aligned pieces)
+  static constexpr int KD = 1;         // 16-deep products per score block
 };
 template <>
 struct QTraits<32> {
-  static constexpr int KROW = 40;      // bf16 per k row (80 B)
-  using Frag = bf16x8;
-  __device__ static f32x4 mma(const Frag& a, const Frag& b) { return mfma32(a, b, zero4()); }
+  static constexpr int KROW = 40;      // 80 B
+  static constexpr int KD = 2;
 };
 
 template <int P>
@@ -48,93 +56,133 @@ struct __align__(16) QLds {
   __bf16 V[2][KB][VROW];
 };
 
-// score operand: row `row` of a row-major [.][ROW] bf16 tile, K-slots of lane group g
-template <int P, int ROW>
-__device__ __forceinline__ typename QTraits<P>::Frag score_frag(const __bf16 (*X)[ROW], int row,
-                                                                 int g) {
-  if constexpr (P == 16)
-    return __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2*>(&X[row][4 * g]));
-  else
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&X[row][8 * g]));
-}
-
-template <int P>
-__device__ __forceinline__ typename QTraits<P>::Frag query_frag(const __bf16* qrow, int g,
-                                                                bool live) {
-  if constexpr (P == 16) {
-    const uint2 u = live ? *reinterpret_cast<const uint2*>(qrow + 4 * g) : uint2{0u, 0u};
-    return __builtin_bit_cast(s16x4, u);
-  } else {
-    const uint4 u = live ? *reinterpret_cast<const uint4*>(qrow + 8 * g) : uint4{0u, 0u, 0u, 0u};
-    return __builtin_bit_cast(bf16x8, u);
-  }
-}
-
-struct QStage {
-  uint4 k, v0, v1;
-};
-
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma3232(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// row of result register v of a 32x32 product in lane half h (= lane / 32)
+__device__ __forceinline__ int row_of(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 
 // two fp32 -> two bf16 (round to nearest even) in one dword
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// Weights of a 16-key x 16-query tile: keys s0 + 4g + r (rows), query t (this lane's column),
-// squared, masked by selection where kMask (s0 + 4g + r <= t), rounded to bf16 and packed.
-// GW < P (KATA-Mg, p = 16 only): one product per group of GW coordinates with the query operand
-// cut to that group's lane groups, the squared group dots summed.
-template <int P, int GW, bool kMask>
-__device__ __forceinline__ uint2 weights(const typename QTraits<P>::Frag& kf,
-                                         const typename QTraits<P>::Frag& qf, int s0, int t,
-                                         int lane) {
-  f32x4 x2;
-  if constexpr (GW == P) {
-    const f32x4 sc = QTraits<P>::mma(kf, qf);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x2[r] = sc[r] * sc[r];
-  } else {
-    static_assert(P == 16, "grouped scores at p = 16");
-    const int grp = (4 * (lane >> 4)) / GW;
-    x2 = zero4();
-#pragma unroll
-    for (int j = 0; j < P / GW; ++j) {
-      const s16x4 qj = grp == j ? qf : s16x4{0, 0, 0, 0};
-      const f32x4 sc = mfma16(kf, qj, zero4());
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x2[r] = fmaf(sc[r], sc[r], x2[r]);
-    }
-  }
-  if (kMask) {
-    const int s = s0 + 4 * (lane >> 4);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x2[r] = (s + r <= t) ? x2[r] : 0.f;   // select, never multiply
-  }
-  return uint2{pack2(x2[0], x2[1]), pack2(x2[2], x2[3])};
+// running fp32 sum of the two bf16 in w
+__device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                         __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
 }
 
-template <typename Tout, int P, int GW>
-__global__ __launch_bounds__(kThreads, 2) void quadratic_kernel(
+// Query operand cut to KATA-Mg group j (p = 16): lane half h holds coordinates 8h .. 8h + 7.
+template <int GW>
+__device__ __forceinline__ bf16x8 group_cut(const bf16x8& q, int h, int j) {
+  const uint4 u = __builtin_bit_cast(uint4, q);
+  uint4 r = {0u, 0u, 0u, 0u};
+  if constexpr (GW == 8) {
+    if (h == j) r = u;
+  } else {                                          // GW == 4: coordinates 8h + 4x .. + 3
+    if (2 * h == j) r = uint4{u.x, u.y, 0u, 0u};
+    if (2 * h + 1 == j) r = uint4{0u, 0u, u.z, u.w};
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Squared scores x2 of a 32-key x 32-query block (keys s0 + row_of(v, h), query t) -> the
+// packed bf16 A operand of P.V, masked by selection where kMask; lsum adds the rounded values.
+template <bool kMask>
+__device__ __forceinline__ void pack_weights(f32x16 x2, int s0, int t, int h, uint32_t (&pw)[8],
+                                             float& lsum) {
+  if (kMask) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) x2[v] = (s0 + row_of(v, h) <= t) ? x2[v] : 0.f;   // select
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pw[j] = pack2(x2[2 * j], x2[2 * j + 1]);
+    lsum = add_pair(pw[j], lsum);
+  }
+}
+
+// Weights of a 32-key x 32-query block as the packed bf16 A operand of P.V: keys s0 +
+// row_of(v, h) against query t (this lane's), squared (GW < P: squared group dots summed),
+// masked by selection where kMask, rounded to bf16; lsum adds the rounded values.
+template <int P, int GW, bool kMask>
+__device__ __forceinline__ void weights(const bf16x8 (&kf)[QTraits<P>::KD],
+                                        const bf16x8 (&qf)[QTraits<P>::KD], int s0, int t,
+                                        int h, uint32_t (&pw)[8], float& lsum) {
+  f32x16 x2;
+  if constexpr (GW == P) {
+    f32x16 sc = mfma3232(kf[0], qf[0], zero16());
+    if constexpr (QTraits<P>::KD == 2) sc = mfma3232(kf[1], qf[1], sc);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) x2[v] = sc[v] * sc[v];
+  } else {
+    static_assert(P == 16, "grouped scores at p = 16");
+    x2 = zero16();
+#pragma unroll
+    for (int j = 0; j < P / GW; ++j) {
+      const f32x16 sc = mfma3232(kf[0], group_cut<GW>(qf[0], h, j), zero16());
+#pragma unroll
+      for (int v = 0; v < 16; ++v) x2[v] = fmaf(sc[v], sc[v], x2[v]);
+    }
+  }
+  pack_weights<kMask>(x2, s0, t, h, pw, lsum);
+}
+
+// V operand of P.V for keys [kb0, kb0 + 16) in score row order and value columns [c0, c0 + 32):
+// lane l needs V[kb0 + row_of(i, h)][c0 + l % 32] in slot i.  Two LDS transpose loads (slots
+// 0-3: keys kb0 + 4h + 0..3, slots 4-7: 8 further); within a 16-lane block, lane j points at
+// V[row + j / 4][col + 4 (j % 4)], which hands lane i the value V[row + r][col + i] in slot r.
+__device__ __forceinline__ bf16x8 v_frag32(const __bf16 (*V)[VROW], int kb0, int c0, int lane) {
+  const int h = lane >> 5, j = lane & 15;
+  const int row = kb0 + 4 * h + (j >> 2), col = c0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&V[row][col]));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&V[row + 8][col]));
+  const uint2 ul = __builtin_bit_cast(uint2, lo), uh = __builtin_bit_cast(uint2, hi);
+  return __builtin_bit_cast(bf16x8, uint4{ul.x, ul.y, uh.x, uh.y});
+}
+
+struct QStage {
+  uint4 k, v0, v1;
+};
+
+template <typename Tout, int P, int GW, int NB>
+__global__ __launch_bounds__(kThreads, NB == 1 ? 3 : 2) void quadratic_kernel(
     DevProblem pr, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den_out) {
+  constexpr int QW = QShape<NB>::QW, QB = QShape<NB>::QB, KD = QTraits<P>::KD;
   __shared__ QLds<P> sm;
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in a scalar
   // Longest query blocks first over all (b, h) (longest-processing-time order), so short
   // sequences end without a long tail.  Consecutive blocks go to consecutive XCDs; with B*H a
   // multiple of 8 every block of one (b, h) lands on the same XCD and shares its L2 for K, V.
   const int nbh = pr.B * pr.H, id = blockIdx.x;
-  const int qb = (gridDim.x / nbh) - 1 - id / nbh, h = (id % nbh) % pr.H, b = (id % nbh) / pr.H;
+  const int qb = (gridDim.x / nbh) - 1 - id / nbh, hd = (id % nbh) % pr.H, b = (id % nbh) / pr.H;
   const int t0 = qb * QB;
   const int tw = t0 + QW * w;                       // this wave's first query
-  int tq[2];                                        // this lane's query in each query tile
-  typename QTraits<P>::Frag qf[2];
+  int tq[NB];                                       // this lane's query in each query block
+  bf16x8 qf[NB][KD];                                // Q^T operands: coordinates 16 d + 8 h + i
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    tq[x] = tw + 16 * x + l16;
-    qf[x] = query_frag<P>(q + row_off(pr.sq, b, min(tq[x], pr.T - 1), h), g, tq[x] < pr.T);
+  for (int x = 0; x < NB; ++x) {
+    tq[x] = tw + 32 * x + l32;
+    const __bf16* qrow = q + row_off(pr.sq, b, min(tq[x], pr.T - 1), hd);
+#pragma unroll
+    for (int d = 0; d < KD; ++d) {
+      const uint4 u = tq[x] < pr.T ? ld16(qrow + 16 * d + 8 * h) : uint4{0u, 0u, 0u, 0u};
+      qf[x][d] = __builtin_bit_cast(bf16x8, u);
+    }
   }
 
   // staging: k rows -- p = 16: threads < 128, 16 B each (row tid / 2, half tid % 2); p = 32:
@@ -144,86 +192,141 @@ __global__ __launch_bounds__(kThreads, 2) void quadratic_kernel(
   constexpr int KPIECES = P / 8;                    // 16-byte pieces per k row
   const bool kth = w < KB * KPIECES / 64;          // wave-uniform (w is a scalar)
   const int kr = tid / KPIECES, kc = tid % KPIECES, a2 = tid >> 3, c8 = tid & 7;
-  const __bf16* kbase = k + row_off(pr.sk, b, 0, h) + 8 * kc;
-  const __bf16* vbase = v + row_off(pr.sv, b, 0, h) + 8 * c8;
+  const __bf16* kbase = k + row_off(pr.sk, b, 0, hd) + 8 * kc;
+  const __bf16* vbase = v + row_off(pr.sv, b, 0, hd) + 8 * c8;
   const long long sk_t = pr.sk[1], sv_t = pr.sv[1];
   const int tmax = pr.T - 1;
+  // this thread's rows within a block (fixed); the block offset s0 * stride is wave-uniform
+  const __bf16* krow = kbase + (long long)kr * sk_t;
+  const __bf16* vrow = vbase + (long long)(2 * a2) * sv_t;
   auto load = [&](int kb) {
-    const int s0 = kb * KB, sv0 = s0 + 2 * a2;
+    const int s0 = kb * KB;
     QStage x;
-    x.k = kth ? ld16(kbase + (long long)min(s0 + kr, tmax) * sk_t) : uint4{0u, 0u, 0u, 0u};
-    x.v0 = ld16(vbase + (long long)min(sv0, tmax) * sv_t);
-    x.v1 = ld16(vbase + (long long)min(sv0 + 1, tmax) * sv_t);
+    if (s0 + KB <= pr.T) {                          // whole block in range
+      const __bf16* vp = vrow + (long long)s0 * sv_t;
+      x.k = kth ? ld16(krow + (long long)s0 * sk_t) : uint4{0u, 0u, 0u, 0u};
+      x.v0 = ld16(vp);
+      x.v1 = ld16(vp + sv_t);
+    } else {                                        // ragged last block: rows clamped to T - 1
+      const int sv0 = s0 + 2 * a2;
+      x.k = kth ? ld16(kbase + (long long)min(s0 + kr, tmax) * sk_t) : uint4{0u, 0u, 0u, 0u};
+      x.v0 = ld16(vbase + (long long)min(sv0, tmax) * sv_t);
+      x.v1 = ld16(vbase + (long long)min(sv0 + 1, tmax) * sv_t);
+    }
     return x;
   };
   auto store = [&](const QStage& x, int kb) {
     const int buf = kb & 1;
-    if (kth) {
-      if constexpr (P == 16) {                       // 40-byte rows: two 8-byte stores
-        *reinterpret_cast<uint2*>(&sm.K[buf][kr][8 * kc]) = uint2{x.k.x, x.k.y};
-        *reinterpret_cast<uint2*>(&sm.K[buf][kr][8 * kc + 4]) = uint2{x.k.z, x.k.w};
-      } else {
-        *reinterpret_cast<uint4*>(&sm.K[buf][kr][8 * kc]) = x.k;
-      }
-    }
+    if (kth) *reinterpret_cast<uint4*>(&sm.K[buf][kr][8 * kc]) = x.k;
     *reinterpret_cast<uint4*>(&sm.V[buf][2 * a2][8 * c8]) = x.v0;
     *reinterpret_cast<uint4*>(&sm.V[buf][2 * a2 + 1][8 * c8]) = x.v1;
     const int s0 = kb * KB;
     if (s0 + KB > pr.T) {                            // ragged last block: zero rows >= T
       const uint4 z = {0u, 0u, 0u, 0u};
-      if (kth && s0 + kr >= pr.T) {
-        if constexpr (P == 16) {
-          *reinterpret_cast<uint2*>(&sm.K[buf][kr][8 * kc]) = uint2{0u, 0u};
-          *reinterpret_cast<uint2*>(&sm.K[buf][kr][8 * kc + 4]) = uint2{0u, 0u};
-        } else {
-          *reinterpret_cast<uint4*>(&sm.K[buf][kr][8 * kc]) = z;
-        }
-      }
+      if (kth && s0 + kr >= pr.T) *reinterpret_cast<uint4*>(&sm.K[buf][kr][8 * kc]) = z;
       if (s0 + 2 * a2 >= pr.T) *reinterpret_cast<uint4*>(&sm.V[buf][2 * a2][8 * c8]) = z;
       if (s0 + 2 * a2 + 1 >= pr.T) *reinterpret_cast<uint4*>(&sm.V[buf][2 * a2 + 1][8 * c8]) = z;
     }
   };
 
-  // O[x][nt]: query tile x, value columns 16 nt..; L[x]: row sums of the same bf16 weights,
-  // on MFMA against a block of ones (every column holds the sum; rows are the queries)
-  f32x4 O[2][4], L[2];
+  // O[x][n]: query block x, value columns 32 n ..; lsum[x]: this lane's share (its 16 keys of
+  // each step) of the row sum of query tq[x]
+  f32x16 O[NB][2];
+  float lsum[NB];
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    L[x] = zero4();
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) O[x][nt] = zero4();
+  for (int x = 0; x < NB; ++x) {
+    lsum[x] = 0.f;
+    O[x][0] = zero16();
+    O[x][1] = zero16();
   }
-  const uint32_t one2 = 0x3F803F80u;                // two bf16 ones
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, uint4{one2, one2, one2, one2});
 
-  // One 32-key step of block kb for both query tiles: weights (A operands of P.V), their row
-  // sums on MFMA, then each V fragment once for both tiles.  kMask: every weight is masked by
-  // selection (keys at or past the wave's first query, future keys too).
+  // One 32-key step m of block kb for the wave's query blocks.  kMask: every weight is masked
+  // by selection, and query blocks wholly before the step's keys are skipped.
   auto step = [&](int kb, int m, auto mask_tag) {
     constexpr bool kMask = decltype(mask_tag)::value;
     const int buf = kb & 1, sm0 = kb * KB + 32 * m;
-    bf16x8 pa[2];
+    bf16x8 kf[KD];                                  // K operand: key 32 m + l32, coords 16 d + 8 h
 #pragma unroll
-    for (int x2 = 0; x2 < 2; ++x2) {
-      uint2 e[2];
+    for (int d = 0; d < KD; ++d)
+      kf[d] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                             &sm.K[buf][32 * m + l32][16 * d + 8 * h]));
+    uint32_t pw[NB][8];
+    bool live[NB];
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
-        e[half] = weights<P, GW, kMask>(score_frag<P>(sm.K[buf], 32 * m + 16 * half + l16, g),
-                                        qf[x2], sm0 + 16 * half, tq[x2], lane);
-      pa[x2] = __builtin_bit_cast(bf16x8, uint4{e[0].x, e[0].y, e[1].x, e[1].y});
-      L[x2] = mfma32(pa[x2], ones, L[x2]);
+    for (int x = 0; x < NB; ++x) {
+      live[x] = !kMask || sm0 <= tw + 32 * x + 31;  // wave-uniform
+      if (live[x]) weights<P, GW, kMask>(kf, qf[x], sm0, tq[x], h, pw[x], lsum[x]);
     }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const bf16x8 vb = v_frag(sm.V[buf], m, nt, lane);
-      O[0][nt] = mfma32(pa[0], vb, O[0][nt]);
-      O[1][nt] = mfma32(pa[1], vb, O[1][nt]);
+    for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const bf16x8 vb = v_frag32(sm.V[buf], 32 * m + 16 * kh, 32 * n, lane);
+#pragma unroll
+        for (int x = 0; x < NB; ++x) {
+          if (!live[x]) continue;
+          const bf16x8 pa = __builtin_bit_cast(
+              bf16x8, uint4{pw[x][4 * kh], pw[x][4 * kh + 1], pw[x][4 * kh + 2], pw[x][4 * kh + 3]});
+          O[x][n] = mfma3232(pa, vb, O[x][n]);
+        }
+      }
     }
   };
   using NoMask = std::integral_constant<bool, false>;
   using Mask = std::integral_constant<bool, true>;
 
-  // Blocks [0, nf) precede every query of the workgroup (t0 is a multiple of 128): one path,
+  // A whole unmasked block (single feature group): every score product of the block first, so
+  // that the weights of one query block (VALU) run beside the P.V products of the previous one.
+  auto block_nomask = [&](int kb) {
+    const int buf = kb & 1;
+    f32x16 sc[2][NB];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      bf16x8 kf[KD];
+#pragma unroll
+      for (int d = 0; d < KD; ++d)
+        kf[d] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                               &sm.K[buf][32 * m + l32][16 * d + 8 * h]));
+#pragma unroll
+      for (int x = 0; x < NB; ++x) {
+        sc[m][x] = mfma3232(kf[0], qf[x][0], zero16());
+        if constexpr (KD == 2) sc[m][x] = mfma3232(kf[1], qf[x][1], sc[m][x]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      bf16x8 vb[2][2];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) vb[kh][n] = v_frag32(sm.V[buf], 32 * m + 16 * kh, 32 * n, lane);
+#pragma unroll
+      for (int x = 0; x < NB; ++x) {
+        f32x16 x2;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x2[r] = sc[m][x][r] * sc[m][x][r];
+        uint32_t pw[8];
+        pack_weights<false>(x2, 0, 0, h, pw, lsum[x]);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          const bf16x8 pa = __builtin_bit_cast(
+              bf16x8, uint4{pw[4 * kh], pw[4 * kh + 1], pw[4 * kh + 2], pw[4 * kh + 3]});
+#pragma unroll
+          for (int n = 0; n < 2; ++n) O[x][n] = mfma3232(pa, vb[kh][n], O[x][n]);
+        }
+      }
+    }
+  };
+  auto full_block = [&](int kb) {
+    if constexpr (GW == P) {
+      block_nomask(kb);
+    } else {
+      step(kb, 0, NoMask{});
+      step(kb, 1, NoMask{});
+    }
+  };
+
+  // Blocks [0, nf) precede every query of the workgroup (t0 is a multiple of 64): one path,
   // no masks.  Blocks [nf, last_kb] meet the diagonal of some wave.
   const int last_kb = min((t0 + QB - 1) / KB, (pr.T - 1) / KB);
   const int nf = t0 / KB;
@@ -232,8 +335,7 @@ __global__ __launch_bounds__(kThreads, 2) void quadratic_kernel(
   x = load(min(1, last_kb));
   __syncthreads();
   for (int kb = 0; kb < nf; ++kb) {
-    step(kb, 0, NoMask{});
-    step(kb, 1, NoMask{});
+    full_block(kb);
     store(x, kb + 1);                                // kb + 1 <= nf <= last_kb; its buffer
     x = load(min(kb + 2, last_kb));                  // was read before the last barrier
     __syncthreads();
@@ -241,8 +343,7 @@ __global__ __launch_bounds__(kThreads, 2) void quadratic_kernel(
   for (int kb = nf; kb <= last_kb; ++kb) {
     const int s_base = kb * KB;
     if (s_base + KB - 1 < tw) {                     // the whole block precedes the wave's queries
-      step(kb, 0, NoMask{});
-      step(kb, 1, NoMask{});
+      full_block(kb);
     } else if (s_base < tw + QW) {                  // the block meets the wave's diagonal
       step(kb, 0, Mask{});
       if (s_base + 32 < tw + QW) step(kb, 1, Mask{});
@@ -254,29 +355,43 @@ __global__ __launch_bounds__(kThreads, 2) void quadratic_kernel(
     __syncthreads();
   }
 
-  // gated outputs: lane holds queries tw + 16 x + 4g + r (rows), columns 16 nt + l16
+  // gated outputs: register v of O[x][n] holds query tw + 32 x + row_of(v, h), column
+  // 32 n + l32; the full row sum of query i of a block is lsum in lanes i and i + 32
 #pragma unroll
-  for (int x2 = 0; x2 < 2; ++x2) {
+  for (int xb = 0; xb < NB; ++xb) {
+    const float lq = lsum[xb] + __shfl_xor(lsum[xb], 32);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tr = tw + 16 * x2 + 4 * g + r;
-      const float D = pr.eps + L[x2][r];
+    for (int vr = 0; vr < 16; ++vr) {
+      const int row = row_of(vr, h), tr = tw + 32 * xb + row;
+      const float D = pr.eps + __shfl(lq, row);
       if (tr >= pr.T) continue;
       const float ir = 1.f / D;
-      Tout* op = o + row_off(pr.so, b, tr, h);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) op[16 * nt + l16] = cvt_out<Tout>(O[x2][nt][r] * ir);
-      if (den_out && l16 == 0) den_out[((long long)b * pr.T + tr) * pr.H + h] = D;
+      Tout* op = o + row_off(pr.so, b, tr, hd);
+      op[l32] = from_f32<Tout>(O[xb][0][vr] * ir);
+      op[32 + l32] = from_f32<Tout>(O[xb][1][vr] * ir);
+      if (den_out && l32 == 0) den_out[((long long)b * pr.T + tr) * pr.H + hd] = D;
     }
   }
+}
+
+// query blocks of 32 per wave: two where the grid still holds several waves of workgroups
+// (each V operand then feeds two products), one for short sequences
+int blocks_per_wave(const DevProblem& pr) {
+  const long long wg2 = (long long)((pr.T + QShape<2>::QB - 1) / QShape<2>::QB) * pr.B * pr.H;
+  return wg2 >= 4096 ? 2 : 1;
 }
 
 template <typename Tout, int P, int GW>
 void launch_t(const DevProblem& pr, hipStream_t st, const void* q, const void* k,
               const void* v, void* o, float* den) {
-  dim3 grid(((pr.T + QB - 1) / QB) * pr.H * pr.B);
-  quadratic_kernel<Tout, P, GW><<<grid, kThreads, 0, st>>>(
-      pr, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (Tout*)o, den);
+  auto go = [&](auto nb_tag) {
+    constexpr int NB = decltype(nb_tag)::value, QB = QShape<NB>::QB;
+    dim3 grid(((pr.T + QB - 1) / QB) * pr.H * pr.B);
+    quadratic_kernel<Tout, P, GW, NB><<<grid, kThreads, 0, st>>>(
+        pr, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (Tout*)o, den);
+  };
+  if (blocks_per_wave(pr) == 2) go(std::integral_constant<int, 2>{});
+  else go(std::integral_constant<int, 1>{});
 }
 
 template <typename Tout>
@@ -294,6 +409,7 @@ hipError_t launch_dispatch(const DevProblem& pr, int gw, hipStream_t st, const v
 
 // The grid is one-dimensional: every query block of every (b, h).
 bool quadratic_mfma_grid_fits(const DevProblem& pr) {
+  constexpr int QB = QShape<1>::QB;                 // the smaller block: the larger grid
   return int64_t((pr.T + QB - 1) / QB) * pr.B * pr.H <= 0x7fffffffLL;
 }
 
