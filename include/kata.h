@@ -219,8 +219,10 @@ const char* kata_status_string(kata_status s);
 const char* kata_last_error(void);
 
 /* ---- Per-kernel timing (measurement support; off by default) --------------------------
- * kata_timing_begin(): on this host thread, from now on every kernel the library enqueues is
- * bracketed by a pair of HIP events on the stream it is launched on.
+ * kata_timing_begin(): on this host thread, from now on every kernel kind an entry point runs
+ * is timed by a pair of HIP events that its kernels' own dispatches stamp (launched with
+ * hipExtLaunchKernel on the caller's stream, so no marker packets sit between kernels): the
+ * span from the start of its first kernel to the end of its last.
  * kata_timing_end(): synchronizes those events and returns, per kernel kind, the number of
  * launches and the summed elapsed milliseconds; recording stops.  Kinds are indexed by
  * kata_kernel_kind.  Returns INVALID_ARGUMENT if begin was not called, DEVICE on an event

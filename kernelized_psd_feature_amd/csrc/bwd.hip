@@ -220,7 +220,7 @@ struct PrepLaunch {
   static hipError_t run(const DevProblem& pr, const void* q, const void* k, const void* v,
                         const void* dO, float* D, float* delta, hipStream_t st) {
     dim3 grid((pr.T + kRows - 1) / kRows, pr.H, pr.B);
-    bwd_prep_kernel<Tin, P, DV><<<grid, kThreads, 0, st>>>(
+    launch_kernel(bwd_prep_kernel<Tin, P, DV>, grid, kThreads, 0, st,
         pr, (const Tin*)q, (const Tin*)k, (const Tin*)v, (const Tin*)dO, D, delta);
     return hipGetLastError();
   }
@@ -232,7 +232,7 @@ struct DqLaunch {
                         const void* dO, const float* D, const float* delta, float* dq,
                         hipStream_t st) {
     dim3 grid((pr.T + kThreads - 1) / kThreads, pr.H, pr.B);
-    bwd_dq_kernel<Tin, P, DV><<<grid, kThreads, 0, st>>>(
+    launch_kernel(bwd_dq_kernel<Tin, P, DV>, grid, kThreads, 0, st,
         pr, (const Tin*)q, (const Tin*)k, (const Tin*)v, (const Tin*)dO, D, delta, dq);
     return hipGetLastError();
   }
@@ -244,7 +244,7 @@ struct DkdvLaunch {
                         const void* dO, const float* D, const float* delta, float* dk,
                         float* dv, hipStream_t st) {
     dim3 grid((pr.T + kThreads - 1) / kThreads, pr.H, pr.B);
-    bwd_dkdv_kernel<Tin, P, DV><<<grid, kThreads, 0, st>>>(
+    launch_kernel(bwd_dkdv_kernel<Tin, P, DV>, grid, kThreads, 0, st,
         pr, (const Tin*)q, (const Tin*)k, (const Tin*)v, (const Tin*)dO, D, delta, dk, dv);
     return hipGetLastError();
   }

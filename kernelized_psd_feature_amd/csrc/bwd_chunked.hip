@@ -252,27 +252,27 @@ struct BwdChunked {
   static hipError_t prep(const DevProblem& pr, const void* dO, float* g, float* e,
                          hipStream_t st) {
     const long long n = (long long)pr.B * pr.T * pr.H;
-    bwd_chunk_prep_kernel<Tin, DV><<<dim3((unsigned)((n + 255) / 256)), 256, 0, st>>>(
-        pr, (const Tin*)dO, g, e);
+    launch_kernel(bwd_chunk_prep_kernel<Tin, DV>, dim3((unsigned)((n + 255) / 256)), 256, 0,
+                  st, pr, (const Tin*)dO, g, e);
     return hipGetLastError();
   }
   static hipError_t dq(const DevProblem& pr, const void* q, const void* k, const void* v,
                        const float* g, const float* e, const float* states, int n_chunks,
                        float* dq, hipStream_t st) {
-    bwd_chunk_dq_kernel<Tin, P, DV><<<dim3(n_chunks, pr.H, pr.B), kThreads, 0, st>>>(
+    launch_kernel(bwd_chunk_dq_kernel<Tin, P, DV>, dim3(n_chunks, pr.H, pr.B), kThreads, 0, st,
         pr, (const Tin*)q, (const Tin*)k, (const Tin*)v, g, e, states, n_chunks, dq);
     return hipGetLastError();
   }
   static hipError_t rev(const DevProblem& pr, const void* q, const float* g, const float* e,
                         float* states, int n_chunks, hipStream_t st) {
-    bwd_rev_state_kernel<Tin, P, DV><<<dim3(n_chunks, pr.H, pr.B), kThreads, 0, st>>>(
+    launch_kernel(bwd_rev_state_kernel<Tin, P, DV>, dim3(n_chunks, pr.H, pr.B), kThreads, 0, st,
         pr, (const Tin*)q, g, e, states, n_chunks);
     return hipGetLastError();
   }
   static hipError_t dkdv(const DevProblem& pr, const void* q, const void* k, const void* v,
                          const float* g, const float* e, const float* states, int n_chunks,
                          float* dk, float* dv, hipStream_t st) {
-    bwd_chunk_dkdv_kernel<Tin, P, DV><<<dim3(n_chunks, pr.H, pr.B), kThreads, 0, st>>>(
+    launch_kernel(bwd_chunk_dkdv_kernel<Tin, P, DV>, dim3(n_chunks, pr.H, pr.B), kThreads, 0, st,
         pr, (const Tin*)q, (const Tin*)k, (const Tin*)v, g, e, states, n_chunks, dk, dv);
     return hipGetLastError();
   }

@@ -162,11 +162,12 @@ template <typename Tin, typename Tout, int P, int DV>
 hipError_t launch_decode_t(const DevProblem& pr, const void* q, const void* k, const void* v,
                            void* o, float* den, float* state, hipStream_t st) {
   static_assert(DV % kWaves == 0 && (P * P) % 64 == 0, "decode tiling");
-  decode_rows_kernel<Tin, Tout, P, DV><<<dim3(DV / kWaves, pr.H, pr.B), kThreads, 0, st>>>(
-      pr, (const Tin*)q, (const Tin*)k, (const Tin*)v, (Tout*)o, den, state);
+  launch_kernel(decode_rows_kernel<Tin, Tout, P, DV>, dim3(DV / kWaves, pr.H, pr.B), kThreads,
+                0, st, pr, (const Tin*)q, (const Tin*)k, (const Tin*)v, (Tout*)o, den, state);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_z_kernel<Tin, P, DV><<<dim3(1, pr.H, pr.B), 64, 0, st>>>(pr, (const Tin*)k, state);
+  launch_kernel(decode_z_kernel<Tin, P, DV>, dim3(1, pr.H, pr.B), 64, 0, st, pr, (const Tin*)k,
+                state);
   return hipGetLastError();
 }
 
@@ -191,8 +192,8 @@ hipError_t launch_state_sum(const float* src, long long n_seq, long long n, long
                             bool tiles, float* dst, hipStream_t st) {
   if (elems % 4 || (tiles && elems != 16 * 16 * 65)) return hipErrorInvalidValue;   // p^2 (dv + 1)
   const long long blocks = (elems / 4 + 255) / 256;
-  state_sum_kernel<<<dim3((unsigned)blocks, (unsigned)n_seq), 256, 0, st>>>(src, n, elems,
-                                                                          tiles ? 1 : 0, dst);
+  launch_kernel(state_sum_kernel, dim3((unsigned)blocks, (unsigned)n_seq), 256, 0, st, src, n,
+                elems, tiles ? 1 : 0, dst);
   return hipGetLastError();
 }
 

@@ -2,11 +2,37 @@
 // API calls.  Nothing here is part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 namespace kata {
+
+// ---- kernel launch -------------------------------------------------------------------
+// The open per-kernel timing scope of this host thread (null when timing is off): a pair of
+// events that the scope's first launch stamps with its start and every launch with its end.
+struct LaunchTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;
+};
+LaunchTiming* launch_timing();
+
+// Every kernel of the library is launched here.  With timing on, the launch goes through
+// hipExtLaunchKernelGGL so the events take the timestamps of the kernel's own dispatch: no
+// marker packets are enqueued between kernels, and the recorded time is the kernels' alone.
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t st,
+                          Args... args) {
+  LaunchTiming* t = launch_timing();
+  if (t) {
+    hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)shmem, st,
+                          t->used ? nullptr : t->start, t->stop, 0u, args...);
+    t->used = true;
+  } else {
+    kernel<<<grid, block, shmem, st>>>(args...);
+  }
+}
 
 // Problem description passed to kernels by value.
 struct DevProblem {

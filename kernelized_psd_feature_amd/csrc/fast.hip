@@ -577,7 +577,7 @@ template <typename Tout, bool kPacked, int GW>
 void walk_launch(const DevProblem& pr, int L, int n_seg, dim3 grid, hipStream_t st,
                  const __bf16* q, const __bf16* k, const __bf16* v, void* o, float* den,
                  const float* states) {
-  chunk_output_fast_kernel<Tout, kPacked, GW><<<grid, kThreads, 0, st>>>(
+  launch_kernel(chunk_output_fast_kernel<Tout, kPacked, GW>, grid, kThreads, 0, st,
       pr, L, n_seg, q, k, v, (Tout*)o, den, states);
 }
 
@@ -605,13 +605,17 @@ hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int gw, in
   dim3 grid(n_seg, pr.H, pr.B);
   const __bf16 *kk = (const __bf16*)k, *vv = (const __bf16*)v;
   if (gw == 8)
-    chunk_state_fast_kernel<true, 8><<<grid, kThreads, 0, st>>>(pr, L, n_seg, n_used, kk, vv, states);
+    launch_kernel(chunk_state_fast_kernel<true, 8>, grid, kThreads, 0, st, pr, L, n_seg, n_used,
+                  kk, vv, states);
   else if (gw == 4)
-    chunk_state_fast_kernel<true, 4><<<grid, kThreads, 0, st>>>(pr, L, n_seg, n_used, kk, vv, states);
+    launch_kernel(chunk_state_fast_kernel<true, 4>, grid, kThreads, 0, st, pr, L, n_seg, n_used,
+                  kk, vv, states);
   else if (packed)
-    chunk_state_fast_kernel<true, P><<<grid, kThreads, 0, st>>>(pr, L, n_seg, n_used, kk, vv, states);
+    launch_kernel(chunk_state_fast_kernel<true, P>, grid, kThreads, 0, st, pr, L, n_seg, n_used,
+                  kk, vv, states);
   else
-    chunk_state_fast_kernel<false, P><<<grid, kThreads, 0, st>>>(pr, L, n_seg, n_used, kk, vv, states);
+    launch_kernel(chunk_state_fast_kernel<false, P>, grid, kThreads, 0, st, pr, L, n_seg, n_used,
+                  kk, vv, states);
   return hipGetLastError();
 }
 

@@ -474,7 +474,7 @@ hipError_t launch_chunk_state32(const DevProblem& pr, int L, int n_seg, int n_us
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_state32_kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  chunk_state32_kernel<<<dim3(n_seg, pr.H, pr.B), kThreads, lds, st>>>(
+  launch_kernel(chunk_state32_kernel, dim3(n_seg, pr.H, pr.B), kThreads, lds, st,
       pr, L, n_seg, n_used, (const __bf16*)k, (const __bf16*)v, states);
   return hipGetLastError();
 }
@@ -491,14 +491,14 @@ hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_output32_kernel<__bf16>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    chunk_output32_kernel<__bf16><<<grid, kThreads, lds, st>>>(pr, L, n_seg, qq, kk, vv,
-                                                               (__bf16*)o, den, states);
+    launch_kernel(chunk_output32_kernel<__bf16>, grid, kThreads, lds, st, pr, L, n_seg, qq, kk,
+                  vv, (__bf16*)o, den, states);
   } else {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_output32_kernel<float>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    chunk_output32_kernel<float><<<grid, kThreads, lds, st>>>(pr, L, n_seg, qq, kk, vv,
-                                                              (float*)o, den, states);
+    launch_kernel(chunk_output32_kernel<float>, grid, kThreads, lds, st, pr, L, n_seg, qq, kk,
+                  vv, (float*)o, den, states);
   }
   return hipGetLastError();
 }

@@ -193,7 +193,7 @@ struct QuadLaunch {
   static hipError_t run(const DevProblem& pr, const void* q, const void* k, const void* v,
                         void* o, float* den, hipStream_t st) {
     dim3 grid((pr.T + kRows - 1) / kRows, pr.H, pr.B);
-    quadratic_generic_kernel<Tin, Tout, P, DV><<<grid, kThreads, 0, st>>>(
+    launch_kernel(quadratic_generic_kernel<Tin, Tout, P, DV>, grid, kThreads, 0, st,
         pr, (const Tin*)q, (const Tin*)k, (const Tin*)v, (Tout*)o, den);
     return hipGetLastError();
   }
@@ -204,7 +204,7 @@ struct StateLaunch {
   static hipError_t run(const DevProblem& pr, const void* k, const void* v, float* states,
                         int n_chunks, hipStream_t st) {
     dim3 grid(n_chunks, pr.H, pr.B);
-    chunk_state_generic_kernel<Tin, P, DV><<<grid, kThreads, 0, st>>>(
+    launch_kernel(chunk_state_generic_kernel<Tin, P, DV>, grid, kThreads, 0, st,
         pr, (const Tin*)k, (const Tin*)v, states, n_chunks);
     return hipGetLastError();
   }
@@ -216,7 +216,7 @@ struct OutputLaunch {
                         void* o, float* den, const float* states, int n_chunks,
                         hipStream_t st) {
     dim3 grid(n_chunks, pr.H, pr.B);
-    chunk_output_generic_kernel<Tin, Tout, P, DV><<<grid, kThreads, 0, st>>>(
+    launch_kernel(chunk_output_generic_kernel<Tin, Tout, P, DV>, grid, kThreads, 0, st,
         pr, (const Tin*)q, (const Tin*)k, (const Tin*)v, (Tout*)o, den, states, n_chunks);
     return hipGetLastError();
   }

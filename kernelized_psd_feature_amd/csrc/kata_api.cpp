@@ -97,32 +97,52 @@ struct TimingState {
 };
 thread_local TimingState g_timing;
 
-// Brackets one launch with events when timing is on.
+// The open timing scope of this host thread: the launches inside it (kata::launch_kernel)
+// stamp its events with their own dispatch timestamps.
+thread_local kata::LaunchTiming* g_scope = nullptr;
+
+// One timing record per scope when timing is on: the span from the start of the scope's first
+// kernel to the end of its last (no record if it launched nothing).
 struct Timed {
   int kind;
-  hipStream_t st;
-  hipEvent_t a = nullptr;
-  Timed(int kind_, hipStream_t st_) : kind(kind_), st(st_) {
-    if (g_timing.on) {
-      a = g_timing.get();
-      if (a && hipEventRecord(a, st) != hipSuccess) {
-        g_timing.pool.push_back(a);
-        a = nullptr;
-      }
+  kata::LaunchTiming lt;
+  kata::LaunchTiming* prev = nullptr;
+  bool open = false;
+  Timed(int kind_, hipStream_t) : kind(kind_) {
+    if (!g_timing.on) return;
+    lt.start = g_timing.get();
+    lt.stop = g_timing.get();
+    if (lt.start && lt.stop) {
+      prev = g_scope;
+      g_scope = &lt;
+      open = true;
+    } else {
+      if (lt.start) g_timing.pool.push_back(lt.start);
+      if (lt.stop) g_timing.pool.push_back(lt.stop);
+      lt.start = lt.stop = nullptr;
     }
   }
   ~Timed() {
-    if (a) {
-      hipEvent_t b = g_timing.get();
-      if (b && hipEventRecord(b, st) == hipSuccess) {
-        g_timing.recs.push_back({kind, a, b});
-      } else {
-        g_timing.pool.push_back(a);
-        if (b) g_timing.pool.push_back(b);
-      }
+    if (!open) return;
+    g_scope = prev;
+    if (lt.used) {
+      g_timing.recs.push_back({kind, lt.start, lt.stop});
+    } else {
+      g_timing.pool.push_back(lt.start);
+      g_timing.pool.push_back(lt.stop);
     }
   }
+  Timed(const Timed&) = delete;
+  Timed& operator=(const Timed&) = delete;
 };
+
+}  // namespace
+
+namespace kata {
+LaunchTiming* launch_timing() { return g_scope; }
+}  // namespace kata
+
+namespace {
 
 kata::DevProblem to_dev(const kata_problem* pr) {
   kata::DevProblem d;

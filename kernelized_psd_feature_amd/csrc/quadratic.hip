@@ -387,7 +387,7 @@ void launch_t(const DevProblem& pr, hipStream_t st, const void* q, const void* k
   auto go = [&](auto nb_tag) {
     constexpr int NB = decltype(nb_tag)::value, QB = QShape<NB>::QB;
     dim3 grid(((pr.T + QB - 1) / QB) * pr.H * pr.B);
-    quadratic_kernel<Tout, P, GW, NB><<<grid, kThreads, 0, st>>>(
+    launch_kernel(quadratic_kernel<Tout, P, GW, NB>, grid, kThreads, 0, st,
         pr, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (Tout*)o, den);
   };
   if (blocks_per_wave(pr) == 2) go(std::integral_constant<int, 2>{});

@@ -164,8 +164,8 @@ hipError_t launch_scan_tiles(float* x, long long n_seq, long long n, long long e
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
     if (e != hipSuccess) return e;
-    kern<<<grid, kScanThreads, lds, st>>>(x, n, elems, strip, tile_rows, n_tiles, exclusive,
-                                          totals, tile_offsets);
+    launch_kernel(kern, grid, kScanThreads, lds, st, x, n, elems, strip, tile_rows, n_tiles,
+                  exclusive, totals, tile_offsets);
     return hipSuccess;
   };
   hipError_t e;
@@ -184,7 +184,7 @@ hipError_t launch_tile_sums(const float* x, long long n_seq, long long n, long l
                             int tile_rows, int n_tiles, float* sums, hipStream_t st) {
   dim3 grid((unsigned)((elems / 4 + kScanThreads - 1) / kScanThreads), n_tiles,
             (unsigned)n_seq);
-  tile_sums_kernel<<<grid, kScanThreads, 0, st>>>(x, n, elems, tile_rows, n_tiles, sums);
+  launch_kernel(tile_sums_kernel, grid, kScanThreads, 0, st, x, n, elems, tile_rows, n_tiles, sums);
   return hipGetLastError();
 }
 
