@@ -126,6 +126,45 @@ def cold_cache_ms(step, n, dev):
     return total / n
 
 
+def measured_peaks(dev):
+    """The box's own ceilings, for calibration beside the spec peaks (never on the hot path):
+    a 1 GiB device-to-device copy (GB/s counting its read and its write) and an 8192^3 bf16
+    GEMM through torch (TFLOP/s)."""
+    import torch
+
+    stream = torch.cuda.current_stream(dev)
+
+    def seconds(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps / 1e3
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    copy = 2 * n / seconds(lambda: dst.copy_(src), 10) / 1e9
+    del src, dst
+    m = 8192
+    x = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    y = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    gemm = 2 * m ** 3 / seconds(lambda: torch.mm(x, y), 10) / 1e12
+    del x, y
+    return {"copy_GBps": round(copy, 1), "bf16_gemm_TFLOPs": round(gemm, 1)}
+
+
+def with_measured_peak(roof, peaks):
+    """roofline fraction of the dominant kernel against the box's measured ceiling"""
+    ceiling = peaks["copy_GBps"] if roof["bound"] == "hbm" else peaks["bf16_gemm_TFLOPs"]
+    return dict(peaks, frac_of_measured=round(roof["achieved"] / ceiling, 4))
+
+
 def cpu_baseline(w, target_s=12.0):
     """Time the oracle's closed form on uniformly sampled query rows of one head of the
     workload; head-tokens/s of the oracle on the full workload = rows / seconds (a uniform
@@ -275,6 +314,11 @@ def run_chunked(args, dev, w):
         "step_roofline_frac": roofline(fpt * tokens, bpt * tokens, ms / 1e3)["frac"],
         "dominant_kernel_source_sha": sha,
     }
+    if args.form == "chunked":
+        line["chunked_plan"] = K.chunked_plan(q, k, v, chunk=w.chunk, seg_chunks=args.seg,
+                                              state=args.state, groups=args.groups)
+    if not args.no_calibration:
+        line["measured_peaks"] = with_measured_peak(roof, measured_peaks(dev))
     if not args.no_cold_cache:
         line["ms_per_step_cold_cache"] = round(cold_cache_ms(step, max(5, args.steps // 5), dev),
                                                5)
@@ -350,6 +394,8 @@ def run_decode(args, dev):
         "kernels_ms": {n: round(t / max(c, 1), 5) for n, (c, t) in per_kernel.items() if c},
         "ms_per_step_with_kernel_events": round(ms_inst, 5),
     }
+    if not args.no_calibration:
+        line["measured_peaks"] = with_measured_peak(line["roofline"], measured_peaks(dev))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(w)
     return line
@@ -372,6 +418,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the T sweep")
     ap.add_argument("--no-cold-cache", action="store_true",
                     help="skip the cache-flushed repetition (profiler runs)")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the measured copy and GEMM ceilings")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="run only a device copy of this many MiB (counter calibration)")
     args = ap.parse_args()

@@ -122,6 +122,26 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
                              const void* v, void* o, float* den, void* workspace,
                              size_t ws_bytes, void* stream);
 
+/* The plan kata_fwd_chunked takes for a problem (host only; no device call).  The chunks of
+ * one (b, h) are walked in `segments` segments of `chunks_per_segment` chunks; a state pass
+ * and an exclusive prefix scan over the segment states, a combining tree of `scan_levels`
+ * levels, feed the walk.  With one segment per (b, h) on the MFMA kernels (the sequential
+ * inter-chunk form) neither runs and scan_levels is 0.  Source: gist.science section 2.3
+ * (inter-chunk depth O(log N_C)).
+ *   out: host struct, filled on success.
+ * Errors: INVALID_ARGUMENT (NULL out, or as kata_fwd_chunked), UNSUPPORTED. */
+typedef struct {
+  int64_t n_chunks;            /* T / chunk, per (b, h) */
+  int64_t chunks_per_segment;
+  int64_t segments;            /* per (b, h) */
+  int64_t state_floats;        /* fp32 values in one segment state */
+  int32_t scan_levels;
+  int32_t mfma;                /* 1: bf16 MFMA kernels; 0: fp32 kernels */
+  int32_t packed;              /* 1: states keep only the unique (i <= j) feature pairs */
+  int32_t reserved;
+} kata_chunked_plan;
+kata_status kata_fwd_chunked_plan(const kata_problem* pr, kata_chunked_plan* out);
+
 /* Bytes of workspace kata_chunk_state_scan needs (0 when n_chunks fits one tree). */
 size_t kata_chunk_state_scan_workspace_size(int64_t n_seq, int64_t n_chunks,
                                             int64_t state_elems);

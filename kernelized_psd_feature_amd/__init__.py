@@ -24,7 +24,7 @@ import os
 import torch
 
 __all__ = [
-    "KataError", "fwd_quadratic", "fwd_chunked", "chunked_workspace_size",
+    "KataError", "fwd_quadratic", "fwd_chunked", "chunked_workspace_size", "chunked_plan",
     "chunk_state_scan", "scan_workspace_size", "bwd", "bwd_workspace_size",
     "recurrent_state", "recurrent_state_workspace_size", "decode", "state_shape",
     "timing_begin", "timing_end", "library_path", "KERNEL_KINDS",
@@ -57,6 +57,13 @@ class _Problem(ctypes.Structure):
     ]
 
 
+class _ChunkedPlan(ctypes.Structure):
+    _fields_ = [("n_chunks", ctypes.c_int64), ("chunks_per_segment", ctypes.c_int64),
+                ("segments", ctypes.c_int64), ("state_floats", ctypes.c_int64),
+                ("scan_levels", ctypes.c_int32), ("mfma", ctypes.c_int32),
+                ("packed", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class _Times(ctypes.Structure):
     _fields_ = [("launches", ctypes.c_int64 * 7), ("total_ms", ctypes.c_double * 7)]
 
@@ -78,6 +85,7 @@ def _lib():
             "kata_fwd_quadratic": (I32, [P, VP, VP, VP, VP, VP, VP]),
             "kata_fwd_chunked_workspace_size": (SZ, [P]),
             "kata_fwd_chunked": (I32, [P, VP, VP, VP, VP, VP, VP, SZ, VP]),
+            "kata_fwd_chunked_plan": (I32, [P, ctypes.POINTER(_ChunkedPlan)]),
             "kata_chunk_state_scan_workspace_size": (SZ, [I64, I64, I64]),
             "kata_chunk_state_scan": (I32, [VP, I64, I64, I64, I32, VP, VP, SZ,
                                             ctypes.POINTER(I32), VP]),
@@ -185,6 +193,19 @@ def chunked_workspace_size(q, k, v, chunk=64, seg_chunks=0, out_dtype=torch.floa
     pr = _make_problem(q, k, v, chunk=chunk, seg_chunks=seg_chunks, out_dtype=out_dtype,
                        state=state, groups=groups)
     return int(_lib().kata_fwd_chunked_workspace_size(ctypes.byref(pr)))
+
+
+def chunked_plan(q, k, v, chunk=64, seg_chunks=0, out_dtype=torch.float32, state="packed",
+                 groups=1):
+    """The plan fwd_chunked takes (host only): n_chunks, chunks_per_segment, segments (per
+    (b, h)), state_floats, scan_levels (0: no state pass and no scan), mfma, packed."""
+    pr = _make_problem(q, k, v, chunk=chunk, seg_chunks=seg_chunks, out_dtype=out_dtype,
+                       state=state, groups=groups)
+    out = _ChunkedPlan()
+    _check(_lib().kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)),
+           "kata_fwd_chunked_plan")
+    return {name: int(getattr(out, name)) for name, _ in _ChunkedPlan._fields_
+            if name != "reserved"}
 
 
 def fwd_chunked(q, k, v, chunk=64, eps=1e-6, out_dtype=torch.float32, seg_chunks=0,

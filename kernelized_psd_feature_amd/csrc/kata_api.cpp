@@ -248,6 +248,25 @@ size_t kata_fwd_chunked_workspace_size(const kata_problem* pr) {
   return kata::plan_chunked(pr, kata::chunk_fast_available()).ws_bytes;
 }
 
+kata_status kata_fwd_chunked_plan(const kata_problem* pr, kata_chunked_plan* out) {
+  g_last_error.clear();
+  if (!out) return set_error(KATA_ERR_INVALID_ARGUMENT, "out is null");
+  std::string why;
+  const kata_status s = kata::validate_problem(pr, Form::Chunked, &why);
+  if (s != KATA_OK) return set_error(s, why);
+  const kata::ChunkPlan cp = kata::plan_chunked(pr, kata::chunk_fast_available());
+  std::memset(out, 0, sizeof(*out));
+  out->n_chunks = cp.n_chunks;
+  out->chunks_per_segment = cp.L;
+  out->segments = cp.n_seg;
+  out->state_floats = cp.state_elems;
+  out->mfma = cp.fast;
+  out->packed = cp.packed;
+  const bool one_segment = cp.fast && cp.n_seg == 1;   // as kata_fwd_chunked
+  out->scan_levels = one_segment ? 0 : kata::plan_scan(cp.n_seq, cp.n_seg, cp.state_elems).levels;
+  return KATA_OK;
+}
+
 kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* k,
                              const void* v, void* o, float* den, void* workspace,
                              size_t ws_bytes, void* stream) {

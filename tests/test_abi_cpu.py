@@ -300,3 +300,29 @@ def test_groups_do_not_change_workspace_sizes():
             lib.kata_fwd_chunked_workspace_size(ctypes.byref(base))
         assert lib.kata_bwd_chunked_workspace_size(ctypes.byref(pr)) == \
             lib.kata_bwd_chunked_workspace_size(ctypes.byref(base))
+
+
+def test_chunked_plan_reports_segments_and_scan_depth():
+    lib = _lib()
+    out = K._ChunkedPlan()
+    # 131k tokens, 16 heads: segments of several chunks, a prefix scan over them
+    pr = _problem(B=1, H=16, T=131072)
+    pr.state_layout = 1
+    assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK
+    assert (out.n_chunks, out.mfma, out.packed) == (2048, 1, 1)
+    assert out.segments == -(-2048 // out.chunks_per_segment) and 1 < out.segments < 2048
+    assert out.scan_levels == math.ceil(math.log2(out.segments))
+    assert out.state_floats == (10 * 16 * 64 + 256)       # 10 packed tiles of 16 x 64, + Z
+    # 256 sequences fill the GPU: one segment each, no state pass, no scan
+    pr = _problem(B=16, H=16, T=1024)
+    assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK
+    assert (out.segments, out.chunks_per_segment, out.scan_levels) == (1, 16, 0)
+    assert out.state_floats == 16 * 16 * 65                # direct layout: p^2 (dv + 1)
+    # fp32 kernels: one state per chunk, a scan of ceil(log2 N_c) levels
+    pr = _problem(B=1, H=1, T=256, p=8, dv=16, chunk=32, in_dt=0)
+    assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK
+    assert (out.mfma, out.n_chunks, out.segments, out.scan_levels) == (0, 8, 8, 3)
+    # errors
+    assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), None) == INVALID
+    assert lib.kata_fwd_chunked_plan(ctypes.byref(_problem(T=100)), ctypes.byref(out)) == \
+        UNSUPPORTED
