@@ -254,7 +254,7 @@ def sweep(q, k, v, args, dev):
                 K.fwd_chunked(qs, ks, vs, seg_chunks=seg, out=os_, workspace=ws,
                               state=args.state)
 
-            ms, _, _ = timed_steps(step, 20, 5, dev)
+            ms, _, _ = timed_steps(step, 30, 10, dev)
             point[key + "ms"] = round(ms, 5)
             point[key + "tokens_per_s"] = round(B * 16 * T / (ms / 1e3), 1)
             del ws
@@ -273,32 +273,35 @@ def run_chunked(args, dev, w):
     if args.layout == "bhtd":
         q, k, v = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
     q, k, v = (x.to(dev) for x in (q, k, v))
-    o = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    out_dtype = torch.bfloat16 if args.out == "bf16" else torch.float32
+    o = torch.empty(v.shape, dtype=out_dtype, device=dev)
     ws = None
     if args.form == "chunked":
         need = K.chunked_workspace_size(q, k, v, chunk=w.chunk, seg_chunks=args.seg,
-                                        state=args.state, groups=args.groups)
+                                        out_dtype=out_dtype, state=args.state,
+                                        groups=args.groups)
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
     def step():
         if args.form == "chunked":
             K.fwd_chunked(q, k, v, chunk=w.chunk, seg_chunks=args.seg, out=o, workspace=ws,
-                          state=args.state, groups=args.groups)
+                          out_dtype=out_dtype, state=args.state, groups=args.groups)
         else:
-            K.fwd_quadratic(q, k, v, out=o, groups=args.groups)
+            K.fwd_quadratic(q, k, v, out=o, out_dtype=out_dtype, groups=args.groups)
 
     ms, per_kernel, ms_inst = timed_steps(step, args.steps, args.warmup, dev)
     tokens = w.B * w.H * w.T
     dom = "chunk_output" if args.form == "chunked" else "quadratic"
     launches, total_ms = per_kernel[dom]
     avg_ms = total_ms / max(launches, 1)
-    bpt = algorithmic_bytes_per_token(w.p, w.dv)
+    bpt = algorithmic_bytes_per_token(w.p, w.dv, out_bytes=2 if args.out == "bf16" else 4)
     fpt = (chunked_flops_per_token(w.p, w.dv, w.chunk) if args.form == "chunked"
            else quadratic_flops_per_token(w.p, w.dv, w.T))
     sources = KERNEL_SOURCES[dom if w.p == 16 else dom + "32"]
     sha = source_sha(sources)
     roof = roofline(fpt * tokens, bpt * tokens, avg_ms / 1e3)
-    roof["traffic"] = load_traffic(dom, w.name, sha)
+    # the committed counters were taken with fp32 outputs
+    roof["traffic"] = load_traffic(dom, w.name, sha) if args.out == "fp32" else None
     line = {
         "metric": METRIC, "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -307,7 +310,7 @@ def run_chunked(args, dev, w):
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "p": w.p, "dv": w.dv,
                    "chunk": w.chunk, "form": args.form, "seg_chunks": args.seg,
                    "state": args.state, "groups": args.groups, "layout": args.layout.upper(),
-                   "out_dtype": "fp32", "eps": 1e-6},
+                   "out_dtype": args.out, "eps": 1e-6},
         "roofline": roof,
         "kernels_ms": {n: round(t / max(c, 1), 5) for n, (c, t) in per_kernel.items() if c},
         "ms_per_step_with_kernel_events": round(ms_inst, 5),
@@ -323,7 +326,7 @@ def run_chunked(args, dev, w):
         line["ms_per_step_cold_cache"] = round(cold_cache_ms(step, max(5, args.steps // 5), dev),
                                                5)
     if args.form == "chunked" and w.name == "long_context_131k" and not args.no_sweep \
-            and args.layout == "bthd":
+            and args.layout == "bthd" and args.out == "fp32":
         del ws
         line["sweep"] = sweep(q, k, v, args, dev)
         sp = [x["scan_speedup"] for x in line["sweep"]]
@@ -414,6 +417,8 @@ def main():
                     help="chunk-state storage: all p^2 rows or the p(p+1)/2 unique ones")
     ap.add_argument("--groups", type=int, default=1,
                     help="KATA-Mg factor count g (1: the single PSD factor)")
+    ap.add_argument("--out", choices=["fp32", "bf16"], default="fp32",
+                    help="output dtype: fp32 (parity mode, the headline) or bf16 (fast mode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the T sweep")
     ap.add_argument("--no-cold-cache", action="store_true",

@@ -158,15 +158,16 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
   if (cp.fast) {
     int L = pr->seg_chunks;
     if (L == 0) {
-      // With a walk per sequence on every CU (B*H >= 256), one segment per sequence: no
-      // segment states (which cost a second read of k and v) and no scan.  Otherwise fill the
-      // workgroup slots of the GPU (256 CUs x 3 resident workgroups) in as few whole rounds as
-      // possible, with segments of at most 64 chunks: fewer, longer segments mean less
-      // prefix-scan traffic, whole rounds avoid an idle tail.
-      // (the p = 32 walk is one eight-wave workgroup per CU: 256 slots)
-      const int64_t cus = 256, slots = cp.fast32 ? 256 : 768;
+      // With one walk per sequence filling at least two thirds of the workgroup slots of the
+      // GPU (256 CUs x 3 resident workgroups; the p = 32 walk is one eight-wave workgroup per
+      // CU: 256 slots), one segment per sequence: no segment states (which cost a second read
+      // of k and v) and no scan.  Otherwise fill the slots in as few whole rounds as possible,
+      // with segments of at most 64 chunks: fewer, longer segments mean less prefix-scan
+      // traffic, whole rounds avoid an idle tail.  (Measured at 131072 tokens: 256 sequences
+      // of 8192 run faster as 3 segments each, 512 of 4096 as one.)
+      const int64_t slots = cp.fast32 ? 256 : 768;
       L = 1;
-      if (cp.n_seq >= cus) {
+      if (3 * cp.n_seq >= 2 * slots) {
         L = cp.n_chunks;
       } else if (cp.n_seq * cp.n_chunks > slots) {
         for (int64_t rounds = 1;; ++rounds) {

@@ -313,11 +313,15 @@ def test_chunked_plan_reports_segments_and_scan_depth():
     assert out.segments == -(-2048 // out.chunks_per_segment) and 1 < out.segments < 2048
     assert out.scan_levels == math.ceil(math.log2(out.segments))
     assert out.state_floats == (10 * 16 * 64 + 256)       # 10 packed tiles of 16 x 64, + Z
-    # 256 sequences fill the GPU: one segment each, no state pass, no scan
-    pr = _problem(B=16, H=16, T=1024)
+    # 512 sequences fill two thirds of the GPU's 768 workgroup slots: one segment each, no
+    # state pass, no scan; 256 sequences take 3 segments each (768 walks)
+    pr = _problem(B=32, H=16, T=1024)
     assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK
     assert (out.segments, out.chunks_per_segment, out.scan_levels) == (1, 16, 0)
     assert out.state_floats == 16 * 16 * 65                # direct layout: p^2 (dv + 1)
+    pr = _problem(B=16, H=16, T=8192)
+    assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK
+    assert (out.segments, out.chunks_per_segment, out.scan_levels) == (3, 43, 2)
     # fp32 kernels: one state per chunk, a scan of ceil(log2 N_c) levels
     pr = _problem(B=1, H=1, T=256, p=8, dv=16, chunk=32, in_dt=0)
     assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK

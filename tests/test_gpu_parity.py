@@ -886,7 +886,8 @@ def test_decode_bench_shape_after_prefill():
 
 @pytest.mark.parametrize("T", [1024, 8192])
 def test_sweep_shapes_sampled(T):
-    # B * T = 131072 with 16 heads: many sequences, one segment per sequence (no state pass)
+    # B * T = 131072 with 16 heads: many sequences; one segment per sequence (no state pass)
+    # at T = 1024, three per sequence at T = 8192 (256 sequences)
     w = W.WORKLOADS[4]
     q, k, v = W.make_inputs(w, 0)
     B = 131072 // T
