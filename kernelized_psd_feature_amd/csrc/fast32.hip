@@ -14,7 +14,10 @@
 //   state tiles  wave w owns tiles rank(w) + 8 s (5 tiles for ranks 0-3, 4 for ranks 4-7; the
 //                waves with the most intra-chunk work own fewer),
 //   tokens       wave w serves tokens [16 tg, 16 tg + 16) of a chunk, tg = w % 4, and the value
-//                columns [32 ch, 32 ch + 32), ch = w / 4, so no partial outputs cross waves.
+//                columns [32 ch, 32 ch + 32), ch = w / 4.  The two waves of a token group
+//                split the readout's K steps instead of its columns (each forms phi(q) for
+//                half the features, the VALU cost of the readout) and swap the partial sums
+//                of each other's columns through LDS.
 #include "device.h"
 #include "kata.h"
 #include "mfma_util.h"
@@ -271,6 +274,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
 struct __align__(16) Walk32Lds {
   Tiles32 tl;
   uint4 Sb[kSteps][4][64];        // S_{<c} as bf16 B operands: [K step][value tile][lane]
+  f32x4 xr[kWaves][2][64];        // readout partials handed to the other wave of a token group
   unsigned char dg[4 * kSteps][2];   // double group -> (a, J)
 };
 
@@ -419,9 +423,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     const float D = pr.eps + (zq + lsum);          // D_t of token t (every lane group)
     const float inv = 1.f / D;
 
-    // ---- readout phi(q_t)^T S_{<c} over the 18 K steps, this wave's two value tiles ----
-#pragma unroll 2
-    for (int kk = 0; kk < kSteps; ++kk) {
+    // ---- readout phi(q_t)^T S_{<c}: K steps [9 ch, 9 ch + 9) for all four value tiles ----
+    f32x4 R[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll 3
+    for (int kk = (kSteps / 2) * ch; kk < (kSteps / 2) * (ch + 1); ++kk) {
       const int ga = sm.dg[4 * kk + g][0], gj = sm.dg[4 * kk + g][1];
       const uint32_t qa = *reinterpret_cast<const uint32_t*>(&tl.Qs[t][ga]);
       const uint2 qj = *reinterpret_cast<const uint2*>(&tl.Qs[t][gj]);
@@ -434,8 +439,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
         a[4 + r] = (__bf16)(i1 * jv[r]);
       }
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
-        O[n] = mfma32(a, __builtin_bit_cast(bf16x8, sm.Sb[kk][2 * ch + n][lane]), O[n]);
+      for (int n = 0; n < 4; ++n)
+        R[n] = mfma32(a, __builtin_bit_cast(bf16x8, sm.Sb[kk][n][lane]), R[n]);
+    }
+    // the other wave of the token group (w ^ 4) owns the other two value tiles (selects, not
+    // a runtime index, keep R in registers)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) sm.xr[w][n][lane] = ch ? R[n] : R[2 + n];
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const f32x4 x = sm.xr[w ^ 4][n][lane], own = ch ? R[2 + n] : R[n];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O[n][r] += own[r] + x[r];
     }
 
     // ---- gate and store: lane holds tokens 16 tg + 4 g + r, columns 32 ch + 16 n + l16 ----
