@@ -38,7 +38,7 @@ KERNEL_SOURCES = {  # files whose content defines each kernel's code
     "chunk_output": ["kernelized_psd_feature_amd/csrc/fast.hip",
                      "kernelized_psd_feature_amd/csrc/mfma_util.h",
                      "kernelized_psd_feature_amd/csrc/device.h"],
-    "quadratic": ["kernelized_psd_feature_amd/csrc/fast.hip",
+    "quadratic": ["kernelized_psd_feature_amd/csrc/quadratic.hip",
                   "kernelized_psd_feature_amd/csrc/mfma_util.h",
                   "kernelized_psd_feature_amd/csrc/device.h"],
     "decode": ["kernelized_psd_feature_amd/csrc/decode.hip",
@@ -46,7 +46,7 @@ KERNEL_SOURCES = {  # files whose content defines each kernel's code
     "chunk_output32": ["kernelized_psd_feature_amd/csrc/fast32.hip",
                        "kernelized_psd_feature_amd/csrc/mfma_util.h",
                        "kernelized_psd_feature_amd/csrc/device.h"],
-    "quadratic32": ["kernelized_psd_feature_amd/csrc/fast32.hip",
+    "quadratic32": ["kernelized_psd_feature_amd/csrc/quadratic.hip",
                     "kernelized_psd_feature_amd/csrc/mfma_util.h",
                     "kernelized_psd_feature_amd/csrc/device.h"],
 }

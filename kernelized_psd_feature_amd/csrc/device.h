@@ -42,6 +42,49 @@ struct DevProblem {
   long long sq[3], sk[3], sv[3], so[3], sdo[3];   // element strides of (b, t, h)
 };
 
+// ---- segment grids: one workgroup per (segment, head, batch) -------------------------
+// Consecutive workgroup ids are dispatched to consecutive XCDs, each with its own L2.  In
+// (B, T, H, D) storage the q and k rows of `hg` neighbouring heads share 128-byte lines, so
+// the workgroups of such a line group (same batch and segment) get ids congruent mod 8: one
+// XCD then fetches each line once.  Line groups are enumerated (batch, segment) first, so
+// when B * n_seg is a multiple of 8 every line group of one (batch, segment) lands on the same
+// XCD too (whole token rows per XCD), and the XCDs get equal shares.  The grid is
+// one-dimensional, padded to a multiple of 8 line groups; padding workgroups exit at once.
+struct SegGrid {
+  int n_seg, hg, n_hgrp;      // segments, heads per line group, line groups per (b, segment)
+  long long bs;               // B * n_seg
+  long long groups;           // bs * n_hgrp
+  long long blocks() const { return ((groups + 7) / 8) * 8 * hg; }
+};
+
+inline SegGrid make_seg_grid(const DevProblem& pr, int n_seg) {
+  SegGrid g;
+  g.n_seg = n_seg;
+  const bool heads_adjacent = pr.sq[2] == pr.p && pr.sk[2] == pr.p;
+  g.hg = heads_adjacent ? (64 / pr.p > 1 ? 64 / pr.p : 1) : 1;   // 2p bytes per bf16 row
+  g.n_hgrp = (pr.H + g.hg - 1) / g.hg;
+  g.bs = (long long)pr.B * n_seg;
+  g.groups = g.bs * g.n_hgrp;
+  return g;
+}
+
+struct SegBlock {
+  int seg, h, b;
+  bool live;
+};
+
+__device__ __forceinline__ SegBlock seg_block(const SegGrid& g, int H) {
+  const long long x = blockIdx.x, xcd = x % 8, r = x / 8;
+  const long long gi = (r / g.hg) * 8 + xcd;       // line group
+  const long long bs = gi % g.bs;
+  SegBlock s;
+  s.h = int((gi / g.bs) * g.hg + r % g.hg);
+  s.seg = int(bs % g.n_seg);
+  s.b = int(bs / g.n_seg);
+  s.live = gi < g.groups && s.h < H;
+  return s;
+}
+
 // ---- KATA-Mg scores ------------------------------------------------------------------
 // The p coordinates form groups of gs consecutive entries; the score of a (query, key) pair
 // is the sum over groups of the squared group dot product (a single group: (q . k)^2), and

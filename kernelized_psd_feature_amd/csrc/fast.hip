@@ -286,16 +286,18 @@ __device__ __forceinline__ void zero_pad_rows(TilesT<kPacked>& tl, int tid) {
 
 // ==========================================================================================
 // Segment state: S_seg = sum over the segment's chunks of Phi(K_c)^T V_c and Z_seg = sum K^T K.
-// Grid (n_seg, H, B).
+// One workgroup per (segment, head, batch), XCD-aware (SegGrid).
 // ==========================================================================================
 template <bool kPacked, int GW>
 __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
-    DevProblem pr, int L, int n_seg, int n_used, const __bf16* __restrict__ k,
+    DevProblem pr, SegGrid sg, int L, int n_seg, int n_used, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, float* __restrict__ states) {
   using LY = Layout<kPacked, GW>;
   __shared__ TilesT<kPacked> tl[2];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const SegBlock blk = seg_block(sg, pr.H);
+  if (!blk.live) return;                           // padding of the grid (whole workgroup)
+  const int seg = blk.seg, h = blk.h, b = blk.b;
   const int n_chunks = pr.T / C;
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
   const long long sv_t = pr.sv[1];
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
 // ==========================================================================================
 // Segment walk: start from the segment's exclusive prefix (S_{<c}, Z_{<c}); for every chunk,
 // outputs = (readout of the prefix + causal intra-chunk tile) / (eps + denominators), then
-// the chunk's own state is added.  Grid (n_seg, H, B).
+// the chunk's own state is added.  One workgroup per (segment, head, batch) (SegGrid).
 //   Each wave owns some state tiles (fp32, in registers, as in the state kernel) and the
 //   chunk's tokens [16 w, 16 w + 16).  Once per chunk every wave publishes its state tiles in
 //   LDS as bf16 B operands; each wave then reads out its own tokens over all state rows, so no
@@ -372,14 +374,16 @@ struct __align__(16) WalkLds {
 
 template <typename Tout, bool kPacked, int GW>
 __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
-    DevProblem pr, int L, int n_seg, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-    const __bf16* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den_out,
-    const float* __restrict__ states) {
+    DevProblem pr, SegGrid sg, int L, int n_seg, const __bf16* __restrict__ q,
+    const __bf16* __restrict__ k, const __bf16* __restrict__ v, Tout* __restrict__ o,
+    float* __restrict__ den_out, const float* __restrict__ states) {
   using LY = Layout<kPacked, GW>;
   __shared__ WalkLds<kPacked, GW> sm;
   TilesT<kPacked>& tl = sm.tl;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
-  const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const SegBlock blk = seg_block(sg, pr.H);
+  if (!blk.live) return;                           // padding of the grid (whole workgroup)
+  const int seg = blk.seg, h = blk.h, b = blk.b;
   const int n_chunks = pr.T / C;
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
   const long long sv_t = pr.sv[1];
@@ -574,25 +578,25 @@ bool chunk_fast_available() { return true; }
 
 namespace {
 template <typename Tout, bool kPacked, int GW>
-void walk_launch(const DevProblem& pr, int L, int n_seg, dim3 grid, hipStream_t st,
-                 const __bf16* q, const __bf16* k, const __bf16* v, void* o, float* den,
-                 const float* states) {
+void walk_launch(const DevProblem& pr, const SegGrid& sg, int L, int n_seg, dim3 grid,
+                 hipStream_t st, const __bf16* q, const __bf16* k, const __bf16* v, void* o,
+                 float* den, const float* states) {
   launch_kernel(chunk_output_fast_kernel<Tout, kPacked, GW>, grid, kThreads, 0, st,
-      pr, L, n_seg, q, k, v, (Tout*)o, den, states);
+      pr, sg, L, n_seg, q, k, v, (Tout*)o, den, states);
 }
 
 template <typename Tout>
-void walk_dispatch(const DevProblem& pr, bool packed, int gw, int L, int n_seg, dim3 grid,
-                   hipStream_t st, const __bf16* q, const __bf16* k, const __bf16* v, void* o,
-                   float* den, const float* states) {
+void walk_dispatch(const DevProblem& pr, const SegGrid& sg, bool packed, int gw, int L, int n_seg,
+                   dim3 grid, hipStream_t st, const __bf16* q, const __bf16* k, const __bf16* v,
+                   void* o, float* den, const float* states) {
   if (gw == 8)
-    walk_launch<Tout, true, 8>(pr, L, n_seg, grid, st, q, k, v, o, den, states);
+    walk_launch<Tout, true, 8>(pr, sg, L, n_seg, grid, st, q, k, v, o, den, states);
   else if (gw == 4)
-    walk_launch<Tout, true, 4>(pr, L, n_seg, grid, st, q, k, v, o, den, states);
+    walk_launch<Tout, true, 4>(pr, sg, L, n_seg, grid, st, q, k, v, o, den, states);
   else if (packed)
-    walk_launch<Tout, true, P>(pr, L, n_seg, grid, st, q, k, v, o, den, states);
+    walk_launch<Tout, true, P>(pr, sg, L, n_seg, grid, st, q, k, v, o, den, states);
   else
-    walk_launch<Tout, false, P>(pr, L, n_seg, grid, st, q, k, v, o, den, states);
+    walk_launch<Tout, false, P>(pr, sg, L, n_seg, grid, st, q, k, v, o, den, states);
 }
 }  // namespace
 
@@ -602,20 +606,22 @@ hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int gw, in
                                    hipStream_t st) {
   if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;
   if (gw != P && gw != 8 && gw != 4) return hipErrorInvalidValue;
-  dim3 grid(n_seg, pr.H, pr.B);
+  const SegGrid sg = make_seg_grid(pr, n_seg);
+  if (sg.blocks() > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)sg.blocks());
   const __bf16 *kk = (const __bf16*)k, *vv = (const __bf16*)v;
   if (gw == 8)
-    launch_kernel(chunk_state_fast_kernel<true, 8>, grid, kThreads, 0, st, pr, L, n_seg, n_used,
-                  kk, vv, states);
+    launch_kernel(chunk_state_fast_kernel<true, 8>, grid, kThreads, 0, st, pr, sg, L, n_seg,
+                  n_used, kk, vv, states);
   else if (gw == 4)
-    launch_kernel(chunk_state_fast_kernel<true, 4>, grid, kThreads, 0, st, pr, L, n_seg, n_used,
-                  kk, vv, states);
+    launch_kernel(chunk_state_fast_kernel<true, 4>, grid, kThreads, 0, st, pr, sg, L, n_seg,
+                  n_used, kk, vv, states);
   else if (packed)
-    launch_kernel(chunk_state_fast_kernel<true, P>, grid, kThreads, 0, st, pr, L, n_seg, n_used,
-                  kk, vv, states);
+    launch_kernel(chunk_state_fast_kernel<true, P>, grid, kThreads, 0, st, pr, sg, L, n_seg,
+                  n_used, kk, vv, states);
   else
-    launch_kernel(chunk_state_fast_kernel<false, P>, grid, kThreads, 0, st, pr, L, n_seg, n_used,
-                  kk, vv, states);
+    launch_kernel(chunk_state_fast_kernel<false, P>, grid, kThreads, 0, st, pr, sg, L, n_seg,
+                  n_used, kk, vv, states);
   return hipGetLastError();
 }
 
@@ -625,12 +631,14 @@ hipError_t launch_chunk_output_fast(const DevProblem& pr, bool packed, int gw, b
                                     hipStream_t st) {
   if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;
   if (gw != P && gw != 8 && gw != 4) return hipErrorInvalidValue;
-  dim3 grid(n_seg, pr.H, pr.B);
+  const SegGrid sg = make_seg_grid(pr, n_seg);
+  if (sg.blocks() > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)sg.blocks());
   const __bf16 *qq = (const __bf16*)q, *kk = (const __bf16*)k, *vv = (const __bf16*)v;
   if (out_bf16)
-    walk_dispatch<__bf16>(pr, packed, gw, L, n_seg, grid, st, qq, kk, vv, o, den, states);
+    walk_dispatch<__bf16>(pr, sg, packed, gw, L, n_seg, grid, st, qq, kk, vv, o, den, states);
   else
-    walk_dispatch<float>(pr, packed, gw, L, n_seg, grid, st, qq, kk, vv, o, den, states);
+    walk_dispatch<float>(pr, sg, packed, gw, L, n_seg, grid, st, qq, kk, vv, o, den, states);
   return hipGetLastError();
 }
 

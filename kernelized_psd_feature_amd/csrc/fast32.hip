@@ -201,17 +201,20 @@ __device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, f32x4 (
 
 // ==========================================================================================
 // Segment state: S_seg = sum over the segment's chunks of Phi(K_c)^T V_c, Z_seg = sum K^T K.
-// Grid (n_seg, H, B); segments seg >= n_used get a zero state without reading their tokens.
+// One workgroup per (segment, head, batch) (SegGrid); segments seg >= n_used get a zero state
+// without reading their tokens.
 // State layout (floats): tile t, value tile nt, lane -> ((t * 4 + nt) * 64 + lane) * 4, then
 // Z tile (mi, kj) -> kZOff + ((mi * 2 + kj) * 64 + lane) * 4.
 // ==========================================================================================
 __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
-    DevProblem pr, int L, int n_seg, int n_used, const __bf16* __restrict__ k,
+    DevProblem pr, SegGrid sg, int L, int n_seg, int n_used, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, float* __restrict__ states) {
   extern __shared__ __align__(16) unsigned char smem[];
   StateTiles32* tl = reinterpret_cast<StateTiles32*>(smem);    // two buffers
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const SegBlock blk = seg_block(sg, pr.H);
+  if (!blk.live) return;                           // padding of the grid (whole workgroup)
+  const int seg = blk.seg, h = blk.h, b = blk.b;
   const int n_chunks = pr.T / C;
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
   float* out = states + ((long long)(b * pr.H + h) * n_seg + seg) * kStateFloats;
@@ -269,7 +272,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
 }
 
 // ==========================================================================================
-// Segment walk (see the file comment for the work split).  Grid (n_seg, H, B).
+// Segment walk (see the file comment for the work split).  One workgroup per (segment, head,
+// batch) (SegGrid).
 // ==========================================================================================
 struct __align__(16) Walk32Lds {
   Tiles32 tl;
@@ -280,15 +284,17 @@ struct __align__(16) Walk32Lds {
 
 template <typename Tout>
 __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
-    DevProblem pr, int L, int n_seg, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-    const __bf16* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den_out,
-    const float* __restrict__ states) {
+    DevProblem pr, SegGrid sg, int L, int n_seg, const __bf16* __restrict__ q,
+    const __bf16* __restrict__ k, const __bf16* __restrict__ v, Tout* __restrict__ o,
+    float* __restrict__ den_out, const float* __restrict__ states) {
   extern __shared__ __align__(16) unsigned char smem[];
   Walk32Lds& sm = *reinterpret_cast<Walk32Lds*>(smem);
   Tiles32& tl = sm.tl;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int tg = w & 3, ch = w >> 2;
-  const int seg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const SegBlock blk = seg_block(sg, pr.H);
+  if (!blk.live) return;                           // padding of the grid (whole workgroup)
+  const int seg = blk.seg, h = blk.h, b = blk.b;
   const int n_chunks = pr.T / C;
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
 
@@ -490,8 +496,10 @@ hipError_t launch_chunk_state32(const DevProblem& pr, int L, int n_seg, int n_us
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_state32_kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  launch_kernel(chunk_state32_kernel, dim3(n_seg, pr.H, pr.B), kThreads, lds, st,
-      pr, L, n_seg, n_used, (const __bf16*)k, (const __bf16*)v, states);
+  const SegGrid sg = make_seg_grid(pr, n_seg);
+  if (sg.blocks() > 0x7fffffffLL) return hipErrorInvalidValue;
+  launch_kernel(chunk_state32_kernel, dim3((unsigned)sg.blocks()), kThreads, lds, st,
+      pr, sg, L, n_seg, n_used, (const __bf16*)k, (const __bf16*)v, states);
   return hipGetLastError();
 }
 
@@ -500,21 +508,23 @@ hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int
                                  float* den, const float* states, hipStream_t st) {
   if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;
   const size_t lds = sizeof(Walk32Lds);
-  dim3 grid(n_seg, pr.H, pr.B);
+  const SegGrid sg = make_seg_grid(pr, n_seg);
+  if (sg.blocks() > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)sg.blocks());
   const __bf16 *qq = (const __bf16*)q, *kk = (const __bf16*)k, *vv = (const __bf16*)v;
   hipError_t e;
   if (out_bf16) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_output32_kernel<__bf16>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    launch_kernel(chunk_output32_kernel<__bf16>, grid, kThreads, lds, st, pr, L, n_seg, qq, kk,
-                  vv, (__bf16*)o, den, states);
+    launch_kernel(chunk_output32_kernel<__bf16>, grid, kThreads, lds, st, pr, sg, L, n_seg, qq,
+                  kk, vv, (__bf16*)o, den, states);
   } else {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_output32_kernel<float>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    launch_kernel(chunk_output32_kernel<float>, grid, kThreads, lds, st, pr, L, n_seg, qq, kk,
-                  vv, (float*)o, den, states);
+    launch_kernel(chunk_output32_kernel<float>, grid, kThreads, lds, st, pr, sg, L, n_seg, qq,
+                  kk, vv, (float*)o, den, states);
   }
   return hipGetLastError();
 }
