@@ -130,6 +130,75 @@ __global__ __launch_bounds__(64) void decode_z_kernel(DevProblem pr, const Tin* 
   store_run(zr, z);
 }
 
+// Fused form for p <= 16: one workgroup of 16 waves per (b, h) holds the whole state, so the
+// Z row needs no second kernel.  Wave w owns the value rows d = w + 16 r (r < dv / 16) and
+// keeps its own register copy of the Z row for the denominators; every wave has used that
+// copy (so read the old Z) before the barrier, after which wave 0 alone writes the advanced
+// Z row.  Grid (H, B), 1024 threads.
+constexpr int kFusedWaves = 16;
+
+template <typename Tin, typename Tout, int P, int DV>
+__global__ __launch_bounds__(64 * kFusedWaves) void decode_fused_kernel(
+    DevProblem pr, const Tin* __restrict__ q, const Tin* __restrict__ k,
+    const Tin* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den,
+    float* __restrict__ state) {
+  constexpr int PP = P * P, E = PP / 64, R = DV / kFusedWaves;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int f0 = E * lane, i = f0 / P, j0 = f0 % P;
+  float* st = state + ((long long)b * pr.H + h) * (long long)(DV + 1) * PP;
+  float s[R][E], z[E];
+#pragma unroll
+  for (int r = 0; r < R; ++r) load_run(s[r], st + (long long)(w + kFusedWaves * r) * PP + f0);
+  load_run(z, st + (long long)DV * PP + f0);
+  unsigned in = 0;                                 // bit e: feature (i, j0 + e) is in a group
+#pragma unroll
+  for (int e = 0; e < E; ++e) in |= same_group(i, j0 + e, pr.gs) ? 1u << e : 0u;
+  for (int t = 0; t < pr.T; ++t) {
+    const Tin* qt = q + row_off(pr.sq, b, t, h);
+    const Tin* kt = k + row_off(pr.sk, b, t, h);
+    const Tin* vt = v + row_off(pr.sv, b, t, h);
+    const float qi = to_f32(qt[i]), ki = to_f32(kt[i]);
+    float kk[E], qq[E], vd[R];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool on = (in >> e) & 1u;
+      kk[e] = on ? ki * to_f32(kt[j0 + e]) : 0.f;    // phi_f(k_t)
+      qq[e] = on ? qi * to_f32(qt[j0 + e]) : 0.f;    // phi_f(q_t)
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) vd[r] = to_f32(vt[w + kFusedWaves * r]);
+    float zq = 0.f, num[R];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      z[e] += kk[e];
+      zq = fmaf(qq[e], z[e], zq);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      num[r] = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        s[r][e] = fmaf(kk[e], vd[r], s[r][e]);
+        num[r] = fmaf(qq[e], s[r][e], num[r]);
+      }
+    }
+    const float D = pr.eps + wave_sum(zq);
+#pragma unroll
+    for (int r = 0; r < R; ++r) num[r] = wave_sum(num[r]);
+    if (lane == 0) {
+      Tout* ot = o + row_off(pr.so, b, t, h);
+#pragma unroll
+      for (int r = 0; r < R; ++r) ot[w + kFusedWaves * r] = from_f32<Tout>(num[r] / D);
+      if (den && w == 0) den[((long long)b * pr.T + t) * pr.H + h] = D;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) store_run(st + (long long)(w + kFusedWaves * r) * PP + f0, s[r]);
+  __syncthreads();                                 // every wave has used its copy of the old Z
+  if (w == 0) store_run(st + (long long)DV * PP + f0, z);
+}
+
 // Sum of n states per sequence, in order, into the [dv + 1][p^2] layout.  Grid
 // (ceil(E / 4 / 256), n_seq); thread x sums float4 x of every state.  tiles != 0: the sources
 // are the MFMA state kernel's accumulator layout for p = 16, dv = 64 (float4 x = tile t, value
@@ -162,6 +231,11 @@ template <typename Tin, typename Tout, int P, int DV>
 hipError_t launch_decode_t(const DevProblem& pr, const void* q, const void* k, const void* v,
                            void* o, float* den, float* state, hipStream_t st) {
   static_assert(DV % kWaves == 0 && (P * P) % 64 == 0, "decode tiling");
+  if constexpr (P <= 16 && DV % kFusedWaves == 0) {
+    launch_kernel(decode_fused_kernel<Tin, Tout, P, DV>, dim3(pr.H, pr.B), 64 * kFusedWaves, 0,
+                  st, pr, (const Tin*)q, (const Tin*)k, (const Tin*)v, (Tout*)o, den, state);
+    return hipGetLastError();
+  }
   launch_kernel(decode_rows_kernel<Tin, Tout, P, DV>, dim3(DV / kWaves, pr.H, pr.B), kThreads,
                 0, st, pr, (const Tin*)q, (const Tin*)k, (const Tin*)v, (Tout*)o, den, state);
   hipError_t e = hipGetLastError();
