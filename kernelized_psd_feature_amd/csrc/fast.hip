@@ -15,7 +15,8 @@
 // convex combination of the values it mixes.  Feature products k_i k_j and q_i q_j are formed
 // in fp32 and rounded to bf16; the running state S is fp32 in registers and rounded to bf16
 // only as a readout operand.  Z = sum k k^T is exact (bf16 x bf16 products in fp32), and the
-// inter-chunk denominator q^T Z q is evaluated in fp32 on the vector ALUs.
+// inter-chunk denominator q^T Z q keeps fp32 accuracy: Z q runs on MFMA with Z split into a
+// bf16 high part and a bf16 remainder (q is exact in bf16), the final dot with q in fp32.
 //
 #include "device.h"
 #include "kata.h"
