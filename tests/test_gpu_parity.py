@@ -418,6 +418,27 @@ def test_non_finite_future_tokens_do_not_leak_fp32_path():
         assert torch.equal(o1[:, :77], o2[:, :77]), form
 
 
+@pytest.mark.parametrize("wid", [2, 3])
+@pytest.mark.parametrize("H", [1, 3, 5])
+def test_segment_grid_partial_line_groups(wid, H):
+    # The chunked kernels put the workgroups of heads whose q, k rows share 128-byte lines
+    # (4 heads at p = 16, 2 at p = 32) on one XCD; H not a multiple of that leaves partial
+    # line groups and padding workgroups.  Every element against the oracle, several segments
+    # per head (seg_chunks = 1 and the default plan), and head-major storage (one head per
+    # line group) bitwise equal.
+    w = W.WORKLOADS[wid]
+    q, k, v = W.make_inputs(w, 50 + H, T=256, B=3, H=H)
+    ref, _ = O.closed_form(_np(q), _np(k), _np(v))
+    qg, kg, vg = _to_gpu(q, k, v)
+    for seg in (0, 1):
+        o = K.fwd_chunked(qg, kg, vg, chunk=64, seg_chunks=seg)
+        err = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
+        say(f"p={w.p} H={H} seg_chunks={seg}: max-abs {err:.3e}")
+        assert err <= TOL[w.dtype]
+        qh, kh, vh = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (qg, kg, vg))
+        assert torch.equal(o, K.fwd_chunked(qh, kh, vh, chunk=64, seg_chunks=seg))
+
+
 @pytest.mark.parametrize("form", ["quadratic", "chunked"])
 def test_deterministic_and_layout_independent(form):
     w = W.WORKLOADS[2]
