@@ -933,6 +933,31 @@ def test_quadratic_ragged_T(case):
     np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=1e-2)
 
 
+@pytest.mark.parametrize("case", ["p16", "p16_g2", "p32"])
+def test_quadratic_two_query_blocks_per_wave_ragged_T(case):
+    # Grids of at least 4096 workgroups of 256 queries take two 32-query blocks per wave; a
+    # ragged T then leaves a partial last workgroup, a partial last key block and queries past
+    # T in both of a wave's blocks.  Edge and random rows of sampled heads, with D_t.
+    wid, g, B, T = {"p16": (2, 1, 1, 65636), "p16_g2": (2, 2, 1, 65636),
+                    "p32": (3, 1, 4, 16421)}[case]
+    w = W.WORKLOADS[wid]
+    q, k, v = W.make_inputs(w, 75, T=T, B=B, H=16)
+    assert B * 16 * -(-T // 256) >= 4096                  # the two-block shape
+    o, d = K.fwd_quadratic(*_to_gpu(q, k, v), groups=g, return_den=True)
+    o, d = o.cpu(), d.cpu()
+    rng = np.random.default_rng(76)
+    worst = 0.0
+    for b, h in [(0, 0), (B - 1, 15), (int(rng.integers(B)), int(rng.integers(16)))]:
+        rows = np.unique(np.concatenate([np.arange(40), np.arange(T - 300, T),
+                                         rng.choice(T, 64, replace=False)]))
+        ref, dref = O.closed_form_rows(_np(q[b, :, h]), _np(k[b, :, h]), _np(v[b, :, h]), rows,
+                                       groups=g)
+        worst = max(worst, float(np.abs(o[b, rows, h].double().numpy() - ref).max()))
+        np.testing.assert_allclose(d[b, rows, h].double().numpy(), dref, rtol=1e-2)
+    say(f"quadratic two blocks per wave {case} T={T}: max-abs {worst:.3e}")
+    assert worst <= TOL[w.dtype]
+
+
 def test_state_pass_skips_only_the_last_segment():
     # several segments per sequence: every segment but the last feeds a prefix; outputs of
     # every segment must still be right (the skipped state is the last one's)
