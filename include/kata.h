@@ -68,14 +68,17 @@ typedef enum { KATA_STATE_DIRECT = 0, KATA_STATE_PACKED = 1 } kata_state_layout;
  *          the state through every chunk in order; no scan).  The fp32 kernels always scan
  *          every chunk state.
  *   state_layout: chunked form only, a kata_state_layout.  PACKED is implemented by the bf16
- *          p = 16, dv = 64, chunk = 64 kernels; the bf16 p = 32 ones always pack; every other
- *          problem computes the direct form whatever this field says.
+ *          p = 16, dv = 64, chunk = 64 kernels; the bf16 p = 32 ones and the bf16 p = 16
+ *          KATA-Mg ones always pack; every other problem computes the direct form whatever
+ *          this field says.
  *   groups: KATA-Mg factor count g (0 or 1: the single PSD factor above).  The p coordinates
  *          form g groups of p/g consecutive entries and the score becomes
  *          a_ts = sum_j (q_t^(j) . k_s^(j))^2, with the same single denominator (gist.science
  *          section 2.3, the variants bullet; ai.info Main Findings, state-size bullet; the KATA
- *          README's concat-SPD call with num_groups).  g must divide p.  g > 1 runs the fp32
- *          kernels; their chunk states keep p^2 rows, the pairs across groups being zero.
+ *          README's concat-SPD call with num_groups).  g must divide p.  The bf16 MFMA
+ *          kernels take g = 2 and 4 at p = 16 (dv = 64; chunk = 64 for the chunked form) and
+ *          keep only the within-group feature pairs; every other grouped problem runs the fp32
+ *          kernels, whose chunk states keep p^2 rows, the pairs across groups being zero.
  *   eps: finite, >= 0 (1e-6 in every workload).
  *   in_dtype: dtype of q, k, v (and dO); out_dtype: dtype of o.  Allowed pairs:
  *          (BF16 -> F32), (BF16 -> BF16), (F32 -> F32).  Gradients are always F32.
@@ -182,8 +185,8 @@ size_t kata_recurrent_state_workspace_size(const kata_problem* pr);
 
 /* Prefill: state <- (S, Z) after the problem's T tokens, from k and v (q is not read).  The
  * problem is checked as for kata_fwd_chunked (T % chunk == 0; state_layout is ignored); the
- * bf16 p = 16, dv = 64, chunk = 64 problem uses the MFMA state kernel (phi(k) rounded to bf16
- * before the products with v, fp32 accumulation), every other one fp32 arithmetic.  The state
+ * bf16 p = 16, dv = 64, chunk = 64, g = 1 problem uses the MFMA state kernel (phi(k) rounded to
+ * bf16 before the products with v, fp32 accumulation), every other one fp32 arithmetic.  The state
  * is overwritten.  Errors: as kata_fwd_chunked. */
 kata_status kata_recurrent_state(const kata_problem* pr, const void* k, const void* v,
                                  float* state, void* workspace, size_t ws_bytes, void* stream);
