@@ -84,48 +84,16 @@ template <typename Tin, int P, int DV>
 __global__ __launch_bounds__(kThreads) void chunk_state_generic_kernel(
     DevProblem pr, const Tin* __restrict__ k, const Tin* __restrict__ v,
     float* __restrict__ states, int n_chunks) {
-  constexpr int PP = P * P;
-  constexpr int E = PP * (DV + 1);
-  __shared__ float ks[kRows][P];
-  __shared__ float vs[kRows][DV + 1];
+  // A (p^2 x C) . (C x (dv + 1)) product with phi(k_s) formed on the fly.  Work item (fq, dq):
+  // the four features (i, 4 jq .. 4 jq + 3), fq = i p / 4 + jq, times the value columns
+  // [16 dq, 16 dq + 16); items with dq == 0 also carry the Z column.  Per key: 6 LDS reads
+  // (broadcasts within a wave) for 4 products and 68 FMAs.
+  constexpr int PP = P * P, E = PP * (DV + 1), NFQ = PP / 4, NDQ = DV / 16;
+  static_assert(DV % 16 == 0 && P % 4 == 0, "state tiling");
+  __shared__ __align__(16) float ks[kRows][P];
+  __shared__ __align__(16) float vs[kRows][DV];
   const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
   const int C = pr.C, tb = c * C;
-  for (int e = threadIdx.x; e < C * P; e += kThreads) {
-    int s = e / P, i = e % P;
-    ks[s][i] = to_f32(k[row_off(pr.sk, b, tb + s, h) + i]);
-  }
-  for (int e = threadIdx.x; e < C * (DV + 1); e += kThreads) {
-    int s = e / (DV + 1), d = e % (DV + 1);
-    vs[s][d] = d < DV ? to_f32(v[row_off(pr.sv, b, tb + s, h) + d]) : 1.f;
-  }
-  __syncthreads();
-  float* out = states + ((long long)(b * pr.H + h) * n_chunks + c) * E;
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    const int d = e / PP, f = e % PP, i = f / P, j = f % P;
-    float acc = 0.f;
-    if (same_group(i, j, pr.gs))               // other feature pairs are zero rows
-      for (int s = 0; s < C; ++s) acc = fmaf(ks[s][i] * ks[s][j], vs[s][d], acc);
-    out[e] = acc;
-  }
-}
-
-// ------------------------------------------------------------------------------------
-// Chunk readout, one chunk per workgroup, from the exclusive prefix state S_{<c}, Z_{<c}.
-// Grid (n_chunks, H, B); thread (row = token in chunk, part = dv/4 columns).
-// ------------------------------------------------------------------------------------
-template <typename Tin, typename Tout, int P, int DV>
-__global__ __launch_bounds__(kThreads) void chunk_output_generic_kernel(
-    DevProblem pr, const Tin* __restrict__ q, const Tin* __restrict__ k,
-    const Tin* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den,
-    const float* __restrict__ states, int n_chunks) {
-  constexpr int PP = P * P;
-  constexpr int E = PP * (DV + 1);
-  constexpr int DP = DV / 4;
-  __shared__ float ks[kRows][P];
-  __shared__ float vs[kRows][DV];
-  const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
-  const int C = pr.C, tb = c * C;
-  const int row = threadIdx.x % kRows, part = threadIdx.x / kRows;
   for (int e = threadIdx.x; e < C * P; e += kThreads) {
     int s = e / P, i = e % P;
     ks[s][i] = to_f32(k[row_off(pr.sk, b, tb + s, h) + i]);
@@ -135,12 +103,97 @@ __global__ __launch_bounds__(kThreads) void chunk_output_generic_kernel(
     vs[s][d] = to_f32(v[row_off(pr.sv, b, tb + s, h) + d]);
   }
   __syncthreads();
-  if (row >= C) return;
+  float* out = states + ((long long)(b * pr.H + h) * n_chunks + c) * E;
+  for (int item = threadIdx.x; item < NFQ * NDQ; item += kThreads) {
+    const int fq = item % NFQ, dq = item / NFQ;
+    const int i = fq / (P / 4), j0 = 4 * (fq % (P / 4)), f0 = i * P + j0;
+    bool in[4];                                  // feature pairs across groups are zero rows
+#pragma unroll
+    for (int x = 0; x < 4; ++x) in[x] = same_group(i, j0 + x, pr.gs);
+    float acc[4][16], zacc[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      zacc[x] = 0.f;
+#pragma unroll
+      for (int y = 0; y < 16; ++y) acc[x][y] = 0.f;
+    }
+    for (int s = 0; s < C; ++s) {
+      const float ki = ks[s][i];
+      const float4 kj = *reinterpret_cast<const float4*>(&ks[s][j0]);
+      const float kjs[4] = {kj.x, kj.y, kj.z, kj.w};
+      float phi[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) phi[x] = in[x] ? ki * kjs[x] : 0.f;   // select
+      float vv[16];
+#pragma unroll
+      for (int y4 = 0; y4 < 4; ++y4) {
+        const float4 u = *reinterpret_cast<const float4*>(&vs[s][16 * dq + 4 * y4]);
+        vv[4 * y4] = u.x; vv[4 * y4 + 1] = u.y; vv[4 * y4 + 2] = u.z; vv[4 * y4 + 3] = u.w;
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        zacc[x] += phi[x];
+#pragma unroll
+        for (int y = 0; y < 16; ++y) acc[x][y] = fmaf(phi[x], vv[y], acc[x][y]);
+      }
+    }
+    // rows across groups are exact zeros (selection: a non-finite value never reaches them)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      zacc[x] = in[x] ? zacc[x] : 0.f;
+#pragma unroll
+      for (int y = 0; y < 16; ++y) acc[x][y] = in[x] ? acc[x][y] : 0.f;
+    }
+#pragma unroll
+    for (int y = 0; y < 16; ++y)
+      *reinterpret_cast<float4*>(out + (long long)(16 * dq + y) * PP + f0) =
+          float4{acc[0][y], acc[1][y], acc[2][y], acc[3][y]};
+    if (dq == 0)
+      *reinterpret_cast<float4*>(out + (long long)DV * PP + f0) =
+          float4{zacc[0], zacc[1], zacc[2], zacc[3]};
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Chunk readout, one chunk per workgroup, from the exclusive prefix state S_{<c}, Z_{<c}.
+// Grid (n_chunks, H, B); thread (row = token in chunk, part = dv/4 columns).  The state is
+// staged in LDS, FB features at a time, as [feature][column] rows (Z in column dv), so every
+// read of a wave is one broadcast; q_t's factor i comes from LDS, its factor j from registers
+// (the j loop is unrolled).
+// ------------------------------------------------------------------------------------
+template <typename Tin, typename Tout, int P, int DV>
+__global__ __launch_bounds__(kThreads) void chunk_output_generic_kernel(
+    DevProblem pr, const Tin* __restrict__ q, const Tin* __restrict__ k,
+    const Tin* __restrict__ v, Tout* __restrict__ o, float* __restrict__ den,
+    const float* __restrict__ states, int n_chunks) {
+  constexpr int PP = P * P;
+  constexpr int E = PP * (DV + 1);
+  constexpr int DP = DV / 4;
+  constexpr int FB = 64;                         // features per staged block (FB / P rows i)
+  constexpr int SROW = DV + 4;                   // floats per staged feature row (Z at DV)
+  static_assert(FB % P == 0 && PP % FB == 0 && DP % 4 == 0, "readout tiling");
+  __shared__ __align__(16) float ks[kRows][P];
+  __shared__ __align__(16) float vs[kRows][DV];
+  __shared__ float qs[kRows][P + 1];
+  __shared__ __align__(16) float sl[FB][SROW];
+  const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
+  const int C = pr.C, tb = c * C;
+  const int row = threadIdx.x % kRows, part = threadIdx.x / kRows;
+  const bool live = row < C;
+  for (int e = threadIdx.x; e < C * P; e += kThreads) {
+    int s = e / P, i = e % P;
+    ks[s][i] = to_f32(k[row_off(pr.sk, b, tb + s, h) + i]);
+    qs[s][i] = to_f32(q[row_off(pr.sq, b, tb + s, h) + i]);
+  }
+  for (int e = threadIdx.x; e < C * DV; e += kThreads) {
+    int s = e / DV, d = e % DV;
+    vs[s][d] = to_f32(v[row_off(pr.sv, b, tb + s, h) + d]);
+  }
+  __syncthreads();
   const int t = tb + row;
   float qr[P];
-  const Tin* qp = q + row_off(pr.sq, b, t, h);
 #pragma unroll
-  for (int i = 0; i < P; ++i) qr[i] = to_f32(qp[i]);
+  for (int i = 0; i < P; ++i) qr[i] = live ? qs[row][i] : 0.f;
 
   // inter-chunk: phi(q)^T S_{<c} and q^T Z_{<c} q, phi_f = q_i q_j
   const float* S = states + ((long long)(b * pr.H + h) * n_chunks + c) * E;
@@ -148,15 +201,32 @@ __global__ __launch_bounds__(kThreads) void chunk_output_generic_kernel(
 #pragma unroll
   for (int j = 0; j < DP; ++j) acc[j] = 0.f;
   float zq = 0.f;
-  for (int i = 0; i < P; ++i) {
-    for (int jj = 0; jj < P; ++jj) {
-      const float phi = qr[i] * qr[jj];
-      const int f = i * P + jj;
+  for (int f0 = 0; f0 < PP; f0 += FB) {
+    __syncthreads();                             // the previous block has been read
+    for (int e = threadIdx.x; e < (DV + 1) * FB; e += kThreads) {
+      const int d = e / FB, f = e % FB;          // coalesced over features
+      sl[f][d] = S[(long long)d * PP + f0 + f];
+    }
+    __syncthreads();
+    for (int ib = 0; ib < FB / P; ++ib) {
+      const float qi = live ? qs[row][f0 / P + ib] : 0.f;
 #pragma unroll
-      for (int j = 0; j < DP; ++j) acc[j] = fmaf(phi, S[(part * DP + j) * PP + f], acc[j]);
-      zq = fmaf(phi, S[DV * PP + f], zq);
+      for (int jj = 0; jj < P; ++jj) {
+        const float phi = qi * qr[jj];
+        const float* srow = sl[ib * P + jj];
+#pragma unroll
+        for (int j4 = 0; j4 < DP / 4; ++j4) {
+          const float4 u = *reinterpret_cast<const float4*>(srow + part * DP + 4 * j4);
+          acc[4 * j4] = fmaf(phi, u.x, acc[4 * j4]);
+          acc[4 * j4 + 1] = fmaf(phi, u.y, acc[4 * j4 + 1]);
+          acc[4 * j4 + 2] = fmaf(phi, u.z, acc[4 * j4 + 2]);
+          acc[4 * j4 + 3] = fmaf(phi, u.w, acc[4 * j4 + 3]);
+        }
+        zq = fmaf(phi, srow[DV], zq);
+      }
     }
   }
+  if (!live) return;                             // no barrier follows
   // intra-chunk: causal tile, diagonal included
   float l = 0.f;
   const Groups grp = make_groups(P, pr.gs);
