@@ -20,6 +20,7 @@
 // m owns the value columns [m dv/4, (m+1) dv/4) of every contraction over dv, and the partial
 // p-vectors of the four parts are summed through LDS at the end.
 #include "device.h"
+#include "phi_product.h"
 
 namespace kata {
 namespace {
@@ -68,24 +69,30 @@ __device__ __forceinline__ void reduce_parts(float (&acc)[P], float (*red)[kRows
   }
 }
 
-// dq.  states: the forward's exclusive prefix (S_{<c}, Z_{<c}) per chunk, layout [dv+1][p^2].
+// dq.  states: the forward's exclusive prefix (S_{<c}, Z_{<c}) per chunk, layout [dv+1][p^2],
+// staged in LDS FB features at a time (the region is then reused for the parts' reduction).
 template <typename Tin, int P, int DV>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_dq_kernel(
     DevProblem pr, const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const float* __restrict__ g, const float* __restrict__ e,
     const float* __restrict__ states, int n_chunks, float* __restrict__ dq) {
   constexpr int PP = P * P, E = PP * (DV + 1), DP = DV / kParts;
-  __shared__ float ks[kRows][P];
+  constexpr int FB = 32, SROW = DV + 4;
+  constexpr int RED = (kParts - 1) * kRows * (P + 1), POOL = RED > FB * SROW ? RED : FB * SROW;
+  static_assert(FB % P == 0, "feature blocks hold whole rows i");
+  __shared__ __align__(16) float ks[kRows][P];
   __shared__ float vs[kRows][DV];
-  __shared__ float red[kParts - 1][kRows][P + 1];
+  __shared__ __align__(16) float pool[POOL];
+  float (*sl)[SROW] = reinterpret_cast<float (*)[SROW]>(pool);
+  float (*red)[kRows][P + 1] = reinterpret_cast<float (*)[kRows][P + 1]>(pool);
   const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
   const int C = pr.C, tb = c * C;
-  const int row = threadIdx.x % kRows, part = threadIdx.x / kRows;
+  const int row = threadIdx.x % kRows;
+  const int part = __builtin_amdgcn_readfirstlane(threadIdx.x / kRows);   // one per wave
   for (int x = threadIdx.x; x < C * P; x += kThreads)
     ks[x / P][x % P] = to_f32(k[row_off(pr.sk, b, tb + x / P, h) + x % P]);
   for (int x = threadIdx.x; x < C * DV; x += kThreads)
     vs[x / DV][x % DV] = to_f32(v[row_off(pr.sv, b, tb + x / DV, h) + x % DV]);
-  __syncthreads();
   const bool live = row < C;
   const int t = tb + (live ? row : 0);
   float qr[P], gr[DP], acc[P];
@@ -99,20 +106,37 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_dq_kernel(
 #pragma unroll
   for (int j = 0; j < DP; ++j) gr[j] = g[tok * DV + part * DP + j];
   const float et = e[tok];
-  if (live) {
-    // earlier chunks: u_i = sum_j q_j (sum_{d in part} S[(i,j)][d] g_d) - [part 0] e Z[i][j] q_j
-    const float* S = states + ((long long)(b * pr.H + h) * n_chunks + c) * E;
-    for (int i = 0; i < P; ++i) {
+  const float zf = part ? 0.f : -et;             // weight of the Z row: part 0 only
+  // earlier chunks: u_i = sum_j q_j (sum_{d in part} S[(i,j)][d] g_d) - [part 0] e Z[i][j] q_j
+  const float* S = states + ((long long)(b * pr.H + h) * n_chunks + c) * E;
+  for (int f0 = 0; f0 < PP; f0 += FB) {
+    __syncthreads();                             // staging done / the previous block read
+    stage_state_block<PP, DV, FB, SROW>(S, f0, sl);
+    __syncthreads();
+#pragma unroll 1
+    for (int jb = 0; jb < FB; jb += P) {
+      const int i = (f0 + jb) / P;
       float u = 0.f;
-      for (int jj = 0; jj < P; ++jj) {
-        const int f = i * P + jj;
-        float m = part ? 0.f : -et * S[DV * PP + f];
 #pragma unroll
-        for (int j = 0; j < DP; ++j) m = fmaf(S[(part * DP + j) * PP + f], gr[j], m);
+      for (int jj = 0; jj < P; ++jj) {
+        const float* srow = sl[jb + jj];
+        float m = zf * srow[DV];                 // branch-free: no wait on the loads
+#pragma unroll
+        for (int j4 = 0; j4 < DP / 4; ++j4) {
+          const float4 u4 = *reinterpret_cast<const float4*>(srow + part * DP + 4 * j4);
+          m = fmaf(u4.x, gr[4 * j4], m);
+          m = fmaf(u4.y, gr[4 * j4 + 1], m);
+          m = fmaf(u4.z, gr[4 * j4 + 2], m);
+          m = fmaf(u4.w, gr[4 * j4 + 3], m);
+        }
         u = fmaf(m, qr[jj], u);
       }
-      acc[i] = u;
+      // row i of this block (i is not a compile-time index: a select per register)
+#pragma unroll
+      for (int ii = 0; ii < P; ++ii) acc[ii] = ii == i ? u : acc[ii];
     }
+  }
+  if (live) {
     // this chunk: sum_{s<=t} (q . k_s) G_ts k_s, G_ts split over the parts' value columns
     const Groups grp = make_groups(P, pr.gs);
     for (int s = 0; s <= row; ++s) {
@@ -125,6 +149,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_dq_kernel(
       for (int i = 0; i < P; ++i) acc[i] = fmaf(sc[i] * G, ks[s][i], acc[i]);
     }
   }
+  __syncthreads();                               // every read of the staged state is done
   reduce_parts<P>(acc, red, row, part);
   if (live && !part) {
     float* out = dq + row_off(pr.sq, b, t, h);
@@ -134,36 +159,33 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_dq_kernel(
 }
 
 // Per-chunk reverse states dR_c[d][f] = sum_{t in c} q_i q_j g_d (d < dv) and
-// dr_c[f] = sum e_t q_i q_j (row dv), written at position n_chunks - 1 - c.
+// dr_c[f] = sum e_t q_i q_j (row dv), written at position n_chunks - 1 - c (phi_product).
 template <typename Tin, int P, int DV>
 __global__ __launch_bounds__(kThreads) void bwd_rev_state_kernel(
     DevProblem pr, const Tin* __restrict__ q, const float* __restrict__ g,
     const float* __restrict__ e, float* __restrict__ states, int n_chunks) {
   constexpr int PP = P * P, E = PP * (DV + 1);
-  __shared__ float qs[kRows][P];
-  __shared__ float gs[kRows][DV + 1];
+  __shared__ __align__(16) float qs[kRows][P];
+  __shared__ __align__(16) float gs[kRows][DV];
+  __shared__ float es[kRows];
   const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
   const int C = pr.C, tb = c * C;
   for (int x = threadIdx.x; x < C * P; x += kThreads)
     qs[x / P][x % P] = to_f32(q[row_off(pr.sq, b, tb + x / P, h) + x % P]);
-  for (int x = threadIdx.x; x < C * (DV + 1); x += kThreads) {
-    const int s = x / (DV + 1), d = x % (DV + 1);
-    const long long tok = ((long long)b * pr.T + tb + s) * pr.H + h;
-    gs[s][d] = d < DV ? g[tok * DV + d] : e[tok];
+  for (int x = threadIdx.x; x < C * DV; x += kThreads) {
+    const long long tok = ((long long)b * pr.T + tb + x / DV) * pr.H + h;
+    gs[x / DV][x % DV] = g[tok * DV + x % DV];
   }
+  for (int x = threadIdx.x; x < C; x += kThreads)
+    es[x] = e[((long long)b * pr.T + tb + x) * pr.H + h];
   __syncthreads();
-  float* out = states + ((long long)(b * pr.H + h) * n_chunks + (n_chunks - 1 - c)) * E;
-  for (int x = threadIdx.x; x < E; x += kThreads) {
-    const int d = x / PP, f = x % PP, i = f / P, jj = f % P;
-    float acc = 0.f;
-    if (same_group(i, jj, pr.gs))
-      for (int s = 0; s < C; ++s) acc = fmaf(qs[s][i] * qs[s][jj], gs[s][d], acc);
-    out[x] = acc;
-  }
+  phi_product<P, DV, false>(qs, gs, es, C, pr.gs,
+                            states + ((long long)(b * pr.H + h) * n_chunks + (n_chunks - 1 - c)) * E);
 }
 
 // dk, dv.  states: R_{>c} at position n_chunks - 1 - c (the exclusive scan of the reversed
-// chunk states).
+// chunk states), staged in LDS FB features at a time (the region is then reused for the
+// parts' reduction).
 template <typename Tin, int P, int DV>
 __global__ __launch_bounds__(kThreads) void bwd_chunk_dkdv_kernel(
     DevProblem pr, const Tin* __restrict__ q, const Tin* __restrict__ k,
@@ -171,21 +193,29 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_dkdv_kernel(
     const float* __restrict__ states, int n_chunks, float* __restrict__ dk,
     float* __restrict__ dv) {
   constexpr int PP = P * P, E = PP * (DV + 1), DP = DV / kParts;
+  constexpr int FB = 32, SROW = DV + 4;
+  constexpr int RED = (kParts - 1) * kRows * (P + 1), POOL = RED > FB * SROW ? RED : FB * SROW;
+  static_assert(FB % P == 0, "feature blocks hold whole rows i");
   __shared__ float qs[kRows][P];
+  __shared__ float ks[kRows][P + 1];              // this chunk's k rows (factor i of phi)
   __shared__ float gs[kRows][DV];
   __shared__ float es[kRows];
-  __shared__ float red[kParts - 1][kRows][P + 1];
+  __shared__ __align__(16) float pool[POOL];
+  float (*rl)[SROW] = reinterpret_cast<float (*)[SROW]>(pool);
+  float (*red)[kRows][P + 1] = reinterpret_cast<float (*)[kRows][P + 1]>(pool);
   const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
   const int C = pr.C, tb = c * C;
-  const int row = threadIdx.x % kRows, part = threadIdx.x / kRows;
-  for (int x = threadIdx.x; x < C * P; x += kThreads)
+  const int row = threadIdx.x % kRows;
+  const int part = __builtin_amdgcn_readfirstlane(threadIdx.x / kRows);   // one per wave
+  for (int x = threadIdx.x; x < C * P; x += kThreads) {
     qs[x / P][x % P] = to_f32(q[row_off(pr.sq, b, tb + x / P, h) + x % P]);
+    ks[x / P][x % P] = to_f32(k[row_off(pr.sk, b, tb + x / P, h) + x % P]);
+  }
   for (int x = threadIdx.x; x < C * DV; x += kThreads) {
     const long long tok = ((long long)b * pr.T + tb + x / DV) * pr.H + h;
     gs[x / DV][x % DV] = g[tok * DV + x % DV];
   }
   for (int x = threadIdx.x; x < C; x += kThreads) es[x] = e[((long long)b * pr.T + tb + x) * pr.H + h];
-  __syncthreads();
   const bool live = row < C;
   const int s = tb + (live ? row : 0);
   float kr[P], vr[DP], acc[P], dvacc[DP];
@@ -201,26 +231,42 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_dkdv_kernel(
     vr[j] = to_f32(vp[j]);
     dvacc[j] = 0.f;
   }
-  if (live) {
-    // later chunks: w_i = sum_j k_j (sum_{d in part} R[(i,j)][d] v_d) - [part 0] r[(i,j)] k_j
-    //               dv_d = sum_f R[f][d] k_i k_j   (d in part)
-    const float* R = states + ((long long)(b * pr.H + h) * n_chunks + (n_chunks - 1 - c)) * E;
-    for (int i = 0; i < P; ++i) {
+  // later chunks: w_i = sum_j k_j (sum_{d in part} R[(i,j)][d] v_d) - [part 0] r[(i,j)] k_j
+  //               dv_d = sum_f R[f][d] k_i k_j   (d in part)
+  const float* R = states + ((long long)(b * pr.H + h) * n_chunks + (n_chunks - 1 - c)) * E;
+  const int srow_l = live ? row : 0;
+  const float rf = part ? 0.f : -1.f;            // weight of the r row: part 0 only
+  for (int f0 = 0; f0 < PP; f0 += FB) {
+    __syncthreads();                             // staging done / the previous block read
+    stage_state_block<PP, DV, FB, SROW>(R, f0, rl);
+    __syncthreads();
+#pragma unroll 1
+    for (int jb = 0; jb < FB; jb += P) {
+      const int i = (f0 + jb) / P;
+      const float ki = ks[srow_l][i];
       float w = 0.f;
-      for (int jj = 0; jj < P; ++jj) {
-        const int f = i * P + jj;
-        const float phi = kr[i] * kr[jj];
-        float m = part ? 0.f : -R[DV * PP + f];
 #pragma unroll
-        for (int j = 0; j < DP; ++j) {
-          const float r = R[(part * DP + j) * PP + f];
-          m = fmaf(r, vr[j], m);
-          dvacc[j] = fmaf(r, phi, dvacc[j]);
+      for (int jj = 0; jj < P; ++jj) {
+        const float* rrow = rl[jb + jj];
+        const float phi = ki * kr[jj];
+        float m = rf * rrow[DV];                 // branch-free: no wait on the loads
+#pragma unroll
+        for (int j4 = 0; j4 < DP / 4; ++j4) {
+          const float4 r4 = *reinterpret_cast<const float4*>(rrow + part * DP + 4 * j4);
+          const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+          for (int y = 0; y < 4; ++y) {
+            m = fmaf(rr[y], vr[4 * j4 + y], m);
+            dvacc[4 * j4 + y] = fmaf(rr[y], phi, dvacc[4 * j4 + y]);
+          }
         }
         w = fmaf(m, kr[jj], w);
       }
-      acc[i] = w;
+#pragma unroll
+      for (int ii = 0; ii < P; ++ii) acc[ii] = ii == i ? w : acc[ii];
     }
+  }
+  if (live) {
     // this chunk: t >= s
     const Groups grp = make_groups(P, pr.gs);
     for (int tt = row; tt < C; ++tt) {
@@ -239,6 +285,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_dkdv_kernel(
 #pragma unroll
     for (int j = 0; j < DP; ++j) dvp[j] = dvacc[j];
   }
+  __syncthreads();                               // every read of the staged state is done
   reduce_parts<P>(acc, red, row, part);
   if (live && !part) {
     float* out = dk + row_off(pr.sk, b, s, h);

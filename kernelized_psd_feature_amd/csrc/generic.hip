@@ -7,6 +7,7 @@
 // inner product), o_t = sum a_ts v_s / (eps + sum a_ts) (section 2.1; ai.info Main Findings,
 // readout-gate bullet).  Chunked form: gist.science section 2.3.
 #include "device.h"
+#include "phi_product.h"
 
 namespace kata {
 namespace {
@@ -84,12 +85,7 @@ template <typename Tin, int P, int DV>
 __global__ __launch_bounds__(kThreads) void chunk_state_generic_kernel(
     DevProblem pr, const Tin* __restrict__ k, const Tin* __restrict__ v,
     float* __restrict__ states, int n_chunks) {
-  // A (p^2 x C) . (C x (dv + 1)) product with phi(k_s) formed on the fly.  Work item (fq, dq):
-  // the four features (i, 4 jq .. 4 jq + 3), fq = i p / 4 + jq, times the value columns
-  // [16 dq, 16 dq + 16); items with dq == 0 also carry the Z column.  Per key: 6 LDS reads
-  // (broadcasts within a wave) for 4 products and 68 FMAs.
-  constexpr int PP = P * P, E = PP * (DV + 1), NFQ = PP / 4, NDQ = DV / 16;
-  static_assert(DV % 16 == 0 && P % 4 == 0, "state tiling");
+  // A (p^2 x C) . (C x (dv + 1)) product with phi(k_s) formed on the fly (phi_product).
   __shared__ __align__(16) float ks[kRows][P];
   __shared__ __align__(16) float vs[kRows][DV];
   const int b = blockIdx.z, h = blockIdx.y, c = blockIdx.x;
@@ -103,55 +99,9 @@ __global__ __launch_bounds__(kThreads) void chunk_state_generic_kernel(
     vs[s][d] = to_f32(v[row_off(pr.sv, b, tb + s, h) + d]);
   }
   __syncthreads();
-  float* out = states + ((long long)(b * pr.H + h) * n_chunks + c) * E;
-  for (int item = threadIdx.x; item < NFQ * NDQ; item += kThreads) {
-    const int fq = item % NFQ, dq = item / NFQ;
-    const int i = fq / (P / 4), j0 = 4 * (fq % (P / 4)), f0 = i * P + j0;
-    bool in[4];                                  // feature pairs across groups are zero rows
-#pragma unroll
-    for (int x = 0; x < 4; ++x) in[x] = same_group(i, j0 + x, pr.gs);
-    float acc[4][16], zacc[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      zacc[x] = 0.f;
-#pragma unroll
-      for (int y = 0; y < 16; ++y) acc[x][y] = 0.f;
-    }
-    for (int s = 0; s < C; ++s) {
-      const float ki = ks[s][i];
-      const float4 kj = *reinterpret_cast<const float4*>(&ks[s][j0]);
-      const float kjs[4] = {kj.x, kj.y, kj.z, kj.w};
-      float phi[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) phi[x] = in[x] ? ki * kjs[x] : 0.f;   // select
-      float vv[16];
-#pragma unroll
-      for (int y4 = 0; y4 < 4; ++y4) {
-        const float4 u = *reinterpret_cast<const float4*>(&vs[s][16 * dq + 4 * y4]);
-        vv[4 * y4] = u.x; vv[4 * y4 + 1] = u.y; vv[4 * y4 + 2] = u.z; vv[4 * y4 + 3] = u.w;
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        zacc[x] += phi[x];
-#pragma unroll
-        for (int y = 0; y < 16; ++y) acc[x][y] = fmaf(phi[x], vv[y], acc[x][y]);
-      }
-    }
-    // rows across groups are exact zeros (selection: a non-finite value never reaches them)
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      zacc[x] = in[x] ? zacc[x] : 0.f;
-#pragma unroll
-      for (int y = 0; y < 16; ++y) acc[x][y] = in[x] ? acc[x][y] : 0.f;
-    }
-#pragma unroll
-    for (int y = 0; y < 16; ++y)
-      *reinterpret_cast<float4*>(out + (long long)(16 * dq + y) * PP + f0) =
-          float4{acc[0][y], acc[1][y], acc[2][y], acc[3][y]};
-    if (dq == 0)
-      *reinterpret_cast<float4*>(out + (long long)DV * PP + f0) =
-          float4{zacc[0], zacc[1], zacc[2], zacc[3]};
-  }
+  constexpr int E = P * P * (DV + 1);
+  phi_product<P, DV, true>(ks, vs, nullptr, C, pr.gs,
+                           states + ((long long)(b * pr.H + h) * n_chunks + c) * E);
 }
 
 // ------------------------------------------------------------------------------------
@@ -203,10 +153,7 @@ __global__ __launch_bounds__(kThreads) void chunk_output_generic_kernel(
   float zq = 0.f;
   for (int f0 = 0; f0 < PP; f0 += FB) {
     __syncthreads();                             // the previous block has been read
-    for (int e = threadIdx.x; e < (DV + 1) * FB; e += kThreads) {
-      const int d = e / FB, f = e % FB;          // coalesced over features
-      sl[f][d] = S[(long long)d * PP + f0 + f];
-    }
+    stage_state_block<PP, DV, FB, SROW>(S, f0, sl);
     __syncthreads();
     for (int ib = 0; ib < FB / P; ++ib) {
       const float qi = live ? qs[row][f0 / P + ib] : 0.f;
