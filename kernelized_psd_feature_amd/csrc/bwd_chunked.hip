@@ -109,10 +109,13 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_dq_kernel(
   const float zf = part ? 0.f : -et;             // weight of the Z row: part 0 only
   // earlier chunks: u_i = sum_j q_j (sum_{d in part} S[(i,j)][d] g_d) - [part 0] e Z[i][j] q_j
   const float* S = states + ((long long)(b * pr.H + h) * n_chunks + c) * E;
+  StateBlock<PP, DV, FB, SROW, kThreads> nb;
+  nb.load(S, 0);
   for (int f0 = 0; f0 < PP; f0 += FB) {
     __syncthreads();                             // staging done / the previous block read
-    stage_state_block<PP, DV, FB, SROW>(S, f0, sl);
+    nb.store(sl);
     __syncthreads();
+    if (f0 + FB < PP) nb.load(S, f0 + FB);   // in flight while this block is computed
 #pragma unroll 1
     for (int jb = 0; jb < FB; jb += P) {
       const int i = (f0 + jb) / P;
@@ -236,10 +239,13 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_dkdv_kernel(
   const float* R = states + ((long long)(b * pr.H + h) * n_chunks + (n_chunks - 1 - c)) * E;
   const int srow_l = live ? row : 0;
   const float rf = part ? 0.f : -1.f;            // weight of the r row: part 0 only
+  StateBlock<PP, DV, FB, SROW, kThreads> nb;
+  nb.load(R, 0);
   for (int f0 = 0; f0 < PP; f0 += FB) {
     __syncthreads();                             // staging done / the previous block read
-    stage_state_block<PP, DV, FB, SROW>(R, f0, rl);
+    nb.store(rl);
     __syncthreads();
+    if (f0 + FB < PP) nb.load(R, f0 + FB);   // in flight while this block is computed
 #pragma unroll 1
     for (int jb = 0; jb < FB; jb += P) {
       const int i = (f0 + jb) / P;

@@ -151,10 +151,13 @@ __global__ __launch_bounds__(kThreads) void chunk_output_generic_kernel(
 #pragma unroll
   for (int j = 0; j < DP; ++j) acc[j] = 0.f;
   float zq = 0.f;
+  StateBlock<PP, DV, FB, SROW, kThreads> nb;
+  nb.load(S, 0);
   for (int f0 = 0; f0 < PP; f0 += FB) {
     __syncthreads();                             // the previous block has been read
-    stage_state_block<PP, DV, FB, SROW>(S, f0, sl);
+    nb.store(sl);
     __syncthreads();
+    if (f0 + FB < PP) nb.load(S, f0 + FB);       // in flight while this block is computed
     for (int ib = 0; ib < FB / P; ++ib) {
       const float qi = live ? qs[row][f0 / P + ib] : 0.f;
 #pragma unroll

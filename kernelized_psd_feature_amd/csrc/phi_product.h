@@ -72,16 +72,28 @@ __device__ __forceinline__ void phi_product(const float (*xs)[P], const float (*
   }
 }
 
-// Stages features [f0, f0 + FB) of a state stored [dv + 1][p^2] (d-major) into LDS as
-// [feature][SROW] rows, column dv holding the last state row (Z or r).  Global reads are
-// coalesced over features.
-template <int PP, int DV, int FB, int SROW>
-__device__ __forceinline__ void stage_state_block(const float* __restrict__ S, int f0,
-                                                  float (*sl)[SROW]) {
-  for (int e = threadIdx.x; e < (DV + 1) * FB; e += blockDim.x) {
-    const int d = e / FB, f = e % FB;
-    sl[f][d] = S[(long long)d * PP + f0 + f];
+// Features [f0, f0 + FB) of a state stored [dv + 1][p^2] (d-major), staged into LDS as
+// [feature][SROW] rows, column dv holding the last state row (Z or r), through registers:
+// load() issues the global reads (coalesced over features) and store() writes LDS, so the
+// next block's reads can be in flight while the current block is computed.  NT threads.
+template <int PP, int DV, int FB, int SROW, int NT>
+struct StateBlock {
+  static constexpr int kVals = (DV + 1) * FB, N = (kVals + NT - 1) / NT;
+  float r[N];
+  __device__ __forceinline__ void load(const float* __restrict__ S, int f0) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int e = threadIdx.x + n * NT;
+      if (e < kVals) r[n] = S[(long long)(e / FB) * PP + f0 + e % FB];
+    }
   }
-}
+  __device__ __forceinline__ void store(float (*sl)[SROW]) const {
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int e = threadIdx.x + n * NT;
+      if (e < kVals) sl[e % FB][e / FB] = r[n];
+    }
+  }
+};
 
 }  // namespace kata
