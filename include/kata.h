@@ -129,8 +129,10 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
  * one (b, h) are walked in `segments` segments of `chunks_per_segment` chunks; a state pass
  * and an exclusive prefix scan over the segment states, a combining tree of `scan_levels`
  * levels, feed the walk.  With one segment per (b, h) on the MFMA kernels (the sequential
- * inter-chunk form) neither runs and scan_levels is 0.  Source: gist.science section 2.3
- * (inter-chunk depth O(log N_C)).
+ * inter-chunk form) neither runs and scan_levels is 0.  With 2 to 8 segments on the MFMA
+ * kernels (walk_sums_prefix = 1) no scan runs either (scan_levels 0): the walk of segment s adds
+ * the states of segments 0 .. s-1 in that order, the same exclusive prefix.  Source:
+ * gist.science section 2.3 (inter-chunk depth O(log N_C)).
  *   out: host struct, filled on success.
  * Errors: INVALID_ARGUMENT (NULL out, or as kata_fwd_chunked), UNSUPPORTED. */
 typedef struct {
@@ -141,7 +143,7 @@ typedef struct {
   int32_t scan_levels;
   int32_t mfma;                /* 1: bf16 MFMA kernels; 0: fp32 kernels */
   int32_t packed;              /* 1: states keep only the unique (i <= j) feature pairs */
-  int32_t reserved;
+  int32_t walk_sums_prefix;    /* 1: the walks add the earlier segment states, no scan */
 } kata_chunked_plan;
 kata_status kata_fwd_chunked_plan(const kata_problem* pr, kata_chunked_plan* out);
 

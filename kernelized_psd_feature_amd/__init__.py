@@ -61,7 +61,7 @@ class _ChunkedPlan(ctypes.Structure):
     _fields_ = [("n_chunks", ctypes.c_int64), ("chunks_per_segment", ctypes.c_int64),
                 ("segments", ctypes.c_int64), ("state_floats", ctypes.c_int64),
                 ("scan_levels", ctypes.c_int32), ("mfma", ctypes.c_int32),
-                ("packed", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("packed", ctypes.c_int32), ("walk_sums_prefix", ctypes.c_int32)]
 
 
 class _Times(ctypes.Structure):
@@ -204,8 +204,7 @@ def chunked_plan(q, k, v, chunk=64, seg_chunks=0, out_dtype=torch.float32, state
     out = _ChunkedPlan()
     _check(_lib().kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)),
            "kata_fwd_chunked_plan")
-    return {name: int(getattr(out, name)) for name, _ in _ChunkedPlan._fields_
-            if name != "reserved"}
+    return {name: int(getattr(out, name)) for name, _ in _ChunkedPlan._fields_}
 
 
 def fwd_chunked(q, k, v, chunk=64, eps=1e-6, out_dtype=torch.float32, seg_chunks=0,

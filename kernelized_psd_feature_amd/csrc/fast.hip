@@ -377,7 +377,7 @@ template <typename Tout, bool kPacked, int GW>
 __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     DevProblem pr, SegGrid sg, int L, int n_seg, const __bf16* __restrict__ q,
     const __bf16* __restrict__ k, const __bf16* __restrict__ v, Tout* __restrict__ o,
-    float* __restrict__ den_out, const float* __restrict__ states) {
+    float* __restrict__ den_out, const float* __restrict__ states, int sum_prefix) {
   using LY = Layout<kPacked, GW>;
   __shared__ WalkLds<kPacked, GW> sm;
   TilesT<kPacked>& tl = sm.tl;
@@ -389,21 +389,38 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
   const long long sv_t = pr.sv[1];
 
-  // prefix state of this segment (states == nullptr: one segment per sequence, prefix zero)
-  const float* pre =
-      states ? states + ((long long)(b * pr.H + h) * n_seg + seg) * LY::kStateFloats : nullptr;
+  // Exclusive prefix (S_{<c}, Z_{<c}) of this segment: the scanned state at position seg, or
+  // (sum_prefix) the states of segments 0 .. seg-1 added in that order; zero without states (one
+  // segment per sequence).  Every wave keeps its own copy of Z (4 registers); lane holds
+  // Z[4g + r][lane % 16].
   f32x4 S[LY::kSlots][4];
 #pragma unroll
-  for (int sl = 0; sl < LY::kSlots; ++sl) {
-    const int t = LY::tile(w, sl);
+  for (int sl = 0; sl < LY::kSlots; ++sl)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      S[sl][nt] = (pre && LY::owns(w, sl))
-                      ? *reinterpret_cast<const f32x4*>(pre + ((t * 4 + nt) * 64 + lane) * 4)
-                      : zero4();
+    for (int nt = 0; nt < 4; ++nt) S[sl][nt] = zero4();
+  f32x4 Z = zero4();
+  {
+    auto add_state = [&](int j) {
+      const float* pre = states + ((long long)(b * pr.H + h) * n_seg + j) * LY::kStateFloats;
+#pragma unroll
+      for (int sl = 0; sl < LY::kSlots; ++sl) {
+        if (!LY::owns(w, sl)) continue;
+        const int t = LY::tile(w, sl);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          S[sl][nt] += *reinterpret_cast<const f32x4*>(pre + ((t * 4 + nt) * 64 + lane) * 4);
+      }
+      Z += *reinterpret_cast<const f32x4*>(pre + LY::kZOff + lane * 4);
+    };
+    const int j0 = sum_prefix ? 0 : seg, j1 = !states ? j0 : sum_prefix ? seg : seg + 1;
+    int j = j0;
+    if constexpr (kPacked)                         // two states' loads in flight
+      for (; j + 1 < j1; j += 2) {
+        add_state(j);
+        add_state(j + 1);
+      }
+    for (; j < j1; ++j) add_state(j);
   }
-  // every wave keeps its own copy of Z_{<c} (4 registers); lane holds Z[4g + r][lane % 16]
-  f32x4 Z = pre ? *reinterpret_cast<const f32x4*>(pre + LY::kZOff + lane * 4) : zero4();
   UpdateRows<kPacked, GW> ur;
   ur.init(w, lane);
   zero_pad_rows(tl, tid);
@@ -581,23 +598,23 @@ namespace {
 template <typename Tout, bool kPacked, int GW>
 void walk_launch(const DevProblem& pr, const SegGrid& sg, int L, int n_seg, dim3 grid,
                  hipStream_t st, const __bf16* q, const __bf16* k, const __bf16* v, void* o,
-                 float* den, const float* states) {
+                 float* den, const float* states, int sum_prefix) {
   launch_kernel(chunk_output_fast_kernel<Tout, kPacked, GW>, grid, kThreads, 0, st,
-      pr, sg, L, n_seg, q, k, v, (Tout*)o, den, states);
+      pr, sg, L, n_seg, q, k, v, (Tout*)o, den, states, sum_prefix);
 }
 
 template <typename Tout>
 void walk_dispatch(const DevProblem& pr, const SegGrid& sg, bool packed, int gw, int L, int n_seg,
                    dim3 grid, hipStream_t st, const __bf16* q, const __bf16* k, const __bf16* v,
-                   void* o, float* den, const float* states) {
+                   void* o, float* den, const float* states, int sum_prefix) {
   if (gw == 8)
-    walk_launch<Tout, true, 8>(pr, sg, L, n_seg, grid, st, q, k, v, o, den, states);
+    walk_launch<Tout, true, 8>(pr, sg, L, n_seg, grid, st, q, k, v, o, den, states, sum_prefix);
   else if (gw == 4)
-    walk_launch<Tout, true, 4>(pr, sg, L, n_seg, grid, st, q, k, v, o, den, states);
+    walk_launch<Tout, true, 4>(pr, sg, L, n_seg, grid, st, q, k, v, o, den, states, sum_prefix);
   else if (packed)
-    walk_launch<Tout, true, P>(pr, sg, L, n_seg, grid, st, q, k, v, o, den, states);
+    walk_launch<Tout, true, P>(pr, sg, L, n_seg, grid, st, q, k, v, o, den, states, sum_prefix);
   else
-    walk_launch<Tout, false, P>(pr, sg, L, n_seg, grid, st, q, k, v, o, den, states);
+    walk_launch<Tout, false, P>(pr, sg, L, n_seg, grid, st, q, k, v, o, den, states, sum_prefix);
 }
 }  // namespace
 
@@ -629,7 +646,7 @@ hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int gw, in
 hipError_t launch_chunk_output_fast(const DevProblem& pr, bool packed, int gw, bool out_bf16,
                                     int L, int n_seg, const void* q, const void* k,
                                     const void* v, void* o, float* den, const float* states,
-                                    hipStream_t st) {
+                                    bool sum_prefix, hipStream_t st) {
   if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;
   if (gw != P && gw != 8 && gw != 4) return hipErrorInvalidValue;
   const SegGrid sg = make_seg_grid(pr, n_seg);
@@ -637,9 +654,11 @@ hipError_t launch_chunk_output_fast(const DevProblem& pr, bool packed, int gw, b
   const dim3 grid((unsigned)sg.blocks());
   const __bf16 *qq = (const __bf16*)q, *kk = (const __bf16*)k, *vv = (const __bf16*)v;
   if (out_bf16)
-    walk_dispatch<__bf16>(pr, sg, packed, gw, L, n_seg, grid, st, qq, kk, vv, o, den, states);
+    walk_dispatch<__bf16>(pr, sg, packed, gw, L, n_seg, grid, st, qq, kk, vv, o, den, states,
+                          sum_prefix);
   else
-    walk_dispatch<float>(pr, sg, packed, gw, L, n_seg, grid, st, qq, kk, vv, o, den, states);
+    walk_dispatch<float>(pr, sg, packed, gw, L, n_seg, grid, st, qq, kk, vv, o, den, states,
+                         sum_prefix);
   return hipGetLastError();
 }
 

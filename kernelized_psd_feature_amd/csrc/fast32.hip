@@ -286,7 +286,7 @@ template <typename Tout>
 __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     DevProblem pr, SegGrid sg, int L, int n_seg, const __bf16* __restrict__ q,
     const __bf16* __restrict__ k, const __bf16* __restrict__ v, Tout* __restrict__ o,
-    float* __restrict__ den_out, const float* __restrict__ states) {
+    float* __restrict__ den_out, const float* __restrict__ states, int sum_prefix) {
   extern __shared__ __align__(16) unsigned char smem[];
   Walk32Lds& sm = *reinterpret_cast<Walk32Lds*>(smem);
   Tiles32& tl = sm.tl;
@@ -298,24 +298,36 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
   const int n_chunks = pr.T / C;
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
 
-  const float* pre =
-      states ? states + ((long long)(b * pr.H + h) * n_seg + seg) * kStateFloats : nullptr;
+  // Exclusive prefix of this segment: the scanned state at position seg, or (sum_prefix)
+  // the states of segments 0 .. seg-1 added in that order; zero without states.
   f32x4 S[kSlots][4], Z[2][2];
 #pragma unroll
-  for (int sl = 0; sl < kSlots; ++sl) {
-    const int t = owns(w, sl) ? tile_of(w, sl) : 0;
+  for (int sl = 0; sl < kSlots; ++sl)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      S[sl][nt] = (pre && owns(w, sl))
-                      ? *reinterpret_cast<const f32x4*>(pre + ((t * 4 + nt) * 64 + lane) * 4)
-                      : zero4();
-  }
+    for (int nt = 0; nt < 4; ++nt) S[sl][nt] = zero4();
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int kj = 0; kj < 2; ++kj)
-      Z[mi][kj] = pre ? *reinterpret_cast<const f32x4*>(pre + kZOff + ((mi * 2 + kj) * 64 + lane) * 4)
-                      : zero4();
+    for (int kj = 0; kj < 2; ++kj) Z[mi][kj] = zero4();
+  {
+    const int j0 = sum_prefix ? 0 : seg, j1 = !states ? j0 : sum_prefix ? seg : seg + 1;
+    for (int j = j0; j < j1; ++j) {
+      const float* pre = states + ((long long)(b * pr.H + h) * n_seg + j) * kStateFloats;
+#pragma unroll
+      for (int sl = 0; sl < kSlots; ++sl) {
+        if (!owns(w, sl)) continue;
+        const int t = tile_of(w, sl);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          S[sl][nt] += *reinterpret_cast<const f32x4*>(pre + ((t * 4 + nt) * 64 + lane) * 4);
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int kj = 0; kj < 2; ++kj)
+          Z[mi][kj] += *reinterpret_cast<const f32x4*>(pre + kZOff + ((mi * 2 + kj) * 64 + lane) * 4);
+    }
+  }
   Rows32 rw;
   rw.init(w, lane);
   zero_row(tl, tid);
@@ -505,7 +517,7 @@ hipError_t launch_chunk_state32(const DevProblem& pr, int L, int n_seg, int n_us
 
 hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int n_seg,
                                  const void* q, const void* k, const void* v, void* o,
-                                 float* den, const float* states, hipStream_t st) {
+                                 float* den, const float* states, bool sum_prefix, hipStream_t st) {
   if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;
   const size_t lds = sizeof(Walk32Lds);
   const SegGrid sg = make_seg_grid(pr, n_seg);
@@ -518,13 +530,13 @@ hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     launch_kernel(chunk_output32_kernel<__bf16>, grid, kThreads, lds, st, pr, sg, L, n_seg, qq,
-                  kk, vv, (__bf16*)o, den, states);
+                  kk, vv, (__bf16*)o, den, states, (int)sum_prefix);
   } else {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_output32_kernel<float>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     launch_kernel(chunk_output32_kernel<float>, grid, kThreads, lds, st, pr, sg, L, n_seg, qq,
-                  kk, vv, (float*)o, den, states);
+                  kk, vv, (float*)o, den, states, (int)sum_prefix);
   }
   return hipGetLastError();
 }

@@ -27,7 +27,7 @@ hipError_t launch_chunk_state32(const DevProblem& pr, int L, int n_seg, int n_us
                                 const void* k, const void* v, float* states, hipStream_t st);
 hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int n_seg,
                                  const void* q, const void* k, const void* v, void* o,
-                                 float* den, const float* states, hipStream_t st);
+                                 float* den, const float* states, bool sum_prefix, hipStream_t st);
 
 // Segment states; segments seg >= n_used get a zero state without reading their tokens.
 hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int gw, int L, int n_seg,
@@ -36,7 +36,7 @@ hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int gw, in
 hipError_t launch_chunk_output_fast(const DevProblem& pr, bool packed, int gw, bool out_bf16,
                                     int L, int n_seg, const void* q, const void* k,
                                     const void* v, void* o, float* den, const float* states,
-                                    hipStream_t st);
+                                    bool sum_prefix, hipStream_t st);
 }  // namespace kata
 
 namespace {
@@ -262,8 +262,9 @@ kata_status kata_fwd_chunked_plan(const kata_problem* pr, kata_chunked_plan* out
   out->state_floats = cp.state_elems;
   out->mfma = cp.fast;
   out->packed = cp.packed;
-  const bool one_segment = cp.fast && cp.n_seg == 1;   // as kata_fwd_chunked
-  out->scan_levels = one_segment ? 0 : kata::plan_scan(cp.n_seq, cp.n_seg, cp.state_elems).levels;
+  out->walk_sums_prefix = cp.walk_sums_prefix;
+  const bool no_scan = (cp.fast && cp.n_seg == 1) || cp.walk_sums_prefix;  // as the forward
+  out->scan_levels = no_scan ? 0 : kata::plan_scan(cp.n_seq, cp.n_seg, cp.state_elems).levels;
   return KATA_OK;
 }
 
@@ -299,7 +300,7 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
                     : kata::launch_chunk_state_generic(dp, in_bf16, k, v, states, cp.n_chunks, st);
     }
     if (e != hipSuccess) return launch_status(e, "chunk-state kernel");
-    {
+    if (!cp.walk_sums_prefix) {
       // exclusive prefix over segments
       Timed t(KATA_K_SCAN, st);
       e = run_scan(states, cp.n_seq, cp.n_seg, cp.state_elems, 1, nullptr, scan_ws, st);
@@ -309,10 +310,11 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
   {
     Timed t(KATA_K_CHUNK_OUTPUT, st);
     const float* pre = one_segment ? nullptr : states;
+    const bool sum_prefix = cp.walk_sums_prefix != 0;
     e = cp.fast32 ? kata::launch_chunk_output32(dp, out_bf16, cp.L, cp.n_seg, q, k, v, o, den,
-                                                pre, st)
+                                                pre, sum_prefix, st)
         : cp.fast ? kata::launch_chunk_output_fast(dp, cp.packed, cp.gw, out_bf16, cp.L,
-                                                   cp.n_seg, q, k, v, o, den, pre, st)
+                                                   cp.n_seg, q, k, v, o, den, pre, sum_prefix, st)
                 : kata::launch_chunk_output_generic(dp, in_bf16, out_bf16, q, k, v, o, den,
                                                     states, cp.n_chunks, st);
   }

@@ -192,8 +192,14 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
     cp.L = 1;   // the VALU path scans every chunk state
   }
   cp.n_seg = (cp.n_chunks + cp.L - 1) / cp.L;
+  // Few segments per sequence (MFMA kernels): the walk of segment s adds the states of
+  // segments 0 .. s-1 itself.  That reads n(n-1)/2 states per sequence; the scan reads and
+  // writes all n and the walks read n prefixes again, 3n, and costs a launch of its own.
+  cp.walk_sums_prefix =
+      (cp.fast && cp.n_seg >= 2 && cp.n_seg <= kWalkPrefixMaxSegments) ? 1 : 0;
   cp.states_bytes = round256(size_t(cp.n_seq) * size_t(cp.n_seg) * size_t(cp.state_elems) * 4);
-  cp.scan_ws_bytes = plan_scan(cp.n_seq, cp.n_seg, cp.state_elems).ws_bytes;
+  cp.scan_ws_bytes =
+      cp.walk_sums_prefix ? 0 : plan_scan(cp.n_seq, cp.n_seg, cp.state_elems).ws_bytes;
   cp.ws_bytes = cp.states_bytes + cp.scan_ws_bytes;
   return cp;
 }

@@ -12,6 +12,9 @@ namespace kata {
 
 enum class Form { Quadratic, Chunked, Backward };
 
+// Most segments per sequence for which the walks form their prefixes without a scan.
+constexpr int kWalkPrefixMaxSegments = 8;
+
 // Which kernels run a chunked forward, and the workspace they need.
 struct ChunkPlan {
   int fast = 0;               // 1: bf16 MFMA kernels; 0: fp32-arithmetic VALU kernels
@@ -21,6 +24,7 @@ struct ChunkPlan {
   int L = 1;                  // chunks per segment
   int n_chunks = 0;           // N_c = T / C per (b, h)
   int n_seg = 0;              // ceil(N_c / L)
+  int walk_sums_prefix = 0;   // 1: each walk adds the earlier segments' states itself, no scan
   int dv_split = 1;           // workgroups sharing one segment, each owning dv / dv_split columns
   int64_t n_seq = 0;          // B * H
   int64_t state_elems = 0;    // floats in one segment state: p^2 (dv + 1)

@@ -311,17 +311,26 @@ def test_chunked_plan_reports_segments_and_scan_depth():
     assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK
     assert (out.n_chunks, out.mfma, out.packed) == (2048, 1, 1)
     assert out.segments == -(-2048 // out.chunks_per_segment) and 1 < out.segments < 2048
-    assert out.scan_levels == math.ceil(math.log2(out.segments))
+    assert out.scan_levels == math.ceil(math.log2(out.segments)) and out.walk_sums_prefix == 0
     assert out.state_floats == (10 * 16 * 64 + 256)       # 10 packed tiles of 16 x 64, + Z
     # 512 sequences fill two thirds of the GPU's 768 workgroup slots: one segment each, no
-    # state pass, no scan; 256 sequences take 3 segments each (768 walks)
+    # state pass, no scan; 256 sequences take 3 segments each (768 walks), and with at most 8
+    # segments the walks add the earlier segments' states themselves: no scan either
     pr = _problem(B=32, H=16, T=1024)
     assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK
     assert (out.segments, out.chunks_per_segment, out.scan_levels) == (1, 16, 0)
+    assert out.walk_sums_prefix == 0
     assert out.state_floats == 16 * 16 * 65                # direct layout: p^2 (dv + 1)
     pr = _problem(B=16, H=16, T=8192)
     assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK
-    assert (out.segments, out.chunks_per_segment, out.scan_levels) == (3, 43, 2)
+    assert (out.segments, out.chunks_per_segment, out.scan_levels) == (3, 43, 0)
+    assert out.walk_sums_prefix == 1
+    for seg, n_seg, walk_sums in ((4, 8, 1), (3, 11, 0)):   # 32 chunks per sequence
+        pr = _problem(B=1, H=2, T=2048)
+        pr.seg_chunks = seg
+        assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK
+        assert (out.segments, out.walk_sums_prefix) == (n_seg, walk_sums)
+        assert (out.scan_levels == 0) == bool(walk_sums)
     # fp32 kernels: one state per chunk, a scan of ceil(log2 N_c) levels
     pr = _problem(B=1, H=1, T=256, p=8, dv=16, chunk=32, in_dt=0)
     assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK

@@ -969,3 +969,25 @@ def test_state_pass_skips_only_the_last_segment():
     _check_rows(q, k, v, o, heads, lambda T: np.array([0, 319, 320, 639, 640, 1600, 1919, 1920,
                                                        2047]), TOL[w.dtype],
                 tag="segment boundaries, all heads")
+
+
+@pytest.mark.parametrize("wid,seg", [(2, 4), (2, 5), (2, 3), (3, 8), (3, 3)])
+def test_walks_that_sum_their_prefix_skip_the_scan(wid, seg):
+    # 2 to 8 segments per sequence: each walk adds the earlier segments' states itself and no
+    # scan is launched; 9 or more: the scan forms the prefixes.  T = 2048 is 32 chunks:
+    # seg_chunks 4, 5, 8 give 8, 7, 4 segments, 3 gives 11.  Every element against the oracle.
+    w = W.WORKLOADS[wid]
+    q, k, v = W.make_inputs(w, 81, T=2048, B=1, H=2)
+    qg, kg, vg = _to_gpu(q, k, v)
+    plan = K.chunked_plan(qg, kg, vg, seg_chunks=seg)
+    n_seg = -(-32 // seg)
+    assert plan["segments"] == n_seg and plan["walk_sums_prefix"] == int(n_seg <= 8)
+    K.timing_begin()
+    o = K.fwd_chunked(qg, kg, vg, seg_chunks=seg).cpu().double()
+    t = K.timing_end()
+    assert t["chunk_state"][0] == 1 and t["chunk_output"][0] == 1
+    assert t["scan"][0] == (0 if n_seg <= 8 else 1)
+    ref, _ = O.closed_form(_np(q), _np(k), _np(v))
+    worst = float((o - torch.from_numpy(ref)).abs().max())
+    say(f"{w.name} seg_chunks={seg} ({n_seg} segments): max-abs {worst:.3e}")
+    assert worst <= TOL[w.dtype]
