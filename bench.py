@@ -2,9 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_context_131k]
 
-A step is one kata_fwd_chunked call (chunk-state build, prefix scan over chunk states,
-intra-chunk tiles + inter-chunk readout + output gate) over the whole workload, with q, k, v
-already resident in HBM and the output and workspace preallocated.  W untimed steps, then K
+A step is one kata_fwd_chunked call (segment-state build, prefix scan over the segment
+states -- formed inside the walk instead when a sequence has at most 8 segments --, intra-chunk
+tiles + inter-chunk readout + output gate) over the whole workload, with q, k, v already
+resident in HBM and the output and workspace preallocated.  W untimed steps, then K
 steps timed with HIP events on the stream the kernels are launched on (value, ms_per_step),
 then K more steps in which the library's own per-kernel events on the same stream give the
 dominant kernel's average duration for the roofline figure (those events add a few
@@ -229,6 +230,34 @@ def timed_steps(step, steps, warmup, dev):
     return ms, per_kernel, ms_inst
 
 
+def graph_ms(step, steps, dev):
+    """The step captured once into a HIP graph (torch.cuda.graph records the library's launches
+    on its capture stream) and replayed K times between two events: the step time without the
+    host's per-call launch costs."""
+    import torch
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        g.replay()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
 def sweep(q, k, v, args, dev):
     """Forward tokens/s of the chunked form at each T of the metric's sweep, B*T = 131072,
     16 heads: the 131k workload's tensors viewed as (131072 / T, T, 16, D)."""
@@ -320,6 +349,8 @@ def run_chunked(args, dev, w):
     if args.form == "chunked":
         line["chunked_plan"] = K.chunked_plan(q, k, v, chunk=w.chunk, seg_chunks=args.seg,
                                               state=args.state, groups=args.groups)
+    if args.graph:
+        line["ms_per_step_graph"] = round(graph_ms(step, args.steps, dev), 5)
     if not args.no_calibration:
         line["measured_peaks"] = with_measured_peak(roof, measured_peaks(dev))
     if not args.no_cold_cache:
@@ -407,8 +438,9 @@ def run_decode(args, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first: the clocks need ~0.1 s of load to settle")
     ap.add_argument("--workload", default="long_context_131k")
     ap.add_argument("--form", choices=["chunked", "quadratic", "decode"], default="chunked")
     ap.add_argument("--seg", type=int, default=0, help="chunks per segment (0 = library default)")
@@ -419,6 +451,8 @@ def main():
                     help="KATA-Mg factor count g (1: the single PSD factor)")
     ap.add_argument("--out", choices=["fp32", "bf16"], default="fp32",
                     help="output dtype: fp32 (parity mode, the headline) or bf16 (fast mode)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a HIP graph (ms_per_step_graph)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the T sweep")
     ap.add_argument("--no-cold-cache", action="store_true",

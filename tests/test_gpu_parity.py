@@ -991,3 +991,45 @@ def test_walks_that_sum_their_prefix_skip_the_scan(wid, seg):
     worst = float((o - torch.from_numpy(ref)).abs().max())
     say(f"{w.name} seg_chunks={seg} ({n_seg} segments): max-abs {worst:.3e}")
     assert worst <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("case", ["chunked_scan", "chunked_walk_sums", "chunked_p32", "quadratic"])
+def test_forward_replays_from_a_hip_graph(case):
+    # The forward captured into a HIP graph (torch.cuda.graph records the library's launches on
+    # the capture stream) and replayed several times, with eager work and synchronizations in
+    # between: every replay equals the eager result bitwise.
+    wid, seg = {"chunked_scan": (2, 3), "chunked_walk_sums": (2, 5), "chunked_p32": (3, 0),
+                "quadratic": (2, 0)}[case]
+    w = W.WORKLOADS[wid]
+    q, k, v = _to_gpu(*W.make_inputs(w, 91, T=2048, B=2, H=4))
+    q2, k2, v2 = _to_gpu(*W.make_inputs(w, 92, T=2048, B=2, H=4))
+    o = torch.empty(v.shape, dtype=torch.float32, device=DEV)
+    ws = None
+    if case != "quadratic":
+        ws = torch.empty(max(K.chunked_workspace_size(q, k, v, seg_chunks=seg), 256),
+                         dtype=torch.uint8, device=DEV)
+
+    def fwd(a, b, c, out):
+        if case == "quadratic":
+            return K.fwd_quadratic(a, b, c, out=out)
+        return K.fwd_chunked(a, b, c, seg_chunks=seg, out=out, workspace=ws)
+
+    eager = fwd(q, k, v, torch.empty_like(o)).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd(q, k, v, o)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd(q, k, v, o)
+    for r in range(4):
+        o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, eager), f"replay {r} differs from the eager forward"
+        other = fwd(q2, k2, v2, torch.empty_like(o))   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(other).all()
+    say(f"graph replays ({case}): 4 bitwise equal to eager")
