@@ -971,26 +971,33 @@ def test_state_pass_skips_only_the_last_segment():
                 tag="segment boundaries, all heads")
 
 
-@pytest.mark.parametrize("wid,seg", [(2, 4), (2, 5), (2, 3), (3, 8), (3, 3)])
-def test_walks_that_sum_their_prefix_skip_the_scan(wid, seg):
+@pytest.mark.parametrize("wid,seg,state,g", [
+    (2, 4, "packed", 1), (2, 5, "packed", 1), (2, 3, "packed", 1), (2, 2, "packed", 1),
+    (2, 16, "packed", 1), (2, 5, "direct", 1), (2, 5, "packed", 2), (2, 4, "packed", 4),
+    (3, 8, "packed", 1), (3, 3, "packed", 1)])
+def test_walks_that_sum_their_prefix_skip_the_scan(wid, seg, state, g):
     # 2 to 8 segments per sequence: each walk adds the earlier segments' states itself and no
     # scan is launched; 9 or more: the scan forms the prefixes.  T = 2048 is 32 chunks:
-    # seg_chunks 4, 5, 8 give 8, 7, 4 segments, 3 gives 11.  Every element against the oracle.
+    # seg_chunks 16, 8, 5, 4 give 2, 4, 7, 8 segments, 3 and 2 give 11 and 16.  Every walk
+    # kernel (packed and direct layouts, KATA-Mg g = 2 and 4, p = 32); every element against
+    # the oracle.
     w = W.WORKLOADS[wid]
     q, k, v = W.make_inputs(w, 81, T=2048, B=1, H=2)
     qg, kg, vg = _to_gpu(q, k, v)
-    plan = K.chunked_plan(qg, kg, vg, seg_chunks=seg)
+    plan = K.chunked_plan(qg, kg, vg, seg_chunks=seg, state=state, groups=g)
     n_seg = -(-32 // seg)
     assert plan["segments"] == n_seg and plan["walk_sums_prefix"] == int(n_seg <= 8)
+    assert plan["mfma"] == 1 and plan["packed"] == int(state == "packed" or g > 1 or wid == 3)
     K.timing_begin()
-    o = K.fwd_chunked(qg, kg, vg, seg_chunks=seg).cpu().double()
+    o, d = K.fwd_chunked(qg, kg, vg, seg_chunks=seg, state=state, groups=g, return_den=True)
     t = K.timing_end()
     assert t["chunk_state"][0] == 1 and t["chunk_output"][0] == 1
     assert t["scan"][0] == (0 if n_seg <= 8 else 1)
-    ref, _ = O.closed_form(_np(q), _np(k), _np(v))
-    worst = float((o - torch.from_numpy(ref)).abs().max())
-    say(f"{w.name} seg_chunks={seg} ({n_seg} segments): max-abs {worst:.3e}")
+    ref, dref = O.closed_form(_np(q), _np(k), _np(v), groups=g)
+    worst = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
+    say(f"{w.name} seg_chunks={seg} ({n_seg} segments, {state}, g={g}): max-abs {worst:.3e}")
     assert worst <= TOL[w.dtype]
+    np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=1e-2)
 
 
 @pytest.mark.parametrize("case", ["chunked_scan", "chunked_walk_sums", "chunked_p32", "quadratic"])
