@@ -17,7 +17,8 @@ peaks (8 TB/s HBM, 2.5 PFLOP/s dense bf16 MFMA), over the dominant kernel's aver
 cpu_baseline: the fp64 CPU oracle (brute-force closed form) timed on a bounded uniform sample
 of the same workload's query rows, scaled to head-tokens/s.  sweep: tokens/s of the chunked
 form at T = 1k .. 128k with B*T = 131072 (the metric's dependence on T), each beside the
-sequential inter-chunk form (one segment per sequence, no scan) and the ratio of the two.
+sequential inter-chunk form (one segment per sequence, no scan), the ratio of the two, and the
+quadratic form.  crossover (--workload crossover_p32): both forms at p = 32, T = 1k .. 16k.
 
     python bench.py --form decode     # one decode step for 512 x 16 heads (recurrent form)
 """
@@ -166,6 +167,37 @@ def with_measured_peak(roof, peaks):
     return dict(peaks, frac_of_measured=round(roof["achieved"] / ceiling, 4))
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def device_info(dev):
+    import torch
+
+    pr = torch.cuda.get_device_properties(dev)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""),
+            "compute_units": pr.multi_processor_count, "memory_GiB": round(pr.total_memory / 2**30, 1)}
+
+
+def input_record(tensors, seed=0):
+    """Seed, generator library version and a hash of the exact input bytes (CPU tensors)."""
+    import numpy as np
+    import torch
+
+    h = hashlib.sha256()
+    for x in tensors:
+        h.update(x.contiguous().view(-1).view(torch.uint8).numpy().tobytes())
+    return {"seed": seed, "numpy": np.__version__, "generator": "kata_workloads.make_inputs",
+            "sha256": h.hexdigest()[:16]}
+
+
 def cpu_baseline(w, target_s=12.0):
     """Time the oracle's closed form on uniformly sampled query rows of one head of the
     workload; head-tokens/s of the oracle on the full workload = rows / seconds (a uniform
@@ -194,16 +226,19 @@ def cpu_baseline(w, target_s=12.0):
         n = min(4 * n, 4096)
     return {
         "value": done / spent, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": f"{done} query rows drawn uniformly from head 0 (T={w.T}) of the {w.name} "
                   f"workload, fp64 brute-force closed form, {spent:.1f} s",
     }
 
 
-def timed_steps(step, steps, warmup, dev):
+def timed_steps(step, steps, warmup, dev, per_step=False):
     """W untimed steps, then K steps between two events on the launch stream (the step time),
     then K more steps with the library's per-kernel events on the same stream (the kernel
     durations; those events cost a few microseconds per kernel, so they stay out of the step
-    time).  Returns (ms per step, {kernel: (launches, total ms)}, instrumented ms per step)."""
+    time).  Returns (ms per step, {kernel: (launches, total ms)}, instrumented ms per step,
+    (median, min) ms of single steps or None): with per_step, K more steps with an event after
+    each give the distribution of single-step times."""
     import torch
 
     import kernelized_psd_feature_amd as K
@@ -227,7 +262,17 @@ def timed_steps(step, steps, warmup, dev):
 
     ms, _ = region(False)
     ms_inst, per_kernel = region(True)
-    return ms, per_kernel, ms_inst
+    dist = None
+    if per_step:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for i in range(steps):
+            step()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        one = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        dist = (one[len(one) // 2], one[0])
+    return ms, per_kernel, ms_inst, dist
 
 
 def graph_ms(step, steps, dev):
@@ -260,7 +305,8 @@ def graph_ms(step, steps, dev):
 
 def sweep(q, k, v, args, dev):
     """Forward tokens/s of the chunked form at each T of the metric's sweep, B*T = 131072,
-    16 heads: the 131k workload's tensors viewed as (131072 / T, T, 16, D)."""
+    16 heads: the 131k workload's tensors viewed as (131072 / T, T, 16, D); beside it the
+    sequential inter-chunk form and the quadratic form on the same tensors."""
     import torch
 
     import kata_workloads as W
@@ -283,12 +329,43 @@ def sweep(q, k, v, args, dev):
                 K.fwd_chunked(qs, ks, vs, seg_chunks=seg, out=os_, workspace=ws,
                               state=args.state)
 
-            ms, _, _ = timed_steps(step, 30, 10, dev)
+            ms, _, _, _ = timed_steps(step, 30, 10, dev)
             point[key + "ms"] = round(ms, 5)
             point[key + "tokens_per_s"] = round(B * 16 * T / (ms / 1e3), 1)
             del ws
         point["scan_speedup"] = round(point["sequential_ms"] / point["ms"], 3)
+        # the quadratic form on the same tensors (O(T^2): a few steps at long T)
+        ms, _, _, _ = timed_steps(lambda: K.fwd_quadratic(qs, ks, vs, out=os_),
+                                  10 if T <= 16384 else 3, 3, dev)
+        point["quadratic_ms"] = round(ms, 5)
+        point["quadratic_tokens_per_s"] = round(B * 16 * T / (ms / 1e3), 1)
         out.append(point)
+    return out
+
+
+def crossover(w, dev):
+    """Both forms at each T of the p = 32 crossover workload (B = 4, H = 16, T = 1k .. 16k):
+    step times, head-tokens/s and which form is faster there."""
+    import torch
+
+    import kata_workloads as W
+    import kernelized_psd_feature_amd as K
+
+    out = []
+    for T in W.CROSSOVER_T:
+        q, k, v = (x.to(dev) for x in W.make_inputs(w, 0, T=T))
+        o = torch.empty(v.shape, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(K.chunked_workspace_size(q, k, v), 256), dtype=torch.uint8,
+                         device=dev)
+        point = {"T": T, "B": w.B}
+        for form, step in (("chunked", lambda: K.fwd_chunked(q, k, v, out=o, workspace=ws)),
+                           ("quadratic", lambda: K.fwd_quadratic(q, k, v, out=o))):
+            ms, _, _, _ = timed_steps(step, 20, 20, dev)
+            point[form + "_ms"] = round(ms, 5)
+            point[form + "_tokens_per_s"] = round(w.B * w.H * T / (ms / 1e3), 1)
+        point["faster"] = "chunked" if point["chunked_ms"] < point["quadratic_ms"] else "quadratic"
+        out.append(point)
+        del q, k, v, o, ws
     return out
 
 
@@ -299,6 +376,7 @@ def run_chunked(args, dev, w):
     import kernelized_psd_feature_amd as K
 
     q, k, v = W.make_inputs(w, 0)
+    inputs = input_record((q, k, v))
     if args.layout == "bhtd":
         q, k, v = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
     q, k, v = (x.to(dev) for x in (q, k, v))
@@ -318,7 +396,7 @@ def run_chunked(args, dev, w):
         else:
             K.fwd_quadratic(q, k, v, out=o, out_dtype=out_dtype, groups=args.groups)
 
-    ms, per_kernel, ms_inst = timed_steps(step, args.steps, args.warmup, dev)
+    ms, per_kernel, ms_inst, dist = timed_steps(step, args.steps, args.warmup, dev, True)
     tokens = w.B * w.H * w.T
     dom = "chunk_output" if args.form == "chunked" else "quadratic"
     launches, total_ms = per_kernel[dom]
@@ -343,8 +421,10 @@ def run_chunked(args, dev, w):
         "roofline": roof,
         "kernels_ms": {n: round(t / max(c, 1), 5) for n, (c, t) in per_kernel.items() if c},
         "ms_per_step_with_kernel_events": round(ms_inst, 5),
+        "ms_per_step_median": round(dist[0], 5), "ms_per_step_min": round(dist[1], 5),
         "step_roofline_frac": roofline(fpt * tokens, bpt * tokens, ms / 1e3)["frac"],
         "dominant_kernel_source_sha": sha,
+        "inputs": inputs, "device": device_info(dev),
     }
     if args.form == "chunked":
         line["chunked_plan"] = K.chunked_plan(q, k, v, chunk=w.chunk, seg_chunks=args.seg,
@@ -362,6 +442,9 @@ def run_chunked(args, dev, w):
         line["sweep"] = sweep(q, k, v, args, dev)
         sp = [x["scan_speedup"] for x in line["sweep"]]
         line["scan_speedup_mean"] = round(sum(sp) / len(sp), 3)
+    if args.form == "chunked" and w.name == "crossover_p32" and not args.no_sweep \
+            and args.layout == "bthd" and args.out == "fp32" and args.groups == 1:
+        line["crossover"] = crossover(w, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     return line
@@ -389,6 +472,7 @@ def cpu_baseline_decode(w, target_s=10.0):
         spent += time.perf_counter() - t0
         done += Q.shape[1]
     return {"value": done / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{done} decode steps of one head (p={w.p}, d_v={w.dv}) by the fp64 "
                       f"token-by-token recurrence, {spent:.1f} s"}
 
@@ -400,14 +484,16 @@ def run_decode(args, dev):
     import kernelized_psd_feature_amd as K
 
     w = W.DECODE
-    q, k, v = (x.to(dev) for x in W.make_inputs(w, 0))
+    cpu = W.make_inputs(w, 0)
+    inputs = input_record(cpu)
+    q, k, v = (x.to(dev) for x in cpu)
     state = torch.zeros(K.state_shape(k, v), dtype=torch.float32, device=dev)
     o = torch.empty(v.shape, dtype=torch.float32, device=dev)
 
     def step():
         K.decode(q, k, v, state, out=o)
 
-    ms, per_kernel, ms_inst = timed_steps(step, args.steps, args.warmup, dev)
+    ms, per_kernel, ms_inst, dist = timed_steps(step, args.steps, args.warmup, dev, True)
     tokens = w.B * w.H * w.T
     launches, total_ms = per_kernel["decode"]
     avg_ms = total_ms / max(launches, 1)
@@ -421,12 +507,14 @@ def run_decode(args, dev):
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "tokens_per_step": w.T, "p": w.p,
                    "dv": w.dv, "form": "decode", "state_bytes": 4 * tokens * w.p ** 2 * (w.dv + 1)},
+        "inputs": inputs, "device": device_info(dev),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic("decode", w.name,
                                              source_sha(KERNEL_SOURCES["decode"]))},
         "kernels_ms": {n: round(t / max(c, 1), 5) for n, (c, t) in per_kernel.items() if c},
         "ms_per_step_with_kernel_events": round(ms_inst, 5),
+        "ms_per_step_median": round(dist[0], 5), "ms_per_step_min": round(dist[1], 5),
     }
     if not args.no_calibration:
         line["measured_peaks"] = with_measured_peak(line["roofline"], measured_peaks(dev))

@@ -20,7 +20,8 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "DECODE", "SWEEP_T", "make_inputs", "sweep_workload"]
+__all__ = ["Workload", "WORKLOADS", "DECODE", "SWEEP_T", "CROSSOVER_T", "make_inputs",
+           "sweep_workload"]
 
 
 @dataclass(frozen=True)
@@ -63,6 +64,9 @@ DECODE = Workload(6, "decode_b512", B=512, H=16, T=1, p=16, dv=64, chunk=64,
 
 # Throughput sweep at p=16, d_v=64, 16 heads, with B*T held at 131072 head-positions.
 SWEEP_T = (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072)
+
+# Sequence lengths of the quadratic/chunked crossover workload (B=4, H=16, p=32).
+CROSSOVER_T = (1024, 4096, 8192, 16384)
 
 
 def sweep_workload(T):
