@@ -1040,3 +1040,44 @@ def test_forward_replays_from_a_hip_graph(case):
         torch.cuda.synchronize()
         assert torch.isfinite(other).all()
     say(f"graph replays ({case}): 4 bitwise equal to eager")
+
+
+@pytest.mark.parametrize("form", ["chunked", "quadratic"])
+def test_outputs_past_two_to_the_31_elements(form):
+    # Maximum sizes: o holds more than 2^31 elements (8.9 GB fp32), so every output index past
+    # the 2^31 - 1 mark needs 64-bit arithmetic.  Inputs: the long-context recipe, repeated
+    # (valid inputs like any other; the oracle gets the same values).  Chunked: 65,536 tokens
+    # x 16 heads repeated 33 times along T (2,162,688 tokens, 528 segments per head: state
+    # pass, scan and walk); quadratic: 32,768 tokens x 16 heads repeated 65 times along H
+    # (1040 heads, so the O(T^2) kernel stays short).  Sampled rows of the first and last head
+    # against the oracle, including rows whose outputs lie past 2^31 elements.
+    w = W.WORKLOADS[4]
+    if form == "chunked":
+        T0, rt, rh = 65536, 33, 1
+    else:
+        T0, rt, rh = 32768, 1, 65
+    base = W.make_inputs(w, 5, T=T0, B=1, H=16)
+    T, H = T0 * rt, 16 * rh
+    assert T * H * w.dv > 2 ** 31
+    qg, kg, vg = (x.to(DEV).repeat(1, rt, rh, 1) for x in base)
+    if form == "chunked":
+        o, d = K.fwd_chunked(qg, kg, vg, chunk=w.chunk, return_den=True)
+    else:
+        o, d = K.fwd_quadratic(qg, kg, vg, return_den=True)
+    del qg, kg, vg
+    # the first row whose output of head H - 1 starts past element 2^31
+    t31 = (2 ** 31 - (H - 1) * w.dv) // (H * w.dv) + 1
+    rows = np.unique(np.array([0, 1, 2, 3, t31 - 2, t31 - 1, t31, t31 + 1, T - 65, T - 2, T - 1]))
+    assert rows.max() < T and (t31 * H + H - 1) * w.dv >= 2 ** 31
+    ridx = torch.from_numpy(rows).to(DEV)
+    worst = 0.0
+    for h in (0, H - 1):
+        got = o[0, ridx, h].cpu().double().numpy()
+        dgot = d[0, ridx, h].cpu().double().numpy()
+        Q, Kk, V = (np.tile(x[0, :, h % 16].to(torch.float64).numpy(), (rt, 1)) for x in base)
+        ref, dref = O.closed_form_rows(Q, Kk, V, rows)
+        worst = max(worst, float(np.abs(got - ref).max()))
+        np.testing.assert_allclose(dgot, dref, rtol=1e-2)
+        del Q, Kk, V
+    say(f"{form}: {T} tokens x {H} heads, o {T * H * w.dv:.3e} elements: max-abs {worst:.3e}")
+    assert worst <= TOL[w.dtype]
