@@ -1081,3 +1081,31 @@ def test_outputs_past_two_to_the_31_elements(form):
         del Q, Kk, V
     say(f"{form}: {T} tokens x {H} heads, o {T * H * w.dv:.3e} elements: max-abs {worst:.3e}")
     assert worst <= TOL[w.dtype]
+
+
+def test_decode_state_past_two_to_the_31_elements():
+    # Maximum decode size: B*H = 65,520 sequences (the ABI's limit is 65,535) at p = 32, so the
+    # fp32 state holds 4.4e9 values (17.4 GB) and sequences from 32,264 on start past element
+    # 2^31.  One token from a zero state: o_t = a v_t / (eps + a) with a = (q.k)^2, and the
+    # state becomes (phi(k) v^T, k k^T); checked for sequences at the start, across the 2^31
+    # mark and at the end.
+    w = W.WORKLOADS[3]
+    B, H = 4095, 16
+    q, k, v = W.make_inputs(w, 23, T=1, B=B, H=H)
+    qg, kg, vg = _to_gpu(q, k, v)
+    state = torch.zeros(K.state_shape(kg, vg), dtype=torch.float32, device=DEV)
+    E = w.p * w.p * (w.dv + 1)
+    assert state.numel() == B * H * E and state.numel() > 2 ** 31
+    o = K.decode(qg, kg, vg, state)
+    n31 = 2 ** 31 // E + 1                           # first sequence starting past 2^31
+    worst_o, worst_s = 0.0, 0.0
+    for n in (0, 1, n31 - 1, n31, n31 + 1, B * H - 1):
+        b, h = divmod(n, H)
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        ref, _ = O.closed_form(_np(q[sl]), _np(k[sl]), _np(v[sl]))
+        worst_o = max(worst_o, float(np.abs(o[sl].cpu().double().numpy() - ref).max()))
+        want, _ = _oracle_state(k[sl], v[sl])
+        worst_s = max(worst_s, float(np.abs(state[b, h].cpu().double().numpy() - want[0, 0]).max()))
+    say(f"decode, {B * H} sequences, state {state.numel():.3e} values: o max-abs {worst_o:.3e}, "
+        f"state max-abs {worst_s:.3e}")
+    assert worst_o <= TOL[w.dtype] and worst_s <= 1e-3
