@@ -42,7 +42,7 @@ extern "C" {
 typedef enum {
   KATA_OK = 0,
   KATA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, stride, alignment or eps       */
-  KATA_ERR_UNSUPPORTED = 2,      /* a valid problem this build has no kernel for          */
+  KATA_ERR_UNSUPPORTED = 2,      /* a valid problem the library has no kernel for         */
   KATA_ERR_WORKSPACE = 3,        /* workspace pointer null or smaller than required       */
   KATA_ERR_DEVICE = 4            /* no usable gfx950 device, or a launch error            */
 } kata_status;
