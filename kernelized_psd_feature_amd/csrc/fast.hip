@@ -583,15 +583,6 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
 
 }  // namespace
 
-// KATA-Mg group count -> group width of the MFMA kernels (0 when they do not take it)
-int fast_group_width(int groups) {
-  return groups <= 1 ? P : groups == 2 ? 8 : groups == 4 ? 4 : 0;
-}
-
-bool quadratic_fast_supported(const kata_problem* pr) {
-  return pr->in_dtype == KATA_BF16 && pr->p == P && pr->dv == DV && fast_group_width(pr->groups);
-}
-
 bool chunk_fast_available() { return true; }
 
 namespace {

@@ -497,10 +497,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
 
 }  // namespace
 
-bool fast32_supported(const kata_problem* pr) {
-  return pr->in_dtype == KATA_BF16 && pr->p == P && pr->dv == DV && pr->groups <= 1;
-}
-
 hipError_t launch_chunk_state32(const DevProblem& pr, int L, int n_seg, int n_used,
                                 const void* k, const void* v, float* states, hipStream_t st) {
   if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;

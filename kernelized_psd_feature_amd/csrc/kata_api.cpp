@@ -15,14 +15,12 @@
 #include "plan.h"
 
 namespace kata {
-int fast_group_width(int groups);
 hipError_t launch_quadratic_mfma(const DevProblem& pr, int gw, bool out_bf16, const void* q,
                                  const void* k, const void* v, void* o, float* den,
                                  hipStream_t st);
-bool quadratic_fast_supported(const kata_problem* pr);
 bool quadratic_mfma_grid_fits(const DevProblem& pr);
+int quadratic_mfma_group_width(const kata_problem* pr);
 bool chunk_fast_available();
-bool fast32_supported(const kata_problem* pr);
 hipError_t launch_chunk_state32(const DevProblem& pr, int L, int n_seg, int n_used,
                                 const void* k, const void* v, float* states, hipStream_t st);
 hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int n_seg,
@@ -228,16 +226,12 @@ kata_status kata_fwd_quadratic(const kata_problem* pr, const void* q, const void
   const kata::DevProblem dp = to_dev(pr);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const bool in_bf16 = pr->in_dtype == KATA_BF16, out_bf16 = pr->out_dtype == KATA_BF16;
-  const bool mfma = kata::quadratic_fast_supported(pr) || kata::fast32_supported(pr);
-  if (mfma && !kata::quadratic_mfma_grid_fits(dp))
+  const int gw = kata::quadratic_mfma_group_width(pr);   // 0: the fp32 kernel
+  if (gw && !kata::quadratic_mfma_grid_fits(dp))
     return set_error(KATA_ERR_UNSUPPORTED, "quadratic forward: more than 2^31 - 1 query blocks");
   Timed t(KATA_K_QUADRATIC, st);
-  if (kata::quadratic_fast_supported(pr))
-    return launch_status(kata::launch_quadratic_mfma(dp, kata::fast_group_width(pr->groups),
-                                                     out_bf16, q, k, v, o, den, st),
-                         "quadratic forward");
-  if (kata::fast32_supported(pr))
-    return launch_status(kata::launch_quadratic_mfma(dp, 32, out_bf16, q, k, v, o, den, st),
+  if (gw)
+    return launch_status(kata::launch_quadratic_mfma(dp, gw, out_bf16, q, k, v, o, den, st),
                          "quadratic forward");
   return launch_status(kata::launch_quadratic_generic(dp, in_bf16, out_bf16, q, k, v, o, den, st),
                        "quadratic forward");

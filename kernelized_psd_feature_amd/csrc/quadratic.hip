@@ -84,7 +84,8 @@ __device__ __forceinline__ float add_pair(uint32_t w, float acc) {
                                          __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
 }
 
-// Query operand cut to KATA-Mg group j (p = 16): lane half h holds coordinates 8h .. 8h + 7.
+// Query operand of one 16-deep K step cut to KATA-Mg group j of width GW (8 or 4) within the
+// step: lane half h holds the step's coordinates 8h .. 8h + 7.
 template <int GW>
 __device__ __forceinline__ bf16x8 group_cut(const bf16x8& q, int h, int j) {
   const uint4 u = __builtin_bit_cast(uint4, q);
@@ -128,14 +129,19 @@ __device__ __forceinline__ void weights(const bf16x8 (&kf)[QTraits<P>::KD],
 #pragma unroll
     for (int v = 0; v < 16; ++v) x2[v] = sc[v] * sc[v];
   } else {
-    static_assert(P == 16, "grouped scores at p = 16");
+    // one product per group: a 16-deep K step holds 16 / GW groups (GW = 16: the whole step)
+    static_assert(GW == 16 || GW == 8 || GW == 4, "group widths 16, 8, 4");
     x2 = zero16();
 #pragma unroll
-    for (int j = 0; j < P / GW; ++j) {
-      const f32x16 sc = mfma3232(kf[0], group_cut<GW>(qf[0], h, j), zero16());
+    for (int d = 0; d < QTraits<P>::KD; ++d)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) x2[v] = fmaf(sc[v], sc[v], x2[v]);
-    }
+      for (int j = 0; j < 16 / GW; ++j) {
+        bf16x8 qg = qf[d];
+        if constexpr (GW < 16) qg = group_cut<GW>(qf[d], h, j);
+        const f32x16 sc = mfma3232(kf[d], qg, zero16());
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x2[v] = fmaf(sc[v], sc[v], x2[v]);
+      }
   }
   pack_weights<kMask>(x2, s0, t, h, pw, lsum);
 }
@@ -401,11 +407,24 @@ hipError_t launch_dispatch(const DevProblem& pr, int gw, hipStream_t st, const v
   else if (pr.p == 16 && gw == 8) launch_t<Tout, 16, 8>(pr, st, q, k, v, o, den);
   else if (pr.p == 16 && gw == 4) launch_t<Tout, 16, 4>(pr, st, q, k, v, o, den);
   else if (pr.p == 32 && gw == 32) launch_t<Tout, 32, 32>(pr, st, q, k, v, o, den);
+  else if (pr.p == 32 && gw == 16) launch_t<Tout, 32, 16>(pr, st, q, k, v, o, den);
+  else if (pr.p == 32 && gw == 8) launch_t<Tout, 32, 8>(pr, st, q, k, v, o, den);
+  else if (pr.p == 32 && gw == 4) launch_t<Tout, 32, 4>(pr, st, q, k, v, o, den);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 }  // namespace
+
+// KATA-Mg group width the MFMA kernel takes for this problem (bf16 in, d_v = 64, p = 16 or
+// 32, groups of 16, 8 or 4 coordinates, or the whole p), 0 when it takes none.
+int quadratic_mfma_group_width(const kata_problem* pr) {
+  if (pr->in_dtype != KATA_BF16 || pr->dv != DV || (pr->p != 16 && pr->p != 32)) return 0;
+  const int g = pr->groups <= 1 ? 1 : pr->groups;
+  if (pr->p % g) return 0;
+  const int gw = pr->p / g;
+  return (gw == pr->p || gw == 16 || gw == 8 || gw == 4) ? gw : 0;
+}
 
 // The grid is one-dimensional: every query block of every (b, h).
 bool quadratic_mfma_grid_fits(const DevProblem& pr) {

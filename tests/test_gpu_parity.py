@@ -711,7 +711,9 @@ def test_decode_bf16_output_is_the_rounded_fp32_output_and_state_is_the_same():
 
 
 # ------------------------------------------------------------ KATA-Mg (groups) ----------
-# g concatenated PSD factors over consecutive coordinate groups; fp32 kernels.
+# g concatenated PSD factors over consecutive coordinate groups: the MFMA quadratic kernel
+# (bf16, groups of 16, 8 or 4 coordinates), the MFMA chunked kernels at p = 16, fp32 kernels
+# for the rest.
 
 MG_CASES = {   # name: (workload, T, B, H, groups)
     "layer340m_g2": (2, 448, 2, 3, 2),
@@ -719,6 +721,8 @@ MG_CASES = {   # name: (workload, T, B, H, groups)
     "tiny_fp32_g2": (1, 256, 1, 1, 2),
     "tiny_fp32_g8": (1, 256, 1, 1, 8),
     "p32_g2": (3, 256, 1, 2, 2),
+    "p32_g4": (3, 320, 1, 2, 4),
+    "p32_g8": (3, 192, 2, 1, 8),
 }
 
 
@@ -933,13 +937,15 @@ def test_quadratic_ragged_T(case):
     np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=1e-2)
 
 
-@pytest.mark.parametrize("case", ["p16", "p16_g2", "p32"])
+@pytest.mark.parametrize("case", ["p16", "p16_g2", "p32", "p32_g2", "p32_g4", "p32_g8"])
 def test_quadratic_two_query_blocks_per_wave_ragged_T(case):
     # Grids of at least 4096 workgroups of 256 queries take two 32-query blocks per wave; a
     # ragged T then leaves a partial last workgroup, a partial last key block and queries past
-    # T in both of a wave's blocks.  Edge and random rows of sampled heads, with D_t.
+    # T in both of a wave's blocks.  Edge and random rows of sampled heads, with D_t.  KATA-Mg
+    # at p = 32: groups of 16, 8 and 4 coordinates.
     wid, g, B, T = {"p16": (2, 1, 1, 65636), "p16_g2": (2, 2, 1, 65636),
-                    "p32": (3, 1, 4, 16421)}[case]
+                    "p32": (3, 1, 4, 16421), "p32_g2": (3, 2, 4, 16421),
+                    "p32_g4": (3, 4, 4, 16421), "p32_g8": (3, 8, 4, 16421)}[case]
     w = W.WORKLOADS[wid]
     q, k, v = W.make_inputs(w, 75, T=T, B=B, H=16)
     assert B * 16 * -(-T // 256) >= 4096                  # the two-block shape
