@@ -59,12 +59,13 @@ def algorithmic_bytes_per_token(p, dv, in_bytes=2, out_bytes=4):
     return in_bytes * (2 * p + dv) + out_bytes * dv
 
 
-def chunked_flops_per_token(p, dv, C):
-    # state build and readout 2 p^2 (d_v + 1) each, intra-chunk tile (C+1)/2 causal pairs on
-    # average of 2 (p + d_v + 1) (score, PV, row sum), q^T Z q 2 p^2, the scan's
-    # 2 p^2 (d_v + 1) / C, epilogue d_v
-    return (4 * p * p * (dv + 1) + (C + 1) * (p + dv + 1) + 2 * p * p
-            + 2 * p * p * (dv + 1) // C + dv)
+def chunked_flops_per_token(p, dv, C, groups=1):
+    # with n = p^2 / g state features (g KATA-Mg groups of p / g coordinates; n = p^2 at g = 1):
+    # state build and readout 2 n (d_v + 1) each, intra-chunk tile (C+1)/2 causal pairs on
+    # average of 2 (p + d_v + 1) (score, PV, row sum), q^T Z q 2 n, the scan's
+    # 2 n (d_v + 1) / C, epilogue d_v
+    n = p * p // groups
+    return (4 * n * (dv + 1) + (C + 1) * (p + dv + 1) + 2 * n + 2 * n * (dv + 1) // C + dv)
 
 
 def quadratic_flops_per_token(p, dv, T):
@@ -399,16 +400,19 @@ def run_chunked(args, dev, w):
     ms, per_kernel, ms_inst, dist = timed_steps(step, args.steps, args.warmup, dev, True)
     tokens = w.B * w.H * w.T
     dom = "chunk_output" if args.form == "chunked" else "quadratic"
-    launches, total_ms = per_kernel[dom]
-    avg_ms = total_ms / max(launches, 1)
+    _, total_ms = per_kernel[dom]
+    # the dominant kernel's time per step (one launch per step; at p = 32 with KATA-Mg groups
+    # the chunked output stage is two p = 16 walks and their combination)
+    avg_ms = total_ms / args.steps
     bpt = algorithmic_bytes_per_token(w.p, w.dv, out_bytes=2 if args.out == "bf16" else 4)
-    fpt = (chunked_flops_per_token(w.p, w.dv, w.chunk) if args.form == "chunked"
+    fpt = (chunked_flops_per_token(w.p, w.dv, w.chunk, args.groups) if args.form == "chunked"
            else quadratic_flops_per_token(w.p, w.dv, w.T))
     sources = KERNEL_SOURCES[dom if w.p == 16 else dom + "32"]
     sha = source_sha(sources)
     roof = roofline(fpt * tokens, bpt * tokens, avg_ms / 1e3)
-    # the committed counters were taken with fp32 outputs
-    roof["traffic"] = load_traffic(dom, w.name, sha) if args.out == "fp32" else None
+    # the committed counters were taken with fp32 outputs and one group
+    roof["traffic"] = (load_traffic(dom, w.name, sha)
+                       if args.out == "fp32" and args.groups == 1 else None)
     line = {
         "metric": METRIC, "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),

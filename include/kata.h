@@ -76,9 +76,13 @@ typedef enum { KATA_STATE_DIRECT = 0, KATA_STATE_PACKED = 1 } kata_state_layout;
  *          a_ts = sum_j (q_t^(j) . k_s^(j))^2, with the same single denominator (gist.science
  *          section 2.3, the variants bullet; ai.info Main Findings, state-size bullet; the KATA
  *          README's concat-SPD call with num_groups).  g must divide p.  The bf16 MFMA
- *          kernels take g = 2 and 4 at p = 16 (dv = 64; chunk = 64 for the chunked form) and
- *          keep only the within-group feature pairs; every other grouped problem runs the fp32
- *          kernels, whose chunk states keep p^2 rows, the pairs across groups being zero.
+ *          kernels (dv = 64; chunk = 64 for the chunked form) take g = 2 and 4 at p = 16 and
+ *          keep only the within-group feature pairs; at p = 32 the quadratic form takes
+ *          g = 2, 4, 8 on MFMA, and the chunked form runs them as two p = 16 passes over the
+ *          coordinate halves (g / 2 groups each) whose numerators and denominators are added
+ *          (workspace for the two passes' fp32 outputs included); every other grouped
+ *          problem runs the fp32 kernels, whose chunk states keep p^2 rows, the pairs across
+ *          groups being zero.
  *   eps: finite, >= 0 (1e-6 in every workload).
  *   in_dtype: dtype of q, k, v (and dO); out_dtype: dtype of o.  Allowed pairs:
  *          (BF16 -> F32), (BF16 -> BF16), (F32 -> F32).  Gradients are always F32.
@@ -131,7 +135,8 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
  * levels, feed the walk.  With one segment per (b, h) on the MFMA kernels (the sequential
  * inter-chunk form) neither runs and scan_levels is 0.  With 2 to 8 segments on the MFMA
  * kernels (walk_sums_prefix = 1) no scan runs either (scan_levels 0): the walk of segment s adds
- * the states of segments 0 .. s-1 in that order, the same exclusive prefix.  Source:
+ * the states of segments 0 .. s-1 in that order, the same exclusive prefix.  For p = 32
+ * KATA-Mg on the MFMA kernels the plan is that of each of the two p = 16 passes.  Source:
  * gist.science section 2.3 (inter-chunk depth O(log N_C)).
  *   out: host struct, filled on success.
  * Errors: INVALID_ARGUMENT (NULL out, or as kata_fwd_chunked), UNSUPPORTED. */

@@ -6,6 +6,8 @@
 // Math: a_ts = (q_t . k_s)^2 for s <= t (gist.science section 2.2: psi(u) = u u^T squares the
 // inner product), o_t = sum a_ts v_s / (eps + sum a_ts) (section 2.1; ai.info Main Findings,
 // readout-gate bullet).  Chunked form: gist.science section 2.3.
+#include <algorithm>
+
 #include "device.h"
 #include "phi_product.h"
 
@@ -263,6 +265,51 @@ hipError_t launch_chunk_output_generic(const DevProblem& pr, bool in_bf16, bool 
                                        hipStream_t st) {
   return dispatch_io<OutputLaunch>(pr.p, pr.dv, in_bf16, out_bf16, pr, q, k, v, o, den,
                                    states, n_chunks, st);
+}
+
+// Two passes over disjoint coordinate sets (p = 32 KATA-Mg as two p = 16 halves): a_ts is the
+// sum of the passes' scores, so the numerators and denominators add.  Pass j left
+// o_j = N_j / D_j and D_j = eps + l_j (fp32, [B][T][H][dv] and [B][T][H], contiguous):
+//   o = (o_0 D_0 + o_1 D_1) / (D_0 + D_1 - eps),   D = D_0 + D_1 - eps.
+// A grid-stride loop over (token, 4 value columns).
+template <typename Tout>
+__global__ __launch_bounds__(256) void halves_combine_kernel(
+    DevProblem pr, const float* __restrict__ o0, const float* __restrict__ d0,
+    const float* __restrict__ o1, const float* __restrict__ d1, Tout* __restrict__ o,
+    float* __restrict__ den) {
+  const int q4 = pr.dv / 4;
+  const long long n = (long long)pr.B * pr.T * pr.H * q4;
+  for (long long x = (long long)blockIdx.x * 256 + threadIdx.x; x < n;
+       x += (long long)gridDim.x * 256) {
+    const long long tok = x / q4;
+    const int c = 4 * int(x % q4);
+    const int h = int(tok % pr.H), t = int((tok / pr.H) % pr.T);
+    const int b = int(tok / ((long long)pr.H * pr.T));
+    const float a0 = d0[tok], a1 = d1[tok], D = (a0 + a1) - pr.eps;
+    const float4 u = *reinterpret_cast<const float4*>(o0 + tok * pr.dv + c);
+    const float4 w = *reinterpret_cast<const float4*>(o1 + tok * pr.dv + c);
+    Tout* op = o + row_off(pr.so, b, t, h) + c;
+    op[0] = from_f32<Tout>(fmaf(u.x, a0, w.x * a1) / D);
+    op[1] = from_f32<Tout>(fmaf(u.y, a0, w.y * a1) / D);
+    op[2] = from_f32<Tout>(fmaf(u.z, a0, w.z * a1) / D);
+    op[3] = from_f32<Tout>(fmaf(u.w, a0, w.w * a1) / D);
+    if (den && c == 0) den[tok] = D;
+  }
+}
+
+hipError_t launch_halves_combine(const DevProblem& pr, bool out_bf16, const float* o0,
+                                 const float* d0, const float* o1, const float* d1, void* o,
+                                 float* den, hipStream_t st) {
+  if (pr.dv % 4) return hipErrorInvalidValue;
+  const long long n = (long long)pr.B * pr.T * pr.H * (pr.dv / 4);
+  const dim3 grid((unsigned)std::min<long long>((n + 255) / 256, 256LL * 64));
+  if (out_bf16)
+    launch_kernel(halves_combine_kernel<__bf16>, grid, 256, 0, st, pr, o0, d0, o1, d1,
+                  (__bf16*)o, den);
+  else
+    launch_kernel(halves_combine_kernel<float>, grid, 256, 0, st, pr, o0, d0, o1, d1,
+                  (float*)o, den);
+  return hipGetLastError();
 }
 
 }  // namespace kata

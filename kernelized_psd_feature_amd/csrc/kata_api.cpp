@@ -31,6 +31,9 @@ hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int
 hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int gw, int L, int n_seg,
                                    int n_used, const void* k, const void* v, float* states,
                                    hipStream_t st);
+hipError_t launch_halves_combine(const DevProblem& pr, bool out_bf16, const float* o0,
+                                 const float* d0, const float* o1, const float* d1, void* o,
+                                 float* den, hipStream_t st);
 hipError_t launch_chunk_output_fast(const DevProblem& pr, bool packed, int gw, bool out_bf16,
                                     int L, int n_seg, const void* q, const void* k,
                                     const void* v, void* o, float* den, const float* states,
@@ -200,6 +203,50 @@ hipError_t run_scan(float* x, int64_t n_seq, int64_t n, int64_t elems, int exclu
                                  (int)sp.n_tiles, exclusive, totals, sums, st);
 }
 
+// The chunked pipeline for one problem and its plan: segment states, their prefix (scan or
+// summed in the walks), the walk; or the fp32 kernels.  Arguments already validated.
+kata_status run_chunked(const kata_problem* pr, const kata::ChunkPlan& cp, const void* q,
+                        const void* k, const void* v, void* o, float* den, void* workspace,
+                        hipStream_t st) {
+  const kata::DevProblem dp = to_dev(pr);
+  const bool in_bf16 = pr->in_dtype == KATA_BF16, out_bf16 = pr->out_dtype == KATA_BF16;
+  float* states = reinterpret_cast<float*>(workspace);
+  char* scan_ws = reinterpret_cast<char*>(workspace) + cp.states_bytes;
+  hipError_t e;
+  // One segment per sequence (the sequential inter-chunk form): every walk starts from a zero
+  // prefix, so no segment state or scan is needed.
+  const bool one_segment = cp.fast && cp.n_seg == 1;
+  if (!one_segment) {
+    {
+      Timed t(KATA_K_CHUNK_STATE, st);
+      // the last segment's state enters no prefix
+      e = cp.fast32 ? kata::launch_chunk_state32(dp, cp.L, cp.n_seg, cp.n_seg - 1, k, v, states, st)
+          : cp.fast ? kata::launch_chunk_state_fast(dp, cp.packed, cp.gw, cp.L, cp.n_seg,
+                                                    cp.n_seg - 1, k, v, states, st)
+                    : kata::launch_chunk_state_generic(dp, in_bf16, k, v, states, cp.n_chunks, st);
+    }
+    if (e != hipSuccess) return launch_status(e, "chunk-state kernel");
+    if (!cp.walk_sums_prefix) {
+      // exclusive prefix over segments
+      Timed t(KATA_K_SCAN, st);
+      e = run_scan(states, cp.n_seq, cp.n_seg, cp.state_elems, 1, nullptr, scan_ws, st);
+    }
+    if (e != hipSuccess) return launch_status(e, "chunk-state scan");
+  }
+  {
+    Timed t(KATA_K_CHUNK_OUTPUT, st);
+    const float* pre = one_segment ? nullptr : states;
+    const bool sum_prefix = cp.walk_sums_prefix != 0;
+    e = cp.fast32 ? kata::launch_chunk_output32(dp, out_bf16, cp.L, cp.n_seg, q, k, v, o, den,
+                                                pre, sum_prefix, st)
+        : cp.fast ? kata::launch_chunk_output_fast(dp, cp.packed, cp.gw, out_bf16, cp.L,
+                                                   cp.n_seg, q, k, v, o, den, pre, sum_prefix, st)
+                : kata::launch_chunk_output_generic(dp, in_bf16, out_bf16, q, k, v, o, den,
+                                                    states, cp.n_chunks, st);
+  }
+  return launch_status(e, "chunk-output kernel");
+}
+
 }  // namespace
 
 extern "C" {
@@ -275,44 +322,34 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
     return set_error(KATA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
   if ((s = check_device()) != KATA_OK) return s;
-  const kata::DevProblem dp = to_dev(pr);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const bool in_bf16 = pr->in_dtype == KATA_BF16, out_bf16 = pr->out_dtype == KATA_BF16;
-  float* states = reinterpret_cast<float*>(workspace);
-  char* scan_ws = reinterpret_cast<char*>(workspace) + cp.states_bytes;
-  hipError_t e;
-  // One segment per sequence (the sequential inter-chunk form): every walk starts from a zero
-  // prefix, so no segment state or scan is needed.
-  const bool one_segment = cp.fast && cp.n_seg == 1;
-  if (!one_segment) {
-    {
-      Timed t(KATA_K_CHUNK_STATE, st);
-      // the last segment's state enters no prefix
-      e = cp.fast32 ? kata::launch_chunk_state32(dp, cp.L, cp.n_seg, cp.n_seg - 1, k, v, states, st)
-          : cp.fast ? kata::launch_chunk_state_fast(dp, cp.packed, cp.gw, cp.L, cp.n_seg,
-                                                    cp.n_seg - 1, k, v, states, st)
-                    : kata::launch_chunk_state_generic(dp, in_bf16, k, v, states, cp.n_chunks, st);
-    }
-    if (e != hipSuccess) return launch_status(e, "chunk-state kernel");
-    if (!cp.walk_sums_prefix) {
-      // exclusive prefix over segments
-      Timed t(KATA_K_SCAN, st);
-      e = run_scan(states, cp.n_seq, cp.n_seg, cp.state_elems, 1, nullptr, scan_ws, st);
-    }
-    if (e != hipSuccess) return launch_status(e, "chunk-state scan");
+  if (!cp.halves) return run_chunked(pr, cp, q, k, v, o, den, workspace, st);
+  // p = 32 KATA-Mg: two p = 16 passes over the coordinate halves (each with g / 2 groups) into
+  // fp32 temporaries, then o = (o_0 D_0 + o_1 D_1) / (D_0 + D_1 - eps)
+  char* ws = reinterpret_cast<char*>(workspace);
+  const size_t pass_ws = cp.ws_bytes - 2 * (cp.half_out_bytes + cp.half_den_bytes);
+  float* oj[2] = {reinterpret_cast<float*>(ws + pass_ws),
+                  reinterpret_cast<float*>(ws + pass_ws + cp.half_out_bytes)};
+  float* dj[2] = {reinterpret_cast<float*>(ws + pass_ws + 2 * cp.half_out_bytes),
+                  reinterpret_cast<float*>(ws + pass_ws + 2 * cp.half_out_bytes +
+                                           cp.half_den_bytes)};
+  for (int j = 0; j < 2; ++j) {
+    kata_problem half = *pr;
+    half.p = 16;
+    half.groups = (pr->groups <= 1 ? 1 : pr->groups) / 2;
+    half.out_dtype = KATA_F32;
+    half.so[2] = pr->dv;
+    half.so[1] = int64_t(pr->H) * pr->dv;
+    half.so[0] = int64_t(pr->T) * half.so[1];
+    const __bf16* qh = static_cast<const __bf16*>(q) + 16 * j;   // coordinates 16j .. 16j + 15
+    const __bf16* kh = static_cast<const __bf16*>(k) + 16 * j;
+    if ((s = run_chunked(&half, cp, qh, kh, v, oj[j], dj[j], workspace, st)) != KATA_OK)
+      return s;
   }
-  {
-    Timed t(KATA_K_CHUNK_OUTPUT, st);
-    const float* pre = one_segment ? nullptr : states;
-    const bool sum_prefix = cp.walk_sums_prefix != 0;
-    e = cp.fast32 ? kata::launch_chunk_output32(dp, out_bf16, cp.L, cp.n_seg, q, k, v, o, den,
-                                                pre, sum_prefix, st)
-        : cp.fast ? kata::launch_chunk_output_fast(dp, cp.packed, cp.gw, out_bf16, cp.L,
-                                                   cp.n_seg, q, k, v, o, den, pre, sum_prefix, st)
-                : kata::launch_chunk_output_generic(dp, in_bf16, out_bf16, q, k, v, o, den,
-                                                    states, cp.n_chunks, st);
-  }
-  return launch_status(e, "chunk-output kernel");
+  Timed t(KATA_K_CHUNK_OUTPUT, st);
+  return launch_status(kata::launch_halves_combine(to_dev(pr), pr->out_dtype == KATA_BF16,
+                                                   oj[0], dj[0], oj[1], dj[1], o, den, st),
+                       "two-pass combine");
 }
 
 size_t kata_chunk_state_scan_workspace_size(int64_t n_seq, int64_t n_chunks,
@@ -353,16 +390,16 @@ kata_status kata_chunk_state_scan(float* states, int64_t n_seq, int64_t n_chunks
 namespace {
 // The recurrent-state build always uses the direct layout: its result is the public
 // [dv + 1][p^2] state, which the sum kernel writes from direct segment states.
-kata::ChunkPlan recurrent_plan(const kata_problem* pr) {
+static kata::ChunkPlan recurrent_plan(const kata_problem* pr) {
   kata_problem d = *pr;
   d.state_layout = KATA_STATE_DIRECT;
   kata::ChunkPlan cp = kata::plan_chunked(&d, kata::chunk_fast_available());
   // the public state is the direct one: p = 32 and KATA-Mg prefill on the fp32 state kernel
-  if (cp.fast32 || cp.gw != 16) cp = kata::plan_chunked(&d, false);
+  if (cp.fast32 || cp.gw != 16 || cp.halves) cp = kata::plan_chunked(&d, false);
   return cp;
 }
 
-kata_status check_state(const float* state) {
+static kata_status check_state(const float* state) {
   if (!state) return set_error(KATA_ERR_INVALID_ARGUMENT, "state is null");
   if (reinterpret_cast<uintptr_t>(state) % 16)
     return set_error(KATA_ERR_INVALID_ARGUMENT, "state is not 16-byte aligned");
@@ -478,7 +515,7 @@ struct BwdChunkedLayout {
   size_t states = 0, scan = 0, g = 0, e = 0, total = 0;
 };
 
-BwdChunkedLayout bwd_chunked_layout(const kata_problem* pr) {
+static BwdChunkedLayout bwd_chunked_layout(const kata_problem* pr) {
   auto r256 = [](size_t b) { return (b + 255) & ~size_t(255); };
   BwdChunkedLayout L;
   L.n_seq = int64_t(pr->B) * pr->H;

@@ -142,6 +142,25 @@ ScanPlan plan_scan(int64_t n_seq, int64_t n, int64_t elems) {
 }
 
 ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
+  // p = 32 KATA-Mg on the MFMA kernels: the groups (16, 8 or 4 coordinates) lie inside the two
+  // 16-coordinate halves, so a_ts is the sum of the halves' grouped scores; each half is a
+  // p = 16 problem with g / 2 groups, run by the p = 16 kernels, and the two passes' numerators
+  // and denominators are added.
+  const int g32 = pr->groups <= 1 ? 1 : pr->groups;
+  if (fast_available && pr->p == 32 && (g32 == 2 || g32 == 4 || g32 == 8) &&
+      pr->in_dtype == KATA_BF16 && pr->dv == 64 && pr->chunk == 64) {
+    kata_problem half = *pr;
+    half.p = 16;
+    half.groups = g32 / 2;
+    half.out_dtype = KATA_F32;
+    ChunkPlan cp = plan_chunked(&half, fast_available);
+    const size_t n_tok = size_t(pr->B) * size_t(pr->T) * size_t(pr->H);
+    cp.halves = 1;
+    cp.half_out_bytes = round256(n_tok * size_t(pr->dv) * 4);
+    cp.half_den_bytes = round256(n_tok * 4);
+    cp.ws_bytes = round256(cp.ws_bytes) + 2 * (cp.half_out_bytes + cp.half_den_bytes);
+    return cp;
+  }
   ChunkPlan cp;
   cp.n_chunks = pr->T / pr->chunk;
   cp.n_seq = int64_t(pr->B) * pr->H;

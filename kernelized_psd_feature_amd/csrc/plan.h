@@ -25,6 +25,11 @@ struct ChunkPlan {
   int n_chunks = 0;           // N_c = T / C per (b, h)
   int n_seg = 0;              // ceil(N_c / L)
   int walk_sums_prefix = 0;   // 1: each walk adds the earlier segments' states itself, no scan
+  // 1: p = 32 KATA-Mg (g >= 2) as two p = 16 passes over the coordinate halves (every other
+  // field then describes one pass); the workspace adds the passes' fp32 outputs and D_t
+  int halves = 0;
+  size_t half_out_bytes = 0;  // one pass's fp32 output [B][T][H][dv], rounded up to 256
+  size_t half_den_bytes = 0;  // one pass's D_t [B][T][H], rounded up to 256
   int dv_split = 1;           // workgroups sharing one segment, each owning dv / dv_split columns
   int64_t n_seq = 0;          // B * H
   int64_t state_elems = 0;    // floats in one segment state: p^2 (dv + 1)

@@ -6,6 +6,8 @@ import ctypes
 import math
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -339,3 +341,15 @@ def test_chunked_plan_reports_segments_and_scan_depth():
     assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), None) == INVALID
     assert lib.kata_fwd_chunked_plan(ctypes.byref(_problem(T=100)), ctypes.byref(out)) == \
         UNSUPPORTED
+
+
+def test_library_exports_only_the_declared_c_functions():
+    # helpers stay internal: every exported C (unmangled) function is one of the header's
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", K.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.split()[1:2] == ["T"]}
+    c_names = {n for n in exported if not n.startswith("_Z")}
+    assert c_names <= set(_declared_functions()), sorted(c_names - set(_declared_functions()))

@@ -27,6 +27,10 @@ def test_flops_per_head_token():
     # chunked: 4 p^2 (d_v + 1) + (C + 1)(p + d_v + 1) + 2 p^2 + 2 p^2 (d_v + 1) / C + d_v
     assert bench.chunked_flops_per_token(16, 64, 64) == 66560 + 5265 + 512 + 520 + 64 == 72921
     assert bench.chunked_flops_per_token(32, 64, 64) == 276737
+    # KATA-Mg: g groups keep n = p^2 / g features (g = 2 at p = 16: 128)
+    n = 128
+    assert bench.chunked_flops_per_token(16, 64, 64, groups=2) == \
+        4 * n * 65 + 65 * 81 + 2 * n + 2 * n * 65 // 64 + 64
     # quadratic: (T + 1)(p + d_v + 1) + d_v
     assert bench.quadratic_flops_per_token(16, 64, 2048) == 2049 * 81 + 64 == 166033
 

@@ -1115,3 +1115,27 @@ def test_decode_state_past_two_to_the_31_elements():
     say(f"decode, {B * H} sequences, state {state.numel():.3e} values: o max-abs {worst_o:.3e}, "
         f"state max-abs {worst_s:.3e}")
     assert worst_o <= TOL[w.dtype] and worst_s <= 1e-3
+
+
+@pytest.mark.parametrize("g,seg,out", [(2, 0, "fp32"), (2, 3, "fp32"), (4, 5, "bf16"), (8, 32, "fp32")])
+def test_p32_kata_mg_chunked_runs_as_two_p16_passes(g, seg, out):
+    # p = 32 KATA-Mg on the MFMA kernels: the groups lie in the two 16-coordinate halves, each
+    # half runs the p = 16 pipeline (segment states, scan or summed prefixes, walk) and the
+    # passes' numerators and denominators are added.  seg_chunks 3, 5, 32 at T = 2048: 11
+    # segments (scan), 7 (summed prefixes), 1 (walk only).  Every element against the oracle.
+    w = W.WORKLOADS[3]
+    q, k, v = W.make_inputs(w, 83, T=2048, B=1, H=3)
+    qg, kg, vg = _to_gpu(q, k, v)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    K.timing_begin()
+    o, d = K.fwd_chunked(qg, kg, vg, groups=g, seg_chunks=seg, out_dtype=od, return_den=True)
+    t = K.timing_end()
+    assert t["chunk_output"][0] == 3                 # two walks and the combination
+    ref, dref = O.closed_form(_np(q), _np(k), _np(v), groups=g)
+    err = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
+    say(f"p32 KATA-Mg g={g} seg_chunks={seg} {out}: max-abs {err:.3e}")
+    assert err <= TOL[w.dtype]
+    np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=1e-2)
+    if out == "bf16":   # the rounded fp32 result
+        of = K.fwd_chunked(qg, kg, vg, groups=g, seg_chunks=seg)
+        assert torch.equal(o, of.to(torch.bfloat16))
