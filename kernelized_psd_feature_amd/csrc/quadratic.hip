@@ -1,6 +1,7 @@
 // Flash-style O(T^2) forward for gfx950 on bf16 MFMA (p = 16 with KATA-Mg group widths 16, 8,
-// 4; p = 32), d_v = 64.  (gist.science "Technische Samenvatting" section 2.3: the quadratic
-// operating point never forms the feature state; section 2.2: a_ts = (q_t . k_s)^2.)
+// 4; p = 32 with group widths 32, 16, 8, 4), d_v = 64.  (gist.science "Technische
+// Samenvatting" section 2.3: the quadratic operating point never forms the feature state;
+// section 2.2: a_ts = (q_t . k_s)^2.)
 //
 //   o_t = sum_{s<=t} a_ts v_s / (eps + sum_{s<=t} a_ts)
 //
