@@ -1139,3 +1139,55 @@ def test_p32_kata_mg_chunked_runs_as_two_p16_passes(g, seg, out):
     if out == "bf16":   # the rounded fp32 result
         of = K.fwd_chunked(qg, kg, vg, groups=g, seg_chunks=seg)
         assert torch.equal(o, of.to(torch.bfloat16))
+
+
+def _random_cases(n, seed):
+    """Seeded random problems at small sizes: even cases take the MFMA kernels' shapes (bf16,
+    d_v = 64, chunk 64, p = 16 or 32, every KATA-Mg group count they take), odd ones range
+    over the ABI (p 8/16/32, d_v 16/64, bf16/fp32, chunk 16/32/64, any dividing group count).
+    Also random B, H, T (ragged for the quadratic form), segment length, state layout and
+    output dtype."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        if i % 2 == 0:
+            p, dv, bf16, chunk = int(rng.choice([16, 32])), 64, True, 64
+            g = int(rng.choice([1, 2, 4] if p == 16 else [1, 2, 4, 8]))
+            T = 64 * int(rng.integers(1, 17))
+        else:
+            p, dv = int(rng.choice([8, 16, 32])), int(rng.choice([16, 64]))
+            bf16, chunk = bool(rng.integers(2)), int(rng.choice([16, 32, 64]))
+            g = int(rng.choice([d for d in (1, 2, 4, 8) if p % d == 0]))
+            T = chunk * int(rng.integers(1, 9))
+        cases.append(dict(p=p, dv=dv, dtype=torch.bfloat16 if bf16 else torch.float32, g=g,
+                          chunk=chunk, T=T, Tq=T + int(rng.integers(0, chunk)),
+                          B=int(rng.integers(1, 3)), H=int(rng.integers(1, 5)),
+                          seg=int(rng.choice([0, 0, 1, 2, 3, 5, T // chunk])),
+                          state=str(rng.choice(["packed", "direct"])),
+                          out=torch.bfloat16 if (bf16 and rng.integers(3) == 0) else torch.float32))
+    return cases
+
+
+@pytest.mark.parametrize("i,case", list(enumerate(_random_cases(24, 2026))))
+def test_random_problems_against_oracle(i, case):
+    # every form on seeded random problems: whichever kernels the library picks (MFMA or fp32,
+    # summed or scanned prefixes, two p = 16 passes) must match the oracle everywhere
+    c = case
+    w = W.Workload(900 + i, f"random{i}", B=c["B"], H=c["H"], T=c["Tq"], p=c["p"], dv=c["dv"],
+                   chunk=c["chunk"], dtype=c["dtype"])
+    q, k, v = W.make_inputs(w, i)
+    tol = TOL[c["dtype"]] if c["out"] == torch.float32 else 2e-2
+    ref, dref = O.closed_form(_np(q), _np(k), _np(v), groups=c["g"])
+    qg, kg, vg = _to_gpu(q, k, v)
+    o, d = K.fwd_quadratic(qg, kg, vg, groups=c["g"], out_dtype=c["out"], return_den=True)
+    errq = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
+    T = c["T"]
+    sl = (slice(None), slice(0, T))
+    o2, d2 = K.fwd_chunked(qg[sl].contiguous(), kg[sl].contiguous(), vg[sl].contiguous(),
+                           chunk=c["chunk"], seg_chunks=c["seg"], state=c["state"],
+                           groups=c["g"], out_dtype=c["out"], return_den=True)
+    errc = float((o2.cpu().double() - torch.from_numpy(ref[:, :T])).abs().max())
+    say(f"random {i} {c}: quadratic {errq:.2e}, chunked {errc:.2e}")
+    assert errq <= tol and errc <= tol
+    np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=1e-2)
+    np.testing.assert_allclose(d2.cpu().double().numpy(), dref[:, :T], rtol=1e-2)
