@@ -173,10 +173,11 @@ struct Rows32 {
   }
 };
 
-// S[slot] += Phi(K)^T V over one staged chunk; Z += K^T K (all four 16 x 16 tiles) if with_z.
+// S[slot] += Phi(K)^T V over one staged chunk; Z += K^T K: all four 16 x 16 tiles (z = 4),
+// tile (z >> 1, z & 1) alone (z = 0 .. 3), or none (z < 0).
 template <class TL>
 __device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, f32x4 (&S)[kSlots][4],
-                                         f32x4 (&Z)[2][2], int w, int lane, bool with_z) {
+                                         f32x4 (&Z)[2][2], int w, int lane, int z) {
 #pragma unroll 1
   for (int m = 0; m < 2; ++m) {
     bf16x8 vb[4];
@@ -189,12 +190,20 @@ __device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, f32x4 (
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) S[sl][nt] = mfma32(a, vb[nt], S[sl][nt]);
     }
-    if (with_z) {
+    if (z == 4) {
       const bf16x8 k0 = kcol(tl, 0, m, lane), k1 = kcol(tl, 1, m, lane);
       Z[0][0] = mfma32(k0, k0, Z[0][0]);
       Z[0][1] = mfma32(k0, k1, Z[0][1]);
       Z[1][0] = mfma32(k1, k0, Z[1][0]);
       Z[1][1] = mfma32(k1, k1, Z[1][1]);
+    } else if (z >= 0) {                           // wave-uniform
+      const int mi = z >> 1, kj = z & 1;
+      const bf16x8 a = kcol(tl, mi, m, lane), bb = kcol(tl, kj, m, lane);
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+          if (x == mi && y == kj) Z[x][y] = mfma32(a, bb, Z[x][y]);
     }
   }
 }
@@ -246,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
   }
   __syncthreads();
   for (int c = 0; c < nc; ++c) {
-    update32(tl[c & 1], rw, S, Z, w, lane, w == 0);
+    update32(tl[c & 1], rw, S, Z, w, lane, w == 0 ? 4 : -1);
     if (c + 1 < nc) store_state32(st, tl[(c + 1) & 1], tid);   // buffer read last iteration
     if (c + 2 < nc) {
       p.next();
@@ -278,7 +287,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
 struct __align__(16) Walk32Lds {
   Tiles32 tl;
   uint4 Sb[kSteps][4][64];        // S_{<c} as bf16 B operands: [K step][value tile][lane]
+  uint2 Zb[4][2][64];             // Z_{<c} tiles (mi, kj) = 2 mi + kj as bf16 hi / lo A operands
   f32x4 xr[kWaves][2][64];        // readout partials handed to the other wave of a token group
+  float zx[kWaves][64];           // q^T Z q halves handed to the other wave of a token group
   unsigned char dg[4 * kSteps][2];   // double group -> (a, J)
 };
 
@@ -338,6 +349,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     sm.dg[tid][1] = (unsigned char)(4 * J);
   }
 
+  // Z: wave w < 4 keeps tile (w >> 1, w & 1) and publishes it split into bf16 hi + lo
+  const int zt = w < 4 ? w : -1;
   auto publish = [&]() {
 #pragma unroll
     for (int sl = 0; sl < kSlots; ++sl) {
@@ -350,6 +363,22 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
         for (int r = 0; r < 4; ++r) x[r] = (__bf16)S[sl][nt][r];
         reinterpret_cast<uint2*>(&sm.Sb[t >> 1][nt][lane])[t & 1] = __builtin_bit_cast(uint2, x);
       }
+    }
+    if (zt >= 0) {
+      f32x4 zr = zero4();
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) zr = (2 * x + y == zt) ? Z[x][y] : zr;
+      s16x4 zhi, zlo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const __bf16 hi = (__bf16)zr[r];
+        zhi[r] = __builtin_bit_cast(short, hi);
+        zlo[r] = __builtin_bit_cast(short, (__bf16)(zr[r] - (float)hi));
+      }
+      sm.Zb[zt][0][lane] = __builtin_bit_cast(uint2, zhi);
+      sm.Zb[zt][1][lane] = __builtin_bit_cast(uint2, zlo);
     }
   };
 
@@ -404,42 +433,32 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
 
     // ---- inter-chunk denominator q^T Z_{<c} q on MFMA (Z = hi + lo in bf16) ----
     // Z tile (mi, kj)'s accumulator layout is, Z being symmetric, the A operand of output rows
-    // 16 kj.. and K rows 16 mi.. of y = Z q.
+    // 16 kj.. and K rows 16 mi.. of y = Z q.  The two waves of a token group take the output
+    // rows of kj = ch each and add their halves after the readout's exchange.
     float zq = 0.f;
     {
       s16x4 qb[2];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
         qb[mi] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2*>(&tl.Qs[t][16 * mi + 4 * g]));
+      f32x4 y = zero4();
 #pragma unroll
-      for (int kj = 0; kj < 2; ++kj) {
-        f32x4 y = zero4();
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-          s16x4 zhi, zlo;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const __bf16 hi = (__bf16)Z[mi][kj][r];
-            zhi[r] = __builtin_bit_cast(short, hi);
-            zlo[r] = __builtin_bit_cast(short, (__bf16)(Z[mi][kj][r] - (float)hi));
-          }
-          y = mfma16(zhi, qb[mi], y);
-          y = mfma16(zlo, qb[mi], y);
-        }
-        // y[r] = (Z q_t)[16 kj + 4 g + r]
-        const uint2 qq = __builtin_bit_cast(uint2, qb[kj]);
-        zq = fmaf(bf_lo(qq.x), y[0], zq);
-        zq = fmaf(bf_hi(qq.x), y[1], zq);
-        zq = fmaf(bf_lo(qq.y), y[2], zq);
-        zq = fmaf(bf_hi(qq.y), y[3], zq);
+      for (int mi = 0; mi < 2; ++mi) {
+        y = mfma16(__builtin_bit_cast(s16x4, sm.Zb[2 * mi + ch][0][lane]), qb[mi], y);
+        y = mfma16(__builtin_bit_cast(s16x4, sm.Zb[2 * mi + ch][1][lane]), qb[mi], y);
       }
+      // y[r] = (Z q_t)[16 ch + 4 g + r]
+      const uint2 qq = __builtin_bit_cast(uint2, ch ? qb[1] : qb[0]);
+      zq = fmaf(bf_lo(qq.x), y[0], zq);
+      zq = fmaf(bf_hi(qq.x), y[1], zq);
+      zq = fmaf(bf_lo(qq.y), y[2], zq);
+      zq = fmaf(bf_hi(qq.y), y[3], zq);
     }
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
     zq += __shfl_xor(zq, 16);
     zq += __shfl_xor(zq, 32);
-    const float D = pr.eps + (zq + lsum);          // D_t of token t (every lane group)
-    const float inv = 1.f / D;
+    sm.zx[w][lane] = zq;
 
     // ---- readout phi(q_t)^T S_{<c}: K steps [9 ch, 9 ch + 9) for all four value tiles ----
     f32x4 R[4] = {zero4(), zero4(), zero4(), zero4()};
@@ -471,6 +490,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) O[n][r] += own[r] + x[r];
     }
+    // both waves add the halves in the order kj = 0, 1: the same D bit for bit
+    const float zo = sm.zx[w ^ 4][lane];
+    const float D = pr.eps + ((ch ? zo + zq : zq + zo) + lsum);   // D_t of token t
+    const float inv = 1.f / D;
 
     // ---- gate and store: lane holds tokens 16 tg + 4 g + r, columns 32 ch + 16 n + l16 ----
 #pragma unroll
@@ -485,7 +508,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     orow += C * so_t;
 
     // ---- state update with this chunk ----
-    update32(tl, rw, S, Z, w, lane, true);
+    update32(tl, rw, S, Z, w, lane, zt);
     __syncthreads();                               // all reads of this chunk's tiles and Sb
     if (c + 1 < nc) {
       store32(st, tl, true, tid);
