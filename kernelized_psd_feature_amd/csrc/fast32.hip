@@ -173,8 +173,8 @@ struct Rows32 {
   }
 };
 
-// S[slot] += Phi(K)^T V over one staged chunk; Z += K^T K: all four 16 x 16 tiles (z = 4),
-// tile (z >> 1, z & 1) alone (z = 0 .. 3), or none (z < 0).
+// S[slot] += Phi(K)^T V over one staged chunk; Z += K^T K for the 16 x 16 tile
+// (z >> 1, z & 1) when z >= 0 (waves 0-3 own one tile each).
 template <class TL>
 __device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, f32x4 (&S)[kSlots][4],
                                          f32x4 (&Z)[2][2], int w, int lane, int z) {
@@ -190,13 +190,7 @@ __device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, f32x4 (
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) S[sl][nt] = mfma32(a, vb[nt], S[sl][nt]);
     }
-    if (z == 4) {
-      const bf16x8 k0 = kcol(tl, 0, m, lane), k1 = kcol(tl, 1, m, lane);
-      Z[0][0] = mfma32(k0, k0, Z[0][0]);
-      Z[0][1] = mfma32(k0, k1, Z[0][1]);
-      Z[1][0] = mfma32(k1, k0, Z[1][0]);
-      Z[1][1] = mfma32(k1, k1, Z[1][1]);
-    } else if (z >= 0) {                           // wave-uniform
+    if (z >= 0) {                                  // wave-uniform
       const int mi = z >> 1, kj = z & 1;
       const bf16x8 a = kcol(tl, mi, m, lane), bb = kcol(tl, kj, m, lane);
 #pragma unroll
@@ -255,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
   }
   __syncthreads();
   for (int c = 0; c < nc; ++c) {
-    update32(tl[c & 1], rw, S, Z, w, lane, w == 0 ? 4 : -1);
+    update32(tl[c & 1], rw, S, Z, w, lane, w < 4 ? w : -1);   // Z tile w on waves 0-3
     if (c + 1 < nc) store_state32(st, tl[(c + 1) & 1], tid);   // buffer read last iteration
     if (c + 2 < nc) {
       p.next();
@@ -271,12 +265,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
     for (int nt = 0; nt < 4; ++nt)
       *reinterpret_cast<f32x4*>(out + ((t * 4 + nt) * 64 + lane) * 4) = S[sl][nt];
   }
-  if (w == 0) {
+  if (w < 4) {
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int kj = 0; kj < 2; ++kj)
-        *reinterpret_cast<f32x4*>(out + kZOff + ((mi * 2 + kj) * 64 + lane) * 4) = Z[mi][kj];
+        if (mi * 2 + kj == w)
+          *reinterpret_cast<f32x4*>(out + kZOff + ((mi * 2 + kj) * 64 + lane) * 4) = Z[mi][kj];
   }
 }
 
