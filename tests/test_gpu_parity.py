@@ -1191,3 +1191,18 @@ def test_random_problems_against_oracle(i, case):
     assert errq <= tol and errc <= tol
     np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=1e-2)
     np.testing.assert_allclose(d2.cpu().double().numpy(), dref[:, :T], rtol=1e-2)
+
+
+@pytest.mark.parametrize("form", ["quadratic", "chunked"])
+def test_p32_kata_mg_deterministic_and_layout_independent(form):
+    # p = 32, g = 2 (the quadratic kernel's group cut; the chunked form's two p = 16 passes
+    # reading q, k at coordinate offsets): repeated calls and head-major storage (passed as a
+    # (B, T, H, D) view, output into a head-major buffer too) give the same bits
+    w = W.WORKLOADS[3]
+    q, k, v = _to_gpu(*W.make_inputs(w, 6, T=1024, B=2, H=3))
+    o1 = _run(form, q, k, v, groups=2)
+    assert torch.equal(o1, _run(form, q, k, v, groups=2))
+    qh, kh, vh = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
+    oh = torch.empty_like(o1).transpose(1, 2).contiguous().transpose(1, 2)
+    _run(form, qh, kh, vh, groups=2, out=oh)
+    assert torch.equal(o1, oh)
