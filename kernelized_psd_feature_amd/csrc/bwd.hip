@@ -12,6 +12,7 @@
 // Three kernels: prep (D_t and delta_t per row, a flash-style forward), dq (one thread per
 // query, keys streamed through LDS) and dk/dv (one thread per key, queries streamed).
 #include "device.h"
+#include "group_scores.h"
 
 namespace kata {
 namespace {
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(
     const int smax = min(kRows, kend - s0);
     for (int s = 0; s < smax; ++s) {
       if (s0 + s <= t) {
-        const float a = grouped_square(qr, ks[s], grp);
+        const float a = score_square(qr, ks[s], grp);
         l += a;
 #pragma unroll
         for (int j = 0; j < DP; ++j) acc[j] = fmaf(a, vs[s][part * DP + j], acc[j]);
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     for (int s = 0; s < smax; ++s) {
       if (live && s0 + s <= t) {
         float sc[P], gv = 0.f;
-        grouped_dots(qr, ks[s], grp, sc);
+        score_dots(qr, ks[s], grp, sc);
 #pragma unroll
         for (int d = 0; d < DV; ++d) gv = fmaf(g[d], vs[s][d], gv);
         const float G = (gv - dl) * invD;
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
     for (int r = 0; r < rmax; ++r) {
       if (live && q0 + r >= s) {
         float sc[P], gv = 0.f;
-        const float a = grouped_dots(kr, qs[r], grp, sc);
+        const float a = score_dots(kr, qs[r], grp, sc);
 #pragma unroll
         for (int d = 0; d < DV; ++d) gv = fmaf(gs[r][d], vr[d], gv);
         const float G = (gv - dls[r]) * invD[r];

@@ -19,6 +19,8 @@
 // Every kernel takes one chunk per workgroup, 256 threads = 64 rows (tokens) x 4 parts; part
 // m owns the value columns [m dv/4, (m+1) dv/4) of every contraction over dv, and the partial
 // p-vectors of the four parts are summed through LDS at the end.
+#include <type_traits>
+
 #include "device.h"
 #include "phi_product.h"
 
@@ -142,15 +144,29 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_dq_kernel(
   if (live) {
     // this chunk: sum_{s<=t} (q . k_s) G_ts k_s, G_ts split over the parts' value columns
     const Groups grp = make_groups(P, pr.gs);
-    for (int s = 0; s <= row; ++s) {
-      float sc[P];
-      grouped_dots(qr, ks[s], grp, sc);
-      float G = part ? 0.f : -et;
+    // one feature group (uniform): sc[i] is the one dot product, and sc[i] * G is one product
+    auto intra = [&](auto one_group) {
+      for (int s = 0; s <= row; ++s) {
+        float G = part ? 0.f : -et;
 #pragma unroll
-      for (int j = 0; j < DP; ++j) G = fmaf(gr[j], vs[s][part * DP + j], G);
+        for (int j = 0; j < DP; ++j) G = fmaf(gr[j], vs[s][part * DP + j], G);
+        if constexpr (decltype(one_group)::value) {
+          float d = 0.f;
 #pragma unroll
-      for (int i = 0; i < P; ++i) acc[i] = fmaf(sc[i] * G, ks[s][i], acc[i]);
-    }
+          for (int i = 0; i < P; ++i) d = fmaf(qr[i], ks[s][i], d);
+          const float dg = d * G;
+#pragma unroll
+          for (int i = 0; i < P; ++i) acc[i] = fmaf(dg, ks[s][i], acc[i]);
+        } else {
+          float sc[P];
+          grouped_dots(qr, ks[s], grp, sc);
+#pragma unroll
+          for (int i = 0; i < P; ++i) acc[i] = fmaf(sc[i] * G, ks[s][i], acc[i]);
+        }
+      }
+    };
+    if (grp.start == 1u) intra(std::true_type{});
+    else intra(std::false_type{});
   }
   __syncthreads();                               // every read of the staged state is done
   reduce_parts<P>(acc, red, row, part);
@@ -275,18 +291,35 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_dkdv_kernel(
   if (live) {
     // this chunk: t >= s
     const Groups grp = make_groups(P, pr.gs);
-    for (int tt = row; tt < C; ++tt) {
-      float sc[P];
-      const float a = grouped_dots(kr, qs[tt], grp, sc);
-      float G = part ? 0.f : -es[tt];
+    // one feature group (uniform): sc[i] is the one dot product, and sc[i] * G is one product
+    auto intra = [&](auto one_group) {
+      for (int tt = row; tt < C; ++tt) {
+        float sc[P], a, d = 0.f;
+        if constexpr (decltype(one_group)::value) {
 #pragma unroll
-      for (int j = 0; j < DP; ++j) {
-        G = fmaf(gs[tt][part * DP + j], vr[j], G);
-        dvacc[j] = fmaf(a, gs[tt][part * DP + j], dvacc[j]);
+          for (int i = 0; i < P; ++i) d = fmaf(kr[i], qs[tt][i], d);
+          a = fmaf(d, d, 0.f);
+        } else {
+          a = grouped_dots(kr, qs[tt], grp, sc);
+        }
+        float G = part ? 0.f : -es[tt];
+#pragma unroll
+        for (int j = 0; j < DP; ++j) {
+          G = fmaf(gs[tt][part * DP + j], vr[j], G);
+          dvacc[j] = fmaf(a, gs[tt][part * DP + j], dvacc[j]);
+        }
+        if constexpr (decltype(one_group)::value) {
+          const float dg = d * G;
+#pragma unroll
+          for (int i = 0; i < P; ++i) acc[i] = fmaf(dg, qs[tt][i], acc[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < P; ++i) acc[i] = fmaf(sc[i] * G, qs[tt][i], acc[i]);
+        }
       }
-#pragma unroll
-      for (int i = 0; i < P; ++i) acc[i] = fmaf(sc[i] * G, qs[tt][i], acc[i]);
-    }
+    };
+    if (grp.start == 1u) intra(std::true_type{});
+    else intra(std::false_type{});
     float* dvp = dv + row_off(pr.sv, b, s, h) + part * DP;
 #pragma unroll
     for (int j = 0; j < DP; ++j) dvp[j] = dvacc[j];

@@ -9,6 +9,7 @@
 #include <algorithm>
 
 #include "device.h"
+#include "group_scores.h"
 #include "phi_product.h"
 
 namespace kata {
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void quadratic_generic_kernel(
     const int smax = min(kRows, kend - s0);
     for (int s = 0; s < smax; ++s) {
       if (s0 + s <= t) {                       // causal mask by selection
-        const float a = grouped_square(qr, ks[s], grp);
+        const float a = score_square(qr, ks[s], grp);
         l += a;
 #pragma unroll
         for (int j = 0; j < DP; ++j) acc[j] = fmaf(a, vs[s][part * DP + j], acc[j]);
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void chunk_output_generic_kernel(
   float l = 0.f;
   const Groups grp = make_groups(P, pr.gs);
   for (int s = 0; s <= row; ++s) {
-    const float a = grouped_square(qr, ks[s], grp);
+    const float a = score_square(qr, ks[s], grp);
     l += a;
 #pragma unroll
     for (int j = 0; j < DP; ++j) acc[j] = fmaf(a, vs[s][part * DP + j], acc[j]);
