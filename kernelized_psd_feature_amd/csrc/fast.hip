@@ -47,8 +47,8 @@ struct __align__(16) TilesT {
 using Tiles = TilesT<false>;
 
 // One thread's share of a chunk's global loads, held in registers while the previous chunk
-// is computed.  Waves 0-1 carry half a q row each (token = lane, half = wave), waves 2-3 half
-// a k row; every thread carries 16 bytes of two consecutive v rows.
+// is computed.  Waves 0-1 carry half a q row each, waves 2-3 half a k row (which row and half:
+// qk_piece); every thread carries 16 bytes of two consecutive v rows.
 struct Stage {
   uint4 qk;
   uint4 v0, v1;
@@ -65,15 +65,30 @@ struct StagePtrs {
   }
 };
 
+// The q or k row of the chunk and the 16-byte half of it that thread tid stages.  With q (the
+// walk), lanes 2i and 2i+1 take the two halves of row 32 (w & 1) + i, so one load touches 32
+// rows whole (in (B,T,H,D) order every 32-byte row sits in its own cache line) rather than half
+// of each of 64 rows.  Without q (the state pass: k on waves 2-3) each lane takes one row and
+// the wave picks the half, which measured faster there.
+struct QkPiece {
+  int row, half;
+};
+__device__ __forceinline__ QkPiece qk_piece(int tid, bool with_q) {
+  return with_q ? QkPiece{32 * ((tid >> 6) & 1) + ((tid & 63) >> 1), tid & 1}
+                : QkPiece{tid & 63, (tid >> 6) & 1};
+}
+
 __device__ __forceinline__ StagePtrs stage_ptrs(const DevProblem& pr, const __bf16* q,
                                                 const __bf16* k, const __bf16* v, int b, int h,
                                                 int tok0, bool with_q, int tid, int dir = 1) {
   StagePtrs sp;
-  const int w = tid >> 6, lane = tid & 63;
+  const int w = tid >> 6;
+  const QkPiece pc = qk_piece(tid, with_q);        // q on waves 0-1, k on waves 2-3
+  const int row = pc.row, half = pc.half;
   if (w < 2)
-    sp.qk = with_q ? q + row_off(pr.sq, b, tok0 + lane, h) + 8 * w : nullptr;
+    sp.qk = with_q ? q + row_off(pr.sq, b, tok0 + row, h) + 8 * half : nullptr;
   else
-    sp.qk = k + row_off(pr.sk, b, tok0 + lane, h) + 8 * (w - 2);
+    sp.qk = k + row_off(pr.sk, b, tok0 + row, h) + 8 * half;
   sp.qk_step = (long long)dir * C * (w < 2 ? pr.sq[1] : pr.sk[1]);
   const int a = tid >> 3, c8 = tid & 7;
   sp.v0 = v + row_off(pr.sv, b, tok0 + 2 * a, h) + 8 * c8;
@@ -90,25 +105,26 @@ __device__ __forceinline__ void stage_load(Stage& st, const StagePtrs& sp, long 
 template <bool kPacked>
 __device__ __forceinline__ void stage_store(const Stage& st, TilesT<kPacked>& tl, bool with_q,
                                             int tid) {
-  const int w = tid >> 6, lane = tid & 63;
+  const int w = tid >> 6;
+  const QkPiece pc = qk_piece(tid, with_q);
+  const int row = pc.row, half = pc.half;
   if (w < 2) {
     if (with_q) {
-      *reinterpret_cast<uint2*>(&tl.Qs[lane][8 * w]) = uint2{st.qk.x, st.qk.y};
-      *reinterpret_cast<uint2*>(&tl.Qs[lane][8 * w + 4]) = uint2{st.qk.z, st.qk.w};
+      *reinterpret_cast<uint2*>(&tl.Qs[row][8 * half]) = uint2{st.qk.x, st.qk.y};
+      *reinterpret_cast<uint2*>(&tl.Qs[row][8 * half + 4]) = uint2{st.qk.z, st.qk.w};
     }
   } else {
-    const int half = w - 2;
-    *reinterpret_cast<uint2*>(&tl.Ks[lane][8 * half]) = uint2{st.qk.x, st.qk.y};
-    *reinterpret_cast<uint2*>(&tl.Ks[lane][8 * half + 4]) = uint2{st.qk.z, st.qk.w};
+    *reinterpret_cast<uint2*>(&tl.Ks[row][8 * half]) = uint2{st.qk.x, st.qk.y};
+    *reinterpret_cast<uint2*>(&tl.Ks[row][8 * half + 4]) = uint2{st.qk.z, st.qk.w};
     const uint32_t wd[4] = {st.qk.x, st.qk.y, st.qk.z, st.qk.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float lo = bf_lo(wd[e]), hi = bf_hi(wd[e]);
-      tl.KT[8 * half + 2 * e][lane] = lo;
-      tl.KT[8 * half + 2 * e + 1][lane] = hi;
+      tl.KT[8 * half + 2 * e][row] = lo;
+      tl.KT[8 * half + 2 * e + 1][row] = hi;
       if (kPacked) {
-        tl.KT[P + 8 * half + 2 * e][lane] = 2.f * lo;       // exact
-        tl.KT[P + 8 * half + 2 * e + 1][lane] = 2.f * hi;
+        tl.KT[P + 8 * half + 2 * e][row] = 2.f * lo;       // exact
+        tl.KT[P + 8 * half + 2 * e + 1][row] = 2.f * hi;
       }
     }
   }
@@ -362,13 +378,13 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
 // the chunk's own state is added.  One workgroup per (segment, head, batch) (SegGrid).
 //   Each wave owns some state tiles (fp32, in registers, as in the state kernel) and the
 //   chunk's tokens [16 w, 16 w + 16).  Once per chunk every wave publishes its state tiles in
-//   LDS as bf16 B operands; each wave then reads out its own tokens over all state rows, so no
+//   LDS as bf16 MFMA operands; each wave then reads out its own tokens over all state rows, so no
 //   partial outputs cross waves.
 // ==========================================================================================
 template <bool kPacked, int GW>
 struct __align__(16) WalkLds {
   TilesT<kPacked> tl;
-  uint4 Sb[Layout<kPacked, GW>::kSteps][4][64];   // S_{<c} as B operands: [K step][value tile][lane]
+  uint4 Sb[Layout<kPacked, GW>::kSteps][4][64];   // S_{<c} as MFMA operands: [K step][value tile][lane]
   float den[C];                               // D_t of the chunk's tokens
   float inv[C];                               // 1 / D_t
 };
@@ -441,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     }
   }
 
-  // publish this wave's state tiles as bf16 B operands: tile t fills slots 4 (t & 1) .. +3
+  // publish this wave's state tiles as bf16 MFMA operands: tile t fills slots 4 (t & 1) .. +3
   // of K step t >> 1 (slot r' of lane group g <-> row 4g + r'%4 of tile 2(t>>1) + r'/4)
   auto publish = [&]() {
 #pragma unroll
@@ -465,8 +481,9 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
   publish();
   __syncthreads();
 
-  // output row pointer of this lane's first token (16w + 4g) in the first chunk
-  Tout* orow = o + row_off(pr.so, b, c0 * C + 16 * w + 4 * g, h) + l16;
+  // output pointer of this lane's first store in the first chunk: token 16w + 8 (lane / 32),
+  // column lane % 32
+  Tout* orow = o + row_off(pr.so, b, c0 * C + 16 * w + 8 * (lane >> 5), h) + (lane & 31);
   const long long so_t = pr.so[1];
 
   for (int c = 0; c < nc; ++c) {
@@ -557,14 +574,24 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
         O[nt] = mfma32(a, __builtin_bit_cast(bf16x8, sm.Sb[kk][nt][lane]), O[nt]);
     }
 
-    // ---- gate and store this wave's tokens: lane holds tokens 16w + 4g + r, column 16nt + l16
+    // ---- gate and store this wave's tokens: lane holds tokens 16w + 4g + r, column 16nt + l16.
+    // Row-group swaps between column tiles 2j and 2j + 1 give each lane half a row of 32
+    // consecutive columns, so every store writes two whole 128-byte rows (fp32) instead of
+    // half rows of four tokens: the first register of a swap then holds tokens 16w + r (lanes
+    // 0-31) and 16w + 8 + r (lanes 32-63), the second tokens 16w + 4 + r and 16w + 12 + r.
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float inv = sm.inv[16 * w + 4 * g + r];
-      Tout* op = orow + r * so_t;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)   // streamed out: never re-read by this kernel
-        __builtin_nontemporal_store(cvt_out<Tout>(O[nt][r] * inv), op + 16 * nt);
+      for (int j = 0; j < 2; ++j) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(O[2 * j][r] * inv),
+                                                         __float_as_uint(O[2 * j + 1][r] * inv),
+                                                         false, false);
+        // streamed out: never re-read by this kernel
+        __builtin_nontemporal_store(cvt_out<Tout>(__uint_as_float(sw[0])), orow + r * so_t + 32 * j);
+        __builtin_nontemporal_store(cvt_out<Tout>(__uint_as_float(sw[1])),
+                                    orow + (4 + r) * so_t + 32 * j);
+      }
     }
     if (den_out && lane < 16)
       den_out[((long long)b * pr.T + tok0 + 16 * w + lane) * pr.H + h] = sm.den[16 * w + lane];
