@@ -276,7 +276,8 @@ __device__ __forceinline__ void state_update(const TL& tl, const UpdateRows<kPac
                                              f32x4 (&S)[Layout<kPacked, GW>::kSlots][4],
                                              f32x4& Z, int w, int lane, bool with_z) {
   using LY = Layout<kPacked, GW>;
-#pragma unroll 1
+  // both 32-key steps unrolled: the LDS addresses of the second become immediate offsets
+#pragma unroll
   for (int m = 0; m < 2; ++m) {
     bf16x8 vb[4];
 #pragma unroll
