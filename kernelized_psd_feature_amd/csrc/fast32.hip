@@ -178,7 +178,8 @@ struct Rows32 {
 template <class TL>
 __device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, f32x4 (&S)[kSlots][4],
                                          f32x4 (&Z)[2][2], int w, int lane, int z) {
-#pragma unroll 1
+  // both 32-key steps unrolled: the LDS addresses of the second become immediate offsets
+#pragma unroll
   for (int m = 0; m < 2; ++m) {
     bf16x8 vb[4];
 #pragma unroll
@@ -385,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
   __syncthreads();
 
   const int t = 16 * tg + l16;                 // this lane's token (fragment column / row)
-  Tout* orow = o + row_off(pr.so, b, c0 * C + 16 * tg + 4 * g, h) + 32 * ch + l16;
+  Tout* orow = o + row_off(pr.so, b, c0 * C + 16 * tg + 8 * (lane >> 5), h) + 32 * ch + (lane & 31);
   const long long so_t = pr.so[1];
 
   for (int c = 0; c < nc; ++c) {
@@ -490,13 +491,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     const float D = pr.eps + ((ch ? zo + zq : zq + zo) + lsum);   // D_t of token t
     const float inv = 1.f / D;
 
-    // ---- gate and store: lane holds tokens 16 tg + 4 g + r, columns 32 ch + 16 n + l16 ----
+    // ---- gate and store: lane holds tokens 16 tg + 4 g + r, columns 32 ch + 16 n + l16.  A
+    // row-group swap between the two column tiles gives each lane a 32-column half row, so every
+    // store writes whole 128-byte rows (fp32): the first register then holds tokens 16 tg + r
+    // (lanes 0-31) and 16 tg + 8 + r (lanes 32-63), the second 16 tg + 4 + r and 16 tg + 12 + r.
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float ir = __shfl(inv, 4 * g + r);    // token 4 g + r's 1 / D (lane 4 g + r)
-      Tout* op = orow + r * so_t;
-#pragma unroll
-      for (int n = 0; n < 2; ++n) __builtin_nontemporal_store(cvt_out<Tout>(O[n][r] * ir), op + 16 * n);
+      const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(O[0][r] * ir),
+                                                       __float_as_uint(O[1][r] * ir), false, false);
+      // streamed out: never re-read by this kernel
+      __builtin_nontemporal_store(cvt_out<Tout>(__uint_as_float(sw[0])), orow + r * so_t);
+      __builtin_nontemporal_store(cvt_out<Tout>(__uint_as_float(sw[1])), orow + (4 + r) * so_t);
     }
     if (den_out && ch == 0 && lane < 16)
       den_out[((long long)b * pr.T + tok0 + t) * pr.H + h] = D;
