@@ -141,6 +141,37 @@ ScanPlan plan_scan(int64_t n_seq, int64_t n, int64_t elems) {
   return sp;
 }
 
+// Segment length when the walks add their earlier segments' states themselves (2 ..
+// kWalkPrefixMaxSegments segments per sequence, one round of walks).  The last segment's walk
+// is the longest: L chunks of token data plus n - 1 states.  Among the segment counts that
+// still fill two thirds of the slots, take the one whose last walk moves the fewest bytes
+// (ties: the most segments).  At 8 x 16 heads x 2048 tokens (32 chunks): 4 segments of 8
+// chunks, 0.051 ms per step against 0.0525 ms for 6 of 6; at 8 x 16 x 4096 it keeps 6.  Not
+// for the p = 32 kernels: their walk is bound by its MFMAs, one workgroup per CU, and fewer
+// segments leave CUs idle (4 x 16 x 1024: 3 segments 0.058 ms, 4 segments 0.054 ms).
+static int walk_sum_segment_length(const kata_problem* pr, const ChunkPlan& cp, int64_t slots,
+                                   int L) {
+  const int64_t n0 = (cp.n_chunks + L - 1) / L;
+  if (cp.fast32 || n0 < 2 || n0 > kWalkPrefixMaxSegments || cp.n_seq * n0 > slots) return L;
+  const int64_t out_bytes = pr->out_dtype == KATA_BF16 ? 2 : 4;
+  const int64_t chunk_bytes =
+      int64_t(pr->chunk) * (2 * (2 * int64_t(pr->p) + pr->dv) + out_bytes * pr->dv);
+  const int64_t state_bytes = cp.state_elems * 4;
+  int best_L = L;
+  int64_t best = int64_t(L) * chunk_bytes + (n0 - 1) * state_bytes;
+  for (int64_t s = n0 - 1; s >= 2; --s) {
+    const int Ls = int((cp.n_chunks + s - 1) / s);
+    const int64_t n = (cp.n_chunks + Ls - 1) / Ls;
+    if (3 * cp.n_seq * n < 2 * slots) break;
+    const int64_t cost = int64_t(Ls) * chunk_bytes + (n - 1) * state_bytes;
+    if (cost < best) {
+      best = cost;
+      best_L = Ls;
+    }
+  }
+  return best_L;
+}
+
 ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
   // p = 32 KATA-Mg on the MFMA kernels: the groups (16, 8 or 4 coordinates) lie inside the two
   // 16-coordinate halves, so a_ts is the sum of the halves' grouped scores; each half is a
@@ -175,6 +206,14 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
   cp.fast32 = (cp.fast && pr->p == 32) ? 1 : 0;
   cp.gw = pr->p / g;
   if (cp.fast) {
+    cp.packed = (pr->state_layout == KATA_STATE_PACKED || cp.fast32 || g > 1) ? 1 : 0;
+    // packed: 10 tiles of 16 rows (the 136 unique (i, j) rows and 24 zero rows) x 64 columns,
+    // plus the full 16 x 16 Z; KATA-Mg at p = 16: 6 tiles (g = 2) or 4 (g = 4), the
+    // within-group pairs only; p = 32: 36 tiles (528 unique rows and 48 zero rows) and Z
+    if (cp.packed) {
+      const int tiles16 = g == 1 ? 10 : g == 2 ? 6 : 4;
+      cp.state_elems = cp.fast32 ? kState32Floats : int64_t(tiles16) * 16 * 64 + 256;
+    }
     int L = pr->seg_chunks;
     if (L == 0) {
       // With one walk per sequence filling at least two thirds of the workgroup slots of the
@@ -195,18 +234,11 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
           L = int((cp.n_chunks + seg_target - 1) / seg_target);
           if (L <= 64) break;
         }
+        L = walk_sum_segment_length(pr, cp, slots, L);
       }
     }
     if (L > cp.n_chunks) L = cp.n_chunks;
     cp.L = L;
-    cp.packed = (pr->state_layout == KATA_STATE_PACKED || cp.fast32 || g > 1) ? 1 : 0;
-    // packed: 10 tiles of 16 rows (the 136 unique (i, j) rows and 24 zero rows) x 64 columns,
-    // plus the full 16 x 16 Z; KATA-Mg at p = 16: 6 tiles (g = 2) or 4 (g = 4), the
-    // within-group pairs only; p = 32: 36 tiles (528 unique rows and 48 zero rows) and Z
-    if (cp.packed) {
-      const int tiles16 = g == 1 ? 10 : g == 2 ? 6 : 4;
-      cp.state_elems = cp.fast32 ? kState32Floats : int64_t(tiles16) * 16 * 64 + 256;
-    }
   } else {
     cp.L = 1;   // the VALU path scans every chunk state
   }

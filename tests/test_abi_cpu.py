@@ -327,6 +327,19 @@ def test_chunked_plan_reports_segments_and_scan_depth():
     assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK
     assert (out.segments, out.chunks_per_segment, out.scan_levels) == (3, 43, 0)
     assert out.walk_sums_prefix == 1
+    # short sequences: the walks' prefix reads decide the segment count.  8 x 16 heads x 2048
+    # tokens (32 chunks): 4 segments of 8 (the last walk moves 8 chunks and 3 states) rather
+    # than 6 of 6 (6 chunks and 5 states); 8 x 16 x 4096 keeps 6 segments of 11
+    for T, n_seg, L in ((2048, 4, 8), (4096, 6, 11)):
+        pr = _problem(B=8, H=16, T=T)
+        pr.state_layout = 1
+        assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK
+        assert (out.segments, out.chunks_per_segment, out.walk_sums_prefix) == (n_seg, L, 1)
+    # p = 32 (MFMA-bound walk, one workgroup per CU) keeps every slot busy: 4 x 16 x 1024
+    # stays at 4 segments of 4
+    pr = _problem(B=4, H=16, T=1024, p=32)
+    assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK
+    assert (out.segments, out.chunks_per_segment, out.walk_sums_prefix) == (4, 4, 1)
     for seg, n_seg, walk_sums in ((4, 8, 1), (3, 11, 0)):   # 32 chunks per sequence
         pr = _problem(B=1, H=2, T=2048)
         pr.seg_chunks = seg
