@@ -114,8 +114,10 @@ __device__ __forceinline__ void stage_store(const Stage& st, TilesT<kPacked>& tl
       *reinterpret_cast<uint2*>(&tl.Qs[row][8 * half + 4]) = uint2{st.qk.z, st.qk.w};
     }
   } else {
-    *reinterpret_cast<uint2*>(&tl.Ks[row][8 * half]) = uint2{st.qk.x, st.qk.y};
-    *reinterpret_cast<uint2*>(&tl.Ks[row][8 * half + 4]) = uint2{st.qk.z, st.qk.w};
+    if (with_q) {   // the row-major K tile feeds only the walk's score tiles
+      *reinterpret_cast<uint2*>(&tl.Ks[row][8 * half]) = uint2{st.qk.x, st.qk.y};
+      *reinterpret_cast<uint2*>(&tl.Ks[row][8 * half + 4]) = uint2{st.qk.z, st.qk.w};
+    }
     const uint32_t wd[4] = {st.qk.x, st.qk.y, st.qk.z, st.qk.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
