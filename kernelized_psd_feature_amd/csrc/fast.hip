@@ -390,7 +390,11 @@ struct __align__(16) WalkLds {
   uint4 Sb[Layout<kPacked, GW>::kSteps][4][64];   // S_{<c} as MFMA operands: [K step][value tile][lane]
   float den[C];                               // D_t of the chunk's tokens
   float inv[C];                               // 1 / D_t
+  uint32_t vbad[4];                           // per wave: its staged v rows hold a non-finite value
 };
+
+static_assert(sizeof(WalkLds<false, P>) <= 160 * 1024 / 3 && sizeof(WalkLds<true, P>) <= 160 * 1024 / 3,
+              "three walks per CU");
 
 template <typename Tout, bool kPacked, int GW>
 __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
@@ -477,10 +481,19 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     }
   };
 
+  // Each wave records whether the v rows it stages hold an infinity or a nan; the chunk's
+  // masked P.V step then takes the slow exact path (nonfinite_fixup in mfma_util.h).
+  auto flag_v = [&](const Stage& x) {
+    const bool bad = (nonfinite_bf16x8(x.v0) | nonfinite_bf16x8(x.v1)) != 0u;
+    const uint32_t any = __any(bad) ? 1u : 0u;
+    if (lane == 0) sm.vbad[w] = any;
+  };
+
   StagePtrs sp = stage_ptrs(pr, q, k, v, b, h, c0 * C, true, tid);
   Stage st;
   stage_load(st, sp, sv_t);
   stage_store(st, tl, true, tid);
+  flag_v(st);
   publish();
   __syncthreads();
 
@@ -496,6 +509,8 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
       stage_load(st, sp, sv_t);
     }
     const int t = 16 * w + l16;                  // this lane's token (fragment column / row)
+    const uint4 vb4 = *reinterpret_cast<const uint4*>(sm.vbad);
+    const bool vbad = __builtin_amdgcn_readfirstlane(vb4.x | vb4.y | vb4.z | vb4.w) != 0;
 
     // ---- intra-chunk tile of this wave's tokens ----
     float lsum = 0.f;
@@ -504,6 +519,9 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       if (2 * m > w) break;                        // key tiles entirely in the future
+      // the step holding the wave's diagonal tile (and any future keys) when a value of the
+      // chunk is an infinity or a nan (rare, wave-uniform): exact path
+      const bool fix = vbad && 2 * m + 1 >= w;
       __bf16 pa[8];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -522,8 +540,16 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
       bf16x8 a;
 #pragma unroll
       for (int r = 0; r < 8; ++r) a[r] = pa[r];
+      if (!fix) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) O[nt] = mfma32(a, v_frag(tl.V, m, nt, lane), O[nt]);
+        for (int nt = 0; nt < 4; ++nt) O[nt] = mfma32(a, v_frag(tl.V, m, nt, lane), O[nt]);
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          O[nt] = mfma32(a, finite_or_zero(v_frag(tl.V, m, nt, lane)), O[nt]);
+        const int cols[4] = {l16, 16 + l16, 32 + l16, 48 + l16};
+        nonfinite_fixup<4>(O, tl.V, a, 32 * m, 16 * w, cols, lane);
+      }
     }
 
     // ---- inter-chunk denominator q^T Z_{<c} q ----
@@ -605,6 +631,7 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     __syncthreads();                               // all reads of this chunk's tiles and Sb done
     if (c + 1 < nc) {
       stage_store(st, tl, true, tid);
+      flag_v(st);
       publish();
     }
     __syncthreads();

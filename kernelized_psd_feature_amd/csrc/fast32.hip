@@ -276,6 +276,58 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
   }
 }
 
+struct Pair4 {
+  f32x4 a, b;
+};
+
+// The intra-chunk tile of wave w's tokens and value columns (the walk's first product), for a
+// chunk whose values hold an infinity or a nan: the step holding the diagonal tile (and any
+// future keys) takes finite_or_zero value operands and nonfinite_fixup adds the exact
+// contributions of the non-finite values of unmasked pairs, so no later token reaches an
+// earlier output.  Not inlined: the walk's loop keeps its registers and schedule, and only
+// this rare path pays for the call.
+__device__ __attribute__((noinline)) Pair4 intra_exact32(const Tiles32& tl, bf16x8 qf, int w,
+                                                         int lane) {
+  const int g = lane >> 4, l16 = lane & 15, tg = w & 3, ch = w >> 2, t = 16 * tg + l16;
+  float lsum = 0.f;
+  f32x4 O[2] = {zero4(), zero4()};
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    if (2 * m > tg) break;
+    __bf16 pa[8];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int ms = 2 * m + half;
+      if (ms <= tg) {
+        const bf16x8 kf = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(&tl.Ks[16 * ms + l16][8 * g]));
+        const f32x4 sc = mfma32(kf, qf, zero4());
+        if (ms < tg)
+          square_mask<false>(sc, 16 * ms, t, lane, &pa[4 * half], lsum);
+        else
+          square_mask<true>(sc, 16 * ms, t, lane, &pa[4 * half], lsum);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pa[4 * half + r] = (__bf16)0.f;
+      }
+    }
+    bf16x8 a;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) a[r] = pa[r];
+    if (2 * m + 1 < tg) {                          // keys before every token of the wave
+#pragma unroll
+      for (int n = 0; n < 2; ++n) O[n] = mfma32(a, v_frag(tl.V, m, 2 * ch + n, lane), O[n]);
+    } else {
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+        O[n] = mfma32(a, finite_or_zero(v_frag(tl.V, m, 2 * ch + n, lane)), O[n]);
+      const int cols[2] = {32 * ch + l16, 32 * ch + 16 + l16};
+      nonfinite_fixup<2>(O, tl.V, a, 32 * m, 16 * tg, cols, lane);
+    }
+  }
+  return Pair4{O[0], O[1]};
+}
+
 // ==========================================================================================
 // Segment walk (see the file comment for the work split).  One workgroup per (segment, head,
 // batch) (SegGrid).
@@ -286,6 +338,7 @@ struct __align__(16) Walk32Lds {
   uint2 Zb[4][2][64];             // Z_{<c} tiles (mi, kj) = 2 mi + kj as bf16 hi / lo A operands
   f32x4 xr[kWaves][2][64];        // readout partials handed to the other wave of a token group
   float zx[kWaves][64];           // q^T Z q halves handed to the other wave of a token group
+  uint32_t vbad[kWaves];          // per wave: its staged v row pieces hold a non-finite value
   unsigned char dg[4 * kSteps][2];   // double group -> (a, J)
 };
 
@@ -378,10 +431,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     }
   };
 
+  // Each wave records whether the v pieces it stages hold an infinity or a nan; the chunk's
+  // masked P.V step then takes the slow exact path (nonfinite_fixup in mfma_util.h).
+  auto flag_v = [&](const Stage32& x) {
+    const uint32_t any = __any(nonfinite_bf16x8(x.v) != 0u) ? 1u : 0u;
+    if (lane == 0) sm.vbad[w] = any;
+  };
+
   Ptrs32 p = ptrs32(pr, q, k, v, b, h, c0 * C, true, tid, 1);
   Stage32 st;
   load32(st, p);
   store32(st, tl, true, tid);
+  flag_v(st);
   publish();
   __syncthreads();
 
@@ -395,6 +456,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
       p.next();
       load32(st, p);
     }
+
+    const uint4 vb0 = *reinterpret_cast<const uint4*>(&sm.vbad[0]);
+    const uint4 vb1 = *reinterpret_cast<const uint4*>(&sm.vbad[4]);
+    const bool vbad = __builtin_amdgcn_readfirstlane(vb0.x | vb0.y | vb0.z | vb0.w | vb1.x |
+                                                     vb1.y | vb1.z | vb1.w) != 0;
 
     // ---- intra-chunk tile of this wave's tokens and value columns ----
     float lsum = 0.f;
@@ -425,6 +491,17 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
       for (int r = 0; r < 8; ++r) a[r] = pa[r];
 #pragma unroll
       for (int n = 0; n < 2; ++n) O[n] = mfma32(a, v_frag(tl.V, m, 2 * ch + n, lane), O[n]);
+    }
+    {
+      // a value of the chunk is an infinity or a nan (rare): the tile again, exactly
+      const uint4 vb0 = *reinterpret_cast<const uint4*>(&sm.vbad[0]);
+      const uint4 vb1 = *reinterpret_cast<const uint4*>(&sm.vbad[4]);
+      if (__builtin_amdgcn_readfirstlane(vb0.x | vb0.y | vb0.z | vb0.w | vb1.x | vb1.y | vb1.z |
+                                         vb1.w) != 0) {
+        const Pair4 e = intra_exact32(tl, qf, w, lane);
+        O[0] = e.a;
+        O[1] = e.b;
+      }
     }
 
     // ---- inter-chunk denominator q^T Z_{<c} q on MFMA (Z = hi + lo in bf16) ----
@@ -513,6 +590,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     __syncthreads();                               // all reads of this chunk's tiles and Sb
     if (c + 1 < nc) {
       store32(st, tl, true, tid);
+      flag_v(st);
       publish();
     }
     __syncthreads();

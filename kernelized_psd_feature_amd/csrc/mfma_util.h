@@ -96,4 +96,72 @@ __device__ __forceinline__ void weight_mask(const f32x4& x2, int s0, int t, int 
 template <typename Tout>
 __device__ __forceinline__ Tout cvt_out(float x) { return from_f32<Tout>(x); }
 
+// ---- non-finite values and masked P.V products ------------------------------------------
+// Inside an MFMA P.V product a masked weight P_ts = 0 still meets the value v_s of every key of
+// the K step, and 0 * inf or 0 * nan is nan: a non-finite value of a later token would reach
+// earlier outputs of the same tile.  The kernels therefore check the values of a tile; when one
+// is non-finite, the tile's masked steps take the value operand with those entries replaced by
+// zero (so masked pairs add exact zeros, as they do for finite values) and add the exact
+// contributions of the non-finite entries of unmasked pairs afterwards, pair by pair.
+
+// Bit 15 (bit 31) of the result is set when the low (high) bf16 of w is an infinity or a nan:
+// the magnitude |h| = h & 0x7fff is >= 0x7f80 exactly then, so |h| + 0x80 reaches 0x8000, and
+// the low half (at most 0x807f) never carries into the high half.
+__device__ __forceinline__ uint32_t nonfinite_bf16x2(uint32_t w) {
+  return ((w & 0x7fff7fffu) + 0x00800080u) & 0x80008000u;
+}
+__device__ __forceinline__ uint32_t nonfinite_bf16x8(const uint4& u) {
+  return nonfinite_bf16x2(u.x) | nonfinite_bf16x2(u.y) | nonfinite_bf16x2(u.z) |
+         nonfinite_bf16x2(u.w);
+}
+__device__ __forceinline__ bool nonfinite_bf16(__bf16 x) {
+  return nonfinite_bf16x2(__builtin_bit_cast(unsigned short, x)) != 0u;
+}
+// w with every non-finite bf16 replaced by +0
+__device__ __forceinline__ uint32_t finite_or_zero_bf16x2(uint32_t w) {
+  return w & ~((nonfinite_bf16x2(w) >> 15) * 0xffffu);
+}
+__device__ __forceinline__ bf16x8 finite_or_zero(const bf16x8& x) {
+  const uint4 u = __builtin_bit_cast(uint4, x);
+  return __builtin_bit_cast(bf16x8, uint4{finite_or_zero_bf16x2(u.x), finite_or_zero_bf16x2(u.y),
+                                          finite_or_zero_bf16x2(u.z), finite_or_zero_bf16x2(u.w)});
+}
+
+// After a walk step's P.V product over keys [s0, s0 + 32) was taken with finite_or_zero value
+// operands: O[n][r] (query row 4 (lane / 16) + r of the wave's 16 tokens, whose chunk-local token
+// is t0 + 4 (lane / 16) + r, value column cols[n]) += P[row][s] * V[s][cols[n]] for every key
+// s <= that token whose value is non-finite.  pa: the step's bf16 weights as the P.V A operand
+// (lane holds query row lane % 16, keys s0 + 16 (i / 4) + 4 (lane / 16) + i % 4 in slot i); the
+// weight of another row is fetched from the lane that holds it.  V: the row-major value tile of
+// the chunk.  Called by all lanes of the wave (the shuffles need them).
+template <int NT, int ROW>
+__device__ __forceinline__ void nonfinite_fixup(f32x4 (&O)[NT], const __bf16 (*V)[ROW],
+                                                const bf16x8& pa, int s0, int t0,
+                                                const int (&cols)[NT], int lane) {
+  const int g = lane >> 4;
+  const uint4 pd = __builtin_bit_cast(uint4, pa);
+  for (int j = 0; j < 32; ++j) {
+    const int s = s0 + j;
+    if (s > t0 + 15) break;                        // past the wave's last token (uniform)
+    const int slot = 4 * (j >> 4) + (j & 3);       // wave-uniform
+    const uint32_t d = slot < 2 ? pd.x : slot < 4 ? pd.y : slot < 6 ? pd.z : pd.w;
+    const int src = 16 * ((j & 15) >> 2) + 4 * g;  // + r: the lane holding row 4 g + r
+    float w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t x = (uint32_t)__shfl((int)d, src + r);
+      w[r] = (slot & 1) ? bf_hi(x) : bf_lo(x);
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const __bf16 x = V[s][cols[n]];
+      if (!nonfinite_bf16(x)) continue;
+      const float xf = (float)x;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (s <= t0 + 4 * g + r) O[n][r] += w[r] * xf;
+    }
+  }
+}
+
 }  // namespace kata

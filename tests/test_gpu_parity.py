@@ -135,19 +135,60 @@ def test_crossover_p32_sampled(T, form):
 
 # ------------------------------------------------------------ workload 4: 131k tokens --
 
-@pytest.mark.parametrize("form", ["chunked", "quadratic"])
+_LONG_REF = {}
+
+
+def _long_context_rows(plan):
+    """Rows of the 131k workload checked on every head: the first and last chunk, both sides of
+    every boundary between the plan's segments and of 64 random chunk boundaries, and 64 random
+    rows (seeded)."""
+    T, C, L = 131072, 64, plan["chunks_per_segment"]
+    rng = np.random.default_rng(4)
+    seg_edges = np.arange(L * C, T, L * C)
+    chunk_edges = C * rng.choice(np.arange(1, T // C), 64, replace=False)
+    edges = np.concatenate([seg_edges, chunk_edges])
+    rows = np.concatenate([np.arange(C), np.arange(T - C, T), edges - 1, edges,
+                           rng.choice(T, 64, replace=False)])
+    return np.unique(rows)
+
+
+def _long_context_check(o, q, k, v, rows, tag):
+    """o (CPU, (1, T, 16, 64)) against the oracle on `rows` of every head (oracle rows cached
+    across the forms checked on the same inputs)."""
+    worst = 0.0
+    for h in range(16):
+        key = (h, rows.tobytes())
+        if key not in _LONG_REF:
+            _LONG_REF[key] = O.closed_form_rows(_np(q[0, :, h]), _np(k[0, :, h]), _np(v[0, :, h]),
+                                                rows)[0]
+        worst = max(worst, float(np.abs(o[0, rows, h].double().numpy() - _LONG_REF[key]).max()))
+    say(f"{tag}: {rows.size} rows x 16 heads, max-abs {worst:.3e} (tol 1e-2)")
+    assert worst <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("form", ["chunked", "quadratic", "literal_scan"])
 def test_long_context_sampled(form):
+    # B=1, H=16, T=131072, p=16, d_v=64, C=64.  chunked: the default plan (segments walked in
+    # registers, a prefix scan over the segment states); literal_scan: seg_chunks = 1, every
+    # one of the 2048 chunk states per head materialized and combined by the prefix scan of
+    # depth log2(2048) = 11 (the form the problem statement names); quadratic: the O(T^2) form.
     w = W.WORKLOADS[4]
     q, k, v = W.make_inputs(w, 0)
     qg, kg, vg = _to_gpu(q, k, v)
-    o = _run(form, qg, kg, vg, chunk=w.chunk)
+    plan = K.chunked_plan(qg, kg, vg)
+    rows = _long_context_rows(plan)
+    if form == "literal_scan":
+        lit = K.chunked_plan(qg, kg, vg, seg_chunks=1)
+        assert lit["segments"] == 2048 and lit["chunks_per_segment"] == 1
+        assert lit["scan_levels"] == 11 and lit["walk_sums_prefix"] == 0
+        o = K.fwd_chunked(qg, kg, vg, seg_chunks=1)
+    else:
+        assert plan["segments"] > 8 and plan["scan_levels"] > 0     # the scan form
+        o = _run(form, qg, kg, vg, chunk=w.chunk)
     torch.cuda.synchronize()
     o = o.cpu()
     assert torch.isfinite(o).all()
-    rng = np.random.default_rng(4)
-    heads = [(0, 0), (0, int(rng.integers(1, w.H)))]
-    _check_rows(q, k, v, o, heads, _rows_sampler(rng, 192), TOL[w.dtype],
-                tag=f"long context {form}")
+    _long_context_check(o, q, k, v, rows, f"long context {form}")
 
 
 # ------------------------------------------------------------ workload 5: backward -----
@@ -393,16 +434,89 @@ def test_future_tokens_do_not_change_earlier_outputs_bitwise(form):
 
 
 @pytest.mark.parametrize("form", ["quadratic", "chunked"])
-def test_non_finite_future_chunks_do_not_leak(form):
-    # a non-finite value in a later 64-token chunk never reaches earlier chunks' outputs
+@pytest.mark.parametrize("P", [337, 320, 383])
+def test_non_finite_future_tokens_do_not_leak(form, P):
+    # non-finite keys and values from token P on (mid-chunk, a chunk boundary, a chunk's last
+    # token) never reach earlier outputs, not even those of P's own 64-token chunk
     w = W.WORKLOADS[2]
     q, k, v = _to_gpu(*W.make_inputs(w, 3, T=512, B=1, H=2))
     o1 = _run(form, q, k, v)
     k2, v2 = k.clone(), v.clone()
-    k2[:, 320:] = float("nan")
-    v2[:, 320:] = float("inf")
+    k2[:, P:] = float("nan")
+    v2[:, P:] = float("inf")
     o2 = _run(form, q, k2, v2)
-    assert torch.equal(o1[:, :320], o2[:, :320])
+    assert torch.equal(o1[:, :P], o2[:, :P])
+    assert torch.isnan(o2[:, P:]).all()          # every later score is nan (oracle: the same)
+
+
+# Every MFMA kernel family: p = 16 (packed and direct state), KATA-Mg g = 2 and 4 at p = 16,
+# p = 32, and p = 32 KATA-Mg g = 2 (two p = 16 passes).
+NONFINITE_CASES = {
+    "p16": dict(wid=2, groups=1, state="packed"),
+    "p16_direct": dict(wid=2, groups=1, state="direct"),
+    "p16_g2": dict(wid=2, groups=2, state="packed"),
+    "p16_g4": dict(wid=2, groups=4, state="packed"),
+    "p32": dict(wid=3, groups=1, state="packed"),
+    "p32_g2": dict(wid=3, groups=2, state="packed"),
+}
+
+
+def _class(x):
+    """0 finite, 1 nan, 2 +inf, 3 -inf, elementwise."""
+    x = np.asarray(x)
+    return np.where(np.isnan(x), 1, np.where(x == np.inf, 2, np.where(x == -np.inf, 3, 0)))
+
+
+@pytest.mark.parametrize("kind", ["neg_inf", "nan"])
+@pytest.mark.parametrize("P", [301, 330, 337, 383])
+@pytest.mark.parametrize("form", ["chunked", "quadratic"])
+@pytest.mark.parametrize("case", sorted(NONFINITE_CASES))
+def test_one_non_finite_value_row_reaches_only_its_own_and_later_tokens(case, form, P, kind):
+    # v_P = -inf (or nan) in every column, everything else finite.  Earlier outputs are
+    # bitwise those of the clean inputs.  Later outputs: the oracle's class where the kernel
+    # adds a_tP v_P to a finite sum (the quadratic form; the chunked form inside P's chunk):
+    # -inf for a_tP > 0, nan for a_tP = 0 or v_P = nan; beyond P's chunk the chunked form reads
+    # v_P out of the state, whose feature rows of both signs meet it: nan or an infinity there.
+    c = NONFINITE_CASES[case]
+    w = W.WORKLOADS[c["wid"]]
+    q, k, v = W.make_inputs(w, 70 + P, T=512, B=1, H=2)
+    kw = dict(groups=c["groups"])
+    if form == "chunked":
+        kw["state"] = c["state"]
+    qg, kg, vg = _to_gpu(q, k, v)
+    o1 = _run(form, qg, kg, vg, **kw)
+    v2 = v.clone()
+    v2[:, P] = float("-inf") if kind == "neg_inf" else float("nan")
+    o2 = _run(form, qg, kg, v2.to(DEV), **kw).cpu()
+    assert torch.equal(o1[:, :P].cpu(), o2[:, :P]), "earlier outputs changed"
+    with np.errstate(invalid="ignore"):
+        ref, _ = O.closed_form(_np(q), _np(k), _np(v2), groups=c["groups"])
+    exact_end = 512 if form == "quadratic" else (P // 64 + 1) * 64
+    got = o2[:, P:exact_end].double().numpy()
+    np.testing.assert_array_equal(_class(got), _class(ref[:, P:exact_end]))
+    assert not np.isfinite(o2[:, exact_end:].double().numpy()).any()
+
+
+@pytest.mark.parametrize("case", ["p16", "p32"])
+def test_one_non_finite_value_row_two_query_blocks_per_wave(case):
+    # the quadratic kernel's two-query-blocks-per-wave shape (grids of >= 4096 workgroups of
+    # 256 queries), a -inf value row at a mid-block token of every head
+    wid, B, T, P = {"p16": (2, 1, 65536, 40000 + 37), "p32": (3, 4, 16384, 9000 + 41)}[case]
+    w = W.WORKLOADS[wid]
+    q, k, v = W.make_inputs(w, 77, T=T, B=B, H=16)
+    assert B * 16 * -(-T // 256) >= 4096
+    qg, kg, vg = _to_gpu(q, k, v)
+    o1 = K.fwd_quadratic(qg, kg, vg)
+    v2 = v.clone()
+    v2[:, P] = float("-inf")
+    o2 = K.fwd_quadratic(qg, kg, v2.to(DEV))
+    assert torch.equal(o1[:, :P], o2[:, :P])
+    o2 = o2.cpu()
+    rows = np.arange(P, P + 150)
+    for b, h in [(0, 0), (B - 1, 15)]:
+        with np.errstate(invalid="ignore"):
+            ref, _ = O.closed_form_rows(_np(q[b, :, h]), _np(k[b, :, h]), _np(v2[b, :, h]), rows)
+        np.testing.assert_array_equal(_class(o2[b, rows, h].double().numpy()), _class(ref))
 
 
 def test_non_finite_future_tokens_do_not_leak_fp32_path():
@@ -590,10 +704,11 @@ def test_packed_state_agrees_with_direct_and_is_causal():
     assert float((a - b).abs().max()) <= 2e-2
     assert torch.equal(b, K.fwd_chunked(q, k, v, state="packed"))
     k2, v2 = k.clone(), v.clone()
-    k2[:, 320:] = float("nan")
-    v2[:, 320:] = float("inf")
-    b2 = K.fwd_chunked(q, k2, v2, state="packed")
-    assert torch.equal(b[:, :320], b2[:, :320])
+    k2[:, 337:] = float("nan")
+    v2[:, 337:] = float("inf")
+    for state, ref in (("packed", b), ("direct", a)):
+        b2 = K.fwd_chunked(q, k2, v2, state=state)
+        assert torch.equal(ref[:, :337], b2[:, :337]), state
 
 
 def test_packed_state_request_on_the_fp32_path_computes_the_direct_form():
@@ -821,9 +936,9 @@ def test_p32_bf16_output_causality_and_determinism():
         assert torch.equal(o32, _run(form, q, k, v))
         assert torch.equal(_run(form, q, k, v, out_dtype=torch.bfloat16), o32.to(torch.bfloat16))
         k2, v2 = k.clone(), v.clone()
-        k2[:, 320:] = float("nan")
-        v2[:, 320:] = float("inf")
-        assert torch.equal(o32[:, :320], _run(form, q, k2, v2)[:, :320]), form
+        k2[:, 337:] = float("nan")
+        v2[:, 337:] = float("inf")
+        assert torch.equal(o32[:, :337], _run(form, q, k2, v2)[:, :337]), form
 
 
 # ------------------------------------------------------------ KATA-Mg on MFMA -----------
@@ -884,9 +999,9 @@ def test_mg_mfma_causality_and_bf16_output():
         assert torch.equal(_run(form, q, k, v, groups=4, out_dtype=torch.bfloat16),
                            o.to(torch.bfloat16))
         k2, v2 = k.clone(), v.clone()
-        k2[:, 320:] = float("nan")
-        v2[:, 320:] = float("inf")
-        assert torch.equal(o[:, :320], _run(form, q, k2, v2, groups=4)[:, :320]), form
+        k2[:, 337:] = float("nan")
+        v2[:, 337:] = float("inf")
+        assert torch.equal(o[:, :337], _run(form, q, k2, v2, groups=4)[:, :337]), form
 
 
 # ------------------------------------------------------------ bench shapes ---------------
