@@ -14,7 +14,8 @@
  * Conventions shared by every call
  *   - All data pointers are DEVICE pointers on the current HIP device, owned by the caller.
  *     The library never allocates, frees or retains them; scratch memory comes only from the
- *     caller's workspace, whose size is queried first.  Inputs are read-only.
+ *     caller's workspace, whose size is queried first (kata_fwd_chunked_noalloc alone uses a
+ *     static array inside the library instead).  Inputs are read-only.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every call only
  *     enqueues work on that stream and returns without synchronizing.  A kernel fault shows
  *     up at the caller's next synchronization, not in the return code.
@@ -128,6 +129,25 @@ size_t kata_fwd_chunked_workspace_size(const kata_problem* pr);
 kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* k,
                              const void* v, void* o, float* den, void* workspace,
                              size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): kata_fwd_chunked without a workspace.  The segment
+ * states and the scan's scratch live in a static array inside the library, one per device,
+ * KATA_NOALLOC_SCRATCH_BYTES long, held from the library's first use on that device until the
+ * process ends; the call itself allocates nothing (no hipMalloc, no allocating library call).
+ * Arguments, results and errors are those of kata_fwd_chunked (same kernels, same plan, the
+ * same outputs bit for bit), except:
+ *   - a problem whose kata_fwd_chunked_workspace_size exceeds KATA_NOALLOC_SCRATCH_BYTES is
+ *     rejected with KATA_ERR_WORKSPACE before anything is enqueued (the 131072-token, 16-head
+ *     p = 16 plan needs 30.8 MiB; the literal one-state-per-chunk scan there, 1.3 GiB, does
+ *     not fit);
+ *   - every call on one device shares that device's array and leaves its contents behind
+ *     (nothing in it has to start at zero): calls that may overlap in time on one device --
+ *     on different streams, or from different host threads -- race and must be ordered by
+ *     the caller (e.g. one stream). */
+#define KATA_NOALLOC_SCRATCH_BYTES (64u << 20)
+kata_status kata_fwd_chunked_noalloc(const kata_problem* pr, const void* q, const void* k,
+                                     const void* v, void* o, float* den, void* stream);
 
 /* The plan kata_fwd_chunked takes for a problem (host only; no device call).  The chunks of
  * one (b, h) are walked in `segments` segments of `chunks_per_segment` chunks; a state pass

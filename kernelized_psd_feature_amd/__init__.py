@@ -24,7 +24,8 @@ import os
 import torch
 
 __all__ = [
-    "KataError", "fwd_quadratic", "fwd_chunked", "chunked_workspace_size", "chunked_plan",
+    "KataError", "fwd_quadratic", "fwd_chunked", "fwd_chunked_noalloc", "chunked_workspace_size",
+    "chunked_plan", "NOALLOC_SCRATCH_BYTES",
     "chunk_state_scan", "scan_workspace_size", "bwd", "bwd_workspace_size",
     "recurrent_state", "recurrent_state_workspace_size", "decode", "state_shape",
     "timing_begin", "timing_end", "library_path", "KERNEL_KINDS",
@@ -35,6 +36,7 @@ _LIB_PATH = os.path.join(_HERE, "libkata.so")
 _LIB = None
 
 KATA_F32, KATA_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 64 << 20     # KATA_NOALLOC_SCRATCH_BYTES of include/kata.h
 KERNEL_KINDS = ("quadratic", "chunk_state", "scan", "chunk_output", "bwd", "decode",
                 "state_sum")
 
@@ -85,6 +87,7 @@ def _lib():
             "kata_fwd_quadratic": (I32, [P, VP, VP, VP, VP, VP, VP]),
             "kata_fwd_chunked_workspace_size": (SZ, [P]),
             "kata_fwd_chunked": (I32, [P, VP, VP, VP, VP, VP, VP, SZ, VP]),
+            "kata_fwd_chunked_noalloc": (I32, [P, VP, VP, VP, VP, VP, VP]),
             "kata_fwd_chunked_plan": (I32, [P, ctypes.POINTER(_ChunkedPlan)]),
             "kata_chunk_state_scan_workspace_size": (SZ, [I64, I64, I64]),
             "kata_chunk_state_scan": (I32, [VP, I64, I64, I64, I32, VP, VP, SZ,
@@ -228,6 +231,25 @@ def fwd_chunked(q, k, v, chunk=64, eps=1e-6, out_dtype=torch.float32, seg_chunks
                                     _ptr(den), _ptr(workspace), workspace.numel(),
                                     _stream(q.device)), "kata_fwd_chunked")
     return (o, den) if return_den else o
+
+
+def fwd_chunked_noalloc(q, k, v, out, chunk=64, eps=1e-6, seg_chunks=0, den=None,
+                        state="packed", groups=1):
+    """fwd_chunked without a workspace: the library's static per-device scratch holds the
+    segment states (problems whose workspace would exceed NOALLOC_SCRATCH_BYTES are rejected).
+    The caller passes the output `out` (its dtype is the output dtype) and optionally `den`
+    (fp32 (B, T, H)); nothing is allocated.  Calls that overlap on one device race."""
+    if out.shape != v.shape or out.device != v.device:
+        raise ValueError("out must match v's shape and device")
+    if den is not None and (den.shape != q.shape[:3] or den.dtype != torch.float32):
+        raise ValueError("den must be fp32 (B, T, H)")
+    pr = _make_problem(q, k, v, out, chunk=chunk, seg_chunks=seg_chunks, eps=eps,
+                       out_dtype=out.dtype, state=state, groups=groups)
+    with torch.cuda.device(q.device):
+        _check(_lib().kata_fwd_chunked_noalloc(ctypes.byref(pr), _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(out), _ptr(den), _stream(q.device)),
+               "kata_fwd_chunked_noalloc")
+    return out
 
 
 def scan_workspace_size(n_seq, n_chunks, state_elems):

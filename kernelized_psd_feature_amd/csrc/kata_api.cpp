@@ -2,7 +2,8 @@
 //
 // Every entry point validates its arguments on the host (plan.cpp), checks that the current
 // device is a gfx950, then enqueues its kernels on the caller's stream and returns without
-// synchronizing.  Scratch memory comes only from the caller's workspace.
+// synchronizing.  Scratch memory comes from the caller's workspace, except for
+// kata_fwd_chunked_noalloc, which uses the static per-device array defined below.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -247,6 +248,38 @@ kata_status run_chunked(const kata_problem* pr, const kata::ChunkPlan& cp, const
   return launch_status(e, "chunk-output kernel");
 }
 
+// The chunked forward after validation (both entry points): the pipeline of run_chunked, or
+// for p = 32 KATA-Mg its two p = 16 passes and their combination.
+kata_status chunked_forward(const kata_problem* pr, const kata::ChunkPlan& cp, const void* q,
+                            const void* k, const void* v, void* o, float* den, void* workspace,
+                            hipStream_t st);
+
+// ---- static scratch of kata_fwd_chunked_noalloc --------------------------------------
+// One array per device (each device that loads the library holds its own copy until the
+// process ends).  Host code never uses the array's name as an address: the device address is
+// taken once per device with hipGetSymbolAddress, with that device current, and kept.
+static __device__ __align__(256) unsigned char scratch[KATA_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+kata_status static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_error(KATA_ERR_DEVICE, std::string("no usable HIP device: ") + hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return set_error(KATA_ERR_DEVICE, std::string("hipGetSymbolAddress(scratch) failed: ") +
+                                            hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KATA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -322,7 +355,34 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
     return set_error(KATA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
   if ((s = check_device()) != KATA_OK) return s;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return chunked_forward(pr, cp, q, k, v, o, den, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+kata_status kata_fwd_chunked_noalloc(const kata_problem* pr, const void* q, const void* k,
+                                     const void* v, void* o, float* den, void* stream) {
+  g_last_error.clear();
+  kata_status s = check_forward_args(pr, Form::Chunked, q, k, v, o, den);
+  if (s != KATA_OK) return s;
+  const kata::ChunkPlan cp = kata::plan_chunked(pr, kata::chunk_fast_available());
+  if (cp.ws_bytes > KATA_NOALLOC_SCRATCH_BYTES)
+    return set_error(KATA_ERR_WORKSPACE,
+                     "the problem needs " + std::to_string(cp.ws_bytes) +
+                         " bytes of scratch; the library's static scratch holds " +
+                         std::to_string(size_t(KATA_NOALLOC_SCRATCH_BYTES)) +
+                         " (use kata_fwd_chunked with a workspace)");
+  if ((s = check_device()) != KATA_OK) return s;
+  void* ws = nullptr;
+  if ((s = static_scratch(&ws)) != KATA_OK) return s;
+  return chunked_forward(pr, cp, q, k, v, o, den, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+kata_status chunked_forward(const kata_problem* pr, const kata::ChunkPlan& cp, const void* q,
+                            const void* k, const void* v, void* o, float* den, void* workspace,
+                            hipStream_t st) {
+  kata_status s;
   if (!cp.halves) return run_chunked(pr, cp, q, k, v, o, den, workspace, st);
   // p = 32 KATA-Mg: two p = 16 passes over the coordinate halves (each with g / 2 groups) into
   // fp32 temporaries, then o = (o_0 D_0 + o_1 D_1) / (D_0 + D_1 - eps)
@@ -351,6 +411,9 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
                                                    oj[0], dj[0], oj[1], dj[1], o, den, st),
                        "two-pass combine");
 }
+}  // namespace
+
+extern "C" {
 
 size_t kata_chunk_state_scan_workspace_size(int64_t n_seq, int64_t n_chunks,
                                             int64_t state_elems) {

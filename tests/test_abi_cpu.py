@@ -366,3 +366,27 @@ def test_library_exports_only_the_declared_c_functions():
     exported = {l.split()[-1] for l in out.splitlines() if l.split()[1:2] == ["T"]}
     c_names = {n for n in exported if not n.startswith("_Z")}
     assert c_names <= set(_declared_functions()), sorted(c_names - set(_declared_functions()))
+
+
+def test_noalloc_forward_rejects_a_problem_beyond_its_static_scratch():
+    # validation runs before any device call: one state per chunk over 2 x 1024 chunks needs
+    # more than the 64 MiB static scratch; the same problem with the default plan fits
+    lib = _lib()
+    q, k, v, o = _fake(4)
+    big = _problem(B=1, H=2, T=65536, seg=1)
+    assert lib.kata_fwd_chunked_workspace_size(ctypes.byref(big)) > K.NOALLOC_SCRATCH_BYTES
+    assert lib.kata_fwd_chunked_noalloc(ctypes.byref(big), q, k, v, o, None, None) == WORKSPACE
+    assert "static scratch" in lib.kata_last_error().decode()
+    fits = _problem(B=1, H=2, T=65536)
+    assert 0 < lib.kata_fwd_chunked_workspace_size(ctypes.byref(fits)) <= K.NOALLOC_SCRATCH_BYTES
+    # argument errors as kata_fwd_chunked
+    assert lib.kata_fwd_chunked_noalloc(None, q, k, v, o, None, None) == INVALID
+    assert lib.kata_fwd_chunked_noalloc(ctypes.byref(_problem(T=100)), q, k, v, o, None,
+                                        None) == UNSUPPORTED
+    assert lib.kata_fwd_chunked_noalloc(ctypes.byref(fits), None, k, v, o, None, None) == INVALID
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define KATA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == K.NOALLOC_SCRATCH_BYTES
