@@ -34,6 +34,11 @@ inline void launch_kernel(F kernel, dim3 grid, dim3 block, size_t shmem, hipStre
   }
 }
 
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once per (kernel,
+// device) in the process -- the attribute stays set -- so that launches after the first pay a
+// table lookup, not a runtime call.  Returns the runtime's error if setting it fails.
+hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
+
 // Problem description passed to kernels by value.
 struct DevProblem {
   int B, H, T, p, dv, C;

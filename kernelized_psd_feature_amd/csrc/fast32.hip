@@ -603,8 +603,7 @@ hipError_t launch_chunk_state32(const DevProblem& pr, int L, int n_seg, int n_us
                                 const void* k, const void* v, float* states, hipStream_t st) {
   if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;
   const size_t lds = 2 * sizeof(StateTiles32);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_state32_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&chunk_state32_kernel), (int)lds);
   if (e != hipSuccess) return e;
   const SegGrid sg = make_seg_grid(pr, n_seg);
   if (sg.blocks() > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -624,14 +623,12 @@ hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int
   const __bf16 *qq = (const __bf16*)q, *kk = (const __bf16*)k, *vv = (const __bf16*)v;
   hipError_t e;
   if (out_bf16) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_output32_kernel<__bf16>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    e = ensure_dynamic_lds(reinterpret_cast<const void*>(&chunk_output32_kernel<__bf16>), (int)lds);
     if (e != hipSuccess) return e;
     launch_kernel(chunk_output32_kernel<__bf16>, grid, kThreads, lds, st, pr, sg, L, n_seg, qq,
                   kk, vv, (__bf16*)o, den, states, (int)sum_prefix);
   } else {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_output32_kernel<float>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    e = ensure_dynamic_lds(reinterpret_cast<const void*>(&chunk_output32_kernel<float>), (int)lds);
     if (e != hipSuccess) return e;
     launch_kernel(chunk_output32_kernel<float>, grid, kThreads, lds, st, pr, sg, L, n_seg, qq,
                   kk, vv, (float*)o, den, states, (int)sum_prefix);

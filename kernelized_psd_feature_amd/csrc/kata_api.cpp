@@ -142,6 +142,24 @@ struct Timed {
 
 namespace kata {
 LaunchTiming* launch_timing() { return g_scope; }
+
+hipError_t ensure_dynamic_lds(const void* kernel, int bytes) {
+  struct Entry {
+    const void* kernel;
+    int dev, bytes;
+  };
+  static std::mutex m;
+  static std::vector<Entry> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(m);
+  for (const Entry& x : done)
+    if (x.kernel == kernel && x.dev == dev && x.bytes >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.push_back({kernel, dev, bytes});
+  return e;
+}
 }  // namespace kata
 
 namespace {
@@ -417,7 +435,7 @@ extern "C" {
 
 size_t kata_chunk_state_scan_workspace_size(int64_t n_seq, int64_t n_chunks,
                                             int64_t state_elems) {
-  if (n_seq < 1 || n_chunks < 1 || state_elems < 4) return 0;
+  if (kata::validate_scan(n_seq, n_chunks, state_elems, nullptr) != KATA_OK) return 0;
   return kata::plan_scan(n_seq, n_chunks, state_elems).ws_bytes;
 }
 
@@ -427,11 +445,9 @@ kata_status kata_chunk_state_scan(float* states, int64_t n_seq, int64_t n_chunks
                                   void* stream) {
   g_last_error.clear();
   if (!states) return set_error(KATA_ERR_INVALID_ARGUMENT, "states is null");
-  if (n_seq < 1 || n_chunks < 1 || state_elems < 4 || state_elems % 4)
-    return set_error(KATA_ERR_INVALID_ARGUMENT,
-                     "need n_seq >= 1, n_chunks >= 1, state_elems >= 4 and a multiple of 4");
-  if (n_seq > 65535 || n_chunks > (int64_t(1) << 26) || state_elems > (int64_t(1) << 30))
-    return set_error(KATA_ERR_INVALID_ARGUMENT, "scan sizes out of range");
+  std::string why;
+  if (kata::validate_scan(n_seq, n_chunks, state_elems, &why) != KATA_OK)
+    return set_error(KATA_ERR_INVALID_ARGUMENT, why);
   if (reinterpret_cast<uintptr_t>(states) % 16 || (totals && reinterpret_cast<uintptr_t>(totals) % 16))
     return set_error(KATA_ERR_INVALID_ARGUMENT, "states/totals must be 16-byte aligned");
   const kata::ScanPlan sp = kata::plan_scan(n_seq, n_chunks, state_elems);

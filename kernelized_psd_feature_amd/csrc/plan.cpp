@@ -85,13 +85,24 @@ kata_status validate_problem(const kata_problem* pr, Form f, std::string* why) {
     // every (b, t, h) row must start past the previous row's last element along some order;
     // the minimal check that catches swapped or zero strides: each stride of an axis with
     // more than one entry is >= the row length.
+    // the largest element offset, sum_a (size_a - 1) stride_a + row length, in bytes must stay
+    // below 2^62 so that every offset the kernels form in 64-bit arithmetic is exact
+    const int64_t kMaxExtent = int64_t(1) << 62;
+    int64_t extent = last[i];
     for (int a = 0; a < 3; ++a) {
       int64_t s = strides[i][a];
       if (s < 0) return fail(why, KATA_ERR_INVALID_ARGUMENT, std::string(names[i]) + ": negative stride");
       if (sizes[a] > 1 && s < last[i])
         return fail(why, KATA_ERR_INVALID_ARGUMENT,
                     std::string(names[i]) + ": stride smaller than the row length");
+      if (sizes[a] > 1 && s > (kMaxExtent - extent) / (sizes[a] - 1))
+        return fail(why, KATA_ERR_INVALID_ARGUMENT,
+                    std::string(names[i]) + ": strides address more than 2^62 elements");
+      extent += (sizes[a] - 1) * s;
     }
+    if (extent > kMaxExtent / 4)
+      return fail(why, KATA_ERR_INVALID_ARGUMENT,
+                  std::string(names[i]) + ": strides address more than 2^62 bytes");
   }
   return KATA_OK;
 }
@@ -105,6 +116,18 @@ kata_status validate_tensor(const void* ptr, const int64_t st[3], size_t esize,
     if ((uint64_t(st[a]) * esize) % 16)
       return fail(why, KATA_ERR_INVALID_ARGUMENT,
                   std::string(name) + ": stride is not a multiple of 16 bytes");
+  return KATA_OK;
+}
+
+kata_status validate_scan(int64_t n_seq, int64_t n, int64_t elems, std::string* why) {
+  if (n_seq < 1 || n < 1 || elems < 4 || elems % 4)
+    return fail(why, KATA_ERR_INVALID_ARGUMENT,
+                "need n_seq >= 1, n_chunks >= 1, state_elems >= 4 and a multiple of 4");
+  if (n_seq > 65535 || n > kMaxT || elems > (int64_t(1) << 30))
+    return fail(why, KATA_ERR_INVALID_ARGUMENT, "scan sizes out of range");
+  // n_seq * n < 2^42 here; the array's bytes must stay below 2^62
+  if (n_seq * n > ((int64_t(1) << 60) - 1) / elems)
+    return fail(why, KATA_ERR_INVALID_ARGUMENT, "states array exceeds 2^62 bytes");
   return KATA_OK;
 }
 

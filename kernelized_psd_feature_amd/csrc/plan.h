@@ -1,5 +1,6 @@
 // Host-side argument validation and launch planning.  Pure C++ (no HIP): it is compiled into
-// libkata.so and, on its own, into a CPU test driver built with sanitizers.
+// libkata.so and, on its own with tests/plan_fuzz.cpp, into a CPU fuzz driver built with
+// AddressSanitizer and UndefinedBehaviorSanitizer (tests/test_plan_sanitizers.py).
 #pragma once
 
 #include <cstddef>
@@ -62,6 +63,14 @@ kata_status validate_problem(const kata_problem* pr, Form f, std::string* why);
 kata_status validate_tensor(const void* ptr, const int64_t st[3], size_t esize,
                             const char* name, std::string* why);
 
+// Checks the sizes of a stand-alone prefix scan (kata_chunk_state_scan): n_seq in
+// [1, 65535], n in [1, 2^26], elems a positive multiple of 4 up to 2^30, and the states array,
+// n_seq * n * elems fp32 values, below 2^62 bytes (so every size and offset derived from it
+// fits 64 bits).  Returns KATA_OK or INVALID_ARGUMENT with `why` filled in.
+kata_status validate_scan(int64_t n_seq, int64_t n, int64_t elems, std::string* why);
+
+// Plan of the prefix scan; the sizes must have passed validate_scan (or come from a valid
+// problem's plan).
 ScanPlan plan_scan(int64_t n_seq, int64_t n, int64_t elems);
 // pr must have passed validate_problem; fast_available: the MFMA chunked kernels are built.
 ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available);

@@ -161,8 +161,7 @@ hipError_t launch_scan_tiles(float* x, long long n_seq, long long n, long long e
   while (ks < slots) ks <<= 1;
   auto go = [&](auto kern) -> hipError_t {
     // up to 128 KiB of the 160 KiB LDS of a gfx950 CU
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
+    hipError_t e = ensure_dynamic_lds((const void*)kern, 131072);
     if (e != hipSuccess) return e;
     launch_kernel(kern, grid, kScanThreads, lds, st, x, n, elems, strip, tile_rows, n_tiles,
                   exclusive, totals, tile_offsets);

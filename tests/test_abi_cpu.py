@@ -390,3 +390,26 @@ def test_noalloc_scratch_size_matches_the_header():
     text = open(HEADER).read()
     m = re.search(r"#define KATA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == K.NOALLOC_SCRATCH_BYTES
+
+
+def test_strides_addressing_beyond_two_to_the_62_bytes_are_rejected():
+    # every offset the kernels form must be exact in 64-bit arithmetic
+    lib = _lib()
+    pr = _problem(B=2, H=2, T=128)
+    pr.sv[0] = 1 << 61                                   # (B - 1) * 2^61 elements of 2 bytes
+    assert _chunked(pr) == INVALID and "2^62" in lib.kata_last_error().decode()
+    pr = _problem(B=1, H=2, T=128)
+    pr.sk[1] = (1 << 62) // 200                          # 127 * that * 2 bytes > 2^62 / 4 ...
+    assert _quad(pr) == INVALID
+
+
+def test_scan_rejects_a_states_array_beyond_two_to_the_62_bytes():
+    lib = _lib()
+    st = ctypes.c_void_p(FAKE)
+    # 65535 sequences x 2^26 chunks x 2^30 floats: each size within its own cap
+    assert lib.kata_chunk_state_scan(st, 65535, 1 << 26, 1 << 30, 1, None, None, 0, None,
+                                     None) == INVALID
+    assert "2^62" in lib.kata_last_error().decode()
+    assert lib.kata_chunk_state_scan_workspace_size(65535, 1 << 26, 1 << 30) == 0
+    assert lib.kata_chunk_state_scan_workspace_size(16, 48, 10496) == 0      # one tile
+    assert lib.kata_chunk_state_scan_workspace_size(16, 5000, 10496) > 0     # tile totals

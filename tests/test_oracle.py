@@ -367,6 +367,47 @@ def test_backward_matches_central_finite_differences(eps, unit):
         np.testing.assert_allclose(g, num, rtol=0, atol=2e-6 * scale, err_msg=name)
 
 
+def _autograd_closed_form_grads(q, k, v, dO, eps, groups):
+    """Gradients of L = sum <dO, o> by torch float64 autograd of the closed form
+    o_t = sum_{s<=t} a_ts v_s / (eps + sum_{s<=t} a_ts), a_ts = sum_j (q_t^(j) . k_s^(j))^2,
+    written here in torch: a second route to the derivative, independent of the hand-derived
+    formulas of oracle.backward."""
+    import torch
+
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    tdO = torch.tensor(dO, dtype=torch.float64)
+    B, T, H, p = q.shape
+    w = p // groups
+    loss = 0.0
+    for b in range(B):
+        for h in range(H):
+            Q, K, V = tq[b, :, h], tk[b, :, h], tv[b, :, h]
+            a = 0.0
+            for j in range(groups):
+                sc = Q[:, j * w:(j + 1) * w] @ K[:, j * w:(j + 1) * w].T
+                a = a + sc * sc
+            a = torch.tril(a)
+            o = (a @ V) / (eps + a.sum(dim=1, keepdim=True))
+            loss = loss + (o * tdO[b, :, h]).sum()
+    return [g.numpy() for g in torch.autograd.grad(loss, (tq, tk, tv))]
+
+
+@pytest.mark.parametrize("groups", [1, 2, 4])
+def test_backward_matches_float64_autograd_of_the_closed_form(groups):
+    # the training workload's head shape (p = 16, d_v = 64) on a T = 256 slice, unit rows with
+    # q scaled by 2 so every D_t >> eps (the gradients grow like 1 / D_t)
+    rng = np.random.default_rng(31 + groups)
+    q, k, v = _rand(rng, 2, 256, 2, 16, 64)
+    q *= 2.0
+    dO = rng.standard_normal(v.shape)
+    eps = O.EPS
+    hand = O.backward(q, k, v, dO, eps, groups=groups)
+    auto = _autograd_closed_form_grads(q, k, v, dO, eps, groups)
+    for name, x, y in zip(("dq", "dk", "dv"), hand, auto):
+        scale = np.abs(y).max()
+        np.testing.assert_allclose(x, y, rtol=1e-10, atol=1e-12 * scale, err_msg=name)
+
+
 def test_backward_tiling_is_invisible():
     rng = np.random.default_rng(16)
     q, k, v = _rand(rng, 1, 40, 2, 4, 3)
