@@ -376,6 +376,183 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
 }
 
 // ==========================================================================================
+// Segment state, single feature group: the same sums as chunk_state_fast_kernel with phi(k)
+// formed from lane broadcasts instead of LDS re-reads.  The chunk's k rows sit row-major in
+// LDS; one transposed read per 32-key step hands lane (g, j) the value k_s[j] (j = lane % 16)
+// of the 8 keys s of its MFMA slots, and the keys of a lane group g are the same for all 16
+// lanes of its row.  Row i of direct state tile i then needs k_s[i] from lane i of the same
+// row: a DPP row broadcast folded into the multiply (v_mul_f32 with row_newbcast:i).  Each
+// wave owns direct tiles 4w .. 4w+3 (rows (i, j) for every j) and the same transposed read
+// is the A and B operand of Z = K^T K.  Per chunk and workgroup this moves about 50 KB
+// through LDS instead of 132 KB (the fp32 K^T rows read for every phi product).
+// Outputs: the direct layout as it is, or the packed one by a lane remap (see
+// store_packed_from_direct).  The products and their summation order are those of
+// chunk_state_fast_kernel, so the states are the same bit for bit (zero rows: +0).
+// ==========================================================================================
+constexpr int KSROW = 24;                     // bf16 per k row: 48 B, 16-byte aligned rows
+
+struct __align__(16) KvTiles {
+  __bf16 K[C][KSROW];                 // k rows (bf16), row-major
+  __bf16 V[C][VROW];                  // v rows (bf16), row-major
+};
+
+template <int I>
+__device__ __forceinline__ float row_bcast(float x) {   // lane I of each 16-lane row
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + I, 0xF, 0xF, true));
+}
+
+// A operand of direct tile I for one 32-key step: slot r = k_s[I] k_s[j], from this lane's
+// k_s[j] values kf (fp32 copies of bf16, so every product is exact before its bf16 rounding)
+template <int I>
+__device__ __forceinline__ bf16x8 phik_bcast(const float (&kf)[8]) {
+  bf16x8 f;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) f[r] = (__bf16)(row_bcast<I>(kf[r]) * kf[r]);
+  return f;
+}
+
+// Direct tile i's accumulators (lane (g, c): rows j = 4g + r, column 16 nt + c) written into
+// the packed layout: the pair (i, j) lives in double group (a, J) = (i - i % 2, g) of column
+// block J = g, i.e. packed tile 2 (idx / 4) + i % 2, lane group idx % 4, idx = J (J + 1) + a / 2,
+// same register r; off-diagonal rows carry weight 2 (exact), pairs with i > j inside a double
+// group are zero rows, and lane groups with i > 4g + 3 hold no packed row.
+__device__ __forceinline__ void store_packed_from_direct(float* out, int i, const f32x4 (&S)[4],
+                                                        int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  if (i > 4 * g + 3) return;
+  const int idx = g * (g + 1) + (i >> 1);
+  const int t = 2 * (idx >> 2) + (i & 1), gp = idx & 3;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    f32x4 x;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 4 * g + r;
+      x[r] = i < j ? 2.f * S[nt][r] : (i == j ? S[nt][r] : 0.f);
+    }
+    *reinterpret_cast<f32x4*>(out + ((t * 4 + nt) * 64 + 16 * gp + c) * 4) = x;
+  }
+}
+
+struct StageKv {
+  uint4 k;         // waves 2-3: 16 bytes of a k row
+  uint4 v0, v1;    // 16 bytes of two consecutive v rows
+};
+
+// The state sum of wave W's four direct tiles over the segment's chunks (the loop of
+// chunk_state_dpp_kernel, one instance per wave so that the broadcast lanes are constants).
+template <int W>
+__device__ __forceinline__ void state_dpp_loop(KvTiles (&tl)[2], const __bf16* kp, const __bf16* vp,
+                                               long long k_step, long long v_step, long long sv_t,
+                                               int nc, int tid, f32x4 (&S)[4][4], f32x4& Z) {
+  const int lane = tid & 63;
+  const int krow = tid & 63, khalf = (tid >> 6) & 1, a = tid >> 3, c8 = tid & 7;
+  auto load = [&](StageKv& x) {
+    if (W >= 2) x.k = ld16(kp);
+    x.v0 = ld16(vp);
+    x.v1 = ld16(vp + sv_t);
+  };
+  auto store = [&](const StageKv& x, KvTiles& t) {
+    if (W >= 2) *reinterpret_cast<uint4*>(&t.K[krow][8 * khalf]) = x.k;
+    *reinterpret_cast<uint4*>(&t.V[2 * a][8 * c8]) = x.v0;
+    *reinterpret_cast<uint4*>(&t.V[2 * a + 1][8 * c8]) = x.v1;
+  };
+  auto advance = [&]() {
+    kp += k_step;
+    vp += v_step;
+  };
+  StageKv sa, sb;
+  load(sa);
+  store(sa, tl[0]);
+  if (nc > 1) { advance(); load(sa); }
+  if (nc > 2) { advance(); load(sb); }
+  __syncthreads();
+  auto step = [&](int c, StageKv& next) {
+    const KvTiles& t = tl[c & 1];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const bf16x8 kt = v_frag(t.K, m, 0, lane);      // k_s[lane % 16] of this lane's keys
+      float kf[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) kf[r] = (float)kt[r];
+      bf16x8 vb[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(t.V, m, nt, lane);
+      const bf16x8 a0 = phik_bcast<4 * W>(kf), a1 = phik_bcast<4 * W + 1>(kf);
+      const bf16x8 a2 = phik_bcast<4 * W + 2>(kf), a3 = phik_bcast<4 * W + 3>(kf);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        S[0][nt] = mfma32(a0, vb[nt], S[0][nt]);
+        S[1][nt] = mfma32(a1, vb[nt], S[1][nt]);
+        S[2][nt] = mfma32(a2, vb[nt], S[2][nt]);
+        S[3][nt] = mfma32(a3, vb[nt], S[3][nt]);
+      }
+      if (W == 0) Z = mfma32(kt, kt, Z);
+    }
+    // the other buffer was last read in the previous iteration, before its barrier
+    if (c + 1 < nc) store(next, tl[(c + 1) & 1]);
+    if (c + 3 < nc) { advance(); load(next); }         // chunk c + 3
+    __syncthreads();
+  };
+  for (int c = 0; c < nc; c += 2) {
+    step(c, sa);                       // chunk c+1 is in sa, chunk c+2 in sb
+    if (c + 1 < nc) step(c + 1, sb);
+  }
+}
+
+template <bool kPackedOut>
+__global__ __launch_bounds__(kThreads, 3) void chunk_state_dpp_kernel(
+    DevProblem pr, SegGrid sg, int L, int n_seg, int n_used, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, float* __restrict__ states) {
+  using LY = Layout<kPackedOut, P>;
+  __shared__ KvTiles tl[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const SegBlock blk = seg_block(sg, pr.H);
+  if (!blk.live) return;                           // padding of the grid (whole workgroup)
+  const int seg = blk.seg, h = blk.h, b = blk.b;
+  const int n_chunks = pr.T / C;
+  const int c0 = seg * L, nc = min(L, n_chunks - c0);
+  float* out = states + ((long long)(b * pr.H + h) * n_seg + seg) * LY::kStateFloats;
+  if (seg >= n_used) {
+    // a state no prefix needs (the last segment's, in the forward): zeros, k and v unread
+    for (int x = tid; x < LY::kStateFloats / 4; x += kThreads)
+      reinterpret_cast<float4*>(out)[x] = float4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  f32x4 S[4][4];
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) S[sl][nt] = zero4();
+  f32x4 Z = zero4();
+  // the segment is read last chunk first (the sum is order-free; the walk that follows starts
+  // on the segment's first chunks, then the most recently read)
+  const int tok_last = (c0 + nc - 1) * C;
+  const __bf16* kp = k + row_off(pr.sk, b, tok_last + (tid & 63), h) + 8 * ((tid >> 6) & 1);
+  const __bf16* vp = v + row_off(pr.sv, b, tok_last + 2 * (tid >> 3), h) + 8 * (tid & 7);
+  const long long k_step = -(long long)C * pr.sk[1], v_step = -(long long)C * pr.sv[1];
+  switch (w) {
+    case 0: state_dpp_loop<0>(tl, kp, vp, k_step, v_step, pr.sv[1], nc, tid, S, Z); break;
+    case 1: state_dpp_loop<1>(tl, kp, vp, k_step, v_step, pr.sv[1], nc, tid, S, Z); break;
+    case 2: state_dpp_loop<2>(tl, kp, vp, k_step, v_step, pr.sv[1], nc, tid, S, Z); break;
+    default: state_dpp_loop<3>(tl, kp, vp, k_step, v_step, pr.sv[1], nc, tid, S, Z); break;
+  }
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) {
+    const int i = 4 * w + sl;
+    if (kPackedOut) {
+      store_packed_from_direct(out, i, S[sl], lane);
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        *reinterpret_cast<f32x4*>(out + ((i * 4 + nt) * 64 + lane) * 4) = S[sl][nt];
+    }
+  }
+  if (w == 0) *reinterpret_cast<f32x4*>(out + LY::kZOff + lane * 4) = Z;
+}
+
+// ==========================================================================================
 // Segment walk: start from the segment's exclusive prefix (S_{<c}, Z_{<c}); for every chunk,
 // outputs = (readout of the prefix + causal intra-chunk tile) / (eps + denominators), then
 // the chunk's own state is added.  One workgroup per (segment, head, batch) (SegGrid).
@@ -683,10 +860,10 @@ hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int gw, in
     launch_kernel(chunk_state_fast_kernel<true, 4>, grid, kThreads, 0, st, pr, sg, L, n_seg,
                   n_used, kk, vv, states);
   else if (packed)
-    launch_kernel(chunk_state_fast_kernel<true, P>, grid, kThreads, 0, st, pr, sg, L, n_seg,
+    launch_kernel(chunk_state_dpp_kernel<true>, grid, kThreads, 0, st, pr, sg, L, n_seg,
                   n_used, kk, vv, states);
   else
-    launch_kernel(chunk_state_fast_kernel<false, P>, grid, kThreads, 0, st, pr, sg, L, n_seg,
+    launch_kernel(chunk_state_dpp_kernel<false>, grid, kThreads, 0, st, pr, sg, L, n_seg,
                   n_used, kk, vv, states);
   return hipGetLastError();
 }
