@@ -14,6 +14,10 @@ microseconds per kernel, so that pass's step time is reported separately).
 Printed: one JSON line.  value = head-tokens (B*H*T) per second.  roofline: the algorithmic
 bytes (bf16 q, k, v in, fp32 o out) or flops of the step, whichever bound is slower at MI355X's
 peaks (8 TB/s HBM, 2.5 PFLOP/s dense bf16 MFMA), over the dominant kernel's average duration.
+step_roofline: the same for the whole step (every kernel of it).  warmup_steps_run: the untimed
+steps actually run before the timed ones (at least W, more until --warmup-floor-s seconds of
+load have passed).  literal_scan: the 131k workload with one state per chunk and the 11-level
+prefix scan over them.
 cpu_baseline: the fp64 CPU oracle (brute-force closed form) timed on a bounded uniform sample
 of the same workload's query rows, scaled to head-tokens/s.  sweep: tokens/s of the chunked
 form at T = 1k .. 128k with B*T = 131072 (the metric's dependence on T), each beside the
@@ -233,20 +237,37 @@ def cpu_baseline(w, target_s=12.0):
     }
 
 
-def timed_steps(step, steps, warmup, dev, per_step=False):
-    """W untimed steps, then K steps between two events on the launch stream (the step time),
-    then K more steps with the library's per-kernel events on the same stream (the kernel
-    durations; those events cost a few microseconds per kernel, so they stay out of the step
-    time).  Returns (ms per step, {kernel: (launches, total ms)}, instrumented ms per step,
-    (median, min) ms of single steps or None): with per_step, K more steps with an event after
-    each give the distribution of single-step times."""
+def warm_up(step, warmup, floor_s=0.0):
+    """At least `warmup` untimed steps, and more until `floor_s` seconds of wall time have
+    passed (the GPU's clocks take a fraction of a second of load to settle); returns the number
+    of steps run.  The host synchronizes every 16 steps, so wall time is GPU time."""
+    import torch
+
+    t0, n = time.perf_counter(), 0
+    while n < warmup or time.perf_counter() - t0 < floor_s:
+        step()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
+def timed_steps(step, steps, warmup, dev, per_step=False, warmup_floor_s=0.0, info=None):
+    """W untimed steps (at least; more until warmup_floor_s seconds have passed, their number
+    stored in info["warmup_steps_run"]), then K steps between two events on the launch stream
+    (the step time), then K more steps with the library's per-kernel events on the same stream
+    (the kernel durations; those events cost a few microseconds per kernel, so they stay out of
+    the step time).  Returns (ms per step, {kernel: (launches, total ms)}, instrumented ms per
+    step, (median, min) ms of single steps or None): with per_step, K more steps with an event
+    after each give the distribution of single-step times."""
     import torch
 
     import kernelized_psd_feature_amd as K
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    n_warm = warm_up(step, warmup, warmup_floor_s)
+    if info is not None:
+        info["warmup_steps_run"] = n_warm
     stream = torch.cuda.current_stream(dev)
 
     def region(instrumented):
@@ -344,6 +365,32 @@ def sweep(q, k, v, args, dev):
     return out
 
 
+def literal_scan(q, k, v, o, w, args, dev):
+    """The chunked form with one state per chunk (seg_chunks = 1): every one of the T / 64 chunk
+    states per head is materialized and combined by the prefix scan, ceil(log2(T / 64)) levels
+    (11 at T = 131072), as the problem statement writes the inter-chunk step; beside the
+    default plan's segment walk it shows what the hierarchical form saves."""
+    import torch
+
+    import kernelized_psd_feature_amd as K
+
+    need = K.chunked_workspace_size(q, k, v, chunk=w.chunk, seg_chunks=1, state=args.state)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    plan = K.chunked_plan(q, k, v, chunk=w.chunk, seg_chunks=1, state=args.state)
+
+    def step():
+        K.fwd_chunked(q, k, v, chunk=w.chunk, seg_chunks=1, out=o, workspace=ws,
+                      state=args.state)
+
+    ms, per_kernel, _, _ = timed_steps(step, 10, 3, dev)
+    del ws
+    tokens = w.B * w.H * w.T
+    return {"ms": round(ms, 5), "tokens_per_s": round(tokens / (ms / 1e3), 1),
+            "segments": plan["segments"], "chunks_per_segment": plan["chunks_per_segment"],
+            "scan_levels": plan["scan_levels"], "workspace_bytes": need,
+            "kernels_ms": {n: round(t / max(c, 1), 5) for n, (c, t) in per_kernel.items() if c}}
+
+
 def crossover(w, dev):
     """Both forms at each T of the p = 32 crossover workload (B = 4, H = 16, T = 1k .. 16k):
     step times, head-tokens/s and which form is faster there."""
@@ -397,7 +444,9 @@ def run_chunked(args, dev, w):
         else:
             K.fwd_quadratic(q, k, v, out=o, out_dtype=out_dtype, groups=args.groups)
 
-    ms, per_kernel, ms_inst, dist = timed_steps(step, args.steps, args.warmup, dev, True)
+    warm = {}
+    ms, per_kernel, ms_inst, dist = timed_steps(step, args.steps, args.warmup, dev, True,
+                                                warmup_floor_s=args.warmup_floor_s, info=warm)
     tokens = w.B * w.H * w.T
     dom = "chunk_output" if args.form == "chunked" else "quadratic"
     _, total_ms = per_kernel[dom]
@@ -426,13 +475,18 @@ def run_chunked(args, dev, w):
         "kernels_ms": {n: round(t / max(c, 1), 5) for n, (c, t) in per_kernel.items() if c},
         "ms_per_step_with_kernel_events": round(ms_inst, 5),
         "ms_per_step_median": round(dist[0], 5), "ms_per_step_min": round(dist[1], 5),
+        "step_roofline": roofline(fpt * tokens, bpt * tokens, ms / 1e3),
         "step_roofline_frac": roofline(fpt * tokens, bpt * tokens, ms / 1e3)["frac"],
+        "warmup_floor_s": args.warmup_floor_s, "warmup_steps_run": warm["warmup_steps_run"],
         "dominant_kernel_source_sha": sha,
         "inputs": inputs, "device": device_info(dev),
     }
     if args.form == "chunked":
         line["chunked_plan"] = K.chunked_plan(q, k, v, chunk=w.chunk, seg_chunks=args.seg,
                                               state=args.state, groups=args.groups)
+    if args.form == "chunked" and w.name == "long_context_131k" and not args.no_literal \
+            and args.layout == "bthd" and args.out == "fp32" and args.groups == 1:
+        line["literal_scan"] = literal_scan(q, k, v, o, w, args, dev)
     if args.graph:
         line["ms_per_step_graph"] = round(graph_ms(step, args.steps, dev), 5)
     if not args.no_calibration:
@@ -497,7 +551,9 @@ def run_decode(args, dev):
     def step():
         K.decode(q, k, v, state, out=o)
 
-    ms, per_kernel, ms_inst, dist = timed_steps(step, args.steps, args.warmup, dev, True)
+    warm = {}
+    ms, per_kernel, ms_inst, dist = timed_steps(step, args.steps, args.warmup, dev, True,
+                                                warmup_floor_s=args.warmup_floor_s, info=warm)
     tokens = w.B * w.H * w.T
     launches, total_ms = per_kernel["decode"]
     avg_ms = total_ms / max(launches, 1)
@@ -519,6 +575,7 @@ def run_decode(args, dev):
         "kernels_ms": {n: round(t / max(c, 1), 5) for n, (c, t) in per_kernel.items() if c},
         "ms_per_step_with_kernel_events": round(ms_inst, 5),
         "ms_per_step_median": round(dist[0], 5), "ms_per_step_min": round(dist[1], 5),
+        "warmup_floor_s": args.warmup_floor_s, "warmup_steps_run": warm["warmup_steps_run"],
     }
     if not args.no_calibration:
         line["measured_peaks"] = with_measured_peak(line["roofline"], measured_peaks(dev))
@@ -532,7 +589,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed steps first: the clocks need ~0.1 s of load to settle")
+                    help="untimed steps first (at least; see --warmup-floor-s)")
+    ap.add_argument("--warmup-floor-s", type=float, default=0.3,
+                    help="keep warming up until this much wall time has passed: the clocks "
+                         "need a fraction of a second of load to settle (the steps run are "
+                         "reported as warmup_steps_run)")
     ap.add_argument("--workload", default="long_context_131k")
     ap.add_argument("--form", choices=["chunked", "quadratic", "decode"], default="chunked")
     ap.add_argument("--seg", type=int, default=0, help="chunks per segment (0 = library default)")
@@ -547,6 +608,8 @@ def main():
                     help="also time the step replayed from a HIP graph (ms_per_step_graph)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the T sweep")
+    ap.add_argument("--no-literal", action="store_true",
+                    help="skip the one-state-per-chunk (literal scan) form")
     ap.add_argument("--no-cold-cache", action="store_true",
                     help="skip the cache-flushed repetition (profiler runs)")
     ap.add_argument("--no-calibration", action="store_true",

@@ -30,7 +30,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_tile_kernel(
   const int sv = strip / 4;                       // float4 slots per row
   const long long seq = blockIdx.z;
   const int tile = blockIdx.y;
-  const long long col0 = (long long)blockIdx.x * strip;
+  // Consecutive workgroups go to consecutive XCDs (8), each with its own L2.  When a strip's
+  // row piece is narrower than a 128-byte line, the strips sharing a line get ids congruent
+  // mod 8, so one XCD fetches each line once (a bijection of [0, gridDim.x)).
+  long long sx = blockIdx.x;
+  const int per_line = 32 / strip;                // strips per 128-byte line of one row
+  if (per_line > 1 && gridDim.x % (8 * per_line) == 0) {
+    const long long id = blockIdx.x, blk = id / (8 * per_line);
+    sx = (blk * 8 + id % 8) * per_line + (id / 8) % per_line;
+  }
+  const long long col0 = sx * strip;
   const long long r0 = (long long)tile * tile_rows;
   const int nr = (int)min((long long)tile_rows, n - r0);
   const int nslots = nr * sv;
