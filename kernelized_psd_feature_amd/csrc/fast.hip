@@ -553,6 +553,177 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_dpp_kernel(
 }
 
 // ==========================================================================================
+// Segment state, single feature group, packed output: the packed state needs the 136 pairs
+// i <= j only, so instead of 16 direct tiles the kernel runs 11:
+//   broadcast tiles  direct tiles i = 0 .. 7 formed as in chunk_state_dpp_kernel (rows (i, j)
+//                    for every j; their packed rows are those with j >= i),
+//   gathered tiles   three tiles of the pairs (i, j) with 8 <= i <= j, formed from fp32 copies
+//                    of k coordinates 8 .. 15 in LDS as in chunk_state_fast_kernel.  They hold
+//                    exactly the twelve packed row quads (i, J) = (i, 4J .. 4J + 3) with i >= 8
+//                    (J = 2: i = 8 .. 11; J = 3: i = 8 .. 15), quad q in lane group q % 4 of
+//                    tile q / 4, so each lane stores its four rows with one 16-byte write.
+// Wave w owns broadcast tiles 2w, 2w + 1 and gathered tile w (w < 3); wave 3 also forms Z.
+// Against 16 broadcast tiles: 88 instead of 128 MFMAs and ~30 % less VALU per chunk, for
+// 24 KB more LDS reads; the same products summed in the same order, so the same states.
+// ==========================================================================================
+constexpr int KT8ROWS = 2 * 8 + 1;            // k_8..15, 2 k_8..15, zeros
+
+struct __align__(16) KvktTiles {
+  __bf16 K[C][KSROW];                 // k rows (bf16), row-major
+  __bf16 V[C][VROW];                  // v rows (bf16), row-major
+  float KT[KT8ROWS][KTROW];           // coordinates 8 .. 15 of k transposed, fp32 (exact)
+};
+
+// quad q = 0 .. 11 of the gathered tiles -> (i, J)
+__device__ __forceinline__ void gathered_quad(int q, int& i, int& J) {
+  J = q < 4 ? 2 : 3;
+  i = q < 4 ? 8 + q : 8 + (q - 4);
+}
+
+template <int W>
+__device__ __forceinline__ void state_hybrid_loop(KvktTiles (&tl)[2], const __bf16* kp,
+                                                  const __bf16* vp, long long k_step,
+                                                  long long v_step, long long sv_t, int nc,
+                                                  int tid, f32x4 (&S)[3][4], f32x4& Z) {
+  const int lane = tid & 63;
+  const int krow = tid & 63, khalf = (tid >> 6) & 1, a = tid >> 3, c8 = tid & 7;
+  // this lane's row of gathered tile W: pair (i, j) -> K^T rows (i for the diagonal, the
+  // doubled copy above it, the zero row below it) and j
+  int irow = 2 * 8, jrow = 0;
+  if (W < 3) {
+    int i, J;
+    gathered_quad(4 * W + ((lane & 15) >> 2), i, J);
+    const int j = 4 * J + (lane & 3);
+    irow = i > j ? 2 * 8 : (i == j ? i - 8 : 8 + i - 8);
+    jrow = j - 8;
+  }
+  auto load = [&](StageKv& x) {
+    if (W >= 2) x.k = ld16(kp);
+    x.v0 = ld16(vp);
+    x.v1 = ld16(vp + sv_t);
+  };
+  auto store = [&](const StageKv& x, KvktTiles& t) {
+    if (W >= 2) *reinterpret_cast<uint4*>(&t.K[krow][8 * khalf]) = x.k;
+    if (W == 3) {                                  // coordinates 8 .. 15 of row krow
+      const uint32_t wd[4] = {x.k.x, x.k.y, x.k.z, x.k.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf_lo(wd[e]), hi = bf_hi(wd[e]);
+        t.KT[2 * e][krow] = lo;
+        t.KT[2 * e + 1][krow] = hi;
+        t.KT[8 + 2 * e][krow] = 2.f * lo;            // exact
+        t.KT[8 + 2 * e + 1][krow] = 2.f * hi;
+      }
+    }
+    *reinterpret_cast<uint4*>(&t.V[2 * a][8 * c8]) = x.v0;
+    *reinterpret_cast<uint4*>(&t.V[2 * a + 1][8 * c8]) = x.v1;
+  };
+  auto advance = [&]() {
+    kp += k_step;
+    vp += v_step;
+  };
+  StageKv sa, sb;
+  load(sa);
+  store(sa, tl[0]);
+  if (nc > 1) { advance(); load(sa); }
+  if (nc > 2) { advance(); load(sb); }
+  __syncthreads();
+  auto step = [&](int c, StageKv& next) {
+    const KvktTiles& t = tl[c & 1];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const bf16x8 kt = v_frag(t.K, m, 0, lane);      // k_s[lane % 16] of this lane's keys
+      float kf[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) kf[r] = (float)kt[r];
+      bf16x8 vb[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(t.V, m, nt, lane);
+      const bf16x8 a0 = phik_bcast<2 * W>(kf), a1 = phik_bcast<2 * W + 1>(kf);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        S[0][nt] = mfma32(a0, vb[nt], S[0][nt]);
+        S[1][nt] = mfma32(a1, vb[nt], S[1][nt]);
+      }
+      if (W < 3) {
+        const bf16x8 a2 = phik_packed_frag(t, irow, jrow, m, lane);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) S[2][nt] = mfma32(a2, vb[nt], S[2][nt]);
+      } else {
+        Z = mfma32(kt, kt, Z);
+      }
+    }
+    // the other buffer was last read in the previous iteration, before its barrier
+    if (c + 1 < nc) store(next, tl[(c + 1) & 1]);
+    if (c + 3 < nc) { advance(); load(next); }         // chunk c + 3
+    __syncthreads();
+  };
+  for (int c = 0; c < nc; c += 2) {
+    step(c, sa);                       // chunk c+1 is in sa, chunk c+2 in sb
+    if (c + 1 < nc) step(c + 1, sb);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 3) void chunk_state_hybrid_kernel(
+    DevProblem pr, SegGrid sg, int L, int n_seg, int n_used, const __bf16* __restrict__ k,
+    const __bf16* __restrict__ v, float* __restrict__ states) {
+  using LY = Layout<true, P>;
+  __shared__ KvktTiles tl[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const SegBlock blk = seg_block(sg, pr.H);
+  if (!blk.live) return;                           // padding of the grid (whole workgroup)
+  const int seg = blk.seg, h = blk.h, b = blk.b;
+  const int n_chunks = pr.T / C;
+  const int c0 = seg * L, nc = min(L, n_chunks - c0);
+  float* out = states + ((long long)(b * pr.H + h) * n_seg + seg) * LY::kStateFloats;
+  if (seg >= n_used) {
+    // a state no prefix needs (the last segment's, in the forward): zeros, k and v unread
+    for (int x = tid; x < LY::kStateFloats / 4; x += kThreads)
+      reinterpret_cast<float4*>(out)[x] = float4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  if (tid < KTROW) {                               // the zero row of both buffers
+    tl[0].KT[2 * 8][tid] = 0.f;
+    tl[1].KT[2 * 8][tid] = 0.f;
+  }
+  f32x4 S[3][4];
+#pragma unroll
+  for (int sl = 0; sl < 3; ++sl)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) S[sl][nt] = zero4();
+  f32x4 Z = zero4();
+  // the segment is read last chunk first (the sum is order-free; the walk that follows starts
+  // on the segment's first chunks, then the most recently read)
+  const int tok_last = (c0 + nc - 1) * C;
+  const __bf16* kp = k + row_off(pr.sk, b, tok_last + (tid & 63), h) + 8 * ((tid >> 6) & 1);
+  const __bf16* vp = v + row_off(pr.sv, b, tok_last + 2 * (tid >> 3), h) + 8 * (tid & 7);
+  const long long k_step = -(long long)C * pr.sk[1], v_step = -(long long)C * pr.sv[1];
+  switch (w) {
+    case 0: state_hybrid_loop<0>(tl, kp, vp, k_step, v_step, pr.sv[1], nc, tid, S, Z); break;
+    case 1: state_hybrid_loop<1>(tl, kp, vp, k_step, v_step, pr.sv[1], nc, tid, S, Z); break;
+    case 2: state_hybrid_loop<2>(tl, kp, vp, k_step, v_step, pr.sv[1], nc, tid, S, Z); break;
+    default: state_hybrid_loop<3>(tl, kp, vp, k_step, v_step, pr.sv[1], nc, tid, S, Z); break;
+  }
+  store_packed_from_direct(out, 2 * w, S[0], lane);
+  store_packed_from_direct(out, 2 * w + 1, S[1], lane);
+  if (w < 3) {
+    // gathered quad 4w + g of this lane: rows (i, 4J + r) -> packed tile 2 (idx / 4) + i % 2,
+    // lane group idx % 4, idx = J (J + 1) + (i - i % 2) / 2, the same register r
+    const int g = lane >> 4, c = lane & 15;
+    int i, J;
+    gathered_quad(4 * w + g, i, J);
+    const int idx = J * (J + 1) + (i >> 1);
+    const int t = 2 * (idx >> 2) + (i & 1), gp = idx & 3;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      *reinterpret_cast<f32x4*>(out + ((t * 4 + nt) * 64 + 16 * gp + c) * 4) = S[2][nt];
+  } else {
+    *reinterpret_cast<f32x4*>(out + LY::kZOff + lane * 4) = Z;
+  }
+}
+
+// ==========================================================================================
 // Segment walk: start from the segment's exclusive prefix (S_{<c}, Z_{<c}); for every chunk,
 // outputs = (readout of the prefix + causal intra-chunk tile) / (eps + denominators), then
 // the chunk's own state is added.  One workgroup per (segment, head, batch) (SegGrid).
@@ -860,8 +1031,8 @@ hipError_t launch_chunk_state_fast(const DevProblem& pr, bool packed, int gw, in
     launch_kernel(chunk_state_fast_kernel<true, 4>, grid, kThreads, 0, st, pr, sg, L, n_seg,
                   n_used, kk, vv, states);
   else if (packed)
-    launch_kernel(chunk_state_dpp_kernel<true>, grid, kThreads, 0, st, pr, sg, L, n_seg,
-                  n_used, kk, vv, states);
+    launch_kernel(chunk_state_hybrid_kernel, grid, kThreads, 0, st, pr, sg, L, n_seg, n_used,
+                  kk, vv, states);
   else
     launch_kernel(chunk_state_dpp_kernel<false>, grid, kThreads, 0, st, pr, sg, L, n_seg,
                   n_used, kk, vv, states);
