@@ -175,6 +175,10 @@ hipError_t launch_chunk_output_generic(const DevProblem& pr, bool in_bf16, bool 
                                        float* den, const float* states, int n_chunks,
                                        hipStream_t st);
 
+// Prefix scan of n <= 64 rows per sequence (one lane per row, the tree across a wave).
+hipError_t launch_scan_short(float* x, long long n_seq, long long n, long long elems,
+                             int exclusive, float* totals, hipStream_t st);
+
 // Prefix scan of one tile-level: rows [tile*tile_rows, ...) of every sequence, `strip`
 // coordinates per workgroup.  tile_offsets (nullable) holds the exclusive offset of each
 // tile, [n_seq][n_tiles][elems].

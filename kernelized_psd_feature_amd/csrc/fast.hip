@@ -192,17 +192,24 @@ __device__ __forceinline__ s16x4 row4_frag(const __bf16 (*X)[QROW], int row0, in
 }
 
 // Squared-score tile of keys [s0, s0 + 16) (rows) against this lane's query t (column), from
-// the A operand kf (k rows) and the B operand qf (q_t[4g .. 4g + 3]), masked and rounded to bf16
-// P.  GW < 16 (KATA-Mg, groups of GW coordinates): one product per group, the query operand cut
-// to the lane groups holding that group's coordinates, and the squared group dots summed.
+// the A operand kf (k rows) and the B operand qf (q_t[4g .. 4g + 3]): the bf16 weights P of
+// slots r = 0, 1 and 2, 3 as packed pairs pw, and their sum added to lsum (a bf16 pair dot with
+// ones, so the sum is taken over the rounded weights).  kMask (the diagonal tile): keep01 and
+// keep23 clear the halves of the future keys (+0).  GW < 16 (KATA-Mg, groups of GW
+// coordinates): one product per group, the query operand cut to the lane groups holding that
+// group's coordinates, and the squared group dots summed.
 template <int GW, bool kMask>
-__device__ __forceinline__ void score_tile(const s16x4& kf, const s16x4& qf, int s0, int t,
-                                           int lane, __bf16 out[4], float& lsum) {
+__device__ __forceinline__ void score_tile(const s16x4& kf, const s16x4& qf, uint32_t keep01,
+                                           uint32_t keep23, int lane, uint32_t (&pw)[2],
+                                           float& lsum) {
+  f32x4 x2;
   if constexpr (GW == P) {
-    square_mask<kMask>(mfma16(kf, qf, zero4()), s0, t, lane, out, lsum);
+    const f32x4 sc = mfma16(kf, qf, zero4());
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x2[r] = sc[r] * sc[r];
   } else {
     const int grp = (4 * (lane >> 4)) / GW;
-    f32x4 x2 = zero4();
+    x2 = zero4();
 #pragma unroll
     for (int j = 0; j < P / GW; ++j) {
       const s16x4 qj = grp == j ? qf : s16x4{0, 0, 0, 0};
@@ -210,8 +217,15 @@ __device__ __forceinline__ void score_tile(const s16x4& kf, const s16x4& qf, int
 #pragma unroll
       for (int r = 0; r < 4; ++r) x2[r] = fmaf(sc[r], sc[r], x2[r]);
     }
-    weight_mask<kMask>(x2, s0, t, lane, out, lsum);
   }
+  pw[0] = pack_bf16x2(x2[0], x2[1]);
+  pw[1] = pack_bf16x2(x2[2], x2[3]);
+  if (kMask) {
+    pw[0] &= keep01;
+    pw[1] &= keep23;
+  }
+  lsum = sum_bf16x2(pw[0], lsum);
+  lsum = sum_bf16x2(pw[1], lsum);
 }
 
 // ==========================================================================================
@@ -296,6 +310,24 @@ __device__ __forceinline__ void state_update(const TL& tl, const UpdateRows<kPac
       const bf16x8 kf = kcol_frag(tl, m, lane);
       Z = mfma32(kf, kf, Z);
     }
+  }
+}
+
+// One 32-key step m of the S update from value fragments vb the caller already holds (the walk
+// shares them with its P.V step).
+template <bool kPacked, int GW, class TL>
+__device__ __forceinline__ void state_update_step(const TL& tl, const UpdateRows<kPacked, GW>& ur,
+                                                  f32x4 (&S)[Layout<kPacked, GW>::kSlots][4],
+                                                  const bf16x8 (&vb)[4], int w, int m,
+                                                  int lane) {
+  using LY = Layout<kPacked, GW>;
+#pragma unroll
+  for (int sl = 0; sl < LY::kSlots; ++sl) {
+    if (!LY::owns(w, sl)) continue;
+    const bf16x8 a = kPacked ? phik_packed_frag(tl, ur.irow[sl], ur.jrow[sl], m, lane)
+                             : phik_frag(tl, ur.irow[sl], m, lane);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) S[sl][nt] = mfma32(a, vb[nt], S[sl][nt]);
   }
 }
 
@@ -632,26 +664,22 @@ __device__ __forceinline__ void state_hybrid_loop(KvktTiles (&tl)[2], const __bf
     const KvktTiles& t = tl[c & 1];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
+      // the A operands first, then one value tile at a time (fewer registers live at once)
+      bf16x8 a2;
+      if (W < 3) a2 = phik_packed_frag(t, irow, jrow, m, lane);
       const bf16x8 kt = v_frag(t.K, m, 0, lane);      // k_s[lane % 16] of this lane's keys
       float kf[8];
 #pragma unroll
       for (int r = 0; r < 8; ++r) kf[r] = (float)kt[r];
-      bf16x8 vb[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(t.V, m, nt, lane);
       const bf16x8 a0 = phik_bcast<2 * W>(kf), a1 = phik_bcast<2 * W + 1>(kf);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        S[0][nt] = mfma32(a0, vb[nt], S[0][nt]);
-        S[1][nt] = mfma32(a1, vb[nt], S[1][nt]);
+        const bf16x8 vb = v_frag(t.V, m, nt, lane);
+        S[0][nt] = mfma32(a0, vb, S[0][nt]);
+        S[1][nt] = mfma32(a1, vb, S[1][nt]);
+        if (W < 3) S[2][nt] = mfma32(a2, vb, S[2][nt]);
       }
-      if (W < 3) {
-        const bf16x8 a2 = phik_packed_frag(t, irow, jrow, m, lane);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) S[2][nt] = mfma32(a2, vb[nt], S[2][nt]);
-      } else {
-        Z = mfma32(kt, kt, Z);
-      }
+      if (W == 3) Z = mfma32(kt, kt, Z);
     }
     // the other buffer was last read in the previous iteration, before its barrier
     if (c + 1 < nc) store(next, tl[(c + 1) & 1]);
@@ -845,6 +873,11 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
   publish();
   __syncthreads();
 
+  // diagonal score tile (keys 16w + 4g + r against token 16w + l16): the key is in the past or
+  // present for 4g + r <= l16; masks of the packed pairs r = 0, 1 and 2, 3
+  const uint32_t keep01 = (4 * g <= l16 ? 0xffffu : 0u) | (4 * g + 1 <= l16 ? 0xffff0000u : 0u);
+  const uint32_t keep23 = (4 * g + 2 <= l16 ? 0xffffu : 0u) | (4 * g + 3 <= l16 ? 0xffff0000u : 0u);
+
   // output pointer of this lane's first store in the first chunk: token 16w + 8 (lane / 32),
   // column lane % 32
   Tout* orow = o + row_off(pr.so, b, c0 * C + 16 * w + 8 * (lane >> 5), h) + (lane & 31);
@@ -860,41 +893,42 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     const uint4 vb4 = *reinterpret_cast<const uint4*>(sm.vbad);
     const bool vbad = __builtin_amdgcn_readfirstlane(vb4.x | vb4.y | vb4.z | vb4.w) != 0;
 
-    // ---- intra-chunk tile of this wave's tokens ----
+    // ---- intra-chunk tile of this wave's tokens, and S += Phi(K)^T V with the same value
+    // fragments (the readout reads the published S_{<c}, not these registers) ----
     float lsum = 0.f;
     f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
     const s16x4 qf = row4_frag(tl.Qs, 16 * w, lane);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      if (2 * m > w) break;                        // key tiles entirely in the future
+      bf16x8 vb[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(tl.V, m, nt, lane);
+      state_update_step<kPacked, GW>(tl, ur, S, vb, w, m, lane);
+      if (2 * m > w) continue;                     // key tiles entirely in the future
       // the step holding the wave's diagonal tile (and any future keys) when a value of the
       // chunk is an infinity or a nan (rare, wave-uniform): exact path
       const bool fix = vbad && 2 * m + 1 >= w;
-      __bf16 pa[8];
+      uint32_t pw[2][2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int ms = 2 * m + half;
         if (ms < w) {
-          score_tile<GW, false>(row4_frag(tl.Ks, 16 * ms, lane), qf, 16 * ms, t, lane,
-                                &pa[4 * half], lsum);
+          score_tile<GW, false>(row4_frag(tl.Ks, 16 * ms, lane), qf, 0u, 0u, lane, pw[half],
+                                lsum);
         } else if (ms == w) {
-          score_tile<GW, true>(row4_frag(tl.Ks, 16 * ms, lane), qf, 16 * ms, t, lane,
-                               &pa[4 * half], lsum);
+          score_tile<GW, true>(row4_frag(tl.Ks, 16 * ms, lane), qf, keep01, keep23, lane,
+                               pw[half], lsum);
         } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pa[4 * half + r] = (__bf16)0.f;
+          pw[half][0] = pw[half][1] = 0u;
         }
       }
-      bf16x8 a;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) a[r] = pa[r];
+      const bf16x8 a = __builtin_bit_cast(bf16x8, uint4{pw[0][0], pw[0][1], pw[1][0], pw[1][1]});
       if (!fix) {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) O[nt] = mfma32(a, v_frag(tl.V, m, nt, lane), O[nt]);
+        for (int nt = 0; nt < 4; ++nt) O[nt] = mfma32(a, vb[nt], O[nt]);
       } else {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          O[nt] = mfma32(a, finite_or_zero(v_frag(tl.V, m, nt, lane)), O[nt]);
+        for (int nt = 0; nt < 4; ++nt) O[nt] = mfma32(a, finite_or_zero(vb[nt]), O[nt]);
         const int cols[4] = {l16, 16 + l16, 32 + l16, 48 + l16};
         nonfinite_fixup<4>(O, tl.V, a, 32 * m, 16 * w, cols, lane);
       }
@@ -923,14 +957,12 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
       zq = fmaf(bf_lo(qq.y), y[2], zq);
       zq = fmaf(bf_hi(qq.y), y[3], zq);
     }
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    zq += __shfl_xor(zq, 16);
-    zq += __shfl_xor(zq, 32);
+    // the lane groups' shares of both sums at once; 1 / D_t from v_rcp_f32 (1 ulp)
+    const float dsum = sum_xor32(sum_xor16(zq + lsum));
     if (g == 0) {
-      const float D = pr.eps + (zq + lsum);
+      const float D = pr.eps + dsum;
       sm.den[t] = D;
-      sm.inv[t] = 1.f / D;
+      sm.inv[t] = __builtin_amdgcn_rcpf(D);
     }
 
     // ---- readout phi(q_t)^T S_{<c} over all published state rows ----
@@ -974,8 +1006,12 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
       den_out[((long long)b * pr.T + tok0 + 16 * w + lane) * pr.H + h] = sm.den[16 * w + lane];
     orow += C * so_t;
 
-    // ---- state update with this chunk: S += Phi(K)^T V, Z += K^T K ----
-    state_update<kPacked, GW>(tl, ur, S, Z, w, lane, true);
+    // ---- Z += K^T K (S was updated with the intra-chunk tile) ----
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const bf16x8 kf = kcol_frag(tl, m, lane);
+      Z = mfma32(kf, kf, Z);
+    }
     __syncthreads();                               // all reads of this chunk's tiles and Sb done
     if (c + 1 < nc) {
       stage_store(st, tl, true, tid);

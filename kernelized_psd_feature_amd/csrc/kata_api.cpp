@@ -208,6 +208,7 @@ kata_status check_forward_args(const kata_problem* pr, Form f, const void* q, co
 hipError_t run_scan(float* x, int64_t n_seq, int64_t n, int64_t elems, int exclusive,
                     float* totals, char* ws, hipStream_t st) {
   kata::ScanPlan sp = kata::plan_scan(n_seq, n, elems);
+  if (sp.wave) return kata::launch_scan_short(x, n_seq, n, elems, exclusive, totals, st);
   if (sp.n_tiles == 1)
     return kata::launch_scan_tiles(x, n_seq, n, elems, (int)sp.strip, (int)n, 1, exclusive,
                                    totals, nullptr, st);

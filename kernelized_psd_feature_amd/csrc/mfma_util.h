@@ -96,6 +96,32 @@ __device__ __forceinline__ void weight_mask(const f32x4& x2, int s0, int t, int 
 template <typename Tout>
 __device__ __forceinline__ Tout cvt_out(float x) { return from_f32<Tout>(x); }
 
+// Two floats rounded to bf16 (round to nearest even) and packed, a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) float f2;
+  typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, b2));
+}
+// acc + lo(w) + hi(w) for a packed bf16 pair w (v_dot2 with ones, fp32 accumulation).
+__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w),
+                                         __builtin_bit_cast(b2, 0x3f803f80u), acc, false);
+}
+
+// x + x(lane ^ 16) and x + x(lane ^ 32) in every lane, from the row-swap permutes (no LDS
+// round trip).  Swapping a register with a copy of itself leaves the two 16-lane rows of each
+// pair in the two results, so their sum is the pair sum in both rows (the same value the two
+// orders of an IEEE add give).
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // ---- non-finite values and masked P.V products ------------------------------------------
 // Inside an MFMA P.V product a masked weight P_ts = 0 still meets the value v_s of every key of
 // the K step, and 0 * inf or 0 * nan is nan: a non-finite value of a later token would reach

@@ -137,6 +137,16 @@ ScanPlan plan_scan(int64_t n_seq, int64_t n, int64_t elems) {
   sp.n = n;
   sp.elems = elems;
   if (n <= 0 || n_seq <= 0 || elems <= 0) return sp;
+  if (n <= kScanWaveRows) {
+    // strips of 64 coordinates, one lane per row, ceil(log2 n) DPP levels
+    sp.wave = true;
+    sp.tile_rows = n;
+    sp.strip = 64;
+    sp.n_tiles = 1;
+    sp.ws_bytes = 0;
+    sp.levels = ceil_log2(n);
+    return sp;
+  }
   int64_t np2 = next_pow2(n);
   if (np2 * 4 <= kScanLdsFloats) {
     // one tree over all n rows; a strip of at least 64 coordinates, widened for short scans

@@ -48,7 +48,10 @@ struct ScanPlan {
   int64_t n_tiles = 0;        // ceil(n / tile_rows)
   size_t ws_bytes = 0;        // tile totals (recursive), 0 for a single tile
   int levels = 0;             // depth of the combining tree
+  bool wave = false;          // n <= kScanWaveRows: one lane per row, the tree across a wave
 };
+
+constexpr int64_t kScanWaveRows = 64;   // rows of the wave form (one per lane)
 
 constexpr int64_t kMaxT = int64_t(1) << 26;
 constexpr int64_t kScanLdsFloats = 16384;   // per buffer; two buffers = 128 KiB of LDS

@@ -3,14 +3,18 @@
 // The states of one sequence form an [n][elems] fp32 array; the scan runs independently for
 // every element.  Because the state update is additive and commutative (ai.info Main
 // Findings, readout-gate bullet), the associative operator is addition, and the scan is a
-// Kogge-Stone tree of depth ceil(log2 n) (gist.science section 2.3: inter-chunk depth
-// O(N_C) -> O(log N_C)).
+// tree of depth ceil(log2 n) (gist.science section 2.3: inter-chunk depth O(N_C) ->
+// O(log N_C)).  Two forms:
 //
-// One workgroup takes one sequence, one tile of rows and a strip of `strip` coordinates
-// (a multiple of 4, so every access is a float4; for strip = 64 a wave reads four whole
-// 256-byte rows per instruction).  The tile is held in two LDS buffers: each tree level
-// writes the thread's float4 slots to one buffer, synchronizes, and adds the slot 2^l rows
-// up; alternating buffers needs a single barrier per level.
+// scan_short_kernel (n <= 64): one lane per row, the tree across the lanes of a wave by DPP
+// moves (see below).
+//
+// scan_tile_kernel (tiles of up to 256 rows, Kogge-Stone): one workgroup takes one sequence,
+// one tile of rows and a strip of `strip` coordinates (a multiple of 4, so every access is a
+// float4; for strip = 64 a wave reads four whole 256-byte rows per instruction).  The tile is
+// held in two LDS buffers: each tree level writes the thread's float4 slots to one buffer,
+// synchronizes, and adds the slot 2^l rows up; alternating buffers needs a single barrier per
+// level.
 #include "device.h"
 
 namespace kata {
@@ -155,7 +159,107 @@ __global__ __launch_bounds__(kScanThreads) void tile_sums_kernel(
   *reinterpret_cast<float4*>(sums + (seq * n_tiles + tile) * elems + e) = acc;
 }
 
+// ---- scans of at most 64 rows --------------------------------------------------------------
+// A workgroup takes a strip of 64 coordinates of one sequence: the rows are read coalesced
+// (a wave covers four whole 256-byte row pieces per instruction) into an LDS tile, then each
+// wave takes 16 of the coordinates with one lane per row and builds the tree across its lanes
+// with DPP moves: row_shr 1, 2, 4 and 8 inside each 16-lane row, then row_bcast:15 joins rows
+// 0-1 and 2-3 and row_bcast:31 joins the halves.  Level l adds the partial sum 2^l lanes back
+// (inside a row) or the last partial of the row block before, so after ceil(log2 n) levels (the
+// ones a shorter scan needs) every lane holds its inclusive prefix; the exclusive one is a wave
+// shift by one lane.  The results go back through the tile and out coalesced: two barriers
+// instead of one per level.
+constexpr int kShortRows = 64;
+constexpr int kShortStrip = 64;                    // coordinates per workgroup
+constexpr int kShortRow = kShortStrip + 4;         // LDS row stride (floats): conflict-free
+constexpr int kShortThreads = 256;
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+  // lanes whose source lies outside the pattern (bound_ctrl) or whose row is masked off get 0
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, true));
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void scan_level(float4 (&v)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j].x += dpp_or_zero<CTRL, ROW_MASK>(v[j].x);
+    v[j].y += dpp_or_zero<CTRL, ROW_MASK>(v[j].y);
+    v[j].z += dpp_or_zero<CTRL, ROW_MASK>(v[j].z);
+    v[j].w += dpp_or_zero<CTRL, ROW_MASK>(v[j].w);
+  }
+}
+
+__global__ __launch_bounds__(kShortThreads) void scan_short_kernel(
+    float* __restrict__ x, long long n, long long elems, int exclusive, float* __restrict__ totals) {
+  __shared__ float4 tile[kShortRows * kShortRow / 4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const long long seq = blockIdx.y;
+  const long long col0 = (long long)blockIdx.x * kShortStrip;
+  float* base = x + seq * n * elems + col0;
+  constexpr int kVec = kShortStrip / 4;            // float4 per row piece
+  const int nv = (int)n * kVec;
+  // rows in: thread s takes row s / 16, float4 s % 16
+  for (int s = tid; s < nv; s += kShortThreads) {
+    const int r = s / kVec, c = s % kVec;
+    if (col0 + 4 * c < elems)
+      tile[r * (kShortRow / 4) + c] = *reinterpret_cast<const float4*>(base + r * elems + 4 * c);
+  }
+  __syncthreads();
+  // wave w: coordinates 16 w .. 16 w + 15 of the strip, lane = row
+  const bool row_ok = lane < n;
+  float4 v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    v[j] = row_ok ? tile[lane * (kShortRow / 4) + 4 * w + j] : make_float4(0.f, 0.f, 0.f, 0.f);
+  // DPP controls: row_shr:k = 0x110 + k, row_bcast:15 = 0x142, row_bcast:31 = 0x143
+  if (n > 1) scan_level<0x111, 0xF>(v);
+  if (n > 2) scan_level<0x112, 0xF>(v);
+  if (n > 4) scan_level<0x114, 0xF>(v);
+  if (n > 8) scan_level<0x118, 0xF>(v);
+  if (n > 16) scan_level<0x142, 0xA>(v);           // rows 1 and 3 take lane 15 of the row before
+  if (n > 32) scan_level<0x143, 0xC>(v);           // rows 2 and 3 take lane 31
+  if (totals && lane == n - 1) {
+    float* tp = totals + seq * elems + col0 + 16 * w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (col0 + 16 * w + 4 * j < elems) *reinterpret_cast<float4*>(tp + 4 * j) = v[j];
+  }
+  if (exclusive) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {                  // wave_shr:1 = 0x138; lane 0 gets 0
+      v[j].x = dpp_or_zero<0x138, 0xF>(v[j].x);
+      v[j].y = dpp_or_zero<0x138, 0xF>(v[j].y);
+      v[j].z = dpp_or_zero<0x138, 0xF>(v[j].z);
+      v[j].w = dpp_or_zero<0x138, 0xF>(v[j].w);
+    }
+  }
+  __syncthreads();                                 // every row read before any is overwritten
+  if (row_ok) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tile[lane * (kShortRow / 4) + 4 * w + j] = v[j];
+  }
+  __syncthreads();
+  for (int s = tid; s < nv; s += kShortThreads) {
+    const int r = s / kVec, c = s % kVec;
+    if (col0 + 4 * c < elems)
+      *reinterpret_cast<float4*>(base + r * elems + 4 * c) = tile[r * (kShortRow / 4) + c];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_scan_short(float* x, long long n_seq, long long n, long long elems,
+                             int exclusive, float* totals, hipStream_t st) {
+  if (n < 1 || n > kShortRows || n_seq < 1 || n_seq > 65535) return hipErrorInvalidValue;
+  const long long blocks = (elems + kShortStrip - 1) / kShortStrip;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  dim3 grid((unsigned)blocks, (unsigned)n_seq);
+  launch_kernel(scan_short_kernel, grid, kShortThreads, 0, st, x, n, elems, exclusive, totals);
+  return hipGetLastError();
+}
 
 hipError_t launch_scan_tiles(float* x, long long n_seq, long long n, long long elems,
                              int strip, int tile_rows, int n_tiles, int exclusive,

@@ -149,6 +149,7 @@ void check_scan(int64_t n_seq, int64_t n, int64_t elems) {
   CHECK(i128(sp.n_tiles) * sp.tile_rows >= n, "scan tiles cover the rows");
   CHECK(sp.levels >= ceil_log2(n) && sp.levels <= 256, "scan depth");
   CHECK(sp.strip >= 1, "scan strip");
+  CHECK(sp.wave == (n <= kata::kScanWaveRows), "wave form exactly for n <= 64 rows");
   if (sp.n_tiles == 1) {
     CHECK(sp.ws_bytes == 0 && sp.tile_rows == n, "single-tile scan");
     CHECK(sp.levels == ceil_log2(n), "single-tile scan depth");
