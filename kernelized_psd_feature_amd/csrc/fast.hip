@@ -760,6 +760,42 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_hybrid_kernel(
 //   LDS as bf16 MFMA operands; each wave then reads out its own tokens over all state rows, so no
 //   partial outputs cross waves.
 // ==========================================================================================
+// Readout K order of the single-group packed walk: the double group (a, J), a = 2A, that lane
+// group g reads out in K step kk.  Steps 0-3 take the 2 x 2 block (A, J) = (g % 2 + TA,
+// g / 2 + TJ) at (TA, TJ) = (0, 0), (0, 2), (2, 1), (4, 2); step 4 takes (A, J) = (2, 3), (3, 3),
+// (6, 3), (7, 3).  The five steps hold the 20 double groups once each, and in steps 0-3 a
+// lane's q offsets move from step to step by constants only: the readout addresses q with 4
+// registers instead of 10.
+struct RoBlock {
+  int A, J;
+};
+__host__ __device__ constexpr RoBlock ro_block(int kk, int g) {
+  return kk == 0 ? RoBlock{g % 2, g / 2}
+       : kk == 1 ? RoBlock{g % 2, g / 2 + 2}
+       : kk == 2 ? RoBlock{g % 2 + 2, g / 2 + 1}
+       : kk == 3 ? RoBlock{g % 2 + 4, g / 2 + 2}
+                 : RoBlock{2 + g % 2 + 4 * (g / 2), 3};
+}
+// 4 kk + g of the step and lane group holding double group (2A, J)
+__host__ __device__ constexpr int ro_slot(int A, int J) {
+  for (int kk = 0; kk < 5; ++kk)
+    for (int g = 0; g < 4; ++g)
+      if (ro_block(kk, g).A == A && ro_block(kk, g).J == J) return 4 * kk + g;
+  return -1;
+}
+constexpr bool ro_order_ok() {
+  bool seen[8][4] = {};
+  for (int kk = 0; kk < 5; ++kk)
+    for (int g = 0; g < 4; ++g) {
+      const RoBlock b = ro_block(kk, g);
+      if (b.A < 0 || b.A > 7 || b.J < 0 || b.J > 3 || b.A > 2 * b.J + 1 || seen[b.A][b.J])
+        return false;
+      seen[b.A][b.J] = true;
+    }
+  return true;
+}
+static_assert(ro_order_ok() && Layout<true, P>::kSteps == 5, "readout K order: 20 double groups");
+
 template <bool kPacked, int GW>
 struct __align__(16) WalkLds {
   TilesT<kPacked> tl;
@@ -825,11 +861,16 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
   zero_pad_rows(tl, tid);
 
   // readout rows of this lane group: direct K step kk covers rows (2kk + r'/4, 4g + r'%4);
-  // packed K step m' covers (a + r'/4, 4J + r'%4) with (a, J) the double group 4m' + g
+  // packed K step kk covers (a + r'/4, 4J + r'%4): (a, J) = ro_block(kk, g) at GW = 16, else the
+  // double group 4kk + g of the grouped list
+  constexpr bool kRo = kPacked && GW == P;
   int qa_off[LY::kSteps], qj_off[LY::kSteps];
 #pragma unroll
   for (int kk = 0; kk < LY::kSteps; ++kk) {
-    if (kPacked) {
+    if (kRo) {
+      qa_off[kk] = 2 * ro_block(kk, g).A;
+      qj_off[kk] = 4 * ro_block(kk, g).J;
+    } else if (kPacked) {
       int a, J;
       LY::dg(4 * kk + g, a, J);
       qa_off[kk] = a;
@@ -839,9 +880,25 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
       qj_off[kk] = 4 * g;
     }
   }
+  // where this lane's rows of each owned tile go in Sb: K step and lane (the tile's lane group
+  // g holds the double group 4 (t >> 1) + g of the layout's list); half t & 1
+  int pub_step[LY::kSlots], pub_lane[LY::kSlots];
+#pragma unroll
+  for (int sl = 0; sl < LY::kSlots; ++sl) {
+    const int t = LY::owns(w, sl) ? LY::tile(w, sl) : 0;
+    pub_step[sl] = t >> 1;
+    pub_lane[sl] = lane;
+    if (kRo) {
+      int a, J;
+      LY::dg(4 * (t >> 1) + g, a, J);
+      const int pos = ro_slot(a >> 1, J);
+      pub_step[sl] = pos >> 2;
+      pub_lane[sl] = 16 * (pos & 3) + l16;
+    }
+  }
 
   // publish this wave's state tiles as bf16 MFMA operands: tile t fills slots 4 (t & 1) .. +3
-  // of K step t >> 1 (slot r' of lane group g <-> row 4g + r'%4 of tile 2(t>>1) + r'/4)
+  // of its rows' K step (slot r' <-> row 4g + r'%4 of tile 2(t>>1) + r'/4)
   auto publish = [&]() {
 #pragma unroll
     for (int sl = 0; sl < LY::kSlots; ++sl) {
@@ -852,7 +909,8 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
         __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 x;
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] = (__bf16)S[sl][nt][r];
-        reinterpret_cast<uint2*>(&sm.Sb[t >> 1][nt][lane])[t & 1] = __builtin_bit_cast(uint2, x);
+        reinterpret_cast<uint2*>(&sm.Sb[pub_step[sl]][nt][pub_lane[sl]])[t & 1] =
+            __builtin_bit_cast(uint2, x);
       }
     }
   };
@@ -893,17 +951,20 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     const uint4 vb4 = *reinterpret_cast<const uint4*>(sm.vbad);
     const bool vbad = __builtin_amdgcn_readfirstlane(vb4.x | vb4.y | vb4.z | vb4.w) != 0;
 
-    // ---- intra-chunk tile of this wave's tokens, and S += Phi(K)^T V with the same value
-    // fragments (the readout reads the published S_{<c}, not these registers) ----
+    // ---- intra-chunk tile of this wave's tokens, and (packed layouts) S += Phi(K)^T V with the
+    // same value fragments: the readout reads the published S_{<c}, not these registers.  The
+    // direct layout (4 tiles a wave) updates after the readout, for its register budget ----
+    constexpr bool kFuse = kPacked;
     float lsum = 0.f;
     f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
     const s16x4 qf = row4_frag(tl.Qs, 16 * w, lane);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
+      if (!kFuse && 2 * m > w) break;
       bf16x8 vb[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(tl.V, m, nt, lane);
-      state_update_step<kPacked, GW>(tl, ur, S, vb, w, m, lane);
+      if (kFuse) state_update_step<kPacked, GW>(tl, ur, S, vb, w, m, lane);
       if (2 * m > w) continue;                     // key tiles entirely in the future
       // the step holding the wave's diagonal tile (and any future keys) when a value of the
       // chunk is an infinity or a nan (rare, wave-uniform): exact path
@@ -1006,11 +1067,15 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
       den_out[((long long)b * pr.T + tok0 + 16 * w + lane) * pr.H + h] = sm.den[16 * w + lane];
     orow += C * so_t;
 
-    // ---- Z += K^T K (S was updated with the intra-chunk tile) ----
+    // ---- Z += K^T K (and S += Phi(K)^T V unless done with the intra-chunk tile) ----
+    if (kFuse) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const bf16x8 kf = kcol_frag(tl, m, lane);
-      Z = mfma32(kf, kf, Z);
+      for (int m = 0; m < 2; ++m) {
+        const bf16x8 kf = kcol_frag(tl, m, lane);
+        Z = mfma32(kf, kf, Z);
+      }
+    } else {
+      state_update<kPacked, GW>(tl, ur, S, Z, w, lane, true);
     }
     __syncthreads();                               // all reads of this chunk's tiles and Sb done
     if (c + 1 < nc) {
