@@ -194,14 +194,13 @@ __device__ __forceinline__ s16x4 row4_frag(const __bf16 (*X)[QROW], int row0, in
 // Squared-score tile of keys [s0, s0 + 16) (rows) against this lane's query t (column), from
 // the A operand kf (k rows) and the B operand qf (q_t[4g .. 4g + 3]): the bf16 weights P of
 // slots r = 0, 1 and 2, 3 as packed pairs pw, and their sum added to lsum (a bf16 pair dot with
-// ones, so the sum is taken over the rounded weights).  kMask (the diagonal tile): keep01 and
-// keep23 clear the halves of the future keys (+0).  GW < 16 (KATA-Mg, groups of GW
+// ones, so the sum is taken over the rounded weights).  kMask (the diagonal tile, keys
+// 16w + 4g + r against token 16w + l16): the future keys' weights are +0.  GW < 16 (KATA-Mg, groups of GW
 // coordinates): one product per group, the query operand cut to the lane groups holding that
 // group's coordinates, and the squared group dots summed.
 template <int GW, bool kMask>
-__device__ __forceinline__ void score_tile(const s16x4& kf, const s16x4& qf, uint32_t keep01,
-                                           uint32_t keep23, int lane, uint32_t (&pw)[2],
-                                           float& lsum) {
+__device__ __forceinline__ void score_tile(const s16x4& kf, const s16x4& qf, int lane,
+                                           uint32_t (&pw)[2], float& lsum) {
   f32x4 x2;
   if constexpr (GW == P) {
     const f32x4 sc = mfma16(kf, qf, zero4());
@@ -218,12 +217,15 @@ __device__ __forceinline__ void score_tile(const s16x4& kf, const s16x4& qf, uin
       for (int r = 0; r < 4; ++r) x2[r] = fmaf(sc[r], sc[r], x2[r]);
     }
   }
+  if (kMask) {
+    // keys 16w + 4g + r against token 16w + l16: future for 4g + r > l16 (select, never
+    // multiply: the lane masks are loop constants)
+    const int g = lane >> 4, l16 = lane & 15;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x2[r] = 4 * g + r <= l16 ? x2[r] : 0.f;
+  }
   pw[0] = pack_bf16x2(x2[0], x2[1]);
   pw[1] = pack_bf16x2(x2[2], x2[3]);
-  if (kMask) {
-    pw[0] &= keep01;
-    pw[1] &= keep23;
-  }
   lsum = sum_bf16x2(pw[0], lsum);
   lsum = sum_bf16x2(pw[1], lsum);
 }
@@ -931,11 +933,6 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
   publish();
   __syncthreads();
 
-  // diagonal score tile (keys 16w + 4g + r against token 16w + l16): the key is in the past or
-  // present for 4g + r <= l16; masks of the packed pairs r = 0, 1 and 2, 3
-  const uint32_t keep01 = (4 * g <= l16 ? 0xffffu : 0u) | (4 * g + 1 <= l16 ? 0xffff0000u : 0u);
-  const uint32_t keep23 = (4 * g + 2 <= l16 ? 0xffffu : 0u) | (4 * g + 3 <= l16 ? 0xffff0000u : 0u);
-
   // output pointer of this lane's first store in the first chunk: token 16w + 8 (lane / 32),
   // column lane % 32
   Tout* orow = o + row_off(pr.so, b, c0 * C + 16 * w + 8 * (lane >> 5), h) + (lane & 31);
@@ -974,11 +971,9 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
       for (int half = 0; half < 2; ++half) {
         const int ms = 2 * m + half;
         if (ms < w) {
-          score_tile<GW, false>(row4_frag(tl.Ks, 16 * ms, lane), qf, 0u, 0u, lane, pw[half],
-                                lsum);
+          score_tile<GW, false>(row4_frag(tl.Ks, 16 * ms, lane), qf, lane, pw[half], lsum);
         } else if (ms == w) {
-          score_tile<GW, true>(row4_frag(tl.Ks, 16 * ms, lane), qf, keep01, keep23, lane,
-                               pw[half], lsum);
+          score_tile<GW, true>(row4_frag(tl.Ks, 16 * ms, lane), qf, lane, pw[half], lsum);
         } else {
           pw[half][0] = pw[half][1] = 0u;
         }
@@ -1027,6 +1022,8 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     }
 
     // ---- readout phi(q_t)^T S_{<c} over all published state rows ----
+    // (issue priority raised over the readout's MFMA stream: other waves' VALU work fills in)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < LY::kSteps; ++kk) {
       const uint32_t qa = *reinterpret_cast<const uint32_t*>(&tl.Qs[t][qa_off[kk]]);
@@ -1043,6 +1040,8 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
       for (int nt = 0; nt < 4; ++nt)
         O[nt] = mfma32(a, __builtin_bit_cast(bf16x8, sm.Sb[kk][nt][lane]), O[nt]);
     }
+
+    __builtin_amdgcn_s_setprio(0);
 
     // ---- gate and store this wave's tokens: lane holds tokens 16w + 4g + r, column 16nt + l16.
     // Row-group swaps between column tiles 2j and 2j + 1 give each lane half a row of 32
