@@ -802,6 +802,7 @@ template <bool kPacked, int GW>
 struct __align__(16) WalkLds {
   TilesT<kPacked> tl;
   uint4 Sb[Layout<kPacked, GW>::kSteps][4][64];   // S_{<c} as MFMA operands: [K step][value tile][lane]
+  uint4 Zb[kPacked ? 64 : 1];                 // Z_{<c} as bf16 hi / lo A operands (packed layouts)
   float den[C];                               // D_t of the chunk's tokens
   float inv[C];                               // 1 / D_t
   uint32_t vbad[4];                           // per wave: its staged v rows hold a non-finite value
@@ -925,12 +926,36 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     if (lane == 0) sm.vbad[w] = any;
   };
 
+  // Z as the bf16 hi + lo A operands of the q^T Z q products (KATA-Mg: only the
+  // within-group blocks of Z enter q^T Z q)
+  auto z_split = [&](const f32x4& Zr, s16x4& zhi, s16x4& zlo) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float zr = (GW == P || (4 * g + r) / GW == l16 / GW) ? Zr[r] : 0.f;
+      const __bf16 hi = (__bf16)zr;
+      zhi[r] = __builtin_bit_cast(short, hi);
+      zlo[r] = __builtin_bit_cast(short, (__bf16)(zr - (float)hi));
+    }
+  };
+  // packed layouts: wave 0 alone keeps Z and publishes its split once per chunk (wave 0 has the
+  // least intra-chunk work)
+  constexpr bool kFuse = kPacked;
+  constexpr int kZWave = 0;
+  auto publish_z = [&]() {
+    if (!kFuse || w != kZWave) return;
+    s16x4 zhi, zlo;
+    z_split(Z, zhi, zlo);
+    const uint2 a = __builtin_bit_cast(uint2, zhi), bb = __builtin_bit_cast(uint2, zlo);
+    sm.Zb[lane] = uint4{a.x, a.y, bb.x, bb.y};
+  };
+
   StagePtrs sp = stage_ptrs(pr, q, k, v, b, h, c0 * C, true, tid);
   Stage st;
   stage_load(st, sp, sv_t);
   stage_store(st, tl, true, tid);
   flag_v(st);
   publish();
+  publish_z();
   __syncthreads();
 
   // output pointer of this lane's first store in the first chunk: token 16w + 8 (lane / 32),
@@ -951,7 +976,6 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     // ---- intra-chunk tile of this wave's tokens, and (packed layouts) S += Phi(K)^T V with the
     // same value fragments: the readout reads the published S_{<c}, not these registers.  The
     // direct layout (4 tiles a wave) updates after the readout, for its register budget ----
-    constexpr bool kFuse = kPacked;
     float lsum = 0.f;
     f32x4 O[4] = {zero4(), zero4(), zero4(), zero4()};
     const s16x4 qf = row4_frag(tl.Qs, 16 * w, lane);
@@ -994,16 +1018,16 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     // Y = Z q_t on MFMA with Z split into bf16 hi + lo (fp32-accurate; q is exact in bf16):
     // Z's accumulator layout (lane: column lane%16, rows 4g + r) is, Z being symmetric, the
     // A layout of a 16 x 16 x 16 product; q_t[4g..4g+3] is the same B operand as the scores.
+    // Packed layouts: the split published by the wave that keeps Z (z_split, sm.Zb).
     float zq = 0.f;
     {
       s16x4 zhi, zlo;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        // KATA-Mg: only the within-group blocks of Z enter q^T Z q
-        const float zr = (GW == P || (4 * g + r) / GW == l16 / GW) ? Z[r] : 0.f;
-        const __bf16 hi = (__bf16)zr;
-        zhi[r] = __builtin_bit_cast(short, hi);
-        zlo[r] = __builtin_bit_cast(short, (__bf16)(zr - (float)hi));
+      if constexpr (kFuse) {
+        const uint4 zz = sm.Zb[lane];
+        zhi = __builtin_bit_cast(s16x4, uint2{zz.x, zz.y});
+        zlo = __builtin_bit_cast(s16x4, uint2{zz.z, zz.w});
+      } else {
+        z_split(Z, zhi, zlo);
       }
       f32x4 y = mfma16(zhi, qf, zero4());
       y = mfma16(zlo, qf, y);                   // y[r] = (Z q_t)[4g + r]
@@ -1068,6 +1092,7 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
 
     // ---- Z += K^T K (and S += Phi(K)^T V unless done with the intra-chunk tile) ----
     if (kFuse) {
+      if (w == kZWave)
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const bf16x8 kf = kcol_frag(tl, m, lane);
@@ -1081,6 +1106,7 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
       stage_store(st, tl, true, tid);
       flag_v(st);
       publish();
+      publish_z();
     }
     __syncthreads();
   }

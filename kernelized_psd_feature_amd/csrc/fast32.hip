@@ -173,11 +173,11 @@ struct Rows32 {
   }
 };
 
-// S[slot] += Phi(K)^T V over one staged chunk; Z += K^T K for the 16 x 16 tile
-// (z >> 1, z & 1) when z >= 0 (waves 0-3 own one tile each).
+// S[slot] += Phi(K)^T V over one staged chunk; Zt += the 16 x 16 tile (z >> 1, z & 1) of
+// K^T K when z >= 0 (waves 0-3 own one tile each and keep only that tile).
 template <class TL>
 __device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, f32x4 (&S)[kSlots][4],
-                                         f32x4 (&Z)[2][2], int w, int lane, int z) {
+                                         f32x4& Zt, int w, int lane, int z) {
   // both 32-key steps unrolled: the LDS addresses of the second become immediate offsets
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
@@ -194,11 +194,7 @@ __device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, f32x4 (
     if (z >= 0) {                                  // wave-uniform
       const int mi = z >> 1, kj = z & 1;
       const bf16x8 a = kcol(tl, mi, m, lane), bb = kcol(tl, kj, m, lane);
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y)
-          if (x == mi && y == kj) Z[x][y] = mfma32(a, bb, Z[x][y]);
+      Zt = mfma32(a, bb, Zt);
     }
   }
 }
@@ -227,12 +223,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
     for (int x = tid; x < kStateFloats / 4; x += kThreads) o4[x] = float4{0.f, 0.f, 0.f, 0.f};
     return;
   }
-  f32x4 S[kSlots][4], Z[2][2];
+  f32x4 S[kSlots][4], Zt = zero4();
 #pragma unroll
   for (int sl = 0; sl < kSlots; ++sl)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) S[sl][nt] = zero4();
-  Z[0][0] = Z[0][1] = Z[1][0] = Z[1][1] = zero4();
   Rows32 rw;
   rw.init(w, lane);
   zero_row(tl[0], tid);
@@ -250,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
   }
   __syncthreads();
   for (int c = 0; c < nc; ++c) {
-    update32(tl[c & 1], rw, S, Z, w, lane, w < 4 ? w : -1);   // Z tile w on waves 0-3
+    update32(tl[c & 1], rw, S, Zt, w, lane, w < 4 ? w : -1);   // Z tile w on waves 0-3
     if (c + 1 < nc) store_state32(st, tl[(c + 1) & 1], tid);   // buffer read last iteration
     if (c + 2 < nc) {
       p.next();
@@ -266,14 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
     for (int nt = 0; nt < 4; ++nt)
       *reinterpret_cast<f32x4*>(out + ((t * 4 + nt) * 64 + lane) * 4) = S[sl][nt];
   }
-  if (w < 4) {
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int kj = 0; kj < 2; ++kj)
-        if (mi * 2 + kj == w)
-          *reinterpret_cast<f32x4*>(out + kZOff + ((mi * 2 + kj) * 64 + lane) * 4) = Z[mi][kj];
-  }
+  if (w < 4) *reinterpret_cast<f32x4*>(out + kZOff + (w * 64 + lane) * 4) = Zt;
 }
 
 struct Pair4 {
@@ -338,6 +326,7 @@ struct __align__(16) Walk32Lds {
   uint2 Zb[4][2][64];             // Z_{<c} tiles (mi, kj) = 2 mi + kj as bf16 hi / lo A operands
   f32x4 xr[kWaves][2][64];        // readout partials handed to the other wave of a token group
   float zx[kWaves][64];           // q^T Z q halves handed to the other wave of a token group
+  float inv[kWaves][16];          // per wave: 1 / D_t of its token group's 16 tokens
   uint32_t vbad[kWaves];          // per wave: its staged v row pieces hold a non-finite value
   unsigned char dg[4 * kSteps][2];   // double group -> (a, J)
 };
@@ -360,15 +349,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
 
   // Exclusive prefix of this segment: the scanned state at position seg, or (sum_prefix)
   // the states of segments 0 .. seg-1 added in that order; zero without states.
-  f32x4 S[kSlots][4], Z[2][2];
+  // Z: wave w < 4 keeps tile (w >> 1, w & 1) in Zt and publishes it split into bf16 hi + lo
+  const int zt = w < 4 ? w : -1;
+  f32x4 S[kSlots][4], Zt = zero4();
 #pragma unroll
   for (int sl = 0; sl < kSlots; ++sl)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) S[sl][nt] = zero4();
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int kj = 0; kj < 2; ++kj) Z[mi][kj] = zero4();
   {
     const int j0 = sum_prefix ? 0 : seg, j1 = !states ? j0 : sum_prefix ? seg : seg + 1;
     for (int j = j0; j < j1; ++j) {
@@ -381,11 +368,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
         for (int nt = 0; nt < 4; ++nt)
           S[sl][nt] += *reinterpret_cast<const f32x4*>(pre + ((t * 4 + nt) * 64 + lane) * 4);
       }
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int kj = 0; kj < 2; ++kj)
-          Z[mi][kj] += *reinterpret_cast<const f32x4*>(pre + kZOff + ((mi * 2 + kj) * 64 + lane) * 4);
+      if (zt >= 0) Zt += *reinterpret_cast<const f32x4*>(pre + kZOff + (zt * 64 + lane) * 4);
     }
   }
   Rows32 rw;
@@ -398,8 +381,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     sm.dg[tid][1] = (unsigned char)(4 * J);
   }
 
-  // Z: wave w < 4 keeps tile (w >> 1, w & 1) and publishes it split into bf16 hi + lo
-  const int zt = w < 4 ? w : -1;
   auto publish = [&]() {
 #pragma unroll
     for (int sl = 0; sl < kSlots; ++sl) {
@@ -414,11 +395,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
       }
     }
     if (zt >= 0) {
-      f32x4 zr = zero4();
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y) zr = (2 * x + y == zt) ? Z[x][y] : zr;
+      const f32x4 zr = Zt;
       s16x4 zhi, zlo;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -469,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       if (2 * m > tg) break;                       // key tiles entirely in the future
-      __bf16 pa[8];
+      uint32_t pw[2][2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int ms = 2 * m + half;
@@ -477,18 +454,23 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
           const bf16x8 kf = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const uint4*>(&tl.Ks[16 * ms + l16][8 * g]));
           const f32x4 sc = mfma32(kf, qf, zero4());
-          if (ms < tg)
-            square_mask<false>(sc, 16 * ms, t, lane, &pa[4 * half], lsum);
-          else
-            square_mask<true>(sc, 16 * ms, t, lane, &pa[4 * half], lsum);
-        } else {
+          f32x4 x2;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) pa[4 * half + r] = (__bf16)0.f;
+          for (int r = 0; r < 4; ++r) {
+            x2[r] = sc[r] * sc[r];
+            // the diagonal tile: keys 16 tg + 4 g + r against token 16 tg + l16 (select)
+            if (ms == tg) x2[r] = 4 * g + r <= l16 ? x2[r] : 0.f;
+          }
+          // bf16 weights in pairs, their row sum from the same rounded values (v_dot2 with ones)
+          pw[half][0] = pack_bf16x2(x2[0], x2[1]);
+          pw[half][1] = pack_bf16x2(x2[2], x2[3]);
+          lsum = sum_bf16x2(pw[half][0], lsum);
+          lsum = sum_bf16x2(pw[half][1], lsum);
+        } else {
+          pw[half][0] = pw[half][1] = 0u;
         }
       }
-      bf16x8 a;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) a[r] = pa[r];
+      const bf16x8 a = __builtin_bit_cast(bf16x8, uint4{pw[0][0], pw[0][1], pw[1][0], pw[1][1]});
 #pragma unroll
       for (int n = 0; n < 2; ++n) O[n] = mfma32(a, v_frag(tl.V, m, 2 * ch + n, lane), O[n]);
     }
@@ -527,10 +509,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
       zq = fmaf(bf_lo(qq.y), y[2], zq);
       zq = fmaf(bf_hi(qq.y), y[3], zq);
     }
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    zq += __shfl_xor(zq, 16);
-    zq += __shfl_xor(zq, 32);
+    lsum = sum_xor32(sum_xor16(lsum));
+    zq = sum_xor32(sum_xor16(zq));
     sm.zx[w][lane] = zq;
 
     // ---- readout phi(q_t)^T S_{<c}: K steps [9 ch, 9 ch + 9) for all four value tiles ----
@@ -566,7 +546,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     // both waves add the halves in the order kj = 0, 1: the same D bit for bit
     const float zo = sm.zx[w ^ 4][lane];
     const float D = pr.eps + ((ch ? zo + zq : zq + zo) + lsum);   // D_t of token t
-    const float inv = 1.f / D;
+    if (g == 0) sm.inv[w][l16] = __builtin_amdgcn_rcpf(D);        // 1 ulp
+    const float4 inv4 = *reinterpret_cast<const float4*>(&sm.inv[w][4 * g]);   // own writes
+    const float invr[4] = {inv4.x, inv4.y, inv4.z, inv4.w};
 
     // ---- gate and store: lane holds tokens 16 tg + 4 g + r, columns 32 ch + 16 n + l16.  A
     // row-group swap between the two column tiles gives each lane a 32-column half row, so every
@@ -574,7 +556,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     // (lanes 0-31) and 16 tg + 8 + r (lanes 32-63), the second 16 tg + 4 + r and 16 tg + 12 + r.
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float ir = __shfl(inv, 4 * g + r);    // token 4 g + r's 1 / D (lane 4 g + r)
+      const float ir = invr[r];                    // token 16 tg + 4 g + r's 1 / D
       const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(O[0][r] * ir),
                                                        __float_as_uint(O[1][r] * ir), false, false);
       // streamed out: never re-read by this kernel
@@ -586,7 +568,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     orow += C * so_t;
 
     // ---- state update with this chunk ----
-    update32(tl, rw, S, Z, w, lane, zt);
+    update32(tl, rw, S, Zt, w, lane, zt);
     __syncthreads();                               // all reads of this chunk's tiles and Sb
     if (c + 1 < nc) {
       store32(st, tl, true, tid);
