@@ -35,13 +35,21 @@ constexpr int KTROW = 68;                      // fp32 per row of the K^T tile
 constexpr int VROW = 80;                       // bf16 per v row: 160 B, 16-byte aligned
 
 // ---- chunk tiles in LDS ------------------------------------------------------------------
-// kPacked adds rows to the K^T tile: rows 16..31 hold 2 k (the weight of an off-diagonal
-// packed state row) and row 32 zeros (the padding rows of the packed layout).
+// kPacked adds rows to the K^T tile: 2 k (the weight of an off-diagonal packed state row) at
+// rows KT_D + i and zeros (the padding rows of the packed layout) at rows KT_Z0 and KT_Z0 + 1.
+// With the row stride KTROW = 68 a row's 16-byte reads start on bank group 4 (row mod 8); the
+// rows one 8-lane group of the update reads hold k_i, 2 k_i, k_{i+2}, 2 k_{i+2} and a zero row
+// for one parity of i (i = a + (t & 1), a even): the doubled rows sit 4 groups over
+// (KT_D = 20) and the zero row has the other parity (KT_Z0 + 1 - (i & 1)), so the group's
+// distinct rows fall on distinct bank groups.
+constexpr int KT_D = 20, KT_Z0 = 36, KT_PACKED_ROWS = 38;
+static_assert(KT_D % 8 == 4 && KT_D >= P && KT_Z0 >= KT_D + P && KT_Z0 % 8 == 4 &&
+              KT_PACKED_ROWS == KT_Z0 + 2, "K^T row placement");
 template <bool kPacked>
 struct __align__(16) TilesT {
   __bf16 Qs[C][QROW];                 // q rows (bf16), row-major
   __bf16 Ks[C][QROW];                 // k rows (bf16), row-major
-  float KT[kPacked ? 2 * P + 1 : P][KTROW];   // k transposed, fp32 (exact copies)
+  float KT[kPacked ? KT_PACKED_ROWS : P][KTROW];   // k transposed, fp32 (exact copies)
   __bf16 V[C][VROW];                  // v rows (bf16), row-major
 };
 using Tiles = TilesT<false>;
@@ -125,8 +133,8 @@ __device__ __forceinline__ void stage_store(const Stage& st, TilesT<kPacked>& tl
       tl.KT[8 * half + 2 * e][row] = lo;
       tl.KT[8 * half + 2 * e + 1][row] = hi;
       if (kPacked) {
-        tl.KT[P + 8 * half + 2 * e][row] = 2.f * lo;       // exact
-        tl.KT[P + 8 * half + 2 * e + 1][row] = 2.f * hi;
+        tl.KT[KT_D + 8 * half + 2 * e][row] = 2.f * lo;    // exact
+        tl.KT[KT_D + 8 * half + 2 * e + 1][row] = 2.f * hi;
       }
     }
   }
@@ -156,7 +164,7 @@ __device__ __forceinline__ bf16x8 phik_frag(const TL& tl, int i, int m, int lane
 // (a, J) the double group 4 (t >> 1) + g of the layout's list.
 
 // A operand of the packed state update: row (lane % 16) of the tile is the pair (i, j);
-// irow selects the K^T row for the i factor (i, 16 + i for the doubled copy, 32 for zeros).
+// irow selects the K^T row for the i factor (i, KT_D + i for the doubled copy, a zero row).
 template <class TL>
 __device__ __forceinline__ bf16x8 phik_packed_frag(const TL& tl, int irow, int jrow, int m,
                                                    int lane) {
@@ -281,7 +289,7 @@ struct UpdateRows {
         int a, J;
         LY::dg(4 * (t >> 1) + (row >> 2), a, J);
         const int i = a + (t & 1), j = 4 * J + (row & 3);
-        irow[sl] = i > j ? 2 * P : (i == j ? i : P + i);
+        irow[sl] = i > j ? KT_Z0 + 1 - (i & 1) : (i == j ? i : KT_D + i);
         jrow[sl] = j;
       }
     }
@@ -335,7 +343,7 @@ __device__ __forceinline__ void state_update_step(const TL& tl, const UpdateRows
 
 template <bool kPacked>
 __device__ __forceinline__ void zero_pad_rows(TilesT<kPacked>& tl, int tid) {
-  if (kPacked && tid < KTROW) tl.KT[kPacked ? 2 * P : 0][tid] = 0.f;
+  if (kPacked && tid < 2 * KTROW) tl.KT[kPacked ? KT_Z0 + tid / KTROW : 0][tid % KTROW] = 0.f;
 }
 
 // ==========================================================================================

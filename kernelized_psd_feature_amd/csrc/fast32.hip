@@ -34,7 +34,14 @@ static_assert(kStateFloats == 36 * 16 * 64 + 4 * 256, "packed p = 32 state size 
 constexpr int QROW = 40;                             // bf16 per q / k row: 80 B
 constexpr int KTROW = 68;                            // fp32 per K^T row
 constexpr int VROW = 80;                             // bf16 per v row: 160 B
-constexpr int KTROWS = 2 * P + 1;                    // k, 2 k, zeros
+// K^T rows: k_i at i, 2 k_i at KT_D + i, zeros at KT_Z0 and KT_Z0 + 1.  The row stride
+// KTROW = 68 starts a row's 16-byte reads on bank group (row mod 8); one 8-lane group of the
+// update reads k_i, 2 k_i, k_{i+2}, 2 k_{i+2} and a zero row for one parity of i, which this
+// placement (doubled rows 4 groups over, the zero row of the other parity) puts on distinct
+// bank groups.
+constexpr int KT_D = 36, KT_Z0 = 68, KTROWS = 70;
+static_assert(KT_D % 8 == 4 && KT_D >= P && KT_Z0 >= KT_D + P && KT_Z0 % 8 == 4 &&
+              KTROWS == KT_Z0 + 2, "K^T row placement");
 
 struct __align__(16) Tiles32 {
   __bf16 Qs[C][QROW];
@@ -102,8 +109,8 @@ __device__ __forceinline__ void store_kt(const Stage32& s, TL& tl, int tid) {
     const float a = bf_lo(wd[e]), c = bf_hi(wd[e]);
     tl.KT[8 * qc + 2 * e][row] = a;
     tl.KT[8 * qc + 2 * e + 1][row] = c;
-    tl.KT[P + 8 * qc + 2 * e][row] = 2.f * a;           // exact
-    tl.KT[P + 8 * qc + 2 * e + 1][row] = 2.f * c;
+    tl.KT[KT_D + 8 * qc + 2 * e][row] = 2.f * a;        // exact
+    tl.KT[KT_D + 8 * qc + 2 * e + 1][row] = 2.f * c;
   }
 }
 
@@ -125,7 +132,7 @@ __device__ __forceinline__ void store_state32(const Stage32& s, StateTiles32& tl
 
 template <class TL>
 __device__ __forceinline__ void zero_row(TL& tl, int tid) {
-  if (tid < KTROW) tl.KT[2 * P][tid] = 0.f;
+  if (tid < 2 * KTROW) tl.KT[KT_Z0 + tid / KTROW][tid % KTROW] = 0.f;
 }
 
 // A operand of the packed update for this lane's tile row (irow selects k_i, 2 k_i or zeros),
@@ -167,7 +174,7 @@ struct Rows32 {
       int a, J;
       double_group(4 * (t >> 1) + (row >> 2), a, J);
       const int i = a + (t & 1), j = 4 * J + (row & 3);
-      irow[sl] = i > j ? 2 * P : (i == j ? i : P + i);
+      irow[sl] = i > j ? KT_Z0 + 1 - (i & 1) : (i == j ? i : KT_D + i);
       jrow[sl] = j;
     }
   }
