@@ -28,8 +28,10 @@ namespace {
 constexpr int P = 16, DV = 64, C = 64, F = P * P;
 constexpr int kThreads = 256;
 constexpr int kStateFloats = F * (DV + 1);     // 16640: S (4 waves x 16 tiles x 256) + Z (256)
-// LDS row strides, chosen so that every access pattern below is free of bank conflicts
-// (32 banks of 4 bytes; 4-, 8- and 16-byte accesses served 32, 16 and 8 lanes at a time):
+// LDS row strides (32 banks of 4 bytes; 4-, 8- and 16-byte accesses served 32, 16 and 8
+// lanes at a time).  The q / k row reads, the transposed v reads and the K^T factor reads of
+// one lane group avoid bank conflicts with these strides (the K^T rows with the placement
+// below); the state's publish, 8-byte words at a 16-byte stride, does not.
 constexpr int QROW = 20;                       // bf16 per q / k row: 40 B, 8-byte aligned
 constexpr int KTROW = 68;                      // fp32 per row of the K^T tile
 constexpr int VROW = 80;                       // bf16 per v row: 160 B, 16-byte aligned
