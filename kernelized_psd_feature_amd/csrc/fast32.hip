@@ -34,14 +34,17 @@ static_assert(kStateFloats == 36 * 16 * 64 + 4 * 256, "packed p = 32 state size 
 constexpr int QROW = 40;                             // bf16 per q / k row: 80 B
 constexpr int KTROW = 68;                            // fp32 per K^T row
 constexpr int VROW = 80;                             // bf16 per v row: 160 B
-// K^T rows: k_i at i, 2 k_i at KT_D + i, zeros at KT_Z0 and KT_Z0 + 1.  The row stride
-// KTROW = 68 starts a row's 16-byte reads on bank group (row mod 8); one 8-lane group of the
-// update reads k_i, 2 k_i, k_{i+2}, 2 k_{i+2} and a zero row for one parity of i, which this
-// placement (doubled rows 4 groups over, the zero row of the other parity) puts on distinct
-// bank groups.
+// K^T rows: k_i at kt_row(i), 2 k_i at KT_D + kt_row(i), zeros at KT_Z0 and KT_Z0 + 1.  The
+// row stride KTROW = 68 starts a row's 16-byte reads on bank group (row mod 8); one 8-lane
+// group of the update reads k_i, 2 k_i, k_{i+2}, 2 k_{i+2} and a zero row for one parity of i,
+// which this placement (doubled rows 4 groups over, the zero row of the other parity) puts on
+// distinct bank groups.  kt_row rotates each block of 8 features by twice the block index:
+// the staging writes of one instruction (features 8 qc + e of 8 tokens for the 4 quarters qc)
+// then fall on 4 distinct bank groups too, and the reads keep their groups distinct.
 constexpr int KT_D = 36, KT_Z0 = 68, KTROWS = 70;
 static_assert(KT_D % 8 == 4 && KT_D >= P && KT_Z0 >= KT_D + P && KT_Z0 % 8 == 4 &&
               KTROWS == KT_Z0 + 2, "K^T row placement");
+__device__ __forceinline__ int kt_row(int f) { return (f & ~7) | (((f & 7) + 2 * (f >> 3)) & 7); }
 
 struct __align__(16) Tiles32 {
   __bf16 Qs[C][QROW];
@@ -107,10 +110,11 @@ __device__ __forceinline__ void store_kt(const Stage32& s, TL& tl, int tid) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const float a = bf_lo(wd[e]), c = bf_hi(wd[e]);
-    tl.KT[8 * qc + 2 * e][row] = a;
-    tl.KT[8 * qc + 2 * e + 1][row] = c;
-    tl.KT[KT_D + 8 * qc + 2 * e][row] = 2.f * a;        // exact
-    tl.KT[KT_D + 8 * qc + 2 * e + 1][row] = 2.f * c;
+    const int ra = kt_row(8 * qc + 2 * e), rc = kt_row(8 * qc + 2 * e + 1);
+    tl.KT[ra][row] = a;
+    tl.KT[rc][row] = c;
+    tl.KT[KT_D + ra][row] = 2.f * a;        // exact
+    tl.KT[KT_D + rc][row] = 2.f * c;
   }
 }
 
@@ -155,7 +159,7 @@ __device__ __forceinline__ bf16x8 phik(const TL& tl, int irow, int jrow, int m, 
 // k_s[16 mi + lane%16] over the slots of 32-key step m (operand of Z = K^T K)
 template <class TL>
 __device__ __forceinline__ bf16x8 kcol(const TL& tl, int mi, int m, int lane) {
-  const int i = 16 * mi + (lane & 15), g = lane >> 4;
+  const int i = kt_row(16 * mi + (lane & 15)), g = lane >> 4;
   const float4 a = *reinterpret_cast<const float4*>(&tl.KT[i][32 * m + 4 * g]);
   const float4 c = *reinterpret_cast<const float4*>(&tl.KT[i][32 * m + 16 + 4 * g]);
   bf16x8 f;
@@ -174,8 +178,8 @@ struct Rows32 {
       int a, J;
       double_group(4 * (t >> 1) + (row >> 2), a, J);
       const int i = a + (t & 1), j = 4 * J + (row & 3);
-      irow[sl] = i > j ? KT_Z0 + 1 - (i & 1) : (i == j ? i : KT_D + i);
-      jrow[sl] = j;
+      irow[sl] = i > j ? KT_Z0 + 1 - (i & 1) : (i == j ? kt_row(i) : KT_D + kt_row(i));
+      jrow[sl] = kt_row(j);
     }
   }
 };
@@ -540,15 +544,23 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
         R[n] = mfma32(a, __builtin_bit_cast(bf16x8, sm.Sb[kk][n][lane]), R[n]);
     }
     // the other wave of the token group (w ^ 4) owns the other two value tiles (selects, not
-    // a runtime index, keep R in registers)
-#pragma unroll
-    for (int n = 0; n < 2; ++n) sm.xr[w][n][lane] = ch ? R[n] : R[2 + n];
-    __syncthreads();
+    // a runtime index, keep R in registers); it reads them after the update's barrier
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      const f32x4 x = sm.xr[w ^ 4][n][lane], own = ch ? R[2 + n] : R[n];
+      sm.xr[w][n][lane] = ch ? R[n] : R[2 + n];
+      const f32x4 own = ch ? R[2 + n] : R[n];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) O[n][r] += own[r] + x[r];
+      for (int r = 0; r < 4; ++r) O[n][r] += own[r];
+    }
+
+    // ---- state update with this chunk (registers only: Sb keeps S_{<c} until the barrier) ----
+    update32(tl, rw, S, Zt, w, lane, zt);
+    __syncthreads();          // all reads of this chunk's tiles, Sb and Zb; xr and zx written
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const f32x4 x = sm.xr[w ^ 4][n][lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O[n][r] += x[r];
     }
     // both waves add the halves in the order kj = 0, 1: the same D bit for bit
     const float zo = sm.zx[w ^ 4][lane];
@@ -574,9 +586,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
       den_out[((long long)b * pr.T + tok0 + t) * pr.H + h] = D;
     orow += C * so_t;
 
-    // ---- state update with this chunk ----
-    update32(tl, rw, S, Zt, w, lane, zt);
-    __syncthreads();                               // all reads of this chunk's tiles and Sb
     if (c + 1 < nc) {
       store32(st, tl, true, tid);
       flag_v(st);
