@@ -11,8 +11,12 @@
 // state-size bullet's packed coordinates): 72 double groups = 36 tiles of 16 rows, 18 readout
 // K steps.  That is 147 KB of fp32 per state, too much for four waves' registers, so a
 // workgroup has eight waves (two per SIMD, one workgroup per CU):
-//   state tiles  wave w owns tiles rank(w) + 8 s (5 tiles for ranks 0-3, 4 for ranks 4-7; the
-//                waves with the most intra-chunk work own fewer),
+//   state tiles  the tiles go in K-step pairs (2 P, 2 P + 1).  Wave w owns pairs w and w + 8
+//                with all four value tiles; the last two pairs are split by value-tile halves
+//                over waves 0, 1, 4 and 5 (the token groups with the least intra-chunk work),
+//                and the four Z tiles go to waves 2, 3, 6 and 7.  The two tiles of a pair share
+//                their j factor rows, which the update reads once, and their accumulators make
+//                whole B-operand words of the readout, which the publish writes at once,
 //   tokens       wave w serves tokens [16 tg, 16 tg + 16) of a chunk, tg = w % 4, and the value
 //                columns [32 ch, 32 ch + 32), ch = w / 4.  The two waves of a token group
 //                split the readout's K steps instead of its columns (each forms phi(q) for
@@ -27,7 +31,7 @@ namespace {
 
 constexpr int P = 32, DV = 64, C = 64;
 constexpr int kWaves = 8, kThreads = 64 * kWaves;
-constexpr int kTiles = 36, kSteps = 18, kSlots = 5;
+constexpr int kTiles = 36, kSteps = 18, kFull = 2;   // kFull: whole pairs per wave
 constexpr int kZOff = kTiles * 16 * DV;              // 36864
 constexpr int kStateFloats = kZOff + 4 * 256;        // + Z as 2 x 2 tiles of 16 x 16
 static_assert(kStateFloats == 36 * 16 * 64 + 4 * 256, "packed p = 32 state size (plan.h)");
@@ -58,10 +62,12 @@ struct __align__(16) StateTiles32 {                  // the state pass needs no 
   __bf16 V[C][VROW];
 };
 
-// waves in the order that receives 5, 5, 5, 5, 4, 4, 4, 4 tiles: token groups 0 and 1 first
-__device__ __forceinline__ int wave_rank(int w) { return (w & 1) | ((w >> 2) << 1) | (((w >> 1) & 1) << 2); }
-__device__ __forceinline__ bool owns(int w, int s) { return wave_rank(w) + 8 * s < kTiles; }
-__device__ __forceinline__ int tile_of(int w, int s) { return wave_rank(w) + 8 * s; }
+// Tile ownership (see the file comment): whole pair ps < kFull of wave w, the half-pair of
+// extra index e (pair 16 + e / 2, value tiles 2 (e % 2) + {0, 1}) and the Z tile index.
+__device__ __forceinline__ int pair_of(int w, int ps) { return w + 8 * ps; }
+__device__ __forceinline__ int extra_of(int w) { return (w & 2) ? -1 : (w & 1) | ((w >> 2) << 1); }
+__device__ __forceinline__ int ztile_of(int w) { return (w & 2) ? (w & 1) | ((w >> 2) << 1) : -1; }
+static_assert(2 * (8 * kFull + 2) == kTiles, "pairs: kFull per wave and two split pairs");
 
 // One thread's share of a chunk's loads: threads 0-255 a quarter q row, 256-511 a quarter
 // k row (row = (tid & 255) / 4, columns 8 (tid % 4) ..), every thread 16 B of one v row
@@ -139,21 +145,22 @@ __device__ __forceinline__ void zero_row(TL& tl, int tid) {
   if (tid < 2 * KTROW) tl.KT[KT_Z0 + tid / KTROW][tid % KTROW] = 0.f;
 }
 
-// A operand of the packed update for this lane's tile row (irow selects k_i, 2 k_i or zeros),
-// 32-key step m in slot order kappa.
+// A operands of the packed update for this lane's row of the two tiles of a pair (irow[tp]
+// selects k_i, 2 k_i or zeros; the pair shares the j row), 32-key step m in slot order kappa.
 template <class TL>
-__device__ __forceinline__ bf16x8 phik(const TL& tl, int irow, int jrow, int m, int lane) {
+__device__ __forceinline__ void phik2(const TL& tl, const int (&irow)[2], int jrow, int m,
+                                      int lane, bf16x8 (&a)[2]) {
   const int g = lane >> 4;
-  const float4 ia = *reinterpret_cast<const float4*>(&tl.KT[irow][32 * m + 4 * g]);
-  const float4 ib = *reinterpret_cast<const float4*>(&tl.KT[irow][32 * m + 16 + 4 * g]);
   const float4 ja = *reinterpret_cast<const float4*>(&tl.KT[jrow][32 * m + 4 * g]);
   const float4 jb = *reinterpret_cast<const float4*>(&tl.KT[jrow][32 * m + 16 + 4 * g]);
-  bf16x8 f;
-  f[0] = (__bf16)(ia.x * ja.x); f[1] = (__bf16)(ia.y * ja.y);
-  f[2] = (__bf16)(ia.z * ja.z); f[3] = (__bf16)(ia.w * ja.w);
-  f[4] = (__bf16)(ib.x * jb.x); f[5] = (__bf16)(ib.y * jb.y);
-  f[6] = (__bf16)(ib.z * jb.z); f[7] = (__bf16)(ib.w * jb.w);
-  return f;
+#pragma unroll
+  for (int tp = 0; tp < 2; ++tp) {
+    const float4 ia = *reinterpret_cast<const float4*>(&tl.KT[irow[tp]][32 * m + 4 * g]);
+    const float4 ib = *reinterpret_cast<const float4*>(&tl.KT[irow[tp]][32 * m + 16 + 4 * g]);
+    const uint4 f{pack_bf16x2(ia.x * ja.x, ia.y * ja.y), pack_bf16x2(ia.z * ja.z, ia.w * ja.w),
+                  pack_bf16x2(ib.x * jb.x, ib.y * jb.y), pack_bf16x2(ib.z * jb.z, ib.w * jb.w)};
+    a[tp] = __builtin_bit_cast(bf16x8, f);
+  }
 }
 
 // k_s[16 mi + lane%16] over the slots of 32-key step m (operand of Z = K^T K)
@@ -168,27 +175,69 @@ __device__ __forceinline__ bf16x8 kcol(const TL& tl, int mi, int m, int lane) {
   return f;
 }
 
-// Row sources of this lane's row of each owned tile.
+// Row sources of this lane's row of each owned pair: ps < kFull the whole pairs, ps = kFull
+// the half-pair (when the wave has one).
 struct Rows32 {
-  int irow[kSlots], jrow[kSlots];
-  __device__ void init(int w, int lane) {
+  int irow[kFull + 1][2], jrow[kFull + 1];
+  __device__ void init(int w, int e, int lane) {
 #pragma unroll
-    for (int sl = 0; sl < kSlots; ++sl) {
-      const int t = owns(w, sl) ? tile_of(w, sl) : 0, row = lane & 15;
+    for (int ps = 0; ps <= kFull; ++ps) {
+      const int P = ps < kFull ? pair_of(w, ps) : 16 + (e >= 0 ? e >> 1 : 0), row = lane & 15;
       int a, J;
-      double_group(4 * (t >> 1) + (row >> 2), a, J);
-      const int i = a + (t & 1), j = 4 * J + (row & 3);
-      irow[sl] = i > j ? KT_Z0 + 1 - (i & 1) : (i == j ? kt_row(i) : KT_D + kt_row(i));
-      jrow[sl] = kt_row(j);
+      double_group(4 * P + (row >> 2), a, J);
+      const int j = 4 * J + (row & 3);
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp) {
+        const int i = a + tp;
+        irow[ps][tp] = i > j ? KT_Z0 + 1 - (i & 1) : (i == j ? kt_row(i) : KT_D + kt_row(i));
+      }
+      jrow[ps] = kt_row(j);
     }
   }
 };
 
-// S[slot] += Phi(K)^T V over one staged chunk; Zt += the 16 x 16 tile (z >> 1, z & 1) of
-// K^T K when z >= 0 (waves 0-3 own one tile each and keep only that tile).
+// The accumulators of one wave's share of S: S[ps][tp][nt] for tile 2 pair_of(w, ps) + tp and
+// value tile nt; Sx[tp][n] for tile 32 + 2 (e / 2) + tp and value tile 2 (e % 2) + n.
+struct Acc32 {
+  f32x4 S[kFull][2][4];
+  f32x4 Sx[2][2];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int ps = 0; ps < kFull; ++ps)
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) S[ps][tp][nt] = zero4();
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) Sx[tp][n] = zero4();
+  }
+  // f(accumulator, state float offset of its fragment) for every owned fragment
+  template <class F>
+  __device__ __forceinline__ void each(int w, int e, int lane, F&& f) {
+#pragma unroll
+    for (int ps = 0; ps < kFull; ++ps)
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          f(S[ps][tp][nt], (((2 * pair_of(w, ps) + tp) * 4 + nt) * 64 + lane) * 4);
+    if (e >= 0) {
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          f(Sx[tp][n], (((2 * (16 + (e >> 1)) + tp) * 4 + 2 * (e & 1) + n) * 64 + lane) * 4);
+    }
+  }
+};
+
+// S += Phi(K)^T V over one staged chunk; Zt += the 16 x 16 tile (z >> 1, z & 1) of K^T K when
+// z >= 0.  e and z are wave-uniform.
 template <class TL>
-__device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, f32x4 (&S)[kSlots][4],
-                                         f32x4& Zt, int w, int lane, int z) {
+__device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, Acc32& acc, f32x4& Zt,
+                                         int e, int lane, int z) {
   // both 32-key steps unrolled: the LDS addresses of the second become immediate offsets
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
@@ -196,13 +245,30 @@ __device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, f32x4 (
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) vb[nt] = v_frag(tl.V, m, nt, lane);
 #pragma unroll
-    for (int sl = 0; sl < kSlots; ++sl) {
-      if (!owns(w, sl)) continue;
-      const bf16x8 a = phik(tl, rw.irow[sl], rw.jrow[sl], m, lane);
+    for (int ps = 0; ps < kFull; ++ps) {
+      bf16x8 a[2];
+      phik2(tl, rw.irow[ps], rw.jrow[ps], m, lane, a);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) S[sl][nt] = mfma32(a, vb[nt], S[sl][nt]);
+      for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc.S[ps][tp][nt] = mfma32(a[tp], vb[nt], acc.S[ps][tp][nt]);
     }
-    if (z >= 0) {                                  // wave-uniform
+    if (e >= 0) {
+      bf16x8 a[2];
+      phik2(tl, rw.irow[kFull], rw.jrow[kFull], m, lane, a);
+      if (e & 1) {
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+          for (int n = 0; n < 2; ++n) acc.Sx[tp][n] = mfma32(a[tp], vb[2 + n], acc.Sx[tp][n]);
+      } else {
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+          for (int n = 0; n < 2; ++n) acc.Sx[tp][n] = mfma32(a[tp], vb[n], acc.Sx[tp][n]);
+      }
+    }
+    if (z >= 0) {
       const int mi = z >> 1, kj = z & 1;
       const bf16x8 a = kcol(tl, mi, m, lane), bb = kcol(tl, kj, m, lane);
       Zt = mfma32(a, bb, Zt);
@@ -222,7 +288,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
     const __bf16* __restrict__ v, float* __restrict__ states) {
   extern __shared__ __align__(16) unsigned char smem[];
   StateTiles32* tl = reinterpret_cast<StateTiles32*>(smem);    // two buffers
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int e = extra_of(w), z = ztile_of(w);
   const SegBlock blk = seg_block(sg, pr.H);
   if (!blk.live) return;                           // padding of the grid (whole workgroup)
   const int seg = blk.seg, h = blk.h, b = blk.b;
@@ -234,13 +301,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
     for (int x = tid; x < kStateFloats / 4; x += kThreads) o4[x] = float4{0.f, 0.f, 0.f, 0.f};
     return;
   }
-  f32x4 S[kSlots][4], Zt = zero4();
-#pragma unroll
-  for (int sl = 0; sl < kSlots; ++sl)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) S[sl][nt] = zero4();
+  Acc32 acc;
+  acc.zero();
+  f32x4 Zt = zero4();
   Rows32 rw;
-  rw.init(w, lane);
+  rw.init(w, e, lane);
   zero_row(tl[0], tid);
   zero_row(tl[1], tid);
 
@@ -256,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
   }
   __syncthreads();
   for (int c = 0; c < nc; ++c) {
-    update32(tl[c & 1], rw, S, Zt, w, lane, w < 4 ? w : -1);   // Z tile w on waves 0-3
+    update32(tl[c & 1], rw, acc, Zt, e, lane, z);
     if (c + 1 < nc) store_state32(st, tl[(c + 1) & 1], tid);   // buffer read last iteration
     if (c + 2 < nc) {
       p.next();
@@ -264,15 +329,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
     }
     __syncthreads();
   }
-#pragma unroll
-  for (int sl = 0; sl < kSlots; ++sl) {
-    if (!owns(w, sl)) continue;
-    const int t = tile_of(w, sl);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      *reinterpret_cast<f32x4*>(out + ((t * 4 + nt) * 64 + lane) * 4) = S[sl][nt];
-  }
-  if (w < 4) *reinterpret_cast<f32x4*>(out + kZOff + (w * 64 + lane) * 4) = Zt;
+  acc.each(w, e, lane, [&](f32x4& x, int off) { *reinterpret_cast<f32x4*>(out + off) = x; });
+  if (z >= 0) *reinterpret_cast<f32x4*>(out + kZOff + (z * 64 + lane) * 4) = Zt;
 }
 
 struct Pair4 {
@@ -350,7 +408,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
   extern __shared__ __align__(16) unsigned char smem[];
   Walk32Lds& sm = *reinterpret_cast<Walk32Lds*>(smem);
   Tiles32& tl = sm.tl;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tg = w & 3, ch = w >> 2;
   const SegBlock blk = seg_block(sg, pr.H);
   if (!blk.live) return;                           // padding of the grid (whole workgroup)
@@ -360,30 +419,22 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
 
   // Exclusive prefix of this segment: the scanned state at position seg, or (sum_prefix)
   // the states of segments 0 .. seg-1 added in that order; zero without states.
-  // Z: wave w < 4 keeps tile (w >> 1, w & 1) in Zt and publishes it split into bf16 hi + lo
-  const int zt = w < 4 ? w : -1;
-  f32x4 S[kSlots][4], Zt = zero4();
-#pragma unroll
-  for (int sl = 0; sl < kSlots; ++sl)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) S[sl][nt] = zero4();
+  // Z: wave w with zt >= 0 keeps tile (zt >> 1, zt & 1) in Zt and publishes it split into
+  // bf16 hi + lo.
+  const int e = extra_of(w), zt = ztile_of(w);
+  Acc32 acc;
+  acc.zero();
+  f32x4 Zt = zero4();
   {
     const int j0 = sum_prefix ? 0 : seg, j1 = !states ? j0 : sum_prefix ? seg : seg + 1;
     for (int j = j0; j < j1; ++j) {
       const float* pre = states + ((long long)(b * pr.H + h) * n_seg + j) * kStateFloats;
-#pragma unroll
-      for (int sl = 0; sl < kSlots; ++sl) {
-        if (!owns(w, sl)) continue;
-        const int t = tile_of(w, sl);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          S[sl][nt] += *reinterpret_cast<const f32x4*>(pre + ((t * 4 + nt) * 64 + lane) * 4);
-      }
+      acc.each(w, e, lane, [&](f32x4& x, int off) { x += *reinterpret_cast<const f32x4*>(pre + off); });
       if (zt >= 0) Zt += *reinterpret_cast<const f32x4*>(pre + kZOff + (zt * 64 + lane) * 4);
     }
   }
   Rows32 rw;
-  rw.init(w, lane);
+  rw.init(w, e, lane);
   zero_row(tl, tid);
   if (tid < 4 * kSteps) {
     int a, J;
@@ -392,18 +443,21 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     sm.dg[tid][1] = (unsigned char)(4 * J);
   }
 
+  // a pair's two accumulators -> one B-operand word of its K step (tile 2 P in the low half)
+  auto bword = [](const f32x4& lo, const f32x4& hi) {
+    return uint4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                 pack_bf16x2(hi[2], hi[3])};
+  };
   auto publish = [&]() {
 #pragma unroll
-    for (int sl = 0; sl < kSlots; ++sl) {
-      if (!owns(w, sl)) continue;
-      const int t = tile_of(w, sl);
+    for (int ps = 0; ps < kFull; ++ps)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 x;
+      for (int nt = 0; nt < 4; ++nt)
+        sm.Sb[pair_of(w, ps)][nt][lane] = bword(acc.S[ps][0][nt], acc.S[ps][1][nt]);
+    if (e >= 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = (__bf16)S[sl][nt][r];
-        reinterpret_cast<uint2*>(&sm.Sb[t >> 1][nt][lane])[t & 1] = __builtin_bit_cast(uint2, x);
-      }
+      for (int n = 0; n < 2; ++n)
+        sm.Sb[16 + (e >> 1)][2 * (e & 1) + n][lane] = bword(acc.Sx[0][n], acc.Sx[1][n]);
     }
     if (zt >= 0) {
       const f32x4 zr = Zt;
@@ -554,7 +608,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     }
 
     // ---- state update with this chunk (registers only: Sb keeps S_{<c} until the barrier) ----
-    update32(tl, rw, S, Zt, w, lane, zt);
+    update32(tl, rw, acc, Zt, e, lane, zt);
     __syncthreads();          // all reads of this chunk's tiles, Sb and Zb; xr and zx written
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
