@@ -10,15 +10,18 @@
 // The state is always packed (the 528 unique pairs i <= j of the 32 x 32 feature, the ai.info
 // state-size bullet's packed coordinates): 72 double groups = 36 tiles of 16 rows, 18 readout
 // K steps.  That is 147 KB of fp32 per state, too much for four waves' registers, so a
-// workgroup has eight waves (two per SIMD, one workgroup per CU):
+// workgroup has eight waves (two per SIMD, one workgroup per CU; waves w and w + 4 share a
+// SIMD):
 //   state tiles  the tiles go in K-step pairs (2 P, 2 P + 1).  Wave w owns pairs w and w + 8
 //                with all four value tiles; the last two pairs are split by value-tile halves
-//                over waves 0, 1, 4 and 5 (the token groups with the least intra-chunk work),
-//                and the four Z tiles go to waves 2, 3, 6 and 7.  The two tiles of a pair share
-//                their j factor rows, which the update reads once, and their accumulators make
-//                whole B-operand words of the readout, which the publish writes at once,
-//   tokens       wave w serves tokens [16 tg, 16 tg + 16) of a chunk, tg = w % 4, and the value
-//                columns [32 ch, 32 ch + 32), ch = w / 4.  The two waves of a token group
+//                over waves 0-3, and the four Z tiles go to waves 4-7 (one of each per SIMD).
+//                The two tiles of a pair share their j factor rows, which the update reads
+//                once, and their accumulators make whole B-operand words of the readout, which
+//                the publish writes at once,
+//   tokens       wave w serves tokens [16 tg, 16 tg + 16) of a chunk and the value columns
+//                [32 ch, 32 ch + 32), ch = w / 4, tg = w % 4 for ch = 0 and 3 - w % 4 for
+//                ch = 1: each SIMD runs token groups tg and 3 - tg, whose causal intra-chunk
+//                tiles add up to the same work.  The two waves of a token group (w and 7 - w)
 //                split the readout's K steps instead of its columns (each forms phi(q) for
 //                half the features, the VALU cost of the readout) and swap the partial sums
 //                of each other's columns through LDS.
@@ -65,8 +68,10 @@ struct __align__(16) StateTiles32 {                  // the state pass needs no 
 // Tile ownership (see the file comment): whole pair ps < kFull of wave w, the half-pair of
 // extra index e (pair 16 + e / 2, value tiles 2 (e % 2) + {0, 1}) and the Z tile index.
 __device__ __forceinline__ int pair_of(int w, int ps) { return w + 8 * ps; }
-__device__ __forceinline__ int extra_of(int w) { return (w & 2) ? -1 : (w & 1) | ((w >> 2) << 1); }
-__device__ __forceinline__ int ztile_of(int w) { return (w & 2) ? (w & 1) | ((w >> 2) << 1) : -1; }
+__device__ __forceinline__ int extra_of(int w) { return w < 4 ? w : -1; }
+__device__ __forceinline__ int ztile_of(int w) { return w < 4 ? -1 : w - 4; }
+// token group of wave w (see the file comment); its partner wave is 7 - w
+__device__ __forceinline__ int tgroup_of(int w) { return w < 4 ? w : 7 - w; }
 static_assert(2 * (8 * kFull + 2) == kTiles, "pairs: kFull per wave and two split pairs");
 
 // One thread's share of a chunk's loads: threads 0-255 a quarter q row, 256-511 a quarter
@@ -345,7 +350,7 @@ struct Pair4 {
 // this rare path pays for the call.
 __device__ __attribute__((noinline)) Pair4 intra_exact32(const Tiles32& tl, bf16x8 qf, int w,
                                                          int lane) {
-  const int g = lane >> 4, l16 = lane & 15, tg = w & 3, ch = w >> 2, t = 16 * tg + l16;
+  const int g = lane >> 4, l16 = lane & 15, tg = tgroup_of(w), ch = w >> 2, t = 16 * tg + l16;
   float lsum = 0.f;
   f32x4 O[2] = {zero4(), zero4()};
 #pragma unroll
@@ -410,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
   Tiles32& tl = sm.tl;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tg = w & 3, ch = w >> 2;
+  const int tg = tgroup_of(w), ch = w >> 2;
   const SegBlock blk = seg_block(sg, pr.H);
   if (!blk.live) return;                           // padding of the grid (whole workgroup)
   const int seg = blk.seg, h = blk.h, b = blk.b;
@@ -597,7 +602,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
       for (int n = 0; n < 4; ++n)
         R[n] = mfma32(a, __builtin_bit_cast(bf16x8, sm.Sb[kk][n][lane]), R[n]);
     }
-    // the other wave of the token group (w ^ 4) owns the other two value tiles (selects, not
+    // the other wave of the token group (7 - w) owns the other two value tiles (selects, not
     // a runtime index, keep R in registers); it reads them after the update's barrier
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
@@ -612,12 +617,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     __syncthreads();          // all reads of this chunk's tiles, Sb and Zb; xr and zx written
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      const f32x4 x = sm.xr[w ^ 4][n][lane];
+      const f32x4 x = sm.xr[7 - w][n][lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) O[n][r] += x[r];
     }
     // both waves add the halves in the order kj = 0, 1: the same D bit for bit
-    const float zo = sm.zx[w ^ 4][lane];
+    const float zo = sm.zx[7 - w][lane];
     const float D = pr.eps + ((ch ? zo + zq : zq + zo) + lsum);   // D_t of token t
     if (g == 0) sm.inv[w][l16] = __builtin_amdgcn_rcpf(D);        // 1 ulp
     const float4 inv4 = *reinterpret_cast<const float4*>(&sm.inv[w][4 * g]);   // own writes
