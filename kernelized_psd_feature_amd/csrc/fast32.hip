@@ -46,8 +46,8 @@ constexpr int VROW = 80;                             // bf16 per v row: 160 B
 // group of the update reads k_i, 2 k_i, k_{i+2}, 2 k_{i+2} and a zero row for one parity of i,
 // which this placement (doubled rows 4 groups over, the zero row of the other parity) puts on
 // distinct bank groups.  kt_row rotates each block of 8 features by twice the block index:
-// the staging writes of one instruction (features 8 qc + e of 8 tokens for the 4 quarters qc)
-// then fall on 4 distinct bank groups too, and the reads keep their groups distinct.
+// the staging writes of one instruction (feature 4 pc + f of 8 tokens for the pieces pc = 0-3
+// or 4-7) then fall on 4 distinct bank groups too, and the reads keep their groups distinct.
 constexpr int KT_D = 36, KT_Z0 = 68, KTROWS = 70;
 static_assert(KT_D % 8 == 4 && KT_D >= P && KT_Z0 >= KT_D + P && KT_Z0 % 8 == 4 &&
               KTROWS == KT_Z0 + 2, "K^T row placement");
@@ -74,19 +74,27 @@ __device__ __forceinline__ int ztile_of(int w) { return w < 4 ? -1 : w - 4; }
 __device__ __forceinline__ int tgroup_of(int w) { return w < 4 ? w : 7 - w; }
 static_assert(2 * (8 * kFull + 2) == kTiles, "pairs: kFull per wave and two split pairs");
 
-// One thread's share of a chunk's loads: threads 0-255 a quarter q row, 256-511 a quarter
-// k row (row = (tid & 255) / 4, columns 8 (tid % 4) ..), every thread 16 B of one v row
-// (row tid / 8, columns 8 (tid % 8) ..).
+// One thread's share of a chunk's loads: 8 bytes (features 4 pc .. 4 pc + 3) of the q row
+// and of the k row of token stage_row, and 16 bytes of one v row (row tid / 8, columns
+// 8 (tid % 8) ..).  Wave w stages tokens 8 w .. 8 w + 7; lanes 0-31 hold features 0-15 and
+// lanes 32-63 features 16-31, so one K^T store instruction (feature 4 pc + f of 8 tokens for
+// 4 pieces pc) falls on 4 distinct bank groups (kt_row) and every thread stores the same share.
+__device__ __forceinline__ int stage_row(int tid) { return 8 * (tid >> 6) + ((tid & 31) >> 2); }
+__device__ __forceinline__ int stage_piece(int tid) { return 4 * ((tid >> 5) & 1) + (tid & 3); }
+
 struct Stage32 {
-  uint4 qk, v;
+  uint2 q, k;
+  uint4 v;
 };
 
 struct Ptrs32 {
-  const __bf16* qk;
+  const __bf16* q;
+  const __bf16* k;
   const __bf16* v;
-  long long qk_step, v_step;
+  long long q_step, k_step, v_step;
   __device__ __forceinline__ void next() {
-    if (qk) qk += qk_step;
+    if (q) q += q_step;
+    k += k_step;
     v += v_step;
   }
 };
@@ -95,33 +103,31 @@ __device__ __forceinline__ Ptrs32 ptrs32(const DevProblem& pr, const __bf16* q, 
                                          const __bf16* v, int b, int h, int tok0, bool with_q,
                                          int tid, int dir) {
   Ptrs32 p;
-  const int lo = tid & 255, row = lo >> 2, qc = lo & 3;
-  if (tid < 256) {
-    p.qk = with_q ? q + row_off(pr.sq, b, tok0 + row, h) + 8 * qc : nullptr;
-    p.qk_step = (long long)dir * C * pr.sq[1];
-  } else {
-    p.qk = k + row_off(pr.sk, b, tok0 + row, h) + 8 * qc;
-    p.qk_step = (long long)dir * C * pr.sk[1];
-  }
+  const int row = stage_row(tid), pc = stage_piece(tid);
+  p.q = with_q ? q + row_off(pr.sq, b, tok0 + row, h) + 4 * pc : nullptr;
+  p.q_step = (long long)dir * C * pr.sq[1];
+  p.k = k + row_off(pr.sk, b, tok0 + row, h) + 4 * pc;
+  p.k_step = (long long)dir * C * pr.sk[1];
   p.v = v + row_off(pr.sv, b, tok0 + (tid >> 3), h) + 8 * (tid & 7);
   p.v_step = (long long)dir * C * pr.sv[1];
   return p;
 }
 
 __device__ __forceinline__ void load32(Stage32& s, const Ptrs32& p) {
-  if (p.qk) s.qk = ld16(p.qk);
+  if (p.q) s.q = *reinterpret_cast<const uint2*>(p.q);
+  s.k = *reinterpret_cast<const uint2*>(p.k);
   s.v = ld16(p.v);
 }
 
-// k piece -> K^T rows (k, 2 k); q / k piece -> row-major rows (when the tile has them)
+// k piece -> K^T rows (k, 2 k)
 template <class TL>
 __device__ __forceinline__ void store_kt(const Stage32& s, TL& tl, int tid) {
-  const int lo = tid & 255, row = lo >> 2, qc = lo & 3;
-  const uint32_t wd[4] = {s.qk.x, s.qk.y, s.qk.z, s.qk.w};
+  const int row = stage_row(tid), pc = stage_piece(tid);
+  const uint32_t wd[2] = {s.k.x, s.k.y};
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
+  for (int e = 0; e < 2; ++e) {
     const float a = bf_lo(wd[e]), c = bf_hi(wd[e]);
-    const int ra = kt_row(8 * qc + 2 * e), rc = kt_row(8 * qc + 2 * e + 1);
+    const int ra = kt_row(4 * pc + 2 * e), rc = kt_row(4 * pc + 2 * e + 1);
     tl.KT[ra][row] = a;
     tl.KT[rc][row] = c;
     tl.KT[KT_D + ra][row] = 2.f * a;        // exact
@@ -129,19 +135,17 @@ __device__ __forceinline__ void store_kt(const Stage32& s, TL& tl, int tid) {
   }
 }
 
+// q / k pieces -> row-major rows (q when the tile has them) and K^T rows; v piece -> V
 __device__ __forceinline__ void store32(const Stage32& s, Tiles32& tl, bool with_q, int tid) {
-  const int lo = tid & 255, row = lo >> 2, qc = lo & 3;
-  if (tid < 256) {
-    if (with_q) *reinterpret_cast<uint4*>(&tl.Qs[row][8 * qc]) = s.qk;
-  } else {
-    *reinterpret_cast<uint4*>(&tl.Ks[row][8 * qc]) = s.qk;
-    store_kt(s, tl, tid);
-  }
+  const int row = stage_row(tid), pc = stage_piece(tid);
+  if (with_q) *reinterpret_cast<uint2*>(&tl.Qs[row][4 * pc]) = s.q;
+  *reinterpret_cast<uint2*>(&tl.Ks[row][4 * pc]) = s.k;
+  store_kt(s, tl, tid);
   *reinterpret_cast<uint4*>(&tl.V[tid >> 3][8 * (tid & 7)]) = s.v;
 }
 
 __device__ __forceinline__ void store_state32(const Stage32& s, StateTiles32& tl, int tid) {
-  if (tid >= 256) store_kt(s, tl, tid);
+  store_kt(s, tl, tid);
   *reinterpret_cast<uint4*>(&tl.V[tid >> 3][8 * (tid & 7)]) = s.v;
 }
 
