@@ -508,11 +508,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
       load32(st, p);
     }
 
-    const uint4 vb0 = *reinterpret_cast<const uint4*>(&sm.vbad[0]);
-    const uint4 vb1 = *reinterpret_cast<const uint4*>(&sm.vbad[4]);
-    const bool vbad = __builtin_amdgcn_readfirstlane(vb0.x | vb0.y | vb0.z | vb0.w | vb1.x |
-                                                     vb1.y | vb1.z | vb1.w) != 0;
-
     // ---- intra-chunk tile of this wave's tokens and value columns ----
     float lsum = 0.f;
     f32x4 O[2] = {zero4(), zero4()};
