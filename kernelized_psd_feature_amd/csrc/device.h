@@ -43,6 +43,8 @@ hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
 struct DevProblem {
   int B, H, T, p, dv, C;
   int gs;                                          // KATA-Mg group width (p: one group)
+  int stored_compact;                              // packed p = 16 segment states stored
+                                                   // without their zero rows (scan plans)
   float eps;
   long long sq[3], sk[3], sv[3], so[3], sdo[3];   // element strides of (b, t, h)
 };

@@ -18,6 +18,8 @@
 // inter-chunk denominator q^T Z q keeps fp32 accuracy: Z q runs on MFMA with Z split into a
 // bf16 high part and a bf16 remainder (q is exact in bf16), the final dot with q in fp32.
 //
+#include <type_traits>
+
 #include "device.h"
 #include "kata.h"
 #include "mfma_util.h"
@@ -275,6 +277,132 @@ static_assert(Layout<false>::kStateFloats == kStateFloats, "direct state size");
 static_assert(Layout<true>::kTiles == 10 && Layout<true, 8>::kTiles == 6 &&
               Layout<true, 4>::kTiles == 4, "packed tile counts (plan.cpp)");
 
+// A state as stored in the workspace (state pass -> scan -> walk).  The direct layout, and the
+// packed ones when the walks add the segment states themselves (few segments), store the
+// fragments as they are (above).  With the segment scan (DevProblem::stored_compact), the
+// packed states leave out their zero rows.  A packed fragment (tile t, lane group gp) holds rows
+// j = 4 J + r, r = 0..3, of double group (a, J) = Layout::dg(4 (t / 2) + gp) at i = a + t % 2;
+// its rows with i > j (inside the diagonal double groups) are zero in every state and are
+// not stored: blocks [t][nt][gp] of 16 columns c x (stored rows), column-major, so a lane's
+// rows sit together (one 16-byte access for a whole fragment), then Z as one 16 x 16 tile
+// (lane-major).  That leaves the p (GW + 1) / 2 unique pairs' rows: 136 of the 160 rows at
+// GW = 16, 15 % fewer bytes for each state the step writes, scans and reads.
+template <int GW>
+struct StoredPacked {
+  static constexpr int kTiles = Layout<true, GW>::kTiles;
+  unsigned char mask[kTiles][4];      // bit r: row r of fragment (t, gp) is stored
+  int base[kTiles][4];                // float offset of block (t, nt = 0, gp)
+  int stride[kTiles];                 // floats from value tile nt to nt + 1 of tile t
+  int zoff;                           // float offset of Z
+};
+constexpr int dg_J(int idx) {
+  int J = 0;
+  while ((J + 1) * (J + 2) <= idx) ++J;
+  return J;
+}
+template <int GW>
+constexpr StoredPacked<GW> make_stored_packed() {
+  using LY = Layout<true, GW>;
+  StoredPacked<GW> sp{};
+  int off = 0;
+  for (int t = 0; t < LY::kTiles; ++t) {
+    int rows = 0;
+    for (int gp = 0; gp < 4; ++gp) {
+      const int idx = 4 * (t >> 1) + gp, grp = idx / LY::kGroupDG, loc = idx - grp * LY::kGroupDG;
+      const int J0 = dg_J(loc), a = 2 * (loc - J0 * (J0 + 1)) + grp * GW;
+      const int J = J0 + grp * (GW / 4), i = a + (t & 1);
+      int m = 0, n = 0;
+      for (int r = 0; r < 4; ++r)
+        if (i <= 4 * J + r) { m |= 1 << r; ++n; }
+      sp.mask[t][gp] = (unsigned char)m;
+      sp.base[t][gp] = off + 16 * rows;
+      rows += n;
+    }
+    sp.stride[t] = 16 * rows;
+    off += 4 * 16 * rows;
+  }
+  sp.zoff = off;
+  return sp;
+}
+template <bool kPacked, int GW>
+struct Stored {
+  static constexpr int kZOffFull = Layout<kPacked, GW>::kZOff;
+  static constexpr int kZOffCompact = kPacked ? make_stored_packed<GW>().zoff : kZOffFull;
+  __device__ static int zoff(bool compact) { return compact ? kZOffCompact : kZOffFull; }
+  __device__ static int floats(bool compact) { return zoff(compact) + 256; }
+};
+// the unique pairs of each group, the count the planner sizes the workspace with (plan.cpp)
+static_assert(Stored<true, 16>::kZOffCompact == 16 * 17 / 2 * DV &&
+              Stored<true, 8>::kZOffCompact == 16 * 9 / 2 * DV &&
+              Stored<true, 4>::kZOffCompact == 16 * 5 / 2 * DV &&
+              Stored<false, P>::kZOffFull + 256 == kStateFloats, "stored state sizes");
+__constant__ StoredPacked<16> kStored16 = make_stored_packed<16>();
+__constant__ StoredPacked<8> kStored8 = make_stored_packed<8>();
+__constant__ StoredPacked<4> kStored4 = make_stored_packed<4>();
+template <int GW>
+__device__ __forceinline__ const StoredPacked<GW>& stored_packed() {
+  if constexpr (GW == 16) return kStored16;
+  else if constexpr (GW == 8) return kStored8;
+  else return kStored4;
+}
+
+// Where one lane's fragment of tile t (rows 4 (slot / 16) + r, column 16 nt + slot % 16)
+// sits in a stored state: float offset off + nt * stride, its stored rows (bit r of mask) in
+// order.  The stored rows of a fragment are always its top ones (masks 0xF, 0xE, 0xC, 0x8:
+// i > j holds for the first rows j = 4 J + r), so row r of a fragment with n stored rows is
+// float r - (4 - n) from off.  slot is the lane of the fragment's owner in the state's layout.
+template <bool kPacked, int GW, bool kCompact>
+struct FragPlace {
+  static constexpr bool compact = kPacked && kCompact;
+  int off, stride, mask;
+  __device__ __forceinline__ void init(int t, int slot) {
+    if constexpr (!compact) {
+      off = (t * 4 * 64 + slot) * 4;
+      stride = 64 * 4;
+      mask = 0xF;
+    } else {
+      const StoredPacked<GW>& sp = stored_packed<GW>();
+      const int gp = slot >> 4;
+      mask = sp.mask[t][gp];
+      off = sp.base[t][gp] + (slot & 15) * __builtin_popcount(mask);
+      stride = sp.stride[t];
+    }
+  }
+  __device__ __forceinline__ void store(float* out, int nt, const f32x4& x) const {
+    float* o = out + off + nt * stride;
+    if (!compact || mask == 0xF) {     // constant, or one lane group's mask
+      *reinterpret_cast<f32x4*>(o) = x;
+    } else {
+#pragma unroll
+      for (int r = 1; r < 4; ++r)          // bit 0 is set only in whole fragments
+        if ((mask >> r) & 1) o[__builtin_popcount(mask & ((1 << r) - 1))] = x[r];
+    }
+  }
+  // Branch-free, so the loads of all fragments are in flight together: the four floats from
+  // row 0's place (before off when rows are missing: the previous lane's or block's floats,
+  // inside the state since the state's first fragment is whole), the missing rows' values
+  // replaced by zero.
+  __device__ __forceinline__ void add(const float* in, int nt, f32x4& x) const {
+    if constexpr (!compact) {
+      x += *reinterpret_cast<const f32x4*>(in + off + nt * stride);
+    } else {
+      const int miss = 4 - __builtin_popcount(mask);
+      const float* q = in + off + nt * stride - miss;
+      float v[4];
+      __builtin_memcpy(v, q, sizeof(v));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] += r >= miss ? v[r] : 0.f;
+    }
+  }
+};
+// f(std::true_type) for compactly stored states, f(std::false_type) otherwise: the layout is
+// a compile-time choice inside f, and the one branch on the wave-uniform flag sits outside it
+template <class F>
+__device__ __forceinline__ void with_stored_layout(bool compact, F&& f) {
+  if (compact) f(std::true_type{});
+  else f(std::false_type{});
+}
+
 // Row sources of the packed update's A operand for this lane's row of each owned tile.
 template <bool kPacked, int GW>
 struct UpdateRows {
@@ -365,12 +493,13 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
   const int n_chunks = pr.T / C;
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
   const long long sv_t = pr.sv[1];
+  const int n_stored = Stored<kPacked, GW>::floats(pr.stored_compact);
   if (seg >= n_used) {
     // a state no prefix needs (the last segment's, in the forward): zeros for the scan, and
     // its k, v are not read
     float4* out = reinterpret_cast<float4*>(
-        states + ((long long)(b * pr.H + h) * n_seg + seg) * LY::kStateFloats);
-    for (int x = tid; x < LY::kStateFloats / 4; x += kThreads) out[x] = float4{0.f, 0.f, 0.f, 0.f};
+        states + ((long long)(b * pr.H + h) * n_seg + seg) * n_stored);
+    for (int x = tid; x < n_stored / 4; x += kThreads) out[x] = float4{0.f, 0.f, 0.f, 0.f};
     return;
   }
 
@@ -407,16 +536,19 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_fast_kernel(
     step(c, sa);                     // chunk c+1 is in sa, chunk c+2 in sb
     if (c + 1 < nc) step(c + 1, sb);
   }
-  float* out = states + ((long long)(b * pr.H + h) * n_seg + seg) * LY::kStateFloats;
+  float* out = states + ((long long)(b * pr.H + h) * n_seg + seg) * n_stored;
+  with_stored_layout(pr.stored_compact, [&](auto compact) {
 #pragma unroll
-  for (int sl = 0; sl < LY::kSlots; ++sl) {
-    if (!LY::owns(w, sl)) continue;
-    const int t = LY::tile(w, sl);
+    for (int sl = 0; sl < LY::kSlots; ++sl) {
+      if (!LY::owns(w, sl)) continue;
+      FragPlace<kPacked, GW, decltype(compact)::value> fp;
+      fp.init(LY::tile(w, sl), lane);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      *reinterpret_cast<f32x4*>(out + ((t * 4 + nt) * 64 + lane) * 4) = S[sl][nt];
-  }
-  if (w == 0) *reinterpret_cast<f32x4*>(out + LY::kZOff + lane * 4) = Z;
+      for (int nt = 0; nt < 4; ++nt) fp.store(out, nt, S[sl][nt]);
+    }
+  });
+  if (w == 0)
+    *reinterpret_cast<f32x4*>(out + Stored<kPacked, GW>::zoff(pr.stored_compact) + lane * 4) = Z;
 }
 
 // ==========================================================================================
@@ -460,12 +592,15 @@ __device__ __forceinline__ bf16x8 phik_bcast(const float (&kf)[8]) {
 // block J = g, i.e. packed tile 2 (idx / 4) + i % 2, lane group idx % 4, idx = J (J + 1) + a / 2,
 // same register r; off-diagonal rows carry weight 2 (exact), pairs with i > j inside a double
 // group are zero rows, and lane groups with i > 4g + 3 hold no packed row.
+template <bool kCompact>
 __device__ __forceinline__ void store_packed_from_direct(float* out, int i, const f32x4 (&S)[4],
                                                         int lane) {
   const int g = lane >> 4, c = lane & 15;
   if (i > 4 * g + 3) return;
   const int idx = g * (g + 1) + (i >> 1);
   const int t = 2 * (idx >> 2) + (i & 1), gp = idx & 3;
+  FragPlace<true, P, kCompact> fp;
+  fp.init(t, 16 * gp + c);
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     f32x4 x;
@@ -474,7 +609,7 @@ __device__ __forceinline__ void store_packed_from_direct(float* out, int i, cons
       const int j = 4 * g + r;
       x[r] = i < j ? 2.f * S[nt][r] : (i == j ? S[nt][r] : 0.f);
     }
-    *reinterpret_cast<f32x4*>(out + ((t * 4 + nt) * 64 + 16 * gp + c) * 4) = x;
+    fp.store(out, nt, x);
   }
 }
 
@@ -557,10 +692,11 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_dpp_kernel(
   const int seg = blk.seg, h = blk.h, b = blk.b;
   const int n_chunks = pr.T / C;
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
-  float* out = states + ((long long)(b * pr.H + h) * n_seg + seg) * LY::kStateFloats;
+  using ST = Stored<kPackedOut, P>;
+  float* out = states + ((long long)(b * pr.H + h) * n_seg + seg) * ST::floats(pr.stored_compact);
   if (seg >= n_used) {
     // a state no prefix needs (the last segment's, in the forward): zeros, k and v unread
-    for (int x = tid; x < LY::kStateFloats / 4; x += kThreads)
+    for (int x = tid; x < ST::floats(pr.stored_compact) / 4; x += kThreads)
       reinterpret_cast<float4*>(out)[x] = float4{0.f, 0.f, 0.f, 0.f};
     return;
   }
@@ -586,14 +722,16 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_dpp_kernel(
   for (int sl = 0; sl < 4; ++sl) {
     const int i = 4 * w + sl;
     if (kPackedOut) {
-      store_packed_from_direct(out, i, S[sl], lane);
+      with_stored_layout(pr.stored_compact, [&](auto compact) {
+        store_packed_from_direct<decltype(compact)::value>(out, i, S[sl], lane);
+      });
     } else {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
         *reinterpret_cast<f32x4*>(out + ((i * 4 + nt) * 64 + lane) * 4) = S[sl][nt];
     }
   }
-  if (w == 0) *reinterpret_cast<f32x4*>(out + LY::kZOff + lane * 4) = Z;
+  if (w == 0) *reinterpret_cast<f32x4*>(out + ST::zoff(pr.stored_compact) + lane * 4) = Z;
 }
 
 // ==========================================================================================
@@ -716,10 +854,11 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_hybrid_kernel(
   const int seg = blk.seg, h = blk.h, b = blk.b;
   const int n_chunks = pr.T / C;
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
-  float* out = states + ((long long)(b * pr.H + h) * n_seg + seg) * LY::kStateFloats;
+  using ST = Stored<true, P>;
+  float* out = states + ((long long)(b * pr.H + h) * n_seg + seg) * ST::floats(pr.stored_compact);
   if (seg >= n_used) {
     // a state no prefix needs (the last segment's, in the forward): zeros, k and v unread
-    for (int x = tid; x < LY::kStateFloats / 4; x += kThreads)
+    for (int x = tid; x < ST::floats(pr.stored_compact) / 4; x += kThreads)
       reinterpret_cast<float4*>(out)[x] = float4{0.f, 0.f, 0.f, 0.f};
     return;
   }
@@ -745,8 +884,10 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_hybrid_kernel(
     case 2: state_hybrid_loop<2>(tl, kp, vp, k_step, v_step, pr.sv[1], nc, tid, S, Z); break;
     default: state_hybrid_loop<3>(tl, kp, vp, k_step, v_step, pr.sv[1], nc, tid, S, Z); break;
   }
-  store_packed_from_direct(out, 2 * w, S[0], lane);
-  store_packed_from_direct(out, 2 * w + 1, S[1], lane);
+  with_stored_layout(pr.stored_compact, [&](auto compact) {
+    store_packed_from_direct<decltype(compact)::value>(out, 2 * w, S[0], lane);
+    store_packed_from_direct<decltype(compact)::value>(out, 2 * w + 1, S[1], lane);
+  });
   if (w < 3) {
     // gathered quad 4w + g of this lane: rows (i, 4J + r) -> packed tile 2 (idx / 4) + i % 2,
     // lane group idx % 4, idx = J (J + 1) + (i - i % 2) / 2, the same register r
@@ -755,11 +896,14 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_state_hybrid_kernel(
     gathered_quad(4 * w + g, i, J);
     const int idx = J * (J + 1) + (i >> 1);
     const int t = 2 * (idx >> 2) + (i & 1), gp = idx & 3;
+    with_stored_layout(pr.stored_compact, [&](auto compact) {
+      FragPlace<true, P, decltype(compact)::value> fp;
+      fp.init(t, 16 * gp + c);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      *reinterpret_cast<f32x4*>(out + ((t * 4 + nt) * 64 + 16 * gp + c) * 4) = S[2][nt];
+      for (int nt = 0; nt < 4; ++nt) fp.store(out, nt, S[2][nt]);
+    });
   } else {
-    *reinterpret_cast<f32x4*>(out + LY::kZOff + lane * 4) = Z;
+    *reinterpret_cast<f32x4*>(out + ST::zoff(pr.stored_compact) + lane * 4) = Z;
   }
 }
 
@@ -821,7 +965,9 @@ struct __align__(16) WalkLds {
 static_assert(sizeof(WalkLds<false, P>) <= 160 * 1024 / 3 && sizeof(WalkLds<true, P>) <= 160 * 1024 / 3,
               "three walks per CU");
 
-template <typename Tout, bool kPacked, int GW>
+// kCompact: the segment states are stored without their zero rows (pr.stored_compact); a
+// template parameter, so that each walk holds one form of the prefix load
+template <typename Tout, bool kPacked, int GW, bool kCompact>
 __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
     DevProblem pr, SegGrid sg, int L, int n_seg, const __bf16* __restrict__ q,
     const __bf16* __restrict__ k, const __bf16* __restrict__ v, Tout* __restrict__ o,
@@ -847,18 +993,25 @@ __global__ __launch_bounds__(kThreads, 3) void chunk_output_fast_kernel(
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) S[sl][nt] = zero4();
   f32x4 Z = zero4();
+  static_assert(kPacked || !kCompact, "only packed states are stored compactly");
   {
+    // the tile indices as scalars: the per-tile part of the places stays in scalar registers
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int n_stored = Stored<kPacked, GW>::floats(kCompact);
+    const int z_stored = Stored<kPacked, GW>::zoff(kCompact);
+    FragPlace<kPacked, GW, kCompact> fp[LY::kSlots];
+#pragma unroll
+    for (int sl = 0; sl < LY::kSlots; ++sl)
+      if (LY::owns(wu, sl)) fp[sl].init(LY::tile(wu, sl), lane);
     auto add_state = [&](int j) {
-      const float* pre = states + ((long long)(b * pr.H + h) * n_seg + j) * LY::kStateFloats;
+      const float* pre = states + ((long long)(b * pr.H + h) * n_seg + j) * n_stored;
 #pragma unroll
       for (int sl = 0; sl < LY::kSlots; ++sl) {
         if (!LY::owns(w, sl)) continue;
-        const int t = LY::tile(w, sl);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          S[sl][nt] += *reinterpret_cast<const f32x4*>(pre + ((t * 4 + nt) * 64 + lane) * 4);
+        for (int nt = 0; nt < 4; ++nt) fp[sl].add(pre, nt, S[sl][nt]);
       }
-      Z += *reinterpret_cast<const f32x4*>(pre + LY::kZOff + lane * 4);
+      Z += *reinterpret_cast<const f32x4*>(pre + z_stored + lane * 4);
     };
     const int j0 = sum_prefix ? 0 : seg, j1 = !states ? j0 : sum_prefix ? seg : seg + 1;
     int j = j0;
@@ -1131,8 +1284,12 @@ template <typename Tout, bool kPacked, int GW>
 void walk_launch(const DevProblem& pr, const SegGrid& sg, int L, int n_seg, dim3 grid,
                  hipStream_t st, const __bf16* q, const __bf16* k, const __bf16* v, void* o,
                  float* den, const float* states, int sum_prefix) {
-  launch_kernel(chunk_output_fast_kernel<Tout, kPacked, GW>, grid, kThreads, 0, st,
-      pr, sg, L, n_seg, q, k, v, (Tout*)o, den, states, sum_prefix);
+  if (kPacked && pr.stored_compact)
+    launch_kernel(chunk_output_fast_kernel<Tout, kPacked, GW, kPacked>, grid, kThreads, 0, st,
+        pr, sg, L, n_seg, q, k, v, (Tout*)o, den, states, sum_prefix);
+  else
+    launch_kernel(chunk_output_fast_kernel<Tout, kPacked, GW, false>, grid, kThreads, 0, st,
+        pr, sg, L, n_seg, q, k, v, (Tout*)o, den, states, sum_prefix);
 }
 
 template <typename Tout>

@@ -173,6 +173,7 @@ kata::DevProblem to_dev(const kata_problem* pr) {
   d.dv = pr->dv;
   d.C = pr->chunk;
   d.gs = pr->groups > 1 ? pr->p / pr->groups : pr->p;
+  d.stored_compact = 0;
   d.eps = pr->eps;
   for (int i = 0; i < 3; ++i) {
     d.sq[i] = pr->sq[i];
@@ -228,7 +229,8 @@ hipError_t run_scan(float* x, int64_t n_seq, int64_t n, int64_t elems, int exclu
 kata_status run_chunked(const kata_problem* pr, const kata::ChunkPlan& cp, const void* q,
                         const void* k, const void* v, void* o, float* den, void* workspace,
                         hipStream_t st) {
-  const kata::DevProblem dp = to_dev(pr);
+  kata::DevProblem dp = to_dev(pr);
+  dp.stored_compact = cp.compact;
   const bool in_bf16 = pr->in_dtype == KATA_BF16, out_bf16 = pr->out_dtype == KATA_BF16;
   float* states = reinterpret_cast<float*>(workspace);
   char* scan_ws = reinterpret_cast<char*>(workspace) + cp.states_bytes;

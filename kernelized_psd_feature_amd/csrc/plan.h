@@ -26,6 +26,7 @@ struct ChunkPlan {
   int n_chunks = 0;           // N_c = T / C per (b, h)
   int n_seg = 0;              // ceil(N_c / L)
   int walk_sums_prefix = 0;   // 1: each walk adds the earlier segments' states itself, no scan
+  int compact = 0;            // 1: packed p = 16 states stored without their zero rows (scan)
   // 1: p = 32 KATA-Mg (g >= 2) as two p = 16 passes over the coordinate halves (every other
   // field then describes one pass); the workspace adds the passes' fp32 outputs and D_t
   int halves = 0;

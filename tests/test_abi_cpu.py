@@ -150,8 +150,9 @@ def test_workspace_size_of_invalid_problem_is_zero():
 
 
 def test_packed_state_workspace_holds_the_unique_rows():
-    # packed states: 10 tiles of 16 x 64 (136 unique rows + 24 zero rows) + the 16 x 16 Z,
-    # against 256 x 64 + 256 for the direct layout; same segmentation for both
+    # packed states: the 136 unique rows x 64 (the 24 zero rows of the 10 tiles are not
+    # stored) + the 16 x 16 Z, against 256 x 64 + 256 for the direct layout; same
+    # segmentation for both
     lib = _lib()
     for T in (1024, 131072):
         d = _problem(B=1, H=16, T=T)
@@ -162,7 +163,7 @@ def test_packed_state_workspace_holds_the_unique_rows():
         assert 0 < npk < nd
         n_states = 16 * (T // 64) if T == 1024 else None
         if n_states:   # one segment per chunk when the chunks do not fill the GPU
-            assert npk >= n_states * (160 * 64 + 256) * 4
+            assert npk >= n_states * (136 * 64 + 256) * 4
             assert nd >= n_states * 16640 * 4
     # a packed request on a problem the MFMA kernels do not take sizes as direct
     f = _problem(B=1, H=2, T=256, p=8, dv=16, chunk=32, in_dt=0)
@@ -314,7 +315,7 @@ def test_chunked_plan_reports_segments_and_scan_depth():
     assert (out.n_chunks, out.mfma, out.packed) == (2048, 1, 1)
     assert out.segments == -(-2048 // out.chunks_per_segment) and 1 < out.segments < 2048
     assert out.scan_levels == math.ceil(math.log2(out.segments)) and out.walk_sums_prefix == 0
-    assert out.state_floats == (10 * 16 * 64 + 256)       # 10 packed tiles of 16 x 64, + Z
+    assert out.state_floats == (136 * 64 + 256)           # the 136 unique (i, j) rows x 64, + Z
     # 512 sequences fill two thirds of the GPU's 768 workgroup slots: one segment each, no
     # state pass, no scan; 256 sequences take 3 segments each (768 walks), and with at most 8
     # segments the walks add the earlier segments' states themselves: no scan either
