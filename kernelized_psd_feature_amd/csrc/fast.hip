@@ -250,8 +250,10 @@ __device__ __forceinline__ void score_tile(const s16x4& kf, const s16x4& qf, int
 //           waves 0-1 own 3 and waves 2-3 (more intra-chunk work) own 2.
 //   KATA-Mg (packed, groups of GW = 8 or 4 consecutive coordinates): only the double groups
 //           inside one group exist, 6 or 4 tiles.
-// State layout in the workspace (floats): tile t, value tile nt, lane -> ((t*4 + nt)*64 +
-// lane)*4 .. +3 (the accumulator registers as they are), then Z as one 16 x 16 tile.
+// Fragment layout of a state (floats): tile t, value tile nt, lane -> ((t*4 + nt)*64 +
+// lane)*4 .. +3 (the accumulator registers as they are), then Z as one 16 x 16 tile; the
+// workspace holds it as it is or, for packed states through the scan, without the zero rows
+// (Stored, below).
 // ==========================================================================================
 template <bool kPacked, int GW = P>
 struct Layout {
