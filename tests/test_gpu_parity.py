@@ -964,14 +964,23 @@ def test_mg_mfma_layer340m_full_size(g):
         assert worst <= TOL[w.dtype]
 
 
+# seg_chunks 1 and 3 give more than 8 segments per sequence: the states go through the scan,
+# stored without the zero rows of the grouped tiles; 32: one segment, no states
+@pytest.mark.parametrize("g", [2, 4])
 @pytest.mark.parametrize("seg", [1, 3, 32])
-def test_mg_mfma_segment_lengths_and_den(seg):
+def test_mg_mfma_segment_lengths_and_den(seg, g):
     w = W.WORKLOADS[2]
     q, k, v = W.make_inputs(w, 53, T=2048, B=1, H=2)
-    ref, dref = O.closed_form(_np(q), _np(k), _np(v), groups=2)
-    o, d = K.fwd_chunked(*_to_gpu(q, k, v), seg_chunks=seg, groups=2, return_den=True)
+    ref, dref = O.closed_form(_np(q), _np(k), _np(v), groups=g)
+    qg, kg, vg = _to_gpu(q, k, v)
+    plan = K.chunked_plan(qg, kg, vg, seg_chunks=seg, groups=g)
+    if seg < 32:
+        # the unique within-group pairs' rows: 16 (16 / g + 1) / 2 of them, x 64, + Z
+        assert plan["scan_levels"] > 0
+        assert plan["state_floats"] == 16 * (16 // g + 1) // 2 * 64 + 256
+    o, d = K.fwd_chunked(qg, kg, vg, seg_chunks=seg, groups=g, return_den=True)
     err = float((o.cpu().double() - torch.from_numpy(ref)).abs().max())
-    say(f"KATA-Mg MFMA seg_chunks={seg}: max-abs {err:.3e}")
+    say(f"KATA-Mg MFMA g={g} seg_chunks={seg}: max-abs {err:.3e}")
     assert err <= TOL[w.dtype]
     np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=1e-2)
 
