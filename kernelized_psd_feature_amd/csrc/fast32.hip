@@ -74,6 +74,41 @@ __device__ __forceinline__ int ztile_of(int w) { return w < 4 ? -1 : w - 4; }
 __device__ __forceinline__ int tgroup_of(int w) { return w < 4 ? w : 7 - w; }
 static_assert(2 * (8 * kFull + 2) == kTiles, "pairs: kFull per wave and two split pairs");
 
+// Order of the 72 double groups (a, J), each the 8 state rows of the features i in {a, a + 1}
+// and j = 4 J + r (r = 0..3), a even and a <= 4 J + 2 (the pairs i <= j, with the zero rows of
+// the diagonal blocks).  K step kk holds groups 4 kk + g (g = lane / 16).  A
+// plain step takes a = a0 + 2 g of one column block J0, so the readout's q loads of every lane
+// group sit at one lane offset plus a constant; column blocks 0, 2, 4 and 6 have 2 J + 2 = 2
+// mod 4 groups, and their first two (a = 0, 2) pair up in two split steps: lane groups 0, 1
+// take block J0 and lane groups 2, 3 block J0 + 2.  Consecutive steps of one column block
+// share their j values.
+struct Step32 {
+  int split, a0, J0;
+};
+__host__ __device__ constexpr Step32 step32(int kk) {
+  constexpr int a0[kSteps] = {0, 0, 4, 0, 8, 0, 4, 12, 0, 8, 16, 4, 12, 20, 0, 8, 16, 24};
+  constexpr int J0[kSteps] = {0, 1, 2, 3, 3, 4, 4, 4, 5, 5, 5, 6, 6, 6, 7, 7, 7, 7};
+  return Step32{kk == 0 || kk == 5 ? 1 : 0, a0[kk], J0[kk]};
+}
+__host__ __device__ constexpr void octet32(int idx, int& a, int& J) {
+  const Step32 s = step32(idx >> 2);
+  const int g = idx & 3;
+  a = s.split ? s.a0 + 2 * (g & 1) : s.a0 + 2 * g;
+  J = s.split ? s.J0 + 2 * (g >> 1) : s.J0;
+}
+// every (a, J) with a even, a <= 4 J + 2 exactly once
+constexpr bool octets32_cover() {
+  int seen[8][16] = {};
+  for (int idx = 0; idx < 4 * kSteps; ++idx) {
+    int a = 0, J = 0;
+    octet32(idx, a, J);
+    if (J < 0 || J > 7 || a < 0 || (a & 1) || a > 4 * J + 2) return false;
+    if (seen[J][a >> 1]++) return false;
+  }
+  return true;
+}
+static_assert(octets32_cover(), "p = 32 double-group order");
+
 // One thread's share of a chunk's loads: 8 bytes (features 4 pc .. 4 pc + 3) of the q row
 // and of the k row of token stage_row, and 16 bytes of one v row (row tid / 8, columns
 // 8 (tid % 8) ..).  Wave w stages tokens 8 w .. 8 w + 7; lanes 0-31 hold features 0-15 and
@@ -193,7 +228,7 @@ struct Rows32 {
     for (int ps = 0; ps <= kFull; ++ps) {
       const int P = ps < kFull ? pair_of(w, ps) : 16 + (e >= 0 ? e >> 1 : 0), row = lane & 15;
       int a, J;
-      double_group(4 * P + (row >> 2), a, J);
+      octet32(4 * P + (row >> 2), a, J);
       const int j = 4 * J + (row & 3);
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
@@ -406,8 +441,33 @@ struct __align__(16) Walk32Lds {
   float zx[kWaves][64];           // q^T Z q halves handed to the other wave of a token group
   float inv[kWaves][16];          // per wave: 1 / D_t of its token group's 16 tokens
   uint32_t vbad[kWaves];          // per wave: its staged v row pieces hold a non-finite value
-  unsigned char dg[4 * kSteps][2];   // double group -> (a, J)
 };
+
+// Readout phi(q_t)^T S_{<c} over the K steps [9 CH, 9 CH + 9) for all four value tiles.  qa and
+// qj point into this lane's q row at the lane offsets of plain (0) and split (1) steps, so each
+// step's loads take constant offsets from them.
+template <int CH>
+__device__ __forceinline__ void readout32(const uint4 (*Sb)[4][64], const __bf16* const (&qa)[2],
+                                          const __bf16* const (&qj)[2], int lane,
+                                          f32x4 (&R)[4]) {
+#pragma unroll
+  for (int s = 0; s < kSteps / 2; ++s) {
+    const int kk = (kSteps / 2) * CH + s;
+    const Step32 st = step32(kk);
+    const uint32_t qi = *reinterpret_cast<const uint32_t*>(qa[st.split] + st.a0);
+    const uint2 qjv = *reinterpret_cast<const uint2*>(qj[st.split] + 4 * st.J0);
+    const float i0 = bf_lo(qi), i1 = bf_hi(qi);
+    const float jv[4] = {bf_lo(qjv.x), bf_hi(qjv.x), bf_lo(qjv.y), bf_hi(qjv.y)};
+    bf16x8 a;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      a[r] = (__bf16)(i0 * jv[r]);
+      a[4 + r] = (__bf16)(i1 * jv[r]);
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) R[n] = mfma32(a, __builtin_bit_cast(bf16x8, Sb[kk][n][lane]), R[n]);
+  }
+}
 
 template <typename Tout>
 __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
@@ -445,12 +505,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
   Rows32 rw;
   rw.init(w, e, lane);
   zero_row(tl, tid);
-  if (tid < 4 * kSteps) {
-    int a, J;
-    double_group(tid, a, J);
-    sm.dg[tid][0] = (unsigned char)a;
-    sm.dg[tid][1] = (unsigned char)(4 * J);
-  }
 
   // a pair's two accumulators -> one B-operand word of its K step (tile 2 P in the low half)
   auto bword = [](const f32x4& lo, const f32x4& hi) {
@@ -498,6 +552,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
   __syncthreads();
 
   const int t = 16 * tg + l16;                 // this lane's token (fragment column / row)
+  const __bf16* const qa[2] = {&tl.Qs[t][2 * g], &tl.Qs[t][2 * (g & 1)]};
+  const __bf16* const qj[2] = {&tl.Qs[t][0], &tl.Qs[t][8 * (g >> 1)]};
   Tout* orow = o + row_off(pr.so, b, c0 * C + 16 * tg + 8 * (lane >> 5), h) + 32 * ch + (lane & 31);
   const long long so_t = pr.so[1];
 
@@ -584,23 +640,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
 
     // ---- readout phi(q_t)^T S_{<c}: K steps [9 ch, 9 ch + 9) for all four value tiles ----
     f32x4 R[4] = {zero4(), zero4(), zero4(), zero4()};
-#pragma unroll 3
-    for (int kk = (kSteps / 2) * ch; kk < (kSteps / 2) * (ch + 1); ++kk) {
-      const int ga = sm.dg[4 * kk + g][0], gj = sm.dg[4 * kk + g][1];
-      const uint32_t qa = *reinterpret_cast<const uint32_t*>(&tl.Qs[t][ga]);
-      const uint2 qj = *reinterpret_cast<const uint2*>(&tl.Qs[t][gj]);
-      const float i0 = bf_lo(qa), i1 = bf_hi(qa);
-      const float jv[4] = {bf_lo(qj.x), bf_hi(qj.x), bf_lo(qj.y), bf_hi(qj.y)};
-      bf16x8 a;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        a[r] = (__bf16)(i0 * jv[r]);
-        a[4 + r] = (__bf16)(i1 * jv[r]);
-      }
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-        R[n] = mfma32(a, __builtin_bit_cast(bf16x8, sm.Sb[kk][n][lane]), R[n]);
-    }
+    if (ch)
+      readout32<1>(sm.Sb, qa, qj, lane, R);
+    else
+      readout32<0>(sm.Sb, qa, qj, lane, R);
     // the other wave of the token group (7 - w) owns the other two value tiles (selects, not
     // a runtime index, keep R in registers); it reads them after the update's barrier
 #pragma unroll
