@@ -8,13 +8,13 @@
 // lo on MFMA).
 //
 // The state is always packed (the 528 unique pairs i <= j of the 32 x 32 feature, the ai.info
-// state-size bullet's packed coordinates): 72 double groups = 36 tiles of 16 rows, 18 readout
-// K steps.  That is 147 KB of fp32 per state, too much for four waves' registers, so a
-// workgroup has eight waves (two per SIMD, one workgroup per CU; waves w and w + 4 share a
-// SIMD):
+// state-size bullet's packed coordinates): 66 octets of 8 rows and two zero octets = 34 tiles of
+// 16 rows, 17 readout K steps.  That is 140 KB of fp32 per state, too much for four waves'
+// registers, so a workgroup has eight waves (two per SIMD, one workgroup per CU; waves w and
+// w + 4 share a SIMD):
 //   state tiles  the tiles go in K-step pairs (2 P, 2 P + 1).  Wave w owns pairs w and w + 8
-//                with all four value tiles; the last two pairs are split by value-tile halves
-//                over waves 0-3, and the four Z tiles go to waves 4-7 (one of each per SIMD).
+//                with all four value tiles; the last pair is split by value tiles over waves
+//                0-3, and the four Z tiles go to waves 4-7 (one of each per SIMD).
 //                The two tiles of a pair share their j factor rows, which the update reads
 //                once, and their accumulators make whole B-operand words of the readout, which
 //                the publish writes at once,
@@ -34,10 +34,11 @@ namespace {
 
 constexpr int P = 32, DV = 64, C = 64;
 constexpr int kWaves = 8, kThreads = 64 * kWaves;
-constexpr int kTiles = 36, kSteps = 18, kFull = 2;   // kFull: whole pairs per wave
-constexpr int kZOff = kTiles * 16 * DV;              // 36864
+constexpr int kTiles = 34, kSteps = 17, kFull = 2;   // kFull: whole pairs per wave
+constexpr int kSteps0 = (kSteps + 1) / 2;            // readout K steps of the waves with ch = 0
+constexpr int kZOff = kTiles * 16 * DV;              // 34816
 constexpr int kStateFloats = kZOff + 4 * 256;        // + Z as 2 x 2 tiles of 16 x 16
-static_assert(kStateFloats == 36 * 16 * 64 + 4 * 256, "packed p = 32 state size (plan.h)");
+static_assert(kStateFloats == 34 * 16 * 64 + 4 * 256, "packed p = 32 state size (plan.h)");
 constexpr int QROW = 40;                             // bf16 per q / k row: 80 B
 constexpr int KTROW = 68;                            // fp32 per K^T row
 constexpr int VROW = 80;                             // bf16 per v row: 160 B
@@ -65,49 +66,97 @@ struct __align__(16) StateTiles32 {                  // the state pass needs no 
   __bf16 V[C][VROW];
 };
 
-// Tile ownership (see the file comment): whole pair ps < kFull of wave w, the half-pair of
-// extra index e (pair 16 + e / 2, value tiles 2 (e % 2) + {0, 1}) and the Z tile index.
+// Tile ownership (see the file comment): whole pair ps < kFull of wave w, the value tile e of
+// the last pair (e >= 0 on waves 0-3) and the Z tile index.
 __device__ __forceinline__ int pair_of(int w, int ps) { return w + 8 * ps; }
 __device__ __forceinline__ int extra_of(int w) { return w < 4 ? w : -1; }
 __device__ __forceinline__ int ztile_of(int w) { return w < 4 ? -1 : w - 4; }
 // token group of wave w (see the file comment); its partner wave is 7 - w
 __device__ __forceinline__ int tgroup_of(int w) { return w < 4 ? w : 7 - w; }
-static_assert(2 * (8 * kFull + 2) == kTiles, "pairs: kFull per wave and two split pairs");
+static_assert(2 * (8 * kFull + 1) == kTiles, "pairs: kFull per wave and one split pair");
 
-// Order of the 72 double groups (a, J), each the 8 state rows of the features i in {a, a + 1}
-// and j = 4 J + r (r = 0..3), a even and a <= 4 J + 2 (the pairs i <= j, with the zero rows of
-// the diagonal blocks).  K step kk holds groups 4 kk + g (g = lane / 16).  A
-// plain step takes a = a0 + 2 g of one column block J0, so the readout's q loads of every lane
-// group sit at one lane offset plus a constant; column blocks 0, 2, 4 and 6 have 2 J + 2 = 2
-// mod 4 groups, and their first two (a = 0, 2) pair up in two split steps: lane groups 0, 1
-// take block J0 and lane groups 2, 3 block J0 + 2.  Consecutive steps of one column block
-// share their j values.
+// Row order of the packed state.  K step kk covers tiles 2 kk and 2 kk + 1; its octet g (the
+// readout's lane group g = lane / 16) is rows 4 g + r of both tiles, r = 0..3, the readout's
+// K slots r and 4 + r of the lane.  The two rows of a slot pair share their second feature
+// j(r), so the update reads one j factor row for both.  Octet kinds (x = the features
+// 4 J .. 4 J + 3 of column block J):
+//   R (a, J)  off the diagonal blocks, a even, a + 1 < 4 J: rows (a, 4 J + r), (a + 1, 4 J + r),
+//   D J       the diagonal block J: rows (x_r, x_r) and (x_{3, 2, 3, 1 [r]}, x_r),
+//   L B       the pairs (x_1, x_0) and (x_2, x_0) of block B + r, the two that D J leaves out,
+//   zero      two octets of zero rows (528 = 66 x 8 pairs, 17 K steps hold 68 octets).
+// Steps: plain R (a = a0 + 2 g, J = J0); split R (lane groups 0, 1: a = a0 + 2 g in block J0,
+// lane groups 2, 3: a = a0 + 2 (g - 2) in block J0 + 2; the column blocks J = 1, 3, 5, 7 have
+// 2 J = 2 mod 4 octets R); D (J = J0 + g); and the last step, L (B = 4 g) in lane groups 0, 1
+// and zero octets in lane groups 2, 3.  Every lane group of a step reads its q values at one
+// lane offset plus a constant, and consecutive R steps of one column block share their j.
+enum { kPlainR = 0, kSplitR = 1, kDiag = 2, kLeft = 3 };
 struct Step32 {
-  int split, a0, J0;
+  int kind, a0, J0;
 };
+// 3-bit fields per step (low step first): J0 and a0 / 4; shifts, not a table in memory, so a
+// runtime kk (the update's row set-up) costs no private memory
+constexpr uint64_t pack3(const int (&f)[kSteps], int div) {
+  uint64_t x = 0;
+  for (int i = kSteps - 1; i >= 0; --i) x = (x << 3) | uint64_t(f[i] / div);
+  return x;
+}
+constexpr int kStepJ0[kSteps] = {1, 2, 3, 4, 4, 5, 5, 5, 6, 6, 6, 7, 7, 7, 0, 4, 0};
+constexpr int kStepA0[kSteps] = {0, 0, 4, 0, 8, 0, 4, 12, 0, 8, 16, 4, 12, 20, 0, 0, 0};
+constexpr uint64_t kJ0Bits = pack3(kStepJ0, 1), kA0Bits = pack3(kStepA0, 4);
 __host__ __device__ constexpr Step32 step32(int kk) {
-  constexpr int a0[kSteps] = {0, 0, 4, 0, 8, 0, 4, 12, 0, 8, 16, 4, 12, 20, 0, 8, 16, 24};
-  constexpr int J0[kSteps] = {0, 1, 2, 3, 3, 4, 4, 4, 5, 5, 5, 6, 6, 6, 7, 7, 7, 7};
-  return Step32{kk == 0 || kk == 5 ? 1 : 0, a0[kk], J0[kk]};
+  const int kind = kk == 0 || kk == 5 ? kSplitR : kk == 14 || kk == 15 ? kDiag
+                 : kk == 16 ? kLeft : kPlainR;
+  return Step32{kind, 4 * int((kA0Bits >> (3 * kk)) & 7), int((kJ0Bits >> (3 * kk)) & 7)};
 }
-__host__ __device__ constexpr void octet32(int idx, int& a, int& J) {
-  const Step32 s = step32(idx >> 2);
-  const int g = idx & 3;
-  a = s.split ? s.a0 + 2 * (g & 1) : s.a0 + 2 * g;
-  J = s.split ? s.J0 + 2 * (g >> 1) : s.J0;
-}
-// every (a, J) with a even, a <= 4 J + 2 exactly once
-constexpr bool octets32_cover() {
-  int seen[8][16] = {};
-  for (int idx = 0; idx < 4 * kSteps; ++idx) {
-    int a = 0, J = 0;
-    octet32(idx, a, J);
-    if (J < 0 || J > 7 || a < 0 || (a & 1) || a > 4 * J + 2) return false;
-    if (seen[J][a >> 1]++) return false;
+// second feature of D J's rows 4 + r (the first rows are the squares)
+__host__ __device__ constexpr int diag_i(int r) { return r == 1 ? 2 : r == 3 ? 1 : 3; }
+// Features (i, j) of row 4 g + r of tile 2 kk + tp; i < 0 for a zero row.
+__host__ __device__ constexpr void row32(int kk, int g, int r, int tp, int& i, int& j) {
+  const Step32 s = step32(kk);
+  if (s.kind == kPlainR || s.kind == kSplitR) {
+    const int a = s.kind == kSplitR ? s.a0 + 2 * (g & 1) : s.a0 + 2 * g;
+    const int J = s.kind == kSplitR ? s.J0 + 2 * (g >> 1) : s.J0;
+    i = a + tp;
+    j = 4 * J + r;
+  } else if (s.kind == kDiag) {
+    const int x = 4 * (s.J0 + g);
+    i = tp ? x + diag_i(r) : x + r;
+    j = x + r;
+  } else if (g < 2) {
+    const int x = 4 * (4 * g + r);
+    i = x + 1 + tp;
+    j = x;
+  } else {
+    i = -1;
+    j = 0;
   }
-  return true;
 }
-static_assert(octets32_cover(), "p = 32 double-group order");
+// every unordered pair of the 32 features exactly once, 16 zero rows, and one j per slot pair
+constexpr bool rows32_cover() {
+  int seen[32][32] = {};
+  int zeros = 0;
+  for (int kk = 0; kk < kSteps; ++kk)
+    for (int g = 0; g < 4; ++g)
+      for (int r = 0; r < 4; ++r) {
+        int j0 = 0;
+        for (int tp = 0; tp < 2; ++tp) {
+          int i = 0, j = 0;
+          row32(kk, g, r, tp, i, j);
+          if (tp == 0) j0 = j;
+          if (i < 0) {
+            ++zeros;
+            continue;
+          }
+          if (i > 31 || j < 0 || j > 31 || j != j0) return false;
+          if (seen[i < j ? i : j][i < j ? j : i]++) return false;
+        }
+      }
+  for (int i = 0; i < 32; ++i)
+    for (int j = i; j < 32; ++j)
+      if (seen[i][j] != 1) return false;
+  return zeros == 16;
+}
+static_assert(rows32_cover(), "p = 32 packed row order");
 
 // One thread's share of a chunk's loads: 8 bytes (features 4 pc .. 4 pc + 3) of the q row
 // and of the k row of token stage_row, and 16 bytes of one v row (row tid / 8, columns
@@ -226,14 +275,13 @@ struct Rows32 {
   __device__ void init(int w, int e, int lane) {
 #pragma unroll
     for (int ps = 0; ps <= kFull; ++ps) {
-      const int P = ps < kFull ? pair_of(w, ps) : 16 + (e >= 0 ? e >> 1 : 0), row = lane & 15;
-      int a, J;
-      octet32(4 * P + (row >> 2), a, J);
-      const int j = 4 * J + (row & 3);
+      const int P = ps < kFull ? pair_of(w, ps) : 16, row = lane & 15;
+      int j = 0;
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
-        const int i = a + tp;
-        irow[ps][tp] = i > j ? KT_Z0 + 1 - (i & 1) : (i == j ? kt_row(i) : KT_D + kt_row(i));
+        int i = 0;
+        row32(P, row >> 2, row & 3, tp, i, j);       // j is the same for both tiles
+        irow[ps][tp] = i < 0 ? KT_Z0 + (row & 1) : (i == j ? kt_row(i) : KT_D + kt_row(i));
       }
       jrow[ps] = kt_row(j);
     }
@@ -241,10 +289,10 @@ struct Rows32 {
 };
 
 // The accumulators of one wave's share of S: S[ps][tp][nt] for tile 2 pair_of(w, ps) + tp and
-// value tile nt; Sx[tp][n] for tile 32 + 2 (e / 2) + tp and value tile 2 (e % 2) + n.
+// value tile nt; Sx[tp] for tile 32 + tp and value tile e.
 struct Acc32 {
   f32x4 S[kFull][2][4];
-  f32x4 Sx[2][2];
+  f32x4 Sx[2];
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int ps = 0; ps < kFull; ++ps)
@@ -253,9 +301,7 @@ struct Acc32 {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) S[ps][tp][nt] = zero4();
 #pragma unroll
-    for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-      for (int n = 0; n < 2; ++n) Sx[tp][n] = zero4();
+    for (int tp = 0; tp < 2; ++tp) Sx[tp] = zero4();
   }
   // f(accumulator, state float offset of its fragment) for every owned fragment
   template <class F>
@@ -269,10 +315,7 @@ struct Acc32 {
           f(S[ps][tp][nt], (((2 * pair_of(w, ps) + tp) * 4 + nt) * 64 + lane) * 4);
     if (e >= 0) {
 #pragma unroll
-      for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-          f(Sx[tp][n], (((2 * (16 + (e >> 1)) + tp) * 4 + 2 * (e & 1) + n) * 64 + lane) * 4);
+      for (int tp = 0; tp < 2; ++tp) f(Sx[tp], (((32 + tp) * 4 + e) * 64 + lane) * 4);
     }
   }
 };
@@ -300,17 +343,9 @@ __device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, Acc32& 
     if (e >= 0) {
       bf16x8 a[2];
       phik2(tl, rw.irow[kFull], rw.jrow[kFull], m, lane, a);
-      if (e & 1) {
+      const bf16x8 ve = v_frag(tl.V, m, e, lane);   // value tile e, a wave-uniform offset
 #pragma unroll
-        for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-          for (int n = 0; n < 2; ++n) acc.Sx[tp][n] = mfma32(a[tp], vb[2 + n], acc.Sx[tp][n]);
-      } else {
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-          for (int n = 0; n < 2; ++n) acc.Sx[tp][n] = mfma32(a[tp], vb[n], acc.Sx[tp][n]);
-      }
+      for (int tp = 0; tp < 2; ++tp) acc.Sx[tp] = mfma32(a[tp], ve, acc.Sx[tp]);
     }
     if (z >= 0) {
       const int mi = z >> 1, kj = z & 1;
@@ -443,27 +478,54 @@ struct __align__(16) Walk32Lds {
   uint32_t vbad[kWaves];          // per wave: its staged v row pieces hold a non-finite value
 };
 
-// Readout phi(q_t)^T S_{<c} over the K steps [9 CH, 9 CH + 9) for all four value tiles.  qa and
-// qj point into this lane's q row at the lane offsets of plain (0) and split (1) steps, so each
-// step's loads take constant offsets from them.
+// Readout phi(q_t)^T S_{<c} over the K steps [kSteps0 CH, ..) of the waves with ch = CH, for all
+// four value tiles.  qa, qj, qd and ql point into this lane's q row at the lane offsets of the
+// step kinds (R plain / split: the i pair and the j quad; D: the block; L: the four blocks),
+// so each step's loads take constant offsets from them.
 template <int CH>
 __device__ __forceinline__ void readout32(const uint4 (*Sb)[4][64], const __bf16* const (&qa)[2],
-                                          const __bf16* const (&qj)[2], int lane,
-                                          f32x4 (&R)[4]) {
+                                          const __bf16* const (&qj)[2], const __bf16* qd,
+                                          const __bf16* ql, int lane, f32x4 (&R)[4]) {
+  constexpr int k0 = CH ? kSteps0 : 0, k1 = CH ? kSteps : kSteps0;
 #pragma unroll
-  for (int s = 0; s < kSteps / 2; ++s) {
-    const int kk = (kSteps / 2) * CH + s;
+  for (int kk = k0; kk < k1; ++kk) {
     const Step32 st = step32(kk);
-    const uint32_t qi = *reinterpret_cast<const uint32_t*>(qa[st.split] + st.a0);
-    const uint2 qjv = *reinterpret_cast<const uint2*>(qj[st.split] + 4 * st.J0);
-    const float i0 = bf_lo(qi), i1 = bf_hi(qi);
-    const float jv[4] = {bf_lo(qjv.x), bf_hi(qjv.x), bf_lo(qjv.y), bf_hi(qjv.y)};
+    float x[8], y[8];                 // slot s of the A operand is x[s] * y[s]
+    if (st.kind == kPlainR || st.kind == kSplitR) {
+      const uint32_t qi = *reinterpret_cast<const uint32_t*>(qa[st.kind] + st.a0);
+      const uint2 qv = *reinterpret_cast<const uint2*>(qj[st.kind] + 4 * st.J0);
+      const float jv[4] = {bf_lo(qv.x), bf_hi(qv.x), bf_lo(qv.y), bf_hi(qv.y)};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[r] = bf_lo(qi);
+        x[4 + r] = bf_hi(qi);
+        y[r] = y[4 + r] = jv[r];
+      }
+    } else if (st.kind == kDiag) {
+      const uint2 qv = *reinterpret_cast<const uint2*>(qd + 4 * st.J0);
+      const float xv[4] = {bf_lo(qv.x), bf_hi(qv.x), bf_lo(qv.y), bf_hi(qv.y)};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[r] = xv[r];
+        x[4 + r] = xv[diag_i(r)];
+        y[r] = y[4 + r] = xv[r];
+      }
+    } else {
+      // blocks 4 (g & 1) + r: x_0, x_1 in the low word of the block, x_2 in the high one
+      const uint4 u0 = *reinterpret_cast<const uint4*>(ql);
+      const uint4 u1 = *reinterpret_cast<const uint4*>(ql + 8);
+      const uint32_t w01[4] = {u0.x, u0.z, u1.x, u1.z}, w23[4] = {u0.y, u0.w, u1.y, u1.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x0 = bf_lo(w01[r]);
+        x[r] = bf_hi(w01[r]);
+        x[4 + r] = bf_lo(w23[r]);
+        y[r] = y[4 + r] = x0;
+      }
+    }
     bf16x8 a;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      a[r] = (__bf16)(i0 * jv[r]);
-      a[4 + r] = (__bf16)(i1 * jv[r]);
-    }
+    for (int sl = 0; sl < 8; ++sl) a[sl] = (__bf16)(x[sl] * y[sl]);
 #pragma unroll
     for (int n = 0; n < 4; ++n) R[n] = mfma32(a, __builtin_bit_cast(bf16x8, Sb[kk][n][lane]), R[n]);
   }
@@ -517,11 +579,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
         sm.Sb[pair_of(w, ps)][nt][lane] = bword(acc.S[ps][0][nt], acc.S[ps][1][nt]);
-    if (e >= 0) {
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-        sm.Sb[16 + (e >> 1)][2 * (e & 1) + n][lane] = bword(acc.Sx[0][n], acc.Sx[1][n]);
-    }
+    if (e >= 0) sm.Sb[16][e][lane] = bword(acc.Sx[0], acc.Sx[1]);
     if (zt >= 0) {
       const f32x4 zr = Zt;
       s16x4 zhi, zlo;
@@ -554,6 +612,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
   const int t = 16 * tg + l16;                 // this lane's token (fragment column / row)
   const __bf16* const qa[2] = {&tl.Qs[t][2 * g], &tl.Qs[t][2 * (g & 1)]};
   const __bf16* const qj[2] = {&tl.Qs[t][0], &tl.Qs[t][8 * (g >> 1)]};
+  const __bf16* const qd = &tl.Qs[t][4 * g];
+  const __bf16* const ql = &tl.Qs[t][16 * (g & 1)];
   Tout* orow = o + row_off(pr.so, b, c0 * C + 16 * tg + 8 * (lane >> 5), h) + 32 * ch + (lane & 31);
   const long long so_t = pr.so[1];
 
@@ -638,12 +698,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     zq = sum_xor32(sum_xor16(zq));
     sm.zx[w][lane] = zq;
 
-    // ---- readout phi(q_t)^T S_{<c}: K steps [9 ch, 9 ch + 9) for all four value tiles ----
+    // ---- readout phi(q_t)^T S_{<c}: the first kSteps0 K steps (ch = 0) or the rest (ch = 1) ----
     f32x4 R[4] = {zero4(), zero4(), zero4(), zero4()};
     if (ch)
-      readout32<1>(sm.Sb, qa, qj, lane, R);
+      readout32<1>(sm.Sb, qa, qj, qd, ql, lane, R);
     else
-      readout32<0>(sm.Sb, qa, qj, lane, R);
+      readout32<0>(sm.Sb, qa, qj, qd, ql, lane, R);
     // the other wave of the token group (7 - w) owns the other two value tiles (selects, not
     // a runtime index, keep R in registers); it reads them after the update's barrier
 #pragma unroll

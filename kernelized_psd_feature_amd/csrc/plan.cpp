@@ -247,7 +247,7 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
     cp.packed = (pr->state_layout == KATA_STATE_PACKED || cp.fast32 || g > 1) ? 1 : 0;
     // packed: 10 tiles of 16 rows (the 136 unique (i, j) rows and 24 zero rows) x 64 columns,
     // plus the full 16 x 16 Z; KATA-Mg at p = 16: 6 tiles (g = 2) or 4 (g = 4), the
-    // within-group pairs only; p = 32: 36 tiles (528 unique rows and 48 zero rows) and Z.
+    // within-group pairs only; p = 32: 34 tiles (528 unique rows and 16 zero rows) and Z.
     // Through the scan the p = 16 states are stored without their zero rows (below).
     if (cp.packed) {
       const int tiles16 = g == 1 ? 10 : g == 2 ? 6 : 4;

@@ -79,8 +79,8 @@ ScanPlan plan_scan(int64_t n_seq, int64_t n, int64_t elems);
 // pr must have passed validate_problem; fast_available: the MFMA chunked kernels are built.
 ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available);
 
-// Floats in one packed p = 32 segment state (36 tiles of 16 x 64 plus Z as four 16 x 16 tiles).
-constexpr int64_t kState32Floats = 36 * 16 * 64 + 4 * 256;
+// Floats in one packed p = 32 segment state (34 tiles of 16 x 64 plus Z as four 16 x 16 tiles).
+constexpr int64_t kState32Floats = 34 * 16 * 64 + 4 * 256;
 size_t bwd_workspace_bytes(const kata_problem* pr);
 
 }  // namespace kata
