@@ -482,53 +482,100 @@ struct __align__(16) Walk32Lds {
 // four value tiles.  qa, qj, qd and ql point into this lane's q row at the lane offsets of the
 // step kinds (R plain / split: the i pair and the j quad; D: the block; L: the four blocks),
 // so each step's loads take constant offsets from them.
+// One readout K step's LDS operands: this lane's q words (the fields its step kind uses) and
+// the four B-operand words of the state.
+struct RdOps32 {
+  uint32_t qi;
+  uint2 qv;
+  uint4 u0, u1;
+  uint4 sb[4];
+};
+template <int KK>
+__device__ __forceinline__ void rd_load32(RdOps32& o, const uint4 (*Sb)[4][64],
+                                          const __bf16* const (&qa)[2], const __bf16* const (&qj)[2],
+                                          const __bf16* qd, const __bf16* ql, int lane) {
+  constexpr Step32 st = step32(KK);
+  if constexpr (st.kind == kPlainR || st.kind == kSplitR) {
+    o.qi = *reinterpret_cast<const uint32_t*>(qa[st.kind] + st.a0);
+    o.qv = *reinterpret_cast<const uint2*>(qj[st.kind] + 4 * st.J0);
+  } else if constexpr (st.kind == kDiag) {
+    o.qv = *reinterpret_cast<const uint2*>(qd + 4 * st.J0);
+  } else {
+    o.u0 = *reinterpret_cast<const uint4*>(ql);
+    o.u1 = *reinterpret_cast<const uint4*>(ql + 8);
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n) o.sb[n] = Sb[KK][n][lane];
+}
+template <int KK>
+__device__ __forceinline__ void rd_step32(const RdOps32& o, f32x4 (&R)[4]) {
+  constexpr Step32 st = step32(KK);
+  float x[8], y[8];                   // slot s of the A operand is x[s] * y[s]
+  if constexpr (st.kind == kPlainR || st.kind == kSplitR) {
+    const float jv[4] = {bf_lo(o.qv.x), bf_hi(o.qv.x), bf_lo(o.qv.y), bf_hi(o.qv.y)};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r] = bf_lo(o.qi);
+      x[4 + r] = bf_hi(o.qi);
+      y[r] = y[4 + r] = jv[r];
+    }
+  } else if constexpr (st.kind == kDiag) {
+    const float xv[4] = {bf_lo(o.qv.x), bf_hi(o.qv.x), bf_lo(o.qv.y), bf_hi(o.qv.y)};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r] = xv[r];
+      x[4 + r] = xv[diag_i(r)];
+      y[r] = y[4 + r] = xv[r];
+    }
+  } else {
+    // blocks 4 (g & 1) + r: x_0, x_1 in the low word of the block, x_2 in the high one
+    const uint32_t w01[4] = {o.u0.x, o.u0.z, o.u1.x, o.u1.z};
+    const uint32_t w23[4] = {o.u0.y, o.u0.w, o.u1.y, o.u1.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x0 = bf_lo(w01[r]);
+      x[r] = bf_hi(w01[r]);
+      x[4 + r] = bf_lo(w23[r]);
+      y[r] = y[4 + r] = x0;
+    }
+  }
+  bf16x8 a;
+#pragma unroll
+  for (int sl = 0; sl < 8; ++sl) a[sl] = (__bf16)(x[sl] * y[sl]);
+#pragma unroll
+  for (int n = 0; n < 4; ++n) R[n] = mfma32(a, __builtin_bit_cast(bf16x8, o.sb[n]), R[n]);
+}
+// Steps KK .. K1 - 1, the operands of KK already in cur: the next step's loads are issued
+// before this step's arithmetic (a scheduling barrier keeps them there), so their LDS latency
+// hides behind it.
+template <int KK, int K1>
+__device__ __forceinline__ void rd_steps32(const RdOps32& cur, const uint4 (*Sb)[4][64],
+                                           const __bf16* const (&qa)[2],
+                                           const __bf16* const (&qj)[2], const __bf16* qd,
+                                           const __bf16* ql, int lane, f32x4 (&R)[4]) {
+  if constexpr (KK + 1 < K1) {
+    RdOps32 nxt;
+    rd_load32<KK + 1>(nxt, Sb, qa, qj, qd, ql, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    rd_step32<KK>(cur, R);
+    rd_steps32<KK + 1, K1>(nxt, Sb, qa, qj, qd, ql, lane, R);
+  } else {
+    rd_step32<KK>(cur, R);
+  }
+}
+
+// Readout phi(q_t)^T S_{<c} over the K steps [kSteps0 CH, ..) of the waves with ch = CH, for all
+// four value tiles.  qa, qj, qd and ql point into this lane's q row at the lane offsets of the
+// step kinds (R plain / split: the i pair and the j quad; D: the block; L: the four blocks),
+// so each step's loads take constant offsets from them.
 template <int CH>
 __device__ __forceinline__ void readout32(const uint4 (*Sb)[4][64], const __bf16* const (&qa)[2],
                                           const __bf16* const (&qj)[2], const __bf16* qd,
                                           const __bf16* ql, int lane, f32x4 (&R)[4]) {
   constexpr int k0 = CH ? kSteps0 : 0, k1 = CH ? kSteps : kSteps0;
-#pragma unroll
-  for (int kk = k0; kk < k1; ++kk) {
-    const Step32 st = step32(kk);
-    float x[8], y[8];                 // slot s of the A operand is x[s] * y[s]
-    if (st.kind == kPlainR || st.kind == kSplitR) {
-      const uint32_t qi = *reinterpret_cast<const uint32_t*>(qa[st.kind] + st.a0);
-      const uint2 qv = *reinterpret_cast<const uint2*>(qj[st.kind] + 4 * st.J0);
-      const float jv[4] = {bf_lo(qv.x), bf_hi(qv.x), bf_lo(qv.y), bf_hi(qv.y)};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[r] = bf_lo(qi);
-        x[4 + r] = bf_hi(qi);
-        y[r] = y[4 + r] = jv[r];
-      }
-    } else if (st.kind == kDiag) {
-      const uint2 qv = *reinterpret_cast<const uint2*>(qd + 4 * st.J0);
-      const float xv[4] = {bf_lo(qv.x), bf_hi(qv.x), bf_lo(qv.y), bf_hi(qv.y)};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[r] = xv[r];
-        x[4 + r] = xv[diag_i(r)];
-        y[r] = y[4 + r] = xv[r];
-      }
-    } else {
-      // blocks 4 (g & 1) + r: x_0, x_1 in the low word of the block, x_2 in the high one
-      const uint4 u0 = *reinterpret_cast<const uint4*>(ql);
-      const uint4 u1 = *reinterpret_cast<const uint4*>(ql + 8);
-      const uint32_t w01[4] = {u0.x, u0.z, u1.x, u1.z}, w23[4] = {u0.y, u0.w, u1.y, u1.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x0 = bf_lo(w01[r]);
-        x[r] = bf_hi(w01[r]);
-        x[4 + r] = bf_lo(w23[r]);
-        y[r] = y[4 + r] = x0;
-      }
-    }
-    bf16x8 a;
-#pragma unroll
-    for (int sl = 0; sl < 8; ++sl) a[sl] = (__bf16)(x[sl] * y[sl]);
-#pragma unroll
-    for (int n = 0; n < 4; ++n) R[n] = mfma32(a, __builtin_bit_cast(bf16x8, Sb[kk][n][lane]), R[n]);
-  }
+  RdOps32 first;
+  rd_load32<k0>(first, Sb, qa, qj, qd, ql, lane);
+  rd_steps32<k0, k1>(first, Sb, qa, qj, qd, ql, lane, R);
 }
 
 template <typename Tout>
