@@ -54,6 +54,12 @@ static_assert(KT_D % 8 == 4 && KT_D >= P && KT_Z0 >= KT_D + P && KT_Z0 % 8 == 4 
               KTROWS == KT_Z0 + 2, "K^T row placement");
 __device__ __forceinline__ int kt_row(int f) { return (f & ~7) | (((f & 7) + 2 * (f >> 3)) & 7); }
 
+// q row t starts 8 bytes in when t mod 16 >= 8: the readout's 4- and 8-byte reads of 16
+// consecutive tokens then fall on distinct banks (the 80-byte pitch alone repeats every 8
+// rows); the 32 values stay inside the 40-value row.  Reads of q rows are 8 bytes or less.
+__device__ __forceinline__ int q_skew(int t) { return 4 * ((t >> 3) & 1); }
+static_assert(QROW >= P + 4, "q row skew");
+
 struct __align__(16) Tiles32 {
   __bf16 Qs[C][QROW];
   __bf16 Ks[C][QROW];
@@ -222,7 +228,7 @@ __device__ __forceinline__ void store_kt(const Stage32& s, TL& tl, int tid) {
 // q / k pieces -> row-major rows (q when the tile has them) and K^T rows; v piece -> V
 __device__ __forceinline__ void store32(const Stage32& s, Tiles32& tl, bool with_q, int tid) {
   const int row = stage_row(tid), pc = stage_piece(tid);
-  if (with_q) *reinterpret_cast<uint2*>(&tl.Qs[row][4 * pc]) = s.q;
+  if (with_q) *reinterpret_cast<uint2*>(&tl.Qs[row][q_skew(row) + 4 * pc]) = s.q;
   *reinterpret_cast<uint2*>(&tl.Ks[row][4 * pc]) = s.k;
   store_kt(s, tl, tid);
   *reinterpret_cast<uint4*>(&tl.V[tid >> 3][8 * (tid & 7)]) = s.v;
@@ -478,10 +484,6 @@ struct __align__(16) Walk32Lds {
   uint32_t vbad[kWaves];          // per wave: its staged v row pieces hold a non-finite value
 };
 
-// Readout phi(q_t)^T S_{<c} over the K steps [kSteps0 CH, ..) of the waves with ch = CH, for all
-// four value tiles.  qa, qj, qd and ql point into this lane's q row at the lane offsets of the
-// step kinds (R plain / split: the i pair and the j quad; D: the block; L: the four blocks),
-// so each step's loads take constant offsets from them.
 // One readout K step's LDS operands: this lane's q words (the fields its step kind uses) and
 // the four B-operand words of the state.
 struct RdOps32 {
@@ -490,19 +492,21 @@ struct RdOps32 {
   uint4 u0, u1;
   uint4 sb[4];
 };
-template <int KK>
+template <int KK, bool kLoadJ = true>
 __device__ __forceinline__ void rd_load32(RdOps32& o, const uint4 (*Sb)[4][64],
                                           const __bf16* const (&qa)[2], const __bf16* const (&qj)[2],
                                           const __bf16* qd, const __bf16* ql, int lane) {
   constexpr Step32 st = step32(KK);
   if constexpr (st.kind == kPlainR || st.kind == kSplitR) {
     o.qi = *reinterpret_cast<const uint32_t*>(qa[st.kind] + st.a0);
-    o.qv = *reinterpret_cast<const uint2*>(qj[st.kind] + 4 * st.J0);
+    if constexpr (kLoadJ) o.qv = *reinterpret_cast<const uint2*>(qj[st.kind] + 4 * st.J0);
   } else if constexpr (st.kind == kDiag) {
     o.qv = *reinterpret_cast<const uint2*>(qd + 4 * st.J0);
   } else {
-    o.u0 = *reinterpret_cast<const uint4*>(ql);
-    o.u1 = *reinterpret_cast<const uint4*>(ql + 8);
+    const uint2 h0 = *reinterpret_cast<const uint2*>(ql), h1 = *reinterpret_cast<const uint2*>(ql + 4);
+    const uint2 h2 = *reinterpret_cast<const uint2*>(ql + 8), h3 = *reinterpret_cast<const uint2*>(ql + 12);
+    o.u0 = uint4{h0.x, h0.y, h1.x, h1.y};
+    o.u1 = uint4{h2.x, h2.y, h3.x, h3.y};
   }
 #pragma unroll
   for (int n = 0; n < 4; ++n) o.sb[n] = Sb[KK][n][lane];
@@ -547,15 +551,19 @@ __device__ __forceinline__ void rd_step32(const RdOps32& o, f32x4 (&R)[4]) {
 }
 // Steps KK .. K1 - 1, the operands of KK already in cur: the next step's loads are issued
 // before this step's arithmetic (a scheduling barrier keeps them there), so their LDS latency
-// hides behind it.
+// hides behind it.  Consecutive plain R steps of one column block take their j quad from the
+// previous step (the barrier would otherwise keep the compiler from sharing it).
 template <int KK, int K1>
 __device__ __forceinline__ void rd_steps32(const RdOps32& cur, const uint4 (*Sb)[4][64],
                                            const __bf16* const (&qa)[2],
                                            const __bf16* const (&qj)[2], const __bf16* qd,
                                            const __bf16* ql, int lane, f32x4 (&R)[4]) {
   if constexpr (KK + 1 < K1) {
+    constexpr Step32 a = step32(KK), b = step32(KK + 1);
+    constexpr bool same_j = a.kind == kPlainR && b.kind == kPlainR && a.J0 == b.J0;
     RdOps32 nxt;
-    rd_load32<KK + 1>(nxt, Sb, qa, qj, qd, ql, lane);
+    rd_load32<KK + 1, !same_j>(nxt, Sb, qa, qj, qd, ql, lane);
+    if constexpr (same_j) nxt.qv = cur.qv;
     __builtin_amdgcn_sched_barrier(0);
     rd_step32<KK>(cur, R);
     rd_steps32<KK + 1, K1>(nxt, Sb, qa, qj, qd, ql, lane, R);
@@ -657,10 +665,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
   __syncthreads();
 
   const int t = 16 * tg + l16;                 // this lane's token (fragment column / row)
-  const __bf16* const qa[2] = {&tl.Qs[t][2 * g], &tl.Qs[t][2 * (g & 1)]};
-  const __bf16* const qj[2] = {&tl.Qs[t][0], &tl.Qs[t][8 * (g >> 1)]};
-  const __bf16* const qd = &tl.Qs[t][4 * g];
-  const __bf16* const ql = &tl.Qs[t][16 * (g & 1)];
+  const __bf16* const qrow = &tl.Qs[t][q_skew(t)];
+  const __bf16* const qa[2] = {qrow + 2 * g, qrow + 2 * (g & 1)};
+  const __bf16* const qj[2] = {qrow, qrow + 8 * (g >> 1)};
+  const __bf16* const qd = qrow + 4 * g;
+  const __bf16* const ql = qrow + 16 * (g & 1);
   Tout* orow = o + row_off(pr.so, b, c0 * C + 16 * tg + 8 * (lane >> 5), h) + 32 * ch + (lane & 31);
   const long long so_t = pr.so[1];
 
@@ -674,7 +683,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     // ---- intra-chunk tile of this wave's tokens and value columns ----
     float lsum = 0.f;
     f32x4 O[2] = {zero4(), zero4()};
-    const bf16x8 qf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&tl.Qs[t][8 * g]));
+    const uint2 qf0 = *reinterpret_cast<const uint2*>(qrow + 8 * g);
+    const uint2 qf1 = *reinterpret_cast<const uint2*>(qrow + 8 * g + 4);
+    const bf16x8 qf = __builtin_bit_cast(bf16x8, uint4{qf0.x, qf0.y, qf1.x, qf1.y});
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       if (2 * m > tg) break;                       // key tiles entirely in the future
@@ -727,7 +738,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
       s16x4 qb[2];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
-        qb[mi] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2*>(&tl.Qs[t][16 * mi + 4 * g]));
+        qb[mi] = __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2*>(qrow + 16 * mi + 4 * g));
       f32x4 y = zero4();
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
