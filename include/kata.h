@@ -140,7 +140,10 @@ kata_status kata_fwd_chunked(const kata_problem* pr, const void* q, const void* 
  *   - a problem whose kata_fwd_chunked_workspace_size exceeds KATA_NOALLOC_SCRATCH_BYTES is
  *     rejected with KATA_ERR_WORKSPACE before anything is enqueued (the 131072-token, 16-head
  *     p = 16 plan needs 30.8 MiB; the literal one-state-per-chunk scan there, 1.3 GiB, does
- *     not fit);
+ *     not fit) -- unless its p = 32 state pass is spread (see kata_chunked_plan) and one state
+ *     per segment, half those states' bytes, fits: then it runs that way, and its outputs
+ *     agree with kata_fwd_chunked's to rounding (the prefixes add the same chunks in another
+ *     grouping) rather than bit for bit;
  *   - every call on one device shares that device's array and leaves its contents behind
  *     (nothing in it has to start at zero): calls that may overlap in time on one device --
  *     on different streams, or from different host threads -- race and must be ordered by
@@ -155,7 +158,10 @@ kata_status kata_fwd_chunked_noalloc(const kata_problem* pr, const void* q, cons
  * levels, feed the walk.  With one segment per (b, h) on the MFMA kernels (the sequential
  * inter-chunk form) neither runs and scan_levels is 0.  With 2 to 8 segments on the MFMA
  * kernels (walk_sums_prefix = 1) no scan runs either (scan_levels 0): the walk of segment s adds
- * the states of segments 0 .. s-1 in that order, the same exclusive prefix.  For p = 32
+ * the states of segments 0 .. s-1 in that order, the same exclusive prefix (p = 32 with at most
+ * 4 segments: the state pass spreads those chunks over one workgroup per segment, each leaving
+ * two partial states, and the walk adds the partials before its first chunk in chunk order;
+ * state_floats is still the size of one state).  For p = 32
  * KATA-Mg on the MFMA kernels the plan is that of each of the two p = 16 passes.  Source:
  * gist.science section 2.3 (inter-chunk depth O(log N_C)).
  *   out: host struct, filled on success.

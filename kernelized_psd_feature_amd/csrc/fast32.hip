@@ -363,13 +363,17 @@ __device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, Acc32& 
 
 // ==========================================================================================
 // Segment state: S_seg = sum over the segment's chunks of Phi(K_c)^T V_c, Z_seg = sum K^T K.
-// One workgroup per (segment, head, batch) (SegGrid); segments seg >= n_used get a zero state
-// without reading their tokens.
+// One workgroup per (segment, head, batch) (SegGrid).  sp == 0: workgroup seg sums segment
+// seg into state seg; segments seg >= n_used get a zero state without reading their tokens.
+// sp > 0 (spread): workgroup u sums the chunks [u sp, min((u + 1) sp, (n_seg - 1) L)) into two
+// partial states 2 u (the chunks before the first segment boundary after u sp) and 2 u + 1
+// (the chunks from that boundary on, written only when the range crosses it); sp <= L, so a
+// range crosses at most one boundary.  Empty ranges write nothing.
 // State layout (floats): tile t, value tile nt, lane -> ((t * 4 + nt) * 64 + lane) * 4, then
 // Z tile (mi, kj) -> kZOff + ((mi * 2 + kj) * 64 + lane) * 4.
 // ==========================================================================================
 __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
-    DevProblem pr, SegGrid sg, int L, int n_seg, int n_used, const __bf16* __restrict__ k,
+    DevProblem pr, SegGrid sg, int L, int n_seg, int n_used, int sp, const __bf16* __restrict__ k,
     const __bf16* __restrict__ v, float* __restrict__ states) {
   extern __shared__ __align__(16) unsigned char smem[];
   StateTiles32* tl = reinterpret_cast<StateTiles32*>(smem);    // two buffers
@@ -379,12 +383,28 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
   if (!blk.live) return;                           // padding of the grid (whole workgroup)
   const int seg = blk.seg, h = blk.h, b = blk.b;
   const int n_chunks = pr.T / C;
-  const int c0 = seg * L, nc = min(L, n_chunks - c0);
-  float* out = states + ((long long)(b * pr.H + h) * n_seg + seg) * kStateFloats;
-  if (seg >= n_used) {
-    float4* o4 = reinterpret_cast<float4*>(out);
-    for (int x = tid; x < kStateFloats / 4; x += kThreads) o4[x] = float4{0.f, 0.f, 0.f, 0.f};
-    return;
+  const long long seq = (long long)b * pr.H + h;
+  int c0, nc, flush = -1;          // chunk range; iteration that first sums a chunk below the boundary
+  float *out, *out_hi = nullptr;
+  if (sp == 0) {
+    c0 = seg * L;
+    nc = min(L, n_chunks - c0);
+    out = states + (seq * n_seg + seg) * kStateFloats;
+    if (seg >= n_used) {
+      float4* o4 = reinterpret_cast<float4*>(out);
+      for (int x = tid; x < kStateFloats / 4; x += kThreads) o4[x] = float4{0.f, 0.f, 0.f, 0.f};
+      return;
+    }
+  } else {
+    c0 = seg * sp;
+    nc = min(sp, (n_seg - 1) * L - c0);
+    if (nc <= 0) return;
+    out = states + (seq * n_seg + seg) * 2 * kStateFloats;
+    const int bnd = (c0 / L + 1) * L;
+    if (bnd < c0 + nc) {
+      out_hi = out + kStateFloats;
+      flush = c0 + nc - bnd;         // chunks are summed last first
+    }
   }
   Acc32 acc;
   acc.zero();
@@ -405,7 +425,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
     load32(st, p);
   }
   __syncthreads();
+  auto emit = [&](float* dst) {
+    acc.each(w, e, lane, [&](f32x4& x, int off) { *reinterpret_cast<f32x4*>(dst + off) = x; });
+    if (z >= 0) *reinterpret_cast<f32x4*>(dst + kZOff + (z * 64 + lane) * 4) = Zt;
+  };
   for (int c = 0; c < nc; ++c) {
+    if (c == flush) {                // the chunks from the segment boundary on are summed
+      emit(out_hi);
+      acc.zero();
+      Zt = zero4();
+    }
     update32(tl[c & 1], rw, acc, Zt, e, lane, z);
     if (c + 1 < nc) store_state32(st, tl[(c + 1) & 1], tid);   // buffer read last iteration
     if (c + 2 < nc) {
@@ -414,8 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
     }
     __syncthreads();
   }
-  acc.each(w, e, lane, [&](f32x4& x, int off) { *reinterpret_cast<f32x4*>(out + off) = x; });
-  if (z >= 0) *reinterpret_cast<f32x4*>(out + kZOff + (z * 64 + lane) * 4) = Zt;
+  emit(out);
 }
 
 struct Pair4 {
@@ -588,7 +616,7 @@ __device__ __forceinline__ void readout32(const uint4 (*Sb)[4][64], const __bf16
 
 template <typename Tout>
 __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
-    DevProblem pr, SegGrid sg, int L, int n_seg, const __bf16* __restrict__ q,
+    DevProblem pr, SegGrid sg, int L, int n_seg, int sp, const __bf16* __restrict__ q,
     const __bf16* __restrict__ k, const __bf16* __restrict__ v, Tout* __restrict__ o,
     float* __restrict__ den_out, const float* __restrict__ states, int sum_prefix) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -604,7 +632,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
 
   // Exclusive prefix of this segment: the scanned state at position seg, or (sum_prefix)
-  // the states of segments 0 .. seg-1 added in that order; zero without states.
+  // the states of segments 0 .. seg-1 added in that order, or (sp > 0) the partial states of
+  // the spread state pass that lie before chunk seg L, in the order of their chunks; zero
+  // without states.
   // Z: wave w with zt >= 0 keeps tile (zt >> 1, zt & 1) in Zt and publishes it split into
   // bf16 hi + lo.
   const int e = extra_of(w), zt = ztile_of(w);
@@ -612,11 +642,22 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
   acc.zero();
   f32x4 Zt = zero4();
   {
-    const int j0 = sum_prefix ? 0 : seg, j1 = !states ? j0 : sum_prefix ? seg : seg + 1;
-    for (int j = j0; j < j1; ++j) {
-      const float* pre = states + ((long long)(b * pr.H + h) * n_seg + j) * kStateFloats;
+    auto add = [&](const float* pre) {
       acc.each(w, e, lane, [&](f32x4& x, int off) { x += *reinterpret_cast<const f32x4*>(pre + off); });
       if (zt >= 0) Zt += *reinterpret_cast<const f32x4*>(pre + kZOff + (zt * 64 + lane) * 4);
+    };
+    const long long seq = (long long)b * pr.H + h;
+    if (states && sp > 0) {
+      for (int u = 0; u < n_seg; ++u) {
+        const int lo = u * sp, hi = min(lo + sp, (n_seg - 1) * L), bnd = (lo / L + 1) * L;
+        if (lo >= hi || lo >= seg * L) break;        // ranges ascend
+        const float* pre = states + (seq * n_seg + u) * 2 * kStateFloats;
+        add(pre);                                    // [lo, min(hi, bnd)): segment lo / L
+        if (bnd < hi && bnd < seg * L) add(pre + kStateFloats);   // [bnd, hi): segment bnd / L
+      }
+    } else {
+      const int j0 = sum_prefix ? 0 : seg, j1 = !states ? j0 : sum_prefix ? seg : seg + 1;
+      for (int j = j0; j < j1; ++j) add(states + (seq * n_seg + j) * kStateFloats);
     }
   }
   Rows32 rw;
@@ -673,6 +714,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
   Tout* orow = o + row_off(pr.so, b, c0 * C + 16 * tg + 8 * (lane >> 5), h) + 32 * ch + (lane & 31);
   const long long so_t = pr.so[1];
 
+
   for (int c = 0; c < nc; ++c) {
     const int tok0 = (c0 + c) * C;
     if (c + 1 < nc) {
@@ -700,9 +742,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
           f32x4 x2;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            x2[r] = sc[r] * sc[r];
-            // the diagonal tile: keys 16 tg + 4 g + r against token 16 tg + l16 (select)
-            if (ms == tg) x2[r] = 4 * g + r <= l16 ? x2[r] : 0.f;
+            // the diagonal tile (ms == tg): keys 16 tg + 4 g + r against token 16 tg + l16; one
+            // select whose condition folds the wave-uniform tile test into the lane mask
+            x2[r] = (ms < tg || 4 * g + r <= l16) ? sc[r] * sc[r] : 0.f;
           }
           // bf16 weights in pairs, their row sum from the same rounded values (v_dot2 with ones)
           pw[half][0] = pack_bf16x2(x2[0], x2[1]);
@@ -816,23 +858,25 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
 
 }  // namespace
 
-hipError_t launch_chunk_state32(const DevProblem& pr, int L, int n_seg, int n_used,
+hipError_t launch_chunk_state32(const DevProblem& pr, int L, int n_seg, int n_used, int sp,
                                 const void* k, const void* v, float* states, hipStream_t st) {
   if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;
+  if (sp < 0 || sp > L) return hipErrorInvalidValue;    // a spread range crosses one boundary
   const size_t lds = 2 * sizeof(StateTiles32);
   hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&chunk_state32_kernel), (int)lds);
   if (e != hipSuccess) return e;
   const SegGrid sg = make_seg_grid(pr, n_seg);
   if (sg.blocks() > 0x7fffffffLL) return hipErrorInvalidValue;
   launch_kernel(chunk_state32_kernel, dim3((unsigned)sg.blocks()), kThreads, lds, st,
-      pr, sg, L, n_seg, n_used, (const __bf16*)k, (const __bf16*)v, states);
+      pr, sg, L, n_seg, n_used, sp, (const __bf16*)k, (const __bf16*)v, states);
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int n_seg,
+hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int n_seg, int sp,
                                  const void* q, const void* k, const void* v, void* o,
                                  float* den, const float* states, bool sum_prefix, hipStream_t st) {
   if (pr.p != P || pr.dv != DV || pr.C != C) return hipErrorInvalidValue;
+  if (sp < 0 || sp > L || (sp > 0 && !sum_prefix)) return hipErrorInvalidValue;
   const size_t lds = sizeof(Walk32Lds);
   const SegGrid sg = make_seg_grid(pr, n_seg);
   if (sg.blocks() > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -842,13 +886,13 @@ hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int
   if (out_bf16) {
     e = ensure_dynamic_lds(reinterpret_cast<const void*>(&chunk_output32_kernel<__bf16>), (int)lds);
     if (e != hipSuccess) return e;
-    launch_kernel(chunk_output32_kernel<__bf16>, grid, kThreads, lds, st, pr, sg, L, n_seg, qq,
-                  kk, vv, (__bf16*)o, den, states, (int)sum_prefix);
+    launch_kernel(chunk_output32_kernel<__bf16>, grid, kThreads, lds, st, pr, sg, L, n_seg, sp,
+                  qq, kk, vv, (__bf16*)o, den, states, (int)sum_prefix);
   } else {
     e = ensure_dynamic_lds(reinterpret_cast<const void*>(&chunk_output32_kernel<float>), (int)lds);
     if (e != hipSuccess) return e;
-    launch_kernel(chunk_output32_kernel<float>, grid, kThreads, lds, st, pr, sg, L, n_seg, qq,
-                  kk, vv, (float*)o, den, states, (int)sum_prefix);
+    launch_kernel(chunk_output32_kernel<float>, grid, kThreads, lds, st, pr, sg, L, n_seg, sp,
+                  qq, kk, vv, (float*)o, den, states, (int)sum_prefix);
   }
   return hipGetLastError();
 }

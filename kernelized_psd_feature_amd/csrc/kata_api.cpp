@@ -22,9 +22,9 @@ hipError_t launch_quadratic_mfma(const DevProblem& pr, int gw, bool out_bf16, co
 bool quadratic_mfma_grid_fits(const DevProblem& pr);
 int quadratic_mfma_group_width(const kata_problem* pr);
 bool chunk_fast_available();
-hipError_t launch_chunk_state32(const DevProblem& pr, int L, int n_seg, int n_used,
+hipError_t launch_chunk_state32(const DevProblem& pr, int L, int n_seg, int n_used, int sp,
                                 const void* k, const void* v, float* states, hipStream_t st);
-hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int n_seg,
+hipError_t launch_chunk_output32(const DevProblem& pr, bool out_bf16, int L, int n_seg, int sp,
                                  const void* q, const void* k, const void* v, void* o,
                                  float* den, const float* states, bool sum_prefix, hipStream_t st);
 
@@ -242,7 +242,8 @@ kata_status run_chunked(const kata_problem* pr, const kata::ChunkPlan& cp, const
     {
       Timed t(KATA_K_CHUNK_STATE, st);
       // the last segment's state enters no prefix
-      e = cp.fast32 ? kata::launch_chunk_state32(dp, cp.L, cp.n_seg, cp.n_seg - 1, k, v, states, st)
+      e = cp.fast32 ? kata::launch_chunk_state32(dp, cp.L, cp.n_seg, cp.n_seg - 1, cp.sp, k, v,
+                                                 states, st)
           : cp.fast ? kata::launch_chunk_state_fast(dp, cp.packed, cp.gw, cp.L, cp.n_seg,
                                                     cp.n_seg - 1, k, v, states, st)
                     : kata::launch_chunk_state_generic(dp, in_bf16, k, v, states, cp.n_chunks, st);
@@ -259,8 +260,8 @@ kata_status run_chunked(const kata_problem* pr, const kata::ChunkPlan& cp, const
     Timed t(KATA_K_CHUNK_OUTPUT, st);
     const float* pre = one_segment ? nullptr : states;
     const bool sum_prefix = cp.walk_sums_prefix != 0;
-    e = cp.fast32 ? kata::launch_chunk_output32(dp, out_bf16, cp.L, cp.n_seg, q, k, v, o, den,
-                                                pre, sum_prefix, st)
+    e = cp.fast32 ? kata::launch_chunk_output32(dp, out_bf16, cp.L, cp.n_seg, cp.sp, q, k, v, o,
+                                                den, pre, sum_prefix, st)
         : cp.fast ? kata::launch_chunk_output_fast(dp, cp.packed, cp.gw, out_bf16, cp.L,
                                                    cp.n_seg, q, k, v, o, den, pre, sum_prefix, st)
                 : kata::launch_chunk_output_generic(dp, in_bf16, out_bf16, q, k, v, o, den,
@@ -384,7 +385,8 @@ kata_status kata_fwd_chunked_noalloc(const kata_problem* pr, const void* q, cons
   g_last_error.clear();
   kata_status s = check_forward_args(pr, Form::Chunked, q, k, v, o, den);
   if (s != KATA_OK) return s;
-  const kata::ChunkPlan cp = kata::plan_chunked(pr, kata::chunk_fast_available());
+  kata::ChunkPlan cp = kata::plan_chunked(pr, kata::chunk_fast_available());
+  if (cp.ws_bytes > KATA_NOALLOC_SCRATCH_BYTES) cp = kata::plan_unspread(cp);
   if (cp.ws_bytes > KATA_NOALLOC_SCRATCH_BYTES)
     return set_error(KATA_ERR_WORKSPACE,
                      "the problem needs " + std::to_string(cp.ws_bytes) +

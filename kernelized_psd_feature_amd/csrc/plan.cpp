@@ -210,6 +210,16 @@ static int walk_sum_segment_length(const kata_problem* pr, const ChunkPlan& cp, 
   return best_L;
 }
 
+// States, scan workspace and total of a plan whose kernels are chosen (not the KATA-Mg halves).
+static void set_workspace(ChunkPlan& cp) {
+  const size_t per_seg = cp.sp ? 2 : 1;
+  cp.states_bytes =
+      round256(size_t(cp.n_seq) * size_t(cp.n_seg) * per_seg * size_t(cp.state_elems) * 4);
+  cp.scan_ws_bytes =
+      cp.walk_sums_prefix ? 0 : plan_scan(cp.n_seq, cp.n_seg, cp.state_elems).ws_bytes;
+  cp.ws_bytes = cp.states_bytes + cp.scan_ws_bytes;
+}
+
 ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
   // p = 32 KATA-Mg on the MFMA kernels: the groups (16, 8 or 4 coordinates) lie inside the two
   // 16-coordinate halves, so a_ts is the sum of the halves' grouped scores; each half is a
@@ -294,10 +304,21 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
   cp.compact =
       (cp.fast && cp.packed && !cp.fast32 && cp.n_seg >= 2 && !cp.walk_sums_prefix) ? 1 : 0;
   if (cp.compact) cp.state_elems = int64_t(16) * (cp.gw + 1) / 2 * 64 + 256;
-  cp.states_bytes = round256(size_t(cp.n_seq) * size_t(cp.n_seg) * size_t(cp.state_elems) * 4);
-  cp.scan_ws_bytes =
-      cp.walk_sums_prefix ? 0 : plan_scan(cp.n_seq, cp.n_seg, cp.state_elems).ws_bytes;
-  cp.ws_bytes = cp.states_bytes + cp.scan_ws_bytes;
+  // The p = 32 state pass otherwise runs n_seg - 1 of its n_seg workgroups per sequence (one
+  // workgroup per CU): with 4 segments a quarter of the GPU idles.  Spread, every workgroup
+  // takes sp = ceil((n_seg - 1) L / n_seg) chunks, and the walk of segment s adds the up to
+  // 2 s partial states before it instead of s states.  Beyond 4 segments the idle share is
+  // small and the walks' extra state reads outweigh it.
+  if (cp.fast32 && cp.walk_sums_prefix && cp.n_seg <= kSpreadMaxSegments)
+    cp.sp = int((int64_t(cp.n_seg - 1) * cp.L + cp.n_seg - 1) / cp.n_seg);
+  set_workspace(cp);
+  return cp;
+}
+
+ChunkPlan plan_unspread(ChunkPlan cp) {
+  if (cp.sp == 0) return cp;
+  cp.sp = 0;
+  set_workspace(cp);
   return cp;
 }
 

@@ -13,6 +13,9 @@ namespace kata {
 
 enum class Form { Quadratic, Chunked, Backward };
 
+// Most segments per sequence for which the p = 32 state pass is spread (ChunkPlan::sp).
+constexpr int kSpreadMaxSegments = 4;
+
 // Most segments per sequence for which the walks form their prefixes without a scan.
 constexpr int kWalkPrefixMaxSegments = 8;
 
@@ -27,6 +30,11 @@ struct ChunkPlan {
   int n_seg = 0;              // ceil(N_c / L)
   int walk_sums_prefix = 0;   // 1: each walk adds the earlier segments' states itself, no scan
   int compact = 0;            // 1: packed p = 16 states stored without their zero rows (scan)
+  // p = 32, walks adding the prefixes themselves, at most 4 segments: the state pass spreads
+  // the (n_seg - 1) L chunks that enter a prefix evenly over n_seg workgroups per sequence, sp
+  // chunks each, and every workgroup leaves two partial states (the part of its range before
+  // and after the segment boundary it crosses).  0: one workgroup and one state per segment.
+  int sp = 0;
   // 1: p = 32 KATA-Mg (g >= 2) as two p = 16 passes over the coordinate halves (every other
   // field then describes one pass); the workspace adds the passes' fp32 outputs and D_t
   int halves = 0;
@@ -35,7 +43,7 @@ struct ChunkPlan {
   int dv_split = 1;           // workgroups sharing one segment, each owning dv / dv_split columns
   int64_t n_seq = 0;          // B * H
   int64_t state_elems = 0;    // floats in one segment state: p^2 (dv + 1)
-  size_t states_bytes = 0;    // n_seq * n_seg * state_elems * 4, rounded up to 256
+  size_t states_bytes = 0;    // n_seq * n_seg * (sp ? 2 : 1) * state_elems * 4, rounded to 256
   size_t scan_ws_bytes = 0;   // extra workspace of the prefix scan over n_seg segments
   size_t ws_bytes = 0;        // total
 };
@@ -78,6 +86,9 @@ kata_status validate_scan(int64_t n_seq, int64_t n, int64_t elems, std::string* 
 ScanPlan plan_scan(int64_t n_seq, int64_t n, int64_t elems);
 // pr must have passed validate_problem; fast_available: the MFMA chunked kernels are built.
 ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available);
+// The same plan with one state per segment in the p = 32 state pass (sp = 0: half the states'
+// workspace), for callers bound to a fixed scratch size.
+ChunkPlan plan_unspread(ChunkPlan cp);
 
 // Floats in one packed p = 32 segment state (34 tiles of 16 x 64 plus Z as four 16 x 16 tiles).
 constexpr int64_t kState32Floats = 34 * 16 * 64 + 4 * 256;

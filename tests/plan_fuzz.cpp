@@ -186,8 +186,22 @@ void check_chunked(const kata_problem& pr, bool fast) {
   if (cp.fast) CHECK(pr.in_dtype == KATA_BF16 && pr.dv == 64 && pr.chunk == 64, "MFMA shape");
   if (cp.walk_sums_prefix)
     CHECK(cp.n_seg >= 2 && cp.n_seg <= kata::kWalkPrefixMaxSegments, "walk-summed prefix");
+  if (cp.sp) {
+    // spread p = 32 state pass: n_seg ranges of sp chunks cover the (n_seg - 1) L chunks before
+    // the last segment, each range crosses at most one segment boundary
+    CHECK(cp.fast32 && cp.walk_sums_prefix && cp.n_seg <= kata::kSpreadMaxSegments, "spread plan");
+    CHECK(cp.sp >= 1 && cp.sp <= cp.L, "spread range length");
+    CHECK(int64_t(cp.sp) * cp.n_seg >= int64_t(cp.n_seg - 1) * cp.L &&
+              int64_t(cp.sp - 1) * cp.n_seg < int64_t(cp.n_seg - 1) * cp.L,
+          "spread ranges cover the prefix chunks, the shortest such length");
+    const kata::ChunkPlan un = kata::plan_unspread(cp);
+    CHECK(un.sp == 0 && 2 * (un.states_bytes / 256) >= cp.states_bytes / 256 &&
+              un.ws_bytes == un.states_bytes + un.scan_ws_bytes,
+          "unspread plan");
+  }
   CHECK(u128(cp.states_bytes) ==
-            round256(u128(cp.n_seq) * u128(cp.n_seg) * u128(cp.state_elems) * 4),
+            round256(u128(cp.n_seq) * u128(cp.n_seg) * u128(cp.sp ? 2 : 1) *
+                     u128(cp.state_elems) * 4),
         "states bytes are the exact product");
   CHECK(cp.states_bytes % 256 == 0, "states aligned");
   CHECK(u128(cp.ws_bytes) == u128(cp.states_bytes) + u128(cp.scan_ws_bytes), "workspace sum");

@@ -917,7 +917,9 @@ def test_p32_every_element(T, form):
     np.testing.assert_allclose(d.cpu().double().numpy(), dref, rtol=1e-2)
 
 
-@pytest.mark.parametrize("seg", [1, 3, 7, 64])
+# seg 5, 6, 7, 8: 4, 3, 3, 2 segments, whose walks add the partial states of the spread state
+# pass (ranges of 4, 4, 5, 4 chunks; all but seg 8 cross a segment boundary)
+@pytest.mark.parametrize("seg", [1, 3, 5, 6, 7, 8, 64])
 def test_p32_segment_lengths(seg):
     w = W.WORKLOADS[3]
     q, k, v = W.make_inputs(w, 41, T=1024, B=1, H=2)

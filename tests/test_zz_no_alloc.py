@@ -1,7 +1,8 @@
 """kata_fwd_chunked_noalloc (the chunked forward on the library's static scratch) against
 kata_fwd_chunked with a caller workspace: the same kernels and plan, so the same outputs bit
 for bit, on two calls in a row (the second with a smaller input, reusing the scratch the first
-left behind), plus the oracle on sampled rows."""
+left behind), plus the oracle on sampled rows; and a p = 32 problem whose spread state pass
+needs more than the scratch, which runs with one state per segment (outputs equal to rounding)."""
 
 import numpy as np
 import pytest
@@ -83,6 +84,21 @@ def test_noalloc_other_kernels_match_the_workspace_entry_point(case):
     ref, dref, out, den = _both(q, k, v, **kw)
     torch.cuda.synchronize()
     assert torch.equal(out, ref) and torch.equal(den, dref)
+
+
+def test_noalloc_unspreads_a_p32_state_pass_beyond_its_scratch():
+    # p = 32 at 4 x 16 heads x 16384 tokens: 4 segments of 64 chunks; the spread state pass
+    # keeps two partial states per segment (73 MB), one state per segment fits (37 MB)
+    w = W.WORKLOADS[3]
+    q, k, v = (x.to(DEV) for x in W.make_inputs(w, 3, B=4, H=16, T=16384))
+    assert K.chunked_workspace_size(q, k, v) > K.NOALLOC_SCRATCH_BYTES
+    ref, dref, out, den = _both(q, k, v)
+    torch.cuda.synchronize()
+    assert float((out - ref).abs().max()) <= 1e-3
+    assert float(((den - dref).abs() / dref).max()) <= 1e-4
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(4096 - 8, 4096 + 8),
+                                     np.arange(16384 - 64, 16384)]))
+    assert _oracle_rows(q, k, v, out, [(0, 0), (3, 15)], rows) <= 1e-2
 
 
 def test_noalloc_rejects_a_problem_beyond_its_scratch():
