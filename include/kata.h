@@ -159,9 +159,9 @@ kata_status kata_fwd_chunked_noalloc(const kata_problem* pr, const void* q, cons
  * inter-chunk form) neither runs and scan_levels is 0.  With 2 to 8 segments on the MFMA
  * kernels (walk_sums_prefix = 1) no scan runs either (scan_levels 0): the walk of segment s adds
  * the states of segments 0 .. s-1 in that order, the same exclusive prefix (p = 32 with at most
- * 4 segments: the state pass spreads those chunks over one workgroup per segment, each leaving
- * two partial states, and the walk adds the partials before its first chunk in chunk order;
- * state_floats is still the size of one state).  For p = 32
+ * 4 segments: the state pass spreads those chunks over one workgroup per segment, and the walk
+ * adds the sums of the ranges before its first chunk in chunk order, the range that crosses it
+ * up to that chunk; state_floats is still the size of one state).  For p = 32
  * KATA-Mg on the MFMA kernels the plan is that of each of the two p = 16 passes.  Source:
  * gist.science section 2.3 (inter-chunk depth O(log N_C)).
  *   out: host struct, filled on success.

@@ -365,10 +365,10 @@ __device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, Acc32& 
 // Segment state: S_seg = sum over the segment's chunks of Phi(K_c)^T V_c, Z_seg = sum K^T K.
 // One workgroup per (segment, head, batch) (SegGrid).  sp == 0: workgroup seg sums segment
 // seg into state seg; segments seg >= n_used get a zero state without reading their tokens.
-// sp > 0 (spread): workgroup u sums the chunks [u sp, min((u + 1) sp, (n_seg - 1) L)) into two
-// partial states 2 u (the chunks before the first segment boundary after u sp) and 2 u + 1
-// (the chunks from that boundary on, written only when the range crosses it); sp <= L, so a
-// range crosses at most one boundary.  Empty ranges write nothing.
+// sp > 0 (spread): workgroup u sums the chunks [u sp, min((u + 1) sp, (n_seg - 1) L)), first to
+// last, into state 2 u: the whole range, or, when the range crosses a segment boundary (sp <=
+// L: at most one), the chunks before it, and then state 2 u + 1 the whole range.  Empty ranges
+// write nothing.
 // State layout (floats): tile t, value tile nt, lane -> ((t * 4 + nt) * 64 + lane) * 4, then
 // Z tile (mi, kj) -> kZOff + ((mi * 2 + kj) * 64 + lane) * 4.
 // ==========================================================================================
@@ -384,8 +384,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
   const int seg = blk.seg, h = blk.h, b = blk.b;
   const int n_chunks = pr.T / C;
   const long long seq = (long long)b * pr.H + h;
-  int c0, nc, flush = -1;          // chunk range; iteration that first sums a chunk below the boundary
-  float *out, *out_hi = nullptr;
+  int c0, nc, flush = -1;          // chunk range; iteration that first sums a chunk past the boundary
+  float *out, *out_all = nullptr;   // spread and crossing: the part before the boundary, the whole
   if (sp == 0) {
     c0 = seg * L;
     nc = min(L, n_chunks - c0);
@@ -402,8 +402,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
     out = states + (seq * n_seg + seg) * 2 * kStateFloats;
     const int bnd = (c0 / L + 1) * L;
     if (bnd < c0 + nc) {
-      out_hi = out + kStateFloats;
-      flush = c0 + nc - bnd;         // chunks are summed last first
+      out_all = out + kStateFloats;
+      flush = bnd - c0;              // chunks are summed first to last
     }
   }
   Acc32 acc;
@@ -414,9 +414,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
   zero_row(tl[0], tid);
   zero_row(tl[1], tid);
 
-  // last chunk first (the sum is order-free; the walk then starts on recently read chunks),
-  // one chunk in flight in registers, two LDS buffers, one barrier per chunk
-  Ptrs32 p = ptrs32(pr, nullptr, k, v, b, h, (c0 + nc - 1) * C, false, tid, -1);
+  // one state per segment: last chunk first (the walk then starts on recently read chunks);
+  // spread: first to last, so the sum at the boundary is the part before it.  One chunk in
+  // flight in registers, two LDS buffers, one barrier per chunk.
+  const int dir = sp == 0 ? -1 : 1;
+  Ptrs32 p = ptrs32(pr, nullptr, k, v, b, h, (dir < 0 ? c0 + nc - 1 : c0) * C, false, tid, dir);
   Stage32 st;
   load32(st, p);
   store_state32(st, tl[0], tid);
@@ -430,11 +432,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
     if (z >= 0) *reinterpret_cast<f32x4*>(dst + kZOff + (z * 64 + lane) * 4) = Zt;
   };
   for (int c = 0; c < nc; ++c) {
-    if (c == flush) {                // the chunks from the segment boundary on are summed
-      emit(out_hi);
-      acc.zero();
-      Zt = zero4();
-    }
+    if (c == flush) emit(out);       // the chunks before the segment boundary
     update32(tl[c & 1], rw, acc, Zt, e, lane, z);
     if (c + 1 < nc) store_state32(st, tl[(c + 1) & 1], tid);   // buffer read last iteration
     if (c + 2 < nc) {
@@ -443,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
     }
     __syncthreads();
   }
-  emit(out);
+  emit(out_all ? out_all : out);
 }
 
 struct Pair4 {
@@ -632,9 +630,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
   const int c0 = seg * L, nc = min(L, n_chunks - c0);
 
   // Exclusive prefix of this segment: the scanned state at position seg, or (sum_prefix)
-  // the states of segments 0 .. seg-1 added in that order, or (sp > 0) the partial states of
-  // the spread state pass that lie before chunk seg L, in the order of their chunks; zero
-  // without states.
+  // the states of segments 0 .. seg-1 added in that order, or (sp > 0) the sums of the spread
+  // state pass over the chunks before seg L, in the order of their ranges (a range that ends
+  // by seg L: its whole sum; the range that crosses seg L: its part before it); zero without
+  // states.
   // Z: wave w with zt >= 0 keeps tile (zt >> 1, zt & 1) in Zt and publishes it split into
   // bf16 hi + lo.
   const int e = extra_of(w), zt = ztile_of(w);
@@ -652,8 +651,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
         const int lo = u * sp, hi = min(lo + sp, (n_seg - 1) * L), bnd = (lo / L + 1) * L;
         if (lo >= hi || lo >= seg * L) break;        // ranges ascend
         const float* pre = states + (seq * n_seg + u) * 2 * kStateFloats;
-        add(pre);                                    // [lo, min(hi, bnd)): segment lo / L
-        if (bnd < hi && bnd < seg * L) add(pre + kStateFloats);   // [bnd, hi): segment bnd / L
+        // crossing a boundary: state 2 u is [lo, bnd), 2 u + 1 the whole range; else 2 u
+        add(bnd < hi && hi <= seg * L ? pre + kStateFloats : pre);
       }
     } else {
       const int j0 = sum_prefix ? 0 : seg, j1 = !states ? j0 : sum_prefix ? seg : seg + 1;

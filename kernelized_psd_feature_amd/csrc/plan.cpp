@@ -306,9 +306,9 @@ ChunkPlan plan_chunked(const kata_problem* pr, bool fast_available) {
   if (cp.compact) cp.state_elems = int64_t(16) * (cp.gw + 1) / 2 * 64 + 256;
   // The p = 32 state pass otherwise runs n_seg - 1 of its n_seg workgroups per sequence (one
   // workgroup per CU): with 4 segments a quarter of the GPU idles.  Spread, every workgroup
-  // takes sp = ceil((n_seg - 1) L / n_seg) chunks, and the walk of segment s adds the up to
-  // 2 s partial states before it instead of s states.  Beyond 4 segments the idle share is
-  // small and the walks' extra state reads outweigh it.
+  // takes sp = ceil((n_seg - 1) L / n_seg) chunks, and the walk of segment s adds up to s + 1
+  // range sums (the last one cut at its start) instead of s states.  Beyond 4 segments the
+  // idle share is small and the walks' extra state reads outweigh it.
   if (cp.fast32 && cp.walk_sums_prefix && cp.n_seg <= kSpreadMaxSegments)
     cp.sp = int((int64_t(cp.n_seg - 1) * cp.L + cp.n_seg - 1) / cp.n_seg);
   set_workspace(cp);

@@ -32,8 +32,8 @@ struct ChunkPlan {
   int compact = 0;            // 1: packed p = 16 states stored without their zero rows (scan)
   // p = 32, walks adding the prefixes themselves, at most 4 segments: the state pass spreads
   // the (n_seg - 1) L chunks that enter a prefix evenly over n_seg workgroups per sequence, sp
-  // chunks each, and every workgroup leaves two partial states (the part of its range before
-  // and after the segment boundary it crosses).  0: one workgroup and one state per segment.
+  // chunks each, and every workgroup leaves up to two states (the sum of its range, and of the
+  // part before the segment boundary it crosses).  0: one workgroup and one state per segment.
   int sp = 0;
   // 1: p = 32 KATA-Mg (g >= 2) as two p = 16 passes over the coordinate halves (every other
   // field then describes one pass); the workspace adds the passes' fp32 outputs and D_t
