@@ -13,8 +13,9 @@
 // registers, so a workgroup has eight waves (two per SIMD, one workgroup per CU; waves w and
 // w + 4 share a SIMD):
 //   state tiles  the tiles go in K-step pairs (2 P, 2 P + 1).  Wave w owns pairs w and w + 8
-//                with all four value tiles; the last pair is split by value tiles over waves
-//                0-3, and the four Z tiles go to waves 4-7 (one of each per SIMD).
+//                with all four value tiles; the two tiles of the last pair go to waves 0 and 1
+//                (SIMDs 0, 1) and the four Z tiles to waves 2, 3, 6, 7 (two on each of SIMDs
+//                2, 3), with all four value tiles each.
 //                The two tiles of a pair share their j factor rows, which the update reads
 //                once, and their accumulators make whole B-operand words of the readout, which
 //                the publish writes at once,
@@ -72,14 +73,18 @@ struct __align__(16) StateTiles32 {                  // the state pass needs no 
   __bf16 V[C][VROW];
 };
 
-// Tile ownership (see the file comment): whole pair ps < kFull of wave w, the value tile e of
-// the last pair (e >= 0 on waves 0-3) and the Z tile index.
-__device__ __forceinline__ int pair_of(int w, int ps) { return w + 8 * ps; }
-__device__ __forceinline__ int extra_of(int w) { return w < 4 ? w : -1; }
-__device__ __forceinline__ int ztile_of(int w) { return w < 4 ? -1 : w - 4; }
+// Tile ownership (see the file comment): whole pair ps < kFull of wave w, the tile 32 + e of
+// the last pair (e >= 0 on waves 0, 1) and the Z tile index (z >= 0 on waves 2, 3, 6, 7).
+__host__ __device__ constexpr int pair_of(int w, int ps) { return w + 8 * ps; }
+__host__ __device__ constexpr int extra_of(int w) { return w < 2 ? w : -1; }
+__host__ __device__ constexpr int ztile_of(int w) { return (w & 2) ? (w & 1) + 2 * (w >> 2) : -1; }
 // token group of wave w (see the file comment); its partner wave is 7 - w
 __device__ __forceinline__ int tgroup_of(int w) { return w < 4 ? w : 7 - w; }
 static_assert(2 * (8 * kFull + 1) == kTiles, "pairs: kFull per wave and one split pair");
+// one extra 16 x 64 tile per wave at most (the last pair's or a Z tile), so one accumulator set
+static_assert(extra_of(0) == 0 && extra_of(1) == 1 && ztile_of(2) == 0 && ztile_of(3) == 1 &&
+              ztile_of(6) == 2 && ztile_of(7) == 3 && extra_of(4) < 0 && ztile_of(5) < 0,
+              "tile ownership");
 
 // Row order of the packed state.  K step kk covers tiles 2 kk and 2 kk + 1; its octet g (the
 // readout's lane group g = lane / 16) is rows 4 g + r of both tiles, r = 0..3, the readout's
@@ -275,7 +280,7 @@ __device__ __forceinline__ bf16x8 kcol(const TL& tl, int mi, int m, int lane) {
 }
 
 // Row sources of this lane's row of each owned pair: ps < kFull the whole pairs, ps = kFull
-// the half-pair (when the wave has one).
+// the last pair (its tile 32 + e in irow[kFull][0], when the wave has one).
 struct Rows32 {
   int irow[kFull + 1][2], jrow[kFull + 1];
   __device__ void init(int w, int e, int lane) {
@@ -286,7 +291,7 @@ struct Rows32 {
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
         int i = 0;
-        row32(P, row >> 2, row & 3, tp, i, j);       // j is the same for both tiles
+        row32(P, row >> 2, row & 3, ps < kFull ? tp : max(e, 0), i, j);   // j: the same for both
         irow[ps][tp] = i < 0 ? KT_Z0 + (row & 1) : (i == j ? kt_row(i) : KT_D + kt_row(i));
       }
       jrow[ps] = kt_row(j);
@@ -294,11 +299,12 @@ struct Rows32 {
   }
 };
 
-// The accumulators of one wave's share of S: S[ps][tp][nt] for tile 2 pair_of(w, ps) + tp and
-// value tile nt; Sx[tp] for tile 32 + tp and value tile e.
+// The accumulators of one wave's share of S and Z: S[ps][tp][nt] for tile 2 pair_of(w, ps) + tp
+// and value tile nt; X[nt] for tile 32 + e and value tile nt (e >= 0), or X[0] for the Z tile
+// (z >> 1, z & 1) (z >= 0).
 struct Acc32 {
   f32x4 S[kFull][2][4];
-  f32x4 Sx[2];
+  f32x4 X[4];
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int ps = 0; ps < kFull; ++ps)
@@ -307,11 +313,11 @@ struct Acc32 {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) S[ps][tp][nt] = zero4();
 #pragma unroll
-    for (int tp = 0; tp < 2; ++tp) Sx[tp] = zero4();
+    for (int nt = 0; nt < 4; ++nt) X[nt] = zero4();
   }
   // f(accumulator, state float offset of its fragment) for every owned fragment
   template <class F>
-  __device__ __forceinline__ void each(int w, int e, int lane, F&& f) {
+  __device__ __forceinline__ void each(int w, int e, int z, int lane, F&& f) {
 #pragma unroll
     for (int ps = 0; ps < kFull; ++ps)
 #pragma unroll
@@ -321,16 +327,17 @@ struct Acc32 {
           f(S[ps][tp][nt], (((2 * pair_of(w, ps) + tp) * 4 + nt) * 64 + lane) * 4);
     if (e >= 0) {
 #pragma unroll
-      for (int tp = 0; tp < 2; ++tp) f(Sx[tp], (((32 + tp) * 4 + e) * 64 + lane) * 4);
+      for (int nt = 0; nt < 4; ++nt) f(X[nt], (((32 + e) * 4 + nt) * 64 + lane) * 4);
     }
+    if (z >= 0) f(X[0], kZOff + (z * 64 + lane) * 4);
   }
 };
 
-// S += Phi(K)^T V over one staged chunk; Zt += the 16 x 16 tile (z >> 1, z & 1) of K^T K when
-// z >= 0.  e and z are wave-uniform.
+// S += Phi(K)^T V over one staged chunk; the Z accumulator += the 16 x 16 tile (z >> 1, z & 1)
+// of K^T K when z >= 0.  e and z are wave-uniform.
 template <class TL>
-__device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, Acc32& acc, f32x4& Zt,
-                                         int e, int lane, int z) {
+__device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, Acc32& acc, int e,
+                                         int lane, int z) {
   // both 32-key steps unrolled: the LDS addresses of the second become immediate offsets
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
@@ -346,17 +353,22 @@ __device__ __forceinline__ void update32(const TL& tl, const Rows32& rw, Acc32& 
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc.S[ps][tp][nt] = mfma32(a[tp], vb[nt], acc.S[ps][tp][nt]);
     }
-    if (e >= 0) {
-      bf16x8 a[2];
-      phik2(tl, rw.irow[kFull], rw.jrow[kFull], m, lane, a);
-      const bf16x8 ve = v_frag(tl.V, m, e, lane);   // value tile e, a wave-uniform offset
+    if (e >= 0) {                    // tile 32 + e, all four value tiles
+      const int g = lane >> 4, ir = rw.irow[kFull][0], jr = rw.jrow[kFull];
+      const float4 ja = *reinterpret_cast<const float4*>(&tl.KT[jr][32 * m + 4 * g]);
+      const float4 jb = *reinterpret_cast<const float4*>(&tl.KT[jr][32 * m + 16 + 4 * g]);
+      const float4 ia = *reinterpret_cast<const float4*>(&tl.KT[ir][32 * m + 4 * g]);
+      const float4 ib = *reinterpret_cast<const float4*>(&tl.KT[ir][32 * m + 16 + 4 * g]);
+      const uint4 f{pack_bf16x2(ia.x * ja.x, ia.y * ja.y), pack_bf16x2(ia.z * ja.z, ia.w * ja.w),
+                    pack_bf16x2(ib.x * jb.x, ib.y * jb.y), pack_bf16x2(ib.z * jb.z, ib.w * jb.w)};
+      const bf16x8 a = __builtin_bit_cast(bf16x8, f);
 #pragma unroll
-      for (int tp = 0; tp < 2; ++tp) acc.Sx[tp] = mfma32(a[tp], ve, acc.Sx[tp]);
+      for (int nt = 0; nt < 4; ++nt) acc.X[nt] = mfma32(a, vb[nt], acc.X[nt]);
     }
     if (z >= 0) {
       const int mi = z >> 1, kj = z & 1;
       const bf16x8 a = kcol(tl, mi, m, lane), bb = kcol(tl, kj, m, lane);
-      Zt = mfma32(a, bb, Zt);
+      acc.X[0] = mfma32(a, bb, acc.X[0]);
     }
   }
 }
@@ -408,7 +420,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
   }
   Acc32 acc;
   acc.zero();
-  f32x4 Zt = zero4();
   Rows32 rw;
   rw.init(w, e, lane);
   zero_row(tl[0], tid);
@@ -428,12 +439,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
   }
   __syncthreads();
   auto emit = [&](float* dst) {
-    acc.each(w, e, lane, [&](f32x4& x, int off) { *reinterpret_cast<f32x4*>(dst + off) = x; });
-    if (z >= 0) *reinterpret_cast<f32x4*>(dst + kZOff + (z * 64 + lane) * 4) = Zt;
+    acc.each(w, e, z, lane, [&](f32x4& x, int off) { *reinterpret_cast<f32x4*>(dst + off) = x; });
   };
   for (int c = 0; c < nc; ++c) {
     if (c == flush) emit(out);       // the chunks before the segment boundary
-    update32(tl[c & 1], rw, acc, Zt, e, lane, z);
+    update32(tl[c & 1], rw, acc, e, lane, z);
     if (c + 1 < nc) store_state32(st, tl[(c + 1) & 1], tid);   // buffer read last iteration
     if (c + 2 < nc) {
       p.next();
@@ -634,16 +644,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
   // state pass over the chunks before seg L, in the order of their ranges (a range that ends
   // by seg L: its whole sum; the range that crosses seg L: its part before it); zero without
   // states.
-  // Z: wave w with zt >= 0 keeps tile (zt >> 1, zt & 1) in Zt and publishes it split into
+  // Z: wave w with zt >= 0 keeps tile (zt >> 1, zt & 1) in acc.X[0] and publishes it split into
   // bf16 hi + lo.
   const int e = extra_of(w), zt = ztile_of(w);
   Acc32 acc;
   acc.zero();
-  f32x4 Zt = zero4();
   {
     auto add = [&](const float* pre) {
-      acc.each(w, e, lane, [&](f32x4& x, int off) { x += *reinterpret_cast<const f32x4*>(pre + off); });
-      if (zt >= 0) Zt += *reinterpret_cast<const f32x4*>(pre + kZOff + (zt * 64 + lane) * 4);
+      acc.each(w, e, zt, lane, [&](f32x4& x, int off) { x += *reinterpret_cast<const f32x4*>(pre + off); });
     };
     const long long seq = (long long)b * pr.H + h;
     if (states && sp > 0) {
@@ -674,9 +682,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
         sm.Sb[pair_of(w, ps)][nt][lane] = bword(acc.S[ps][0][nt], acc.S[ps][1][nt]);
-    if (e >= 0) sm.Sb[16][e][lane] = bword(acc.Sx[0], acc.Sx[1]);
+    if (e >= 0) {                    // tile 32 + e: half e of the last K step's words
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        reinterpret_cast<uint2*>(&sm.Sb[16][nt][lane])[e] =
+            uint2{pack_bf16x2(acc.X[nt][0], acc.X[nt][1]), pack_bf16x2(acc.X[nt][2], acc.X[nt][3])};
+    }
     if (zt >= 0) {
-      const f32x4 zr = Zt;
+      const f32x4 zr = acc.X[0];
       s16x4 zhi, zlo;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -814,7 +827,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_output32_kernel(
     }
 
     // ---- state update with this chunk (registers only: Sb keeps S_{<c} until the barrier) ----
-    update32(tl, rw, acc, Zt, e, lane, zt);
+    update32(tl, rw, acc, e, lane, zt);
     __syncthreads();          // all reads of this chunk's tiles, Sb and Zb; xr and zx written
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
