@@ -15,7 +15,8 @@
 // (a + x, 4J + r) for x in {0, 1}, r in {0..3}, over J = 0 .. p/4 - 1 and even a <= 4J + 2.
 // Every pair i <= j appears exactly once; the few pairs with i > j that the groups also list
 // are zero rows.  Off the diagonal a row carries weight 2, since
-// vec(q q^T) . vec(k k^T) = sum_i q_i^2 k_i^2 + 2 sum_{i<j} q_i q_j k_i k_j.
+// vec(q q^T) . vec(k k^T) = sum_i q_i^2 k_i^2 + 2 sum_{i<j} q_i q_j k_i k_j.  (The p = 32
+// kernels order their rows differently, without most of the zero rows: fast32.hip.)
 #pragma once
 
 #include "device.h"
@@ -56,7 +57,7 @@ __device__ __forceinline__ bf16x8 v_frag(const __bf16 (*V)[ROW], int m, int nt, 
 }
 
 // Double group idx -> (a, J): the groups of column block J are indices J (J + 1) ..
-// J (J + 1) + 2J + 1, one for each even a = 0, 2, .., 4J + 2.  p = 16 has 20 groups, p = 32 72.
+// J (J + 1) + 2J + 1, one for each even a = 0, 2, .., 4J + 2.  p = 16 has 20 groups.
 __device__ __forceinline__ void double_group(int idx, int& a, int& J) {
   J = 0;
   while ((J + 1) * (J + 2) <= idx) ++J;
