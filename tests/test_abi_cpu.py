@@ -305,6 +305,22 @@ def test_groups_do_not_change_workspace_sizes():
             lib.kata_bwd_chunked_workspace_size(ctypes.byref(base))
 
 
+def test_p32_spread_state_pass_workspace():
+    # with 2 to 4 segments whose walks add the prefixes, the p = 32 state pass keeps two states
+    # per segment (the sum of a workgroup's range and of its part before a segment boundary);
+    # with more segments one
+    lib = _lib()
+    out = K._ChunkedPlan()
+    state_bytes = (34 * 16 * 64 + 4 * 256) * 4
+    for B, H, T, seg, n_seg, per_seg in ((4, 16, 16384, 0, 4, 2), (1, 2, 1024, 7, 3, 2),
+                                         (1, 2, 1024, 8, 2, 2), (2, 16, 4096, 0, 8, 1)):
+        pr = _problem(B=B, H=H, T=T, p=32, seg=seg)
+        assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK
+        assert (out.segments, out.walk_sums_prefix, out.scan_levels) == (n_seg, 1, 0)
+        need = lib.kata_fwd_chunked_workspace_size(ctypes.byref(pr))
+        assert need == -(-B * H * n_seg * per_seg * state_bytes // 256) * 256
+
+
 def test_chunked_plan_reports_segments_and_scan_depth():
     lib = _lib()
     out = K._ChunkedPlan()
@@ -341,6 +357,9 @@ def test_chunked_plan_reports_segments_and_scan_depth():
     pr = _problem(B=4, H=16, T=1024, p=32)
     assert lib.kata_fwd_chunked_plan(ctypes.byref(pr), ctypes.byref(out)) == OK
     assert (out.segments, out.chunks_per_segment, out.walk_sums_prefix) == (4, 4, 1)
+    # p = 32 packed state: the 528 unique (i, j) rows and 16 zero rows (34 tiles of 16) x 64,
+    # + Z as four 16 x 16 tiles
+    assert out.state_floats == 34 * 16 * 64 + 4 * 256
     for seg, n_seg, walk_sums in ((4, 8, 1), (3, 11, 0)):   # 32 chunks per sequence
         pr = _problem(B=1, H=2, T=2048)
         pr.seg_chunks = seg
