@@ -236,7 +236,9 @@ def fwd_chunked(q, k, v, chunk=64, eps=1e-6, out_dtype=torch.float32, seg_chunks
 def fwd_chunked_noalloc(q, k, v, out, chunk=64, eps=1e-6, seg_chunks=0, den=None,
                         state="packed", groups=1):
     """fwd_chunked without a workspace: the library's static per-device scratch holds the
-    segment states (problems whose workspace would exceed NOALLOC_SCRATCH_BYTES are rejected).
+    segment states (problems whose workspace would exceed NOALLOC_SCRATCH_BYTES are rejected,
+    except a spread p = 32 state pass that fits with one state per segment, which then runs
+    that way and matches fwd_chunked to rounding).
     The caller passes the output `out` (its dtype is the output dtype) and optionally `den`
     (fp32 (B, T, H)); nothing is allocated.  Calls that overlap on one device race."""
     if out.shape != v.shape or out.device != v.device:

@@ -66,9 +66,11 @@ def test_noalloc_matches_the_workspace_entry_point_twice_second_smaller():
     assert _oracle_rows(q, k, v, out, [(0, 0), (1, 3)], np.arange(1024)) <= 1e-2
 
 
-@pytest.mark.parametrize("case", ["p32", "p16_g2_bf16_out", "p32_g2", "p8_fp32"])
+# p32_spread: 4 segments of 10 chunks, the spread p = 32 state pass (two states per segment)
+@pytest.mark.parametrize("case", ["p32", "p32_spread", "p16_g2_bf16_out", "p32_g2", "p8_fp32"])
 def test_noalloc_other_kernels_match_the_workspace_entry_point(case):
     wid, kw, shape = {"p32": (3, {}, dict(B=2, H=16, T=4096)),
+                      "p32_spread": (3, {"seg_chunks": 10}, dict(B=1, H=4, T=2048)),
                       "p16_g2_bf16_out": (2, {"groups": 2}, dict(B=2, H=8, T=2048)),
                       "p32_g2": (3, {"groups": 2}, dict(B=2, H=8, T=2048)),
                       "p8_fp32": (1, {"chunk": 32}, dict(B=2, H=3, T=256))}[case]
