@@ -9,6 +9,7 @@ path: if libkata.so is missing, or a call fails, an exception is raised.
     o = fwd_chunked(q, k, v, chunk=64)          # exact O(T) chunked-state form
     o = fwd_quadratic(q, k, v)                  # flash-style O(T^2) form
     dq, dk, dv = bwd(q, k, v, dO)               # fp32 gradients of sum(dO * o)
+    o = parallel_kata_attn(q, k, v)             # differentiable: forward + bwd under autograd
     levels, totals = chunk_state_scan(states)   # in-place exclusive prefix scan
     state = recurrent_state(k, v)               # (S, Z) after the given tokens (prefill)
     o = decode(q, k, v, state)                  # advance the state token by token
@@ -24,7 +25,7 @@ import os
 import torch
 
 __all__ = [
-    "KataError", "fwd_quadratic", "fwd_chunked", "fwd_chunked_noalloc", "chunked_workspace_size",
+    "KataError", "parallel_kata_attn", "fwd_quadratic", "fwd_chunked", "fwd_chunked_noalloc", "chunked_workspace_size",
     "chunked_plan", "NOALLOC_SCRATCH_BYTES",
     "chunk_state_scan", "scan_workspace_size", "bwd", "bwd_workspace_size",
     "recurrent_state", "recurrent_state_workspace_size", "decode", "state_shape",
@@ -358,6 +359,45 @@ def bwd(q, k, v, dO, eps=1e-6, workspace=None, chunk=None, groups=1):
         _check(fn(ctypes.byref(pr), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(dO), _ptr(dq), _ptr(dk),
                   _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q.device)), name)
     return dq, dk, dv
+
+
+class _KataAttn(torch.autograd.Function):
+    """fwd_chunked / fwd_quadratic as the forward and bwd as the backward of one autograd node.
+    Only the inputs are kept for the backward, which recomputes what it needs in the library."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, num_groups, form, chunk, eps):
+        if form == "chunked":
+            o = fwd_chunked(q, k, v, chunk=chunk, eps=eps, out_dtype=q.dtype, groups=num_groups)
+        else:
+            o = fwd_quadratic(q, k, v, eps=eps, out_dtype=q.dtype, groups=num_groups)
+        ctx.save_for_backward(q, k, v)
+        # the chunked O(T) backward where T is a multiple of the chunk, else the flash one
+        ctx.cfg = (num_groups, chunk if q.shape[1] % chunk == 0 else None, eps)
+        return o
+
+    @staticmethod
+    def backward(ctx, dO):
+        q, k, v = ctx.saved_tensors
+        groups, chunk, eps = ctx.cfg
+        dq, dk, dv = bwd(q, k, v, dO.contiguous(), eps=eps, chunk=chunk, groups=groups)
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None, None
+
+
+def parallel_kata_attn(q, k, v, num_groups=1, form="auto", chunk=64, eps=1e-6):
+    """Causal KATA attention as a differentiable op: (B, T, H, D) -> (B, T, H, d_v), the
+    output in the inputs' dtype, named and laid out like the KATA README's kernel call
+    (num_groups: the KATA-Mg factor count g).
+
+    form: "chunked" (exact O(T) chunked-state forward; T a multiple of chunk), "quadratic"
+    (flash-style O(T^2)), or "auto" (chunked where T is a multiple of chunk, else quadratic).
+    Under autograd the backward runs bwd (chunked where T is a multiple of chunk, else flash);
+    its fp32 gradients are handed back in the inputs' dtype."""
+    if form == "auto":
+        form = "chunked" if q.shape[1] % chunk == 0 else "quadratic"
+    if form not in ("chunked", "quadratic"):
+        raise ValueError("form must be 'auto', 'chunked' or 'quadratic'")
+    return _KataAttn.apply(q, k, v, num_groups, form, chunk, eps)
 
 
 def timing_begin():

@@ -433,3 +433,14 @@ def test_scan_rejects_a_states_array_beyond_two_to_the_62_bytes():
     assert lib.kata_chunk_state_scan_workspace_size(65535, 1 << 26, 1 << 30) == 0
     assert lib.kata_chunk_state_scan_workspace_size(16, 48, 10496) == 0      # one tile
     assert lib.kata_chunk_state_scan_workspace_size(16, 5000, 10496) > 0     # tile totals
+
+
+def test_parallel_kata_attn_has_no_cpu_path():
+    # the differentiable op marshals into the same entry points: host tensors are refused
+    # before anything reaches the library (there is no CPU fallback)
+    import torch
+    q = torch.randn(1, 64, 2, 16, dtype=torch.bfloat16)
+    v = torch.randn(1, 64, 2, 64, dtype=torch.bfloat16)
+    for form in ("auto", "chunked", "quadratic"):
+        with pytest.raises(ValueError, match="GPU tensor"):
+            K.parallel_kata_attn(q, q, v, form=form)
