@@ -103,6 +103,40 @@ def test_noalloc_unspreads_a_p32_state_pass_beyond_its_scratch():
     assert _oracle_rows(q, k, v, out, [(0, 0), (3, 15)], rows) <= 1e-2
 
 
+@pytest.mark.parametrize("seg", [3, 5])
+def test_noalloc_replays_from_a_hip_graph(seg):
+    # what the entry point is for: a forward captured into a HIP graph with nothing allocated.
+    # Every replay equals the eager call bitwise, with eager calls of the same entry point on
+    # other inputs (the same static scratch) between the replays; seg 3: 11 segments per
+    # sequence and the segment scan, seg 5: 7 segments whose walks sum their prefixes
+    w = W.WORKLOADS[2]
+    q, k, v = (x.to(DEV) for x in W.make_inputs(w, 93, T=2048, B=2, H=4))
+    q2, k2, v2 = (x.to(DEV) for x in W.make_inputs(w, 94, T=2048, B=2, H=4))
+    plan = K.chunked_plan(q, k, v, seg_chunks=seg)
+    assert plan["walk_sums_prefix"] == (seg == 5) and (plan["scan_levels"] > 0) == (seg == 3)
+    o = torch.empty(v.shape, dtype=torch.float32, device=DEV)
+    eager = K.fwd_chunked_noalloc(q, k, v, torch.empty_like(o), seg_chunks=seg).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        K.fwd_chunked_noalloc(q, k, v, o, seg_chunks=seg)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        K.fwd_chunked_noalloc(q, k, v, o, seg_chunks=seg)
+    other = torch.empty_like(o)
+    for r in range(4):
+        o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, eager), f"replay {r} differs from the eager call"
+        K.fwd_chunked_noalloc(q2, k2, v2, other, seg_chunks=seg)
+        torch.cuda.synchronize()
+        assert torch.isfinite(other).all()
+    assert torch.equal(eager, K.fwd_chunked(q, k, v, seg_chunks=seg))
+
+
 def test_noalloc_rejects_a_problem_beyond_its_scratch():
     # one state per chunk (seg_chunks = 1) over 2 x 1024 chunks: 86 MB of states
     w4 = W.WORKLOADS[4]
