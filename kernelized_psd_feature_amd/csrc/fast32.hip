@@ -426,30 +426,41 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_state32_kernel(
   zero_row(tl[1], tid);
 
   // one state per segment: last chunk first (the walk then starts on recently read chunks);
-  // spread: first to last, so the sum at the boundary is the part before it.  One chunk in
-  // flight in registers, two LDS buffers, one barrier per chunk.
+  // spread: first to last, so the sum at the boundary is the part before it.  Two chunks in
+  // flight in registers (one workgroup per CU: no other workgroup hides their latency), two
+  // LDS buffers, one barrier per chunk.
   const int dir = sp == 0 ? -1 : 1;
   Ptrs32 p = ptrs32(pr, nullptr, k, v, b, h, (dir < 0 ? c0 + nc - 1 : c0) * C, false, tid, dir);
-  Stage32 st;
-  load32(st, p);
-  store_state32(st, tl[0], tid);
-  if (nc > 1) {
+  Stage32 sa, sb;
+  load32(sa, p);
+  store_state32(sa, tl[0], tid);
+  if (nc > 1) {                      // chunk 1
     p.next();
-    load32(st, p);
+    load32(sa, p);
+  }
+  if (nc > 2) {                      // chunk 2
+    p.next();
+    load32(sb, p);
   }
   __syncthreads();
   auto emit = [&](float* dst) {
     acc.each(w, e, z, lane, [&](f32x4& x, int off) { *reinterpret_cast<f32x4*>(dst + off) = x; });
   };
-  for (int c = 0; c < nc; ++c) {
+  // chunk c from LDS; `nx` holds chunk c + 1, which goes to the other buffer (read in the
+  // previous iteration, before its barrier), and then takes chunk c + 3
+  auto step = [&](int c, Stage32& nx) {
     if (c == flush) emit(out);       // the chunks before the segment boundary
     update32(tl[c & 1], rw, acc, e, lane, z);
-    if (c + 1 < nc) store_state32(st, tl[(c + 1) & 1], tid);   // buffer read last iteration
-    if (c + 2 < nc) {
+    if (c + 1 < nc) store_state32(nx, tl[(c + 1) & 1], tid);
+    if (c + 3 < nc) {
       p.next();
-      load32(st, p);
+      load32(nx, p);
     }
     __syncthreads();
+  };
+  for (int c = 0; c < nc; c += 2) {
+    step(c, sa);
+    if (c + 1 < nc) step(c + 1, sb);
   }
   emit(out_all ? out_all : out);
 }
