@@ -444,3 +444,43 @@ def test_parallel_kata_attn_has_no_cpu_path():
     for form in ("auto", "chunked", "quadratic"):
         with pytest.raises(ValueError, match="GPU tensor"):
             K.parallel_kata_attn(q, q, v, form=form)
+
+
+def test_parallel_kata_attn_dispatch_and_gradient_plumbing(monkeypatch):
+    # the op's host logic with the library calls replaced by recorders (no arithmetic here):
+    # "auto" takes the chunked forward where T is a multiple of the chunk, else the quadratic
+    # one; the backward is the chunked one in the first case and the flash one in the second;
+    # the output is requested in the inputs' dtype and the fp32 gradients come back in it
+    import torch
+    calls = []
+
+    def fake_fwd(name):
+        def f(q, k, v, **kw):
+            calls.append((name, kw))
+            return torch.full(v.shape, 0.5, dtype=kw["out_dtype"])
+        return f
+
+    def fake_bwd(q, k, v, dO, eps, chunk, groups):
+        calls.append(("bwd", dict(chunk=chunk, groups=groups, eps=eps, dO_dtype=dO.dtype)))
+        return (torch.full(q.shape, 1.0), torch.full(k.shape, 2.0), torch.full(v.shape, 3.0))
+
+    monkeypatch.setattr(K, "fwd_chunked", fake_fwd("chunked"))
+    monkeypatch.setattr(K, "fwd_quadratic", fake_fwd("quadratic"))
+    monkeypatch.setattr(K, "bwd", fake_bwd)
+    for T, fwd_name, bwd_chunk in ((128, "chunked", 64), (100, "quadratic", None)):
+        calls.clear()
+        q = torch.zeros(1, T, 2, 16, dtype=torch.bfloat16, requires_grad=True)
+        k = torch.zeros(1, T, 2, 16, dtype=torch.bfloat16, requires_grad=True)
+        v = torch.zeros(1, T, 2, 64, dtype=torch.bfloat16, requires_grad=True)
+        o = K.parallel_kata_attn(q, k, v, num_groups=2, eps=1e-5)
+        assert o.dtype == torch.bfloat16 and calls[0][0] == fwd_name
+        assert calls[0][1]["groups"] == 2 and calls[0][1]["eps"] == 1e-5
+        o.float().sum().backward()
+        assert calls[1] == ("bwd", dict(chunk=bwd_chunk, groups=2, eps=1e-5,
+                                         dO_dtype=torch.bfloat16))
+        for x, val in ((q, 1.0), (k, 2.0), (v, 3.0)):
+            assert x.grad.dtype == torch.bfloat16 and bool((x.grad == val).all())
+    calls.clear()
+    q = torch.zeros(1, 128, 2, 16, requires_grad=True)
+    K.parallel_kata_attn(q, q, torch.zeros(1, 128, 2, 64), form="quadratic", chunk=32)
+    assert calls[0][0] == "quadratic" and calls[0][1]["out_dtype"] == torch.float32
